@@ -1,0 +1,474 @@
+/*
+ * Plain CPU oracle for the MATE token-mixing core of LinGen.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, obviously-correct
+ * definition that the GPU library is checked against. Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it. It shares
+ * no code, header, table or helper with the HIP library, and the HIP library
+ * never calls it.
+ *
+ * Everything is computed in double precision with explicit loops, in the
+ * order the method is described:
+ *
+ *   - Rotary Major Scan (RMS) and the flipped sequence: four unroll orders of
+ *     the T x H x W latent tensor that swap which axis is unrolled first
+ *     (QbitAI article "LinGen ...", section "方法", the RMS paragraphs; the
+ *     xllm-io review "LinGen: Towards High-Resolution Minute-Length ...",
+ *     section 三 "MA-Branch" item 2, which names the four orders and the flip
+ *     n_flip = T*H*W - n).
+ *   - Review tokens: an average-pooled copy of the token tensor, unrolled in
+ *     the same order and put in front of the sequence (forward) or, flipped,
+ *     in front of the flipped sequence (xllm-io review, section 三 item 3;
+ *     QbitAI article, review-token paragraph).
+ *   - Bidirectional Mamba2 scan: the sequential state-space recurrence
+ *     h_u = exp(dt_u A) h_{u-1} + dt_u x_u B_u^T, y_u = C_u^T h_u + D x_u,
+ *     run over the forward sequence and over the flipped sequence, the two
+ *     outputs summed (xllm-io review, section 三 item 1: Mamba2 alone gives the
+ *     lower-triangular map, the bidirectional version the full map).
+ *   - TESA: softmax attention restricted to 3D windows Tw x Sw x Sw whose
+ *     partition is offset by a shift on alternate layers (xllm-io review,
+ *     section 三 "TE-Branch"; nav.superapi summary, "TE-branch" bullet).
+ *
+ * Readings where the pages are silent (all documented in the design notes):
+ *   - flip is the reversal i -> N-1-i;
+ *   - pooling windows do not overlap (stride = kernel) and must divide the grid;
+ *   - the recurrence starts from h = 0; outputs at review positions are dropped;
+ *   - both directions share x, B, C, dt, A, D, so the sum carries 2 D x;
+ *   - shifted windows: along each axis the region id of coordinate c is
+ *     (c + w - s) div w, so edge regions are smaller and nothing wraps around;
+ *   - attention scale is 1/sqrt(d) unless given; no position bias.
+ *
+ * Inputs are float32 arrays (values that may already be bf16-rounded; the
+ * upcast to double is exact). Outputs are double.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL -1
+#define ORACLE_ENOMEM -2
+
+/* ------------------------------------------------------------------------ */
+/* Rotary Major Scan                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* seq[i] = canonical index n(t,h,w) = (t*H + h)*W + w of the token at scan
+ * position i.  Loops are written outermost first:
+ *   order 0 spatial-row major:     for t, for h, for w
+ *   order 1 spatial-column major:  for t, for w, for h
+ *   order 2 temporal-row major:    for h, for w, for t
+ *   order 3 temporal-column major: for w, for h, for t
+ * flip != 0 reverses the sequence. */
+int oracle_rms_sequence(int64_t T, int64_t H, int64_t W, int order, int flip, int64_t *seq)
+{
+    if (T <= 0 || H <= 0 || W <= 0 || order < 0 || order > 3 || !seq) return ORACLE_EINVAL;
+    int64_t i = 0;
+    if (order == 0) {
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t w = 0; w < W; ++w) seq[i++] = (t * H + h) * W + w;
+    } else if (order == 1) {
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t w = 0; w < W; ++w)
+                for (int64_t h = 0; h < H; ++h) seq[i++] = (t * H + h) * W + w;
+    } else if (order == 2) {
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t w = 0; w < W; ++w)
+                for (int64_t t = 0; t < T; ++t) seq[i++] = (t * H + h) * W + w;
+    } else {
+        for (int64_t w = 0; w < W; ++w)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t t = 0; t < T; ++t) seq[i++] = (t * H + h) * W + w;
+    }
+    if (flip) {
+        int64_t N = T * H * W;
+        for (int64_t a = 0, b = N - 1; a < b; ++a, --b) {
+            int64_t tmp = seq[a];
+            seq[a] = seq[b];
+            seq[b] = tmp;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Whole-row permutation of a [batch][T][H][W][row_bytes] byte tensor.
+ * inverse == 0: dst[b][i] = src[b][seq[i]]  (canonical -> scan order)
+ * inverse != 0: dst[b][seq[i]] = src[b][i]  (scan order -> canonical) */
+int oracle_rms_reorder(const uint8_t *src, uint8_t *dst, int64_t batch, int64_t T, int64_t H,
+                       int64_t W, int64_t row_bytes, int order, int flip, int inverse)
+{
+    if (!src || !dst || batch <= 0 || row_bytes <= 0) return ORACLE_EINVAL;
+    int64_t N = T * H * W;
+    int64_t *seq = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+    if (!seq) return ORACLE_ENOMEM;
+    int rc = oracle_rms_sequence(T, H, W, order, flip, seq);
+    if (rc) {
+        free(seq);
+        return rc;
+    }
+    for (int64_t b = 0; b < batch; ++b) {
+        const uint8_t *s = src + b * N * row_bytes;
+        uint8_t *d = dst + b * N * row_bytes;
+        for (int64_t i = 0; i < N; ++i) {
+            if (!inverse)
+                memcpy(d + i * row_bytes, s + seq[i] * row_bytes, (size_t)row_bytes);
+            else
+                memcpy(d + seq[i] * row_bytes, s + i * row_bytes, (size_t)row_bytes);
+        }
+    }
+    free(seq);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Review tokens                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Average-pool one batch element of a [T][H][W][C] tensor over disjoint
+ * pt x ph x pw blocks, then unroll the pooled T' x H' x W' grid in RMS order
+ * `order` (not flipped): out[j][c] for j = 0 .. T'H'W' - 1. */
+int oracle_review_pool(const float *src, int64_t T, int64_t H, int64_t W, int64_t C, int pt,
+                       int ph, int pw, int order, double *out)
+{
+    if (!src || !out || C <= 0 || pt <= 0 || ph <= 0 || pw <= 0) return ORACLE_EINVAL;
+    if (T % pt || H % ph || W % pw) return ORACLE_EINVAL;
+    int64_t Tp = T / pt, Hp = H / ph, Wp = W / pw, R = Tp * Hp * Wp;
+    int64_t *seq = (int64_t *)malloc(sizeof(int64_t) * (size_t)R);
+    double *pooled = (double *)calloc((size_t)(R * C), sizeof(double));
+    if (!seq || !pooled) {
+        free(seq);
+        free(pooled);
+        return ORACLE_ENOMEM;
+    }
+    double count = (double)pt * (double)ph * (double)pw;
+    for (int64_t tq = 0; tq < Tp; ++tq)
+        for (int64_t hq = 0; hq < Hp; ++hq)
+            for (int64_t wq = 0; wq < Wp; ++wq) {
+                double *acc = pooled + ((tq * Hp + hq) * Wp + wq) * C;
+                for (int64_t t = tq * pt; t < (tq + 1) * pt; ++t)
+                    for (int64_t h = hq * ph; h < (hq + 1) * ph; ++h)
+                        for (int64_t w = wq * pw; w < (wq + 1) * pw; ++w) {
+                            const float *row = src + ((t * H + h) * W + w) * C;
+                            for (int64_t c = 0; c < C; ++c) acc[c] += (double)row[c];
+                        }
+                for (int64_t c = 0; c < C; ++c) acc[c] /= count;
+            }
+    int rc = oracle_rms_sequence(Tp, Hp, Wp, order, 0, seq);
+    if (!rc)
+        for (int64_t j = 0; j < R; ++j) memcpy(out + j * C, pooled + seq[j] * C, sizeof(double) * (size_t)C);
+    free(seq);
+    free(pooled);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A tiny work queue over pthreads                                           */
+/* ------------------------------------------------------------------------ */
+
+typedef void (*unit_fn)(void *ctx, int64_t unit);
+typedef struct {
+    unit_fn fn;
+    void *ctx;
+    int64_t nunits;
+    int64_t next;
+    pthread_mutex_t lock;
+} work_queue;
+
+static void *worker(void *arg)
+{
+    work_queue *q = (work_queue *)arg;
+    for (;;) {
+        pthread_mutex_lock(&q->lock);
+        int64_t u = q->next++;
+        pthread_mutex_unlock(&q->lock);
+        if (u >= q->nunits) break;
+        q->fn(q->ctx, u);
+    }
+    return NULL;
+}
+
+static void run_units(unit_fn fn, void *ctx, int64_t nunits, int nthreads)
+{
+    work_queue q;
+    q.fn = fn;
+    q.ctx = ctx;
+    q.nunits = nunits;
+    q.next = 0;
+    pthread_mutex_init(&q.lock, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 1024) nthreads = 1024;
+    if ((int64_t)nthreads > nunits) nthreads = (int)(nunits > 0 ? nunits : 1);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    int started = 0;
+    for (int i = 1; th && i < nthreads; ++i)
+        if (pthread_create(&th[started], NULL, worker, &q) == 0) ++started;
+    worker(&q);
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&q.lock);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bidirectional Mamba2 scan                                                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float *x, *B, *C, *dt, *A, *D;
+    int64_t batch, N, R;
+    int nheads, P, S, G, head_lo, head_hi;
+    const int64_t *seq;      /* scan order, N entries */
+    const double *rx, *rB, *rdt; /* review tokens per batch: [b][R][nheads*P], [b][R][G*S], [b][R][nheads] */
+    double *yf, *yb;         /* [b][N][nh][P] for the forward / backward direction */
+} ssd_ctx;
+
+/* One recurrence step on the P x S state of one head. */
+static void ssd_step(double *h, int P, int S, double decay, double dt, const double *xv, const double *bv)
+{
+    for (int p = 0; p < P; ++p)
+        for (int s = 0; s < S; ++s) h[p * S + s] = decay * h[p * S + s] + dt * xv[p] * bv[s];
+}
+
+static void ssd_unit(void *vctx, int64_t unit)
+{
+    ssd_ctx *c = (ssd_ctx *)vctx;
+    int nh = c->head_hi - c->head_lo;
+    int64_t b = unit / (2 * nh);
+    int hl = (int)((unit / 2) % nh);
+    int dir = (int)(unit % 2);
+    int head = c->head_lo + hl;
+    int g = head / (c->nheads / c->G); /* heads are split evenly over the B/C groups */
+    int P = c->P, S = c->S;
+    int64_t N = c->N, R = c->R;
+    double A = (double)c->A[head], D = (double)c->D[head];
+    double *h = (double *)calloc((size_t)P * S, sizeof(double));
+    double *xv = (double *)malloc(sizeof(double) * P);
+    double *bv = (double *)malloc(sizeof(double) * S);
+    double *out = (dir == 0 ? c->yf : c->yb) + b * N * nh * P;
+    if (!h || !xv || !bv) { free(h); free(xv); free(bv); return; }
+
+    /* Review prefix: rev_o for the forward direction, its reversal for the
+     * backward direction. Only the state is kept. */
+    for (int64_t jj = 0; jj < R; ++jj) {
+        int64_t j = dir == 0 ? jj : R - 1 - jj;
+        const double *rx = c->rx + (b * R + j) * c->nheads * P + head * P;
+        const double *rB = c->rB + (b * R + j) * c->G * S + g * S;
+        double dt = c->rdt[(b * R + j) * c->nheads + head];
+        ssd_step(h, P, S, exp(dt * A), dt, rx, rB);
+    }
+    /* Main sequence: seq_o forward, seq_o reversed backward. */
+    for (int64_t ii = 0; ii < N; ++ii) {
+        int64_t i = dir == 0 ? ii : N - 1 - ii;
+        int64_t n = c->seq[i];
+        const float *xr = c->x + ((b * N + n) * c->nheads + head) * P;
+        const float *Br = c->B + ((b * N + n) * c->G + g) * S;
+        const float *Cr = c->C + ((b * N + n) * c->G + g) * S;
+        double dt = (double)c->dt[(b * N + n) * c->nheads + head];
+        for (int p = 0; p < P; ++p) xv[p] = (double)xr[p];
+        for (int s = 0; s < S; ++s) bv[s] = (double)Br[s];
+        ssd_step(h, P, S, exp(dt * A), dt, xv, bv);
+        double *yo = out + (n * nh + hl) * P;
+        for (int p = 0; p < P; ++p) {
+            double acc = 0.0;
+            for (int s = 0; s < S; ++s) acc += h[p * S + s] * (double)Cr[s];
+            yo[p] = acc + D * xv[p];
+        }
+    }
+    free(h);
+    free(xv);
+    free(bv);
+}
+
+/* y[b][n][head - head_lo][p] for heads in [head_lo, head_hi).
+ * x  [batch][T][H][W][nheads][P]      B, C [batch][T][H][W][G][S]
+ * dt [batch][T][H][W][nheads] (> 0)    A, D [nheads]
+ * pool_* all zero: no review tokens; otherwise they must divide T, H, W. */
+int oracle_bissd(const float *x, const float *B, const float *C, const float *dt, const float *A,
+                 const float *D, int64_t batch, int64_t T, int64_t H, int64_t W, int nheads, int P,
+                 int S, int G, int order, int pool_t, int pool_h, int pool_w, int head_lo,
+                 int head_hi, int nthreads, double *y)
+{
+    if (!x || !B || !C || !dt || !A || !D || !y) return ORACLE_EINVAL;
+    if (batch <= 0 || T <= 0 || H <= 0 || W <= 0 || nheads <= 0 || P <= 0 || S <= 0 || G <= 0)
+        return ORACLE_EINVAL;
+    if (nheads % G || order < 0 || order > 3) return ORACLE_EINVAL;
+    if (head_lo < 0 || head_hi > nheads || head_lo >= head_hi) return ORACLE_EINVAL;
+    int pooled = pool_t || pool_h || pool_w;
+    if (pooled && (pool_t <= 0 || pool_h <= 0 || pool_w <= 0 || T % pool_t || H % pool_h || W % pool_w))
+        return ORACLE_EINVAL;
+    int64_t N = T * H * W;
+    int64_t R = pooled ? (T / pool_t) * (H / pool_h) * (W / pool_w) : 0;
+    int nh = head_hi - head_lo;
+    int rc = ORACLE_OK;
+
+    int64_t *seq = (int64_t *)malloc(sizeof(int64_t) * (size_t)N);
+    double *yb = (double *)malloc(sizeof(double) * (size_t)(batch * N * nh * P));
+    double *rx = NULL, *rB = NULL, *rdt = NULL;
+    if (!seq || !yb) { rc = ORACLE_ENOMEM; goto done; }
+    rc = oracle_rms_sequence(T, H, W, order, 0, seq);
+    if (rc) goto done;
+    if (R > 0) {
+        rx = (double *)malloc(sizeof(double) * (size_t)(batch * R * nheads * P));
+        rB = (double *)malloc(sizeof(double) * (size_t)(batch * R * G * S));
+        rdt = (double *)malloc(sizeof(double) * (size_t)(batch * R * nheads));
+        if (!rx || !rB || !rdt) { rc = ORACLE_ENOMEM; goto done; }
+        for (int64_t b = 0; b < batch && !rc; ++b) {
+            rc = oracle_review_pool(x + b * N * nheads * P, T, H, W, (int64_t)nheads * P, pool_t, pool_h,
+                                    pool_w, order, rx + b * R * nheads * P);
+            if (!rc)
+                rc = oracle_review_pool(B + b * N * G * S, T, H, W, (int64_t)G * S, pool_t, pool_h, pool_w,
+                                        order, rB + b * R * G * S);
+            if (!rc)
+                rc = oracle_review_pool(dt + b * N * nheads, T, H, W, nheads, pool_t, pool_h, pool_w, order,
+                                        rdt + b * R * nheads);
+        }
+        if (rc) goto done;
+    }
+    {
+        ssd_ctx c;
+        c.x = x; c.B = B; c.C = C; c.dt = dt; c.A = A; c.D = D;
+        c.batch = batch; c.N = N; c.R = R;
+        c.nheads = nheads; c.P = P; c.S = S; c.G = G; c.head_lo = head_lo; c.head_hi = head_hi;
+        c.seq = seq; c.rx = rx; c.rB = rB; c.rdt = rdt;
+        c.yf = y; c.yb = yb;
+        run_units(ssd_unit, &c, batch * nh * 2, nthreads);
+        int64_t total = batch * N * nh * P;
+        for (int64_t e = 0; e < total; ++e) y[e] += yb[e];
+    }
+done:
+    free(seq);
+    free(yb);
+    free(rx);
+    free(rB);
+    free(rdt);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* TESA: attention inside shifted 3D windows                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Region id of coordinate c along an axis with window w and shift s. */
+static int64_t region_id(int64_t c, int64_t w, int64_t s) { return (c + w - s) / w; }
+
+typedef struct {
+    const float *q, *k, *v;
+    int64_t batch, T, H, W, N;
+    int nheads, d, head_lo, head_hi;
+    int64_t wt, wh, ww, st, sh, sw;
+    int64_t id0t, id0h, id0w; /* region id of coordinate 0 along each axis */
+    int64_t nrt, nrh, nrw;    /* number of regions along each axis */
+    const int64_t *regions;   /* region list (linear ids) or NULL for all */
+    int64_t nregions;
+    double scale;
+    double *o;                /* [b][N][nh][d] */
+} tesa_ctx;
+
+static void tesa_unit(void *vctx, int64_t unit)
+{
+    tesa_ctx *c = (tesa_ctx *)vctx;
+    int nh = c->head_hi - c->head_lo;
+    int64_t r_idx = unit % c->nregions;
+    int hl = (int)((unit / c->nregions) % nh);
+    int64_t b = unit / (c->nregions * nh);
+    int head = c->head_lo + hl;
+    int64_t r = c->regions ? c->regions[r_idx] : r_idx;
+    int64_t rw = r % c->nrw, rh = (r / c->nrw) % c->nrh, rt = r / (c->nrw * c->nrh);
+    int64_t want_t = c->id0t + rt, want_h = c->id0h + rh, want_w = c->id0w + rw;
+    int d = c->d;
+
+    /* The region's tokens, in canonical order. */
+    int64_t cap = c->wt * c->wh * c->ww, m = 0;
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)cap);
+    if (!tok || !sc) { free(tok); free(sc); return; }
+    for (int64_t t = 0; t < c->T; ++t) {
+        if (region_id(t, c->wt, c->st) != want_t) continue;
+        for (int64_t h = 0; h < c->H; ++h) {
+            if (region_id(h, c->wh, c->sh) != want_h) continue;
+            for (int64_t w = 0; w < c->W; ++w) {
+                if (region_id(w, c->ww, c->sw) != want_w) continue;
+                if (m < cap) tok[m] = (t * c->H + h) * c->W + w;
+                ++m;
+            }
+        }
+    }
+    if (m > cap) m = cap; /* cannot happen: a region never exceeds the window */
+
+    for (int64_t i = 0; i < m; ++i) {
+        const float *qi = c->q + ((b * c->N + tok[i]) * c->nheads + head) * d;
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < m; ++j) {
+            const float *kj = c->k + ((b * c->N + tok[j]) * c->nheads + head) * d;
+            double s = 0.0;
+            for (int e = 0; e < d; ++e) s += (double)qi[e] * (double)kj[e];
+            sc[j] = c->scale * s;
+            if (sc[j] > mx) mx = sc[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            sc[j] = exp(sc[j] - mx);
+            l += sc[j];
+        }
+        double *oi = c->o + ((b * c->N + tok[i]) * nh + hl) * d;
+        for (int e = 0; e < d; ++e) oi[e] = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            const float *vj = c->v + ((b * c->N + tok[j]) * c->nheads + head) * d;
+            double pj = sc[j] / l;
+            for (int e = 0; e < d; ++e) oi[e] += pj * (double)vj[e];
+        }
+    }
+    free(tok);
+    free(sc);
+}
+
+/* Number of regions along each axis (useful to build region lists). */
+int oracle_tesa_region_counts(int64_t T, int64_t H, int64_t W, int wt, int wh, int ww, int st, int sh,
+                              int sw, int64_t *counts3)
+{
+    if (!counts3 || wt <= 0 || wh <= 0 || ww <= 0) return ORACLE_EINVAL;
+    if (st < 0 || st >= wt || sh < 0 || sh >= wh || sw < 0 || sw >= ww) return ORACLE_EINVAL;
+    counts3[0] = region_id(T - 1, wt, st) - region_id(0, wt, st) + 1;
+    counts3[1] = region_id(H - 1, wh, sh) - region_id(0, wh, sh) + 1;
+    counts3[2] = region_id(W - 1, ww, sw) - region_id(0, ww, sw) + 1;
+    return ORACLE_OK;
+}
+
+/* o[b][n][head - head_lo][e] for heads in [head_lo, head_hi).
+ * q, k, v [batch][T][H][W][nheads][d]. regions: NULL for every region, else a
+ * list of linear region ids (rt * nrh + rh) * nrw + rw; only tokens of the
+ * listed regions are written. scale <= 0 selects 1/sqrt(d). */
+int oracle_tesa(const float *q, const float *k, const float *v, int64_t batch, int64_t T, int64_t H,
+                int64_t W, int nheads, int d, int wt, int wh, int ww, int st, int sh, int sw, double scale,
+                int head_lo, int head_hi, const int64_t *regions, int64_t nregions, int nthreads, double *o)
+{
+    if (!q || !k || !v || !o || batch <= 0 || T <= 0 || H <= 0 || W <= 0 || nheads <= 0 || d <= 0)
+        return ORACLE_EINVAL;
+    if (head_lo < 0 || head_hi > nheads || head_lo >= head_hi) return ORACLE_EINVAL;
+    if (T % wt || H % wh || W % ww) return ORACLE_EINVAL;
+    int64_t counts[3];
+    int rc = oracle_tesa_region_counts(T, H, W, wt, wh, ww, st, sh, sw, counts);
+    if (rc) return rc;
+    int64_t total_regions = counts[0] * counts[1] * counts[2];
+    if (regions) {
+        for (int64_t i = 0; i < nregions; ++i)
+            if (regions[i] < 0 || regions[i] >= total_regions) return ORACLE_EINVAL;
+    } else {
+        nregions = total_regions;
+    }
+    if (nregions <= 0) return ORACLE_OK;
+    tesa_ctx c;
+    c.q = q; c.k = k; c.v = v;
+    c.batch = batch; c.T = T; c.H = H; c.W = W; c.N = T * H * W;
+    c.nheads = nheads; c.d = d; c.head_lo = head_lo; c.head_hi = head_hi;
+    c.wt = wt; c.wh = wh; c.ww = ww; c.st = st; c.sh = sh; c.sw = sw;
+    c.id0t = region_id(0, wt, st); c.id0h = region_id(0, wh, sh); c.id0w = region_id(0, ww, sw);
+    c.nrt = counts[0]; c.nrh = counts[1]; c.nrw = counts[2];
+    c.regions = regions; c.nregions = nregions;
+    c.scale = scale > 0 ? scale : 1.0 / sqrt((double)d);
+    c.o = o;
+    run_units(tesa_unit, &c, batch * (int64_t)(head_hi - head_lo) * nregions, nthreads);
+    return ORACLE_OK;
+}

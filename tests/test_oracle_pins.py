@@ -1,0 +1,401 @@
+"""Pins for the CPU oracle: each check reaches the same result by a route that
+shares nothing with the oracle's own loops (closed forms, library routines,
+the quadratic dual form of the scan, the Swin roll-and-mask construction,
+brute force), so a dropped term, a wrong sign or index, or a swapped operand
+in the oracle fails at least one of them.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# ----------------------------------------------------------------------------
+# Independent helpers (numpy only; nothing here is imported from the oracle)
+# ----------------------------------------------------------------------------
+
+_AXES = {0: (0, 1, 2), 1: (0, 2, 1), 2: (1, 2, 0), 3: (2, 1, 0)}
+
+
+def rms_closed_form(T, H, W, order, flip=False):
+    """The four unroll orders as a transpose of the canonical index grid."""
+    s = np.arange(T * H * W).reshape(T, H, W).transpose(_AXES[order]).ravel()
+    return s[::-1].copy() if flip else s
+
+
+def pool_brute(a, T, H, W, pool, order):
+    pt, ph, pw = pool
+    C = a.size // (T * H * W)
+    m = a.reshape(T // pt, pt, H // ph, ph, W // pw, pw, C).astype(np.float64).mean(axis=(1, 3, 5))
+    m = m.reshape(-1, C)
+    return m[rms_closed_form(T // pt, H // ph, W // pw, order)]
+
+
+def ssd_dual_one_direction(xs, Bs, Cs, dts, A, D):
+    """Quadratic (masked attention) form of one causal Mamba2 scan:
+    y = M x + D x with M_uv = (C_u . B_v) exp(cs_u - cs_v) dt_v for v <= u."""
+    L = xs.shape[0]
+    cs = np.cumsum(dts * A)
+    M = (Cs @ Bs.T) * np.exp(cs[:, None] - cs[None, :]) * dts[None, :]
+    M = np.tril(M)
+    return M @ xs + D * xs
+
+
+def ssd_dual_bidirectional(x, B, C, dt, A, D, T, H, W, order, pool):
+    """Sum of the dual forms over rev ++ seq and flip(rev) ++ flip(seq); one batch."""
+    N = T * H * W
+    nheads, P = x.shape[-2], x.shape[-1]
+    G, S = B.shape[-2], B.shape[-1]
+    x = x.reshape(N, nheads, P).astype(np.float64)
+    B = B.reshape(N, G, S).astype(np.float64)
+    C = C.reshape(N, G, S).astype(np.float64)
+    dt = dt.reshape(N, nheads).astype(np.float64)
+    seq = rms_closed_form(T, H, W, order)
+    y = np.zeros((N, nheads, P))
+    for h in range(nheads):
+        g = h // (nheads // G)
+        if any(pool):
+            rx = pool_brute(x[:, h, :], T, H, W, pool, order)
+            rB = pool_brute(B[:, g, :], T, H, W, pool, order)
+            rdt = pool_brute(dt[:, h:h + 1], T, H, W, pool, order)[:, 0]
+        else:
+            rx, rB, rdt = np.zeros((0, P)), np.zeros((0, S)), np.zeros(0)
+        R = rx.shape[0]
+        # review outputs are computed with C = 0: they are dropped anyway
+        for s_main, rsel in ((seq, slice(None)), (seq[::-1], slice(None, None, -1))):
+            xs = np.concatenate([rx[rsel], x[s_main, h]])
+            Bs = np.concatenate([rB[rsel], B[s_main, g]])
+            Cs = np.concatenate([np.zeros((R, S)), C[s_main, g]])
+            ds = np.concatenate([rdt[rsel], dt[s_main, h]])
+            yy = ssd_dual_one_direction(xs, Bs, Cs, ds, float(A[h]), float(D[h]))
+            y[s_main, h] += yy[R:]
+    return y.reshape(1, T, H, W, nheads, P)
+
+
+def rand_ssd(rng, T, H, W, nheads, P, S, G=1, a_scale=1.0):
+    x = rng.standard_normal((1, T, H, W, nheads, P)).astype(np.float32)
+    B = rng.standard_normal((1, T, H, W, G, S)).astype(np.float32)
+    C = rng.standard_normal((1, T, H, W, G, S)).astype(np.float32)
+    dt = np.log1p(np.exp(rng.normal(-1.0, 0.5, (1, T, H, W, nheads)))).astype(np.float32)
+    A = (-np.exp(rng.uniform(0, 1, nheads)) * a_scale).astype(np.float32)
+    D = rng.standard_normal(nheads).astype(np.float32)
+    return x, B, C, dt, A, D
+
+
+def relerr(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ----------------------------------------------------------------------------
+# Rotary Major Scan
+# ----------------------------------------------------------------------------
+
+def test_rms_golden_hand_example(oracle_mod):
+    rows = [l for l in open(os.path.join(GOLDEN, "rms_2x2x3.txt")) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 8
+    for line in rows:
+        head, seq = line.split(":")
+        order, flip = (int(v) for v in head.split())
+        want = np.array([int(v) for v in seq.split()])
+        got = oracle_mod.rms_sequence(2, 2, 3, order, bool(flip))
+        np.testing.assert_array_equal(got, want)
+
+
+def test_rms_closed_form_bijection_and_flip(oracle_mod):
+    for T, H, W in itertools.product(range(1, 6), repeat=3):
+        N = T * H * W
+        for order in range(4):
+            s = oracle_mod.rms_sequence(T, H, W, order, False)
+            f = oracle_mod.rms_sequence(T, H, W, order, True)
+            np.testing.assert_array_equal(np.sort(s), np.arange(N))          # bijection
+            np.testing.assert_array_equal(s, rms_closed_form(T, H, W, order))  # library transpose
+            np.testing.assert_array_equal(f, s[::-1])                         # flip = reversal
+            np.testing.assert_array_equal(f[::-1], s)                         # involution
+
+
+def test_rms_reorder_roundtrip(oracle_mod):
+    rng = np.random.default_rng(1)
+    for (T, H, W) in [(2, 3, 5), (4, 1, 7), (3, 3, 3)]:
+        N = T * H * W
+        src = rng.integers(0, 256, size=(2, N, 6), dtype=np.uint8)
+        for order in range(4):
+            for flip in (False, True):
+                fwd = oracle_mod.rms_reorder(src, T, H, W, order, flip, inverse=False)
+                seq = rms_closed_form(T, H, W, order, flip)
+                np.testing.assert_array_equal(fwd, src[:, seq])
+                back = oracle_mod.rms_reorder(fwd, T, H, W, order, flip, inverse=True)
+                np.testing.assert_array_equal(back, src)
+
+
+def test_rms_rejects_bad_order(oracle_mod):
+    with pytest.raises(ValueError):
+        oracle_mod.rms_sequence(2, 2, 2, 4)
+
+
+# ----------------------------------------------------------------------------
+# Review tokens
+# ----------------------------------------------------------------------------
+
+def test_review_pool_brute_force(oracle_mod):
+    rng = np.random.default_rng(2)
+    for (T, H, W, pool) in [(4, 4, 6, (2, 2, 3)), (2, 4, 4, (2, 2, 2)), (6, 2, 4, (3, 1, 2))]:
+        a = rng.standard_normal((T, H, W, 5)).astype(np.float32)
+        for order in range(4):
+            got = oracle_mod.review_pool(a, T, H, W, pool, order)
+            np.testing.assert_allclose(got, pool_brute(a, T, H, W, pool, order), rtol=1e-13, atol=1e-14)
+
+
+def test_review_pool_unit_window_is_identity(oracle_mod):
+    rng = np.random.default_rng(3)
+    a = rng.standard_normal((3, 2, 4, 3)).astype(np.float32)
+    for order in range(4):
+        got = oracle_mod.review_pool(a, 3, 2, 4, (1, 1, 1), order)
+        np.testing.assert_array_equal(got, a.reshape(-1, 3)[rms_closed_form(3, 2, 4, order)].astype(np.float64))
+
+
+# ----------------------------------------------------------------------------
+# Bidirectional Mamba2 scan
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", [0, 1, 2, 3])
+@pytest.mark.parametrize("pool", [(0, 0, 0), (2, 2, 2)])
+def test_ssd_equals_quadratic_dual_form(oracle_mod, order, pool):
+    rng = np.random.default_rng(10 + order)
+    T, H, W = 2, 4, 4
+    x, B, C, dt, A, D = rand_ssd(rng, T, H, W, nheads=2, P=3, S=5)
+    got = oracle_mod.bissd(x, B, C, dt, A, D, (1, T, H, W), order, pool)
+    want = ssd_dual_bidirectional(x[0], B[0], C[0], dt[0], A, D, T, H, W, order, pool)
+    assert relerr(got, want) < 1e-12
+
+
+def test_ssd_groups_split_heads(oracle_mod):
+    rng = np.random.default_rng(11)
+    T, H, W = 2, 2, 4
+    x, B, C, dt, A, D = rand_ssd(rng, T, H, W, nheads=4, P=2, S=3, G=2)
+    got = oracle_mod.bissd(x, B, C, dt, A, D, (1, T, H, W), 1, (1, 2, 2))
+    want = ssd_dual_bidirectional(x[0], B[0], C[0], dt[0], A, D, T, H, W, 1, (1, 2, 2))
+    assert relerr(got, want) < 1e-12
+
+
+def test_ssd_dense_bidirectional_matrix(oracle_mod):
+    """Without review tokens the sum of both directions is one dense matrix:
+    lower triangle exp(sum_{k=s+1..t} a_k), upper exp(sum_{k=t..s-1} a_k), diagonal twice."""
+    rng = np.random.default_rng(12)
+    T, H, W = 3, 2, 3
+    x, B, C, dt, A, D = rand_ssd(rng, T, H, W, nheads=2, P=4, S=3)
+    order = 3
+    got = oracle_mod.bissd(x, B, C, dt, A, D, (1, T, H, W), order)
+    seq = rms_closed_form(T, H, W, order)
+    N = T * H * W
+    for h in range(2):
+        xs = x[0].reshape(N, 2, 4)[seq, h].astype(np.float64)
+        Bs = B[0].reshape(N, 3)[seq].astype(np.float64)
+        Cs = C[0].reshape(N, 3)[seq].astype(np.float64)
+        a = dt[0].reshape(N, 2)[seq, h].astype(np.float64) * float(A[h])
+        ds = dt[0].reshape(N, 2)[seq, h].astype(np.float64)
+        M = np.zeros((N, N))
+        for t in range(N):
+            for s in range(N):
+                if s < t:
+                    w = np.exp(a[s + 1:t + 1].sum())
+                elif s > t:
+                    w = np.exp(a[t:s].sum())
+                else:
+                    w = 2.0
+                M[t, s] = (Cs[t] @ Bs[s]) * ds[s] * w
+        want = M @ xs + 2.0 * float(D[h]) * xs
+        np.testing.assert_allclose(got[0].reshape(N, 2, 4)[seq, h], want, rtol=1e-11, atol=1e-12)
+
+
+def test_ssd_zero_B_gives_2Dx(oracle_mod):
+    rng = np.random.default_rng(13)
+    x, B, C, dt, A, D = rand_ssd(rng, 2, 2, 2, nheads=3, P=4, S=2)
+    B[:] = 0
+    got = oracle_mod.bissd(x, B, C, dt, A, D, (1, 2, 2, 2), 2, (2, 1, 2))
+    np.testing.assert_array_equal(got, 2.0 * D.astype(np.float64)[:, None] * x.astype(np.float64))
+
+
+def test_ssd_strong_decay_keeps_diagonal(oracle_mod):
+    """exp(dt*A) = 0 wipes every earlier token (and the review prefix):
+    y_t = 2 (dt_t C_t . B_t + D) x_t."""
+    rng = np.random.default_rng(14)
+    x, B, C, dt, A, D = rand_ssd(rng, 2, 2, 4, nheads=2, P=3, S=4)
+    A[:] = -1e6
+    got = oracle_mod.bissd(x, B, C, dt, A, D, (1, 2, 2, 4), 1, (1, 2, 2))
+    cb = np.sum(C.astype(np.float64) * B.astype(np.float64), axis=-1)  # [1,T,H,W,1]
+    want = 2.0 * (dt.astype(np.float64)[..., None] * cb[..., None] + D.astype(np.float64)[:, None]) * x
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_ssd_zero_decay_is_cumulative_linear_attention(oracle_mod):
+    """A = 0: forward y_t = sum_{s<=t} (C_t.B_s) dt_s x_s; backward the same for s >= t."""
+    rng = np.random.default_rng(15)
+    T, H, W = 2, 3, 2
+    x, B, C, dt, A, D = rand_ssd(rng, T, H, W, nheads=1, P=2, S=3)
+    A[:] = 0
+    D[:] = 0
+    got = oracle_mod.bissd(x, B, C, dt, A, D, (1, T, H, W), 0)
+    N = T * H * W
+    xs = x.reshape(N, 2).astype(np.float64)
+    Bs = B.reshape(N, 3).astype(np.float64)
+    Cs = C.reshape(N, 3).astype(np.float64)
+    ds = dt.reshape(N).astype(np.float64)
+    kv = np.cumsum(ds[:, None, None] * xs[:, :, None] * Bs[:, None, :], axis=0)       # prefix states
+    kvb = np.cumsum((ds[:, None, None] * xs[:, :, None] * Bs[:, None, :])[::-1], axis=0)[::-1]
+    want = np.einsum("tps,ts->tp", kv + kvb, Cs)
+    np.testing.assert_allclose(got.reshape(N, 2), want, rtol=1e-12, atol=1e-12)
+
+
+def test_ssd_review_equals_initial_state(oracle_mod):
+    """Scanning rev ++ seq equals scanning seq from the state the review tokens leave."""
+    rng = np.random.default_rng(16)
+    T, H, W, pool, order = 2, 4, 4, (2, 2, 2), 2
+    x, B, C, dt, A, D = rand_ssd(rng, T, H, W, nheads=1, P=2, S=3)
+    got = oracle_mod.bissd(x, B, C, dt, A, D, (1, T, H, W), order, pool)
+    N = T * H * W
+    xs = x.reshape(N, 2).astype(np.float64)
+    Bs = B.reshape(N, 3).astype(np.float64)
+    Cs = C.reshape(N, 3).astype(np.float64)
+    ds = dt.reshape(N).astype(np.float64)
+    rx = pool_brute(xs, T, H, W, pool, order)
+    rB = pool_brute(Bs, T, H, W, pool, order)
+    rd = pool_brute(ds[:, None], T, H, W, pool, order)[:, 0]
+    a0 = float(A[0])
+
+    def final_state(xr, Br, dr):
+        h = np.zeros((2, 3))
+        for j in range(len(dr)):
+            h = np.exp(dr[j] * a0) * h + dr[j] * np.outer(xr[j], Br[j])
+        return h
+
+    seq = rms_closed_form(T, H, W, order)
+    y = np.zeros((N, 2))
+    for s_main, h0 in ((seq, final_state(rx, rB, rd)), (seq[::-1], final_state(rx[::-1], rB[::-1], rd[::-1]))):
+        h = h0
+        for n in s_main:
+            h = np.exp(ds[n] * a0) * h + ds[n] * np.outer(xs[n], Bs[n])
+            y[n] += h @ Cs[n] + float(D[0]) * xs[n]
+    np.testing.assert_allclose(got.reshape(N, 2), y, rtol=1e-12, atol=1e-12)
+
+
+def test_ssd_linear_in_x(oracle_mod):
+    rng = np.random.default_rng(17)
+    x1, B, C, dt, A, D = rand_ssd(rng, 2, 2, 2, nheads=2, P=3, S=2)
+    x2 = rng.standard_normal(x1.shape).astype(np.float32)
+    g = (1, 2, 2, 2)
+    y1 = oracle_mod.bissd(x1, B, C, dt, A, D, g, 1, (1, 1, 2))
+    y2 = oracle_mod.bissd(x2, B, C, dt, A, D, g, 1, (1, 1, 2))
+    y12 = oracle_mod.bissd(x1 + 2 * x2, B, C, dt, A, D, g, 1, (1, 1, 2))
+    assert relerr(y12, y1 + 2 * y2) < 1e-6  # x1 + 2 x2 is rounded to float32 once
+
+
+def test_ssd_head_range_matches_full(oracle_mod):
+    rng = np.random.default_rng(18)
+    x, B, C, dt, A, D = rand_ssd(rng, 2, 2, 4, nheads=4, P=2, S=3)
+    full = oracle_mod.bissd(x, B, C, dt, A, D, (1, 2, 2, 4), 3, (2, 2, 2))
+    part = oracle_mod.bissd(x, B, C, dt, A, D, (1, 2, 2, 4), 3, (2, 2, 2), heads=(1, 3))
+    np.testing.assert_array_equal(part, full[..., 1:3, :])
+
+
+def test_ssd_rejects_non_dividing_pool(oracle_mod):
+    rng = np.random.default_rng(19)
+    x, B, C, dt, A, D = rand_ssd(rng, 2, 2, 3, nheads=1, P=2, S=2)
+    with pytest.raises(ValueError):
+        oracle_mod.bissd(x, B, C, dt, A, D, (1, 2, 2, 3), 0, (2, 2, 2))
+
+
+# ----------------------------------------------------------------------------
+# TESA
+# ----------------------------------------------------------------------------
+
+def swin_same_window(T, H, W, window, shift):
+    """Attend mask from the Swin construction: cyclically roll the grid by -shift,
+    cut the rolled grid into windows, and inside the windows that straddle the
+    roll boundary keep the two sides apart with slice labels."""
+    def axis_labels(D, w, s):
+        c = np.arange(D)
+        rolled = (c - s) % D                    # position after roll(-s)
+        win = rolled // w
+        lab = np.zeros(D, dtype=int)
+        if s > 0:                               # slices (0,-w), (-w,-s), (-s,None) of the rolled axis
+            lab[(rolled >= D - w) & (rolled < D - s)] = 1
+            lab[rolled >= D - s] = 2
+        return win * 3 + lab
+    lt, lh, lw = (axis_labels(D, w, s) for D, w, s in zip((T, H, W), window, shift))
+    key = (lt[:, None, None] * 10_000 + lh[None, :, None] * 100 + lw[None, None, :]).ravel()
+    return key[:, None] == key[None, :]
+
+
+def masked_attention(q, k, v, mask, scale):
+    s = scale * (q @ k.T)
+    s = np.where(mask, s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+@pytest.mark.parametrize("window,shift", [((2, 2, 2), (0, 0, 0)), ((2, 2, 2), (1, 1, 1)),
+                                          ((2, 4, 2), (1, 2, 1)), ((4, 2, 4), (2, 1, 3))])
+def test_tesa_equals_swin_masked_full_attention(oracle_mod, window, shift):
+    rng = np.random.default_rng(20)
+    T, H, W, nh, d = 4, 4, 8, 2, 5
+    q, k, v = (rng.standard_normal((1, T, H, W, nh, d)).astype(np.float32) for _ in range(3))
+    got = oracle_mod.tesa(q, k, v, (1, T, H, W), window, shift)
+    mask = swin_same_window(T, H, W, window, shift)
+    N = T * H * W
+    for h in range(nh):
+        want = masked_attention(*(a.reshape(N, nh, d)[:, h].astype(np.float64) for a in (q, k, v)),
+                                mask, 1.0 / np.sqrt(d))
+        np.testing.assert_allclose(got.reshape(N, nh, d)[:, h], want, rtol=1e-11, atol=1e-12)
+
+
+def test_tesa_whole_grid_is_sdpa(oracle_mod):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    T, H, W, nh, d = 2, 3, 4, 3, 8
+    q, k, v = (rng.standard_normal((1, T, H, W, nh, d)).astype(np.float32) for _ in range(3))
+    got = oracle_mod.tesa(q, k, v, (1, T, H, W), (T, H, W), (0, 0, 0))
+    tq, tk, tv = (torch.from_numpy(a.reshape(T * H * W, nh, d).astype(np.float64)).transpose(0, 1)
+                  for a in (q, k, v))
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).transpose(0, 1).numpy()
+    np.testing.assert_allclose(got.reshape(-1, nh, d), want, rtol=1e-11, atol=1e-12)
+
+
+def test_tesa_unit_window_returns_v(oracle_mod):
+    rng = np.random.default_rng(22)
+    q, k, v = (rng.standard_normal((1, 2, 3, 4, 2, 3)).astype(np.float32) for _ in range(3))
+    got = oracle_mod.tesa(q, k, v, (1, 2, 3, 4), (1, 1, 1), (0, 0, 0))
+    np.testing.assert_array_equal(got, v.astype(np.float64))
+
+
+def test_tesa_zero_query_gives_window_mean(oracle_mod):
+    rng = np.random.default_rng(23)
+    T, H, W, d = 4, 4, 4, 3
+    q = np.zeros((1, T, H, W, 1, d), np.float32)
+    k, v = (rng.standard_normal((1, T, H, W, 1, d)).astype(np.float32) for _ in range(2))
+    got = oracle_mod.tesa(q, k, v, (1, T, H, W), (2, 2, 4), (0, 0, 0))
+    mean = v.reshape(2, 2, 2, 2, 1, 4, d).astype(np.float64).mean(axis=(1, 3, 5), keepdims=True)
+    want = np.broadcast_to(mean, (2, 2, 2, 2, 1, 4, d)).reshape(1, T, H, W, 1, d)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-14)
+
+
+def test_tesa_region_counts_and_subset(oracle_mod):
+    assert oracle_mod.tesa_region_counts(32, 32, 32, (8, 8, 8), (4, 4, 4)) == (5, 5, 5)
+    assert oracle_mod.tesa_region_counts(32, 32, 32, (8, 8, 8), (0, 0, 0)) == (4, 4, 4)
+    assert oracle_mod.tesa_region_counts(2, 4, 4, (2, 2, 2), (1, 1, 1)) == (2, 3, 3)
+    rng = np.random.default_rng(24)
+    q, k, v = (rng.standard_normal((1, 4, 4, 4, 2, 3)).astype(np.float32) for _ in range(3))
+    full = oracle_mod.tesa(q, k, v, (1, 4, 4, 4), (2, 2, 2), (1, 1, 1))
+    part = oracle_mod.tesa(q, k, v, (1, 4, 4, 4), (2, 2, 2), (1, 1, 1), heads=(1, 2), regions=[0, 13])
+    ok = ~np.isnan(part)
+    assert ok.sum() == (1 + 8) * 3          # corner region 1x1x1, centre region 2x2x2
+    np.testing.assert_array_equal(part[ok], full[..., 1:2, :][ok])
+
+
+def test_tesa_rejects_bad_shift(oracle_mod):
+    q = np.zeros((1, 2, 2, 2, 1, 2), np.float32)
+    with pytest.raises(ValueError):
+        oracle_mod.tesa(q, q, q, (1, 2, 2, 2), (2, 2, 2), (2, 0, 0))
