@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""MATE-core forward throughput on one MI355X.
+
+One step is the four-layer schedule of the long-grid workload (128 x 48 x 48
+latent tokens, LinGen-4B widths): layer l scans in RMS order l and its TESA
+windows are shifted on odd layers. Each layer is one ``mate_forward`` call
+(bidirectional SSD with review tokens + TESA) through the C ABI. Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints one JSON line with tokens/s (tokens = T*H*W per layer forward), the
+roofline position of the dominant kernel, per-call timings and the CPU oracle
+timed on a bounded sample on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MATE-core tokens/sec (bi-SSD + TESA fwd) at 1 GPU; % MFMA / HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0   # dense MFMA, MI355X
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work (what the method must compute and move)
+# ---------------------------------------------------------------------------
+
+def region_sizes(D, w, s):
+    if s == 0:
+        return [w] * (D // w)
+    return [s] + [w] * ((D - s) // w) + ([D - s - ((D - s) // w) * w] if (D - s) % w else [])
+
+
+def tesa_pairs(wl, shift):
+    """Sum over windows of |window|^2 (in-window query-key pairs)."""
+    st = [a * a for a in region_sizes(wl.T, wl.window[0], shift[0])]
+    sh = [a * a for a in region_sizes(wl.H, wl.window[1], shift[1])]
+    sw = [a * a for a in region_sizes(wl.W, wl.window[2], shift[2])]
+    return sum(st) * sum(sh) * sum(sw)
+
+
+def work(wl):
+    e = 2 if wl.dtype == "bf16" else 4
+    Hs, P, S, G, Q = wl.nheads, wl.headdim, wl.d_state, wl.ngroups, wl.chunk
+    scanned = wl.N + wl.R
+    ssd_flops = 2.0 * (Hs * (4 * P * S + P * (Q + 1)) + G * S * (Q + 1)) * scanned
+    ssd_bytes = (2 * Hs * P * e + 2 * G * S * e + 4 * Hs) * wl.N
+    tesa_bytes = 4 * wl.t_heads * wl.t_dim * e * wl.N
+    tesa_flops = {sh: 4.0 * wl.t_dim * wl.t_heads * tesa_pairs(wl, wl.layer_shift(sh)) for sh in (False, True)}
+    return dict(ssd_flops=ssd_flops, ssd_bytes=ssd_bytes, tesa_flops=tesa_flops, tesa_bytes=tesa_bytes,
+                reorder_bytes=2 * wl.N * Hs * P * e)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same layers
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, si, ti, threads):
+    import numpy as np
+
+    import oracle
+    from linear_complexity_video_amd import synth
+
+    def f32(t, hs=None):
+        a = t.dev if hs is None else t.dev[..., hs[0]:hs[1], :]
+        return synth.bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.ascontiguousarray(a)
+
+    hs = max(1, threads // 2)  # (head, direction) units: one per thread
+    x = f32(si["x"], (0, hs))
+    Bm, Cm = f32(si["B"]), f32(si["C"])
+    dt = np.ascontiguousarray(si["dt"].dev[..., :hs])
+    t0 = time.perf_counter()
+    oracle.bissd(x, Bm, Cm, dt, si["A"].dev[:hs], si["D"].dev[:hs], wl.grid, 0, wl.pool, nthreads=threads)
+    t_ssd = (time.perf_counter() - t0) * wl.nheads / hs
+    qkv = [f32(ti[k], (0, 1)) for k in ("q", "k", "v")]
+    t_tesa = {}
+    for shifted in (False, True):
+        t0 = time.perf_counter()
+        oracle.tesa(*qkv, wl.grid, wl.window, wl.layer_shift(shifted), nthreads=threads)
+        t_tesa[shifted] = (time.perf_counter() - t0) * wl.t_heads
+    layer_s = sum(t_ssd + t_tesa[sh] for _, sh in wl.schedule) / len(wl.schedule)
+    return {
+        "value": wl.N / layer_s,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"bi-SSD heads 0..{hs - 1} of {wl.nheads} (order 0, review tokens) and TESA head 0 of "
+                   f"{wl.t_heads} (unshifted and shifted) over the full {wl.T}x{wl.H}x{wl.W} grid; "
+                   f"per-layer time scaled by heads and averaged over the layer schedule"),
+        "layer_seconds_est": layer_s,
+    }
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="workload index (default: the long grid)")
+    ap.add_argument("--algo", choices=("auto", "portable", "fast"), default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=5, help="timed repetitions of each single call")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the MATE core here runs on a single MI355X; "
+              f"--gpus {args.gpus} (WORLD_SIZE {world}) is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_complexity_video_amd import binding as B
+    from linear_complexity_video_amd import synth
+    from linear_complexity_video_amd.workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()
+    algo = {"auto": B.ALGO_AUTO, "portable": B.ALGO_PORTABLE, "fast": B.ALGO_FAST}[args.algo]
+    wl = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+
+    log(f"generating inputs for {wl.name} ...")
+    t0 = time.perf_counter()
+    si = synth.make_ssd_inputs(wl, keep_f32=False)
+    ti = synth.make_tesa_inputs(wl, keep_f32=False)
+
+    def to_dev(t):
+        a = t.dev
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    ssd = {k: to_dev(si[n]) for k, n in (("x", "x"), ("b", "B"), ("c", "C"), ("dt", "dt"), ("a", "A"), ("d", "D"))}
+    att = {k: to_dev(ti[k]) for k in ("q", "k", "v")}
+    ssd["y"] = torch.empty_like(ssd["x"])
+    att["o"] = torch.empty_like(att["q"])
+    sdesc = B.ssd_desc(ssd["x"], ssd["b"], wl.chunk, wl.pool, algo)
+    tdesc = B.tesa_desc(att["q"], wl.window, (0, 0, 0), 0.0, algo)
+    ws = torch.empty(max(1, B.mate_forward_workspace_size(wl.grid, sdesc, tdesc)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; workspace {ws.numel() / 2**30:.2f} GiB")
+
+    def layer(order, shifted):
+        B.mate_forward(ssd, att, order, wl.chunk, wl.pool, wl.window, wl.layer_shift(shifted), algo=algo,
+                       workspace=ws)
+
+    def step():
+        for order, shifted in wl.schedule:
+            layer(order, shifted)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_step = wl.N * len(wl.schedule)
+    value = tokens_per_step * args.steps / elapsed
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value / 1e6:.3f} M tokens/s")
+
+    # Per-call timings with events on the launch stream (torch's current stream).
+    stream = torch.cuda.current_stream()
+
+    def time_call(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+    w = work(wl)
+    reps = args.kernel_reps
+    t_tesa = {sh: time_call(lambda sh=sh: B.mate_tesa(att["q"], att["k"], att["v"], att["o"], wl.window,
+                                                      wl.layer_shift(sh), 0.0, algo), reps) for sh in (False, True)}
+    t_ssd = time_call(lambda: B.mate_bissd_scan(ssd["x"], ssd["b"], ssd["c"], ssd["dt"], ssd["a"], ssd["d"],
+                                                ssd["y"], 0, wl.chunk, wl.pool, algo, workspace=ws), reps)
+    xr = ssd["x"].view(wl.batch, wl.N, -1)
+    xo = torch.empty_like(xr)
+    t_rms = time_call(lambda: B.mate_rms_reorder(xr, xo, wl.grid, 1, True, False), reps)
+
+    peak_flops = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    tesa_tf = w["tesa_flops"][False] / t_tesa[False] / 1e12
+    ssd_tf = w["ssd_flops"] / t_ssd / 1e12
+    kernels = {
+        "tesa_unshifted": {"ms": t_tesa[False] * 1e3, "tflops": tesa_tf, "mfma_frac": tesa_tf / peak_flops,
+                           "hbm_frac": w["tesa_bytes"] / t_tesa[False] / 1e9 / PEAK_HBM_GBS},
+        "tesa_shifted": {"ms": t_tesa[True] * 1e3, "tflops": w["tesa_flops"][True] / t_tesa[True] / 1e12,
+                         "mfma_frac": w["tesa_flops"][True] / t_tesa[True] / 1e12 / peak_flops},
+        "bissd": {"ms": t_ssd * 1e3, "tflops": ssd_tf, "mfma_frac": ssd_tf / peak_flops,
+                  "hbm_frac": w["ssd_bytes"] / t_ssd / 1e9 / PEAK_HBM_GBS},
+        "rms_reorder_x": {"ms": t_rms * 1e3, "gbs": w["reorder_bytes"] / t_rms / 1e9,
+                          "hbm_frac": w["reorder_bytes"] / t_rms / 1e9 / PEAK_HBM_GBS},
+    }
+    # The TESA kernel is one launch per call, so the events above time exactly that kernel.
+    roofline = {"bound": "mfma", "kernel": "tesa (unshifted layer)", "achieved": tesa_tf, "peak": peak_flops,
+                "unit": "TFLOP/s", "frac": tesa_tf / peak_flops, "traffic": None,
+                "algorithmic_per_launch": {"flops": w["tesa_flops"][False], "bytes": w["tesa_bytes"]}}
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: batch {wl.batch}, {wl.N} tokens, four-layer schedule "
+                        f"(RMS order l, TESA shifted on odd l)",
+            "grid": [wl.T, wl.H, wl.W], "batch": wl.batch, "tokens_per_layer": wl.N,
+            "layers_per_step": len(wl.schedule), "review_tokens": wl.R,
+            "ssd": {"heads": wl.nheads, "headdim": wl.headdim, "d_state": wl.d_state, "groups": wl.ngroups,
+                    "chunk": wl.chunk, "pool": list(wl.pool)},
+            "tesa": {"heads": wl.t_heads, "headdim": wl.t_dim, "window": list(wl.window), "shift": list(wl.shift)},
+            "algo": args.algo,
+        },
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"timing the CPU oracle on a sample with {threads} threads ...")
+        out["cpu_baseline"] = cpu_baseline(wl, si, ti, threads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

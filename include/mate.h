@@ -1,0 +1,193 @@
+/*
+ * mate.h -- C ABI of the MI355X (gfx950) forward core of LinGen's MATE block.
+ *
+ * The MATE block replaces DiT self-attention with two branches (QbitAI article
+ * on LinGen, section "方法"; arXiv-daily abstract of "LinGen: Towards
+ * High-Resolution Minute-Length Text-to-Video Generation with Linear
+ * Computational Complexity"):
+ *   - the MA branch: Rotary Major Scan (RMS) of the T x H x W latent tokens,
+ *     average-pooled review tokens put in front, and a bidirectional Mamba2
+ *     (SSD) scan over the sequence and its flip;
+ *   - the TE branch: TESA, attention inside 3D windows Tw x Sw x Sw whose
+ *     partition shifts on alternate layers.
+ * This library computes that token-mixing core. The projections around it are
+ * not part of it.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA storage).
+ *     The caller owns every buffer; the library never allocates, frees or
+ *     keeps device memory between calls.
+ *   - Token tensors are channels-last: [batch][T][H][W][...], so the canonical
+ *     token index is n = (t*H + h)*W + w and a token's channels are contiguous.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *     call enqueues its kernels asynchronously on it and returns; nothing
+ *     synchronises. Calls are thread-safe; buffers used by calls in flight on
+ *     different streams must not overlap.
+ *   - Arguments are validated on the host before anything is launched. A call
+ *     that returns a status other than MATE_OK has launched nothing and written
+ *     nothing; mate_last_error() then describes why (thread-local string).
+ *   - bf16 means bfloat16 (1 sign, 8 exponent, 7 mantissa bits); arithmetic is
+ *     fp32 inside, results are rounded to nearest-even on store.
+ */
+#ifndef MATE_H
+#define MATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MATE_ABI_VERSION 1
+
+typedef enum {
+    MATE_OK = 0,
+    MATE_ERR_NULL = 1,        /* a required pointer is NULL */
+    MATE_ERR_SHAPE = 2,       /* an extent <= 0, order not in 0..3, window/pool not dividing
+                                 the grid, shift outside [0, window), heads not divisible by
+                                 groups, chunk < 1 */
+    MATE_ERR_UNSUPPORTED = 3, /* legal for the method but not built (e.g. a head size the
+                                 kernels are not instantiated for) */
+    MATE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the *_workspace_size result */
+    MATE_ERR_DEVICE = 5       /* a HIP call or kernel launch failed */
+} mate_status;
+
+typedef enum { MATE_F32 = 0, MATE_BF16 = 1 } mate_dtype;
+
+/* Kernel family. AUTO picks the MFMA kernels when the shape has them and the
+ * portable kernels otherwise; the other values force one family (FAST returns
+ * MATE_ERR_UNSUPPORTED when the shape has no MFMA kernel). Both compute the
+ * same result up to rounding order. */
+typedef enum { MATE_ALGO_AUTO = 0, MATE_ALGO_PORTABLE = 1, MATE_ALGO_FAST = 2 } mate_algo;
+
+typedef struct {
+    int64_t batch, T, H, W;
+} mate_grid;
+
+/* ------------------------------------------------------------------------ */
+/* Rotary Major Scan                                                         */
+/* ------------------------------------------------------------------------ */
+/* Unrolls the T x H x W token tensor into one of four 1D orders that differ in
+ * which axis is unrolled first (QbitAI article, section "方法", RMS paragraphs;
+ * xllm-io review of the LinGen paper, section 三 "MA-Branch" item 2, which
+ * names the four orders and the flipped sequence). Scan position i maps to the
+ * canonical token perm(i), with the loops written outermost first:
+ *   order 0 spatial-row major      for t, for h, for w   (canonical order)
+ *   order 1 spatial-column major   for t, for w, for h
+ *   order 2 temporal-row major     for h, for w, for t
+ *   order 3 temporal-column major  for w, for h, for t
+ * flip != 0 reverses the sequence: perm'(i) = perm(N-1-i), N = T*H*W.
+ *
+ * Copies whole token rows of `row_bytes` bytes:
+ *   inverse == 0:  dst[b][i]       = src[b][perm(i)]   (canonical -> scan order)
+ *   inverse != 0:  dst[b][perm(i)] = src[b][i]         (scan order -> canonical)
+ * src and dst are [batch][N][row_bytes] and must not overlap. The copy is
+ * bit-exact for any row content. row_bytes may be any positive value; rows
+ * whose size and addresses are multiples of 16 bytes take the vector path. */
+mate_status mate_rms_reorder(const void *src, void *dst, mate_grid g, int64_t row_bytes, int order,
+                             int flip, int inverse, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Bidirectional Mamba2 (SSD) scan with review tokens                         */
+/* ------------------------------------------------------------------------ */
+/* For every head h (group g = h / (nheads / ngroups)) and for each direction
+ * the recurrence
+ *     h_u = exp(dt_u * A_h) h_{u-1} + dt_u x_u B_u^T,   y_u = h_u C_u + D_h x_u,
+ * runs from h = 0 over the sequence in RMS order `order` (forward) and over
+ * the flipped sequence (backward); y = y_forward + y_backward, written back in
+ * canonical order (xllm-io review, section 三 "MA-Branch" item 1: Mamba2 gives
+ * the lower-triangular map, the bidirectional form the full one).
+ *
+ * Review tokens (xllm-io review, section 三 item 3; QbitAI article, review-token
+ * paragraph): when pool_t, pool_h, pool_w are not all zero, x, B, C and dt are
+ * average-pooled over disjoint pool_t x pool_h x pool_w blocks, the pooled grid
+ * is unrolled in the same order and put in front of the forward sequence, and
+ * its reversal in front of the flipped sequence. Their outputs are dropped;
+ * they only prime the state. The pool extents must divide T, H, W.
+ *
+ * Layouts: x, y [batch][T][H][W][nheads][headdim]          (dtype)
+ *          b, c [batch][T][H][W][ngroups][d_state]          (dtype)
+ *          dt   [batch][T][H][W][nheads]   fp32, already positive (post-softplus)
+ *          a, d [nheads]                   fp32, a < 0 expected
+ * `chunk` is the chunk length of the chunked (SSD) evaluation; it does not
+ * change the result beyond rounding. */
+typedef struct {
+    int32_t nheads, headdim, d_state, ngroups, chunk;
+    int32_t pool_t, pool_h, pool_w; /* all 0: no review tokens */
+    mate_dtype dtype;               /* of x, b, c, y */
+    mate_algo algo;
+} mate_ssd_desc;
+
+typedef struct {
+    const void *x, *b, *c;
+    const float *dt, *a, *d;
+    void *y;
+} mate_ssd_tensors;
+
+/* Bytes of device workspace mate_bissd_scan needs (0 on invalid arguments). */
+size_t mate_bissd_workspace_size(mate_grid g, const mate_ssd_desc *d);
+
+/* Supported: headdim and d_state in 8..128 for the portable kernels (the
+ * product headdim*d_state <= 16384), chunk in 1..128; bf16 with headdim 64,
+ * d_state 64 or 128 and chunk 64 or 128 also has MFMA kernels. The workspace
+ * (device memory, at least mate_bissd_workspace_size bytes, 256-byte aligned)
+ * is scratch for the call; its contents on entry do not matter. */
+mate_status mate_bissd_scan(const mate_ssd_tensors *t, mate_grid g, int order, const mate_ssd_desc *d,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* TESA: attention inside shifted 3D windows                                  */
+/* ------------------------------------------------------------------------ */
+/* The grid is cut into windows win_t x win_h x win_w (Tw x Sw x Sw) and every
+ * token attends only to the tokens of its own window (xllm-io review, section
+ * 三 "TE-Branch"); on shifted layers the partition moves (nav.superapi
+ * summary, "TE-branch" bullet: windows shift alternately between layers).
+ * Along an axis of extent D with window w and shift s (0 <= s < w) the window
+ * id of coordinate c is (c + w - s) div w: the interior windows have size w,
+ * the first has size s and the last w - s (when s > 0); nothing wraps around.
+ * For every head and window:  O_i = sum_j softmax_j(scale * q_i . k_j) v_j.
+ * Layouts: q, k, v, o [batch][T][H][W][nheads][headdim] (dtype). The windows
+ * must divide the grid. scale <= 0 selects 1/sqrt(headdim). */
+typedef struct {
+    int32_t nheads, headdim;
+    int32_t win_t, win_h, win_w;
+    int32_t shift_t, shift_h, shift_w; /* 0 on unshifted layers */
+    float scale;
+    mate_dtype dtype;
+    mate_algo algo;
+} mate_tesa_desc;
+
+typedef struct {
+    const void *q, *k, *v;
+    void *o;
+} mate_tesa_tensors;
+
+/* Supported: headdim 8..128 (multiple of 8) and windows of at most 1024 tokens
+ * for the portable kernel; bf16 with headdim 64 or 128 also has MFMA kernels. */
+mate_status mate_tesa(const mate_tesa_tensors *t, mate_grid g, const mate_tesa_desc *d, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* One MATE core forward                                                     */
+/* ------------------------------------------------------------------------ */
+/* One layer's token mixing: the MA branch (mate_bissd_scan in RMS order
+ * `order`) and the TE branch (mate_tesa with the descriptor's shift) on the
+ * same grid. The two branch outputs are returned separately (s->y and a->o):
+ * their widths differ and the pages leave their combination to the layer's
+ * projections. The result equals the two calls made one after the other. */
+size_t mate_forward_workspace_size(mate_grid g, const mate_ssd_desc *sd, const mate_tesa_desc *td);
+mate_status mate_forward(const mate_ssd_tensors *s, const mate_ssd_desc *sd, const mate_tesa_tensors *a,
+                         const mate_tesa_desc *td, mate_grid g, int order, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+const char *mate_status_string(mate_status s);
+const char *mate_last_error(void); /* detail of the last non-OK status on this thread */
+int mate_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MATE_H */

@@ -1,0 +1,217 @@
+"""ctypes binding of ``libmate.so`` (the C ABI in ``include/mate.h``).
+
+Argument marshalling only: tensors are torch CUDA tensors (contiguous,
+channels-last ``[batch][T][H][W][heads][dim]``); their data pointers and the
+current HIP stream are passed to the C functions of the same names. Every step
+of the computation runs in the library's HIP kernels; if the library is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmate.so")
+
+MATE_OK, MATE_ERR_NULL, MATE_ERR_SHAPE, MATE_ERR_UNSUPPORTED, MATE_ERR_WORKSPACE, MATE_ERR_DEVICE = range(6)
+MATE_F32, MATE_BF16 = 0, 1
+ALGO_AUTO, ALGO_PORTABLE, ALGO_FAST = 0, 1, 2
+
+EXPORTED = (
+    "mate_rms_reorder", "mate_bissd_workspace_size", "mate_bissd_scan", "mate_tesa",
+    "mate_forward_workspace_size", "mate_forward", "mate_status_string", "mate_last_error",
+    "mate_abi_version",
+)
+
+
+class MateError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+        self.detail = detail
+
+
+class Grid(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64)]
+
+
+class SsdDesc(ctypes.Structure):
+    _fields_ = [("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32), ("d_state", ctypes.c_int32),
+                ("ngroups", ctypes.c_int32), ("chunk", ctypes.c_int32), ("pool_t", ctypes.c_int32),
+                ("pool_h", ctypes.c_int32), ("pool_w", ctypes.c_int32), ("dtype", ctypes.c_int),
+                ("algo", ctypes.c_int)]
+
+
+class SsdTensors(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p), ("dt", ctypes.c_void_p),
+                ("a", ctypes.c_void_p), ("d", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class TesaDesc(ctypes.Structure):
+    _fields_ = [("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32), ("win_t", ctypes.c_int32),
+                ("win_h", ctypes.c_int32), ("win_w", ctypes.c_int32), ("shift_t", ctypes.c_int32),
+                ("shift_h", ctypes.c_int32), ("shift_w", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int), ("algo", ctypes.c_int)]
+
+
+class TesaTensors(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with linear_complexity_video_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.mate_rms_reorder.argtypes = [P, P, Grid, I64, I32, I32, I32, P]
+    L.mate_bissd_workspace_size.argtypes = [Grid, ctypes.POINTER(SsdDesc)]
+    L.mate_bissd_workspace_size.restype = SZ
+    L.mate_bissd_scan.argtypes = [ctypes.POINTER(SsdTensors), Grid, I32, ctypes.POINTER(SsdDesc), P, SZ, P]
+    L.mate_tesa.argtypes = [ctypes.POINTER(TesaTensors), Grid, ctypes.POINTER(TesaDesc), P]
+    L.mate_forward_workspace_size.argtypes = [Grid, ctypes.POINTER(SsdDesc), ctypes.POINTER(TesaDesc)]
+    L.mate_forward_workspace_size.restype = SZ
+    L.mate_forward.argtypes = [ctypes.POINTER(SsdTensors), ctypes.POINTER(SsdDesc), ctypes.POINTER(TesaTensors),
+                               ctypes.POINTER(TesaDesc), Grid, I32, P, SZ, P]
+    for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_tesa", "mate_forward"):
+        getattr(L, f).restype = ctypes.c_int
+    L.mate_status_string.argtypes = [ctypes.c_int]
+    L.mate_status_string.restype = ctypes.c_char_p
+    L.mate_last_error.restype = ctypes.c_char_p
+    L.mate_abi_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != MATE_OK:
+        raise MateError(status, lib().mate_last_error().decode())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MATE_F32
+    if t.dtype == torch.bfloat16:
+        return MATE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16 expected")
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts):
+    for t in ts:
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+
+
+def grid_of(t) -> Grid:
+    """Grid of a [batch][T][H][W][...] tensor."""
+    return Grid(*t.shape[:4])
+
+
+# ---------------------------------------------------------------------------
+# Rotary Major Scan
+# ---------------------------------------------------------------------------
+
+def mate_rms_reorder(src, dst, grid, order: int, flip: bool = False, inverse: bool = False, stream=None):
+    """Row permutation src -> dst in RMS ``order`` (see include/mate.h)."""
+    _dev(src, dst)
+    g = Grid(*grid)
+    rows = g.batch * g.T * g.H * g.W
+    nbytes = src.numel() * src.element_size()
+    _need(nbytes == dst.numel() * dst.element_size() and nbytes % rows == 0, "src/dst size mismatch with grid")
+    _check(lib().mate_rms_reorder(_ptr(src), _ptr(dst), g, nbytes // rows, order, int(flip), int(inverse),
+                                  _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Bidirectional SSD scan
+# ---------------------------------------------------------------------------
+
+def ssd_desc(x, b, chunk: int, pool=(0, 0, 0), algo: int = ALGO_AUTO) -> SsdDesc:
+    return SsdDesc(x.shape[-2], x.shape[-1], b.shape[-1], b.shape[-2], chunk, pool[0], pool[1], pool[2],
+                   _dtype(x), algo)
+
+
+def mate_bissd_workspace_size(grid, desc: SsdDesc) -> int:
+    return int(lib().mate_bissd_workspace_size(Grid(*grid), ctypes.byref(desc)))
+
+
+def _workspace(nbytes: int, like):
+    import torch
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+
+
+def mate_bissd_scan(x, b, c, dt, a, d, y, order: int, chunk: int, pool=(0, 0, 0), algo: int = ALGO_AUTO,
+                    workspace=None, stream=None):
+    """y = bidirectional Mamba2 scan of x in RMS ``order`` (see include/mate.h)."""
+    _dev(x, b, c, dt, a, d, y)
+    grid = tuple(x.shape[:4])
+    desc = ssd_desc(x, b, chunk, pool, algo)
+    if workspace is None:
+        workspace = _workspace(mate_bissd_workspace_size(grid, desc), x)
+    t = SsdTensors(_ptr(x), _ptr(b), _ptr(c), _ptr(dt), _ptr(a), _ptr(d), _ptr(y))
+    _check(lib().mate_bissd_scan(ctypes.byref(t), Grid(*grid), order, ctypes.byref(desc), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# TESA
+# ---------------------------------------------------------------------------
+
+def tesa_desc(q, window, shift=(0, 0, 0), scale: float = 0.0, algo: int = ALGO_AUTO) -> TesaDesc:
+    return TesaDesc(q.shape[-2], q.shape[-1], window[0], window[1], window[2], shift[0], shift[1], shift[2],
+                    scale, _dtype(q), algo)
+
+
+def mate_tesa(q, k, v, o, window, shift=(0, 0, 0), scale: float = 0.0, algo: int = ALGO_AUTO, stream=None):
+    """o = attention of q, k, v inside (shifted) 3D windows (see include/mate.h)."""
+    _dev(q, k, v, o)
+    desc = tesa_desc(q, window, shift, scale, algo)
+    t = TesaTensors(_ptr(q), _ptr(k), _ptr(v), _ptr(o))
+    _check(lib().mate_tesa(ctypes.byref(t), grid_of(q), ctypes.byref(desc), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# MATE core forward
+# ---------------------------------------------------------------------------
+
+def mate_forward_workspace_size(grid, sdesc: SsdDesc, tdesc: TesaDesc) -> int:
+    return int(lib().mate_forward_workspace_size(Grid(*grid), ctypes.byref(sdesc), ctypes.byref(tdesc)))
+
+
+def mate_forward(ssd: dict, tesa: dict, order: int, chunk: int, pool, window, shift, scale: float = 0.0,
+                 algo: int = ALGO_AUTO, workspace=None, stream=None):
+    """One layer's MATE core: ssd{x,b,c,dt,a,d,y} and tesa{q,k,v,o} (see include/mate.h)."""
+    x = ssd["x"]
+    _dev(*ssd.values(), *tesa.values())
+    grid = tuple(x.shape[:4])
+    sdesc = ssd_desc(x, ssd["b"], chunk, pool, algo)
+    tdesc = tesa_desc(tesa["q"], window, shift, scale, algo)
+    if workspace is None:
+        workspace = _workspace(mate_forward_workspace_size(grid, sdesc, tdesc), x)
+    st = SsdTensors(*(_ptr(ssd[k]) for k in ("x", "b", "c", "dt", "a", "d", "y")))
+    tt = TesaTensors(*(_ptr(tesa[k]) for k in ("q", "k", "v", "o")))
+    _check(lib().mate_forward(ctypes.byref(st), ctypes.byref(sdesc), ctypes.byref(tt), ctypes.byref(tdesc),
+                              Grid(*grid), order, _ptr(workspace), workspace.numel(), _stream(stream)))

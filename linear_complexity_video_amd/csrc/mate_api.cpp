@@ -1,0 +1,280 @@
+// C ABI of the MATE core: argument validation (before any launch), workspace
+// sizing and kernel dispatch. See include/mate.h for the contract.
+#include "mate.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mate_status fail(mate_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+mate_status device_fail(hipError_t e, const char *what)
+{
+    return fail(MATE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;
+
+mate_status check_grid(mate_grid g)
+{
+    if (g.batch <= 0 || g.T <= 0 || g.H <= 0 || g.W <= 0)
+        return fail(MATE_ERR_SHAPE, "grid extents must be positive (batch=%lld T=%lld H=%lld W=%lld)",
+                    (long long)g.batch, (long long)g.T, (long long)g.H, (long long)g.W);
+    if (g.T > kMaxTokens || g.H > kMaxTokens || g.W > kMaxTokens ||
+        g.T * g.H > kMaxTokens || g.T * g.H * g.W >= kMaxTokens || g.batch * g.T * g.H * g.W >= kMaxTokens)
+        return fail(MATE_ERR_UNSUPPORTED, "grid too large: batch*T*H*W must stay below 2^31 tokens");
+    return MATE_OK;
+}
+
+// Per-device one-time function attributes (LDS limits).
+mate_status prepare_device()
+{
+    static std::atomic<int> done[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return MATE_OK;
+    if (done[dev].load(std::memory_order_acquire)) return MATE_OK;
+    if ((e = mate::ssd_portable_prepare()) != hipSuccess) return device_fail(e, "hipFuncSetAttribute");
+    if ((e = mate::ssd_fast_prepare()) != hipSuccess) return device_fail(e, "hipFuncSetAttribute");
+    done[dev].store(1, std::memory_order_release);
+    return MATE_OK;
+}
+
+bool valid_dtype(mate_dtype d) { return d == MATE_F32 || d == MATE_BF16; }
+bool valid_algo(mate_algo a) { return a == MATE_ALGO_AUTO || a == MATE_ALGO_PORTABLE || a == MATE_ALGO_FAST; }
+
+// Validates the SSD descriptor and fills the derived problem; `fast` tells
+// which kernel family will run.
+mate_status make_ssd_problem(mate_grid g, int order, const mate_ssd_desc *d, mate::SsdProblem &p, bool &fast)
+{
+    if (!d) return fail(MATE_ERR_NULL, "ssd descriptor is NULL");
+    mate_status s = check_grid(g);
+    if (s != MATE_OK) return s;
+    if (order < 0 || order > 3) return fail(MATE_ERR_SHAPE, "order %d not in 0..3", order);
+    if (d->nheads <= 0 || d->headdim <= 0 || d->d_state <= 0 || d->ngroups <= 0)
+        return fail(MATE_ERR_SHAPE, "nheads, headdim, d_state and ngroups must be positive");
+    if (d->chunk < 1) return fail(MATE_ERR_SHAPE, "chunk %d < 1", d->chunk);
+    if (d->nheads % d->ngroups) return fail(MATE_ERR_SHAPE, "nheads %d not divisible by ngroups %d", d->nheads, d->ngroups);
+    if (!valid_dtype(d->dtype)) return fail(MATE_ERR_SHAPE, "unknown dtype %d", (int)d->dtype);
+    if (!valid_algo(d->algo)) return fail(MATE_ERR_SHAPE, "unknown algo %d", (int)d->algo);
+    const bool pooled = d->pool_t || d->pool_h || d->pool_w;
+    if (pooled) {
+        if (d->pool_t <= 0 || d->pool_h <= 0 || d->pool_w <= 0)
+            return fail(MATE_ERR_SHAPE, "pool extents must be all zero or all positive");
+        if (g.T % d->pool_t || g.H % d->pool_h || g.W % d->pool_w)
+            return fail(MATE_ERR_SHAPE, "pool %dx%dx%d does not divide the grid", d->pool_t, d->pool_h, d->pool_w);
+    }
+    if (d->headdim > 128 || d->d_state > 128)
+        return fail(MATE_ERR_UNSUPPORTED, "headdim and d_state above 128 are not built");
+    if (d->chunk > 128) return fail(MATE_ERR_UNSUPPORTED, "chunk above 128 is not built");
+    if ((int64_t)d->nheads * g.batch * g.T * g.H * g.W >= kMaxTokens)
+        return fail(MATE_ERR_UNSUPPORTED, "batch*tokens*nheads must stay below 2^31");
+    p.batch = g.batch; p.T = g.T; p.H = g.H; p.W = g.W; p.N = g.T * g.H * g.W;
+    p.nheads = d->nheads; p.headdim = d->headdim; p.d_state = d->d_state; p.ngroups = d->ngroups;
+    p.chunk = d->chunk; p.order = order;
+    p.pool_t = pooled ? d->pool_t : 0; p.pool_h = pooled ? d->pool_h : 0; p.pool_w = pooled ? d->pool_w : 0;
+    p.R = pooled ? (g.T / d->pool_t) * (g.H / d->pool_h) * (g.W / d->pool_w) : 0;
+    p.nch = (int)((p.N + d->chunk - 1) / d->chunk);
+    p.nchR = (int)((p.R + d->chunk - 1) / d->chunk);
+    p.dtype = d->dtype == MATE_BF16 ? 1 : 0;
+    const bool has_fast = mate::ssd_fast_supports(p);
+    if (d->algo == MATE_ALGO_FAST && !has_fast)
+        return fail(MATE_ERR_UNSUPPORTED, "no MFMA scan kernel for dtype %d headdim %d d_state %d chunk %d",
+                    (int)d->dtype, d->headdim, d->d_state, d->chunk);
+    fast = d->algo != MATE_ALGO_PORTABLE && has_fast;
+    return MATE_OK;
+}
+
+mate_status make_tesa_problem(mate_grid g, const mate_tesa_desc *d, mate::TesaProblem &p, bool &fast)
+{
+    if (!d) return fail(MATE_ERR_NULL, "tesa descriptor is NULL");
+    mate_status s = check_grid(g);
+    if (s != MATE_OK) return s;
+    if (d->nheads <= 0 || d->headdim <= 0) return fail(MATE_ERR_SHAPE, "nheads and headdim must be positive");
+    if (d->win_t <= 0 || d->win_h <= 0 || d->win_w <= 0) return fail(MATE_ERR_SHAPE, "window extents must be positive");
+    if (g.T % d->win_t || g.H % d->win_h || g.W % d->win_w)
+        return fail(MATE_ERR_SHAPE, "window %dx%dx%d does not divide the grid", d->win_t, d->win_h, d->win_w);
+    if (d->shift_t < 0 || d->shift_t >= d->win_t || d->shift_h < 0 || d->shift_h >= d->win_h || d->shift_w < 0 ||
+        d->shift_w >= d->win_w)
+        return fail(MATE_ERR_SHAPE, "shift (%d,%d,%d) outside [0, window)", d->shift_t, d->shift_h, d->shift_w);
+    if (!valid_dtype(d->dtype)) return fail(MATE_ERR_SHAPE, "unknown dtype %d", (int)d->dtype);
+    if (!valid_algo(d->algo)) return fail(MATE_ERR_SHAPE, "unknown algo %d", (int)d->algo);
+    if ((int64_t)d->nheads * g.batch * g.T * g.H * g.W >= kMaxTokens)
+        return fail(MATE_ERR_UNSUPPORTED, "batch*tokens*nheads must stay below 2^31");
+    p.batch = g.batch; p.T = g.T; p.H = g.H; p.W = g.W;
+    p.nheads = d->nheads; p.headdim = d->headdim;
+    p.wt = d->win_t; p.wh = d->win_h; p.ww = d->win_w;
+    p.st = d->shift_t; p.sh = d->shift_h; p.sw = d->shift_w;
+    p.nrt = (int)(g.T / d->win_t) + (d->shift_t ? 1 : 0);
+    p.nrh = (int)(g.H / d->win_h) + (d->shift_h ? 1 : 0);
+    p.nrw = (int)(g.W / d->win_w) + (d->shift_w ? 1 : 0);
+    p.scale = d->scale;
+    p.dtype = d->dtype == MATE_BF16 ? 1 : 0;
+    const bool has_fast = mate::tesa_fast_supports(p);
+    const bool has_portable = mate::tesa_portable_supports(p);
+    if (d->algo == MATE_ALGO_FAST && !has_fast)
+        return fail(MATE_ERR_UNSUPPORTED, "no MFMA TESA kernel for dtype %d headdim %d", (int)d->dtype, d->headdim);
+    if (d->algo == MATE_ALGO_PORTABLE && !has_portable)
+        return fail(MATE_ERR_UNSUPPORTED, "portable TESA needs headdim in {8,16,32,64,128} and <= 1024-token windows");
+    if (!has_fast && !has_portable)
+        return fail(MATE_ERR_UNSUPPORTED, "TESA not built for headdim %d with %dx%dx%d windows", d->headdim, d->win_t,
+                    d->win_h, d->win_w);
+    fast = d->algo != MATE_ALGO_PORTABLE && has_fast;
+    return MATE_OK;
+}
+
+size_t ssd_workspace(const mate::SsdProblem &p, bool fast)
+{
+    return fast ? mate::ssd_fast_workspace(p) : mate::ssd_portable_workspace(p);
+}
+
+mate_status check_ssd_tensors(const mate_ssd_tensors *t)
+{
+    if (!t) return fail(MATE_ERR_NULL, "ssd tensors struct is NULL");
+    if (!t->x || !t->b || !t->c || !t->dt || !t->a || !t->d || !t->y)
+        return fail(MATE_ERR_NULL, "an ssd tensor pointer (x, b, c, dt, a, d, y) is NULL");
+    return MATE_OK;
+}
+
+mate_status check_tesa_tensors(const mate_tesa_tensors *t)
+{
+    if (!t) return fail(MATE_ERR_NULL, "tesa tensors struct is NULL");
+    if (!t->q || !t->k || !t->v || !t->o) return fail(MATE_ERR_NULL, "a tesa tensor pointer (q, k, v, o) is NULL");
+    return MATE_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int mate_abi_version(void) { return MATE_ABI_VERSION; }
+
+const char *mate_status_string(mate_status s)
+{
+    switch (s) {
+    case MATE_OK: return "MATE_OK";
+    case MATE_ERR_NULL: return "MATE_ERR_NULL: a required pointer is NULL";
+    case MATE_ERR_SHAPE: return "MATE_ERR_SHAPE: invalid extents, order, window, shift, pool or chunk";
+    case MATE_ERR_UNSUPPORTED: return "MATE_ERR_UNSUPPORTED: valid for the method but not built";
+    case MATE_ERR_WORKSPACE: return "MATE_ERR_WORKSPACE: workspace missing or too small";
+    case MATE_ERR_DEVICE: return "MATE_ERR_DEVICE: a HIP call or kernel launch failed";
+    }
+    return "unknown mate_status";
+}
+
+const char *mate_last_error(void) { return g_err; }
+
+mate_status mate_rms_reorder(const void *src, void *dst, mate_grid g, int64_t row_bytes, int order, int flip,
+                             int inverse, void *stream)
+{
+    if (!src || !dst) return fail(MATE_ERR_NULL, "src or dst is NULL");
+    mate_status s = check_grid(g);
+    if (s != MATE_OK) return s;
+    if (row_bytes <= 0) return fail(MATE_ERR_SHAPE, "row_bytes %lld must be positive", (long long)row_bytes);
+    if (order < 0 || order > 3) return fail(MATE_ERR_SHAPE, "order %d not in 0..3", order);
+    const int64_t rows = g.batch * g.T * g.H * g.W;
+    if (row_bytes > ((int64_t)1 << 40) / rows) return fail(MATE_ERR_UNSUPPORTED, "tensor above 1 TiB");
+    const uintptr_t bytes = (uintptr_t)(rows * row_bytes);
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+    if (a < b + bytes && b < a + bytes) return fail(MATE_ERR_SHAPE, "src and dst overlap");
+    hipError_t e = mate::launch_rms_reorder(src, dst, g.batch, g.T, g.H, g.W, row_bytes, order, flip ? 1 : 0,
+                                            inverse ? 1 : 0, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "rms reorder launch");
+    return MATE_OK;
+}
+
+size_t mate_bissd_workspace_size(mate_grid g, const mate_ssd_desc *d)
+{
+    mate::SsdProblem p;
+    bool fast = false;
+    if (make_ssd_problem(g, 0, d, p, fast) != MATE_OK) return 0;
+    return ssd_workspace(p, fast);
+}
+
+mate_status mate_bissd_scan(const mate_ssd_tensors *t, mate_grid g, int order, const mate_ssd_desc *d,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    mate_status s = check_ssd_tensors(t);
+    if (s != MATE_OK) return s;
+    mate::SsdProblem p;
+    bool fast = false;
+    if ((s = make_ssd_problem(g, order, d, p, fast)) != MATE_OK) return s;
+    const size_t need = ssd_workspace(p, fast);
+    if (!workspace || workspace_bytes < need)
+        return fail(MATE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+    if ((uintptr_t)workspace & 255) return fail(MATE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if ((s = prepare_device()) != MATE_OK) return s;
+    mate::SsdArgs a{t->x, t->b, t->c, t->dt, t->a, t->d, t->y};
+    hipError_t e = fast ? mate::ssd_fast(p, a, workspace, (hipStream_t)stream)
+                        : mate::ssd_portable(p, a, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "bissd launch");
+    return MATE_OK;
+}
+
+mate_status mate_tesa(const mate_tesa_tensors *t, mate_grid g, const mate_tesa_desc *d, void *stream)
+{
+    mate_status s = check_tesa_tensors(t);
+    if (s != MATE_OK) return s;
+    mate::TesaProblem p;
+    bool fast = false;
+    if ((s = make_tesa_problem(g, d, p, fast)) != MATE_OK) return s;
+    if ((s = prepare_device()) != MATE_OK) return s;
+    mate::TesaArgs a{t->q, t->k, t->v, t->o};
+    hipError_t e = fast ? mate::tesa_fast(p, a, (hipStream_t)stream) : mate::tesa_portable(p, a, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "tesa launch");
+    return MATE_OK;
+}
+
+size_t mate_forward_workspace_size(mate_grid g, const mate_ssd_desc *sd, const mate_tesa_desc *td)
+{
+    mate::TesaProblem tp;
+    bool tf = false;
+    if (make_tesa_problem(g, td, tp, tf) != MATE_OK) return 0;
+    return mate_bissd_workspace_size(g, sd);
+}
+
+mate_status mate_forward(const mate_ssd_tensors *s, const mate_ssd_desc *sd, const mate_tesa_tensors *a,
+                         const mate_tesa_desc *td, mate_grid g, int order, void *workspace, size_t workspace_bytes,
+                         void *stream)
+{
+    // Validate everything before the first launch so that a rejected call writes nothing.
+    mate_status st = check_ssd_tensors(s);
+    if (st != MATE_OK) return st;
+    if ((st = check_tesa_tensors(a)) != MATE_OK) return st;
+    mate::SsdProblem sp;
+    mate::TesaProblem tp;
+    bool sfast = false, tfast = false;
+    if ((st = make_ssd_problem(g, order, sd, sp, sfast)) != MATE_OK) return st;
+    if ((st = make_tesa_problem(g, td, tp, tfast)) != MATE_OK) return st;
+    const size_t need = ssd_workspace(sp, sfast);
+    if (!workspace || workspace_bytes < need)
+        return fail(MATE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+    if ((uintptr_t)workspace & 255) return fail(MATE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if ((st = prepare_device()) != MATE_OK) return st;
+    const hipStream_t stream_h = (hipStream_t)stream;
+    mate::SsdArgs sa{s->x, s->b, s->c, s->dt, s->a, s->d, s->y};
+    mate::TesaArgs ta{a->q, a->k, a->v, a->o};
+    hipError_t e = sfast ? mate::ssd_fast(sp, sa, workspace, stream_h) : mate::ssd_portable(sp, sa, workspace, stream_h);
+    if (e != hipSuccess) return device_fail(e, "forward: bissd launch");
+    e = tfast ? mate::tesa_fast(tp, ta, stream_h) : mate::tesa_portable(tp, ta, stream_h);
+    if (e != hipSuccess) return device_fail(e, "forward: tesa launch");
+    return MATE_OK;
+}
+
+} // extern "C"

@@ -1,0 +1,450 @@
+// Portable chunked evaluation of the bidirectional Mamba2 scan (fp32 FMA, any
+// supported head size). It is the path for fp32 tensors and for shapes the
+// MFMA kernels are not built for.
+//
+// The recurrence h_u = exp(a_u) h_{u-1} + dt_u x_u B_u^T, y_u = h_u C_u + D x_u
+// (a_u = dt_u A) is evaluated in chunks of Q tokens (the Mamba2 "state space
+// duality" split that the xllm-io review of LinGen, section 三 item 1, refers
+// to). With cs_t the inclusive cumulative sum of a inside a chunk,
+// ce_t = cs_t - a_t and tot = cs_{Q-1}, the sum of both directions is
+//   y_t = sum_u (C_t . B_u) dt_u w(t,u) x_u                         (intra chunk)
+//       + exp(cs_t) Hf C_t + exp(tot - ce_t) Hb C_t                  (inter chunk)
+//       + 2 D x_t
+// with w = exp(cs_t - cs_u) below the diagonal, exp(ce_u - ce_t) above it and
+// 2 on it; Hf is the forward state entering the chunk from the left and Hb the
+// backward state entering it from the right. Chunk contributions to the states:
+//   Sf = sum_u exp(tot - cs_u) dt_u x_u B_u^T,  Sb = sum_u exp(ce_u) dt_u x_u B_u^T,
+// and across a chunk both states decay by exp(tot).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mate {
+
+namespace {
+
+constexpr int kMaxQ = 128;
+
+// Row index of scan position i: the RMS permutation for the main sequence, the
+// identity for the (already ordered) review sequence.
+template <bool PERM>
+__device__ __forceinline__ uint32_t seq_row(uint32_t i, int order, uint32_t T, uint32_t H, uint32_t W)
+{
+    return PERM ? rms_index32(i, order, T, H, W) : i;
+}
+
+// dt in scan order, one row per head, and its within-chunk inclusive cumsum of
+// dt * A. Positions >= L are zero (exact no-ops of the recurrence).
+// grid (nchunks, ceil(nheads / 64), batch), 256 threads.
+template <bool PERM>
+__global__ __launch_bounds__(256) void k_prep_dt(const float *__restrict__ dt, const float *__restrict__ A,
+                                                 float *__restrict__ dtT, float *__restrict__ csT, int nheads,
+                                                 uint32_t L, uint32_t Lpad, int Q, int order, uint32_t T,
+                                                 uint32_t H, uint32_t W)
+{
+    __shared__ float sdt[kMaxQ][65];
+    __shared__ float scs[kMaxQ][65];
+    const uint32_t c = blockIdx.x, b = blockIdx.z;
+    const int h0 = blockIdx.y * 64;
+    for (int k = threadIdx.x; k < Q * 64; k += 256) {
+        const int u = k >> 6, hh = k & 63, h = h0 + hh;
+        const uint32_t i = c * Q + u;
+        float v = 0.f;
+        if (i < L && h < nheads) v = dt[((size_t)b * L + seq_row<PERM>(i, order, T, H, W)) * nheads + h];
+        sdt[u][hh] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64 && h0 + (int)threadIdx.x < nheads) {
+        const float a = A[h0 + threadIdx.x];
+        float cs = 0.f;
+        for (int u = 0; u < Q; ++u) {
+            cs += sdt[u][threadIdx.x] * a;
+            scs[u][threadIdx.x] = cs;
+        }
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < Q * 64; k += 256) {
+        const int hh = k / Q, u = k - hh * Q, h = h0 + hh;
+        if (h >= nheads) continue;
+        const size_t o = ((size_t)b * nheads + h) * Lpad + (size_t)c * Q + u;
+        dtT[o] = sdt[u][hh];
+        csT[o] = scs[u][hh];
+    }
+}
+
+// Average pool over disjoint pt x ph x pw blocks; out[b][j][ch] with j in RMS
+// order `order` of the pooled grid. grid (ceil(C / 256), R, batch).
+template <typename E>
+__global__ __launch_bounds__(256) void k_pool(const E *__restrict__ src, float *__restrict__ out, int64_t C,
+                                              uint32_t Tn, uint32_t Hn, uint32_t Wn, int pt, int ph, int pw,
+                                              int order)
+{
+    const int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (ch >= C) return;
+    const uint32_t j = blockIdx.y, b = blockIdx.z, R = gridDim.y;
+    const uint32_t Tp = Tn / pt, Hp = Hn / ph, Wp = Wn / pw;
+    const uint32_t np = rms_index32(j, order, Tp, Hp, Wp);
+    const uint32_t tq = np / (Hp * Wp), hq = (np / Wp) % Hp, wq = np % Wp;
+    const size_t N = (size_t)Tn * Hn * Wn;
+    float acc = 0.f;
+    for (int dt_ = 0; dt_ < pt; ++dt_)
+        for (int dh = 0; dh < ph; ++dh)
+            for (int dw = 0; dw < pw; ++dw) {
+                const size_t n = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw + dw;
+                acc += elem<E>::load(src + ((size_t)b * N + n) * C + ch);
+            }
+    out[((size_t)b * R + j) * C + ch] = acc / (float)(pt * ph * pw);
+}
+
+// Per-chunk state contributions Sf, Sb (P x S, fp32) of one head.
+// grid (nchunks, nheads, batch), 256 threads. LDS: X (Q x P) and B (Q x S) in fp32.
+template <typename E, bool PERM>
+__global__ __launch_bounds__(256) void k_chunk_states(const E *__restrict__ x, const E *__restrict__ Bm,
+                                                      const float *__restrict__ dtT, const float *__restrict__ csT,
+                                                      const float *__restrict__ A, float *__restrict__ Sf,
+                                                      float *__restrict__ Sb, int nheads, int P, int S, int G,
+                                                      uint32_t L, uint32_t Lpad, int Q, int order, uint32_t T,
+                                                      uint32_t H, uint32_t W)
+{
+    extern __shared__ float smem[];
+    float *Xs = smem;                 // [Q][P]
+    float *Bs = Xs + Q * P;           // [Q][S]
+    float *wf = Bs + Q * S;           // [Q]
+    float *wb = wf + Q;               // [Q]
+    const uint32_t c = blockIdx.x, b = blockIdx.z;
+    const int h = blockIdx.y, g = h / (nheads / G);
+    const uint32_t nch = gridDim.x;
+    for (int k = threadIdx.x; k < Q * P; k += 256) {
+        const int u = k / P, p = k - u * P;
+        const uint32_t i = c * Q + u;
+        float v = 0.f;
+        if (i < L) v = elem<E>::load(x + (((size_t)b * L + seq_row<PERM>(i, order, T, H, W)) * nheads + h) * P + p);
+        Xs[k] = v;
+    }
+    for (int k = threadIdx.x; k < Q * S; k += 256) {
+        const int u = k / S, s = k - u * S;
+        const uint32_t i = c * Q + u;
+        float v = 0.f;
+        if (i < L) v = elem<E>::load(Bm + (((size_t)b * L + seq_row<PERM>(i, order, T, H, W)) * G + g) * S + s);
+        Bs[k] = v;
+    }
+    const size_t row = ((size_t)b * nheads + h) * Lpad + (size_t)c * Q;
+    const float a = A[h];
+    const float tot = csT[row + Q - 1];
+    for (int u = threadIdx.x; u < Q; u += 256) {
+        const float d = dtT[row + u], cs = csT[row + u];
+        wf[u] = d * __expf(tot - cs);
+        wb[u] = d * __expf(cs - d * a);
+    }
+    __syncthreads();
+    const int PS = P * S;
+    float *outf = Sf + (((size_t)b * nheads + h) * nch + c) * PS;
+    float *outb = Sb + (((size_t)b * nheads + h) * nch + c) * PS;
+    for (int e = threadIdx.x; e < PS; e += 256) {
+        const int p = e / S, s = e - p * S;
+        float af = 0.f, ab = 0.f;
+        for (int u = 0; u < Q; ++u) {
+            const float xb = Xs[u * P + p] * Bs[u * S + s];
+            af += xb * wf[u];
+            ab += xb * wb[u];
+        }
+        outf[e] = af;
+        outb[e] = ab;
+    }
+}
+
+// Turns chunk contributions into the states entering each chunk: Sf[c] becomes
+// the forward state after chunk c-1, Sb[c] the backward state after chunk c+1.
+// h0f / h0b (optional) are the initial states; finF / finB (optional) receive
+// the final states. grid (ceil(P*S / 256), nheads, batch).
+__global__ __launch_bounds__(256) void k_state_pass(float *__restrict__ Sf, float *__restrict__ Sb,
+                                                    const float *__restrict__ csT, const float *__restrict__ h0f,
+                                                    const float *__restrict__ h0b, float *__restrict__ finF,
+                                                    float *__restrict__ finB, int PS, int nch, int Q, uint32_t Lpad)
+{
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= PS) return;
+    const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+    const float *cs = csT + bh * Lpad;
+    float *f = Sf + bh * nch * PS + e;
+    float *bk = Sb + bh * nch * PS + e;
+    float run = h0f ? h0f[bh * PS + e] : 0.f;
+    for (int c = 0; c < nch; ++c) {
+        const float tot = cs[(size_t)c * Q + Q - 1];
+        const float s = f[(size_t)c * PS];
+        f[(size_t)c * PS] = run;
+        run = __expf(tot) * run + s;
+    }
+    if (finF) finF[bh * PS + e] = run;
+    run = h0b ? h0b[bh * PS + e] : 0.f;
+    for (int c = nch - 1; c >= 0; --c) {
+        const float tot = cs[(size_t)c * Q + Q - 1];
+        const float s = bk[(size_t)c * PS];
+        bk[(size_t)c * PS] = run;
+        run = __expf(tot) * run + s;
+    }
+    if (finB) finB[bh * PS + e] = run;
+}
+
+// CB[t][u] = C_t . B_u for every chunk and group. grid (nchunks, G, batch).
+template <typename E>
+__global__ __launch_bounds__(256) void k_cb(const E *__restrict__ Bm, const E *__restrict__ Cm,
+                                            float *__restrict__ CB, int G, int S, uint32_t L, int Q, int order,
+                                            uint32_t T_, uint32_t H, uint32_t W)
+{
+    __shared__ float Bs[kMaxQ][33];
+    __shared__ float Cs[kMaxQ][33];
+    const uint32_t c = blockIdx.x, b = blockIdx.z;
+    const int g = blockIdx.y;
+    const int QQ = Q * Q;
+    float acc[kMaxQ * kMaxQ / 256];
+#pragma unroll
+    for (int k = 0; k < kMaxQ * kMaxQ / 256; ++k) acc[k] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 32) {
+        __syncthreads();
+        for (int k = threadIdx.x; k < Q * 32; k += 256) {
+            const int u = k >> 5, s = k & 31;
+            const uint32_t i = c * Q + u;
+            float bv = 0.f, cv = 0.f;
+            if (i < L && s0 + s < S) {
+                const size_t off = (((size_t)b * L + rms_index32(i, order, T_, H, W)) * G + g) * S + s0 + s;
+                bv = elem<E>::load(Bm + off);
+                cv = elem<E>::load(Cm + off);
+            }
+            Bs[u][s] = bv;
+            Cs[u][s] = cv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMaxQ * kMaxQ / 256; ++k) {
+            const int e = threadIdx.x + 256 * k;
+            if (e < QQ) {
+                const int t = e / Q, u = e - t * Q;
+                float a = 0.f;
+                for (int s = 0; s < 32; ++s) a += Cs[t][s] * Bs[u][s];
+                acc[k] += a;
+            }
+        }
+    }
+    float *out = CB + (((size_t)b * G + g) * gridDim.x + c) * QQ;
+#pragma unroll
+    for (int k = 0; k < kMaxQ * kMaxQ / 256; ++k) {
+        const int e = threadIdx.x + 256 * k;
+        if (e < QQ) out[e] = acc[k];
+    }
+}
+
+// Outputs of one chunk and head; Sf / Sb hold the entering states.
+// grid (nchunks, nheads, batch), 256 threads.
+template <typename E>
+__global__ __launch_bounds__(256) void k_output(const E *__restrict__ x, const E *__restrict__ Cm,
+                                                const float *__restrict__ CB, const float *__restrict__ dtT,
+                                                const float *__restrict__ csT, const float *__restrict__ A,
+                                                const float *__restrict__ Dv, const float *__restrict__ Hf,
+                                                const float *__restrict__ Hb, E *__restrict__ y, int nheads, int P,
+                                                int S, int G, uint32_t N, uint32_t Lpad, int Q, int order,
+                                                uint32_t T_, uint32_t H, uint32_t W)
+{
+    constexpr int kMaxOut = kMaxQ * 128 / 256;  // Q * P / 256 outputs per thread at most
+    __shared__ float sm[kMaxQ * (kMaxQ + 1) + kMaxQ * 129];
+    __shared__ float s_dt[kMaxQ], s_cs[kMaxQ];
+    const uint32_t c = blockIdx.x, b = blockIdx.z, nch = gridDim.x;
+    const int h = blockIdx.y, g = h / (nheads / G);
+    const int QP = Q * P, PS = P * S;
+    const size_t row = ((size_t)b * nheads + h) * Lpad + (size_t)c * Q;
+    const float a = A[h];
+    const float tot = csT[row + Q - 1];
+    for (int u = threadIdx.x; u < Q; u += 256) {
+        s_dt[u] = dtT[row + u];
+        s_cs[u] = csT[row + u];
+    }
+    const float *hf = Hf + (((size_t)b * nheads + h) * nch + c) * PS;
+    const float *hb = Hb + (((size_t)b * nheads + h) * nch + c) * PS;
+
+    // Phase 1: inter-chunk terms. LDS: Hf, Hb (P x 33) and C (Q x 33) per 32-wide slice of S.
+    float *sHf = sm, *sHb = sm + P * 33, *sC = sm + 2 * P * 33;
+    float accf[kMaxOut], accb[kMaxOut];
+#pragma unroll
+    for (int k = 0; k < kMaxOut; ++k) accf[k] = accb[k] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 32) {
+        __syncthreads();
+        for (int k = threadIdx.x; k < P * 32; k += 256) {
+            const int p = k >> 5, s = k & 31;
+            const bool ok = s0 + s < S;
+            sHf[p * 33 + s] = ok ? hf[p * S + s0 + s] : 0.f;
+            sHb[p * 33 + s] = ok ? hb[p * S + s0 + s] : 0.f;
+        }
+        for (int k = threadIdx.x; k < Q * 32; k += 256) {
+            const int u = k >> 5, s = k & 31;
+            const uint32_t i = c * Q + u;
+            float v = 0.f;
+            if (i < N && s0 + s < S)
+                v = elem<E>::load(Cm + (((size_t)b * N + rms_index32(i, order, T_, H, W)) * G + g) * S + s0 + s);
+            sC[u * 33 + s] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMaxOut; ++k) {
+            const int e = threadIdx.x + 256 * k;
+            if (e < QP) {
+                const int t = e / P, p = e - t * P;
+                float af = 0.f, ab = 0.f;
+                for (int s = 0; s < 32; ++s) {
+                    const float cv = sC[t * 33 + s];
+                    af += sHf[p * 33 + s] * cv;
+                    ab += sHb[p * 33 + s] * cv;
+                }
+                accf[k] += af;
+                accb[k] += ab;
+            }
+        }
+    }
+    __syncthreads();
+
+    // Phase 2: intra-chunk term. LDS: weighted CB (Q x Q+1) and X (Q x P+1).
+    float *sM = sm, *sX = sm + Q * (Q + 1);
+    const float *cb = CB + (((size_t)b * G + g) * nch + c) * Q * Q;
+    for (int k = threadIdx.x; k < Q * Q; k += 256) {
+        const int t = k / Q, u = k - t * Q;
+        float w;
+        if (u < t)
+            w = __expf(s_cs[t] - s_cs[u]);
+        else if (u > t)
+            w = __expf((s_cs[u] - s_dt[u] * a) - (s_cs[t] - s_dt[t] * a));
+        else
+            w = 2.f;
+        sM[t * (Q + 1) + u] = cb[k] * s_dt[u] * w;
+    }
+    for (int k = threadIdx.x; k < Q * P; k += 256) {
+        const int u = k / P, p = k - u * P;
+        const uint32_t i = c * Q + u;
+        float v = 0.f;
+        if (i < N) v = elem<E>::load(x + (((size_t)b * N + rms_index32(i, order, T_, H, W)) * nheads + h) * P + p);
+        sX[u * (P + 1) + p] = v;
+    }
+    __syncthreads();
+    const float two_d = 2.f * Dv[h];
+#pragma unroll
+    for (int k = 0; k < kMaxOut; ++k) {
+        const int e = threadIdx.x + 256 * k;
+        if (e < QP) {
+            const int t = e / P, p = e - t * P;
+            const uint32_t i = c * Q + t;
+            float acc = __expf(s_cs[t]) * accf[k] + __expf(tot - (s_cs[t] - s_dt[t] * a)) * accb[k];
+            for (int u = 0; u < Q; ++u) acc += sM[t * (Q + 1) + u] * sX[u * (P + 1) + p];
+            acc += two_d * sX[t * (P + 1) + p];
+            if (i < N)
+                elem<E>::store(y + (((size_t)b * N + rms_index32(i, order, T_, H, W)) * nheads + h) * P + p, acc);
+        }
+    }
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+} // namespace
+
+// Workspace carve-up of the portable path (all fp32):
+//   dtT, csT      [batch][nheads][Lpad]            main sequence
+//   Sf, Sb        [batch][nheads][nch][P][S]       chunk states, then entering states
+//   CB            [batch][G][nch][Q][Q]
+//   review only:  rx [batch][R][nheads][P], rB [batch][R][G][S], rdt [batch][R][nheads],
+//                 rdtT, rcsT [batch][nheads][Rpad], rSf, rSb [batch][nheads][nchR][P][S],
+//                 h0f, h0b [batch][nheads][P][S]
+struct PortableLayout {
+    size_t dtT, csT, Sf, Sb, CB, rx, rB, rdt, rdtT, rcsT, rSf, rSb, h0f, h0b, total;
+};
+
+static PortableLayout portable_layout(const SsdProblem &p)
+{
+    PortableLayout l{};
+    const size_t B = p.batch, Hs = p.nheads, PS = (size_t)p.headdim * p.d_state;
+    const size_t Lpad = (size_t)p.nch * p.chunk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    l.dtT = take(B * Hs * Lpad * 4);
+    l.csT = take(B * Hs * Lpad * 4);
+    l.Sf = take(B * Hs * p.nch * PS * 4);
+    l.Sb = take(B * Hs * p.nch * PS * 4);
+    l.CB = take(B * p.ngroups * p.nch * (size_t)p.chunk * p.chunk * 4);
+    if (p.R > 0) {
+        const size_t Rpad = (size_t)p.nchR * p.chunk;
+        l.rx = take(B * p.R * Hs * p.headdim * 4);
+        l.rB = take(B * p.R * p.ngroups * p.d_state * 4);
+        l.rdt = take(B * p.R * Hs * 4);
+        l.rdtT = take(B * Hs * Rpad * 4);
+        l.rcsT = take(B * Hs * Rpad * 4);
+        l.rSf = take(B * Hs * p.nchR * PS * 4);
+        l.rSb = take(B * Hs * p.nchR * PS * 4);
+        l.h0f = take(B * Hs * PS * 4);
+        l.h0b = take(B * Hs * PS * 4);
+    }
+    l.total = off;
+    return l;
+}
+
+size_t ssd_portable_workspace(const SsdProblem &p) { return portable_layout(p).total; }
+
+template <typename E>
+static hipError_t run_portable(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
+{
+    const PortableLayout l = portable_layout(p);
+    char *w = (char *)ws;
+    float *dtT = (float *)(w + l.dtT), *csT = (float *)(w + l.csT);
+    float *Sf = (float *)(w + l.Sf), *Sb = (float *)(w + l.Sb), *CB = (float *)(w + l.CB);
+    const int Hs = p.nheads, P = p.headdim, S = p.d_state, G = p.ngroups, Q = p.chunk;
+    const uint32_t N = (uint32_t)p.N, Lpad = (uint32_t)(p.nch * Q);
+    const uint32_t T = (uint32_t)p.T, H = (uint32_t)p.H, W = (uint32_t)p.W;
+    const int B = (int)p.batch;
+    const E *x = (const E *)a.x, *Bm = (const E *)a.b, *Cm = (const E *)a.c;
+    const size_t states_lds = ((size_t)Q * P + (size_t)Q * S + 2 * Q) * 4;
+    hipError_t e;
+
+    float *h0f = nullptr, *h0b = nullptr;
+    if (p.R > 0) {
+        float *rx = (float *)(w + l.rx), *rB = (float *)(w + l.rB), *rdt = (float *)(w + l.rdt);
+        float *rdtT = (float *)(w + l.rdtT), *rcsT = (float *)(w + l.rcsT);
+        float *rSf = (float *)(w + l.rSf), *rSb = (float *)(w + l.rSb);
+        h0f = (float *)(w + l.h0f);
+        h0b = (float *)(w + l.h0b);
+        const uint32_t R = (uint32_t)p.R, Rpad = (uint32_t)(p.nchR * Q);
+        const int64_t Cx = (int64_t)Hs * P, Cb = (int64_t)G * S;
+        k_pool<E><<<dim3((Cx + 255) / 256, R, B), 256, 0, st>>>(x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        k_pool<E><<<dim3((Cb + 255) / 256, R, B), 256, 0, st>>>(Bm, rB, Cb, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        k_pool<float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, B), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1, R);
+        k_chunk_states<float, false><<<dim3(p.nchR, Hs, B), 256, states_lds, st>>>(
+            rx, rB, rdtT, rcsT, a.a, rSf, rSb, Hs, P, S, G, R, Rpad, Q, 0, 1, 1, R);
+        k_state_pass<<<dim3((P * S + 255) / 256, Hs, B), 256, 0, st>>>(rSf, rSb, rcsT, nullptr, nullptr, h0f, h0b,
+                                                                      P * S, p.nchR, Q, Rpad);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, B), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q, p.order, T, H, W);
+    k_chunk_states<E, true><<<dim3(p.nch, Hs, B), 256, states_lds, st>>>(x, Bm, dtT, csT, a.a, Sf, Sb, Hs, P, S, G, N,
+                                                                         Lpad, Q, p.order, T, H, W);
+    k_state_pass<<<dim3((P * S + 255) / 256, Hs, B), 256, 0, st>>>(Sf, Sb, csT, h0f, h0b, nullptr, nullptr, P * S,
+                                                                  p.nch, Q, Lpad);
+    k_cb<E><<<dim3(p.nch, G, B), 256, 0, st>>>(Bm, Cm, CB, G, S, N, Q, p.order, T, H, W);
+    k_output<E><<<dim3(p.nch, Hs, B), 256, 0, st>>>(x, Cm, CB, dtT, csT, a.a, a.d, Sf, Sb, (E *)a.y, Hs, P, S, G, N,
+                                                    Lpad, Q, p.order, T, H, W);
+    return hipGetLastError();
+}
+
+hipError_t ssd_portable(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
+{
+    if (p.dtype == 0) return run_portable<float>(p, a, ws, st);
+    return run_portable<bf16_t>(p, a, ws, st);
+}
+
+hipError_t ssd_portable_prepare()
+{
+    // The state kernel may take more than 64 KB of dynamic LDS.
+    const int lds = 160 * 1024;
+    hipError_t e;
+    if ((e = hipFuncSetAttribute((const void *)k_chunk_states<float, false>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)k_chunk_states<float, true>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
+    return hipFuncSetAttribute((const void *)k_chunk_states<bf16_t, true>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+}
+
+} // namespace mate

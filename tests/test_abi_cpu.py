@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/mate.h
+declares, and rejects bad arguments before touching a device (no GPU needed:
+every call here fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_complexity_video_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mate.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libmate.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mate_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(B.EXPORTED) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+    lib = B.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name)
+    assert lib.mate_abi_version() == 1
+
+
+def test_status_strings():
+    lib = B.lib()
+    for s in range(6):
+        assert lib.mate_status_string(s).decode().startswith("MATE_")
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+
+
+def test_rms_validation():
+    lib = B.lib()
+    g = B.Grid(1, 2, 2, 2)
+    assert lib.mate_rms_reorder(None, FAKE, g, 16, 0, 0, 0, None) == B.MATE_ERR_NULL
+    assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), g, 16, 4, 0, 0, None) == B.MATE_ERR_SHAPE
+    assert "order" in lib.mate_last_error().decode()
+    assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), B.Grid(1, 0, 2, 2), 16, 0, 0, 0, None) == B.MATE_ERR_SHAPE
+    assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), g, 0, 0, 0, 0, None) == B.MATE_ERR_SHAPE
+    # overlapping buffers
+    assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x100010), g, 16, 0, 0, 0, None) == B.MATE_ERR_SHAPE
+    assert "overlap" in lib.mate_last_error().decode()
+    # more than 2^31 tokens
+    assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), B.Grid(1, 2048, 2048, 1024), 2, 0, 0, 0,
+                                None) == B.MATE_ERR_UNSUPPORTED
+
+
+def _ssd(**kw):
+    d = dict(nheads=2, headdim=16, d_state=8, ngroups=1, chunk=8, pool_t=0, pool_h=0, pool_w=0,
+             dtype=B.MATE_F32, algo=B.ALGO_AUTO)
+    d.update(kw)
+    return B.SsdDesc(**d)
+
+
+def _ssd_t(**kw):
+    d = {k: 0x100000 + 0x1000 * i for i, k in enumerate(("x", "b", "c", "dt", "a", "d", "y"))}
+    d.update(kw)
+    return B.SsdTensors(**d)
+
+
+def _scan(t, g, order, desc, ws=0x800000, wsb=1 << 40):
+    return B.lib().mate_bissd_scan(ctypes.byref(t), g, order, ctypes.byref(desc), ctypes.c_void_p(ws), wsb, None)
+
+
+def test_ssd_validation():
+    g = B.Grid(1, 2, 4, 4)
+    assert _scan(_ssd_t(y=0), g, 0, _ssd()) == B.MATE_ERR_NULL
+    assert _scan(_ssd_t(), g, 5, _ssd()) == B.MATE_ERR_SHAPE
+    assert _scan(_ssd_t(), g, 0, _ssd(chunk=0)) == B.MATE_ERR_SHAPE
+    assert _scan(_ssd_t(), g, 0, _ssd(nheads=3, ngroups=2)) == B.MATE_ERR_SHAPE
+    assert _scan(_ssd_t(), g, 0, _ssd(pool_t=2, pool_h=3, pool_w=2)) == B.MATE_ERR_SHAPE   # 3 does not divide 4
+    assert _scan(_ssd_t(), g, 0, _ssd(pool_t=2, pool_h=0, pool_w=2)) == B.MATE_ERR_SHAPE
+    assert _scan(_ssd_t(), g, 0, _ssd(headdim=256)) == B.MATE_ERR_UNSUPPORTED
+    assert _scan(_ssd_t(), g, 0, _ssd(chunk=256)) == B.MATE_ERR_UNSUPPORTED
+    assert _scan(_ssd_t(), g, 0, _ssd(dtype=7)) == B.MATE_ERR_SHAPE
+    # fp32 has no MFMA kernel
+    assert _scan(_ssd_t(), g, 0, _ssd(algo=B.ALGO_FAST)) == B.MATE_ERR_UNSUPPORTED
+    # workspace too small, NULL, or misaligned
+    assert _scan(_ssd_t(), g, 0, _ssd(), wsb=16) == B.MATE_ERR_WORKSPACE
+    assert _scan(_ssd_t(), g, 0, _ssd(), ws=0) == B.MATE_ERR_WORKSPACE
+    assert _scan(_ssd_t(), g, 0, _ssd(), ws=0x800010) == B.MATE_ERR_WORKSPACE
+
+
+def test_ssd_workspace_size_is_positive_and_grows():
+    lib = B.lib()
+    small = lib.mate_bissd_workspace_size(B.Grid(1, 2, 4, 4), ctypes.byref(_ssd()))
+    big = lib.mate_bissd_workspace_size(B.Grid(1, 4, 4, 4), ctypes.byref(_ssd()))
+    pooled = lib.mate_bissd_workspace_size(B.Grid(1, 2, 4, 4), ctypes.byref(_ssd(pool_t=2, pool_h=2, pool_w=2)))
+    assert 0 < small < big and small < pooled
+    assert lib.mate_bissd_workspace_size(B.Grid(1, 2, 4, 4), ctypes.byref(_ssd(chunk=0))) == 0
+
+
+def _tesa(**kw):
+    d = dict(nheads=2, headdim=16, win_t=2, win_h=2, win_w=2, shift_t=0, shift_h=0, shift_w=0, scale=0.0,
+             dtype=B.MATE_F32, algo=B.ALGO_AUTO)
+    d.update(kw)
+    return B.TesaDesc(**d)
+
+
+def _att(t, g, desc):
+    return B.lib().mate_tesa(ctypes.byref(t), g, ctypes.byref(desc), None)
+
+
+def test_tesa_validation():
+    g = B.Grid(1, 2, 4, 4)
+    t = B.TesaTensors(0x100000, 0x200000, 0x300000, 0x400000)
+    assert _att(B.TesaTensors(0x100000, 0, 0x300000, 0x400000), g, _tesa()) == B.MATE_ERR_NULL
+    assert _att(t, g, _tesa(win_h=3)) == B.MATE_ERR_SHAPE
+    assert _att(t, g, _tesa(shift_t=2)) == B.MATE_ERR_SHAPE
+    assert _att(t, g, _tesa(shift_w=-1)) == B.MATE_ERR_SHAPE
+    assert _att(t, g, _tesa(headdim=12)) == B.MATE_ERR_UNSUPPORTED
+    assert _att(t, g, _tesa(algo=B.ALGO_FAST)) == B.MATE_ERR_UNSUPPORTED
+    assert B.lib().mate_tesa(None, g, ctypes.byref(_tesa()), None) == B.MATE_ERR_NULL
+
+
+def test_forward_validation_rejects_before_launch():
+    lib = B.lib()
+    g = B.Grid(1, 2, 4, 4)
+    st, sd = _ssd_t(), _ssd()
+    tt, td = B.TesaTensors(0x100000, 0x200000, 0x300000, 0x400000), _tesa(win_t=3)
+    rc = lib.mate_forward(ctypes.byref(st), ctypes.byref(sd), ctypes.byref(tt), ctypes.byref(td), g, 0,
+                          ctypes.c_void_p(0x800000), 1 << 40, None)
+    assert rc == B.MATE_ERR_SHAPE
+    assert lib.mate_forward_workspace_size(g, ctypes.byref(sd), ctypes.byref(td)) == 0
