@@ -17,83 +17,17 @@
 // and across a chunk both states decay by exp(tot).
 #include "common.hpp"
 #include "launch.hpp"
+#include "ssd_common.hpp"
 
 namespace mate {
 
 namespace {
 
-constexpr int kMaxQ = 128;
+using ssd::kMaxQ;
+using ssd::k_pool;
+using ssd::k_prep_dt;
+using ssd::seq_row;
 
-// Row index of scan position i: the RMS permutation for the main sequence, the
-// identity for the (already ordered) review sequence.
-template <bool PERM>
-__device__ __forceinline__ uint32_t seq_row(uint32_t i, int order, uint32_t T, uint32_t H, uint32_t W)
-{
-    return PERM ? rms_index32(i, order, T, H, W) : i;
-}
-
-// dt in scan order, one row per head, and its within-chunk inclusive cumsum of
-// dt * A. Positions >= L are zero (exact no-ops of the recurrence).
-// grid (nchunks, ceil(nheads / 64), batch), 256 threads.
-template <bool PERM>
-__global__ __launch_bounds__(256) void k_prep_dt(const float *__restrict__ dt, const float *__restrict__ A,
-                                                 float *__restrict__ dtT, float *__restrict__ csT, int nheads,
-                                                 uint32_t L, uint32_t Lpad, int Q, int order, uint32_t T,
-                                                 uint32_t H, uint32_t W)
-{
-    __shared__ float sdt[kMaxQ][65];
-    __shared__ float scs[kMaxQ][65];
-    const uint32_t c = blockIdx.x, b = blockIdx.z;
-    const int h0 = blockIdx.y * 64;
-    for (int k = threadIdx.x; k < Q * 64; k += 256) {
-        const int u = k >> 6, hh = k & 63, h = h0 + hh;
-        const uint32_t i = c * Q + u;
-        float v = 0.f;
-        if (i < L && h < nheads) v = dt[((size_t)b * L + seq_row<PERM>(i, order, T, H, W)) * nheads + h];
-        sdt[u][hh] = v;
-    }
-    __syncthreads();
-    if (threadIdx.x < 64 && h0 + (int)threadIdx.x < nheads) {
-        const float a = A[h0 + threadIdx.x];
-        float cs = 0.f;
-        for (int u = 0; u < Q; ++u) {
-            cs += sdt[u][threadIdx.x] * a;
-            scs[u][threadIdx.x] = cs;
-        }
-    }
-    __syncthreads();
-    for (int k = threadIdx.x; k < Q * 64; k += 256) {
-        const int hh = k / Q, u = k - hh * Q, h = h0 + hh;
-        if (h >= nheads) continue;
-        const size_t o = ((size_t)b * nheads + h) * Lpad + (size_t)c * Q + u;
-        dtT[o] = sdt[u][hh];
-        csT[o] = scs[u][hh];
-    }
-}
-
-// Average pool over disjoint pt x ph x pw blocks; out[b][j][ch] with j in RMS
-// order `order` of the pooled grid. grid (ceil(C / 256), R, batch).
-template <typename E>
-__global__ __launch_bounds__(256) void k_pool(const E *__restrict__ src, float *__restrict__ out, int64_t C,
-                                              uint32_t Tn, uint32_t Hn, uint32_t Wn, int pt, int ph, int pw,
-                                              int order)
-{
-    const int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (ch >= C) return;
-    const uint32_t j = blockIdx.y, b = blockIdx.z, R = gridDim.y;
-    const uint32_t Tp = Tn / pt, Hp = Hn / ph, Wp = Wn / pw;
-    const uint32_t np = rms_index32(j, order, Tp, Hp, Wp);
-    const uint32_t tq = np / (Hp * Wp), hq = (np / Wp) % Hp, wq = np % Wp;
-    const size_t N = (size_t)Tn * Hn * Wn;
-    float acc = 0.f;
-    for (int dt_ = 0; dt_ < pt; ++dt_)
-        for (int dh = 0; dh < ph; ++dh)
-            for (int dw = 0; dw < pw; ++dw) {
-                const size_t n = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw + dw;
-                acc += elem<E>::load(src + ((size_t)b * N + n) * C + ch);
-            }
-    out[((size_t)b * R + j) * C + ch] = acc / (float)(pt * ph * pw);
-}
 
 // Per-chunk state contributions Sf, Sb (P x S, fp32) of one head.
 // grid (nchunks, nheads, batch), 256 threads. LDS: X (Q x P) and B (Q x S) in fp32.
@@ -407,9 +341,9 @@ static hipError_t run_portable(const SsdProblem &p, const SsdArgs &a, void *ws, 
         h0b = (float *)(w + l.h0b);
         const uint32_t R = (uint32_t)p.R, Rpad = (uint32_t)(p.nchR * Q);
         const int64_t Cx = (int64_t)Hs * P, Cb = (int64_t)G * S;
-        k_pool<E><<<dim3((Cx + 255) / 256, R, B), 256, 0, st>>>(x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
-        k_pool<E><<<dim3((Cb + 255) / 256, R, B), 256, 0, st>>>(Bm, rB, Cb, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
-        k_pool<float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        k_pool<E, float><<<dim3((Cx + 255) / 256, R, B), 256, 0, st>>>(x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        k_pool<E, float><<<dim3((Cb + 255) / 256, R, B), 256, 0, st>>>(Bm, rB, Cb, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        k_pool<float, float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
         k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, B), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1, R);
         k_chunk_states<float, false><<<dim3(p.nchR, Hs, B), 256, states_lds, st>>>(
             rx, rB, rdtT, rcsT, a.a, rSf, rSb, Hs, P, S, G, R, Rpad, Q, 0, 1, 1, R);

@@ -1,7 +1,267 @@
-// MFMA path of TESA (not built yet: every shape uses the portable kernel).
+// TESA on bf16 MFMA (gfx950, v_mfma_f32_32x32x16_bf16), flash-style inside
+// each (shifted) 3D window.
+//
+// Work item = (window, head, block of 256 queries); a workgroup of 8 waves
+// owns one item, each wave 32 queries. Keys and values stream through LDS in
+// tiles of 64 (double buffered, V stored transposed). Per tile each wave
+// computes S^T = K Q^T, so that a lane holds one query's scores and the
+// softmax needs only one cross-lane exchange; exp'd P^T is then directly the
+// B operand of O^T += V^T P^T, and O^T again has one query per lane, so the
+// online-softmax rescale is a per-lane multiply. Consecutive block ids are
+// spread over the 8 XCDs; they are remapped so that the query blocks of one
+// window land on the same XCD and share its K/V in L2.
+#include "common.hpp"
 #include "launch.hpp"
 
 namespace mate {
-bool tesa_fast_supports(const TesaProblem &) { return false; }
-hipError_t tesa_fast(const TesaProblem &, const TesaArgs &, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int KT = 64;            // keys per LDS tile
+constexpr int QW = 32;            // queries per wave
+constexpr int NWAVE = 8;          // waves per workgroup
+constexpr int QB = QW * NWAVE;    // queries per workgroup
+constexpr int KPAD = 8;           // K tile row padding (bf16)
+constexpr int VPAD = 4;           // V^T tile row padding (bf16)
+
+__device__ __forceinline__ void region_extent(int r, int D, int w, int s, int &lo, int &hi)
+{
+    if (s == 0) {
+        lo = r * w;
+        hi = lo + w;
+    } else if (r == 0) {
+        lo = 0;
+        hi = s;
+    } else {
+        lo = s + (r - 1) * w;
+        hi = lo + w;
+    }
+    if (hi > D) hi = D;
+}
+
+template <int DH>
+struct Smem {
+    __bf16 k[2][KT][DH + KPAD];
+    __bf16 vt[2][DH][KT + VPAD];
+};
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int DH>
+__global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
+                                                   const __bf16 *__restrict__ v, __bf16 *__restrict__ o,
+                                                   int nheads, int Tn, int Hn, int Wn, int wt, int wh, int ww,
+                                                   int st, int sh, int sw, int nrt, int nrh, int nrw, int nqb,
+                                                   uint32_t total, float c_log2)
+{
+    __shared__ Smem<DH> sm;
+    constexpr int DC = DH / 8;  // 16-byte chunks per row
+
+    // XCD-aware item index: block L runs on XCD L % 8; items w, w+1, ... of one
+    // XCD are consecutive query blocks / windows.
+    const uint32_t per_xcd = gridDim.x / 8;
+    const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (item >= total) return;
+    const int qb = item % nqb;
+    const uint32_t rest = item / nqb;
+    const int nreg = nrt * nrh * nrw;
+    const int r = rest % nreg;
+    const int bh = rest / nreg;
+    const int h = bh % nheads, b = bh / nheads;
+    const int rw = r % nrw, rh = (r / nrw) % nrh, rt = r / (nrw * nrh);
+    int t0, t1, h0, h1, w0, w1;
+    region_extent(rt, Tn, wt, st, t0, t1);
+    region_extent(rh, Hn, wh, sh, h0, h1);
+    region_extent(rw, Wn, ww, sw, w0, w1);
+    const int nt = t1 - t0, nh_ = h1 - h0, nw_ = w1 - w0, m = nt * nh_ * nw_;
+    const int q_base = qb * QB;
+    if (q_base >= m) return;  // uniform over the workgroup
+
+    const size_t N = (size_t)Tn * Hn * Wn;
+    const size_t rowstride = (size_t)nheads * DH;
+    const size_t head_off = ((size_t)b * N) * rowstride + (size_t)h * DH;
+    auto token = [&](int l) -> size_t {
+        const int lw = l % nw_, lh = (l / nw_) % nh_, lt = l / (nw_ * nh_);
+        return ((size_t)(t0 + lt) * Hn + (h0 + lh)) * Wn + (w0 + lw);
+    };
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const int qi = q_base + wave * QW + col;
+    const bool qvalid = qi < m;
+    const bool wave_active = q_base + wave * QW < m;
+
+    // Q^T fragments (B operand of S^T = K Q^T): query col, d = 16 kb + 8 half + 0..7.
+    bf16x8 qf[DH / 16];
+    {
+        const __bf16 *qrow = q + head_off + token(qvalid ? qi : 0) * rowstride;
+#pragma unroll
+        for (int kb = 0; kb < DH / 16; ++kb) {
+            u32x4 raw = qvalid ? *(const u32x4 *)(qrow + 16 * kb + 8 * half) : u32x4{0, 0, 0, 0};
+            qf[kb] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+
+    f32x16 acc[DH / 32];
+#pragma unroll
+    for (int i = 0; i < DH / 32; ++i) acc[i] = f32x16{};
+    float mrun = -INFINITY, lrun = 0.f;
+    const int ntiles = (m + KT - 1) / KT;
+
+    // Tile loaders: K rows as 16-byte chunks; V as key pairs packed into dwords of V^T.
+    constexpr int KCH = KT * DC;                  // K chunks per tile
+    constexpr int KPER = (KCH + 511) / 512;       // per thread
+    constexpr int VPAIRS = KT / 2 * DC;           // (key pair, chunk) units per tile
+    u32x4 kreg[KPER];
+    u32x4 vreg0, vreg1;
+    auto fetch = [&](int kt) {
+#pragma unroll
+        for (int it = 0; it < KPER; ++it) {
+            const int c = tid + 512 * it;
+            const int jj = c / DC, dc = c % DC;
+            const int kidx = kt * KT + jj;
+            kreg[it] = (c < KCH && kidx < m) ? *(const u32x4 *)(k + head_off + token(kidx) * rowstride + 8 * dc)
+                                             : u32x4{0, 0, 0, 0};
+        }
+        if (tid < VPAIRS) {
+            const int kp = tid % 32, dc = tid / 32;
+            const int k0 = kt * KT + 2 * kp;
+            vreg0 = k0 < m ? *(const u32x4 *)(v + head_off + token(k0) * rowstride + 8 * dc) : u32x4{0, 0, 0, 0};
+            vreg1 = k0 + 1 < m ? *(const u32x4 *)(v + head_off + token(k0 + 1) * rowstride + 8 * dc)
+                               : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < KPER; ++it) {
+            const int c = tid + 512 * it;
+            if (c < KCH) *(u32x4 *)&sm.k[buf][c / DC][8 * (c % DC)] = kreg[it];
+        }
+        if (tid < VPAIRS) {
+            const int kp = tid % 32, dc = tid / 32;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t a0 = vreg0[e], a1 = vreg1[e];
+                // element 2e and 2e+1 of each key's chunk
+                *(uint32_t *)&sm.vt[buf][8 * dc + 2 * e][2 * kp] = (a0 & 0xffffu) | (a1 << 16);
+                *(uint32_t *)&sm.vt[buf][8 * dc + 2 * e + 1][2 * kp] = (a0 >> 16) | (a1 & 0xffff0000u);
+            }
+        }
+    };
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < ntiles) fetch(kt + 1);
+        if (wave_active) {
+            f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int kb = 0; kb < DH / 16; ++kb) {
+                    const bf16x8 a = *(const bf16x8 *)&sm.k[cur][32 * sub + col][16 * kb + 8 * half];
+                    s[sub] = mfma(a, qf[kb], s[sub]);
+                }
+            // Scale (log2 domain), mask keys past the window, running max.
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int j = kt * KT + 32 * sub + 8 * (rr >> 2) + 4 * half + (rr & 3);
+                    const float val = j < m ? s[sub][rr] * c_log2 : -INFINITY;
+                    s[sub][rr] = val;
+                    mloc = fmaxf(mloc, val);
+                }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+            const float mnew = fmaxf(mrun, mloc);
+            const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
+            lrun *= corr;
+#pragma unroll
+            for (int i = 0; i < DH / 32; ++i) acc[i] *= corr;
+            bf16x8 pf[4];
+            float lsum = 0.f;
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const float p = __builtin_amdgcn_exp2f(s[sub][8 * hb + jj] - mnew);
+                        lsum += p;
+                        pf[2 * sub + hb][jj] = (__bf16)p;
+                    }
+            lrun += lsum;
+            mrun = mnew;
+#pragma unroll
+            for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 4; ++kb2) {
+                    const int kk = 16 * kb2 + 4 * half;
+                    const __bf16 *row = &sm.vt[cur][32 * dt + col][0];
+                    const bf16x4 lo = *(const bf16x4 *)(row + kk);
+                    const bf16x4 hi = *(const bf16x4 *)(row + kk + 8);
+                    const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[dt] = mfma(a, pf[kb2], acc[dt]);
+                }
+        }
+        if (kt + 1 < ntiles) stash(cur ^ 1);
+        __syncthreads();
+    }
+
+    const float lt = lrun + __shfl_xor(lrun, 32);
+    if (qvalid) {
+        const float inv = 1.f / lt;
+        __bf16 *orow = o + head_off + token(qi) * rowstride;
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 out;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) out[i] = (__bf16)(acc[dt][4 * g + i] * inv);
+                *(bf16x4 *)(orow + 32 * dt + 8 * g + 4 * half) = out;
+            }
+    }
+}
+
+template <int DH>
+hipError_t launch(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
+{
+    const int maxw = p.wt * p.wh * p.ww;
+    const int nqb = (maxw + QB - 1) / QB;
+    const uint64_t total = (uint64_t)p.batch * p.nheads * p.nrt * p.nrh * p.nrw * nqb;
+    const uint64_t blocks = (total + 7) / 8 * 8;
+    const float scale = p.scale > 0.f ? p.scale : 1.f / sqrtf((float)DH);
+    k_tesa_fast<DH><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+        (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, p.nheads, (int)p.T,
+        (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st, p.sh, p.sw, p.nrt, p.nrh, p.nrw, nqb, (uint32_t)total,
+        scale * 1.4426950408889634f);
+    return hipGetLastError();
+}
+
+} // namespace
+
+bool tesa_fast_supports(const TesaProblem &p)
+{
+    return p.dtype == 1 && (p.headdim == 64 || p.headdim == 128) && p.wt * p.wh * p.ww <= 4096 &&
+           p.batch * p.nheads * (int64_t)p.nrt * p.nrh * p.nrw * 16 < ((int64_t)1 << 31);
+}
+
+hipError_t tesa_fast(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
+{
+    if (p.headdim == 64) return launch<64>(p, a, stream);
+    return launch<128>(p, a, stream);
+}
+
 } // namespace mate

@@ -287,3 +287,69 @@ def test_forward_equals_composed_calls(cfg):
         B.mate_tesa(td["q"], td["k"], td["v"], o2, wl.window, shift)
         torch.cuda.synchronize()
         assert torch.equal(y1, y2) and torch.equal(o1, o2)
+
+
+# ----------------------------------------------------------------------------
+# MFMA kernels against the oracle on ragged shapes, and against the portable kernels
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,chunk", [(64, 64), (128, 128), (128, 64), (64, 128)])
+def test_ssd_fast_ragged_with_review(oracle_mod, S, chunk):
+    """105 tokens (ragged last chunk), 5 review tokens, batch 2, 2 groups, headdim 64."""
+    rng = np.random.default_rng(S + chunk)
+    bsz, T, H, W, nh, P, G = 2, 3, 5, 7, 4, 64, 2
+    rnd = lambda *s: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32)))
+    x = rnd(bsz, T, H, W, nh, P) / 8
+    Bm, Cm = rnd(bsz, T, H, W, G, S) / 8, rnd(bsz, T, H, W, G, S) / 8
+    dt = np.log1p(np.exp(rng.normal(-1, 0.5, (bsz, T, H, W, nh)))).astype(np.float32)
+    A = -np.exp(rng.uniform(0, 1, nh)).astype(np.float32)
+    D = rng.standard_normal(nh).astype(np.float32)
+    dev = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in (x, Bm, Cm)] + \
+          [torch.from_numpy(a).cuda() for a in (dt, A, D)]
+    y = torch.full_like(dev[0], float("nan"))
+    for order in range(4):
+        B.mate_bissd_scan(*dev, y, order, chunk, (3, 1, 7), B.ALGO_FAST)
+        want = oracle_mod.bissd(x, Bm, Cm, dt, A, D, (bsz, T, H, W), order, (3, 1, 7))
+        err = parity_error(to_f64(y), want)
+        assert err <= 2e-2, (order, err)
+
+
+@pytest.mark.parametrize("cfg,order", [(1, 0), (1, 3), (2, 0), (3, 2)])
+def test_ssd_fast_matches_portable(cfg, order):
+    say(f"ssd fast vs portable cfg{cfg} order{order}")
+    _, yf = run_ssd(cfg, order, algo=B.ALGO_FAST)
+    _, yp = run_ssd(cfg, order, algo=B.ALGO_PORTABLE)
+    err = parity_error(to_f64(yf), to_f64(yp))
+    say(f"  err={err:.3e}")
+    assert err <= 2e-2
+
+
+@pytest.mark.parametrize("window,shift", [((3, 5, 7), (0, 0, 0)), ((3, 5, 7), (1, 2, 3)), ((1, 5, 7), (0, 4, 6))])
+@pytest.mark.parametrize("d", [64, 128])
+def test_tesa_fast_ragged_windows(oracle_mod, window, shift, d):
+    rng = np.random.default_rng(d)
+    qkv = [synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal((2, 3, 5, 7, 3, d)).astype(np.float32)))
+           for _ in range(3)]
+    dev = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in qkv]
+    o = torch.full_like(dev[0], float("nan"))
+    B.mate_tesa(*dev, o, window, shift, 0.0, B.ALGO_FAST)
+    want = oracle_mod.tesa(*qkv, (2, 3, 5, 7), window, shift)
+    assert parity_error(to_f64(o), want) <= 2e-2
+
+
+@pytest.mark.parametrize("cfg,shifted", [(1, False), (1, True), (2, False), (2, True)])
+def test_tesa_fast_matches_portable(cfg, shifted):
+    dev = tesa_device(cfg)
+    _, of = run_tesa(cfg, shifted, B.ALGO_FAST, dev)
+    _, op = run_tesa(cfg, shifted, B.ALGO_PORTABLE, dev)
+    assert parity_error(to_f64(of), to_f64(op)) <= 2e-2
+
+
+def test_fast_paths_deterministic():
+    _, y1 = run_ssd(2, 0, algo=B.ALGO_FAST)
+    _, y2 = run_ssd(2, 0, algo=B.ALGO_FAST)
+    assert torch.equal(y1, y2)
+    dev = tesa_device(2)
+    _, o1 = run_tesa(2, True, B.ALGO_FAST, dev)
+    _, o2 = run_tesa(2, True, B.ALGO_FAST, dev)
+    assert torch.equal(o1, o2)
