@@ -80,5 +80,41 @@ __global__ __launch_bounds__(256) void k_pool(const E *__restrict__ src, O *__re
     elem<O>::store(out + ((size_t)b * R + j) * C + ch, acc / (float)(pt * ph * pw));
 }
 
+// The same average pool on bf16 input, 8 channels (one 16-byte load) per
+// thread; C must be a multiple of 8. Output bf16 (rounded) or fp32.
+// grid (ceil(C / 2048), R, batch).
+template <typename O>
+__global__ __launch_bounds__(256) void k_pool8(const bf16_t *__restrict__ src, O *__restrict__ out, int64_t C,
+                                               uint32_t Tn, uint32_t Hn, uint32_t Wn, int pt, int ph, int pw,
+                                               int order)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int64_t ch = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (ch >= C) return;
+    const uint32_t j = blockIdx.y, b = blockIdx.z, R = gridDim.y;
+    const uint32_t Tp = Tn / pt, Hp = Hn / ph, Wp = Wn / pw;
+    const uint32_t np = rms_index32(j, order, Tp, Hp, Wp);
+    const uint32_t tq = np / (Hp * Wp), hq = (np / Wp) % Hp, wq = np % Wp;
+    const size_t N = (size_t)Tn * Hn * Wn;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int dt_ = 0; dt_ < pt; ++dt_)
+        for (int dh = 0; dh < ph; ++dh) {
+            const size_t row0 = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw;
+#pragma unroll 8
+            for (int dw = 0; dw < pw; ++dw) {
+                const u32x4 v = *(const u32x4 *)(src + ((size_t)b * N + row0 + dw) * C + ch);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += __uint_as_float(v[e] << 16);
+                    acc[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+                }
+            }
+        }
+    const float inv = 1.f / (float)(pt * ph * pw);
+    O *o = out + ((size_t)b * R + j) * C + ch;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) elem<O>::store(o + e, acc[e] * inv);
+}
+
 } // namespace ssd
 } // namespace mate

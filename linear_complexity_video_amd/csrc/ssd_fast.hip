@@ -12,21 +12,37 @@
 //              The review tokens form one extra segment whose G and F are the
 //              initial states of the two directions.
 //  2. seg pass turns summaries into the true states at every segment border.
-//  3. cb       C_t . B_u (fp32) for every chunk (shared by all heads of a group).
+//  3. cb       C_t . B_u for every chunk (fp16, diagonal also in fp32; shared by
+//              all heads of a group).
 //  4. out      sweeps its segment left to right carrying the forward state Hf
 //              and computes, per chunk,
-//                 Y^T = X^T M^T + [Hf | Hb] [diag(ef) C | diag(eb) C]^T
-//              with M the dense bidirectional intra-chunk matrix (decays below
-//              and above the diagonal, 2 C.B dt + 2D on it; fed to the MFMA as
-//              an exact hi + lo pair of bf16 fragments), ef = exp(cs),
-//              eb = exp(tot - ce), Hb = stored G + decay * border state.
+//                 Y^T = X^T M^T + ef * (Hf C^T) + eb * (Hb C^T)
+//              with M the bidirectional intra-chunk matrix without its
+//              diagonal (decays below and above it), ef = exp(cs),
+//              eb = exp(tot - ce) applied per token to the accumulators,
+//              Hb = stored G + decay * border state; the diagonal term
+//              (2 C_t.B_t dt_t + 2D) x_t is added in fp32 when Y is stored.
+//              X^T M^T runs on fp16 MFMA (x is converted exactly, M rounded
+//              to fp16): its weights carry the largest values of the scan and
+//              fp16 keeps 3 more mantissa bits than bf16.
 //              Then Hf = exp(tot) Hf + sum_u exp(tot - cs_u) dt_u x_u B_u^T.
-// Contractions over tokens need token-contiguous operands, so x and B are
-// written to LDS transposed (pairs of tokens per dword); C, CB and the stored
-// states are already contiguous along the contraction and are read as MFMA
-// fragments straight from memory. Block ids are remapped so that the
-// workgroups resident on one XCD work on consecutive heads of one segment and
-// share B, C and CB in that XCD's L2.
+//
+// Data layout on chip: x and B chunks are staged in LDS in their natural
+// row-major layout (token rows) with plain 16-byte copies; the operands of the
+// contractions over tokens are read with the gfx950 LDS transpose read
+// (ds_read_b64_tr_b16), which hands each lane 4 consecutive rows of one
+// column. C rows, CB rows and the stored states are contiguous along their
+// contraction axis and are used as MFMA fragments directly.
+//
+// Decay weights of M: inside the 32x32 diagonal block of a lane's token block
+// each weight is one exp2; in the blocks below (above) it, exp(cs_t - cs_u)
+// (exp(ce_u - ce_t)) is split at the block edge into a per-lane factor and a
+// per-token factor, both <= 1, so no exponent is evaluated per element.
+//
+// Scan order: a table of the RMS permutation (scan position -> canonical
+// token) is built once per call; every gather reads it instead of dividing.
+// Block ids are remapped so that the workgroups resident on one XCD work on
+// consecutive heads of one segment and share B, C and CB in that XCD's L2.
 #include "common.hpp"
 #include "launch.hpp"
 #include "ssd_common.hpp"
@@ -41,14 +57,25 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int P = 64;       // head dim of the MFMA kernels
 constexpr int NT = 256;     // threads per workgroup
+constexpr int XPAD = 32;    // LDS row padding (bf16) of token-row tiles
 constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma16(f16x8 a, f16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
@@ -62,6 +89,17 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
     return __builtin_bit_cast(uint32_t, r);
 }
 
+__device__ __forceinline__ uint32_t pack2h(float a, float b)
+{
+    f16x2 r;
+    r[0] = (_Float16)a;
+    r[1] = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
+
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // XCD-aware item index of this block (the grid is a multiple of 8).
@@ -71,79 +109,114 @@ __device__ __forceinline__ uint32_t xcd_item()
     return (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 }
 
-// Loads token pairs (2v, 2v+1) x 16-byte column chunk cc of a chunk of Q rows
-// with `cols` bf16 columns per row (x: cols = P per head; B: cols = S per group).
-template <int Q, int COLS, bool PERM>
-struct PairLoader {
-    static constexpr int PAIRS = Q / 2;
-    static constexpr int UNITS = PAIRS * (COLS / 8);
-    static constexpr int PER = UNITS / NT;
-    static_assert(UNITS % NT == 0, "tile must split evenly over the workgroup");
-    u32x4 r0[PER], r1[PER];
+// MFMA operand fragment from a row-major [k][n] LDS tile (row stride ld):
+// lane l gets column n_base + l % 32 at rows k_base + 8 (l / 32) + 0..7.
+__device__ __forceinline__ bf16x8 frag_tr(const __bf16 *tile, int ld, int k_base, int n_base)
+{
+    const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
+    const __bf16 *p = tile + (k_base + 8 * (g >> 1) + (s >> 2)) * ld + n_base + 16 * (g & 1) + 4 * (s & 3);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 4 * ld));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
-    // base + row * row_stride + col_off addresses one row's head/group slice.
-    __device__ __forceinline__ void load(const __bf16 *base, size_t row_stride, uint32_t c, uint32_t L,
-                                         uint32_t batch_rows, int order, uint32_t T, uint32_t H, uint32_t W)
+// MFMA operand fragment from a row-major [m][k] LDS tile: lane l gets row
+// m_base + l % 32 at columns k_base + 8 (l / 32) + 0..7.
+__device__ __forceinline__ bf16x8 frag_rm(const __bf16 *tile, int ld, int m_base, int k_base)
+{
+    const int l = threadIdx.x & 63;
+    return *(const bf16x8 *)(tile + (m_base + (l & 31)) * ld + k_base + 8 * (l >> 5));
+}
+
+// Q token rows of COLS bf16 each, split in 16-byte units over the workgroup.
+// Row u of the chunk is read from global row srow[u] (an LDS table of the
+// chunk's rows; ~0u marks a position past the end, which reads as zero).
+// Loads are unconditional (an invalid row reads row 0 and is then zeroed).
+template <int Q, int COLS>
+struct Rows {
+    static constexpr int UPR = COLS / 8;
+    static constexpr int PER = Q * UPR / NT;
+    static_assert(Q * UPR % NT == 0, "tile must split evenly over the workgroup");
+    u32x4 r[PER];
+
+    __device__ __forceinline__ static int row_of(int it) { return (threadIdx.x + NT * it) / UPR; }
+    __device__ __forceinline__ static int cc_of(int it) { return (threadIdx.x + NT * it) % UPR; }
+
+    __device__ __forceinline__ void load(const __bf16 *base, size_t row_stride, const uint32_t *srow,
+                                         size_t batch_rows)
     {
 #pragma unroll
         for (int it = 0; it < PER; ++it) {
-            const int k = threadIdx.x + NT * it;
-            const int v = k % PAIRS, cc = k / PAIRS;
-            const uint32_t i0 = c * Q + 2 * v, i1 = i0 + 1;
-            r0[it] = u32x4{0, 0, 0, 0};
-            r1[it] = u32x4{0, 0, 0, 0};
-            if (i0 < L)
-                r0[it] = *(const u32x4 *)(base + (batch_rows + ssd::seq_row<PERM>(i0, order, T, H, W)) * row_stride + 8 * cc);
-            if (i1 < L)
-                r1[it] = *(const u32x4 *)(base + (batch_rows + ssd::seq_row<PERM>(i1, order, T, H, W)) * row_stride + 8 * cc);
-        }
-    }
-    // dst[col][2v..2v+1] (row stride LD bf16) = the pair, optionally scaled by w0 / w1.
-    template <int LD>
-    __device__ __forceinline__ void store_t(__bf16 *dst, int it) const
-    {
-        const int k = threadIdx.x + NT * it;
-        const int v = k % PAIRS, cc = k / PAIRS;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t a0 = r0[it][e], a1 = r1[it][e];
-            *(uint32_t *)(dst + (8 * cc + 2 * e) * LD + 2 * v) = (a0 & 0xffffu) | (a1 << 16);
-            *(uint32_t *)(dst + (8 * cc + 2 * e + 1) * LD + 2 * v) = (a0 >> 16) | (a1 & 0xffff0000u);
+            const uint32_t row = srow[row_of(it)];
+            const bool ok = row != ~0u;
+            const u32x4 v = *(const u32x4 *)(base + (batch_rows + (ok ? row : 0u)) * row_stride + 8 * cc_of(it));
+            r[it] = ok ? v : u32x4{0, 0, 0, 0};
         }
     }
     template <int LD>
-    __device__ __forceinline__ void store_t_scaled(__bf16 *dst, int it, float w0, float w1) const
+    __device__ __forceinline__ void store(__bf16 *dst) const
     {
-        const int k = threadIdx.x + NT * it;
-        const int v = k % PAIRS, cc = k / PAIRS;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t a0 = r0[it][e], a1 = r1[it][e];
-            *(uint32_t *)(dst + (8 * cc + 2 * e) * LD + 2 * v) = pack2(lo_f(a0) * w0, lo_f(a1) * w1);
-            *(uint32_t *)(dst + (8 * cc + 2 * e + 1) * LD + 2 * v) = pack2(hi_f(a0) * w0, hi_f(a1) * w1);
+        for (int it = 0; it < PER; ++it) *(u32x4 *)(dst + row_of(it) * LD + 8 * cc_of(it)) = r[it];
+    }
+    // bf16 -> fp16 (exact for values inside the fp16 normal range)
+    template <int LD>
+    __device__ __forceinline__ void store_f16(__bf16 *dst) const
+    {
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack2h(lo_f(r[it][e]), hi_f(r[it][e]));
+            *(u32x4 *)(dst + row_of(it) * LD + 8 * cc_of(it)) = o;
         }
     }
-    __device__ __forceinline__ static int pair_of(int it) { return (threadIdx.x + NT * it) % PAIRS; }
+    template <int LD>
+    __device__ __forceinline__ void store_scaled(__bf16 *dst, int it, float w) const
+    {
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack2(lo_f(r[it][e]) * w, hi_f(r[it][e]) * w);
+        *(u32x4 *)(dst + row_of(it) * LD + 8 * cc_of(it)) = o;
+    }
 };
+
+// Global row of sequence position i (< L): through the permutation table, or
+// the identity when there is none; ~0u past the end.
+__device__ __forceinline__ uint32_t seq_row(const uint32_t *perm, uint32_t i, uint32_t L)
+{
+    return i < L ? (perm ? perm[i] : i) : ~0u;
+}
+
+// ---------------------------------------------------------------------------
+// 0. RMS permutation table: perm[i] = canonical token of scan position i.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_perm(uint32_t *__restrict__ perm, uint32_t N, int order, uint32_t T,
+                                              uint32_t H, uint32_t W)
+{
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i < N) perm[i] = rms_index32(i, order, T, H, W);
+}
 
 // ---------------------------------------------------------------------------
 // 1. Right-to-left segment sweep: stored backward chunk states + summaries.
 // grid = 8 * ceil(batch * nseg * nheads / 8); item = (b * nseg + seg) * nheads + h.
 // ---------------------------------------------------------------------------
-template <int S, int Q, bool PERM>
+template <int S, int Q>
 __global__ __launch_bounds__(NT) void k_states(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
-                                               const float *__restrict__ dtT, const float *__restrict__ csT,
-                                               const float *__restrict__ A, __bf16 *__restrict__ hb_local,
-                                               float *__restrict__ delta, float *__restrict__ segF,
-                                               float *__restrict__ segB, float *__restrict__ segA, int nheads,
-                                               int G, uint32_t L, uint32_t Lpad, int nch, int segch, int nseg,
-                                               int seg_base, int nseg_total, int order, uint32_t T, uint32_t H,
-                                               uint32_t W, uint32_t total_items)
+                                               const uint32_t *__restrict__ perm, const float *__restrict__ dtT,
+                                               const float *__restrict__ csT, const float *__restrict__ A,
+                                               __bf16 *__restrict__ hb_local, float *__restrict__ delta,
+                                               float *__restrict__ segF, float *__restrict__ segB,
+                                               float *__restrict__ segA, int nheads, int G, uint32_t L,
+                                               uint32_t Lpad, int nch, int segch, int nseg, int seg_base,
+                                               int nseg_total, uint32_t total_items)
 {
-    constexpr int QS = Q + 8;
-    __shared__ __bf16 xtb[P * QS];
-    __shared__ __bf16 xtf[P * QS];
-    __shared__ __bf16 bt[S * QS];
+    constexpr int LX = P + XPAD, LB = S + XPAD;
+    __shared__ __bf16 xb[Q * LX];   // x * dt exp(ce)              (backward weights)
+    __shared__ __bf16 xf[Q * LX];   // x * dt exp(tot - cs + logD) (forward weights)
+    __shared__ __bf16 bn[Q * LB];   // B
+    __shared__ uint32_t s_row[Q];   // global rows of the next chunk to fetch
 
     const uint32_t item = xcd_item();
     if (item >= total_items) return;
@@ -153,26 +226,42 @@ __global__ __launch_bounds__(NT) void k_states(const __bf16 *__restrict__ x, con
     const int g = h / (nheads / G);
     const int c_lo = seg * segch, c_hi = min(nch, c_lo + segch);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool isF = wave >= 2;            // waves 0-1: backward state G^T; 2-3: forward sum F^T
     constexpr int SBW = S / 64;            // s-blocks per wave
     const int sb0 = (wave & 1) * SBW;
+    const bool row_thread = wave < Q / 64; // tid < Q: owns one row-table entry
     f32x16 acc[SBW][2];
 #pragma unroll
     for (int i = 0; i < SBW; ++i) acc[i][0] = acc[i][1] = f32x16{};
 
     const float a = A[h];
-    const size_t drow = ((size_t)b * nheads + h) * Lpad;
     const size_t bh = (size_t)b * nheads + h;
-    PairLoader<Q, P, PERM> xl;
-    PairLoader<Q, S, PERM> bl;
-    float logD = 0.f;  // sum of dt*A over the chunks right of the current one (natural log of the decay)
+    const size_t drow = bh * Lpad;
+    Rows<Q, P> xr;
+    Rows<Q, S> br;
+    float wd[Rows<Q, P>::PER], wc[Rows<Q, P>::PER];
+    float tot = 0.f;
+    uint32_t pnext = ~0u;  // row-table entry of the chunk after the one being fetched
+    auto fetch = [&](int c) {
+        xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
+        br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * L);
+#pragma unroll
+        for (int it = 0; it < xr.PER; ++it) {
+            const size_t i = drow + (size_t)c * Q + xr.row_of(it);
+            wd[it] = dtT[i];
+            wc[it] = csT[i];
+        }
+        tot = csT[drow + (size_t)c * Q + Q - 1];
+        if (row_thread) pnext = c > c_lo ? seq_row(perm, (uint32_t)(c - 1) * Q + tid, L) : ~0u;
+    };
+    if (row_thread) s_row[tid] = seq_row(perm, (uint32_t)(c_hi - 1) * Q + tid, L);
+    __syncthreads();
+    fetch(c_hi - 1);
+    float logD = 0.f;  // sum of dt*A over the chunks right of the current one
 
     for (int c = c_hi - 1; c >= c_lo; --c) {
-        xl.load(x + (size_t)h * P, (size_t)nheads * P, c, L, (size_t)b * L, order, T, H, W);
-        bl.load(Bm + (size_t)g * S, (size_t)G * S, c, L, (size_t)b * L, order, T, H, W);
-        const float tot = csT[drow + (size_t)c * Q + Q - 1];
-
         // Backward state entering chunk c from the right.
         if (hb_local && !isF) {
             __bf16 *dst = hb_local + (bh * nch + c) * (size_t)(P * S);
@@ -190,44 +279,40 @@ __global__ __launch_bounds__(NT) void k_states(const __bf16 *__restrict__ x, con
         }
         if (delta && tid == 0) delta[bh * nch + c] = ex2(logD * LOG2E);
 
-        __syncthreads();  // previous chunk's MFMA reads of LDS are done
+        __syncthreads();  // previous chunk's MFMA reads of LDS and this chunk's row-table reads are done
 #pragma unroll
-        for (int it = 0; it < xl.PER; ++it) {
-            const int v = xl.pair_of(it);
-            const size_t i0 = drow + (size_t)c * Q + 2 * v;
-            const float d0 = dtT[i0], d1 = dtT[i0 + 1];
-            const float c0 = csT[i0], c1 = csT[i0 + 1];
-            // backward weights exp(ce) dt, forward weights exp(tot - cs + logD) dt
-            xl.template store_t_scaled<QS>(xtb, it, d0 * ex2((c0 - d0 * a) * LOG2E), d1 * ex2((c1 - d1 * a) * LOG2E));
-            xl.template store_t_scaled<QS>(xtf, it, d0 * ex2((tot - c0 + logD) * LOG2E),
-                                           d1 * ex2((tot - c1 + logD) * LOG2E));
+        for (int it = 0; it < xr.PER; ++it) {
+            xr.template store_scaled<LX>(xb, it, wd[it] * ex2((wc[it] - wd[it] * a) * LOG2E));
+            xr.template store_scaled<LX>(xf, it, wd[it] * ex2((tot - wc[it] + logD) * LOG2E));
         }
-#pragma unroll
-        for (int it = 0; it < bl.PER; ++it) bl.template store_t<QS>(bt, it);
+        br.template store<LB>(bn);
+        if (row_thread) s_row[tid] = pnext;
         __syncthreads();
 
+        const float tot_c = tot;
+        if (c > c_lo) fetch(c - 1);
         if (!isF) {
-            const float dec = ex2(tot * LOG2E);
+            const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
             for (int i = 0; i < SBW; ++i) {
                 acc[i][0] *= dec;
                 acc[i][1] *= dec;
             }
         }
-        const __bf16 *xs = isF ? xtf : xtb;
+        const __bf16 *xs = isF ? xf : xb;
 #pragma unroll
         for (int kb = 0; kb < Q / 16; ++kb) {
             bf16x8 af[SBW], bfr[2];
 #pragma unroll
-            for (int i = 0; i < SBW; ++i) af[i] = *(const bf16x8 *)&bt[(32 * (sb0 + i) + col) * QS + 16 * kb + 8 * half];
+            for (int i = 0; i < SBW; ++i) af[i] = frag_tr(bn, LB, 16 * kb, 32 * (sb0 + i));
 #pragma unroll
-            for (int pb = 0; pb < 2; ++pb) bfr[pb] = *(const bf16x8 *)&xs[(32 * pb + col) * QS + 16 * kb + 8 * half];
+            for (int pb = 0; pb < 2; ++pb) bfr[pb] = frag_tr(xs, LX, 16 * kb, 32 * pb);
 #pragma unroll
             for (int i = 0; i < SBW; ++i)
 #pragma unroll
                 for (int pb = 0; pb < 2; ++pb) acc[i][pb] = mfma(af[i], bfr[pb], acc[i][pb]);
         }
-        logD += tot;
+        logD += tot_c;
     }
 
     float *dst = (isF ? segF : segB) + (bh * nseg_total + seg_base + seg) * (size_t)(P * S);
@@ -248,7 +333,7 @@ __global__ __launch_bounds__(NT) void k_states(const __bf16 *__restrict__ x, con
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_seg_pass(const float *__restrict__ segF, const float *__restrict__ segB,
                                                   const float *__restrict__ segA, float *__restrict__ hinF,
-                                                  float *__restrict__ hinB, int PS, int nseg, int nseg_total,
+                                                  __bf16 *__restrict__ hinB, int PS, int nseg, int nseg_total,
                                                   int has_review)
 {
     const int e = blockIdx.x * 256 + threadIdx.x;
@@ -264,46 +349,58 @@ __global__ __launch_bounds__(256) void k_seg_pass(const float *__restrict__ segF
     }
     run = has_review ? Bk[(size_t)nseg * PS] : 0.f;
     for (int j = nseg - 1; j >= 0; --j) {
-        hinB[(bh * nseg + j) * PS + e] = run;
+        hinB[(bh * nseg + j) * PS + e] = (__bf16)run;
         run = ex2(sa[j] * LOG2E) * run + Bk[(size_t)j * PS];
     }
 }
 
 // ---------------------------------------------------------------------------
-// 3. CB[t][u] = C_t . B_u per chunk and group (fp32). grid (nch, G, batch).
-// Computed as CB^T = B C^T so each lane holds 4 consecutive u of one t.
+// 3. CB[t][u] = C_t . B_u per chunk and group: fp16 matrix plus its diagonal
+// in fp32. grid (nch, G, batch). Computed as CB^T = B C^T so each lane holds
+// 4 consecutive u of one t.
 // ---------------------------------------------------------------------------
 template <int S, int Q>
 __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
-                                           float *__restrict__ cb, int G, uint32_t L, int order, uint32_t T,
-                                           uint32_t H, uint32_t W)
+                                           const uint32_t *__restrict__ perm, _Float16 *__restrict__ cb,
+                                           float *__restrict__ cbd, int G, uint32_t L)
 {
     const uint32_t c = blockIdx.x;
     const int g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     constexpr int TB = Q / 32;
     constexpr int TILES = TB * TB / 4;  // per wave
     const size_t rs = (size_t)G * S;
-    float *out = cb + (((size_t)b * G + g) * gridDim.x + c) * (size_t)(Q * Q);
+    const size_t chunk = ((size_t)b * G + g) * gridDim.x + c;
+    _Float16 *out = cb + chunk * (size_t)(Q * Q);
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
         const int ti = wave + 4 * k;
         const int ub = ti / TB, tb = ti % TB;
         const uint32_t iu = c * Q + 32 * ub + col, itk = c * Q + 32 * tb + col;
-        const __bf16 *brow = iu < L ? Bm + ((size_t)b * L + rms_index32(iu, order, T, H, W)) * rs + (size_t)g * S : nullptr;
-        const __bf16 *crow = itk < L ? Cm + ((size_t)b * L + rms_index32(itk, order, T, H, W)) * rs + (size_t)g * S : nullptr;
+        const bool uok = iu < L, tok = itk < L;
+        const __bf16 *brow = Bm + ((size_t)b * L + (uok ? perm[iu] : 0u)) * rs + (size_t)g * S;
+        const __bf16 *crow = Cm + ((size_t)b * L + (tok ? perm[itk] : 0u)) * rs + (size_t)g * S;
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int kb = 0; kb < S / 16; ++kb) {
-            const u32x4 av = brow ? *(const u32x4 *)(brow + 16 * kb + 8 * half) : u32x4{0, 0, 0, 0};
-            const u32x4 bv = crow ? *(const u32x4 *)(crow + 16 * kb + 8 * half) : u32x4{0, 0, 0, 0};
+            u32x4 av = *(const u32x4 *)(brow + 16 * kb + 8 * half);
+            u32x4 bv = *(const u32x4 *)(crow + 16 * kb + 8 * half);
+            av = uok ? av : u32x4{0, 0, 0, 0};
+            bv = tok ? bv : u32x4{0, 0, 0, 0};
             acc = mfma(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc);
         }
         // acc: rows u = 32ub + 8g4 + 4half + j, column t = 32tb + col
+        const int t = 32 * tb + col;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 v4 = {acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
-            *(f32x4 *)(out + (size_t)(32 * tb + col) * Q + 32 * ub + 8 * g4 + 4 * half) = v4;
+            f16x4 v4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v4[j] = (_Float16)acc[4 * g4 + j];
+                if (ub == tb && 8 * g4 + 4 * half + j == col) cbd[chunk * Q + t] = acc[4 * g4 + j];
+            }
+            *(f16x4 *)(out + (size_t)t * Q + 32 * ub + 8 * g4 + 4 * half) = v4;
         }
     }
 }
@@ -313,22 +410,24 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
 // ---------------------------------------------------------------------------
 template <int S, int Q>
 __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
-                                            const __bf16 *__restrict__ Cm, const float *__restrict__ cb,
+                                            const __bf16 *__restrict__ Cm, const _Float16 *__restrict__ cb,
+                                            const float *__restrict__ cbd, const uint32_t *__restrict__ perm,
                                             const float *__restrict__ dtT, const float *__restrict__ csT,
                                             const float *__restrict__ A, const float *__restrict__ Dv,
                                             const __bf16 *__restrict__ hb_local, const float *__restrict__ delta,
-                                            const float *__restrict__ hinF, const float *__restrict__ hinB,
+                                            const float *__restrict__ hinF, const __bf16 *__restrict__ hinB,
                                             __bf16 *__restrict__ y, int nheads, int G, uint32_t N, uint32_t Lpad,
-                                            int nch, int segch, int nseg, int order, uint32_t T, uint32_t H,
-                                            uint32_t W, uint32_t total_items)
+                                            int nch, int segch, int nseg, uint32_t total_items)
 {
-    constexpr int QS = Q + 8, SS = S + 8;
-    __shared__ __bf16 xt[P * QS];    // x^T
-    __shared__ __bf16 xtf[P * QS];   // x^T weighted by dt exp(tot - cs)
-    __shared__ __bf16 bt[S * QS];    // B^T
-    __shared__ __bf16 hfl[P * SS];   // forward state entering the chunk
-    __shared__ __bf16 hbl[P * SS];   // backward state entering the chunk from the right
-    __shared__ float s_cs[Q], s_ce[Q], s_dt[Q];  // cs, ce in log2 units
+    constexpr int LX = P + XPAD, LB = S + XPAD, SS = S + 8;
+    __shared__ __bf16 xn[Q * LX];    // x, converted to fp16 (operand of the fp16 intra-chunk product)
+    __shared__ __bf16 xf[Q * LX];    // x * dt exp(tot - cs)
+    __shared__ __bf16 bn[Q * LB];    // B
+    __shared__ __bf16 hfl[P * SS];   // forward state entering the chunk, [p][s]
+    __shared__ __bf16 hbl[P * SS];   // backward state entering the chunk from the right, [p][s]
+    // per token: cs, ce (log2 units), dt, and the split decay factors of the off-diagonal blocks
+    __shared__ __attribute__((aligned(16))) float s_cs[Q], s_ce[Q], s_dt[Q], s_gl[Q], s_gu[Q];
+    __shared__ uint32_t s_row[Q];    // global rows: of chunk c at the top of iteration c, then of chunk c+1
 
     const uint32_t item = xcd_item();
     if (item >= total_items) return;
@@ -340,7 +439,9 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
     const size_t bh = (size_t)b * nheads + h;
     const size_t drow = bh * Lpad;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool row_thread = wave < Q / 64;  // tid < Q
     // Y^T tiles: Q = 128 -> t-block = wave, p-blocks 0 and 1; Q = 64 -> t-block wave / 2, p-block wave % 2.
     constexpr int YT = Q / 64;
     const int tb = Q == 128 ? wave : wave >> 1;
@@ -366,65 +467,79 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
                 for (int j = 0; j < 4; ++j) hacc[i][4 * g4 + j] = v4[j];
             }
     }
-    // Border state of the backward direction, for this thread's staging chunks.
+    // Border state of the backward direction (bf16), for this thread's staging chunks.
     constexpr int HBC = PS / 8 / NT;  // 16-byte chunks of Hb per thread
-    float hinb[HBC][8];
+    u32x4 hinb[HBC];
     {
-        const float *src = hinB + (bh * nseg + seg) * (size_t)PS;
+        const __bf16 *src = hinB + (bh * nseg + seg) * (size_t)PS;
 #pragma unroll
-        for (int it = 0; it < HBC; ++it) {
-            const int k = tid + NT * it;
-            const f32x4 v0 = *(const f32x4 *)(src + 8 * k), v1 = *(const f32x4 *)(src + 8 * k + 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hinb[it][j] = v0[j];
-                hinb[it][4 + j] = v1[j];
-            }
-        }
+        for (int it = 0; it < HBC; ++it) hinb[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
     }
 
-    PairLoader<Q, P, true> xl;
-    PairLoader<Q, S, true> bl;
+    Rows<Q, P> xr;
+    Rows<Q, S> br;
     const size_t cb_base = ((size_t)b * G + g) * nch;
     const int t_tok = 32 * tb + col;  // this lane's token inside the chunk (Y^T column)
 
-    for (int c = c_lo; c < c_hi; ++c) {
-        // ---- global loads ----
-        xl.load(x + (size_t)h * P, (size_t)nheads * P, c, N, (size_t)b * N, order, T, H, W);
-        bl.load(Bm + (size_t)g * S, (size_t)G * S, c, N, (size_t)b * N, order, T, H, W);
-        u32x4 hbr[HBC];
-        {
-            const __bf16 *src = hb_local + (bh * nch + c) * (size_t)PS;
+    // Data staged through LDS, fetched one chunk ahead.
+    u32x4 hbr[HBC];
+    float wd[Rows<Q, P>::PER], wc[Rows<Q, P>::PER];
+    float tok_d = 0.f, tok_c = 0.f, blk_cs_end = 0.f, blk_cs0 = 0.f, blk_dt0 = 0.f, tot = 0.f, dl = 0.f;
+    uint32_t pnext = ~0u;
+    auto fetch = [&](int c) {
+        xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * N);
+        br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * N);
+        const size_t crow0 = drow + (size_t)c * Q;
 #pragma unroll
-            for (int it = 0; it < HBC; ++it) hbr[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
+        for (int it = 0; it < xr.PER; ++it) {
+            wd[it] = dtT[crow0 + xr.row_of(it)];
+            wc[it] = csT[crow0 + xr.row_of(it)];
         }
-        const uint32_t ti = c * Q + t_tok;
-        const bool tvalid = ti < N;
-        const size_t trow = tvalid ? (size_t)b * N + rms_index32(ti, order, T, H, W) : 0;
-        u32x4 cfr[S / 16];
+        const __bf16 *src = hb_local + (bh * nch + c) * (size_t)PS;
+#pragma unroll
+        for (int it = 0; it < HBC; ++it) hbr[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
+        if (row_thread) {
+            const int ub = tid & ~31;
+            tok_d = dtT[crow0 + tid];
+            tok_c = csT[crow0 + tid];
+            blk_cs_end = csT[crow0 + ub + 31];
+            blk_cs0 = csT[crow0 + ub];
+            blk_dt0 = dtT[crow0 + ub];
+            pnext = c + 1 < c_hi ? seq_row(perm, (uint32_t)(c + 1) * Q + tid, N) : ~0u;
+        }
+        tot = csT[crow0 + Q - 1];
+        dl = delta[bh * nch + c];
+    };
+    if (row_thread) s_row[tid] = seq_row(perm, (uint32_t)c_lo * Q + tid, N);
+    __syncthreads();
+    fetch(c_lo);
+
+    for (int c = c_lo; c < c_hi; ++c) {
+        // C row, CB row and CB diagonal of this lane's token (MFMA fragments of the Y phase).
+        const uint32_t rt = s_row[t_tok];
+        const bool tvalid = rt != ~0u;
+        const size_t trow = (size_t)b * N + (tvalid ? rt : 0u);
+        u32x4 cfr[S / 16], cbf[Q / 16];
         {
             const __bf16 *crow = Cm + trow * ((size_t)G * S) + (size_t)g * S;
 #pragma unroll
-            for (int kb = 0; kb < S / 16; ++kb)
-                cfr[kb] = tvalid ? *(const u32x4 *)(crow + 16 * kb + 8 * half) : u32x4{0, 0, 0, 0};
+            for (int kb = 0; kb < S / 16; ++kb) {
+                const u32x4 v = *(const u32x4 *)(crow + 16 * kb + 8 * half);
+                cfr[kb] = tvalid ? v : u32x4{0, 0, 0, 0};
+            }
+            const _Float16 *cbrow = cb + (cb_base + c) * (size_t)(Q * Q) + (size_t)t_tok * Q;
+#pragma unroll
+            for (int kb = 0; kb < Q / 16; ++kb) cbf[kb] = *(const u32x4 *)(cbrow + 16 * kb + 8 * half);
         }
-        const float *cbrow = cb + (cb_base + c) * (size_t)(Q * Q) + (size_t)t_tok * Q;
-        const float tot = csT[drow + (size_t)c * Q + Q - 1];
-        const float dl = delta[bh * nch + c];
+        const float cb_tt = cbd[(cb_base + c) * Q + t_tok];
 
-        __syncthreads();  // previous chunk's LDS reads are done
+        __syncthreads();  // previous chunk's LDS reads (and this chunk's row-table reads) are done
         // ---- LDS writes ----
+        xr.template store_f16<LX>(xn);
 #pragma unroll
-        for (int it = 0; it < xl.PER; ++it) {
-            const int v = xl.pair_of(it);
-            const size_t i0 = drow + (size_t)c * Q + 2 * v;
-            const float d0 = dtT[i0], d1 = dtT[i0 + 1];
-            const float c0 = csT[i0], c1 = csT[i0 + 1];
-            xl.template store_t<QS>(xt, it);
-            xl.template store_t_scaled<QS>(xtf, it, d0 * ex2((tot - c0) * LOG2E), d1 * ex2((tot - c1) * LOG2E));
-        }
-#pragma unroll
-        for (int it = 0; it < bl.PER; ++it) bl.template store_t<QS>(bt, it);
+        for (int it = 0; it < xr.PER; ++it)
+            xr.template store_scaled<LX>(xf, it, wd[it] * ex2((tot - wc[it]) * LOG2E));
+        br.template store<LB>(bn);
 #pragma unroll
         for (int i = 0; i < HT; ++i)
 #pragma unroll
@@ -441,96 +556,113 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                o[e] = pack2(lo_f(hbr[it][e]) + dl * hinb[it][2 * e], hi_f(hbr[it][e]) + dl * hinb[it][2 * e + 1]);
+                o[e] = pack2(lo_f(hbr[it][e]) + dl * lo_f(hinb[it][e]), hi_f(hbr[it][e]) + dl * hi_f(hinb[it][e]));
             *(u32x4 *)&hbl[p * SS + s0] = o;
         }
-        if (tid < Q) {
-            const float d = dtT[drow + (size_t)c * Q + tid], cs = csT[drow + (size_t)c * Q + tid];
-            s_dt[tid] = d;
-            s_cs[tid] = cs * LOG2E;
-            s_ce[tid] = (cs - d * a) * LOG2E;
+        if (row_thread) {
+            const float cs2 = tok_c * LOG2E, ce2 = (tok_c - tok_d * a) * LOG2E;
+            s_dt[tid] = tok_d;
+            s_cs[tid] = cs2;
+            s_ce[tid] = ce2;
+            // below-diagonal blocks: exp(cs_end - cs_u); above: exp(ce_u - ce_start); both <= 1
+            s_gl[tid] = tok_d * ex2(blk_cs_end * LOG2E - cs2);
+            s_gu[tid] = tok_d * ex2(ce2 - (blk_cs0 - blk_dt0 * a) * LOG2E);
+            s_row[tid] = pnext;
         }
         __syncthreads();
 
-        // ---- Y^T = X^T M^T + [Hf | Hb] [ef C | eb C]^T ----
-        const float cs_t = s_cs[t_tok], ce_t = s_ce[t_tok], dt_t = s_dt[t_tok];
-        f32x16 yacc[YT];
-#pragma unroll
-        for (int i = 0; i < YT; ++i) yacc[i] = f32x16{};
-#pragma unroll
-        for (int kb = 0; kb < Q / 16; ++kb) {
-            const int u0 = 16 * kb + 8 * half;
-            const f32x4 cb0 = *(const f32x4 *)(cbrow + u0), cb1 = *(const f32x4 *)(cbrow + u0 + 4);
-            // M as an exact pair of bf16 fragments (hi + lo), so the intra-chunk
-            // product carries fp32-level weights.
-            bf16x8 mhi, mlo;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int u = u0 + j;
-                const float cbv = j < 4 ? cb0[j] : cb1[j - 4];
-                float m;
-                if (u == t_tok)
-                    m = 2.f * cbv * dt_t + twoD;
-                else
-                    m = cbv * s_dt[u] * ex2(u < t_tok ? cs_t - s_cs[u] : s_ce[u] - ce_t);
-                mhi[j] = (__bf16)m;
-                mlo[j] = (__bf16)(m - (float)mhi[j]);
-            }
-#pragma unroll
-            for (int i = 0; i < YT; ++i) {
-                const bf16x8 af = *(const bf16x8 *)&xt[(32 * (pb0 + i) + col) * QS + u0];
-                yacc[i] = mfma(af, mhi, yacc[i]);
-                yacc[i] = mfma(af, mlo, yacc[i]);
-            }
-        }
-        {
-            const float ef = ex2(cs_t), eb = ex2(tot * LOG2E - ce_t);
-#pragma unroll
-            for (int kb = 0; kb < S / 16; ++kb) {
-                const int s0 = 16 * kb + 8 * half;
-                u32x4 fe, fb;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float l = lo_f(cfr[kb][e]), hgh = hi_f(cfr[kb][e]);
-                    fe[e] = pack2(l * ef, hgh * ef);
-                    fb[e] = pack2(l * eb, hgh * eb);
-                }
-#pragma unroll
-                for (int i = 0; i < YT; ++i) {
-                    const int prow = 32 * (pb0 + i) + col;
-                    yacc[i] = mfma(*(const bf16x8 *)&hfl[prow * SS + s0], __builtin_bit_cast(bf16x8, fe), yacc[i]);
-                    yacc[i] = mfma(*(const bf16x8 *)&hbl[prow * SS + s0], __builtin_bit_cast(bf16x8, fb), yacc[i]);
-                }
-            }
-        }
+        const float tot_c = tot;
+        if (c + 1 < c_hi) fetch(c + 1);
 
-        // ---- Hf = exp(tot) Hf + B^T-weighted x (as Hf^T = B^T xtf^T) ----
+        // ---- Hf = exp(tot) Hf + B^T-weighted x (as Hf^T = B^T xf^T); LDS operands only ----
         {
-            const float dec = ex2(tot * LOG2E);
+            const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
             for (int i = 0; i < HT; ++i) hacc[i] *= dec;
 #pragma unroll
             for (int kb = 0; kb < Q / 16; ++kb) {
-                const bf16x8 af = *(const bf16x8 *)&bt[(32 * hsb + col) * QS + 16 * kb + 8 * half];
+                const bf16x8 af = frag_tr(bn, LB, 16 * kb, 32 * hsb);
 #pragma unroll
-                for (int i = 0; i < HT; ++i) {
-                    const bf16x8 bfr = *(const bf16x8 *)&xtf[(32 * (hpb0 + i) + col) * QS + 16 * kb + 8 * half];
-                    hacc[i] = mfma(af, bfr, hacc[i]);
-                }
+                for (int i = 0; i < HT; ++i) hacc[i] = mfma(af, frag_tr(xf, LX, 16 * kb, 32 * (hpb0 + i)), hacc[i]);
             }
         }
 
-        // ---- store Y (lane: token t_tok, 4 consecutive p per group) ----
-        if (tvalid) {
+        const float cs_t = s_cs[t_tok], ce_t = s_ce[t_tok], dt_t = s_dt[t_tok];
+        // ---- forward inter-chunk term: ef * (Hf C^T) ----
+        f32x16 yacc[YT], yb[YT];
+#pragma unroll
+        for (int i = 0; i < YT; ++i) yacc[i] = yb[i] = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < S / 16; ++kb)
+#pragma unroll
+            for (int i = 0; i < YT; ++i)
+                yacc[i] = mfma(frag_rm(hfl, SS, 32 * (pb0 + i), 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yacc[i]);
+        {
+            const float ef = ex2(cs_t);
+#pragma unroll
+            for (int i = 0; i < YT; ++i) yacc[i] *= ef;
+        }
+        // ---- intra-chunk term X^T M^T (diagonal of M excluded: added in fp32 below) ----
+#pragma unroll
+        for (int U = 0; U < Q / 32; ++U) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int kb = 2 * U + kk, u0 = 16 * kb + 8 * half;
+                f16x8 mf;
+                if (U == tb) {
+                    const f32x4 d0 = *(const f32x4 *)(s_dt + u0), d1 = *(const f32x4 *)(s_dt + u0 + 4);
+                    const f32x4 c0 = *(const f32x4 *)(s_cs + u0), c1 = *(const f32x4 *)(s_cs + u0 + 4);
+                    const f32x4 e0 = *(const f32x4 *)(s_ce + u0), e1 = *(const f32x4 *)(s_ce + u0 + 4);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int u = u0 + j;
+                        const float cbv = (j & 1) ? h_hi(cbf[kb][j >> 1]) : h_lo(cbf[kb][j >> 1]);
+                        const float dtu = j < 4 ? d0[j] : d1[j - 4];
+                        const float csu = j < 4 ? c0[j] : c1[j - 4];
+                        const float ceu = j < 4 ? e0[j] : e1[j - 4];
+                        const float m = cbv * dtu * ex2(u < t_tok ? cs_t - csu : ceu - ce_t);
+                        mf[j] = (_Float16)(u == t_tok ? 0.f : m);
+                    }
+                } else {
+                    const bool below = U < tb;
+                    const float f = below ? ex2(cs_t - s_cs[32 * U + 31]) : ex2(s_ce[32 * U] - ce_t);
+                    const float *gw = below ? s_gl : s_gu;
+                    const f32x4 g0 = *(const f32x4 *)(gw + u0), g1 = *(const f32x4 *)(gw + u0 + 4);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float cbv = (j & 1) ? h_hi(cbf[kb][j >> 1]) : h_lo(cbf[kb][j >> 1]);
+                        mf[j] = (_Float16)(cbv * (j < 4 ? g0[j] : g1[j - 4]) * f);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < YT; ++i)
+                    yacc[i] = mfma16(__builtin_bit_cast(f16x8, frag_tr(xn, LX, 16 * kb, 32 * (pb0 + i))), mf, yacc[i]);
+            }
+        }
+        // ---- backward inter-chunk term: eb * (Hb C^T) ----
+#pragma unroll
+        for (int kb = 0; kb < S / 16; ++kb)
+#pragma unroll
+            for (int i = 0; i < YT; ++i)
+                yb[i] = mfma(frag_rm(hbl, SS, 32 * (pb0 + i), 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb[i]);
+
+        // ---- store Y = acc + eb * yb + (2 C_t.B_t dt_t + 2D) x_t (lane: token t_tok, 4 consecutive p per group) ----
+        {
+            const float eb = ex2(tot_c * LOG2E - ce_t);
+            const float diag = 2.f * cb_tt * dt_t + twoD;
             __bf16 *yrow = y + (trow * nheads + h) * P;
 #pragma unroll
             for (int i = 0; i < YT; ++i)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
+                    const int p0 = 32 * (pb0 + i) + 8 * g4 + 4 * half;
+                    const uint2 xv = *(const uint2 *)&xn[t_tok * LX + p0];
+                    const float xs[4] = {h_lo(xv.x), h_hi(xv.x), h_lo(xv.y), h_hi(xv.y)};
                     bf16x4 v4;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) v4[j] = (__bf16)yacc[i][4 * g4 + j];
-                    *(bf16x4 *)(yrow + 32 * (pb0 + i) + 8 * g4 + 4 * half) = v4;
+                    for (int j = 0; j < 4; ++j)
+                        v4[j] = (__bf16)(yacc[i][4 * g4 + j] + eb * yb[i][4 * g4 + j] + diag * xs[j]);
+                    if (tvalid) *(bf16x4 *)(yrow + p0) = v4;
                 }
         }
     }
@@ -540,7 +672,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
     int nseg, segch, nsegT;
-    size_t dtT, csT, cb, hbl, delta, segF, segB, segA, hinF, hinB, rx, rB, rdt, rdtT, rcsT, total;
+    size_t perm, dtT, csT, cb, cbd, hbl, delta, segF, segB, segA, hinF, hinB, rx, rB, rdt, rdtT, rcsT, total;
 };
 
 Plan make_plan(const SsdProblem &p)
@@ -557,16 +689,18 @@ Plan make_plan(const SsdProblem &p)
     pl.nsegT = pl.nseg + (p.R > 0 ? 1 : 0);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    pl.perm = take((size_t)p.N * 4);
     pl.dtT = take(B * Hs * Lpad * 4);
     pl.csT = take(B * Hs * Lpad * 4);
-    pl.cb = take(B * p.ngroups * p.nch * Q * Q * 4);
+    pl.cb = take(B * p.ngroups * p.nch * Q * Q * 2);
+    pl.cbd = take(B * p.ngroups * p.nch * Q * 4);
     pl.hbl = take(B * Hs * p.nch * PS * 2);
     pl.delta = take(B * Hs * p.nch * 4);
     pl.segF = take(B * Hs * pl.nsegT * PS * 4);
     pl.segB = take(B * Hs * pl.nsegT * PS * 4);
     pl.segA = take(B * Hs * pl.nsegT * 4);
     pl.hinF = take(B * Hs * pl.nseg * PS * 4);
-    pl.hinB = take(B * Hs * pl.nseg * PS * 4);
+    pl.hinB = take(B * Hs * pl.nseg * PS * 2);
     if (p.R > 0) {
         const size_t Rpad = (size_t)p.nchR * Q;
         pl.rx = take(B * p.R * Hs * P * 2);
@@ -586,11 +720,14 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
 {
     const Plan pl = make_plan(p);
     char *w = (char *)ws;
+    uint32_t *perm = (uint32_t *)(w + pl.perm);
     float *dtT = (float *)(w + pl.dtT), *csT = (float *)(w + pl.csT);
-    float *cb = (float *)(w + pl.cb);
+    _Float16 *cb = (_Float16 *)(w + pl.cb);
+    float *cbd = (float *)(w + pl.cbd);
     __bf16 *hbl = (__bf16 *)(w + pl.hbl);
     float *delta = (float *)(w + pl.delta), *segF = (float *)(w + pl.segF), *segB = (float *)(w + pl.segB);
-    float *segA = (float *)(w + pl.segA), *hinF = (float *)(w + pl.hinF), *hinB = (float *)(w + pl.hinB);
+    float *segA = (float *)(w + pl.segA), *hinF = (float *)(w + pl.hinF);
+    __bf16 *hinB = (__bf16 *)(w + pl.hinB);
     const int Hs = p.nheads, G = p.ngroups, Bn = (int)p.batch;
     const uint32_t N = (uint32_t)p.N, Lpad = (uint32_t)(p.nch * Q);
     const uint32_t T = (uint32_t)p.T, H = (uint32_t)p.H, W = (uint32_t)p.W;
@@ -601,31 +738,31 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
         float *rdt = (float *)(w + pl.rdt), *rdtT = (float *)(w + pl.rdtT), *rcsT = (float *)(w + pl.rcsT);
         const uint32_t R = (uint32_t)p.R, Rpad = (uint32_t)(p.nchR * Q);
         const int64_t Cx = (int64_t)Hs * P, Cb = (int64_t)G * S;
-        ssd::k_pool<bf16_t, bf16_t><<<dim3((Cx + 255) / 256, R, Bn), 256, 0, st>>>(
+        ssd::k_pool8<bf16_t><<<dim3((Cx + 2047) / 2048, R, Bn), 256, 0, st>>>(
             (const bf16_t *)a.x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
-        ssd::k_pool<bf16_t, bf16_t><<<dim3((Cb + 255) / 256, R, Bn), 256, 0, st>>>(
+        ssd::k_pool8<bf16_t><<<dim3((Cb + 2047) / 2048, R, Bn), 256, 0, st>>>(
             (const bf16_t *)a.b, rB, Cb, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
         ssd::k_pool<float, float><<<dim3((Hs + 255) / 256, R, Bn), 256, 0, st>>>(
             a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
         ssd::k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, Bn), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad,
                                                                                 Q, 0, 1, 1, R);
         const uint64_t items = (uint64_t)Bn * Hs;
-        k_states<S, Q, false><<<grid_of(items), NT, 0, st>>>(
-            (const __bf16 *)rx, (const __bf16 *)rB, rdtT, rcsT, a.a, nullptr, nullptr, segF, segB, segA, Hs, G, R,
-            Rpad, p.nchR, p.nchR, 1, pl.nseg, pl.nsegT, 0, 1, 1, R, (uint32_t)items);
+        k_states<S, Q><<<grid_of(items), NT, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, rdtT, rcsT,
+                                                      a.a, nullptr, nullptr, segF, segB, segA, Hs, G, R, Rpad,
+                                                      p.nchR, p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)items);
     }
+    k_perm<<<(N + 255) / 256, 256, 0, st>>>(perm, N, p.order, T, H, W);
     ssd::k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, Bn), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q,
                                                                          p.order, T, H, W);
-    k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, cb, G, N, p.order, T, H, W);
+    k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, cbd, G, N);
     const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
-    k_states<S, Q, true><<<grid_of(items), NT, 0, st>>>(x, Bm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
-                                                        N, Lpad, p.nch, pl.segch, pl.nseg, 0, pl.nsegT, p.order, T,
-                                                        H, W, (uint32_t)items);
+    k_states<S, Q><<<grid_of(items), NT, 0, st>>>(x, Bm, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
+                                                  N, Lpad, p.nch, pl.segch, pl.nseg, 0, pl.nsegT, (uint32_t)items);
     k_seg_pass<<<dim3((P * S + 255) / 256, Hs, Bn), 256, 0, st>>>(segF, segB, segA, hinF, hinB, P * S, pl.nseg,
                                                                   pl.nsegT, p.R > 0 ? 1 : 0);
-    k_out<S, Q><<<grid_of(items), NT, 0, st>>>(x, Bm, Cm, cb, dtT, csT, a.a, a.d, hbl, delta, hinF, hinB,
-                                               (__bf16 *)a.y, Hs, G, N, Lpad, p.nch, pl.segch, pl.nseg, p.order, T,
-                                               H, W, (uint32_t)items);
+    k_out<S, Q><<<grid_of(items), NT, 0, st>>>(x, Bm, Cm, cb, cbd, perm, dtT, csT, a.a, a.d, hbl, delta, hinF, hinB,
+                                               (__bf16 *)a.y, Hs, G, N, Lpad, p.nch, pl.segch, pl.nseg,
+                                               (uint32_t)items);
     return hipGetLastError();
 }
 

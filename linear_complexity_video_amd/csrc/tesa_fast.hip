@@ -3,7 +3,8 @@
 //
 // Work item = (window, head, block of 256 queries); a workgroup of 8 waves
 // owns one item, each wave 32 queries. Keys and values stream through LDS in
-// tiles of 64 (double buffered, V stored transposed). Per tile each wave
+// tiles of 64 (double buffered, both in their natural row layout; the V^T
+// operand is read with the gfx950 LDS transpose read). Per tile each wave
 // computes S^T = K Q^T, so that a lane holds one query's scores and the
 // softmax needs only one cross-lane exchange; exp'd P^T is then directly the
 // B operand of O^T += V^T P^T, and O^T again has one query per lane, so the
@@ -21,13 +22,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int KT = 64;            // keys per LDS tile
 constexpr int QW = 32;            // queries per wave
 constexpr int NWAVE = 8;          // waves per workgroup
 constexpr int QB = QW * NWAVE;    // queries per workgroup
 constexpr int KPAD = 8;           // K tile row padding (bf16)
-constexpr int VPAD = 4;           // V^T tile row padding (bf16)
+constexpr int VPAD = 32;          // V tile row padding (bf16): spreads transpose reads over the banks
 
 __device__ __forceinline__ void region_extent(int r, int D, int w, int s, int &lo, int &hi)
 {
@@ -47,8 +50,21 @@ __device__ __forceinline__ void region_extent(int r, int D, int w, int s, int &l
 template <int DH>
 struct Smem {
     __bf16 k[2][KT][DH + KPAD];
-    __bf16 vt[2][DH][KT + VPAD];
+    __bf16 v[2][KT][DH + VPAD];
 };
+
+// A operand of O^T += V^T P^T from the row-major V tile: lane l gets column
+// (value dim) n_base + l % 32 at keys k_base + 4 (l / 32) + {0..3} and
+// k_base + 8 + 4 (l / 32) + {0..3}, the key order of the P^T fragment.
+template <int LD>
+__device__ __forceinline__ bf16x8 v_frag(const __bf16 *tile, int k_base, int n_base)
+{
+    const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
+    const __bf16 *p = tile + (k_base + 4 * (g >> 1) + (s >> 2)) * LD + n_base + 16 * (g & 1) + 4 * (s & 3);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * LD));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
 {
@@ -116,43 +132,29 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     float mrun = -INFINITY, lrun = 0.f;
     const int ntiles = (m + KT - 1) / KT;
 
-    // Tile loaders: K rows as 16-byte chunks; V as key pairs packed into dwords of V^T.
-    constexpr int KCH = KT * DC;                  // K chunks per tile
+    // Tile loader: K and V rows as 16-byte chunks, natural layout.
+    constexpr int KCH = KT * DC;                  // chunks per tile
     constexpr int KPER = (KCH + 511) / 512;       // per thread
-    constexpr int VPAIRS = KT / 2 * DC;           // (key pair, chunk) units per tile
-    u32x4 kreg[KPER];
-    u32x4 vreg0, vreg1;
+    u32x4 kreg[KPER], vreg[KPER];
     auto fetch = [&](int kt) {
 #pragma unroll
         for (int it = 0; it < KPER; ++it) {
             const int c = tid + 512 * it;
             const int jj = c / DC, dc = c % DC;
             const int kidx = kt * KT + jj;
-            kreg[it] = (c < KCH && kidx < m) ? *(const u32x4 *)(k + head_off + token(kidx) * rowstride + 8 * dc)
-                                             : u32x4{0, 0, 0, 0};
-        }
-        if (tid < VPAIRS) {
-            const int kp = tid % 32, dc = tid / 32;
-            const int k0 = kt * KT + 2 * kp;
-            vreg0 = k0 < m ? *(const u32x4 *)(v + head_off + token(k0) * rowstride + 8 * dc) : u32x4{0, 0, 0, 0};
-            vreg1 = k0 + 1 < m ? *(const u32x4 *)(v + head_off + token(k0 + 1) * rowstride + 8 * dc)
-                               : u32x4{0, 0, 0, 0};
+            const bool ok = c < KCH && kidx < m;
+            const size_t off = ok ? head_off + token(kidx) * rowstride + 8 * dc : 0;
+            kreg[it] = ok ? *(const u32x4 *)(k + off) : u32x4{0, 0, 0, 0};
+            vreg[it] = ok ? *(const u32x4 *)(v + off) : u32x4{0, 0, 0, 0};
         }
     };
     auto stash = [&](int buf) {
 #pragma unroll
         for (int it = 0; it < KPER; ++it) {
             const int c = tid + 512 * it;
-            if (c < KCH) *(u32x4 *)&sm.k[buf][c / DC][8 * (c % DC)] = kreg[it];
-        }
-        if (tid < VPAIRS) {
-            const int kp = tid % 32, dc = tid / 32;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t a0 = vreg0[e], a1 = vreg1[e];
-                // element 2e and 2e+1 of each key's chunk
-                *(uint32_t *)&sm.vt[buf][8 * dc + 2 * e][2 * kp] = (a0 & 0xffffu) | (a1 << 16);
-                *(uint32_t *)&sm.vt[buf][8 * dc + 2 * e + 1][2 * kp] = (a0 >> 16) | (a1 & 0xffff0000u);
+            if (c < KCH) {
+                *(u32x4 *)&sm.k[buf][c / DC][8 * (c % DC)] = kreg[it];
+                *(u32x4 *)&sm.v[buf][c / DC][8 * (c % DC)] = vreg[it];
             }
         }
     };
@@ -172,23 +174,32 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
                     const bf16x8 a = *(const bf16x8 *)&sm.k[cur][32 * sub + col][16 * kb + 8 * half];
                     s[sub] = mfma(a, qf[kb], s[sub]);
                 }
-            // Scale (log2 domain), mask keys past the window, running max.
+            // Keys past the window (only in the last, ragged tile) get -inf.
+            if (kt * KT + KT > m) {
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) {
+                        const int j = kt * KT + 32 * sub + 8 * (rr >> 2) + 4 * half + (rr & 3);
+                        s[sub][rr] = j < m ? s[sub][rr] : -INFINITY;
+                    }
+            }
+            // Running max on raw scores; the scale (log2 units) enters the exponent by one FMA.
             float mloc = -INFINITY;
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int j = kt * KT + 32 * sub + 8 * (rr >> 2) + 4 * half + (rr & 3);
-                    const float val = j < m ? s[sub][rr] * c_log2 : -INFINITY;
-                    s[sub][rr] = val;
-                    mloc = fmaxf(mloc, val);
-                }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            const float mnew = fmaxf(mrun, mloc);
-            const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
-            lrun *= corr;
+                for (int rr = 0; rr < 16; ++rr) mloc = fmaxf(mloc, s[sub][rr]);
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * c_log2;
+            // O and l are rescaled only when some lane's maximum grew.
+            if (!__all(mloc <= mrun)) {
+                const float mnew = fmaxf(mrun, mloc);
+                const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
+                lrun *= corr;
 #pragma unroll
-            for (int i = 0; i < DH / 32; ++i) acc[i] *= corr;
+                for (int i = 0; i < DH / 32; ++i) acc[i] *= corr;
+                mrun = mnew;
+            }
             bf16x8 pf[4];
             float lsum = 0.f;
 #pragma unroll
@@ -197,23 +208,16 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
                 for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj) {
-                        const float p = __builtin_amdgcn_exp2f(s[sub][8 * hb + jj] - mnew);
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][8 * hb + jj], c_log2, -mrun));
                         lsum += p;
                         pf[2 * sub + hb][jj] = (__bf16)p;
                     }
             lrun += lsum;
-            mrun = mnew;
 #pragma unroll
             for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
-                for (int kb2 = 0; kb2 < 4; ++kb2) {
-                    const int kk = 16 * kb2 + 4 * half;
-                    const __bf16 *row = &sm.vt[cur][32 * dt + col][0];
-                    const bf16x4 lo = *(const bf16x4 *)(row + kk);
-                    const bf16x4 hi = *(const bf16x4 *)(row + kk + 8);
-                    const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    acc[dt] = mfma(a, pf[kb2], acc[dt]);
-                }
+                for (int kb2 = 0; kb2 < 4; ++kb2)
+                    acc[dt] = mfma(v_frag<DH + VPAD>(&sm.v[cur][0][0], 16 * kb2, 32 * dt), pf[kb2], acc[dt]);
         }
         if (kt + 1 < ntiles) stash(cur ^ 1);
         __syncthreads();
