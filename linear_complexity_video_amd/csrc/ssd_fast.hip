@@ -2,7 +2,8 @@
 //
 // Same chunked (state space duality) evaluation as the portable path, with
 // the chunk states kept on chip. The sequence of each head is cut into
-// segments of whole chunks; a workgroup (4 waves) owns one (head, segment):
+// segments of whole chunks; a workgroup of Q/16 waves (two per SIMD at
+// Q = 128) owns one (head, segment):
 //
 //  1. states   sweeps its segment right to left, carrying the backward state
 //              G in MFMA accumulators. Before adding chunk c it stores G (the
@@ -12,19 +13,17 @@
 //              The review tokens form one extra segment whose G and F are the
 //              initial states of the two directions.
 //  2. seg pass turns summaries into the true states at every segment border.
-//  3. cb       C_t . B_u for every chunk (fp16, diagonal also in fp32; shared by
-//              all heads of a group).
+//  3. cb       C_t . B_u (fp16) for every chunk (shared by all heads of a group).
 //  4. out      sweeps its segment left to right carrying the forward state Hf
 //              and computes, per chunk,
 //                 Y^T = X^T M^T + ef * (Hf C^T) + eb * (Hb C^T)
-//              with M the bidirectional intra-chunk matrix without its
-//              diagonal (decays below and above it), ef = exp(cs),
-//              eb = exp(tot - ce) applied per token to the accumulators,
-//              Hb = stored G + decay * border state; the diagonal term
-//              (2 C_t.B_t dt_t + 2D) x_t is added in fp32 when Y is stored.
-//              X^T M^T runs on fp16 MFMA (x is converted exactly, M rounded
-//              to fp16): its weights carry the largest values of the scan and
-//              fp16 keeps 3 more mantissa bits than bf16.
+//              with M the dense bidirectional intra-chunk matrix (decays below
+//              and above the diagonal, 2 C.B dt + 2D on it), ef = exp(cs),
+//              eb = exp(tot - ce) applied per token to the accumulators, and
+//              Hb = stored G + decay * border state. X^T M^T runs on fp16
+//              MFMA (x is converted exactly, M rounded to fp16): its weights
+//              are the largest values of the scan and fp16 keeps 3 more
+//              mantissa bits than bf16.
 //              Then Hf = exp(tot) Hf + sum_u exp(tot - cs_u) dt_u x_u B_u^T.
 //
 // Data layout on chip: x and B chunks are staged in LDS in their natural
@@ -132,7 +131,7 @@ __device__ __forceinline__ bf16x8 frag_rm(const __bf16 *tile, int ld, int m_base
 // Row u of the chunk is read from global row srow[u] (an LDS table of the
 // chunk's rows; ~0u marks a position past the end, which reads as zero).
 // Loads are unconditional (an invalid row reads row 0 and is then zeroed).
-template <int Q, int COLS>
+template <int Q, int COLS, int NT>
 struct Rows {
     static constexpr int UPR = COLS / 8;
     static constexpr int PER = Q * UPR / NT;
@@ -203,16 +202,20 @@ __global__ __launch_bounds__(256) void k_perm(uint32_t *__restrict__ perm, uint3
 // grid = 8 * ceil(batch * nseg * nheads / 8); item = (b * nseg + seg) * nheads + h.
 // ---------------------------------------------------------------------------
 template <int S, int Q>
-__global__ __launch_bounds__(NT) void k_states(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
-                                               const uint32_t *__restrict__ perm, const float *__restrict__ dtT,
-                                               const float *__restrict__ csT, const float *__restrict__ A,
-                                               __bf16 *__restrict__ hb_local, float *__restrict__ delta,
-                                               float *__restrict__ segF, float *__restrict__ segB,
-                                               float *__restrict__ segA, int nheads, int G, uint32_t L,
-                                               uint32_t Lpad, int nch, int segch, int nseg, int seg_base,
-                                               int nseg_total, uint32_t total_items)
+__global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
+                                                  const uint32_t *__restrict__ perm, const float *__restrict__ dtT,
+                                                  const float *__restrict__ csT, const float *__restrict__ A,
+                                                  __bf16 *__restrict__ hb_local, float *__restrict__ delta,
+                                                  float *__restrict__ segF, float *__restrict__ segB,
+                                                  float *__restrict__ segA, int nheads, int G, uint32_t L,
+                                                  uint32_t Lpad, int nch, int segch, int nseg, int seg_base,
+                                                  int nseg_total, uint32_t total_items)
 {
+    constexpr int NT = Q * 4, NW = Q / 16;          // Q/16 waves, two per SIMD at Q = 128
     constexpr int LX = P + XPAD, LB = S + XPAD;
+    // Output tiles G^T and F^T (S/32 x 2 each) over NW/2 waves per matrix.
+    constexpr int TPW = 2 * S / Q;
+    constexpr int PBW = TPW >= 2 ? 2 : 1, SBW = TPW >= 2 ? TPW / 2 : 1;
     __shared__ __bf16 xb[Q * LX];   // x * dt exp(ce)              (backward weights)
     __shared__ __bf16 xf[Q * LX];   // x * dt exp(tot - cs + logD) (forward weights)
     __shared__ __bf16 bn[Q * LB];   // B
@@ -228,102 +231,118 @@ __global__ __launch_bounds__(NT) void k_states(const __bf16 *__restrict__ x, con
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool isF = wave >= 2;            // waves 0-1: backward state G^T; 2-3: forward sum F^T
-    constexpr int SBW = S / 64;            // s-blocks per wave
-    const int sb0 = (wave & 1) * SBW;
+    const bool isF = wave >= NW / 2;       // first half of the waves: backward state G^T; second: forward sum F^T
+    const int wg = wave % (NW / 2);
+    const int sb0 = PBW == 2 ? wg * SBW : wg >> 1;
+    const int pb0 = PBW == 2 ? 0 : (wg & 1);
     const bool row_thread = wave < Q / 64; // tid < Q: owns one row-table entry
-    f32x16 acc[SBW][2];
+    f32x16 acc[SBW][PBW];
 #pragma unroll
-    for (int i = 0; i < SBW; ++i) acc[i][0] = acc[i][1] = f32x16{};
+    for (int i = 0; i < SBW; ++i)
+#pragma unroll
+        for (int j = 0; j < PBW; ++j) acc[i][j] = f32x16{};
 
     const float a = A[h];
     const size_t bh = (size_t)b * nheads + h;
     const size_t drow = bh * Lpad;
-    Rows<Q, P> xr;
-    Rows<Q, S> br;
-    float wd[Rows<Q, P>::PER], wc[Rows<Q, P>::PER];
-    float tot = 0.f;
+    // Chunk data is fetched two chunks ahead into two alternating register stages.
+    struct Stage {
+        Rows<Q, P, NT> xr;
+        Rows<Q, S, NT> br;
+        float wd[Rows<Q, P, NT>::PER], wc[Rows<Q, P, NT>::PER];
+        float tot;
+    };
+    Stage st0, st1;
     uint32_t pnext = ~0u;  // row-table entry of the chunk after the one being fetched
-    auto fetch = [&](int c) {
-        xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
-        br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * L);
+    auto fetch = [&](Stage &stg, int c) {
+        stg.xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
+        stg.br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * L);
 #pragma unroll
-        for (int it = 0; it < xr.PER; ++it) {
-            const size_t i = drow + (size_t)c * Q + xr.row_of(it);
-            wd[it] = dtT[i];
-            wc[it] = csT[i];
+        for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) {
+            const size_t i = drow + (size_t)c * Q + Rows<Q, P, NT>::row_of(it);
+            stg.wd[it] = dtT[i];
+            stg.wc[it] = csT[i];
         }
-        tot = csT[drow + (size_t)c * Q + Q - 1];
+        stg.tot = csT[drow + (size_t)c * Q + Q - 1];
         if (row_thread) pnext = c > c_lo ? seq_row(perm, (uint32_t)(c - 1) * Q + tid, L) : ~0u;
     };
+    // Prologue: rows and data of the two rightmost chunks.
     if (row_thread) s_row[tid] = seq_row(perm, (uint32_t)(c_hi - 1) * Q + tid, L);
     __syncthreads();
-    fetch(c_hi - 1);
+    fetch(st0, c_hi - 1);
+    __syncthreads();
+    if (row_thread) s_row[tid] = pnext;
+    __syncthreads();
+    if (c_hi - 2 >= c_lo) fetch(st1, c_hi - 2);
     float logD = 0.f;  // sum of dt*A over the chunks right of the current one
 
-    for (int c = c_hi - 1; c >= c_lo; --c) {
+    auto step = [&](Stage &cur, int c) {
         // Backward state entering chunk c from the right.
         if (hb_local && !isF) {
             __bf16 *dst = hb_local + (bh * nch + c) * (size_t)(P * S);
 #pragma unroll
             for (int i = 0; i < SBW; ++i)
 #pragma unroll
-                for (int pb = 0; pb < 2; ++pb)
+                for (int pb = 0; pb < PBW; ++pb)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
                         bf16x4 v4;
 #pragma unroll
                         for (int j = 0; j < 4; ++j) v4[j] = (__bf16)acc[i][pb][4 * g4 + j];
-                        *(bf16x4 *)(dst + (32 * pb + col) * S + 32 * (sb0 + i) + 8 * g4 + 4 * half) = v4;
+                        *(bf16x4 *)(dst + (32 * (pb0 + pb) + col) * S + 32 * (sb0 + i) + 8 * g4 + 4 * half) = v4;
                     }
         }
         if (delta && tid == 0) delta[bh * nch + c] = ex2(logD * LOG2E);
 
-        __syncthreads();  // previous chunk's MFMA reads of LDS and this chunk's row-table reads are done
+        __syncthreads();  // previous chunk's MFMA reads of LDS and the row-table reads are done
+        const float tot_c = cur.tot;
 #pragma unroll
-        for (int it = 0; it < xr.PER; ++it) {
-            xr.template store_scaled<LX>(xb, it, wd[it] * ex2((wc[it] - wd[it] * a) * LOG2E));
-            xr.template store_scaled<LX>(xf, it, wd[it] * ex2((tot - wc[it] + logD) * LOG2E));
+        for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) {
+            const float d = cur.wd[it], cs = cur.wc[it];
+            cur.xr.template store_scaled<LX>(xb, it, d * ex2((cs - d * a) * LOG2E));
+            cur.xr.template store_scaled<LX>(xf, it, d * ex2((tot_c - cs + logD) * LOG2E));
         }
-        br.template store<LB>(bn);
+        cur.br.template store<LB>(bn);
         if (row_thread) s_row[tid] = pnext;
         __syncthreads();
 
-        const float tot_c = tot;
-        if (c > c_lo) fetch(c - 1);
+        if (c - 2 >= c_lo) fetch(cur, c - 2);
         if (!isF) {
             const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
-            for (int i = 0; i < SBW; ++i) {
-                acc[i][0] *= dec;
-                acc[i][1] *= dec;
-            }
+            for (int i = 0; i < SBW; ++i)
+#pragma unroll
+                for (int j = 0; j < PBW; ++j) acc[i][j] *= dec;
         }
         const __bf16 *xs = isF ? xf : xb;
 #pragma unroll
         for (int kb = 0; kb < Q / 16; ++kb) {
-            bf16x8 af[SBW], bfr[2];
+            bf16x8 af[SBW], bfr[PBW];
 #pragma unroll
             for (int i = 0; i < SBW; ++i) af[i] = frag_tr(bn, LB, 16 * kb, 32 * (sb0 + i));
 #pragma unroll
-            for (int pb = 0; pb < 2; ++pb) bfr[pb] = frag_tr(xs, LX, 16 * kb, 32 * pb);
+            for (int pb = 0; pb < PBW; ++pb) bfr[pb] = frag_tr(xs, LX, 16 * kb, 32 * (pb0 + pb));
 #pragma unroll
             for (int i = 0; i < SBW; ++i)
 #pragma unroll
-                for (int pb = 0; pb < 2; ++pb) acc[i][pb] = mfma(af[i], bfr[pb], acc[i][pb]);
+                for (int pb = 0; pb < PBW; ++pb) acc[i][pb] = mfma(af[i], bfr[pb], acc[i][pb]);
         }
         logD += tot_c;
+    };
+    for (int c = c_hi - 1; c >= c_lo; c -= 2) {
+        step(st0, c);
+        if (c - 1 >= c_lo) step(st1, c - 1);
     }
 
     float *dst = (isF ? segF : segB) + (bh * nseg_total + seg_base + seg) * (size_t)(P * S);
 #pragma unroll
     for (int i = 0; i < SBW; ++i)
 #pragma unroll
-        for (int pb = 0; pb < 2; ++pb)
+        for (int pb = 0; pb < PBW; ++pb)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 f32x4 v4 = {acc[i][pb][4 * g4], acc[i][pb][4 * g4 + 1], acc[i][pb][4 * g4 + 2], acc[i][pb][4 * g4 + 3]};
-                *(f32x4 *)(dst + (32 * pb + col) * S + 32 * (sb0 + i) + 8 * g4 + 4 * half) = v4;
+                *(f32x4 *)(dst + (32 * (pb0 + pb) + col) * S + 32 * (sb0 + i) + 8 * g4 + 4 * half) = v4;
             }
     if (tid == 0) segA[bh * nseg_total + seg_base + seg] = logD;
 }
@@ -355,14 +374,13 @@ __global__ __launch_bounds__(256) void k_seg_pass(const float *__restrict__ segF
 }
 
 // ---------------------------------------------------------------------------
-// 3. CB[t][u] = C_t . B_u per chunk and group: fp16 matrix plus its diagonal
-// in fp32. grid (nch, G, batch). Computed as CB^T = B C^T so each lane holds
+// 3. CB[t][u] = C_t . B_u per chunk and group (fp16). grid (nch, G, batch). Computed as CB^T = B C^T so each lane holds
 // 4 consecutive u of one t.
 // ---------------------------------------------------------------------------
 template <int S, int Q>
 __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
-                                           const uint32_t *__restrict__ perm, _Float16 *__restrict__ cb,
-                                           float *__restrict__ cbd, int G, uint32_t L)
+                                           const uint32_t *__restrict__ perm, _Float16 *__restrict__ cb, int G,
+                                           uint32_t L)
 {
     const uint32_t c = blockIdx.x;
     const int g = blockIdx.y, b = blockIdx.z;
@@ -396,10 +414,7 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
         for (int g4 = 0; g4 < 4; ++g4) {
             f16x4 v4;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v4[j] = (_Float16)acc[4 * g4 + j];
-                if (ub == tb && 8 * g4 + 4 * half + j == col) cbd[chunk * Q + t] = acc[4 * g4 + j];
-            }
+            for (int j = 0; j < 4; ++j) v4[j] = (_Float16)acc[4 * g4 + j];
             *(f16x4 *)(out + (size_t)t * Q + 32 * ub + 8 * g4 + 4 * half) = v4;
         }
     }
@@ -409,9 +424,9 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
 // 4. Left-to-right output sweep. Same grid/items as k_states (main segments).
 // ---------------------------------------------------------------------------
 template <int S, int Q>
-__global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
+__global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
                                             const __bf16 *__restrict__ Cm, const _Float16 *__restrict__ cb,
-                                            const float *__restrict__ cbd, const uint32_t *__restrict__ perm,
+                                            const uint32_t *__restrict__ perm,
                                             const float *__restrict__ dtT, const float *__restrict__ csT,
                                             const float *__restrict__ A, const float *__restrict__ Dv,
                                             const __bf16 *__restrict__ hb_local, const float *__restrict__ delta,
@@ -419,6 +434,7 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
                                             __bf16 *__restrict__ y, int nheads, int G, uint32_t N, uint32_t Lpad,
                                             int nch, int segch, int nseg, uint32_t total_items)
 {
+    constexpr int NT = Q * 4, NW = Q / 16;  // Q/16 waves, two per SIMD at Q = 128
     constexpr int LX = P + XPAD, LB = S + XPAD, SS = S + 8;
     __shared__ __bf16 xn[Q * LX];    // x, converted to fp16 (operand of the fp16 intra-chunk product)
     __shared__ __bf16 xf[Q * LX];    // x * dt exp(tot - cs)
@@ -426,7 +442,8 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
     __shared__ __bf16 hfl[P * SS];   // forward state entering the chunk, [p][s]
     __shared__ __bf16 hbl[P * SS];   // backward state entering the chunk from the right, [p][s]
     // per token: cs, ce (log2 units), dt, and the split decay factors of the off-diagonal blocks
-    __shared__ __attribute__((aligned(16))) float s_cs[Q], s_ce[Q], s_dt[Q], s_gl[Q], s_gu[Q];
+    __shared__ __attribute__((aligned(16))) float s_cs[Q], s_ce[Q], s_dt[Q];
+    __shared__ __attribute__((aligned(16))) _Float16 s_gl[Q], s_gu[Q];
     __shared__ uint32_t s_row[Q];    // global rows: of chunk c at the top of iteration c, then of chunk c+1
 
     const uint32_t item = xcd_item();
@@ -442,21 +459,23 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool row_thread = wave < Q / 64;  // tid < Q
-    // Y^T tiles: Q = 128 -> t-block = wave, p-blocks 0 and 1; Q = 64 -> t-block wave / 2, p-block wave % 2.
-    constexpr int YT = Q / 64;
-    const int tb = Q == 128 ? wave : wave >> 1;
-    const int pb0 = Q == 128 ? 0 : (wave & 1);
-    // Hf^T tiles: S = 128 -> s-block = wave, p-blocks 0 and 1; S = 64 -> s-block wave / 2, p-block wave % 2.
-    constexpr int HT = S / 64;
-    const int hsb = S == 128 ? wave : wave >> 1;
-    const int hpb0 = S == 128 ? 0 : (wave & 1);
-
+    // One Y^T tile per wave: t-block wave / 2, p-block wave % 2.
+    const int tb = wave >> 1, pb = wave & 1;
+    // Hf^T tiles (S/32 s-blocks x 2 p-blocks) over the waves: HT per wave, or one
+    // tile for the first S/16 waves when there are fewer tiles than waves.
+    constexpr int HTILES = S / 16;
+    constexpr int HT = HTILES >= NW ? HTILES / NW : 1;
+    const bool hact = wave < HTILES;
+    const int hsb = (wave * HT) >> 1;
+    const int hpb0 = (wave * HT) & 1;
     const float a = A[h];
     const float twoD = 2.f * Dv[h];
     constexpr int PS = P * S;
 
     f32x16 hacc[HT];
-    {
+#pragma unroll
+    for (int i = 0; i < HT; ++i) hacc[i] = f32x16{};
+    if (hact) {
         const float *src = hinF + (bh * nseg + seg) * (size_t)PS;
 #pragma unroll
         for (int i = 0; i < HT; ++i)
@@ -476,14 +495,14 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
         for (int it = 0; it < HBC; ++it) hinb[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
     }
 
-    Rows<Q, P> xr;
-    Rows<Q, S> br;
+    Rows<Q, P, NT> xr;
+    Rows<Q, S, NT> br;
     const size_t cb_base = ((size_t)b * G + g) * nch;
     const int t_tok = 32 * tb + col;  // this lane's token inside the chunk (Y^T column)
 
     // Data staged through LDS, fetched one chunk ahead.
     u32x4 hbr[HBC];
-    float wd[Rows<Q, P>::PER], wc[Rows<Q, P>::PER];
+    float wd[Rows<Q, P, NT>::PER], wc[Rows<Q, P, NT>::PER];
     float tok_d = 0.f, tok_c = 0.f, blk_cs_end = 0.f, blk_cs0 = 0.f, blk_dt0 = 0.f, tot = 0.f, dl = 0.f;
     uint32_t pnext = ~0u;
     auto fetch = [&](int c) {
@@ -515,23 +534,10 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
     fetch(c_lo);
 
     for (int c = c_lo; c < c_hi; ++c) {
-        // C row, CB row and CB diagonal of this lane's token (MFMA fragments of the Y phase).
+        // Row of this lane's token (Y^T column); read before the table moves on to chunk c + 1.
         const uint32_t rt = s_row[t_tok];
         const bool tvalid = rt != ~0u;
         const size_t trow = (size_t)b * N + (tvalid ? rt : 0u);
-        u32x4 cfr[S / 16], cbf[Q / 16];
-        {
-            const __bf16 *crow = Cm + trow * ((size_t)G * S) + (size_t)g * S;
-#pragma unroll
-            for (int kb = 0; kb < S / 16; ++kb) {
-                const u32x4 v = *(const u32x4 *)(crow + 16 * kb + 8 * half);
-                cfr[kb] = tvalid ? v : u32x4{0, 0, 0, 0};
-            }
-            const _Float16 *cbrow = cb + (cb_base + c) * (size_t)(Q * Q) + (size_t)t_tok * Q;
-#pragma unroll
-            for (int kb = 0; kb < Q / 16; ++kb) cbf[kb] = *(const u32x4 *)(cbrow + 16 * kb + 8 * half);
-        }
-        const float cb_tt = cbd[(cb_base + c) * Q + t_tok];
 
         __syncthreads();  // previous chunk's LDS reads (and this chunk's row-table reads) are done
         // ---- LDS writes ----
@@ -540,15 +546,17 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
         for (int it = 0; it < xr.PER; ++it)
             xr.template store_scaled<LX>(xf, it, wd[it] * ex2((tot - wc[it]) * LOG2E));
         br.template store<LB>(bn);
+        if (hact) {
 #pragma unroll
-        for (int i = 0; i < HT; ++i)
+            for (int i = 0; i < HT; ++i)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                bf16x4 v4;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    bf16x4 v4;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v4[j] = (__bf16)hacc[i][4 * g4 + j];
-                *(bf16x4 *)&hfl[(32 * (hpb0 + i) + col) * SS + 32 * hsb + 8 * g4 + 4 * half] = v4;
-            }
+                    for (int j = 0; j < 4; ++j) v4[j] = (__bf16)hacc[i][4 * g4 + j];
+                    *(bf16x4 *)&hfl[(32 * (hpb0 + i) + col) * SS + 32 * hsb + 8 * g4 + 4 * half] = v4;
+                }
+        }
 #pragma unroll
         for (int it = 0; it < HBC; ++it) {
             const int k = tid + NT * it;
@@ -565,8 +573,8 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
             s_cs[tid] = cs2;
             s_ce[tid] = ce2;
             // below-diagonal blocks: exp(cs_end - cs_u); above: exp(ce_u - ce_start); both <= 1
-            s_gl[tid] = tok_d * ex2(blk_cs_end * LOG2E - cs2);
-            s_gu[tid] = tok_d * ex2(ce2 - (blk_cs0 - blk_dt0 * a) * LOG2E);
+            s_gl[tid] = (_Float16)(tok_d * ex2(blk_cs_end * LOG2E - cs2));
+            s_gu[tid] = (_Float16)(tok_d * ex2(ce2 - (blk_cs0 - blk_dt0 * a) * LOG2E));
             s_row[tid] = pnext;
         }
         __syncthreads();
@@ -574,8 +582,24 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
         const float tot_c = tot;
         if (c + 1 < c_hi) fetch(c + 1);
 
-        // ---- Hf = exp(tot) Hf + B^T-weighted x (as Hf^T = B^T xf^T); LDS operands only ----
+        // CB row of this lane's token (first 32-column block now, the rest one block
+        // ahead inside the intra loop) and its C row.
+        const _Float16 *cbrow = cb + (cb_base + c) * (size_t)(Q * Q) + (size_t)t_tok * Q;
+        u32x4 cb_cur[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) cb_cur[kk] = *(const u32x4 *)(cbrow + 16 * kk + 8 * half);
+        u32x4 cfr[S / 16];
         {
+            const __bf16 *crow = Cm + trow * ((size_t)G * S) + (size_t)g * S;
+#pragma unroll
+            for (int kb = 0; kb < S / 16; ++kb) {
+                const u32x4 v = *(const u32x4 *)(crow + 16 * kb + 8 * half);
+                cfr[kb] = tvalid ? v : u32x4{0, 0, 0, 0};
+            }
+        }
+
+        // ---- Hf = exp(tot) Hf + B^T-weighted x (as Hf^T = B^T xf^T); LDS operands only ----
+        if (hact) {
             const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
             for (int i = 0; i < HT; ++i) hacc[i] *= dec;
@@ -588,82 +612,74 @@ __global__ __launch_bounds__(NT) void k_out(const __bf16 *__restrict__ x, const 
         }
 
         const float cs_t = s_cs[t_tok], ce_t = s_ce[t_tok], dt_t = s_dt[t_tok];
-        // ---- forward inter-chunk term: ef * (Hf C^T) ----
-        f32x16 yacc[YT], yb[YT];
-#pragma unroll
-        for (int i = 0; i < YT; ++i) yacc[i] = yb[i] = f32x16{};
-#pragma unroll
-        for (int kb = 0; kb < S / 16; ++kb)
-#pragma unroll
-            for (int i = 0; i < YT; ++i)
-                yacc[i] = mfma(frag_rm(hfl, SS, 32 * (pb0 + i), 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yacc[i]);
-        {
-            const float ef = ex2(cs_t);
-#pragma unroll
-            for (int i = 0; i < YT; ++i) yacc[i] *= ef;
-        }
-        // ---- intra-chunk term X^T M^T (diagonal of M excluded: added in fp32 below) ----
-#pragma unroll
+        f32x16 yacc = f32x16{}, yb = f32x16{};
+        // ---- intra-chunk term X^T M^T ----
+#pragma unroll 1
         for (int U = 0; U < Q / 32; ++U) {
+            u32x4 cb_nxt[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                cb_nxt[kk] = U + 1 < Q / 32 ? *(const u32x4 *)(cbrow + 32 * (U + 1) + 16 * kk + 8 * half) : cb_cur[kk];
+            const bool diag_blk = U == tb;
+            const bool below = U < tb;
+            const float f = below ? ex2(cs_t - s_cs[32 * U + 31]) : ex2(s_ce[32 * U] - ce_t);
+            const _Float16 *gw = below ? s_gl : s_gu;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int kb = 2 * U + kk, u0 = 16 * kb + 8 * half;
                 f16x8 mf;
-                if (U == tb) {
+                if (diag_blk) {
                     const f32x4 d0 = *(const f32x4 *)(s_dt + u0), d1 = *(const f32x4 *)(s_dt + u0 + 4);
                     const f32x4 c0 = *(const f32x4 *)(s_cs + u0), c1 = *(const f32x4 *)(s_cs + u0 + 4);
                     const f32x4 e0 = *(const f32x4 *)(s_ce + u0), e1 = *(const f32x4 *)(s_ce + u0 + 4);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int u = u0 + j;
-                        const float cbv = (j & 1) ? h_hi(cbf[kb][j >> 1]) : h_lo(cbf[kb][j >> 1]);
+                        const float cbv = (j & 1) ? h_hi(cb_cur[kk][j >> 1]) : h_lo(cb_cur[kk][j >> 1]);
                         const float dtu = j < 4 ? d0[j] : d1[j - 4];
                         const float csu = j < 4 ? c0[j] : c1[j - 4];
                         const float ceu = j < 4 ? e0[j] : e1[j - 4];
-                        const float m = cbv * dtu * ex2(u < t_tok ? cs_t - csu : ceu - ce_t);
-                        mf[j] = (_Float16)(u == t_tok ? 0.f : m);
+                        // the decay exponent of the right direction is the non-positive one
+                        const float m = cbv * dtu * ex2(fminf(cs_t - csu, ceu - ce_t));
+                        mf[j] = (_Float16)(u == t_tok ? 2.f * cbv * dt_t + twoD : m);
                     }
                 } else {
-                    const bool below = U < tb;
-                    const float f = below ? ex2(cs_t - s_cs[32 * U + 31]) : ex2(s_ce[32 * U] - ce_t);
-                    const float *gw = below ? s_gl : s_gu;
-                    const f32x4 g0 = *(const f32x4 *)(gw + u0), g1 = *(const f32x4 *)(gw + u0 + 4);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float cbv = (j & 1) ? h_hi(cbf[kb][j >> 1]) : h_lo(cbf[kb][j >> 1]);
-                        mf[j] = (_Float16)(cbv * (j < 4 ? g0[j] : g1[j - 4]) * f);
-                    }
+                    // packed fp16: CB * (g_u * f)
+                    const f16x8 g8 = *(const f16x8 *)(gw + u0);
+                    const _Float16 fh = (_Float16)f;
+                    mf = __builtin_bit_cast(f16x8, cb_cur[kk]) * (g8 * fh);
                 }
-#pragma unroll
-                for (int i = 0; i < YT; ++i)
-                    yacc[i] = mfma16(__builtin_bit_cast(f16x8, frag_tr(xn, LX, 16 * kb, 32 * (pb0 + i))), mf, yacc[i]);
+                yacc = mfma16(__builtin_bit_cast(f16x8, frag_tr(xn, LX, 16 * kb, 32 * pb)), mf, yacc);
             }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) cb_cur[kk] = cb_nxt[kk];
         }
+        // ---- forward inter-chunk term: ef * (Hf C^T) ----
+#pragma unroll
+        for (int kb = 0; kb < S / 16; ++kb)
+            yb = mfma(frag_rm(hfl, SS, 32 * pb, 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb);
+        {
+            const float ef = ex2(cs_t);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) yacc[j] += ef * yb[j];
+        }
+        yb = f32x16{};
         // ---- backward inter-chunk term: eb * (Hb C^T) ----
 #pragma unroll
         for (int kb = 0; kb < S / 16; ++kb)
-#pragma unroll
-            for (int i = 0; i < YT; ++i)
-                yb[i] = mfma(frag_rm(hbl, SS, 32 * (pb0 + i), 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb[i]);
+            yb = mfma(frag_rm(hbl, SS, 32 * pb, 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb);
 
-        // ---- store Y = acc + eb * yb + (2 C_t.B_t dt_t + 2D) x_t (lane: token t_tok, 4 consecutive p per group) ----
-        {
+        // ---- store Y = acc + eb * yb (lane: token t_tok, 4 consecutive p per group) ----
+        if (tvalid) {
             const float eb = ex2(tot_c * LOG2E - ce_t);
-            const float diag = 2.f * cb_tt * dt_t + twoD;
             __bf16 *yrow = y + (trow * nheads + h) * P;
 #pragma unroll
-            for (int i = 0; i < YT; ++i)
+            for (int g4 = 0; g4 < 4; ++g4) {
+                bf16x4 v4;
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int p0 = 32 * (pb0 + i) + 8 * g4 + 4 * half;
-                    const uint2 xv = *(const uint2 *)&xn[t_tok * LX + p0];
-                    const float xs[4] = {h_lo(xv.x), h_hi(xv.x), h_lo(xv.y), h_hi(xv.y)};
-                    bf16x4 v4;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        v4[j] = (__bf16)(yacc[i][4 * g4 + j] + eb * yb[i][4 * g4 + j] + diag * xs[j]);
-                    if (tvalid) *(bf16x4 *)(yrow + p0) = v4;
-                }
+                for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(yacc[4 * g4 + j] + eb * yb[4 * g4 + j]);
+                *(bf16x4 *)(yrow + 32 * pb + 8 * g4 + 4 * half) = v4;
+            }
         }
     }
 }
@@ -672,7 +688,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
     int nseg, segch, nsegT;
-    size_t perm, dtT, csT, cb, cbd, hbl, delta, segF, segB, segA, hinF, hinB, rx, rB, rdt, rdtT, rcsT, total;
+    size_t perm, dtT, csT, cb, hbl, delta, segF, segB, segA, hinF, hinB, rx, rB, rdt, rdtT, rcsT, total;
 };
 
 Plan make_plan(const SsdProblem &p)
@@ -693,7 +709,6 @@ Plan make_plan(const SsdProblem &p)
     pl.dtT = take(B * Hs * Lpad * 4);
     pl.csT = take(B * Hs * Lpad * 4);
     pl.cb = take(B * p.ngroups * p.nch * Q * Q * 2);
-    pl.cbd = take(B * p.ngroups * p.nch * Q * 4);
     pl.hbl = take(B * Hs * p.nch * PS * 2);
     pl.delta = take(B * Hs * p.nch * 4);
     pl.segF = take(B * Hs * pl.nsegT * PS * 4);
@@ -723,7 +738,6 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
     uint32_t *perm = (uint32_t *)(w + pl.perm);
     float *dtT = (float *)(w + pl.dtT), *csT = (float *)(w + pl.csT);
     _Float16 *cb = (_Float16 *)(w + pl.cb);
-    float *cbd = (float *)(w + pl.cbd);
     __bf16 *hbl = (__bf16 *)(w + pl.hbl);
     float *delta = (float *)(w + pl.delta), *segF = (float *)(w + pl.segF), *segB = (float *)(w + pl.segB);
     float *segA = (float *)(w + pl.segA), *hinF = (float *)(w + pl.hinF);
@@ -747,20 +761,20 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
         ssd::k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, Bn), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad,
                                                                                 Q, 0, 1, 1, R);
         const uint64_t items = (uint64_t)Bn * Hs;
-        k_states<S, Q><<<grid_of(items), NT, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, rdtT, rcsT,
+        k_states<S, Q><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, rdtT, rcsT,
                                                       a.a, nullptr, nullptr, segF, segB, segA, Hs, G, R, Rpad,
                                                       p.nchR, p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)items);
     }
     k_perm<<<(N + 255) / 256, 256, 0, st>>>(perm, N, p.order, T, H, W);
     ssd::k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, Bn), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q,
                                                                          p.order, T, H, W);
-    k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, cbd, G, N);
+    k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, G, N);
     const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
-    k_states<S, Q><<<grid_of(items), NT, 0, st>>>(x, Bm, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
+    k_states<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
                                                   N, Lpad, p.nch, pl.segch, pl.nseg, 0, pl.nsegT, (uint32_t)items);
     k_seg_pass<<<dim3((P * S + 255) / 256, Hs, Bn), 256, 0, st>>>(segF, segB, segA, hinF, hinB, P * S, pl.nseg,
                                                                   pl.nsegT, p.R > 0 ? 1 : 0);
-    k_out<S, Q><<<grid_of(items), NT, 0, st>>>(x, Bm, Cm, cb, cbd, perm, dtT, csT, a.a, a.d, hbl, delta, hinF, hinB,
+    k_out<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, Cm, cb, perm, dtT, csT, a.a, a.d, hbl, delta, hinF, hinB,
                                                (__bf16 *)a.y, Hs, G, N, Lpad, p.nch, pl.segch, pl.nseg,
                                                (uint32_t)items);
     return hipGetLastError();
