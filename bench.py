@@ -27,6 +27,7 @@ METRIC = "MATE-core tokens/sec (bi-SSD + TESA fwd) at 1 GPU; % MFMA / HBM roofli
 PEAK_BF16_TFLOPS = 2500.0   # dense MFMA, MI355X
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 1 << 30
 
 
 def log(msg):
@@ -58,9 +59,41 @@ def work(wl):
     ssd_flops = 2.0 * (Hs * (4 * P * S + P * (Q + 1)) + G * S * (Q + 1)) * scanned
     ssd_bytes = (2 * Hs * P * e + 2 * G * S * e + 4 * Hs) * wl.N
     tesa_bytes = 4 * wl.t_heads * wl.t_dim * e * wl.N
-    tesa_flops = {sh: 4.0 * wl.t_dim * wl.t_heads * tesa_pairs(wl, wl.layer_shift(sh)) for sh in (False, True)}
-    return dict(ssd_flops=ssd_flops, ssd_bytes=ssd_bytes, tesa_flops=tesa_flops, tesa_bytes=tesa_bytes,
-                reorder_bytes=2 * wl.N * Hs * P * e)
+    tesa_flops = {sh: 4.0 * wl.t_dim * wl.t_heads * tesa_pairs(wl, wl.layer_shift(sh)) * wl.batch
+                  for sh in (False, True)}
+    # The output sweep (one launch per scan) runs over the N main tokens: the intra-chunk product (both
+    # triangles and the diagonal), the forward state update and both inter-chunk read-outs; it reads x, B, C,
+    # dt once and writes y once, i.e. all of the scan's algorithmic bytes.
+    out_flops = 2.0 * Hs * (3 * P * S + P * (Q + 1)) * wl.N * wl.batch
+    out_bytes = ssd_bytes * wl.batch
+    return dict(ssd_flops=ssd_flops * wl.batch, ssd_bytes=ssd_bytes * wl.batch, tesa_flops=tesa_flops,
+                tesa_bytes=tesa_bytes * wl.batch, reorder_bytes=2 * wl.N * Hs * P * e * wl.batch,
+                out_flops=out_flops, out_bytes=out_bytes)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ssd_out_long_grid_traffic.txt")
+OUT_KERNEL_SOURCE = os.path.join(ROOT, "linear_complexity_video_amd", "csrc", "ssd_fast.hip")
+
+
+def measured_traffic(wl):
+    """HBM bytes per output-sweep launch from the committed rocprofv3 counter summary, scaled by the copy-kernel
+    calibration recorded with it; None when there is none for this workload or the kernel source changed since."""
+    import hashlib
+
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    digest = hashlib.sha256(open(OUT_KERNEL_SOURCE, "rb").read()).hexdigest()
+    if kv.get("source_sha256") != digest or kv.get("workload") != wl.name:
+        return None
+    copy_kib = float(kv["copy_bytes"]) / 1024.0
+    fetch = float(kv["fetch_kib_per_dispatch"]) * copy_kib / float(kv["copy_fetch_kib"])
+    write = float(kv["write_kib_per_dispatch"]) * copy_kib / float(kv["copy_write_kib"])
+    return (fetch + write) * 1024.0
 
 
 # ---------------------------------------------------------------------------
@@ -116,6 +149,8 @@ def main():
     ap.add_argument("--algo", choices=("auto", "portable", "fast"), default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed repetitions of each single call")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="finish with a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -173,16 +208,22 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
 
+    # Timed region: the output sweep of the scan (the dominant kernel) is bracketed by HIP events on the
+    # stream it runs on, launch by launch, through the library's timing hook.
     torch.cuda.synchronize()
+    B.mate_timing_begin("ssd_out")
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    out_launches, out_ms_total = B.mate_timing_end()
     ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_step = wl.N * len(wl.schedule)
+    tokens_per_step = wl.N * wl.batch * len(wl.schedule)
     value = tokens_per_step * args.steps / elapsed
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value / 1e6:.3f} M tokens/s")
+    t_out = out_ms_total / max(1, out_launches) * 1e-3
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value / 1e6:.3f} M tokens/s; "
+        f"output sweep {t_out * 1e3:.3f} ms over {out_launches} launches")
 
     # Per-call timings with events on the launch stream (torch's current stream).
     stream = torch.cuda.current_stream()
@@ -209,20 +250,31 @@ def main():
     peak_flops = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
     tesa_tf = w["tesa_flops"][False] / t_tesa[False] / 1e12
     ssd_tf = w["ssd_flops"] / t_ssd / 1e12
+    out_tf = w["out_flops"] / t_out / 1e12
+    out_gbs = w["out_bytes"] / t_out / 1e9
     kernels = {
+        "ssd_out_sweep": {"ms": t_out * 1e3, "tflops": out_tf, "mfma_frac": out_tf / peak_flops, "gbs": out_gbs,
+                          "hbm_frac": out_gbs / PEAK_HBM_GBS, "launches_timed": out_launches},
+        "bissd_call": {"ms": t_ssd * 1e3, "tflops": ssd_tf, "mfma_frac": ssd_tf / peak_flops,
+                       "hbm_frac": w["ssd_bytes"] / t_ssd / 1e9 / PEAK_HBM_GBS},
         "tesa_unshifted": {"ms": t_tesa[False] * 1e3, "tflops": tesa_tf, "mfma_frac": tesa_tf / peak_flops,
                            "hbm_frac": w["tesa_bytes"] / t_tesa[False] / 1e9 / PEAK_HBM_GBS},
         "tesa_shifted": {"ms": t_tesa[True] * 1e3, "tflops": w["tesa_flops"][True] / t_tesa[True] / 1e12,
                          "mfma_frac": w["tesa_flops"][True] / t_tesa[True] / 1e12 / peak_flops},
-        "bissd": {"ms": t_ssd * 1e3, "tflops": ssd_tf, "mfma_frac": ssd_tf / peak_flops,
-                  "hbm_frac": w["ssd_bytes"] / t_ssd / 1e9 / PEAK_HBM_GBS},
         "rms_reorder_x": {"ms": t_rms * 1e3, "gbs": w["reorder_bytes"] / t_rms / 1e9,
                           "hbm_frac": w["reorder_bytes"] / t_rms / 1e9 / PEAK_HBM_GBS},
     }
-    # The TESA kernel is one launch per call, so the events above time exactly that kernel.
-    roofline = {"bound": "mfma", "kernel": "tesa (unshifted layer)", "achieved": tesa_tf, "peak": peak_flops,
-                "unit": "TFLOP/s", "frac": tesa_tf / peak_flops, "traffic": None,
-                "algorithmic_per_launch": {"flops": w["tesa_flops"][False], "bytes": w["tesa_bytes"]}}
+    # Roofline of the dominant kernel: whichever of its algorithmic flops and bytes takes longer at peak.
+    hbm_bound = w["out_bytes"] / (PEAK_HBM_GBS * 1e9) >= w["out_flops"] / (peak_flops * 1e12)
+    roofline = {"bound": "hbm" if hbm_bound else "mfma",
+                "achieved": out_gbs if hbm_bound else out_tf,
+                "peak": PEAK_HBM_GBS if hbm_bound else peak_flops,
+                "unit": "GB/s" if hbm_bound else "TFLOP/s",
+                "frac": out_gbs / PEAK_HBM_GBS if hbm_bound else out_tf / peak_flops,
+                "traffic": measured_traffic(wl),
+                "kernel": "bi-SSD output sweep (k_out)",
+                "algorithmic_per_launch": {"flops": w["out_flops"], "bytes": w["out_bytes"]},
+                "mfma_frac": out_tf / peak_flops}
     out = {
         "metric": METRIC,
         "value": value,
@@ -249,6 +301,16 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if args.calibrate_copy:
+        # A plain streaming kernel of known size (reads and writes COPY_BYTES once each: an elementwise
+        # negation), for scaling HBM byte counters taken on this same run.
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = COPY_BYTES
     if not args.no_cpu_baseline:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
         log(f"timing the CPU oracle on a sample with {threads} threads ...")

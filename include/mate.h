@@ -16,7 +16,8 @@
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA storage).
  *     The caller owns every buffer; the library never allocates, frees or
- *     keeps device memory between calls.
+ *     keeps device memory between calls (the HIP events of the timing
+ *     diagnostics below aside).
  *   - Token tensors are channels-last: [batch][T][H][W][...], so the canonical
  *     token index is n = (t*H + h)*W + w and a token's channels are contiguous.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
@@ -26,6 +27,8 @@
  *   - Arguments are validated on the host before anything is launched. A call
  *     that returns a status other than MATE_OK has launched nothing and written
  *     nothing; mate_last_error() then describes why (thread-local string).
+ *   - Token tensors (x, b, c, y, q, k, v, o) must be 16-byte aligned (torch
+ *     and hipMalloc allocations are); otherwise MATE_ERR_UNSUPPORTED.
  *   - bf16 means bfloat16 (1 sign, 8 exponent, 7 mantissa bits); arithmetic is
  *     fp32 inside, results are rounded to nearest-even on store.
  */
@@ -186,6 +189,22 @@ mate_status mate_forward(const mate_ssd_tensors *s, const mate_ssd_desc *sd, con
 const char *mate_status_string(mate_status s);
 const char *mate_last_error(void); /* detail of the last non-OK status on this thread */
 int mate_abi_version(void);
+
+/* Per-kernel timing with HIP events, for measuring one kernel of the path
+ * inside a running workload.
+ * mate_timing_begin(kernel) arms the named kernel: from then on, every launch
+ * of it (by any call, any stream) is bracketed by a pair of HIP events
+ * recorded on the stream it is launched on. Other kernels are untouched.
+ * Names: "rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb", "ssd_states",
+ * "ssd_seg_pass", "ssd_out", "tesa" (unknown name: MATE_ERR_SHAPE; a timing
+ * already armed: MATE_ERR_SHAPE).
+ * mate_timing_end waits for the recorded events (a host synchronisation on
+ * them), stores the number of timed launches and their summed duration in
+ * milliseconds, and disarms. NULL outputs: MATE_ERR_NULL (timing stays armed).
+ * Events are created on first use and reused; they stay owned by the library.
+ * One timing at a time per process. */
+mate_status mate_timing_begin(const char *kernel);
+mate_status mate_timing_end(int64_t *launches, double *total_ms);
 
 #ifdef __cplusplus
 }

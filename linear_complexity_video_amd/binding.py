@@ -21,7 +21,7 @@ ALGO_AUTO, ALGO_PORTABLE, ALGO_FAST = 0, 1, 2
 EXPORTED = (
     "mate_rms_reorder", "mate_bissd_workspace_size", "mate_bissd_scan", "mate_tesa",
     "mate_forward_workspace_size", "mate_forward", "mate_status_string", "mate_last_error",
-    "mate_abi_version",
+    "mate_abi_version", "mate_timing_begin", "mate_timing_end",
 )
 
 
@@ -86,6 +86,10 @@ def lib() -> ctypes.CDLL:
     L.mate_status_string.restype = ctypes.c_char_p
     L.mate_last_error.restype = ctypes.c_char_p
     L.mate_abi_version.restype = ctypes.c_int
+    L.mate_timing_begin.argtypes = [ctypes.c_char_p]
+    L.mate_timing_begin.restype = ctypes.c_int
+    L.mate_timing_end.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+    L.mate_timing_end.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -215,3 +219,19 @@ def mate_forward(ssd: dict, tesa: dict, order: int, chunk: int, pool, window, sh
     tt = TesaTensors(*(_ptr(tesa[k]) for k in ("q", "k", "v", "o")))
     _check(lib().mate_forward(ctypes.byref(st), ctypes.byref(sdesc), ctypes.byref(tt), ctypes.byref(tdesc),
                               Grid(*grid), order, _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def mate_timing_begin(kernel: str):
+    """Arms HIP event timing of every later launch of one library kernel."""
+    status = lib().mate_timing_begin(kernel.encode())
+    if status != MATE_OK:
+        raise MateError(status, f"mate_timing_begin({kernel!r}) refused")
+
+
+def mate_timing_end():
+    """Disarms the timing; returns (launches, summed milliseconds)."""
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+    status = lib().mate_timing_end(ctypes.byref(n), ctypes.byref(ms))
+    if status != MATE_OK:
+        raise MateError(status, "mate_timing_end failed")
+    return int(n.value), float(ms.value)

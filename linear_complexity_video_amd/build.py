@@ -28,7 +28,7 @@ DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "mate_api.cpp")]
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "mate_api.cpp"), os.path.join(CSRC, "timing.cpp")]
 
 
 def _compile(src: str) -> str:

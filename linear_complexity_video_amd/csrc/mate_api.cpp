@@ -149,6 +149,10 @@ mate_status check_ssd_tensors(const mate_ssd_tensors *t)
     if (!t) return fail(MATE_ERR_NULL, "ssd tensors struct is NULL");
     if (!t->x || !t->b || !t->c || !t->dt || !t->a || !t->d || !t->y)
         return fail(MATE_ERR_NULL, "an ssd tensor pointer (x, b, c, dt, a, d, y) is NULL");
+    if (((uintptr_t)t->x | (uintptr_t)t->b | (uintptr_t)t->c | (uintptr_t)t->y) & 15)
+        return fail(MATE_ERR_UNSUPPORTED, "x, b, c and y must be 16-byte aligned");
+    if (((uintptr_t)t->dt | (uintptr_t)t->a | (uintptr_t)t->d) & 3)
+        return fail(MATE_ERR_UNSUPPORTED, "dt, a and d must be 4-byte aligned");
     return MATE_OK;
 }
 
@@ -156,6 +160,8 @@ mate_status check_tesa_tensors(const mate_tesa_tensors *t)
 {
     if (!t) return fail(MATE_ERR_NULL, "tesa tensors struct is NULL");
     if (!t->q || !t->k || !t->v || !t->o) return fail(MATE_ERR_NULL, "a tesa tensor pointer (q, k, v, o) is NULL");
+    if (((uintptr_t)t->q | (uintptr_t)t->k | (uintptr_t)t->v | (uintptr_t)t->o) & 15)
+        return fail(MATE_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
     return MATE_OK;
 }
 

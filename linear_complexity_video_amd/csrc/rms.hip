@@ -3,6 +3,7 @@
 // row is read once and written once with the widest aligned vector type.
 #include "common.hpp"
 #include "launch.hpp"
+#include "timing.hpp"
 
 namespace mate {
 
@@ -100,6 +101,7 @@ hipError_t launch_rms_reorder(const void *src, void *dst, int64_t batch, int64_t
     while (e > 1 && (align & (uintptr_t)(e - 1))) e >>= 1;
     const uint32_t vpr = (uint32_t)(row_bytes / e);
     const uint32_t b = (uint32_t)batch, t = (uint32_t)T, h = (uint32_t)H, w = (uint32_t)W;
+    timing::Scope ts_(K_RMS_REORDER, stream);
     switch (e) {
     case 16: return launch_typed<u32x4>(src, dst, b, t, h, w, vpr, order, flip, inverse, stream);
     case 8: return launch_typed<u32x2>(src, dst, b, t, h, w, vpr, order, flip, inverse, stream);

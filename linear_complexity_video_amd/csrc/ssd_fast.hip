@@ -45,6 +45,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "ssd_common.hpp"
+#include "timing.hpp"
 
 namespace mate {
 
@@ -752,31 +753,64 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
         float *rdt = (float *)(w + pl.rdt), *rdtT = (float *)(w + pl.rdtT), *rcsT = (float *)(w + pl.rcsT);
         const uint32_t R = (uint32_t)p.R, Rpad = (uint32_t)(p.nchR * Q);
         const int64_t Cx = (int64_t)Hs * P, Cb = (int64_t)G * S;
-        ssd::k_pool8<bf16_t><<<dim3((Cx + 2047) / 2048, R, Bn), 256, 0, st>>>(
-            (const bf16_t *)a.x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
-        ssd::k_pool8<bf16_t><<<dim3((Cb + 2047) / 2048, R, Bn), 256, 0, st>>>(
-            (const bf16_t *)a.b, rB, Cb, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
-        ssd::k_pool<float, float><<<dim3((Hs + 255) / 256, R, Bn), 256, 0, st>>>(
-            a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
-        ssd::k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, Bn), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad,
-                                                                                Q, 0, 1, 1, R);
+        {
+            timing::Scope ts_(K_SSD_POOL, st);
+            ssd::k_pool8<bf16_t><<<dim3((Cx + 2047) / 2048, R, Bn), 256, 0, st>>>(
+                (const bf16_t *)a.x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        }
+        {
+            timing::Scope ts_(K_SSD_POOL, st);
+            ssd::k_pool8<bf16_t><<<dim3((Cb + 2047) / 2048, R, Bn), 256, 0, st>>>(
+                (const bf16_t *)a.b, rB, Cb, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        }
+        {
+            timing::Scope ts_(K_SSD_POOL, st);
+            ssd::k_pool<float, float><<<dim3((Hs + 255) / 256, R, Bn), 256, 0, st>>>(
+                a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        }
+        {
+            timing::Scope ts_(K_SSD_PREP, st);
+            ssd::k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, Bn), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad,
+                                                                                    Q, 0, 1, 1, R);
+        }
         const uint64_t items = (uint64_t)Bn * Hs;
-        k_states<S, Q><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, rdtT, rcsT,
-                                                      a.a, nullptr, nullptr, segF, segB, segA, Hs, G, R, Rpad,
-                                                      p.nchR, p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)items);
+        {
+            timing::Scope ts_(K_SSD_STATES, st);
+            k_states<S, Q><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, rdtT, rcsT,
+                                                          a.a, nullptr, nullptr, segF, segB, segA, Hs, G, R, Rpad,
+                                                          p.nchR, p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)items);
+        }
     }
-    k_perm<<<(N + 255) / 256, 256, 0, st>>>(perm, N, p.order, T, H, W);
-    ssd::k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, Bn), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q,
-                                                                         p.order, T, H, W);
-    k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, G, N);
+    {
+        timing::Scope ts_(K_SSD_PREP, st);
+        k_perm<<<(N + 255) / 256, 256, 0, st>>>(perm, N, p.order, T, H, W);
+    }
+    {
+        timing::Scope ts_(K_SSD_PREP, st);
+        ssd::k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, Bn), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q,
+                                                                             p.order, T, H, W);
+    }
+    {
+        timing::Scope ts_(K_SSD_CB, st);
+        k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, G, N);
+    }
     const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
-    k_states<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
-                                                  N, Lpad, p.nch, pl.segch, pl.nseg, 0, pl.nsegT, (uint32_t)items);
-    k_seg_pass<<<dim3((P * S + 255) / 256, Hs, Bn), 256, 0, st>>>(segF, segB, segA, hinF, hinB, P * S, pl.nseg,
-                                                                  pl.nsegT, p.R > 0 ? 1 : 0);
-    k_out<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, Cm, cb, perm, dtT, csT, a.a, a.d, hbl, delta, hinF, hinB,
-                                               (__bf16 *)a.y, Hs, G, N, Lpad, p.nch, pl.segch, pl.nseg,
-                                               (uint32_t)items);
+    {
+        timing::Scope ts_(K_SSD_STATES, st);
+        k_states<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
+                                                      N, Lpad, p.nch, pl.segch, pl.nseg, 0, pl.nsegT, (uint32_t)items);
+    }
+    {
+        timing::Scope ts_(K_SSD_SEG_PASS, st);
+        k_seg_pass<<<dim3((P * S + 255) / 256, Hs, Bn), 256, 0, st>>>(segF, segB, segA, hinF, hinB, P * S, pl.nseg,
+                                                                      pl.nsegT, p.R > 0 ? 1 : 0);
+    }
+    {
+        timing::Scope ts_(K_SSD_OUT, st);
+        k_out<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, Cm, cb, perm, dtT, csT, a.a, a.d, hbl, delta, hinF, hinB,
+                                                   (__bf16 *)a.y, Hs, G, N, Lpad, p.nch, pl.segch, pl.nseg,
+                                                   (uint32_t)items);
+    }
     return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "ssd_common.hpp"
+#include "timing.hpp"
 
 namespace mate {
 
@@ -341,24 +342,57 @@ static hipError_t run_portable(const SsdProblem &p, const SsdArgs &a, void *ws, 
         h0b = (float *)(w + l.h0b);
         const uint32_t R = (uint32_t)p.R, Rpad = (uint32_t)(p.nchR * Q);
         const int64_t Cx = (int64_t)Hs * P, Cb = (int64_t)G * S;
-        k_pool<E, float><<<dim3((Cx + 255) / 256, R, B), 256, 0, st>>>(x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
-        k_pool<E, float><<<dim3((Cb + 255) / 256, R, B), 256, 0, st>>>(Bm, rB, Cb, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
-        k_pool<float, float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
-        k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, B), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1, R);
-        k_chunk_states<float, false><<<dim3(p.nchR, Hs, B), 256, states_lds, st>>>(
-            rx, rB, rdtT, rcsT, a.a, rSf, rSb, Hs, P, S, G, R, Rpad, Q, 0, 1, 1, R);
-        k_state_pass<<<dim3((P * S + 255) / 256, Hs, B), 256, 0, st>>>(rSf, rSb, rcsT, nullptr, nullptr, h0f, h0b,
-                                                                      P * S, p.nchR, Q, Rpad);
+        {
+            timing::Scope ts_(K_SSD_POOL, st);
+            k_pool<E, float><<<dim3((Cx + 255) / 256, R, B), 256, 0, st>>>(x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        }
+        {
+            timing::Scope ts_(K_SSD_POOL, st);
+            k_pool<E, float><<<dim3((Cb + 255) / 256, R, B), 256, 0, st>>>(Bm, rB, Cb, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        }
+        {
+            timing::Scope ts_(K_SSD_POOL, st);
+            k_pool<float, float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        }
+        {
+            timing::Scope ts_(K_SSD_PREP, st);
+            k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, B), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1, R);
+        }
+        {
+            timing::Scope ts_(K_SSD_STATES, st);
+            k_chunk_states<float, false><<<dim3(p.nchR, Hs, B), 256, states_lds, st>>>(
+                rx, rB, rdtT, rcsT, a.a, rSf, rSb, Hs, P, S, G, R, Rpad, Q, 0, 1, 1, R);
+        }
+        {
+            timing::Scope ts_(K_SSD_SEG_PASS, st);
+            k_state_pass<<<dim3((P * S + 255) / 256, Hs, B), 256, 0, st>>>(rSf, rSb, rcsT, nullptr, nullptr, h0f, h0b,
+                                                                          P * S, p.nchR, Q, Rpad);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, B), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q, p.order, T, H, W);
-    k_chunk_states<E, true><<<dim3(p.nch, Hs, B), 256, states_lds, st>>>(x, Bm, dtT, csT, a.a, Sf, Sb, Hs, P, S, G, N,
-                                                                         Lpad, Q, p.order, T, H, W);
-    k_state_pass<<<dim3((P * S + 255) / 256, Hs, B), 256, 0, st>>>(Sf, Sb, csT, h0f, h0b, nullptr, nullptr, P * S,
-                                                                  p.nch, Q, Lpad);
-    k_cb<E><<<dim3(p.nch, G, B), 256, 0, st>>>(Bm, Cm, CB, G, S, N, Q, p.order, T, H, W);
-    k_output<E><<<dim3(p.nch, Hs, B), 256, 0, st>>>(x, Cm, CB, dtT, csT, a.a, a.d, Sf, Sb, (E *)a.y, Hs, P, S, G, N,
-                                                    Lpad, Q, p.order, T, H, W);
+    {
+        timing::Scope ts_(K_SSD_PREP, st);
+        k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, B), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q, p.order, T, H, W);
+    }
+    {
+        timing::Scope ts_(K_SSD_STATES, st);
+        k_chunk_states<E, true><<<dim3(p.nch, Hs, B), 256, states_lds, st>>>(x, Bm, dtT, csT, a.a, Sf, Sb, Hs, P, S, G, N,
+                                                                             Lpad, Q, p.order, T, H, W);
+    }
+    {
+        timing::Scope ts_(K_SSD_SEG_PASS, st);
+        k_state_pass<<<dim3((P * S + 255) / 256, Hs, B), 256, 0, st>>>(Sf, Sb, csT, h0f, h0b, nullptr, nullptr, P * S,
+                                                                      p.nch, Q, Lpad);
+    }
+    {
+        timing::Scope ts_(K_SSD_CB, st);
+        k_cb<E><<<dim3(p.nch, G, B), 256, 0, st>>>(Bm, Cm, CB, G, S, N, Q, p.order, T, H, W);
+    }
+    {
+        timing::Scope ts_(K_SSD_OUT, st);
+        k_output<E><<<dim3(p.nch, Hs, B), 256, 0, st>>>(x, Cm, CB, dtT, csT, a.a, a.d, Sf, Sb, (E *)a.y, Hs, P, S, G, N,
+                                                        Lpad, Q, p.order, T, H, W);
+    }
     return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@
 // window land on the same XCD and share its K/V in L2.
 #include "common.hpp"
 #include "launch.hpp"
+#include "timing.hpp"
 
 namespace mate {
 
@@ -247,6 +248,7 @@ hipError_t launch(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
     const uint64_t total = (uint64_t)p.batch * p.nheads * p.nrt * p.nrh * p.nrw * nqb;
     const uint64_t blocks = (total + 7) / 8 * 8;
     const float scale = p.scale > 0.f ? p.scale : 1.f / sqrtf((float)DH);
+    timing::Scope ts_(K_TESA, stream);
     k_tesa_fast<DH><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
         (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, p.nheads, (int)p.T,
         (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st, p.sh, p.sw, p.nrt, p.nrh, p.nrw, nqb, (uint32_t)total,

@@ -3,6 +3,7 @@
 // online softmax. Used for fp32 tensors and head sizes without MFMA kernels.
 #include "common.hpp"
 #include "launch.hpp"
+#include "timing.hpp"
 
 namespace mate {
 
@@ -113,6 +114,7 @@ hipError_t launch_dh(const TesaProblem &p, const TesaArgs &a, hipStream_t st)
 {
     const float scale = p.scale > 0.f ? p.scale : 1.f / sqrtf((float)DH);
     dim3 grid((unsigned)(p.nrt * p.nrh * p.nrw), (unsigned)p.nheads, (unsigned)p.batch);
+    timing::Scope ts_(K_TESA, st);
     k_tesa_portable<T, DH><<<grid, 256, 0, st>>>((const T *)a.q, (const T *)a.k, (const T *)a.v, (T *)a.o,
                                                   p.nheads, (int)p.T, (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st,
                                                   p.sh, p.sw, p.nrh, p.nrw, scale);

@@ -139,3 +139,26 @@ def test_forward_validation_rejects_before_launch():
                           ctypes.c_void_p(0x800000), 1 << 40, None)
     assert rc == B.MATE_ERR_SHAPE
     assert lib.mate_forward_workspace_size(g, ctypes.byref(sd), ctypes.byref(td)) == 0
+
+
+def test_misaligned_token_tensors_are_rejected():
+    g = B.Grid(1, 2, 4, 4)
+    assert _scan(_ssd_t(x=0x100008), g, 0, _ssd()) == B.MATE_ERR_UNSUPPORTED
+    assert "16-byte" in B.lib().mate_last_error().decode()
+    assert _scan(_ssd_t(dt=0x103002), g, 0, _ssd()) == B.MATE_ERR_UNSUPPORTED
+    t = B.TesaTensors(0x100000, 0x200000, 0x300004, 0x400000)
+    assert _att(t, g, _tesa()) == B.MATE_ERR_UNSUPPORTED
+
+
+def test_timing_arming_rules():
+    """Arming and disarming touch no device when nothing was launched."""
+    lib = B.lib()
+    assert lib.mate_timing_begin(b"no_such_kernel") == B.MATE_ERR_SHAPE
+    assert lib.mate_timing_begin(None) == B.MATE_ERR_NULL
+    B.mate_timing_begin("ssd_out")
+    assert lib.mate_timing_begin(b"tesa") == B.MATE_ERR_SHAPE      # one timing at a time
+    assert lib.mate_timing_end(None, None) == B.MATE_ERR_NULL      # stays armed
+    assert B.mate_timing_end() == (0, 0.0)
+    for name in ("rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb", "ssd_states", "ssd_seg_pass", "ssd_out", "tesa"):
+        B.mate_timing_begin(name)
+        assert B.mate_timing_end() == (0, 0.0)
