@@ -375,13 +375,17 @@ __global__ __launch_bounds__(256) void k_seg_pass(const float *__restrict__ segF
 }
 
 // ---------------------------------------------------------------------------
-// 3. CB[t][u] = C_t . B_u per chunk and group (fp16). grid (nch, G, batch). Computed as CB^T = B C^T so each lane holds
-// 4 consecutive u of one t.
+// 3. Per chunk and group (grid (nch, G, batch)), for the output sweep:
+//    cb    CB[t][u] = C_t . B_u (fp16), computed as CB^T = B C^T so each lane holds 4 consecutive u of one t;
+//    b16   the chunk's B rows in scan order, as fp16 ([Q][S]);
+//    cfrag the chunk's C rows in MFMA operand order: for token block tb and k-block kb, lane l's 8 values
+//          C[32 tb + l % 32][16 kb + 8 (l / 32) + 0..7] are the l-th 16 bytes of a 1 KB block, so the sweep
+//          reads each operand with one contiguous load per wave.
 // ---------------------------------------------------------------------------
 template <int S, int Q>
 __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
-                                           const uint32_t *__restrict__ perm, _Float16 *__restrict__ cb, int G,
-                                           uint32_t L)
+                                           const uint32_t *__restrict__ perm, _Float16 *__restrict__ cb,
+                                           _Float16 *__restrict__ b16, __bf16 *__restrict__ cfrag, int G, uint32_t L)
 {
     const uint32_t c = blockIdx.x;
     const int g = blockIdx.y, b = blockIdx.z;
@@ -419,33 +423,76 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
             *(f16x4 *)(out + (size_t)t * Q + 32 * ub + 8 * g4 + 4 * half) = v4;
         }
     }
+    // B rows as fp16 (exact for bf16 values in fp16's normal range) and C rows in operand order.
+    constexpr int PIECES = Q * S / 8, PER = PIECES / NT;
+    static_assert(PIECES % NT == 0, "pieces must split evenly");
+    _Float16 *bo = b16 + chunk * (size_t)(Q * S);
+    __bf16 *co = cfrag + chunk * (size_t)(Q * S);
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int k = tid + NT * it;
+        {
+            const int row = k / (S / 8), c8 = k % (S / 8);
+            const uint32_t i = c * Q + row;
+            const u32x4 v = *(const u32x4 *)(Bm + ((size_t)b * L + (i < L ? perm[i] : 0u)) * rs + (size_t)g * S + 8 * c8);
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = i < L ? pack2h(lo_f(v[e]), hi_f(v[e])) : 0u;
+            *(u32x4 *)(bo + (size_t)row * S + 8 * c8) = o;
+        }
+        {
+            const int l = k % 64, kb = (k / 64) % (S / 16), tb = k / (64 * (S / 16));
+            const uint32_t i = c * Q + 32 * tb + (l & 31);
+            const u32x4 v = *(const u32x4 *)(Cm + ((size_t)b * L + (i < L ? perm[i] : 0u)) * rs + (size_t)g * S +
+                                              16 * kb + 8 * (l >> 5));
+            *(u32x4 *)(co + 8 * (size_t)k) = i < L ? v : u32x4{0, 0, 0, 0};
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
 // 4. Left-to-right output sweep. Same grid/items as k_states (main segments).
+//
+// Per chunk, three phases separated by barriers:
+//   build  this chunk's C operands are requested (contiguous, in operand order), then the next chunk's
+//          data; Hf advances on fp16 MFMA (Hf^T += B^T (w x)^T with w = dt exp(tot - cs) applied to the
+//          x operand in registers); every thread turns one 8-column piece of CB per 32-column block into M
+//          in place (fp16, row t = token); the 16 rows of a wave lie in one 32-row block, so each piece is
+//          uniformly below, on or above the diagonal block across the wave;
+//   use    Y^T = X^T M^T + ef (Hf C^T) + eb (Hb C^T); Y goes to LDS as bf16 rows;
+//   store  Y rows leave as contiguous 16-byte pieces; the next chunk is staged: x (fp16), B (fp16), the
+//          forward state Hf (from the accumulators), the backward state Hb = stored local state + decay *
+//          border state, CB, and the per-token decay data.
+// Every load and store in the loop is unconditional (a lane past the end of the sequence reads row 0
+// and stores into a scratch row), and no load result crosses the loop edge, so the compiler's memory
+// waits stay exact.
 // ---------------------------------------------------------------------------
 template <int S, int Q>
-__global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
-                                            const __bf16 *__restrict__ Cm, const _Float16 *__restrict__ cb,
+__global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ b16,
+                                            const __bf16 *__restrict__ cfrag, const _Float16 *__restrict__ cb,
                                             const uint32_t *__restrict__ perm,
                                             const float *__restrict__ dtT, const float *__restrict__ csT,
                                             const float *__restrict__ A, const float *__restrict__ Dv,
                                             const __bf16 *__restrict__ hb_local, const float *__restrict__ delta,
                                             const float *__restrict__ hinF, const __bf16 *__restrict__ hinB,
-                                            __bf16 *__restrict__ y, int nheads, int G, uint32_t N, uint32_t Lpad,
-                                            int nch, int segch, int nseg, uint32_t total_items)
+                                            __bf16 *__restrict__ y, __bf16 *__restrict__ ytrash, int nheads, int G,
+                                            uint32_t N, uint32_t Lpad, int nch, int segch, int nseg,
+                                            uint32_t total_items)
 {
     constexpr int NT = Q * 4, NW = Q / 16;  // Q/16 waves, two per SIMD at Q = 128
-    constexpr int LX = P + XPAD, LB = S + XPAD, SS = S + 8;
-    __shared__ __bf16 xn[Q * LX];    // x, converted to fp16 (operand of the fp16 intra-chunk product)
-    __shared__ __bf16 xf[Q * LX];    // x * dt exp(tot - cs)
-    __shared__ __bf16 bn[Q * LB];    // B
+    constexpr int LX = P + XPAD, LB = S + XPAD, SS = S + 8, LM = Q + 8, LY = P + 8;
+    constexpr int UB = Q / 32;              // 32-column blocks of M
+    __shared__ _Float16 xn[Q * LX];  // x as fp16: operand of the intra-chunk product and of the state update
+    __shared__ _Float16 bn[Q * LB];  // B as fp16
     __shared__ __bf16 hfl[P * SS];   // forward state entering the chunk, [p][s]
     __shared__ __bf16 hbl[P * SS];   // backward state entering the chunk from the right, [p][s]
-    // per token: cs, ce (log2 units), dt, and the split decay factors of the off-diagonal blocks
+    __shared__ __attribute__((aligned(16))) _Float16 mt[Q * LM];  // CB, then M[t][u] (fp16)
+    __shared__ __attribute__((aligned(16))) __bf16 ybuf[Q * LY];  // output rows [t][p]
+    // per token: cs, ce (log2 units), dt, the split decay factors of the off-diagonal blocks, the state weight
     __shared__ __attribute__((aligned(16))) float s_cs[Q], s_ce[Q], s_dt[Q];
-    __shared__ __attribute__((aligned(16))) _Float16 s_gl[Q], s_gu[Q];
-    __shared__ uint32_t s_row[Q];    // global rows: of chunk c at the top of iteration c, then of chunk c+1
+    __shared__ __attribute__((aligned(16))) _Float16 s_gl[Q], s_gu[Q], s_w[Q];
+    __shared__ uint32_t s_row[Q];    // global rows of the chunk after the staged one
+    __shared__ uint32_t s_rowy[Q];   // global rows of the chunk whose output is in ybuf
 
     const uint32_t item = xcd_item();
     if (item >= total_items) return;
@@ -462,6 +509,9 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
     const bool row_thread = wave < Q / 64;  // tid < Q
     // One Y^T tile per wave: t-block wave / 2, p-block wave % 2.
     const int tb = wave >> 1, pb = wave & 1;
+    // Role in building M: row mrow, columns 32 U + 8 msub + 0..7 for every block U;
+    // the wave's rows 16 wave .. 16 wave + 15 all lie in row block wave / 2.
+    const int mrow = tid >> 2, msub = tid & 3, mtb = wave >> 1;
     // Hf^T tiles (S/32 s-blocks x 2 p-blocks) over the waves: HT per wave, or one
     // tile for the first S/16 waves when there are fewer tiles than waves.
     constexpr int HTILES = S / 16;
@@ -497,56 +547,50 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
     }
 
     Rows<Q, P, NT> xr;
-    Rows<Q, S, NT> br;
-    const size_t cb_base = ((size_t)b * G + g) * nch;
+    constexpr int BPER = Q * S / 8 / NT;  // 16-byte pieces of the B tile per thread
+    const size_t gch = ((size_t)b * G + g) * nch;  // chunk index base of this group
     const int t_tok = 32 * tb + col;  // this lane's token inside the chunk (Y^T column)
 
-    // Data staged through LDS, fetched one chunk ahead.
+    // Staging data of the next chunk: loaded in the build phase, consumed by the staging at the end of
+    // the same iteration.
+    u32x4 bru[BPER];
     u32x4 hbr[HBC];
-    float wd[Rows<Q, P, NT>::PER], wc[Rows<Q, P, NT>::PER];
-    float tok_d = 0.f, tok_c = 0.f, blk_cs_end = 0.f, blk_cs0 = 0.f, blk_dt0 = 0.f, tot = 0.f, dl = 0.f;
-    uint32_t pnext = ~0u;
+    u32x4 cbr[UB];  // CB row pieces, for mt
+    float tok_d = 0.f, tok_c = 0.f, tot = 0.f, dl = 0.f;
+    uint32_t pnext = 0u;
+    bool pvalid = false;
     auto fetch = [&](int c) {
         xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * N);
-        br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * N);
-        const size_t crow0 = drow + (size_t)c * Q;
+        const _Float16 *bsrc = b16 + (gch + c) * (size_t)(Q * S);
 #pragma unroll
-        for (int it = 0; it < xr.PER; ++it) {
-            wd[it] = dtT[crow0 + xr.row_of(it)];
-            wc[it] = csT[crow0 + xr.row_of(it)];
-        }
+        for (int it = 0; it < BPER; ++it) bru[it] = *(const u32x4 *)(bsrc + 8 * (tid + NT * it));
         const __bf16 *src = hb_local + (bh * nch + c) * (size_t)PS;
 #pragma unroll
         for (int it = 0; it < HBC; ++it) hbr[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
-        if (row_thread) {
-            const int ub = tid & ~31;
-            tok_d = dtT[crow0 + tid];
-            tok_c = csT[crow0 + tid];
-            blk_cs_end = csT[crow0 + ub + 31];
-            blk_cs0 = csT[crow0 + ub];
-            blk_dt0 = dtT[crow0 + ub];
-            pnext = c + 1 < c_hi ? seq_row(perm, (uint32_t)(c + 1) * Q + tid, N) : ~0u;
+        const _Float16 *cbs = cb + (gch + c) * (size_t)(Q * Q) + (size_t)mrow * Q + 8 * msub;
+#pragma unroll
+        for (int U = 0; U < UB; ++U) cbr[U] = *(const u32x4 *)(cbs + 32 * U);
+        // Every thread issues the same loads; the per-token values matter for tid < Q only.
+        const int tq = tid & (Q - 1);
+        const size_t crow0 = drow + (size_t)c * Q;
+        tok_d = dtT[crow0 + tq];
+        tok_c = csT[crow0 + tq];
+        {
+            const uint32_t i = (uint32_t)(c + 1) * Q + tq;
+            pvalid = c + 1 < c_hi && i < N;
+            pnext = perm[pvalid ? i : 0u];  // selected against pvalid where it is stored
         }
         tot = csT[crow0 + Q - 1];
         dl = delta[bh * nch + c];
     };
-    if (row_thread) s_row[tid] = seq_row(perm, (uint32_t)c_lo * Q + tid, N);
-    __syncthreads();
-    fetch(c_lo);
-
-    for (int c = c_lo; c < c_hi; ++c) {
-        // Row of this lane's token (Y^T column); read before the table moves on to chunk c + 1.
-        const uint32_t rt = s_row[t_tok];
-        const bool tvalid = rt != ~0u;
-        const size_t trow = (size_t)b * N + (tvalid ? rt : 0u);
-
-        __syncthreads();  // previous chunk's LDS reads (and this chunk's row-table reads) are done
-        // ---- LDS writes ----
-        xr.template store_f16<LX>(xn);
+    uint32_t rowc = 0u;  // row-thread: global row of token tid of the staged chunk (~0u past the end)
+    auto stage = [&]() {
+        xr.template store_f16<LX>((__bf16 *)xn);
 #pragma unroll
-        for (int it = 0; it < xr.PER; ++it)
-            xr.template store_scaled<LX>(xf, it, wd[it] * ex2((tot - wc[it]) * LOG2E));
-        br.template store<LB>(bn);
+        for (int it = 0; it < BPER; ++it) {
+            const int k = tid + NT * it;
+            *(u32x4 *)&bn[(k / (S / 8)) * LB + 8 * (k % (S / 8))] = bru[it];
+        }
         if (hact) {
 #pragma unroll
             for (int i = 0; i < HT; ++i)
@@ -568,7 +612,19 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
                 o[e] = pack2(lo_f(hbr[it][e]) + dl * lo_f(hinb[it][e]), hi_f(hbr[it][e]) + dl * hi_f(hinb[it][e]));
             *(u32x4 *)&hbl[p * SS + s0] = o;
         }
+#pragma unroll
+        for (int U = 0; U < UB; ++U) *(u32x4 *)(mt + mrow * LM + 32 * U + 8 * msub) = cbr[U];
+        // Block-edge values of this token's 32-token block, from its lanes 0/31 (or 32/63).
+        const int c0l = __builtin_amdgcn_readlane(__float_as_int(tok_c), 0);
+        const int c31l = __builtin_amdgcn_readlane(__float_as_int(tok_c), 31);
+        const int d0l = __builtin_amdgcn_readlane(__float_as_int(tok_d), 0);
+        const int c0h = __builtin_amdgcn_readlane(__float_as_int(tok_c), 32);
+        const int c31h = __builtin_amdgcn_readlane(__float_as_int(tok_c), 63);
+        const int d0h = __builtin_amdgcn_readlane(__float_as_int(tok_d), 32);
         if (row_thread) {
+            const float blk_cs0 = __int_as_float(half ? c0h : c0l);
+            const float blk_cs_end = __int_as_float(half ? c31h : c31l);
+            const float blk_dt0 = __int_as_float(half ? d0h : d0l);
             const float cs2 = tok_c * LOG2E, ce2 = (tok_c - tok_d * a) * LOG2E;
             s_dt[tid] = tok_d;
             s_cs[tid] = cs2;
@@ -576,112 +632,132 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
             // below-diagonal blocks: exp(cs_end - cs_u); above: exp(ce_u - ce_start); both <= 1
             s_gl[tid] = (_Float16)(tok_d * ex2(blk_cs_end * LOG2E - cs2));
             s_gu[tid] = (_Float16)(tok_d * ex2(ce2 - (blk_cs0 - blk_dt0 * a) * LOG2E));
-            s_row[tid] = pnext;
+            // weight of token u in the state carried out of the chunk
+            s_w[tid] = (_Float16)(tok_d * ex2(tot * LOG2E - cs2));
+            rowc = s_row[tid];
+            s_row[tid] = pvalid ? pnext : ~0u;
         }
-        __syncthreads();
+    };
+    // Output rows of the chunk in ybuf: contiguous 16-byte pieces (a past-the-end row goes to scratch).
+    auto store_y = [&]() {
+#pragma unroll
+        for (int it = 0; it < Q * (P / 8) / NT; ++it) {
+            const int k = tid + NT * it;
+            const int t = k / (P / 8), p8 = 8 * (k % (P / 8));
+            const uint32_t r = s_rowy[t];
+            __bf16 *dst = r != ~0u ? y + (((size_t)b * N + r) * nheads + h) * P + p8 : ytrash + p8;
+            *(u32x4 *)dst = *(const u32x4 *)&ybuf[t * LY + p8];
+        }
+    };
 
+    // Prologue: rows of the first chunk, its data, staged.
+    if (row_thread) s_row[tid] = seq_row(perm, (uint32_t)c_lo * Q + tid, N);
+    __syncthreads();
+    fetch(c_lo);
+    __syncthreads();
+    stage();
+
+    for (int c = c_lo; c < c_hi; ++c) {
+        __syncthreads();  // staged chunk c visible
+
+        // ---- build ----
         const float tot_c = tot;
-        if (c + 1 < c_hi) fetch(c + 1);
-
-        // CB row of this lane's token (first 32-column block now, the rest one block
-        // ahead inside the intra loop) and its C row.
-        const _Float16 *cbrow = cb + (cb_base + c) * (size_t)(Q * Q) + (size_t)t_tok * Q;
-        u32x4 cb_cur[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) cb_cur[kk] = *(const u32x4 *)(cbrow + 16 * kk + 8 * half);
-        u32x4 cfr[S / 16];
+        const int cn = c + 1 < c_hi ? c + 1 : c;  // on the last iteration the loads are issued but unused
+        u32x4 cfr[S / 16];  // C operands of this lane's token: contiguous 1 KB per wave and k-block
         {
-            const __bf16 *crow = Cm + trow * ((size_t)G * S) + (size_t)g * S;
+            const __bf16 *src = cfrag + (gch + c) * (size_t)(Q * S) + (size_t)tb * (S / 16) * 512 + 8 * lane;
 #pragma unroll
-            for (int kb = 0; kb < S / 16; ++kb) {
-                const u32x4 v = *(const u32x4 *)(crow + 16 * kb + 8 * half);
-                cfr[kb] = tvalid ? v : u32x4{0, 0, 0, 0};
-            }
+            for (int kb = 0; kb < S / 16; ++kb) cfr[kb] = *(const u32x4 *)(src + 512 * kb);
         }
+        fetch(cn);
 
-        // ---- Hf = exp(tot) Hf + B^T-weighted x (as Hf^T = B^T xf^T); LDS operands only ----
+        // Hf = exp(tot) Hf + sum_u w_u x_u B_u^T (as Hf^T = B^T (w x)^T, fp16 operands)
         if (hact) {
             const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
             for (int i = 0; i < HT; ++i) hacc[i] *= dec;
 #pragma unroll
             for (int kb = 0; kb < Q / 16; ++kb) {
-                const bf16x8 af = frag_tr(bn, LB, 16 * kb, 32 * hsb);
+                const f16x8 af = __builtin_bit_cast(f16x8, frag_tr((const __bf16 *)bn, LB, 16 * kb, 32 * hsb));
+                const f16x8 w8 = *(const f16x8 *)(s_w + 16 * kb + 8 * half);
 #pragma unroll
-                for (int i = 0; i < HT; ++i) hacc[i] = mfma(af, frag_tr(xf, LX, 16 * kb, 32 * (hpb0 + i)), hacc[i]);
+                for (int i = 0; i < HT; ++i) {
+                    const f16x8 xv = __builtin_bit_cast(f16x8, frag_tr((const __bf16 *)xn, LX, 16 * kb, 32 * (hpb0 + i)));
+                    hacc[i] = mfma16(af, xv * w8, hacc[i]);
+                }
             }
         }
 
-        const float cs_t = s_cs[t_tok], ce_t = s_ce[t_tok], dt_t = s_dt[t_tok];
-        f32x16 yacc = f32x16{}, yb = f32x16{};
-        // ---- intra-chunk term X^T M^T ----
-#pragma unroll 1
-        for (int U = 0; U < Q / 32; ++U) {
-            u32x4 cb_nxt[2];
+        {
+            const float cs_t = s_cs[mrow], ce_t = s_ce[mrow], dt_t = s_dt[mrow];
+            _Float16 *mrw = mt + mrow * LM + 8 * msub;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                cb_nxt[kk] = U + 1 < Q / 32 ? *(const u32x4 *)(cbrow + 32 * (U + 1) + 16 * kk + 8 * half) : cb_cur[kk];
-            const bool diag_blk = U == tb;
-            const bool below = U < tb;
-            const float f = below ? ex2(cs_t - s_cs[32 * U + 31]) : ex2(s_ce[32 * U] - ce_t);
-            const _Float16 *gw = below ? s_gl : s_gu;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int kb = 2 * U + kk, u0 = 16 * kb + 8 * half;
+            for (int U = 0; U < UB; ++U) {
+                const int u0 = 32 * U + 8 * msub;
+                const f16x8 cb8 = *(const f16x8 *)(mrw + 32 * U);
                 f16x8 mf;
-                if (diag_blk) {
+                if (U == mtb) {
                     const f32x4 d0 = *(const f32x4 *)(s_dt + u0), d1 = *(const f32x4 *)(s_dt + u0 + 4);
                     const f32x4 c0 = *(const f32x4 *)(s_cs + u0), c1 = *(const f32x4 *)(s_cs + u0 + 4);
                     const f32x4 e0 = *(const f32x4 *)(s_ce + u0), e1 = *(const f32x4 *)(s_ce + u0 + 4);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const int u = u0 + j;
-                        const float cbv = (j & 1) ? h_hi(cb_cur[kk][j >> 1]) : h_lo(cb_cur[kk][j >> 1]);
+                        const float cbv = (float)cb8[j];
                         const float dtu = j < 4 ? d0[j] : d1[j - 4];
                         const float csu = j < 4 ? c0[j] : c1[j - 4];
                         const float ceu = j < 4 ? e0[j] : e1[j - 4];
                         // the decay exponent of the right direction is the non-positive one
                         const float m = cbv * dtu * ex2(fminf(cs_t - csu, ceu - ce_t));
-                        mf[j] = (_Float16)(u == t_tok ? 2.f * cbv * dt_t + twoD : m);
+                        mf[j] = (_Float16)(u0 + j == mrow ? 2.f * cbv * dt_t + twoD : m);
                     }
+                } else if (U < mtb) {
+                    const f16x8 g8 = *(const f16x8 *)(s_gl + u0);
+                    mf = cb8 * (g8 * (_Float16)ex2(cs_t - s_cs[32 * U + 31]));
                 } else {
-                    // packed fp16: CB * (g_u * f)
-                    const f16x8 g8 = *(const f16x8 *)(gw + u0);
-                    const _Float16 fh = (_Float16)f;
-                    mf = __builtin_bit_cast(f16x8, cb_cur[kk]) * (g8 * fh);
+                    const f16x8 g8 = *(const f16x8 *)(s_gu + u0);
+                    mf = cb8 * (g8 * (_Float16)ex2(s_ce[32 * U] - ce_t));
                 }
-                yacc = mfma16(__builtin_bit_cast(f16x8, frag_tr(xn, LX, 16 * kb, 32 * pb)), mf, yacc);
+                *(f16x8 *)(mrw + 32 * U) = mf;
             }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) cb_cur[kk] = cb_nxt[kk];
         }
-        // ---- forward inter-chunk term: ef * (Hf C^T) ----
+        __syncthreads();  // M complete
+
+        // ---- use ----
+        f32x16 yacc = f32x16{}, yb = f32x16{};
+        // intra-chunk term X^T M^T (fp16 MFMA)
+#pragma unroll
+        for (int kb = 0; kb < Q / 16; ++kb)
+            yacc = mfma16(__builtin_bit_cast(f16x8, frag_tr((const __bf16 *)xn, LX, 16 * kb, 32 * pb)),
+                          *(const f16x8 *)(mt + t_tok * LM + 16 * kb + 8 * half), yacc);
+        // forward inter-chunk term: ef * (Hf C^T)
 #pragma unroll
         for (int kb = 0; kb < S / 16; ++kb)
             yb = mfma(frag_rm(hfl, SS, 32 * pb, 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb);
         {
-            const float ef = ex2(cs_t);
+            const float ef = ex2(s_cs[t_tok]);
 #pragma unroll
             for (int j = 0; j < 16; ++j) yacc[j] += ef * yb[j];
         }
         yb = f32x16{};
-        // ---- backward inter-chunk term: eb * (Hb C^T) ----
+        // backward inter-chunk term: eb * (Hb C^T)
 #pragma unroll
         for (int kb = 0; kb < S / 16; ++kb)
             yb = mfma(frag_rm(hbl, SS, 32 * pb, 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb);
-
-        // ---- store Y = acc + eb * yb (lane: token t_tok, 4 consecutive p per group) ----
-        if (tvalid) {
-            const float eb = ex2(tot_c * LOG2E - ce_t);
-            __bf16 *yrow = y + (trow * nheads + h) * P;
+        const float eb = ex2(tot_c * LOG2E - s_ce[t_tok]);
+        // Y = acc + eb * yb into ybuf (lane: token t_tok, 4 consecutive p per group)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                bf16x4 v4;
+        for (int g4 = 0; g4 < 4; ++g4) {
+            bf16x4 v4;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(yacc[4 * g4 + j] + eb * yb[4 * g4 + j]);
-                *(bf16x4 *)(yrow + 32 * pb + 8 * g4 + 4 * half) = v4;
-            }
+            for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(yacc[4 * g4 + j] + eb * yb[4 * g4 + j]);
+            *(bf16x4 *)&ybuf[t_tok * LY + 32 * pb + 8 * g4 + 4 * half] = v4;
         }
+        if (row_thread) s_rowy[tid] = rowc;
+        __syncthreads();  // ybuf complete; this chunk's other LDS reads are done
+
+        // ---- store, then stage the next chunk ----
+        store_y();
+        if (c + 1 < c_hi) stage();
     }
 }
 
@@ -689,7 +765,8 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
     int nseg, segch, nsegT;
-    size_t perm, dtT, csT, cb, hbl, delta, segF, segB, segA, hinF, hinB, rx, rB, rdt, rdtT, rcsT, total;
+    size_t perm, dtT, csT, cb, b16, cfrag, hbl, delta, segF, segB, segA, hinF, hinB, ytrash, rx, rB, rdt, rdtT, rcsT,
+        total;
 };
 
 Plan make_plan(const SsdProblem &p)
@@ -710,6 +787,8 @@ Plan make_plan(const SsdProblem &p)
     pl.dtT = take(B * Hs * Lpad * 4);
     pl.csT = take(B * Hs * Lpad * 4);
     pl.cb = take(B * p.ngroups * p.nch * Q * Q * 2);
+    pl.b16 = take(B * p.ngroups * p.nch * Q * S * 2);
+    pl.cfrag = take(B * p.ngroups * p.nch * Q * S * 2);
     pl.hbl = take(B * Hs * p.nch * PS * 2);
     pl.delta = take(B * Hs * p.nch * 4);
     pl.segF = take(B * Hs * pl.nsegT * PS * 4);
@@ -717,6 +796,7 @@ Plan make_plan(const SsdProblem &p)
     pl.segA = take(B * Hs * pl.nsegT * 4);
     pl.hinF = take(B * Hs * pl.nseg * PS * 4);
     pl.hinB = take(B * Hs * pl.nseg * PS * 2);
+    pl.ytrash = take((size_t)P * 2);
     if (p.R > 0) {
         const size_t Rpad = (size_t)p.nchR * Q;
         pl.rx = take(B * p.R * Hs * P * 2);
@@ -738,7 +818,8 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
     char *w = (char *)ws;
     uint32_t *perm = (uint32_t *)(w + pl.perm);
     float *dtT = (float *)(w + pl.dtT), *csT = (float *)(w + pl.csT);
-    _Float16 *cb = (_Float16 *)(w + pl.cb);
+    _Float16 *cb = (_Float16 *)(w + pl.cb), *b16 = (_Float16 *)(w + pl.b16);
+    __bf16 *cfrag = (__bf16 *)(w + pl.cfrag);
     __bf16 *hbl = (__bf16 *)(w + pl.hbl);
     float *delta = (float *)(w + pl.delta), *segF = (float *)(w + pl.segF), *segB = (float *)(w + pl.segB);
     float *segA = (float *)(w + pl.segA), *hinF = (float *)(w + pl.hinF);
@@ -792,7 +873,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
     }
     {
         timing::Scope ts_(K_SSD_CB, st);
-        k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, G, N);
+        k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, b16, cfrag, G, N);
     }
     const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
     {
@@ -807,9 +888,9 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
     }
     {
         timing::Scope ts_(K_SSD_OUT, st);
-        k_out<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, Cm, cb, perm, dtT, csT, a.a, a.d, hbl, delta, hinF, hinB,
-                                                   (__bf16 *)a.y, Hs, G, N, Lpad, p.nch, pl.segch, pl.nseg,
-                                                   (uint32_t)items);
+        k_out<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, b16, cfrag, cb, perm, dtT, csT, a.a, a.d, hbl, delta, hinF,
+                                                   hinB, (__bf16 *)a.y, (__bf16 *)(w + pl.ytrash), Hs, G, N, Lpad,
+                                                   p.nch, pl.segch, pl.nseg, (uint32_t)items);
     }
     return hipGetLastError();
 }
