@@ -18,41 +18,107 @@ __device__ __forceinline__ uint32_t seq_row(uint32_t i, int order, uint32_t T, u
 }
 
 // dt in scan order, one row per head, and its within-chunk inclusive cumsum of
-// dt * A. Positions >= L are zero (exact no-ops of the recurrence).
-// grid (nchunks, ceil(nheads / 64), batch), 256 threads.
+// dt * A. Positions >= L are zero (exact no-ops of the recurrence). The rows of
+// a chunk come from `perm` when given (scan position -> canonical token), else
+// from the RMS index (PERM) or the identity.
+// grid (nchunks, ceil(nheads / 64), batch), 256 threads; Q <= 128.
 template <bool PERM>
 __global__ __launch_bounds__(256) void k_prep_dt(const float *__restrict__ dt, const float *__restrict__ A,
                                                  float *__restrict__ dtT, float *__restrict__ csT, int nheads,
                                                  uint32_t L, uint32_t Lpad, int Q, int order, uint32_t T,
-                                                 uint32_t H, uint32_t W)
+                                                 uint32_t H, uint32_t W, const uint32_t *__restrict__ perm = nullptr)
 {
     __shared__ float sdt[kMaxQ][65];
-    __shared__ float scs[kMaxQ][65];
     const uint32_t c = blockIdx.x, b = blockIdx.z;
     const int h0 = blockIdx.y * 64;
     for (int k = threadIdx.x; k < Q * 64; k += 256) {
         const int u = k >> 6, hh = k & 63, h = h0 + hh;
         const uint32_t i = c * Q + u;
         float v = 0.f;
-        if (i < L && h < nheads) v = dt[((size_t)b * L + seq_row<PERM>(i, order, T, H, W)) * nheads + h];
+        if (i < L && h < nheads) {
+            const uint32_t row = perm ? perm[i] : seq_row<PERM>(i, order, T, H, W);
+            v = dt[((size_t)b * L + row) * nheads + h];
+        }
         sdt[u][hh] = v;
     }
     __syncthreads();
-    if (threadIdx.x < 64 && h0 + (int)threadIdx.x < nheads) {
-        const float a = A[h0 + threadIdx.x];
-        float cs = 0.f;
-        for (int u = 0; u < Q; ++u) {
-            cs += sdt[u][threadIdx.x] * a;
-            scs[u][threadIdx.x] = cs;
+    // One wave per head at a time: lane l owns positions 2l and 2l + 1; a wave-wide
+    // inclusive scan of the lane sums gives the cumulative sums.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int hh = wave; hh < 64 && h0 + hh < nheads; hh += 4) {
+        const int h = h0 + hh;
+        const float a = A[h];
+        const int u0 = 2 * lane;
+        const float d0 = u0 < Q ? sdt[u0][hh] : 0.f, d1 = u0 + 1 < Q ? sdt[u0 + 1][hh] : 0.f;
+        const float v0 = d0 * a, v1 = d1 * a;
+        float run = v0 + v1;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_up(run, off, 64);
+            if (lane >= off) run += o;
+        }
+        const float cs1 = run, cs0 = run - v1;
+        if (u0 < Q) {
+            const size_t o = ((size_t)b * nheads + h) * Lpad + (size_t)c * Q + u0;
+            if (u0 + 1 < Q && (Q & 1) == 0) {  // o is even: 8-byte aligned pair
+                *(float2 *)(dtT + o) = make_float2(d0, d1);
+                *(float2 *)(csT + o) = make_float2(cs0, cs1);
+            } else {
+                dtT[o] = d0;
+                csT[o] = cs0;
+                if (u0 + 1 < Q) {
+                    dtT[o + 1] = d1;
+                    csT[o + 1] = cs1;
+                }
+            }
         }
     }
+}
+
+// Whether k_pool_f32x4 applies: 16-byte aligned rows of at most 1024 channels.
+inline bool pool_f32x4_ok(const float *src, int C)
+{
+    return C % 4 == 0 && C / 4 <= 256 && ((uintptr_t)src & 15) == 0;
+}
+
+// Average pool of fp32 rows, 4 channels per thread, several pooled tokens' rows
+// read in parallel per block and reduced through LDS. C must be a multiple of 4
+// and C / 4 <= 256. out[b][j][ch] with j in RMS order `order` of the pooled grid.
+// grid (R, batch), 256 threads.
+template <typename F = float>
+__global__ __launch_bounds__(256) void k_pool_f32x4(const F *__restrict__ src, F *__restrict__ out, int C,
+                                                    uint32_t Tn, uint32_t Hn, uint32_t Wn, int pt, int ph, int pw,
+                                                    int order)
+{
+    __shared__ float4 part[256];
+    const int cg = C / 4, rp = 256 / cg;  // channel groups; rows in flight
+    const int r = threadIdx.x / cg, g = threadIdx.x % cg;
+    const uint32_t j = blockIdx.x, b = blockIdx.y, R = gridDim.x;
+    const uint32_t Tp = Tn / pt, Hp = Hn / ph, Wp = Wn / pw;
+    const uint32_t np = rms_index32(j, order, Tp, Hp, Wp);
+    const uint32_t tq = np / (Hp * Wp), hq = (np / Wp) % Hp, wq = np % Wp;
+    const size_t N = (size_t)Tn * Hn * Wn;
+    const int cnt = pt * ph * pw;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < rp) {
+        for (int e = r; e < cnt; e += rp) {
+            const int dw = e % pw, dh = (e / pw) % ph, dt_ = e / (pw * ph);
+            const size_t n = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw + dw;
+            const float4 v = *(const float4 *)(src + ((size_t)b * N + n) * C + 4 * g);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+    }
+    part[threadIdx.x] = acc;
     __syncthreads();
-    for (int k = threadIdx.x; k < Q * 64; k += 256) {
-        const int hh = k / Q, u = k - hh * Q, h = h0 + hh;
-        if (h >= nheads) continue;
-        const size_t o = ((size_t)b * nheads + h) * Lpad + (size_t)c * Q + u;
-        dtT[o] = sdt[u][hh];
-        csT[o] = scs[u][hh];
+    if (threadIdx.x < cg) {
+        float4 s = part[threadIdx.x];
+        for (int k = 1; k < rp; ++k) {
+            const float4 v = part[k * cg + threadIdx.x];
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
+        const float inv = 1.f / (float)cnt;
+        *(float4 *)(out + ((size_t)b * R + j) * C + 4 * threadIdx.x) =
+            make_float4(s.x * inv, s.y * inv, s.z * inv, s.w * inv);
     }
 }
 
@@ -81,39 +147,77 @@ __global__ __launch_bounds__(256) void k_pool(const E *__restrict__ src, O *__re
 }
 
 // The same average pool on bf16 input, 8 channels (one 16-byte load) per
-// thread; C must be a multiple of 8. Output bf16 (rounded) or fp32.
-// grid (ceil(C / 2048), R, batch).
+// thread; C must be a multiple of 8. Narrow rows (C / 8 < 256) are split over
+// several row slots of the block, reduced through LDS. Output bf16 (rounded) or
+// fp32. grid (ceil(C / 2048), R, batch).
 template <typename O>
 __global__ __launch_bounds__(256) void k_pool8(const bf16_t *__restrict__ src, O *__restrict__ out, int64_t C,
                                                uint32_t Tn, uint32_t Hn, uint32_t Wn, int pt, int ph, int pw,
                                                int order)
 {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const int64_t ch = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-    if (ch >= C) return;
+    __shared__ float part[256][9];
+    const int64_t groups = C / 8;
+    const int cg = groups < 256 ? (int)groups : 256;  // channel groups per block
+    const int rp = 256 / cg;                          // row slots
+    const int r = threadIdx.x / cg, gi = threadIdx.x % cg;
+    const int64_t ch = ((int64_t)blockIdx.x * 256 + gi) * 8;
     const uint32_t j = blockIdx.y, b = blockIdx.z, R = gridDim.y;
     const uint32_t Tp = Tn / pt, Hp = Hn / ph, Wp = Wn / pw;
     const uint32_t np = rms_index32(j, order, Tp, Hp, Wp);
     const uint32_t tq = np / (Hp * Wp), hq = (np / Wp) % Hp, wq = np % Wp;
     const size_t N = (size_t)Tn * Hn * Wn;
+    const int cnt = pt * ph * pw;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int dt_ = 0; dt_ < pt; ++dt_)
-        for (int dh = 0; dh < ph; ++dh) {
-            const size_t row0 = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw;
+    if (rp == 1) {  // wide rows: one slot walks the whole pool block
+        if (ch < C)
+            for (int dt_ = 0; dt_ < pt; ++dt_)
+                for (int dh = 0; dh < ph; ++dh) {
+                    const size_t row0 = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw;
 #pragma unroll 8
-            for (int dw = 0; dw < pw; ++dw) {
-                const u32x4 v = *(const u32x4 *)(src + ((size_t)b * N + row0 + dw) * C + ch);
+                    for (int dw = 0; dw < pw; ++dw) {
+                        const u32x4 v = *(const u32x4 *)(src + ((size_t)b * N + row0 + dw) * C + ch);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += __uint_as_float(v[e] << 16);
-                    acc[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+                        for (int e2 = 0; e2 < 4; ++e2) {
+                            acc[2 * e2] += __uint_as_float(v[e2] << 16);
+                            acc[2 * e2 + 1] += __uint_as_float(v[e2] & 0xffff0000u);
+                        }
+                    }
                 }
+    } else if (r < rp && ch < C) {
+#pragma unroll 4
+        for (int e = r; e < cnt; e += rp) {
+            const int dw = e % pw, dh = (e / pw) % ph, dt_ = e / (pw * ph);
+            const size_t n = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw + dw;
+            const u32x4 v = *(const u32x4 *)(src + ((size_t)b * N + n) * C + ch);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                acc[2 * e2] += __uint_as_float(v[e2] << 16);
+                acc[2 * e2 + 1] += __uint_as_float(v[e2] & 0xffff0000u);
             }
         }
-    const float inv = 1.f / (float)(pt * ph * pw);
-    O *o = out + ((size_t)b * R + j) * C + ch;
+    }
+    const float inv = 1.f / (float)cnt;
+    if (rp == 1) {
+        if (ch < C) {
+            O *o = out + ((size_t)b * R + j) * C + ch;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) elem<O>::store(o + e, acc[e] * inv);
+            for (int e = 0; e < 8; ++e) elem<O>::store(o + e, acc[e] * inv);
+        }
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[threadIdx.x][e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < cg && ch < C) {
+        O *o = out + ((size_t)b * R + j) * C + ch;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float sum = 0.f;
+            for (int k = 0; k < rp; ++k) sum += part[k * cg + threadIdx.x][e];
+            elem<O>::store(o + e, sum * inv);
+        }
+    }
 }
 
 } // namespace ssd

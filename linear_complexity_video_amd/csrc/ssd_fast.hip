@@ -57,6 +57,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -102,6 +103,14 @@ __device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Pins a value at this point of the program: an empty volatile asm that reads and redefines it, so the
+// compiler cannot compute with the value (and wait for the load that produced it) any earlier.
+template <typename T>
+__device__ __forceinline__ void pin(T &v)
+{
+    asm volatile("" : "+v"(v));
+}
+
 // XCD-aware item index of this block (the grid is a multiple of 8).
 __device__ __forceinline__ uint32_t xcd_item()
 {
@@ -130,8 +139,10 @@ __device__ __forceinline__ bf16x8 frag_rm(const __bf16 *tile, int ld, int m_base
 
 // Q token rows of COLS bf16 each, split in 16-byte units over the workgroup.
 // Row u of the chunk is read from global row srow[u] (an LDS table of the
-// chunk's rows; ~0u marks a position past the end, which reads as zero).
-// Loads are unconditional (an invalid row reads row 0 and is then zeroed).
+// chunk's rows; ~0u marks a position past the end). Loads are unconditional:
+// a position past the end reads row 0 of the batch, a finite row that the
+// kernels multiply by that position's weight dt = 0 (or never store), so no
+// select waits on the load.
 template <int Q, int COLS, int NT>
 struct Rows {
     static constexpr int UPR = COLS / 8;
@@ -148,9 +159,7 @@ struct Rows {
 #pragma unroll
         for (int it = 0; it < PER; ++it) {
             const uint32_t row = srow[row_of(it)];
-            const bool ok = row != ~0u;
-            const u32x4 v = *(const u32x4 *)(base + (batch_rows + (ok ? row : 0u)) * row_stride + 8 * cc_of(it));
-            r[it] = ok ? v : u32x4{0, 0, 0, 0};
+            r[it] = *(const u32x4 *)(base + (batch_rows + (row != ~0u ? row : 0u)) * row_stride + 8 * cc_of(it));
         }
     }
     template <int LD>
@@ -188,6 +197,19 @@ __device__ __forceinline__ uint32_t seq_row(const uint32_t *perm, uint32_t i, ui
     return i < L ? (perm ? perm[i] : i) : ~0u;
 }
 
+// Stored local backward states (P x S per chunk) are kept in accumulator order: 16-byte piece k holds
+// the 8 values of accumulator registers 8q..8q+7 of lane l of the 32x32 tile (s-block sb, p-block pt)
+// of G^T, k = ((sb * 2 + pt) * 2 + q) * 64 + l. Those are p = 32 pt + l % 32 and two runs of 4
+// consecutive s starting at s_a = 32 sb + 16 q + 4 (l / 32) and s_a + 8.
+struct HbPiece {
+    int p, s_a;
+};
+__device__ __forceinline__ HbPiece hb_piece(int k)
+{
+    const int l = k & 63, q = (k >> 6) & 1, t = k >> 7;
+    return {32 * (t & 1) + (l & 31), 32 * (t >> 1) + 16 * q + 4 * (l >> 5)};
+}
+
 // ---------------------------------------------------------------------------
 // 0. RMS permutation table: perm[i] = canonical token of scan position i.
 // ---------------------------------------------------------------------------
@@ -201,8 +223,14 @@ __global__ __launch_bounds__(256) void k_perm(uint32_t *__restrict__ perm, uint3
 // ---------------------------------------------------------------------------
 // 1. Right-to-left segment sweep: stored backward chunk states + summaries.
 // grid = 8 * ceil(batch * nseg * nheads / 8); item = (b * nseg + seg) * nheads + h.
+// MAIN: the main sequence (rows through perm; stores the per-chunk states); else the review sequence
+// (rows in order; summaries only).
+// Each wave owns (s-block, p-block) tile pairs: the backward state G^T and the forward sum F^T of the
+// same tile share the B^T operand. Loads of the chunk two to the left are issued every step (clamped at
+// the segment start) and the per-step stores are made by every wave, so the compiler's memory waits are
+// not widened by paths that skip them.
 // ---------------------------------------------------------------------------
-template <int S, int Q>
+template <int S, int Q, bool MAIN>
 __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
                                                   const uint32_t *__restrict__ perm, const float *__restrict__ dtT,
                                                   const float *__restrict__ csT, const float *__restrict__ A,
@@ -214,9 +242,8 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
 {
     constexpr int NT = Q * 4, NW = Q / 16;          // Q/16 waves, two per SIMD at Q = 128
     constexpr int LX = P + XPAD, LB = S + XPAD;
-    // Output tiles G^T and F^T (S/32 x 2 each) over NW/2 waves per matrix.
-    constexpr int TPW = 2 * S / Q;
-    constexpr int PBW = TPW >= 2 ? 2 : 1, SBW = TPW >= 2 ? TPW / 2 : 1;
+    constexpr int PAIRS = S / 16;                   // tile pairs: (S/32 s-blocks) x (2 p-blocks)
+    constexpr int TP = PAIRS >= NW ? PAIRS / NW : 1;
     __shared__ __bf16 xb[Q * LX];   // x * dt exp(ce)              (backward weights)
     __shared__ __bf16 xf[Q * LX];   // x * dt exp(tot - cs + logD) (forward weights)
     __shared__ __bf16 bn[Q * LB];   // B
@@ -230,18 +257,13 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
     const int g = h / (nheads / G);
     const int c_lo = seg * segch, c_hi = min(nch, c_lo + segch);
 
-    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool isF = wave >= NW / 2;       // first half of the waves: backward state G^T; second: forward sum F^T
-    const int wg = wave % (NW / 2);
-    const int sb0 = PBW == 2 ? wg * SBW : wg >> 1;
-    const int pb0 = PBW == 2 ? 0 : (wg & 1);
-    const bool row_thread = wave < Q / 64; // tid < Q: owns one row-table entry
-    f32x16 acc[SBW][PBW];
+    const bool active = PAIRS >= NW || wave * TP < PAIRS;  // every wave when there are enough pairs
+    const bool row_thread = wave < Q / 64;  // tid < Q: owns one row-table entry
+    f32x16 accG[TP], accF[TP];
 #pragma unroll
-    for (int i = 0; i < SBW; ++i)
-#pragma unroll
-        for (int j = 0; j < PBW; ++j) acc[i][j] = f32x16{};
+    for (int i = 0; i < TP; ++i) accG[i] = accF[i] = f32x16{};
 
     const float a = A[h];
     const size_t bh = (size_t)b * nheads + h;
@@ -254,48 +276,69 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
         float tot;
     };
     Stage st0, st1;
-    uint32_t pnext = ~0u;  // row-table entry of the chunk after the one being fetched
+    uint32_t pnext = 0u;  // row-table entry of the chunk after the one fetched last
+    bool pvalid = false;
     auto fetch = [&](Stage &stg, int c) {
+        // The row-table load first: the compiler may move its use above the next barrier, and a wait for
+        // it then covers only older loads.
+        const uint32_t i = (uint32_t)(c - 1) * Q + (tid & (Q - 1));
+        pvalid = c > c_lo && i < L;
+        if constexpr (MAIN)
+            pnext = perm[pvalid ? i : 0u];  // selected against pvalid where it is stored
+        else
+            pnext = i;
         stg.xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
         stg.br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * L);
 #pragma unroll
         for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) {
-            const size_t i = drow + (size_t)c * Q + Rows<Q, P, NT>::row_of(it);
-            stg.wd[it] = dtT[i];
-            stg.wc[it] = csT[i];
+            const size_t i2 = drow + (size_t)c * Q + Rows<Q, P, NT>::row_of(it);
+            stg.wd[it] = dtT[i2];
+            stg.wc[it] = csT[i2];
         }
         stg.tot = csT[drow + (size_t)c * Q + Q - 1];
-        if (row_thread) pnext = c > c_lo ? seq_row(perm, (uint32_t)(c - 1) * Q + tid, L) : ~0u;
     };
     // Prologue: rows and data of the two rightmost chunks.
-    if (row_thread) s_row[tid] = seq_row(perm, (uint32_t)(c_hi - 1) * Q + tid, L);
+    if (row_thread) s_row[tid] = seq_row(MAIN ? perm : nullptr, (uint32_t)(c_hi - 1) * Q + tid, L);
     __syncthreads();
     fetch(st0, c_hi - 1);
     __syncthreads();
-    if (row_thread) s_row[tid] = pnext;
+    if (row_thread) s_row[tid] = pvalid ? pnext : ~0u;
     __syncthreads();
-    if (c_hi - 2 >= c_lo) fetch(st1, c_hi - 2);
+    fetch(st1, max(c_hi - 2, c_lo));
     float logD = 0.f;  // sum of dt*A over the chunks right of the current one
 
     auto step = [&](Stage &cur, int c) {
-        // Backward state entering chunk c from the right.
-        if (hb_local && !isF) {
-            __bf16 *dst = hb_local + (bh * nch + c) * (size_t)(P * S);
+        if constexpr (MAIN) {
+            // Backward state entering chunk c from the right, in accumulator order (see hb_piece).
+            if (active) {
+                __bf16 *dst = hb_local + (bh * nch + c) * (size_t)(P * S);
 #pragma unroll
-            for (int i = 0; i < SBW; ++i)
+                for (int i = 0; i < TP; ++i) {
+                    const int j = wave * TP + i;
 #pragma unroll
-                for (int pb = 0; pb < PBW; ++pb)
+                    for (int q = 0; q < 2; ++q) {
+                        bf16x8 v8;
 #pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        bf16x4 v4;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) v4[j] = (__bf16)acc[i][pb][4 * g4 + j];
-                        *(bf16x4 *)(dst + (32 * (pb0 + pb) + col) * S + 32 * (sb0 + i) + 8 * g4 + 4 * half) = v4;
+                        for (int e = 0; e < 8; ++e) v8[e] = (__bf16)accG[i][8 * q + e];
+                        *(bf16x8 *)(dst + ((j * 2 + q) * 64 + lane) * 8) = v8;
                     }
+                }
+            }
+            delta[bh * nch + c] = ex2(logD * LOG2E);  // every thread writes the same value
         }
-        if (delta && tid == 0) delta[bh * nch + c] = ex2(logD * LOG2E);
 
         __syncthreads();  // previous chunk's MFMA reads of LDS and the row-table reads are done
+        // The staged values are used from here on (their loads had two steps to complete).
+#pragma unroll
+        for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) {
+            pin(cur.xr.r[it]);
+            pin(cur.wd[it]);
+            pin(cur.wc[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < Rows<Q, S, NT>::PER; ++it) pin(cur.br.r[it]);
+        pin(cur.tot);
+        pin(pnext);
         const float tot_c = cur.tot;
 #pragma unroll
         for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) {
@@ -304,47 +347,51 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
             cur.xr.template store_scaled<LX>(xf, it, d * ex2((tot_c - cs + logD) * LOG2E));
         }
         cur.br.template store<LB>(bn);
-        if (row_thread) s_row[tid] = pnext;
+        // Every thread stores its (identical) entry: a use on all paths keeps the row load where it is issued.
+        s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
         __syncthreads();
 
-        if (c - 2 >= c_lo) fetch(cur, c - 2);
-        if (!isF) {
+        fetch(cur, max(c - 2, c_lo));  // at the segment start: issued, unused
+        if (active) {
             const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
-            for (int i = 0; i < SBW; ++i)
+            for (int i = 0; i < TP; ++i) accG[i] *= dec;
 #pragma unroll
-                for (int j = 0; j < PBW; ++j) acc[i][j] *= dec;
-        }
-        const __bf16 *xs = isF ? xf : xb;
+            for (int kb = 0; kb < Q / 16; ++kb) {
 #pragma unroll
-        for (int kb = 0; kb < Q / 16; ++kb) {
-            bf16x8 af[SBW], bfr[PBW];
-#pragma unroll
-            for (int i = 0; i < SBW; ++i) af[i] = frag_tr(bn, LB, 16 * kb, 32 * (sb0 + i));
-#pragma unroll
-            for (int pb = 0; pb < PBW; ++pb) bfr[pb] = frag_tr(xs, LX, 16 * kb, 32 * (pb0 + pb));
-#pragma unroll
-            for (int i = 0; i < SBW; ++i)
-#pragma unroll
-                for (int pb = 0; pb < PBW; ++pb) acc[i][pb] = mfma(af[i], bfr[pb], acc[i][pb]);
+                for (int i = 0; i < TP; ++i) {
+                    const int j = wave * TP + i;
+                    const bf16x8 af = frag_tr(bn, LB, 16 * kb, 32 * (j >> 1));
+                    accG[i] = mfma(af, frag_tr(xb, LX, 16 * kb, 32 * (j & 1)), accG[i]);
+                    accF[i] = mfma(af, frag_tr(xf, LX, 16 * kb, 32 * (j & 1)), accF[i]);
+                }
+            }
         }
         logD += tot_c;
     };
-    for (int c = c_hi - 1; c >= c_lo; c -= 2) {
+    int c = c_hi - 1;
+    for (; c - 1 >= c_lo; c -= 2) {
         step(st0, c);
-        if (c - 1 >= c_lo) step(st1, c - 1);
+        step(st1, c - 1);
     }
+    if (c >= c_lo) step(st0, c);
 
-    float *dst = (isF ? segF : segB) + (bh * nseg_total + seg_base + seg) * (size_t)(P * S);
+    // Segment summaries: G (backward state entering the segment from its right end, from zero) and F.
+    if (active) {
+        const int col = lane & 31, half = lane >> 5;
+        float *dG = segB + (bh * nseg_total + seg_base + seg) * (size_t)(P * S);
+        float *dF = segF + (bh * nseg_total + seg_base + seg) * (size_t)(P * S);
 #pragma unroll
-    for (int i = 0; i < SBW; ++i)
-#pragma unroll
-        for (int pb = 0; pb < PBW; ++pb)
+        for (int i = 0; i < TP; ++i) {
+            const int j = wave * TP + i, sb = j >> 1, pb = j & 1;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                f32x4 v4 = {acc[i][pb][4 * g4], acc[i][pb][4 * g4 + 1], acc[i][pb][4 * g4 + 2], acc[i][pb][4 * g4 + 3]};
-                *(f32x4 *)(dst + (32 * (pb0 + pb) + col) * S + 32 * (sb0 + i) + 8 * g4 + 4 * half) = v4;
+                const size_t o = (size_t)(32 * pb + col) * S + 32 * sb + 8 * g4 + 4 * half;
+                *(f32x4 *)(dG + o) = f32x4{accG[i][4 * g4], accG[i][4 * g4 + 1], accG[i][4 * g4 + 2], accG[i][4 * g4 + 3]};
+                *(f32x4 *)(dF + o) = f32x4{accF[i][4 * g4], accF[i][4 * g4 + 1], accF[i][4 * g4 + 2], accF[i][4 * g4 + 3]};
             }
+        }
+    }
     if (tid == 0) segA[bh * nseg_total + seg_base + seg] = logD;
 }
 
@@ -539,11 +586,17 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
     }
     // Border state of the backward direction (bf16), for this thread's staging chunks.
     constexpr int HBC = PS / 8 / NT;  // 16-byte chunks of Hb per thread
+    // (pieces in the stored states' accumulator order; see hb_piece)
     u32x4 hinb[HBC];
     {
         const __bf16 *src = hinB + (bh * nseg + seg) * (size_t)PS;
 #pragma unroll
-        for (int it = 0; it < HBC; ++it) hinb[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
+        for (int it = 0; it < HBC; ++it) {
+            const HbPiece pc = hb_piece(tid + NT * it);
+            const u32x2 lo = *(const u32x2 *)(src + pc.p * S + pc.s_a);
+            const u32x2 hi = *(const u32x2 *)(src + pc.p * S + pc.s_a + 8);
+            hinb[it] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
     }
 
     Rows<Q, P, NT> xr;
@@ -604,13 +657,13 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
         }
 #pragma unroll
         for (int it = 0; it < HBC; ++it) {
-            const int k = tid + NT * it;
-            const int p = k / (S / 8), s0 = 8 * (k % (S / 8));
+            const HbPiece pc = hb_piece(tid + NT * it);
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 o[e] = pack2(lo_f(hbr[it][e]) + dl * lo_f(hinb[it][e]), hi_f(hbr[it][e]) + dl * hi_f(hinb[it][e]));
-            *(u32x4 *)&hbl[p * SS + s0] = o;
+            *(u32x2 *)&hbl[pc.p * SS + pc.s_a] = u32x2{o[0], o[1]};
+            *(u32x2 *)&hbl[pc.p * SS + pc.s_a + 8] = u32x2{o[2], o[3]};
         }
 #pragma unroll
         for (int U = 0; U < UB; ++U) *(u32x4 *)(mt + mrow * LM + 32 * U + 8 * msub) = cbr[U];
@@ -846,8 +899,12 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
         }
         {
             timing::Scope ts_(K_SSD_POOL, st);
-            ssd::k_pool<float, float><<<dim3((Hs + 255) / 256, R, Bn), 256, 0, st>>>(
-                a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+            if (ssd::pool_f32x4_ok(a.dt, Hs))
+                ssd::k_pool_f32x4<<<dim3(R, Bn), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w,
+                                                              p.order);
+            else
+                ssd::k_pool<float, float><<<dim3((Hs + 255) / 256, R, Bn), 256, 0, st>>>(
+                    a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
         }
         {
             timing::Scope ts_(K_SSD_PREP, st);
@@ -857,7 +914,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
         const uint64_t items = (uint64_t)Bn * Hs;
         {
             timing::Scope ts_(K_SSD_STATES, st);
-            k_states<S, Q><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, rdtT, rcsT,
+            k_states<S, Q, false><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, rdtT, rcsT,
                                                           a.a, nullptr, nullptr, segF, segB, segA, Hs, G, R, Rpad,
                                                           p.nchR, p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)items);
         }
@@ -869,7 +926,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
     {
         timing::Scope ts_(K_SSD_PREP, st);
         ssd::k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, Bn), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q,
-                                                                             p.order, T, H, W);
+                                                                             p.order, T, H, W, perm);
     }
     {
         timing::Scope ts_(K_SSD_CB, st);
@@ -878,7 +935,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
     const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
     {
         timing::Scope ts_(K_SSD_STATES, st);
-        k_states<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
+        k_states<S, Q, true><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
                                                       N, Lpad, p.nch, pl.segch, pl.nseg, 0, pl.nsegT, (uint32_t)items);
     }
     {

@@ -27,6 +27,8 @@ namespace {
 using ssd::kMaxQ;
 using ssd::k_pool;
 using ssd::k_prep_dt;
+using ssd::k_pool_f32x4;
+using ssd::pool_f32x4_ok;
 using ssd::seq_row;
 
 
@@ -352,7 +354,11 @@ static hipError_t run_portable(const SsdProblem &p, const SsdArgs &a, void *ws, 
         }
         {
             timing::Scope ts_(K_SSD_POOL, st);
-            k_pool<float, float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+            if (pool_f32x4_ok(a.dt, Hs))
+                k_pool_f32x4<<<dim3(R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+            else
+                k_pool<float, float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t,
+                                                                                  p.pool_h, p.pool_w, p.order);
         }
         {
             timing::Scope ts_(K_SSD_PREP, st);
