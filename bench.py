@@ -225,10 +225,22 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value / 1e6:.3f} M tokens/s; "
         f"output sweep {t_out * 1e3:.3f} ms over {out_launches} launches")
 
-    # Per-call timings with events on the launch stream (torch's current stream).
+    # Per-kernel timings: the library brackets each launch of the named kernel with HIP events on its
+    # stream (host launch latency of the Python calls is not included). A whole scan call is timed with
+    # events on torch's current stream, which it launches on.
     stream = torch.cuda.current_stream()
 
+    def time_kernel(kernel, fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        B.mate_timing_begin(kernel)
+        for _ in range(reps):
+            fn()
+        n, ms = B.mate_timing_end()
+        return ms / max(1, n) * 1e-3
+
     def time_call(fn, reps):
+        fn()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in ev:
             a.record(stream)
@@ -239,13 +251,17 @@ def main():
 
     w = work(wl)
     reps = args.kernel_reps
-    t_tesa = {sh: time_call(lambda sh=sh: B.mate_tesa(att["q"], att["k"], att["v"], att["o"], wl.window,
-                                                      wl.layer_shift(sh), 0.0, algo), reps) for sh in (False, True)}
+    t_tesa = {sh: time_kernel("tesa", lambda sh=sh: B.mate_tesa(att["q"], att["k"], att["v"], att["o"], wl.window,
+                                                                wl.layer_shift(sh), 0.0, algo), reps)
+              for sh in (False, True)}
     t_ssd = time_call(lambda: B.mate_bissd_scan(ssd["x"], ssd["b"], ssd["c"], ssd["dt"], ssd["a"], ssd["d"],
                                                 ssd["y"], 0, wl.chunk, wl.pool, algo, workspace=ws), reps)
     xr = ssd["x"].view(wl.batch, wl.N, -1)
     xo = torch.empty_like(xr)
-    t_rms = time_call(lambda: B.mate_rms_reorder(xr, xo, wl.grid, 1, True, False), reps)
+    t_rms = time_kernel("rms_reorder", lambda: B.mate_rms_reorder(xr, xo, wl.grid, 1, True, False), reps)
+    t_states = time_kernel("ssd_states", lambda: B.mate_bissd_scan(ssd["x"], ssd["b"], ssd["c"], ssd["dt"], ssd["a"],
+                                                                   ssd["d"], ssd["y"], 0, wl.chunk, wl.pool, algo,
+                                                                   workspace=ws), reps)
 
     peak_flops = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
     tesa_tf = w["tesa_flops"][False] / t_tesa[False] / 1e12
@@ -255,6 +271,7 @@ def main():
     kernels = {
         "ssd_out_sweep": {"ms": t_out * 1e3, "tflops": out_tf, "mfma_frac": out_tf / peak_flops, "gbs": out_gbs,
                           "hbm_frac": out_gbs / PEAK_HBM_GBS, "launches_timed": out_launches},
+        "ssd_states_sweep_avg_of_review_and_main": {"ms": t_states * 1e3},
         "bissd_call": {"ms": t_ssd * 1e3, "tflops": ssd_tf, "mfma_frac": ssd_tf / peak_flops,
                        "hbm_frac": w["ssd_bytes"] / t_ssd / 1e9 / PEAK_HBM_GBS},
         "tesa_unshifted": {"ms": t_tesa[False] * 1e3, "tflops": tesa_tf, "mfma_frac": tesa_tf / peak_flops,

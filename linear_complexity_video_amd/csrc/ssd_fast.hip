@@ -210,6 +210,15 @@ __device__ __forceinline__ HbPiece hb_piece(int k)
     return {32 * (t & 1) + (l & 31), 32 * (t >> 1) + 16 * q + 4 * (l >> 5)};
 }
 
+// CB of a chunk is stored in 8-element pieces in the order the output sweep reads them: thread lane l
+// of wave w (Q/16 waves) owns row t = 16 w + l % 16 and, in every 32-column block U, columns
+// 32 U + 8 (l / 16) + 0..7. Returns the element offset of piece (t, U, m = (u % 32) / 8).
+template <int Q>
+__device__ __forceinline__ int cb_piece(int t, int U, int m)
+{
+    return (((U * (Q / 16) + (t >> 4)) * 64) + (t & 15) + 16 * m) * 8;
+}
+
 // ---------------------------------------------------------------------------
 // 0. RMS permutation table: perm[i] = canonical token of scan position i.
 // ---------------------------------------------------------------------------
@@ -423,7 +432,8 @@ __global__ __launch_bounds__(256) void k_seg_pass(const float *__restrict__ segF
 
 // ---------------------------------------------------------------------------
 // 3. Per chunk and group (grid (nch, G, batch)), for the output sweep:
-//    cb    CB[t][u] = C_t . B_u (fp16), computed as CB^T = B C^T so each lane holds 4 consecutive u of one t;
+//    cb    CB[t][u] = C_t . B_u (fp16), computed as CB^T = B C^T so each lane holds 4 consecutive u of one t,
+//          stored in the output sweep's piece order (cb_piece);
 //    b16   the chunk's B rows in scan order, as fp16 ([Q][S]);
 //    cfrag the chunk's C rows in MFMA operand order: for token block tb and k-block kb, lane l's 8 values
 //          C[32 tb + l % 32][16 kb + 8 (l / 32) + 0..7] are the l-th 16 bytes of a 1 KB block, so the sweep
@@ -460,14 +470,14 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
             bv = tok ? bv : u32x4{0, 0, 0, 0};
             acc = mfma(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc);
         }
-        // acc: rows u = 32ub + 8g4 + 4half + j, column t = 32tb + col
+        // acc: rows u = 32ub + 8g4 + 4half + j, column t = 32tb + col; stored in piece order (see cb_piece)
         const int t = 32 * tb + col;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             f16x4 v4;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v4[j] = (_Float16)acc[4 * g4 + j];
-            *(f16x4 *)(out + (size_t)t * Q + 32 * ub + 8 * g4 + 4 * half) = v4;
+            *(f16x4 *)(out + cb_piece<Q>(t, ub, g4) + 4 * half) = v4;
         }
     }
     // B rows as fp16 (exact for bf16 values in fp16's normal range) and C rows in operand order.
@@ -556,9 +566,10 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
     const bool row_thread = wave < Q / 64;  // tid < Q
     // One Y^T tile per wave: t-block wave / 2, p-block wave % 2.
     const int tb = wave >> 1, pb = wave & 1;
-    // Role in building M: row mrow, columns 32 U + 8 msub + 0..7 for every block U;
-    // the wave's rows 16 wave .. 16 wave + 15 all lie in row block wave / 2.
-    const int mrow = tid >> 2, msub = tid & 3, mtb = wave >> 1;
+    // Role in building M: row mrow, columns 32 U + 8 msub + 0..7 for every block U (one row per lane of
+    // each 16-lane group, so LDS accesses of a group hit distinct banks); the wave's rows
+    // 16 wave .. 16 wave + 15 all lie in row block wave / 2.
+    const int mrow = 16 * wave + (lane & 15), msub = lane >> 4, mtb = wave >> 1;
     // Hf^T tiles (S/32 s-blocks x 2 p-blocks) over the waves: HT per wave, or one
     // tile for the first S/16 waves when there are fewer tiles than waves.
     constexpr int HTILES = S / 16;
@@ -612,17 +623,15 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
     float tok_d = 0.f, tok_c = 0.f, tot = 0.f, dl = 0.f;
     uint32_t pnext = 0u;
     bool pvalid = false;
+    // The next chunk's data comes in two groups: per-head data that misses to HBM (x, the stored
+    // states, per-token values) early in the build phase, and the chunk's group data that other
+    // heads have just read (B, CB; L2-resident) in the use phase, where it overlaps the MFMAs
+    // instead of queueing in one burst before them.
     auto fetch = [&](int c) {
         xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * N);
-        const _Float16 *bsrc = b16 + (gch + c) * (size_t)(Q * S);
-#pragma unroll
-        for (int it = 0; it < BPER; ++it) bru[it] = *(const u32x4 *)(bsrc + 8 * (tid + NT * it));
         const __bf16 *src = hb_local + (bh * nch + c) * (size_t)PS;
 #pragma unroll
         for (int it = 0; it < HBC; ++it) hbr[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
-        const _Float16 *cbs = cb + (gch + c) * (size_t)(Q * Q) + (size_t)mrow * Q + 8 * msub;
-#pragma unroll
-        for (int U = 0; U < UB; ++U) cbr[U] = *(const u32x4 *)(cbs + 32 * U);
         // Every thread issues the same loads; the per-token values matter for tid < Q only.
         const int tq = tid & (Q - 1);
         const size_t crow0 = drow + (size_t)c * Q;
@@ -635,6 +644,14 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
         }
         tot = csT[crow0 + Q - 1];
         dl = delta[bh * nch + c];
+    };
+    auto fetch_group = [&](int c) {
+        const _Float16 *bsrc = b16 + (gch + c) * (size_t)(Q * S);
+#pragma unroll
+        for (int it = 0; it < BPER; ++it) bru[it] = *(const u32x4 *)(bsrc + 8 * (tid + NT * it));
+        const _Float16 *cbs = cb + (gch + c) * (size_t)(Q * Q) + 8 * (size_t)tid;  // cb_piece(mrow, U, msub)
+#pragma unroll
+        for (int U = 0; U < UB; ++U) cbr[U] = *(const u32x4 *)(cbs + U * (Q / 16) * 512);
     };
     uint32_t rowc = 0u;  // row-thread: global row of token tid of the staged chunk (~0u past the end)
     auto stage = [&]() {
@@ -707,6 +724,7 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
     if (row_thread) s_row[tid] = seq_row(perm, (uint32_t)c_lo * Q + tid, N);
     __syncthreads();
     fetch(c_lo);
+    fetch_group(c_lo);
     __syncthreads();
     stage();
 
@@ -776,6 +794,7 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
         __syncthreads();  // M complete
 
         // ---- use ----
+        fetch_group(cn);
         f32x16 yacc = f32x16{}, yb = f32x16{};
         // intra-chunk term X^T M^T (fp16 MFMA)
 #pragma unroll

@@ -2,7 +2,8 @@
 // each (shifted) 3D window.
 //
 // Work item = (window, head, block of 256 queries); a workgroup of 8 waves
-// owns one item, each wave 32 queries. Keys and values stream through LDS in
+// owns one item, each wave 32 queries. The canonical token of every window
+// position is tabulated in LDS once per item. Keys and values stream through LDS in
 // tiles of 64 (double buffered, both in their natural row layout; the V^T
 // operand is read with the gfx950 LDS transpose read). Per tile each wave
 // computes S^T = K Q^T, so that a lane holds one query's scores and the
@@ -48,10 +49,13 @@ __device__ __forceinline__ void region_extent(int r, int D, int w, int s, int &l
     if (hi > D) hi = D;
 }
 
+constexpr int MAXW = 4096;        // largest window (tokens) of the MFMA kernel
+
 template <int DH>
-struct Smem {
+struct __attribute__((aligned(16))) Smem {
     __bf16 k[2][KT][DH + KPAD];
     __bf16 v[2][KT][DH + VPAD];
+    uint32_t row[MAXW];           // canonical token of each window position
 };
 
 // A operand of O^T += V^T P^T from the row-major V tile: lane l gets column
@@ -111,6 +115,9 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     };
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // Canonical token of every window position, computed once (the tile loader only looks it up).
+    for (int l = tid; l < m; l += 512) sm.row[l] = (uint32_t)token(l);
+    __syncthreads();
     const int half = lane >> 5, col = lane & 31;
     const int qi = q_base + wave * QW + col;
     const bool qvalid = qi < m;
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     // Q^T fragments (B operand of S^T = K Q^T): query col, d = 16 kb + 8 half + 0..7.
     bf16x8 qf[DH / 16];
     {
-        const __bf16 *qrow = q + head_off + token(qvalid ? qi : 0) * rowstride;
+        const __bf16 *qrow = q + head_off + (size_t)sm.row[qvalid ? qi : 0] * rowstride;
 #pragma unroll
         for (int kb = 0; kb < DH / 16; ++kb) {
             u32x4 raw = qvalid ? *(const u32x4 *)(qrow + 16 * kb + 8 * half) : u32x4{0, 0, 0, 0};
@@ -135,7 +142,8 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
 
     // Tile loader: K and V rows as 16-byte chunks, natural layout.
     constexpr int KCH = KT * DC;                  // chunks per tile
-    constexpr int KPER = (KCH + 511) / 512;       // per thread
+    constexpr int KPER = KCH / 512;               // per thread
+    static_assert(KCH % 512 == 0, "tile chunks must split evenly over the workgroup");
     u32x4 kreg[KPER], vreg[KPER];
     auto fetch = [&](int kt) {
 #pragma unroll
@@ -143,20 +151,18 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
             const int c = tid + 512 * it;
             const int jj = c / DC, dc = c % DC;
             const int kidx = kt * KT + jj;
-            const bool ok = c < KCH && kidx < m;
-            const size_t off = ok ? head_off + token(kidx) * rowstride + 8 * dc : 0;
-            kreg[it] = ok ? *(const u32x4 *)(k + off) : u32x4{0, 0, 0, 0};
-            vreg[it] = ok ? *(const u32x4 *)(v + off) : u32x4{0, 0, 0, 0};
+            // A key past the window reads the window's first key: finite, and its score is masked.
+            const size_t off = head_off + (size_t)sm.row[kidx < m ? kidx : 0] * rowstride + 8 * dc;
+            kreg[it] = *(const u32x4 *)(k + off);
+            vreg[it] = *(const u32x4 *)(v + off);
         }
     };
     auto stash = [&](int buf) {
 #pragma unroll
         for (int it = 0; it < KPER; ++it) {
             const int c = tid + 512 * it;
-            if (c < KCH) {
-                *(u32x4 *)&sm.k[buf][c / DC][8 * (c % DC)] = kreg[it];
-                *(u32x4 *)&sm.v[buf][c / DC][8 * (c % DC)] = vreg[it];
-            }
+            *(u32x4 *)&sm.k[buf][c / DC][8 * (c % DC)] = kreg[it];
+            *(u32x4 *)&sm.v[buf][c / DC][8 * (c % DC)] = vreg[it];
         }
     };
 
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     const float lt = lrun + __shfl_xor(lrun, 32);
     if (qvalid) {
         const float inv = 1.f / lt;
-        __bf16 *orow = o + head_off + token(qi) * rowstride;
+        __bf16 *orow = o + head_off + (size_t)sm.row[qi] * rowstride;
 #pragma unroll
         for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
