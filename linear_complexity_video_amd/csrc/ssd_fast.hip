@@ -232,15 +232,18 @@ __global__ __launch_bounds__(256) void k_perm(uint32_t *__restrict__ perm, uint3
 // ---------------------------------------------------------------------------
 // 1. Right-to-left segment sweep: stored backward chunk states + summaries.
 // grid = 8 * ceil(batch * nseg * nheads / 8); item = (b * nseg + seg) * nheads + h.
-// MAIN: the main sequence (rows through perm; stores the per-chunk states); else the review sequence
-// (rows in order; summaries only).
+// MAIN: the main sequence (x rows through perm, B from the fp16 scan-order copy; stores the per-chunk
+// states); else the review sequence (rows in order, B pooled bf16; summaries only).
 // Each wave owns (s-block, p-block) tile pairs: the backward state G^T and the forward sum F^T of the
-// same tile share the B^T operand. Loads of the chunk two to the left are issued every step (clamped at
-// the segment start) and the per-step stores are made by every wave, so the compiler's memory waits are
-// not widened by paths that skip them.
+// same tile share both operand tiles, B^T and x (fp16); the per-token weights of the two sums,
+// dt exp(ce) and dt exp(tot - cs + logD), are applied to the x operand in registers (packed fp16).
+// Loads of the chunk two to the left are issued every step (clamped at the segment start) and the
+// per-step stores are made by every wave, so the compiler's memory waits are not widened by paths that
+// skip them.
 // ---------------------------------------------------------------------------
 template <int S, int Q, bool MAIN>
 __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
+                                                  const _Float16 *__restrict__ b16,
                                                   const uint32_t *__restrict__ perm, const float *__restrict__ dtT,
                                                   const float *__restrict__ csT, const float *__restrict__ A,
                                                   __bf16 *__restrict__ hb_local, float *__restrict__ delta,
@@ -253,10 +256,11 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
     constexpr int LX = P + XPAD, LB = S + XPAD;
     constexpr int PAIRS = S / 16;                   // tile pairs: (S/32 s-blocks) x (2 p-blocks)
     constexpr int TP = PAIRS >= NW ? PAIRS / NW : 1;
-    __shared__ __bf16 xb[Q * LX];   // x * dt exp(ce)              (backward weights)
-    __shared__ __bf16 xf[Q * LX];   // x * dt exp(tot - cs + logD) (forward weights)
-    __shared__ __bf16 bn[Q * LB];   // B
-    __shared__ uint32_t s_row[Q];   // global rows of the next chunk to fetch
+    constexpr int BPER = Q * S / 8 / NT;            // 16-byte pieces of the B tile per thread
+    __shared__ _Float16 xn[Q * LX];   // x (fp16)
+    __shared__ _Float16 bn[Q * LB];   // B (fp16)
+    __shared__ __attribute__((aligned(16))) _Float16 s_wb[Q], s_wf[Q];  // per-token weights
+    __shared__ uint32_t s_row[Q];     // global rows of the next chunk to fetch
 
     const uint32_t item = xcd_item();
     if (item >= total_items) return;
@@ -266,10 +270,10 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
     const int g = h / (nheads / G);
     const int c_lo = seg * segch, c_hi = min(nch, c_lo + segch);
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool active = PAIRS >= NW || wave * TP < PAIRS;  // every wave when there are enough pairs
-    const bool row_thread = wave < Q / 64;  // tid < Q: owns one row-table entry
+    const bool row_thread = wave < Q / 64;  // tid < Q: owns one row-table entry and one token's weights
     f32x16 accG[TP], accF[TP];
 #pragma unroll
     for (int i = 0; i < TP; ++i) accG[i] = accF[i] = f32x16{};
@@ -277,43 +281,46 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
     const float a = A[h];
     const size_t bh = (size_t)b * nheads + h;
     const size_t drow = bh * Lpad;
+    const size_t gch = ((size_t)b * G + g) * nch;
     // Chunk data is fetched two chunks ahead into two alternating register stages.
     struct Stage {
         Rows<Q, P, NT> xr;
-        Rows<Q, S, NT> br;
-        float wd[Rows<Q, P, NT>::PER], wc[Rows<Q, P, NT>::PER];
-        float tot;
+        u32x4 bq[BPER];  // B pieces k = tid + NT it: row k / (S / 8), 8 columns at 8 (k % (S / 8))
+        float tok_d, tok_c, tot;
     };
-    Stage st0, st1;
+    Stage st0;
     uint32_t pnext = 0u;  // row-table entry of the chunk after the one fetched last
     bool pvalid = false;
     auto fetch = [&](Stage &stg, int c) {
         // The row-table load first: the compiler may move its use above the next barrier, and a wait for
         // it then covers only older loads.
-        const uint32_t i = (uint32_t)(c - 1) * Q + (tid & (Q - 1));
+        const int tq = tid & (Q - 1);
+        const uint32_t i = (uint32_t)(c - 1) * Q + tq;
         pvalid = c > c_lo && i < L;
         if constexpr (MAIN)
             pnext = perm[pvalid ? i : 0u];  // selected against pvalid where it is stored
         else
             pnext = i;
         stg.xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
-        stg.br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * L);
+        if constexpr (MAIN) {
+            const _Float16 *src = b16 + (gch + c) * (size_t)(Q * S);
 #pragma unroll
-        for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) {
-            const size_t i2 = drow + (size_t)c * Q + Rows<Q, P, NT>::row_of(it);
-            stg.wd[it] = dtT[i2];
-            stg.wc[it] = csT[i2];
+            for (int it = 0; it < BPER; ++it) stg.bq[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
+        } else {
+            Rows<Q, S, NT> br;
+            br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * L);
+#pragma unroll
+            for (int it = 0; it < BPER; ++it) stg.bq[it] = br.r[it];
         }
-        stg.tot = csT[drow + (size_t)c * Q + Q - 1];
+        const size_t crow0 = drow + (size_t)c * Q;
+        stg.tok_d = dtT[crow0 + tq];
+        stg.tok_c = csT[crow0 + tq];
+        stg.tot = csT[crow0 + Q - 1];
     };
-    // Prologue: rows and data of the two rightmost chunks.
+    // Prologue: rows and data of the rightmost chunk.
     if (row_thread) s_row[tid] = seq_row(MAIN ? perm : nullptr, (uint32_t)(c_hi - 1) * Q + tid, L);
     __syncthreads();
     fetch(st0, c_hi - 1);
-    __syncthreads();
-    if (row_thread) s_row[tid] = pvalid ? pnext : ~0u;
-    __syncthreads();
-    fetch(st1, max(c_hi - 2, c_lo));
     float logD = 0.f;  // sum of dt*A over the chunks right of the current one
 
     auto step = [&](Stage &cur, int c) {
@@ -337,57 +344,62 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
         }
 
         __syncthreads();  // previous chunk's MFMA reads of LDS and the row-table reads are done
-        // The staged values are used from here on (their loads had two steps to complete).
+        // The staged values are used from here on (their loads had a step to complete).
 #pragma unroll
-        for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) {
-            pin(cur.xr.r[it]);
-            pin(cur.wd[it]);
-            pin(cur.wc[it]);
-        }
+        for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) pin(cur.xr.r[it]);
 #pragma unroll
-        for (int it = 0; it < Rows<Q, S, NT>::PER; ++it) pin(cur.br.r[it]);
+        for (int it = 0; it < BPER; ++it) pin(cur.bq[it]);
+        pin(cur.tok_d);
+        pin(cur.tok_c);
         pin(cur.tot);
         pin(pnext);
         const float tot_c = cur.tot;
+        cur.xr.template store_f16<LX>((__bf16 *)xn);
 #pragma unroll
-        for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) {
-            const float d = cur.wd[it], cs = cur.wc[it];
-            cur.xr.template store_scaled<LX>(xb, it, d * ex2((cs - d * a) * LOG2E));
-            cur.xr.template store_scaled<LX>(xf, it, d * ex2((tot_c - cs + logD) * LOG2E));
+        for (int it = 0; it < BPER; ++it) {
+            const int k = tid + NT * it;
+            u32x4 v = cur.bq[it];
+            if constexpr (!MAIN) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = pack2h(lo_f(v[e]), hi_f(v[e]));
+            }
+            *(u32x4 *)&bn[(k / (S / 8)) * LB + 8 * (k % (S / 8))] = v;
         }
-        cur.br.template store<LB>(bn);
+        if (row_thread) {
+            const float d = cur.tok_d, cs = cur.tok_c;
+            s_wb[tid] = (_Float16)(d * ex2((cs - d * a) * LOG2E));
+            s_wf[tid] = (_Float16)(d * ex2((tot_c - cs + logD) * LOG2E));
+        }
         // Every thread stores its (identical) entry: a use on all paths keeps the row load where it is issued.
         s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
         __syncthreads();
 
-        fetch(cur, max(c - 2, c_lo));  // at the segment start: issued, unused
+        fetch(cur, max(c - 1, c_lo));  // at the segment start: issued, unused
         if (active) {
             const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
             for (int i = 0; i < TP; ++i) accG[i] *= dec;
 #pragma unroll
             for (int kb = 0; kb < Q / 16; ++kb) {
+                const f16x8 wb8 = *(const f16x8 *)(s_wb + 16 * kb + 8 * half);
+                const f16x8 wf8 = *(const f16x8 *)(s_wf + 16 * kb + 8 * half);
 #pragma unroll
                 for (int i = 0; i < TP; ++i) {
                     const int j = wave * TP + i;
-                    const bf16x8 af = frag_tr(bn, LB, 16 * kb, 32 * (j >> 1));
-                    accG[i] = mfma(af, frag_tr(xb, LX, 16 * kb, 32 * (j & 1)), accG[i]);
-                    accF[i] = mfma(af, frag_tr(xf, LX, 16 * kb, 32 * (j & 1)), accF[i]);
+                    const f16x8 af = __builtin_bit_cast(f16x8, frag_tr((const __bf16 *)bn, LB, 16 * kb, 32 * (j >> 1)));
+                    const f16x8 xv = __builtin_bit_cast(f16x8, frag_tr((const __bf16 *)xn, LX, 16 * kb, 32 * (j & 1)));
+                    accG[i] = mfma16(af, xv * wb8, accG[i]);
+                    accF[i] = mfma16(af, xv * wf8, accF[i]);
                 }
             }
         }
         logD += tot_c;
     };
-    int c = c_hi - 1;
-    for (; c - 1 >= c_lo; c -= 2) {
-        step(st0, c);
-        step(st1, c - 1);
-    }
-    if (c >= c_lo) step(st0, c);
+    for (int c = c_hi - 1; c >= c_lo; --c) step(st0, c);
 
     // Segment summaries: G (backward state entering the segment from its right end, from zero) and F.
     if (active) {
-        const int col = lane & 31, half = lane >> 5;
+        const int col = lane & 31;
         float *dG = segB + (bh * nseg_total + seg_base + seg) * (size_t)(P * S);
         float *dF = segF + (bh * nseg_total + seg_base + seg) * (size_t)(P * S);
 #pragma unroll
@@ -933,7 +945,8 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
         const uint64_t items = (uint64_t)Bn * Hs;
         {
             timing::Scope ts_(K_SSD_STATES, st);
-            k_states<S, Q, false><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, rdtT, rcsT,
+            k_states<S, Q, false><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, nullptr,
+                                                                 rdtT, rcsT,
                                                           a.a, nullptr, nullptr, segF, segB, segA, Hs, G, R, Rpad,
                                                           p.nchR, p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)items);
         }
@@ -954,7 +967,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
     const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
     {
         timing::Scope ts_(K_SSD_STATES, st);
-        k_states<S, Q, true><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
+        k_states<S, Q, true><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, b16, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
                                                       N, Lpad, p.nch, pl.segch, pl.nseg, 0, pl.nsegT, (uint32_t)items);
     }
     {
