@@ -28,15 +28,12 @@ __global__ __launch_bounds__(256) void rms_rows_wave(const V *__restrict__ src, 
         const V *s = src + srow * vpr;
         V *d = dst + drow * vpr;
         uint32_t c = lane;
-        for (; c + 192u < vpr; c += 256u) {
-            V a0 = __builtin_nontemporal_load(s + c);
-            V a1 = __builtin_nontemporal_load(s + c + 64u);
-            V a2 = __builtin_nontemporal_load(s + c + 128u);
-            V a3 = __builtin_nontemporal_load(s + c + 192u);
-            __builtin_nontemporal_store(a0, d + c);
-            __builtin_nontemporal_store(a1, d + c + 64u);
-            __builtin_nontemporal_store(a2, d + c + 128u);
-            __builtin_nontemporal_store(a3, d + c + 192u);
+        for (; c + 448u < vpr; c += 512u) {
+            V a[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) a[k] = __builtin_nontemporal_load(s + c + 64u * k);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) __builtin_nontemporal_store(a[k], d + c + 64u * k);
         }
         for (; c < vpr; c += 64u) __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
     }
@@ -71,7 +68,6 @@ hipError_t launch_typed(const void *src, void *dst, uint32_t batch, uint32_t T, 
     V *d = (V *)dst;
     if (vpr >= 64) {
         uint32_t blocks = (total + 3u) / 4u;
-        if (blocks > 8192u) blocks = 8192u;
         if (inverse)
             rms_rows_wave<V, true><<<blocks, 256, 0, stream>>>(s, d, N, vpr, total, order, flip, T, H, W);
         else
