@@ -16,8 +16,8 @@
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA storage).
  *     The caller owns every buffer; the library never allocates, frees or
- *     keeps device memory between calls (the HIP events of the timing
- *     diagnostics below aside).
+ *     keeps device memory between calls (HIP streams and events aside: the
+ *     side stream of mate_forward and the timing diagnostics below).
  *   - Token tensors are channels-last: [batch][T][H][W][...], so the canonical
  *     token index is n = (t*H + h)*W + w and a token's channels are contiguous.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
@@ -177,7 +177,12 @@ mate_status mate_tesa(const mate_tesa_tensors *t, mate_grid g, const mate_tesa_d
  * `order`) and the TE branch (mate_tesa with the descriptor's shift) on the
  * same grid. The two branch outputs are returned separately (s->y and a->o):
  * their widths differ and the pages leave their combination to the layer's
- * projections. The result equals the two calls made one after the other. */
+ * projections. The result equals the two calls made one after the other.
+ * The TE branch runs beside the MA branch on a stream the library creates for
+ * the current device on first use (kept until the process ends). It starts
+ * after the work already queued on `stream`, and `stream` waits for it before
+ * the call's last kernel, so both outputs are ordered on `stream` exactly as
+ * if every kernel had been launched there. */
 size_t mate_forward_workspace_size(mate_grid g, const mate_ssd_desc *sd, const mate_tesa_desc *td);
 mate_status mate_forward(const mate_ssd_tensors *s, const mate_ssd_desc *sd, const mate_tesa_tensors *a,
                          const mate_tesa_desc *td, mate_grid g, int order, void *workspace,

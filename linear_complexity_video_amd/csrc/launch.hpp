@@ -46,7 +46,8 @@ hipError_t ssd_portable_prepare();
 
 bool ssd_fast_supports(const SsdProblem &p);
 size_t ssd_fast_workspace(const SsdProblem &p);
-hipError_t ssd_fast(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st);
+// `before_out`, when given, is waited for on `st` before the output sweep is launched.
+hipError_t ssd_fast(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, hipEvent_t before_out = nullptr);
 hipError_t ssd_fast_prepare();
 
 bool tesa_portable_supports(const TesaProblem &p);
