@@ -9,7 +9,9 @@
 // computes S^T = K Q^T, so that a lane holds one query's scores and the
 // softmax needs only one cross-lane exchange; exp'd P^T is then directly the
 // B operand of O^T += V^T P^T, and O^T again has one query per lane, so the
-// online-softmax rescale is a per-lane multiply. Consecutive block ids are
+// online-softmax rescale is a per-lane multiply. The exponent base is the
+// first tile's maximum and is raised (with the rescale) only when a later
+// tile's probabilities reach 2^20, so most tiles compute no maximum at all. Consecutive block ids are
 // spread over the 8 XCDs; they are remapped so that the query blocks of one
 // window land on the same XCD and share its K/V in L2.
 #include "common.hpp"
@@ -22,6 +24,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     f32x16 acc[DH / 32];
 #pragma unroll
     for (int i = 0; i < DH / 32; ++i) acc[i] = f32x16{};
-    float mrun = -INFINITY, lrun = 0.f;
+    float mrun = 0.f, lrun = 0.f;
     const int ntiles = (m + KT - 1) / KT;
 
     // Tile loader: K and V rows as 16-byte chunks, natural layout.
@@ -166,6 +169,35 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
         }
     };
 
+    // Maximum score of one tile for this lane's query, in log2 units.
+    auto tile_max = [&](const f32x16 (&s)[2]) -> float {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) mloc = fmaxf(mloc, s[sub][rr]);
+        return fmaxf(mloc, __shfl_xor(mloc, 32)) * c_log2;
+    };
+    // P^T fragments of one tile against base m, and this lane's sum of them
+    // (of the bf16-rounded values that enter P V).
+    auto probs = [&](const f32x16 (&s)[2], float m, bf16x8 (&pf)[4]) -> float {
+        float lsum = 0.f;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int jj = 0; jj < 8; jj += 2) {
+                    bf16x2 p2;
+                    p2[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][8 * hb + jj], c_log2, -m));
+                    p2[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][8 * hb + jj + 1], c_log2, -m));
+                    pf[2 * sub + hb][jj] = p2[0];
+                    pf[2 * sub + hb][jj + 1] = p2[1];
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(p2, bf16x2{(__bf16)1.f, (__bf16)1.f}, lsum, false);
+                }
+        return lsum;
+    };
+
     fetch(0);
     stash(0);
     __syncthreads();
@@ -191,34 +223,22 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
                         s[sub][rr] = j < m ? s[sub][rr] : -INFINITY;
                     }
             }
-            // Running max on raw scores; the scale (log2 units) enters the exponent by one FMA.
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) mloc = fmaxf(mloc, s[sub][rr]);
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * c_log2;
-            // O and l are rescaled only when some lane's maximum grew.
-            if (!__all(mloc <= mrun)) {
-                const float mnew = fmaxf(mrun, mloc);
+            // Probabilities against the base mrun (log2 units): the exact maximum
+            // of the first tile, raised later only when a tile's probabilities
+            // reach 2^20 (or overflow): then O and l are rescaled and the tile's
+            // probabilities recomputed.
+            if (kt == 0) mrun = tile_max(s);
+            bf16x8 pf[4];
+            float lsum = probs(s, mrun, pf);
+            if (__any(!(lsum < 0x1p20f))) {
+                const float mnew = fmaxf(mrun, tile_max(s));
                 const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
                 lrun *= corr;
 #pragma unroll
                 for (int i = 0; i < DH / 32; ++i) acc[i] *= corr;
                 mrun = mnew;
+                lsum = probs(s, mrun, pf);
             }
-            bf16x8 pf[4];
-            float lsum = 0.f;
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][8 * hb + jj], c_log2, -mrun));
-                        lsum += p;
-                        pf[2 * sub + hb][jj] = (__bf16)p;
-                    }
             lrun += lsum;
 #pragma unroll
             for (int dt = 0; dt < DH / 32; ++dt)

@@ -337,6 +337,36 @@ def test_tesa_fast_ragged_windows(oracle_mod, window, shift, d):
     assert parity_error(to_f64(o), want) <= 2e-2
 
 
+@pytest.mark.parametrize("grid,window,shift", [((1, 8, 8, 8), (8, 8, 8), (0, 0, 0)),
+                                               ((1, 16, 8, 8), (8, 8, 8), (4, 4, 4))])
+@pytest.mark.parametrize("d", [64, 128])
+def test_tesa_fast_late_dominant_keys(oracle_mod, grid, window, shift, d):
+    """Some keys score ~160 (log2 units) above all others, and none of them sits
+    in a window's first 64 positions.
+
+    Against the first key tile's maximum their probabilities overflow, so the
+    kernel must raise its exponent base and rescale what it has accumulated. The
+    output is the mean of V over the window's dominant keys (plain softmax
+    weights for windows that hold none).
+    """
+    rng = np.random.default_rng(100 + d)
+    shape = grid + (2, d)
+    u = rng.standard_normal(d).astype(np.float32)
+    q = u + 0.3 * rng.standard_normal(shape).astype(np.float32)
+    k = 0.1 * rng.standard_normal(shape).astype(np.float32)
+    t, h, w = np.meshgrid(*(np.arange(n) for n in grid[1:]), indexing="ij")
+    dominant = np.isin(t, [5, 9, 14]) & ((h * 8 + w) % 7 == 3)
+    k[0][dominant] = 10.0 * u
+    v = rng.standard_normal(shape).astype(np.float32)
+    qkv = [synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)) for a in (q, k, v)]
+    dev = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in qkv]
+    say(f"tesa fast dominant keys grid={grid} shift={shift} d={d}")
+    o = torch.full_like(dev[0], float("nan"))
+    B.mate_tesa(*dev, o, window, shift, 0.0, B.ALGO_FAST)
+    want = oracle_mod.tesa(*qkv, grid, window, shift)
+    assert parity_error(to_f64(o), want) <= 2e-2
+
+
 @pytest.mark.parametrize("cfg,shifted", [(1, False), (1, True), (2, False), (2, True)])
 def test_tesa_fast_matches_portable(cfg, shifted):
     dev = tesa_device(cfg)
