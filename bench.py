@@ -140,6 +140,73 @@ def cpu_baseline(wl, si, ti, threads):
 # GPU timing
 # ---------------------------------------------------------------------------
 
+def scaling_sweep(torch, np, B, reps):
+    """Per-layer forward time of the MATE core against full self-attention as the video grows.
+
+    T = 32, 64, 128 latent frames at 48x48 (the 1:2:4 ratio of 17, 34 and 68 s clips). MATE core: one
+    mate_forward at LinGen-4B widths (bi-SSD 80 x 64, d_s 128, chunk 128, 8^3 review pooling; TESA 20 x
+    128, 8^3 windows). Full attention: the same TESA kernel with one window spanning the whole grid, at
+    DiT-4B width (24 heads x 128). Inputs are synthetic (N(0,1)/sqrt(dim); dt, A as the long-grid
+    workload). Prints one JSON line.
+    """
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    stream = torch.cuda.current_stream()
+
+    def rn(*shape, scale=1.0):
+        return (torch.randn(*shape, device=dev, generator=g) * scale).to(torch.bfloat16)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(2, reps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    points = []
+    for T in (32, 64, 128):
+        H = W = 48
+        N = T * H * W
+        log(f"scaling: T={T} ({N} tokens)")
+        ssd = {"x": rn(1, T, H, W, 80, 64, scale=1 / 8), "b": rn(1, T, H, W, 1, 128, scale=128 ** -0.5),
+               "c": rn(1, T, H, W, 1, 128, scale=128 ** -0.5)}
+        ssd["dt"] = torch.nn.functional.softplus(torch.randn(1, T, H, W, 80, device=dev, generator=g) * 0.5 - 2)
+        ssd["a"] = -torch.exp(torch.rand(80, device=dev, generator=g) * 2)
+        ssd["d"] = torch.randn(80, device=dev, generator=g)
+        ssd["y"] = torch.empty_like(ssd["x"])
+        att = {k: rn(1, T, H, W, 20, 128, scale=128 ** -0.5) for k in ("q", "k", "v")}
+        att["o"] = torch.empty_like(att["q"])
+        ws = torch.empty(B.mate_forward_workspace_size((1, T, H, W), B.ssd_desc(ssd["x"], ssd["b"], 128, (8, 8, 8)),
+                                                       B.tesa_desc(att["q"], (8, 8, 8))),
+                         dtype=torch.uint8, device=dev)
+        t_mate = timed(lambda: B.mate_forward(ssd, att, 0, 128, (8, 8, 8), (8, 8, 8), (0, 0, 0), workspace=ws))
+        del ssd, att, ws
+        full = {k: rn(1, T, H, W, 24, 128, scale=128 ** -0.5) for k in ("q", "k", "v")}
+        full["o"] = torch.empty_like(full["q"])
+        t_full = timed(lambda: B.mate_tesa(full["q"], full["k"], full["v"], full["o"], (T, H, W), (0, 0, 0)))
+        del full
+        attn_flops = 4.0 * N * N * 24 * 128
+        points.append({"T": T, "H": H, "W": W, "tokens": N, "mate_core_ms": t_mate * 1e3,
+                       "full_attention_ms": t_full * 1e3, "full_over_mate": t_full / t_mate,
+                       "mate_core_tokens_per_s": N / t_mate,
+                       "full_attention_tflops": attn_flops / t_full / 1e12})
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "per-layer forward time: MATE core vs full self-attention (one MI355X)",
+                      "unit": "ms", "data": "synthetic", "points": points}), flush=True)
+
+
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +216,8 @@ def main():
     ap.add_argument("--algo", choices=("auto", "portable", "fast"), default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed repetitions of each single call")
+    ap.add_argument("--scaling", action="store_true",
+                    help="instead of the throughput line: MATE core vs full attention per layer as T grows")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -170,6 +239,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     B.lib()
+    if args.scaling:
+        scaling_sweep(torch, np, B, args.kernel_reps)
+        return
     algo = {"auto": B.ALGO_AUTO, "portable": B.ALGO_PORTABLE, "fast": B.ALGO_FAST}[args.algo]
     wl = WORKLOADS[args.config]
     dev = torch.device("cuda:0")
@@ -256,6 +328,21 @@ def main():
               for sh in (False, True)}
     t_ssd = time_call(lambda: B.mate_bissd_scan(ssd["x"], ssd["b"], ssd["c"], ssd["dt"], ssd["a"], ssd["d"],
                                                 ssd["y"], 0, wl.chunk, wl.pool, algo, workspace=ws), reps)
+    # One layer per RMS order (mate_forward alone, events on torch's stream; TESA's side stream is
+    # joined back into it inside the call): median of the repetitions.
+    layers = []
+    for order, shifted in wl.schedule:
+        ts = []
+        for _ in range(max(3, reps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            layer(order, shifted)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = float(np.median(ts))
+        layers.append({"order": order, "tesa_shifted": shifted, "ms": t * 1e3,
+                       "tokens_per_s": wl.N * wl.batch / t})
     xr = ssd["x"].view(wl.batch, wl.N, -1)
     xo = torch.empty_like(xr)
     t_rms = time_kernel("rms_reorder", lambda: B.mate_rms_reorder(xr, xo, wl.grid, 1, True, False), reps)
@@ -316,7 +403,9 @@ def main():
             "algo": args.algo,
         },
         "roofline": roofline,
+        "layers": layers,
         "kernels": kernels,
+        "device": device_info(torch),
     }
     if args.calibrate_copy:
         # A plain streaming kernel of known size (reads and writes COPY_BYTES once each: an elementwise

@@ -167,7 +167,9 @@ typedef struct {
 } mate_tesa_tensors;
 
 /* Supported: headdim 8..128 (multiple of 8) and windows of at most 1024 tokens
- * for the portable kernel; bf16 with headdim 64 or 128 also has MFMA kernels. */
+ * for the portable kernel; bf16 with headdim 64 or 128 also has MFMA kernels,
+ * for windows of at most 4096 tokens and for one unshifted window spanning the
+ * whole grid (full attention over all T*H*W tokens, any size). */
 mate_status mate_tesa(const mate_tesa_tensors *t, mate_grid g, const mate_tesa_desc *d, void *stream);
 
 /* ------------------------------------------------------------------------ */

@@ -54,11 +54,11 @@ __device__ __forceinline__ void region_extent(int r, int D, int w, int s, int &l
 
 constexpr int MAXW = 4096;        // largest window (tokens) of the MFMA kernel
 
-template <int DH>
+template <int DH, int ROWS>
 struct __attribute__((aligned(16))) Smem {
     __bf16 k[2][KT][DH + KPAD];
     __bf16 v[2][KT][DH + VPAD];
-    uint32_t row[MAXW];           // canonical token of each window position
+    uint32_t row[ROWS];           // canonical token of each window position
 };
 
 // A operand of O^T += V^T P^T from the row-major V tile: lane l gets column
@@ -79,14 +79,16 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int DH>
+// WHOLE: one window spanning the whole unshifted grid (full attention); a
+// window position is then its canonical token, and no table is kept.
+template <int DH, bool WHOLE>
 __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                                                    const __bf16 *__restrict__ v, __bf16 *__restrict__ o,
                                                    int nheads, int Tn, int Hn, int Wn, int wt, int wh, int ww,
                                                    int st, int sh, int sw, int nrt, int nrh, int nrw, int nqb,
                                                    uint32_t total, float c_log2)
 {
-    __shared__ Smem<DH> sm;
+    __shared__ Smem<DH, WHOLE ? 4 : MAXW> sm;
     constexpr int DC = DH / 8;  // 16-byte chunks per row
 
     // XCD-aware item index: block L runs on XCD L % 8; items w, w+1, ... of one
@@ -119,8 +121,11 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     // Canonical token of every window position, computed once (the tile loader only looks it up).
-    for (int l = tid; l < m; l += 512) sm.row[l] = (uint32_t)token(l);
-    __syncthreads();
+    if (!WHOLE) {
+        for (int l = tid; l < m; l += 512) sm.row[l] = (uint32_t)token(l);
+        __syncthreads();
+    }
+    auto row_of = [&](int l) -> size_t { return WHOLE ? (size_t)l : (size_t)sm.row[l]; };
     const int half = lane >> 5, col = lane & 31;
     const int qi = q_base + wave * QW + col;
     const bool qvalid = qi < m;
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     // Q^T fragments (B operand of S^T = K Q^T): query col, d = 16 kb + 8 half + 0..7.
     bf16x8 qf[DH / 16];
     {
-        const __bf16 *qrow = q + head_off + (size_t)sm.row[qvalid ? qi : 0] * rowstride;
+        const __bf16 *qrow = q + head_off + row_of(qvalid ? qi : 0) * rowstride;
 #pragma unroll
         for (int kb = 0; kb < DH / 16; ++kb) {
             u32x4 raw = qvalid ? *(const u32x4 *)(qrow + 16 * kb + 8 * half) : u32x4{0, 0, 0, 0};
@@ -155,7 +160,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
             const int jj = c / DC, dc = c % DC;
             const int kidx = kt * KT + jj;
             // A key past the window reads the window's first key: finite, and its score is masked.
-            const size_t off = head_off + (size_t)sm.row[kidx < m ? kidx : 0] * rowstride + 8 * dc;
+            const size_t off = head_off + row_of(kidx < m ? kidx : 0) * rowstride + 8 * dc;
             kreg[it] = *(const u32x4 *)(k + off);
             vreg[it] = *(const u32x4 *)(v + off);
         }
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     const float lt = lrun + __shfl_xor(lrun, 32);
     if (qvalid) {
         const float inv = 1.f / lt;
-        __bf16 *orow = o + head_off + (size_t)sm.row[qi] * rowstride;
+        __bf16 *orow = o + head_off + row_of(qi) * rowstride;
 #pragma unroll
         for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     }
 }
 
-template <int DH>
+template <int DH, bool WHOLE>
 hipError_t launch(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
 {
     const int maxw = p.wt * p.wh * p.ww;
@@ -275,7 +280,7 @@ hipError_t launch(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
     const uint64_t blocks = (total + 7) / 8 * 8;
     const float scale = p.scale > 0.f ? p.scale : 1.f / sqrtf((float)DH);
     timing::Scope ts_(K_TESA, stream);
-    k_tesa_fast<DH><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+    k_tesa_fast<DH, WHOLE><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
         (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, p.nheads, (int)p.T,
         (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st, p.sh, p.sw, p.nrt, p.nrh, p.nrw, nqb, (uint32_t)total,
         scale * 1.4426950408889634f);
@@ -286,14 +291,18 @@ hipError_t launch(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
 
 bool tesa_fast_supports(const TesaProblem &p)
 {
-    return p.dtype == 1 && (p.headdim == 64 || p.headdim == 128) && p.wt * p.wh * p.ww <= 4096 &&
-           p.batch * p.nheads * (int64_t)p.nrt * p.nrh * p.nrw * 16 < ((int64_t)1 << 31);
+    const int64_t wsize = (int64_t)p.wt * p.wh * p.ww;
+    const bool whole = p.nrt == 1 && p.nrh == 1 && p.nrw == 1;
+    const int64_t items = p.batch * p.nheads * (int64_t)p.nrt * p.nrh * p.nrw * ((wsize + QB - 1) / QB);
+    return p.dtype == 1 && (p.headdim == 64 || p.headdim == 128) && (whole || wsize <= MAXW) &&
+           items < ((int64_t)1 << 30);
 }
 
 hipError_t tesa_fast(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
 {
-    if (p.headdim == 64) return launch<64>(p, a, stream);
-    return launch<128>(p, a, stream);
+    const bool whole = p.nrt == 1 && p.nrh == 1 && p.nrw == 1;
+    if (p.headdim == 64) return whole ? launch<64, true>(p, a, stream) : launch<64, false>(p, a, stream);
+    return whole ? launch<128, true>(p, a, stream) : launch<128, false>(p, a, stream);
 }
 
 } // namespace mate

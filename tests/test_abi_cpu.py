@@ -128,6 +128,12 @@ def test_tesa_validation():
     assert _att(t, g, _tesa(headdim=12)) == B.MATE_ERR_UNSUPPORTED
     assert _att(t, g, _tesa(algo=B.ALGO_FAST)) == B.MATE_ERR_UNSUPPORTED
     assert B.lib().mate_tesa(None, g, ctypes.byref(_tesa()), None) == B.MATE_ERR_NULL
+    # Windows above 4096 tokens have a kernel only when one window spans the whole unshifted grid.
+    big = B.Grid(1, 16, 48, 48)
+    bf = dict(headdim=128, dtype=B.MATE_BF16, win_t=8, win_h=48, win_w=48)
+    assert _att(t, big, _tesa(**bf)) == B.MATE_ERR_UNSUPPORTED
+    assert _att(t, big, _tesa(**dict(bf, win_t=16, shift_t=4))) == B.MATE_ERR_UNSUPPORTED
+    assert _att(t, big, _tesa(**dict(bf, win_t=16, dtype=B.MATE_F32))) == B.MATE_ERR_UNSUPPORTED
 
 
 def test_forward_validation_rejects_before_launch():

@@ -367,6 +367,22 @@ def test_tesa_fast_late_dominant_keys(oracle_mod, grid, window, shift, d):
     assert parity_error(to_f64(o), want) <= 2e-2
 
 
+@pytest.mark.parametrize("grid", [(1, 4, 16, 16), (1, 5, 24, 23), (1, 8, 24, 24)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_tesa_whole_grid_window(oracle_mod, grid, d):
+    """A window spanning the whole grid is full attention; beyond 4096 tokens only the MFMA kernel
+    runs it (no window table). The 5x24x23 grid leaves ragged key and query blocks."""
+    rng = np.random.default_rng(200 + d)
+    qkv = [synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(
+        (rng.standard_normal(grid + (2, d)) / np.sqrt(d)).astype(np.float32))) for _ in range(3)]
+    dev = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in qkv]
+    say(f"tesa whole-grid window grid={grid} d={d}")
+    o = torch.full_like(dev[0], float("nan"))
+    B.mate_tesa(*dev, o, grid[1:], (0, 0, 0))
+    want = oracle_mod.tesa(*qkv, grid, grid[1:], (0, 0, 0), nthreads=16)
+    assert parity_error(to_f64(o), want) <= 2e-2
+
+
 @pytest.mark.parametrize("cfg,shifted", [(1, False), (1, True), (2, False), (2, True)])
 def test_tesa_fast_matches_portable(cfg, shifted):
     dev = tesa_device(cfg)
