@@ -1,19 +1,24 @@
 // TESA on bf16 MFMA (gfx950, v_mfma_f32_32x32x16_bf16), flash-style inside
 // each (shifted) 3D window.
 //
-// Work item = (window, head, block of 256 queries); a workgroup of 8 waves
-// owns one item, each wave 32 queries. The canonical token of every window
-// position is tabulated in LDS once per item. Keys and values stream through LDS in
-// tiles of 64 (double buffered, both in their natural row layout; the V^T
-// operand is read with the gfx950 LDS transpose read). Per tile each wave
-// computes S^T = K Q^T, so that a lane holds one query's scores and the
-// softmax needs only one cross-lane exchange; exp'd P^T is then directly the
-// B operand of O^T += V^T P^T, and O^T again has one query per lane, so the
-// online-softmax rescale is a per-lane multiply. The exponent base is the
-// first tile's maximum and is raised (with the rescale) only when a later
-// tile's probabilities reach 2^20, so most tiles compute no maximum at all. Consecutive block ids are
-// spread over the 8 XCDs; they are remapped so that the query blocks of one
-// window land on the same XCD and share its K/V in L2.
+// Work item = (window, head, block of 256 queries). One persistent workgroup
+// of 8 waves per CU runs a sequence of items, each wave 32 queries of the
+// current one. The canonical token of every window position is tabulated in
+// LDS one item ahead. Keys and values stream through LDS in tiles of 64
+// (double buffered, both in their natural row layout; the V^T operand is read
+// with the gfx950 LDS transpose read), and the tile stream runs on across
+// items: the next item's first tile and Q rows load during the current one's
+// last tiles. Per tile each wave computes S^T = K Q^T, so that a lane holds
+// one query's scores and the softmax needs only one cross-lane exchange; exp'd
+// P^T is then directly the B operand of O^T += V^T P^T, and O^T again has one
+// query per lane, so the online-softmax rescale is a per-lane multiply. The
+// exponent base is the first tile's maximum and is raised (with the rescale)
+// only when a later tile's probabilities reach 2^20, so most tiles compute no
+// maximum at all. O leaves through LDS as whole row segments. Each XCD owns a
+// contiguous range of items, so the query blocks of one window run side by
+// side on one XCD and share its K/V in L2.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -79,8 +84,32 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// a / d for 0 <= a, d < 2^22 from a float reciprocal of d: the estimate is
+// within one of the quotient, and one correction step makes it exact.
+__device__ __forceinline__ int div_small(int a, int d, float inv_d)
+{
+    int qt = (int)((float)a * inv_d);
+    const int r = a - qt * d;
+    qt += (r >= d) - (r < 0);
+    return qt;
+}
+
+// One work item: a (batch, head, region, query block) and what the kernel
+// derives from it.
+struct Item {
+    int m;            // tokens in the region
+    int q_base;       // first query of the block
+    int t0, h0, w0, nt, nh, nw;
+    size_t head_off;  // element offset of (batch, head) in q, k, v, o
+};
+
 // WHOLE: one window spanning the whole unshifted grid (full attention); a
 // window position is then its canonical token, and no table is kept.
+//
+// Persistent: each workgroup runs a sequence of items. The tiles of
+// consecutive items form one stream, so during an item's last key tile the
+// next item's first tile and its Q fragments are already loading, and its
+// window table is built one item ahead.
 template <int DH, bool WHOLE>
 __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                                                    const __bf16 *__restrict__ v, __bf16 *__restrict__ o,
@@ -88,79 +117,96 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
                                                    int st, int sh, int sw, int nrt, int nrh, int nrw, int nqb,
                                                    uint32_t total, float c_log2)
 {
-    __shared__ Smem<DH, WHOLE ? 4 : MAXW> sm;
+    __shared__ Smem<DH, WHOLE ? 4 : 2 * MAXW> sm;
     constexpr int DC = DH / 8;  // 16-byte chunks per row
 
-    // XCD-aware item index: block L runs on XCD L % 8; items w, w+1, ... of one
-    // XCD are consecutive query blocks / windows.
-    const uint32_t per_xcd = gridDim.x / 8;
-    const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (item >= total) return;
-    const int qb = item % nqb;
-    const uint32_t rest = item / nqb;
-    const int nreg = nrt * nrh * nrw;
-    const int r = rest % nreg;
-    const int bh = rest / nreg;
-    const int h = bh % nheads, b = bh / nheads;
-    const int rw = r % nrw, rh = (r / nrw) % nrh, rt = r / (nrw * nrh);
-    int t0, t1, h0, h1, w0, w1;
-    region_extent(rt, Tn, wt, st, t0, t1);
-    region_extent(rh, Hn, wh, sh, h0, h1);
-    region_extent(rw, Wn, ww, sw, w0, w1);
-    const int nt = t1 - t0, nh_ = h1 - h0, nw_ = w1 - w0, m = nt * nh_ * nw_;
-    const int q_base = qb * QB;
-    if (q_base >= m) return;  // uniform over the workgroup
+    // Item sequence of this workgroup. Block L runs on XCD L % 8; XCD x owns the
+    // contiguous item range [x per, (x + 1) per), and its workgroups take those
+    // items in turn, so the query blocks of one window run side by side on one
+    // XCD and share its K/V in L2.
+    const uint32_t wpx = gridDim.x / 8;
+    const uint32_t per = (total + 7) / 8;
+    const uint32_t xcd = blockIdx.x % 8;
+    const uint32_t i_end = min(total, (xcd + 1) * per);
+    uint32_t i_next = xcd * per + blockIdx.x / 8;
 
     const size_t N = (size_t)Tn * Hn * Wn;
     const size_t rowstride = (size_t)nheads * DH;
-    const size_t head_off = ((size_t)b * N) * rowstride + (size_t)h * DH;
-    auto token = [&](int l) -> size_t {
-        const int lw = l % nw_, lh = (l / nw_) % nh_, lt = l / (nw_ * nh_);
-        return ((size_t)(t0 + lt) * Hn + (h0 + lh)) * Wn + (w0 + lw);
+    const int nreg = nrt * nrh * nrw;
+    // Next item of the sequence with queries in it (false when none is left).
+    auto next_item = [&](Item &I) -> bool {
+        for (; i_next < i_end; i_next += wpx) {
+            const uint32_t item = i_next;
+            const int qb = item % nqb;
+            const uint32_t rest = item / nqb;
+            const int r = rest % nreg;
+            const int bh = rest / nreg;
+            const int h = bh % nheads, b = bh / nheads;
+            const int rw = r % nrw, rh = (r / nrw) % nrh, rt = r / (nrw * nrh);
+            int t0, t1, h0, h1, w0, w1;
+            region_extent(rt, Tn, wt, st, t0, t1);
+            region_extent(rh, Hn, wh, sh, h0, h1);
+            region_extent(rw, Wn, ww, sw, w0, w1);
+            I.nt = t1 - t0;
+            I.nh = h1 - h0;
+            I.nw = w1 - w0;
+            I.m = I.nt * I.nh * I.nw;
+            I.q_base = qb * QB;
+            I.t0 = t0;
+            I.h0 = h0;
+            I.w0 = w0;
+            I.head_off = ((size_t)b * N) * rowstride + (size_t)h * DH;
+            if (I.q_base < I.m) {
+                i_next += wpx;
+                return true;
+            }
+        }
+        return false;
     };
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    // Canonical token of every window position, computed once (the tile loader only looks it up).
-    if (!WHOLE) {
-        for (int l = tid; l < m; l += 512) sm.row[l] = (uint32_t)token(l);
-        __syncthreads();
-    }
-    auto row_of = [&](int l) -> size_t { return WHOLE ? (size_t)l : (size_t)sm.row[l]; };
     const int half = lane >> 5, col = lane & 31;
-    const int qi = q_base + wave * QW + col;
-    const bool qvalid = qi < m;
-    const bool wave_active = q_base + wave * QW < m;
+    // Canonical token of every window position, in table tb (0 or 1).
+    auto build_table = [&](const Item &I, int tb) {
+        if (!WHOLE) {
+            const int nhw = I.nh * I.nw;
+            const float inv_hw = 1.f / (float)nhw, inv_w = 1.f / (float)I.nw;
+            for (int l = tid; l < I.m; l += 512) {
+                const int lt = div_small(l, nhw, inv_hw);
+                const int rem = l - lt * nhw;
+                const int lh = div_small(rem, I.nw, inv_w);
+                const int lw = rem - lh * I.nw;
+                sm.row[tb * MAXW + l] = (uint32_t)(((I.t0 + lt) * Hn + (I.h0 + lh)) * Wn + (I.w0 + lw));
+            }
+        }
+    };
+    auto row_of = [&](int tb, int l) -> size_t { return WHOLE ? (size_t)l : (size_t)sm.row[tb * MAXW + l]; };
 
-    // Q^T fragments (B operand of S^T = K Q^T): query col, d = 16 kb + 8 half + 0..7.
-    bf16x8 qf[DH / 16];
-    {
-        const __bf16 *qrow = q + head_off + row_of(qvalid ? qi : 0) * rowstride;
+    // Q^T fragments (B operand of S^T = K Q^T) of this lane's query: d = 16 kb + 8 half + 0..7.
+    auto load_q = [&](const Item &I, int tb, bf16x8 (&qf)[DH / 16]) {
+        const int qi = I.q_base + wave * QW + col;
+        const bool ok = qi < I.m;
+        const __bf16 *qrow = q + I.head_off + row_of(tb, ok ? qi : 0) * rowstride;
 #pragma unroll
         for (int kb = 0; kb < DH / 16; ++kb) {
-            u32x4 raw = qvalid ? *(const u32x4 *)(qrow + 16 * kb + 8 * half) : u32x4{0, 0, 0, 0};
-            qf[kb] = __builtin_bit_cast(bf16x8, raw);
+            const u32x4 raw = *(const u32x4 *)(qrow + 16 * kb + 8 * half);
+            qf[kb] = __builtin_bit_cast(bf16x8, ok ? raw : u32x4{0, 0, 0, 0});
         }
-    }
-
-    f32x16 acc[DH / 32];
-#pragma unroll
-    for (int i = 0; i < DH / 32; ++i) acc[i] = f32x16{};
-    float mrun = 0.f, lrun = 0.f;
-    const int ntiles = (m + KT - 1) / KT;
+    };
 
     // Tile loader: K and V rows as 16-byte chunks, natural layout.
     constexpr int KCH = KT * DC;                  // chunks per tile
     constexpr int KPER = KCH / 512;               // per thread
     static_assert(KCH % 512 == 0, "tile chunks must split evenly over the workgroup");
     u32x4 kreg[KPER], vreg[KPER];
-    auto fetch = [&](int kt) {
+    auto fetch = [&](const Item &I, int tb, int kt) {
 #pragma unroll
         for (int it = 0; it < KPER; ++it) {
             const int c = tid + 512 * it;
             const int jj = c / DC, dc = c % DC;
             const int kidx = kt * KT + jj;
             // A key past the window reads the window's first key: finite, and its score is masked.
-            const size_t off = head_off + row_of(kidx < m ? kidx : 0) * rowstride + 8 * dc;
+            const size_t off = I.head_off + row_of(tb, kidx < I.m ? kidx : 0) * rowstride + 8 * dc;
             kreg[it] = *(const u32x4 *)(k + off);
             vreg[it] = *(const u32x4 *)(v + off);
         }
@@ -203,72 +249,141 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
         return lsum;
     };
 
-    fetch(0);
+    Item I, J;
+    if (!next_item(I)) return;  // uniform over the workgroup
+    bool has_j = next_item(J);
+    int rt = 0;                 // table of the current item
+    build_table(I, rt);
+    if (has_j) build_table(J, rt ^ 1);
+    __syncthreads();
+    bf16x8 qf[DH / 16], qn[DH / 16];
+    load_q(I, rt, qf);
+    fetch(I, rt, 0);
     stash(0);
     __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < ntiles) fetch(kt + 1);
-        if (wave_active) {
-            f32x16 s[2] = {f32x16{}, f32x16{}};
+    int buf = 0;  // LDS buffer of the current tile
+
+    for (;;) {
+        const bool wave_active = I.q_base + wave * QW < I.m;
+        const int ntiles = (I.m + KT - 1) / KT;
+        f32x16 acc[DH / 32];
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int kb = 0; kb < DH / 16; ++kb) {
-                    const bf16x8 a = *(const bf16x8 *)&sm.k[cur][32 * sub + col][16 * kb + 8 * half];
-                    s[sub] = mfma(a, qf[kb], s[sub]);
-                }
-            // Keys past the window (only in the last, ragged tile) get -inf.
-            if (kt * KT + KT > m) {
+        for (int i = 0; i < DH / 32; ++i) acc[i] = f32x16{};
+        float mrun = 0.f, lrun = 0.f;
+        for (int kt = 0; kt < ntiles; ++kt) {
+            const bool more = kt + 1 < ntiles;
+            if (more) {
+                fetch(I, rt, kt + 1);
+            } else if (has_j) {
+                fetch(J, rt ^ 1, 0);
+            }
+            if (wave_active) {
+                f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) {
-                        const int j = kt * KT + 32 * sub + 8 * (rr >> 2) + 4 * half + (rr & 3);
-                        s[sub][rr] = j < m ? s[sub][rr] : -INFINITY;
+                    for (int kb = 0; kb < DH / 16; ++kb) {
+                        const bf16x8 a = *(const bf16x8 *)&sm.k[buf][32 * sub + col][16 * kb + 8 * half];
+                        s[sub] = mfma(a, qf[kb], s[sub]);
                     }
+                // Keys past the window (only in the last, ragged tile) get -inf.
+                if (kt * KT + KT > I.m) {
+#pragma unroll
+                    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) {
+                            const int j = kt * KT + 32 * sub + 8 * (rr >> 2) + 4 * half + (rr & 3);
+                            s[sub][rr] = j < I.m ? s[sub][rr] : -INFINITY;
+                        }
+                }
+                // Probabilities against the base mrun (log2 units): the exact maximum
+                // of the first tile, raised later only when a tile's probabilities
+                // reach 2^20 (or overflow): then O and l are rescaled and the tile's
+                // probabilities recomputed.
+                if (kt == 0) mrun = tile_max(s);
+                bf16x8 pf[4];
+                float lsum = probs(s, mrun, pf);
+                if (__any(!(lsum < 0x1p20f))) {
+                    const float mnew = fmaxf(mrun, tile_max(s));
+                    const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
+                    lrun *= corr;
+#pragma unroll
+                    for (int i = 0; i < DH / 32; ++i) acc[i] *= corr;
+                    mrun = mnew;
+                    lsum = probs(s, mrun, pf);
+                }
+                lrun += lsum;
+#pragma unroll
+                for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+                    for (int kb2 = 0; kb2 < 4; ++kb2)
+                        acc[dt] = mfma(v_frag<DH + VPAD>(&sm.v[buf][0][0], 16 * kb2, 32 * dt), pf[kb2], acc[dt]);
             }
-            // Probabilities against the base mrun (log2 units): the exact maximum
-            // of the first tile, raised later only when a tile's probabilities
-            // reach 2^20 (or overflow): then O and l are rescaled and the tile's
-            // probabilities recomputed.
-            if (kt == 0) mrun = tile_max(s);
-            bf16x8 pf[4];
-            float lsum = probs(s, mrun, pf);
-            if (__any(!(lsum < 0x1p20f))) {
-                const float mnew = fmaxf(mrun, tile_max(s));
-                const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
-                lrun *= corr;
-#pragma unroll
-                for (int i = 0; i < DH / 32; ++i) acc[i] *= corr;
-                mrun = mnew;
-                lsum = probs(s, mrun, pf);
-            }
-            lrun += lsum;
-#pragma unroll
-            for (int dt = 0; dt < DH / 32; ++dt)
-#pragma unroll
-                for (int kb2 = 0; kb2 < 4; ++kb2)
-                    acc[dt] = mfma(v_frag<DH + VPAD>(&sm.v[cur][0][0], 16 * kb2, 32 * dt), pf[kb2], acc[dt]);
+            if (more || has_j) stash(buf ^ 1);
+            // The next item's Q rows are requested at the end of the tile before its last
+            // (after that tile's own wait), so that neither wait includes them.
+            if (has_j && kt == (ntiles >= 2 ? ntiles - 2 : ntiles - 1)) load_q(J, rt ^ 1, qn);
+            __syncthreads();
+            buf ^= 1;
         }
-        if (kt + 1 < ntiles) stash(cur ^ 1);
-        __syncthreads();
-    }
 
-    const float lt = lrun + __shfl_xor(lrun, 32);
-    if (qvalid) {
-        const float inv = 1.f / lt;
-        __bf16 *orow = o + head_off + row_of(qi) * rowstride;
+        // O leaves through LDS, in rounds of RD value dims: each wave writes its
+        // 32 rows into a private area of the tile buffer nobody reads any more
+        // (16-byte chunks XOR-swizzled by row against bank conflicts), then
+        // stores whole row segments of RD values with consecutive lanes.
+        {
+            constexpr int RD = DH == 128 ? 64 : 32;  // value dims per round
+            constexpr int CPR = RD / 8;              // 16-byte chunks per row segment
+            __bf16 *stage = (wave < 4 ? &sm.k[buf ^ 1][0][0] : &sm.v[buf ^ 1][0][0]) + (wave & 3) * 32 * RD;
+            const float inv = 1.f / (lrun + __shfl_xor(lrun, 32));
 #pragma unroll
-        for (int dt = 0; dt < DH / 32; ++dt)
+            for (int r = 0; r < DH / RD; ++r) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 out;
+                for (int d2 = 0; d2 < RD / 32; ++d2)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) out[i] = (__bf16)(acc[dt][4 * g + i] * inv);
-                *(bf16x4 *)(orow + 32 * dt + 8 * g + 4 * half) = out;
+                    for (int g = 0; g < 4; ++g) {
+                        bf16x4 out;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) out[i] = (__bf16)(acc[r * (RD / 32) + d2][4 * g + i] * inv);
+                        const int ch = (4 * d2 + g) ^ (col & (CPR - 1));
+                        *(bf16x4 *)(stage + col * RD + 8 * ch + 4 * half) = out;
+                    }
+#pragma unroll
+                for (int j = 0; j < 32 * CPR / 64; ++j) {
+                    const int idx = lane + 64 * j, rq = idx / CPR, ch = idx % CPR;
+                    const u32x4 val = *(const u32x4 *)(stage + rq * RD + 8 * (ch ^ (rq & (CPR - 1))));
+                    const int qq = I.q_base + wave * QW + rq;
+                    if (qq < I.m) *(u32x4 *)(o + I.head_off + row_of(rt, qq) * rowstride + RD * r + 8 * ch) = val;
+                }
             }
+        }
+        if (!has_j) break;
+        I = J;
+        rt ^= 1;
+#pragma unroll
+        for (int kb = 0; kb < DH / 16; ++kb) qf[kb] = qn[kb];
+        has_j = next_item(J);
+        // Every wave is past its output rows: the staging area (stored into by the
+        // next tile) and the finished item's table are free.
+        __syncthreads();
+        if (!WHOLE && has_j) {
+            build_table(J, rt ^ 1);
+            __syncthreads();
+        }
     }
+}
+
+int cu_count()
+{
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <int DH, bool WHOLE>
@@ -277,7 +392,9 @@ hipError_t launch(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
     const int maxw = p.wt * p.wh * p.ww;
     const int nqb = (maxw + QB - 1) / QB;
     const uint64_t total = (uint64_t)p.batch * p.nheads * p.nrt * p.nrh * p.nrw * nqb;
-    const uint64_t blocks = (total + 7) / 8 * 8;
+    // One workgroup per CU (the LDS footprint allows no second), a multiple of 8 (one set per XCD).
+    const uint64_t want = ((uint64_t)cu_count() + 7) / 8 * 8;
+    const uint64_t blocks = std::min<uint64_t>(want, (total + 7) / 8 * 8);
     const float scale = p.scale > 0.f ? p.scale : 1.f / sqrtf((float)DH);
     timing::Scope ts_(K_TESA, stream);
     k_tesa_fast<DH, WHOLE><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
