@@ -6,9 +6,9 @@
 // current one. The canonical token of every window position is tabulated in
 // LDS one item ahead. Keys and values stream through LDS in tiles of 64
 // (double buffered, both in their natural row layout; the V^T operand is read
-// with the gfx950 LDS transpose read), and the tile stream runs on across
-// items: the next item's first tile and Q rows load during the current one's
-// last tiles. Per tile each wave computes S^T = K Q^T, so that a lane holds
+// with the gfx950 LDS transpose read), loaded two tiles ahead through two
+// register sets, and the tile stream runs on across items: the next item's
+// first tiles load during the current one's last, its Q rows right after. Per tile each wave computes S^T = K Q^T, so that a lane holds
 // one query's scores and the softmax needs only one cross-lane exchange; exp'd
 // P^T is then directly the B operand of O^T += V^T P^T, and O^T again has one
 // query per lane, so the online-softmax rescale is a per-lane multiply. The
@@ -198,25 +198,24 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     constexpr int KCH = KT * DC;                  // chunks per tile
     constexpr int KPER = KCH / 512;               // per thread
     static_assert(KCH % 512 == 0, "tile chunks must split evenly over the workgroup");
-    u32x4 kreg[KPER], vreg[KPER];
-    auto fetch = [&](const Item &I, int tb, int kt) {
+    auto fetch = [&](const Item &X, int tb, int kt, u32x4 (&kreg)[KPER], u32x4 (&vreg)[KPER]) {
 #pragma unroll
         for (int it = 0; it < KPER; ++it) {
             const int c = tid + 512 * it;
             const int jj = c / DC, dc = c % DC;
             const int kidx = kt * KT + jj;
             // A key past the window reads the window's first key: finite, and its score is masked.
-            const size_t off = I.head_off + row_of(tb, kidx < I.m ? kidx : 0) * rowstride + 8 * dc;
+            const size_t off = X.head_off + row_of(tb, kidx < X.m ? kidx : 0) * rowstride + 8 * dc;
             kreg[it] = *(const u32x4 *)(k + off);
             vreg[it] = *(const u32x4 *)(v + off);
         }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int b, const u32x4 (&kreg)[KPER], const u32x4 (&vreg)[KPER]) {
 #pragma unroll
         for (int it = 0; it < KPER; ++it) {
             const int c = tid + 512 * it;
-            *(u32x4 *)&sm.k[buf][c / DC][8 * (c % DC)] = kreg[it];
-            *(u32x4 *)&sm.v[buf][c / DC][8 * (c % DC)] = vreg[it];
+            *(u32x4 *)&sm.k[b][c / DC][8 * (c % DC)] = kreg[it];
+            *(u32x4 *)&sm.v[b][c / DC][8 * (c % DC)] = vreg[it];
         }
     };
 
@@ -249,6 +248,57 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
         return lsum;
     };
 
+    // One key tile of the current item from LDS buffer b: S^T, softmax, O^T.
+    auto compute = [&](const Item &X, int kt, int b, const bf16x8 (&qf)[DH / 16], f32x16 (&acc)[DH / 32],
+                       float &mrun, float &lrun) {
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int kb = 0; kb < DH / 16; ++kb) {
+                const bf16x8 a = *(const bf16x8 *)&sm.k[b][32 * sub + col][16 * kb + 8 * half];
+                s[sub] = mfma(a, qf[kb], s[sub]);
+            }
+        // Keys past the window (only in the last, ragged tile) get -inf.
+        if (kt * KT + KT > X.m) {
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int j = kt * KT + 32 * sub + 8 * (rr >> 2) + 4 * half + (rr & 3);
+                    s[sub][rr] = j < X.m ? s[sub][rr] : -INFINITY;
+                }
+        }
+        // Probabilities against the base mrun (log2 units): the exact maximum of the
+        // first tile, raised later only when a tile's probabilities reach 2^20 (or
+        // overflow): then O and l are rescaled and the tile's probabilities recomputed.
+        if (kt == 0) mrun = tile_max(s);
+        bf16x8 pf[4];
+        float lsum = probs(s, mrun, pf);
+        if (__any(!(lsum < 0x1p20f))) {
+            const float mnew = fmaxf(mrun, tile_max(s));
+            const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
+            lrun *= corr;
+#pragma unroll
+            for (int i = 0; i < DH / 32; ++i) acc[i] *= corr;
+            mrun = mnew;
+            lsum = probs(s, mrun, pf);
+        }
+        lrun += lsum;
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+            for (int kb2 = 0; kb2 < 4; ++kb2)
+                acc[dt] = mfma(v_frag<DH + VPAD>(&sm.v[b][0][0], 16 * kb2, 32 * dt), pf[kb2], acc[dt]);
+    };
+
+    // Tiles of an item, rounded up to even: a tile's LDS buffer and register set
+    // follow its parity. A padded tile holds no key and skips the arithmetic.
+    auto tiles_of = [](const Item &X) {
+        const int n = (X.m + KT - 1) / KT;
+        return n + (n & 1);
+    };
+
     Item I, J;
     if (!next_item(I)) return;  // uniform over the workgroup
     bool has_j = next_item(J);
@@ -256,85 +306,54 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     build_table(I, rt);
     if (has_j) build_table(J, rt ^ 1);
     __syncthreads();
-    bf16x8 qf[DH / 16], qn[DH / 16];
+    bf16x8 qf[DH / 16];
     load_q(I, rt, qf);
-    fetch(I, rt, 0);
-    stash(0);
+    // Two tiles in flight: set 0 carries even tiles, set 1 odd ones.
+    u32x4 k0[KPER], v0[KPER], k1[KPER], v1[KPER];
+    fetch(I, rt, 0, k0, v0);
+    fetch(I, rt, 1, k1, v1);
+    stash(0, k0, v0);
     __syncthreads();
-    int buf = 0;  // LDS buffer of the current tile
+
+    // Stream position kt of the current item (n tiles); past its end the next
+    // item's tile kt - n; with nothing left the current item's tile 0 again.
+    // Every fetch is issued, so the compiler's memory waits stay exact.
+    auto fetch_pos = [&](int kt, int n, u32x4 (&kreg)[KPER], u32x4 (&vreg)[KPER]) {
+        const bool in_i = kt < n, use_j = !in_i && has_j;
+        fetch(use_j ? J : I, use_j ? (rt ^ 1) : rt, in_i ? kt : (use_j ? kt - n : 0), kreg, vreg);
+    };
 
     for (;;) {
         const bool wave_active = I.q_base + wave * QW < I.m;
-        const int ntiles = (I.m + KT - 1) / KT;
+        const int n = tiles_of(I);
         f32x16 acc[DH / 32];
 #pragma unroll
         for (int i = 0; i < DH / 32; ++i) acc[i] = f32x16{};
         float mrun = 0.f, lrun = 0.f;
-        for (int kt = 0; kt < ntiles; ++kt) {
-            const bool more = kt + 1 < ntiles;
-            if (more) {
-                fetch(I, rt, kt + 1);
-            } else if (has_j) {
-                fetch(J, rt ^ 1, 0);
-            }
-            if (wave_active) {
-                f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                    for (int kb = 0; kb < DH / 16; ++kb) {
-                        const bf16x8 a = *(const bf16x8 *)&sm.k[buf][32 * sub + col][16 * kb + 8 * half];
-                        s[sub] = mfma(a, qf[kb], s[sub]);
-                    }
-                // Keys past the window (only in the last, ragged tile) get -inf.
-                if (kt * KT + KT > I.m) {
-#pragma unroll
-                    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                        for (int rr = 0; rr < 16; ++rr) {
-                            const int j = kt * KT + 32 * sub + 8 * (rr >> 2) + 4 * half + (rr & 3);
-                            s[sub][rr] = j < I.m ? s[sub][rr] : -INFINITY;
-                        }
-                }
-                // Probabilities against the base mrun (log2 units): the exact maximum
-                // of the first tile, raised later only when a tile's probabilities
-                // reach 2^20 (or overflow): then O and l are rescaled and the tile's
-                // probabilities recomputed.
-                if (kt == 0) mrun = tile_max(s);
-                bf16x8 pf[4];
-                float lsum = probs(s, mrun, pf);
-                if (__any(!(lsum < 0x1p20f))) {
-                    const float mnew = fmaxf(mrun, tile_max(s));
-                    const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
-                    lrun *= corr;
-#pragma unroll
-                    for (int i = 0; i < DH / 32; ++i) acc[i] *= corr;
-                    mrun = mnew;
-                    lsum = probs(s, mrun, pf);
-                }
-                lrun += lsum;
-#pragma unroll
-                for (int dt = 0; dt < DH / 32; ++dt)
-#pragma unroll
-                    for (int kb2 = 0; kb2 < 4; ++kb2)
-                        acc[dt] = mfma(v_frag<DH + VPAD>(&sm.v[buf][0][0], 16 * kb2, 32 * dt), pf[kb2], acc[dt]);
-            }
-            if (more || has_j) stash(buf ^ 1);
-            // The next item's Q rows are requested at the end of the tile before its last
-            // (after that tile's own wait), so that neither wait includes them.
-            if (has_j && kt == (ntiles >= 2 ? ntiles - 2 : ntiles - 1)) load_q(J, rt ^ 1, qn);
+        for (int kt = 0; kt < n; kt += 2) {
+            // even tile kt (buffer 0); tile kt + 1 waits in set 1, tile kt + 2 goes to set 0
+            fetch_pos(kt + 2, n, k0, v0);
+            if (wave_active && kt * KT < I.m) compute(I, kt, 0, qf, acc, mrun, lrun);
+            stash(1, k1, v1);
             __syncthreads();
-            buf ^= 1;
+            // odd tile kt + 1 (buffer 1); tile kt + 2 waits in set 0, tile kt + 3 goes to set 1
+            fetch_pos(kt + 3, n, k1, v1);
+            if (wave_active && (kt + 1) * KT < I.m) compute(I, kt + 1, 1, qf, acc, mrun, lrun);
+            stash(0, k0, v0);
+            __syncthreads();
         }
+        // The next item's Q rows (or the current ones again: the load is always issued),
+        // straight into the fragments this item no longer reads.
+        load_q(has_j ? J : I, has_j ? (rt ^ 1) : rt, qf);
 
-        // O leaves through LDS, in rounds of RD value dims: each wave writes its
-        // 32 rows into a private area of the tile buffer nobody reads any more
-        // (16-byte chunks XOR-swizzled by row against bank conflicts), then
+        // O leaves through LDS, in rounds of RD value dims: each wave writes its 32
+        // rows into a private area of buffer 1 (the item's last tile, read by now),
+        // with 16-byte chunks XOR-swizzled by row against bank conflicts, then
         // stores whole row segments of RD values with consecutive lanes.
         {
             constexpr int RD = DH == 128 ? 64 : 32;  // value dims per round
             constexpr int CPR = RD / 8;              // 16-byte chunks per row segment
-            __bf16 *stage = (wave < 4 ? &sm.k[buf ^ 1][0][0] : &sm.v[buf ^ 1][0][0]) + (wave & 3) * 32 * RD;
+            __bf16 *stage = (wave < 4 ? &sm.k[1][0][0] : &sm.v[1][0][0]) + (wave & 3) * 32 * RD;
             const float inv = 1.f / (lrun + __shfl_xor(lrun, 32));
 #pragma unroll
             for (int r = 0; r < DH / RD; ++r) {
@@ -360,8 +379,6 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
         if (!has_j) break;
         I = J;
         rt ^= 1;
-#pragma unroll
-        for (int kb = 0; kb < DH / 16; ++kb) qf[kb] = qn[kb];
         has_j = next_item(J);
         // Every wave is past its output rows: the staging area (stored into by the
         // next tile) and the finished item's table are free.
