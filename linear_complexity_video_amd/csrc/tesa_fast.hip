@@ -4,17 +4,19 @@
 // Work item = (window, head, block of 256 queries). One persistent workgroup
 // of 8 waves per CU runs a sequence of items, each wave 32 queries of the
 // current one. The canonical token of every window position is tabulated in
-// LDS one item ahead. Keys and values stream through LDS in tiles of 64
+// LDS two items ahead. Keys and values stream through LDS in tiles of 64
 // (double buffered, both in their natural row layout; the V^T operand is read
 // with the gfx950 LDS transpose read), loaded two tiles ahead through two
 // register sets, and the tile stream runs on across items: the next item's
-// first tiles load during the current one's last, its Q rows right after. Per tile each wave computes S^T = K Q^T, so that a lane holds
-// one query's scores and the softmax needs only one cross-lane exchange; exp'd
+// first tiles load during the current one's last, its Q rows right after.
+// Per tile each wave computes S^T = K Q^T, so that a lane holds one query's
+// scores and the softmax needs only one cross-lane exchange; exp'd
 // P^T is then directly the B operand of O^T += V^T P^T, and O^T again has one
 // query per lane, so the online-softmax rescale is a per-lane multiply. The
 // exponent base is the first tile's maximum and is raised (with the rescale)
 // only when a later tile's probabilities reach 2^20, so most tiles compute no
-// maximum at all. O leaves through LDS as whole row segments. Each XCD owns a
+// maximum at all. O leaves through a per-wave LDS staging area as whole row
+// segments, so moving to the next item needs no barrier. Each XCD owns a
 // contiguous range of items, so the query blocks of one window run side by
 // side on one XCD and share its K/V in L2.
 #include <algorithm>
@@ -63,6 +65,7 @@ template <int DH, int ROWS>
 struct __attribute__((aligned(16))) Smem {
     __bf16 k[2][KT][DH + KPAD];
     __bf16 v[2][KT][DH + VPAD];
+    __bf16 ostage[8][32 * (DH == 128 ? 64 : 32)];  // per wave: output rows on their way out
     uint32_t row[ROWS];           // canonical token of each window position
 };
 
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
                                                    int st, int sh, int sw, int nrt, int nrh, int nrw, int nqb,
                                                    uint32_t total, float c_log2)
 {
-    __shared__ Smem<DH, WHOLE ? 4 : 2 * MAXW> sm;
+    __shared__ Smem<DH, WHOLE ? 4 : 3 * MAXW> sm;
     constexpr int DC = DH / 8;  // 16-byte chunks per row
 
     // Item sequence of this workgroup. Block L runs on XCD L % 8; XCD x owns the
@@ -299,12 +302,18 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
         return n + (n & 1);
     };
 
-    Item I, J;
+    // Items run in sequence; item number s keeps its window table in table s % 3.
+    // The table (and the decode) of the item after the next one is made during
+    // the current item's first tile pair, after that pair's first barrier: by
+    // then every wave has finished the item that used the same table.
+    Item I, J, K;
     if (!next_item(I)) return;  // uniform over the workgroup
     bool has_j = next_item(J);
+    bool has_k = false;
     int rt = 0;                 // table of the current item
+    auto nxt = [](int t) { return t == 2 ? 0 : t + 1; };
     build_table(I, rt);
-    if (has_j) build_table(J, rt ^ 1);
+    if (has_j) build_table(J, nxt(rt));
     __syncthreads();
     bf16x8 qf[DH / 16];
     load_q(I, rt, qf);
@@ -320,7 +329,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     // Every fetch is issued, so the compiler's memory waits stay exact.
     auto fetch_pos = [&](int kt, int n, u32x4 (&kreg)[KPER], u32x4 (&vreg)[KPER]) {
         const bool in_i = kt < n, use_j = !in_i && has_j;
-        fetch(use_j ? J : I, use_j ? (rt ^ 1) : rt, in_i ? kt : (use_j ? kt - n : 0), kreg, vreg);
+        fetch(use_j ? J : I, use_j ? nxt(rt) : rt, in_i ? kt : (use_j ? kt - n : 0), kreg, vreg);
     };
 
     for (;;) {
@@ -338,23 +347,36 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
             __syncthreads();
             // odd tile kt + 1 (buffer 1); tile kt + 2 waits in set 0, tile kt + 3 goes to set 1
             fetch_pos(kt + 3, n, k1, v1);
+            if (kt == 0 && has_j) {
+                has_k = next_item(K);
+                if (has_k) build_table(K, nxt(nxt(rt)));
+            }
             if (wave_active && (kt + 1) * KT < I.m) compute(I, kt + 1, 1, qf, acc, mrun, lrun);
             stash(0, k0, v0);
             __syncthreads();
         }
         // The next item's Q rows (or the current ones again: the load is always issued),
         // straight into the fragments this item no longer reads.
-        load_q(has_j ? J : I, has_j ? (rt ^ 1) : rt, qf);
+        load_q(has_j ? J : I, has_j ? nxt(rt) : rt, qf);
 
-        // O leaves through LDS, in rounds of RD value dims: each wave writes its 32
-        // rows into a private area of buffer 1 (the item's last tile, read by now),
-        // with 16-byte chunks XOR-swizzled by row against bank conflicts, then
-        // stores whole row segments of RD values with consecutive lanes.
+        // O leaves through this wave's staging area, in rounds of RD value dims
+        // (16-byte chunks XOR-swizzled by row against bank conflicts): all rows are
+        // read back first, then stored as whole row segments by consecutive lanes.
         {
             constexpr int RD = DH == 128 ? 64 : 32;  // value dims per round
             constexpr int CPR = RD / 8;              // 16-byte chunks per row segment
-            __bf16 *stage = (wave < 4 ? &sm.k[1][0][0] : &sm.v[1][0][0]) + (wave & 3) * 32 * RD;
+            constexpr int PER = 32 * CPR / 64;       // chunks per lane and round
+            __bf16 *stage = sm.ostage[wave];
             const float inv = 1.f / (lrun + __shfl_xor(lrun, 32));
+            size_t dst[PER];
+            bool ok[PER];
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int rq = (lane + 64 * j) / CPR, qq = I.q_base + wave * QW + rq;
+                ok[j] = qq < I.m;
+                dst[j] = I.head_off + row_of(rt, ok[j] ? qq : 0) * rowstride + 8 * ((lane + 64 * j) % CPR);
+            }
+            u32x4 val[DH / RD][PER];
 #pragma unroll
             for (int r = 0; r < DH / RD; ++r) {
 #pragma unroll
@@ -368,25 +390,23 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
                         *(bf16x4 *)(stage + col * RD + 8 * ch + 4 * half) = out;
                     }
 #pragma unroll
-                for (int j = 0; j < 32 * CPR / 64; ++j) {
+                for (int j = 0; j < PER; ++j) {
                     const int idx = lane + 64 * j, rq = idx / CPR, ch = idx % CPR;
-                    const u32x4 val = *(const u32x4 *)(stage + rq * RD + 8 * (ch ^ (rq & (CPR - 1))));
-                    const int qq = I.q_base + wave * QW + rq;
-                    if (qq < I.m) *(u32x4 *)(o + I.head_off + row_of(rt, qq) * rowstride + RD * r + 8 * ch) = val;
+                    val[r][j] = *(const u32x4 *)(stage + rq * RD + 8 * (ch ^ (rq & (CPR - 1))));
                 }
             }
+#pragma unroll
+            for (int r = 0; r < DH / RD; ++r)
+#pragma unroll
+                for (int j = 0; j < PER; ++j)
+                    if (ok[j]) *(u32x4 *)(o + dst[j] + RD * r) = val[r][j];
         }
         if (!has_j) break;
         I = J;
-        rt ^= 1;
-        has_j = next_item(J);
-        // Every wave is past its output rows: the staging area (stored into by the
-        // next tile) and the finished item's table are free.
-        __syncthreads();
-        if (!WHOLE && has_j) {
-            build_table(J, rt ^ 1);
-            __syncthreads();
-        }
+        J = K;
+        has_j = has_k;
+        has_k = false;
+        rt = nxt(rt);
     }
 }
 
