@@ -237,9 +237,9 @@ __global__ __launch_bounds__(256) void k_perm(uint32_t *__restrict__ perm, uint3
 // Each wave owns (s-block, p-block) tile pairs: the backward state G^T and the forward sum F^T of the
 // same tile share both operand tiles, B^T and x (fp16); the per-token weights of the two sums,
 // dt exp(ce) and dt exp(tot - cs + logD), are applied to the x operand in registers (packed fp16).
-// Loads of the chunk two to the left are issued every step (clamped at the segment start) and the
-// per-step stores are made by every wave, so the compiler's memory waits are not widened by paths that
-// skip them.
+// The x rows and per-token values of the chunk two to the left (and B of the next one) are loaded every
+// step (clamped at the segment start), and the per-step stores are made by every wave, so the
+// compiler's memory waits are not widened by paths that skip them.
 // ---------------------------------------------------------------------------
 template <int S, int Q, bool MAIN>
 __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
@@ -282,13 +282,17 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
     const size_t bh = (size_t)b * nheads + h;
     const size_t drow = bh * Lpad;
     const size_t gch = ((size_t)b * G + g) * nch;
-    // Chunk data is fetched two chunks ahead into two alternating register stages.
+    // x rows and per-token values are fetched two chunks ahead into two alternating
+    // register stages (their HBM latency exceeds a chunk's work). B of the main pass
+    // (contiguous fp16 rows of group data, L2-resident) comes one chunk ahead; the
+    // review pass gathers B with the chunk's row table, so it rides in the stage.
     struct Stage {
         Rows<Q, P, NT> xr;
-        u32x4 bq[BPER];  // B pieces k = tid + NT it: row k / (S / 8), 8 columns at 8 (k % (S / 8))
+        u32x4 bq[BPER];  // review pass: B pieces k = tid + NT it (row k / (S / 8), 8 columns at 8 (k % (S / 8)))
         float tok_d, tok_c, tot;
     };
-    Stage st0;
+    Stage stA, stB;
+    u32x4 bm[BPER];       // main pass: B of the chunk after the current one, same pieces
     uint32_t pnext = 0u;  // row-table entry of the chunk after the one fetched last
     bool pvalid = false;
     auto fetch = [&](Stage &stg, int c) {
@@ -302,11 +306,7 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
         else
             pnext = i;
         stg.xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
-        if constexpr (MAIN) {
-            const _Float16 *src = b16 + (gch + c) * (size_t)(Q * S);
-#pragma unroll
-            for (int it = 0; it < BPER; ++it) stg.bq[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
-        } else {
+        if constexpr (!MAIN) {
             Rows<Q, S, NT> br;
             br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * L);
 #pragma unroll
@@ -317,10 +317,22 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
         stg.tok_c = csT[crow0 + tq];
         stg.tot = csT[crow0 + Q - 1];
     };
-    // Prologue: rows and data of the rightmost chunk.
+    auto fetch_b = [&](int c) {
+        if constexpr (MAIN) {
+            const _Float16 *src = b16 + (gch + c) * (size_t)(Q * S);
+#pragma unroll
+            for (int it = 0; it < BPER; ++it) bm[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
+        }
+    };
+    // Prologue: rows and data of the rightmost chunk, then the rows and x of the one before.
     if (row_thread) s_row[tid] = seq_row(MAIN ? perm : nullptr, (uint32_t)(c_hi - 1) * Q + tid, L);
     __syncthreads();
-    fetch(st0, c_hi - 1);
+    fetch(stA, c_hi - 1);
+    fetch_b(c_hi - 1);
+    __syncthreads();  // every lane has read the rows of chunk c_hi - 1
+    s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
+    __syncthreads();
+    fetch(stB, max(c_hi - 2, c_lo));  // a one-chunk segment: issued, unused
     float logD = 0.f;  // sum of dt*A over the chunks right of the current one
 
     auto step = [&](Stage &cur, int c) {
@@ -344,11 +356,16 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
         }
 
         __syncthreads();  // previous chunk's MFMA reads of LDS and the row-table reads are done
-        // The staged values are used from here on (their loads had a step to complete).
+        // The staged values are used from here on (their loads had two steps to complete).
 #pragma unroll
         for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) pin(cur.xr.r[it]);
 #pragma unroll
-        for (int it = 0; it < BPER; ++it) pin(cur.bq[it]);
+        for (int it = 0; it < BPER; ++it) {
+            if constexpr (MAIN)
+                pin(bm[it]);
+            else
+                pin(cur.bq[it]);
+        }
         pin(cur.tok_d);
         pin(cur.tok_c);
         pin(cur.tot);
@@ -358,8 +375,11 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
 #pragma unroll
         for (int it = 0; it < BPER; ++it) {
             const int k = tid + NT * it;
-            u32x4 v = cur.bq[it];
-            if constexpr (!MAIN) {
+            u32x4 v;
+            if constexpr (MAIN) {
+                v = bm[it];
+            } else {
+                v = cur.bq[it];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = pack2h(lo_f(v[e]), hi_f(v[e]));
             }
@@ -370,11 +390,13 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
             s_wb[tid] = (_Float16)(d * ex2((cs - d * a) * LOG2E));
             s_wf[tid] = (_Float16)(d * ex2((tot_c - cs + logD) * LOG2E));
         }
-        // Every thread stores its (identical) entry: a use on all paths keeps the row load where it is issued.
+        // Rows of chunk c - 2. Every thread stores its (identical) entry: a use on all paths keeps
+        // the row load where it is issued.
         s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
         __syncthreads();
 
-        fetch(cur, max(c - 1, c_lo));  // at the segment start: issued, unused
+        fetch(cur, max(c - 2, c_lo));  // near the segment start: issued, unused
+        fetch_b(max(c - 1, c_lo));
         if (active) {
             const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
@@ -395,7 +417,12 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
         }
         logD += tot_c;
     };
-    for (int c = c_hi - 1; c >= c_lo; --c) step(st0, c);
+    int c = c_hi - 1;
+    for (; c - 1 >= c_lo; c -= 2) {
+        step(stA, c);
+        step(stB, c - 1);
+    }
+    if (c >= c_lo) step(stA, c);
 
     // Segment summaries: G (backward state entering the segment from its right end, from zero) and F.
     if (active) {
