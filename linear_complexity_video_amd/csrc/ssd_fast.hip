@@ -395,8 +395,9 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
         s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
         __syncthreads();
 
-        fetch(cur, max(c - 2, c_lo));  // near the segment start: issued, unused
+        // B (needed next step) before x (needed in two): waits complete in issue order.
         fetch_b(max(c - 1, c_lo));
+        fetch(cur, max(c - 2, c_lo));  // near the segment start: issued, unused
         if (active) {
             const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
