@@ -180,6 +180,19 @@ struct Rows {
             *(u32x4 *)(dst + row_of(it) * LD + 8 * cc_of(it)) = o;
         }
     }
+    // store_f16 with the thread index passed in (t = threadIdx.x)
+    template <int LD>
+    __device__ __forceinline__ void store_f16_at(__bf16 *dst, int t) const
+    {
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack2h(lo_f(r[it][e]), hi_f(r[it][e]));
+            const int k = t + NT * it;
+            *(u32x4 *)(dst + (k / UPR) * LD + 8 * (k % UPR)) = o;
+        }
+    }
     template <int LD>
     __device__ __forceinline__ void store_scaled(__bf16 *dst, int it, float w) const
     {
@@ -210,13 +223,13 @@ __device__ __forceinline__ HbPiece hb_piece(int k)
     return {32 * (t & 1) + (l & 31), 32 * (t >> 1) + 16 * q + 4 * (l >> 5)};
 }
 
-// CB of a chunk is stored in 8-element pieces in the order the output sweep reads them: thread lane l
-// of wave w (Q/16 waves) owns row t = 16 w + l % 16 and, in every 32-column block U, columns
-// 32 U + 8 (l / 16) + 0..7. Returns the element offset of piece (t, U, m = (u % 32) / 8).
-template <int Q>
-__device__ __forceinline__ int cb_piece(int t, int U, int m)
+// Operands in MFMA operand order: block blk (a 32-row block of the operand's m or n index) and k-block kb
+// (16 consecutive values of the contraction index, kblocks of them per block) hold, for lane l, the 8
+// values of row 32 blk + l % 32 at k = 16 kb + 8 (l / 32) + 0..7, as the l-th 16 bytes of a 1 KB piece.
+// Returns the element offset of that lane's 8 values.
+__device__ __forceinline__ int op_piece(int blk, int kb, int kblocks, int l)
 {
-    return (((U * (Q / 16) + (t >> 4)) * 64) + (t & 15) + 16 * m) * 8;
+    return ((blk * kblocks + kb) * 64 + l) * 8;
 }
 
 // ---------------------------------------------------------------------------
@@ -471,24 +484,28 @@ __global__ __launch_bounds__(256) void k_seg_pass(const float *__restrict__ segF
 }
 
 // ---------------------------------------------------------------------------
-// 3. Per chunk and group (grid (nch, G, batch)), for the output sweep:
-//    cb    CB[t][u] = C_t . B_u (fp16), computed as CB^T = B C^T so each lane holds 4 consecutive u of one t,
-//          stored in the output sweep's piece order (cb_piece);
-//    b16   the chunk's B rows in scan order, as fp16 ([Q][S]);
-//    cfrag the chunk's C rows in MFMA operand order: for token block tb and k-block kb, lane l's 8 values
-//          C[32 tb + l % 32][16 kb + 8 (l / 32) + 0..7] are the l-th 16 bytes of a 1 KB block, so the sweep
-//          reads each operand with one contiguous load per wave.
+// 3. Per chunk and group (grid (nch, G, batch)), the output sweep's operands in MFMA operand order
+//    (see op_piece), so that each wave reads each operand with one contiguous 1 KB load per k-block:
+//    cb    CB[t][u] = C_t . B_u (fp16), token block tb = t / 32, k-blocks over u;
+//    cfrag C rows (bf16), token block tb, k-blocks over the state index s;
+//    bfrag B^T rows (fp16), state block sb = s / 32, k-blocks over u;
+//    b16   and, for the state sweep, the chunk's B rows in scan order as fp16 ([Q][S]).
+// CB is computed as CB^T = B C^T so each lane holds 4 consecutive u of one t. B^T goes through LDS:
+// the B rows are written there and read back with the transposing LDS read.
 // ---------------------------------------------------------------------------
 template <int S, int Q>
 __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
                                            const uint32_t *__restrict__ perm, _Float16 *__restrict__ cb,
-                                           _Float16 *__restrict__ b16, __bf16 *__restrict__ cfrag, int G, uint32_t L)
+                                           _Float16 *__restrict__ b16, __bf16 *__restrict__ cfrag,
+                                           _Float16 *__restrict__ bfrag, int G, uint32_t L)
 {
+    constexpr int LB = S + XPAD;
+    __shared__ __attribute__((aligned(16))) _Float16 bt[Q * LB];
     const uint32_t c = blockIdx.x;
     const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    constexpr int TB = Q / 32;
+    constexpr int TB = Q / 32, KU = Q / 16, KS = S / 16;
     constexpr int TILES = TB * TB / 4;  // per wave
     const size_t rs = (size_t)G * S;
     const size_t chunk = ((size_t)b * G + g) * gridDim.x + c;
@@ -510,17 +527,18 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
             bv = tok ? bv : u32x4{0, 0, 0, 0};
             acc = mfma(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc);
         }
-        // acc: rows u = 32ub + 8g4 + 4half + j, column t = 32tb + col; stored in piece order (see cb_piece)
-        const int t = 32 * tb + col;
+        // acc: rows u = 32 ub + 8 g4 + 4 half + j, column t = 32 tb + col. The 8-value piece holding
+        // u = 32 ub + 8 g4 + 0..7 is k-block 2 ub + g4 / 2, lane col + 32 (g4 % 2).
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             f16x4 v4;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v4[j] = (_Float16)acc[4 * g4 + j];
-            *(f16x4 *)(out + cb_piece<Q>(t, ub, g4) + 4 * half) = v4;
+            *(f16x4 *)(out + op_piece(tb, 2 * ub + (g4 >> 1), KU, col + 32 * (g4 & 1)) + 4 * half) = v4;
         }
     }
-    // B rows as fp16 (exact for bf16 values in fp16's normal range) and C rows in operand order.
+    // B rows as fp16 (exact for bf16 values in fp16's normal range), to global and LDS; C rows in
+    // operand order.
     constexpr int PIECES = Q * S / 8, PER = PIECES / NT;
     static_assert(PIECES % NT == 0, "pieces must split evenly");
     _Float16 *bo = b16 + chunk * (size_t)(Q * S);
@@ -536,54 +554,68 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = i < L ? pack2h(lo_f(v[e]), hi_f(v[e])) : 0u;
             *(u32x4 *)(bo + (size_t)row * S + 8 * c8) = o;
+            *(u32x4 *)(bt + row * LB + 8 * c8) = o;
         }
         {
-            const int l = k % 64, kb = (k / 64) % (S / 16), tb = k / (64 * (S / 16));
+            const int l = k % 64, kb = (k / 64) % KS, tb = k / (64 * KS);
             const uint32_t i = c * Q + 32 * tb + (l & 31);
             const u32x4 v = *(const u32x4 *)(Cm + ((size_t)b * L + (i < L ? perm[i] : 0u)) * rs + (size_t)g * S +
                                               16 * kb + 8 * (l >> 5));
             *(u32x4 *)(co + 8 * (size_t)k) = i < L ? v : u32x4{0, 0, 0, 0};
         }
     }
+    __syncthreads();
+    // B^T pieces: block (state block sb, k-block kb) holds, for lane l, B[16 kb + 8 (l / 32) + 0..7][32 sb + l % 32].
+    _Float16 *bfo = bfrag + chunk * (size_t)(Q * S);
+    constexpr int BLOCKS = (S / 32) * KU;
+    static_assert(BLOCKS % 4 == 0, "blocks must split evenly over the waves");
+#pragma unroll
+    for (int k = 0; k < BLOCKS / 4; ++k) {
+        const int blk = wave + 4 * k;
+        const int sb = blk / KU, kb = blk % KU;
+        *(bf16x8 *)(bfo + op_piece(sb, kb, KU, lane)) = frag_tr((const __bf16 *)bt, LB, 16 * kb, 32 * sb);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// 4. Left-to-right output sweep. Same grid/items as k_states (main segments).
+// 4. Left-to-right output sweep. Same items as k_states (main segments); workgroups of four waves (one
+// per SIMD) and two workgroups per CU, so that the phases of one overlap those of the other.
 //
-// Per chunk, three phases separated by barriers:
-//   build  this chunk's C operands are requested (contiguous, in operand order), then the next chunk's
-//          data; Hf advances on fp16 MFMA (Hf^T += B^T (w x)^T with w = dt exp(tot - cs) applied to the
-//          x operand in registers); every thread turns one 8-column piece of CB per 32-column block into M
-//          in place (fp16, row t = token); the 16 rows of a wave lie in one 32-row block, so each piece is
-//          uniformly below, on or above the diagonal block across the wave;
-//   use    Y^T = X^T M^T + ef (Hf C^T) + eb (Hb C^T); Y goes to LDS as bf16 rows;
-//   store  Y rows leave as contiguous 16-byte pieces; the next chunk is staged: x (fp16), B (fp16), the
-//          forward state Hf (from the accumulators), the backward state Hb = stored local state + decay *
-//          border state, CB, and the per-token decay data.
+// Per chunk, two phases separated by barriers:
+//   compute  The operands with a single consumer come from global memory in operand order (B^T, CB, C;
+//            group data that the heads of a group share in L2), so only x and the two states pass
+//            through LDS. Wave w owns the Y^T tiles of one token block (both p-blocks at Q = 128) and the
+//            Hf^T tiles of one state block. Per 16-token k-block, the x operands (transposed LDS reads)
+//            serve both the intra-chunk product X^T M^T (fp16) and the state update
+//            Hf^T = exp(tot) Hf^T + B^T (w x)^T (w = dt exp(tot - cs) applied to the x operand in
+//            registers); each lane builds its M^T operand (row t = its token, 8 consecutive u) from its
+//            CB piece in registers. Then the inter-chunk terms ef (Hf C^T) + eb (Hb C^T) are added with
+//            ef = exp(cs), eb = exp(tot - ce) per token, and Y goes to LDS as bf16 rows.
+//   store    Y rows leave as contiguous 16-byte pieces; the next chunk is staged: x (fp16), the forward
+//            state Hf (from the accumulators), the backward state Hb = stored local state + decay *
+//            border state, and the per-token decay data.
 // Every load and store in the loop is unconditional (a lane past the end of the sequence reads row 0
 // and stores into a scratch row), and no load result crosses the loop edge, so the compiler's memory
 // waits stay exact.
 // ---------------------------------------------------------------------------
 template <int S, int Q>
-__global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ b16,
-                                            const __bf16 *__restrict__ cfrag, const _Float16 *__restrict__ cb,
-                                            const uint32_t *__restrict__ perm,
-                                            const float *__restrict__ dtT, const float *__restrict__ csT,
-                                            const float *__restrict__ A, const float *__restrict__ Dv,
-                                            const __bf16 *__restrict__ hb_local, const float *__restrict__ delta,
-                                            const float *__restrict__ hinF, const __bf16 *__restrict__ hinB,
-                                            __bf16 *__restrict__ y, __bf16 *__restrict__ ytrash, int nheads, int G,
-                                            uint32_t N, uint32_t Lpad, int nch, int segch, int nseg,
-                                            uint32_t total_items)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, const __bf16 *__restrict__ cfrag,
+           const _Float16 *__restrict__ cb, const uint32_t *__restrict__ perm, const float *__restrict__ dtT,
+           const float *__restrict__ csT, const float *__restrict__ A, const float *__restrict__ Dv,
+           const __bf16 *__restrict__ hb_local, const float *__restrict__ delta, const float *__restrict__ hinF,
+           const __bf16 *__restrict__ hinB, __bf16 *__restrict__ y, __bf16 *__restrict__ ytrash, int nheads, int G,
+           uint32_t N, uint32_t Lpad, int nch, int segch, int nseg, uint32_t total_items)
 {
-    constexpr int NT = Q * 4, NW = Q / 16;  // Q/16 waves, two per SIMD at Q = 128
-    constexpr int LX = P + XPAD, LB = S + XPAD, SS = S + 8, LM = Q + 8, LY = P + 8;
-    constexpr int UB = Q / 32;              // 32-column blocks of M
+    constexpr int LX = P + XPAD, SS = S + 8, LY = P + 8;
+    constexpr int KU = Q / 16;  // k-blocks over the chunk's tokens
+    constexpr int KS = S / 16;  // k-blocks over the state
+    constexpr int YT = Q / 64;  // Y^T tiles per wave: token block tb, p-blocks pb0 ..
+    constexpr int HT = S / 64;  // Hf^T tiles per wave: state block hsb, p-blocks hpb0 ..
+    constexpr int NPX = (YT == 2 || HT == 2) ? 2 : 1;  // p-blocks of the x operands a wave reads
     __shared__ _Float16 xn[Q * LX];  // x as fp16: operand of the intra-chunk product and of the state update
-    __shared__ _Float16 bn[Q * LB];  // B as fp16
     __shared__ __bf16 hfl[P * SS];   // forward state entering the chunk, [p][s]
     __shared__ __bf16 hbl[P * SS];   // backward state entering the chunk from the right, [p][s]
-    __shared__ __attribute__((aligned(16))) _Float16 mt[Q * LM];  // CB, then M[t][u] (fp16)
     __shared__ __attribute__((aligned(16))) __bf16 ybuf[Q * LY];  // output rows [t][p]
     // per token: cs, ce (log2 units), dt, the split decay factors of the off-diagonal blocks, the state weight
     __shared__ __attribute__((aligned(16))) float s_cs[Q], s_ce[Q], s_dt[Q];
@@ -603,28 +635,16 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool row_thread = wave < Q / 64;  // tid < Q
-    // One Y^T tile per wave: t-block wave / 2, p-block wave % 2.
-    const int tb = wave >> 1, pb = wave & 1;
-    // Role in building M: row mrow, columns 32 U + 8 msub + 0..7 for every block U (one row per lane of
-    // each 16-lane group, so LDS accesses of a group hit distinct banks); the wave's rows
-    // 16 wave .. 16 wave + 15 all lie in row block wave / 2.
-    const int mrow = 16 * wave + (lane & 15), msub = lane >> 4, mtb = wave >> 1;
-    // Hf^T tiles (S/32 s-blocks x 2 p-blocks) over the waves: HT per wave, or one
-    // tile for the first S/16 waves when there are fewer tiles than waves.
-    constexpr int HTILES = S / 16;
-    constexpr int HT = HTILES >= NW ? HTILES / NW : 1;
-    const bool hact = wave < HTILES;
-    const int hsb = (wave * HT) >> 1;
-    const int hpb0 = (wave * HT) & 1;
+    const bool row_thread = tid < Q;
+    const int tb = (wave * YT) >> 1, pb0 = (wave * YT) & 1;
+    const int hsb = (wave * HT) >> 1, hpb0 = (wave * HT) & 1;
+    const int px0 = NPX == 2 ? 0 : (wave & 1);  // with one p-block each, pb0 = hpb0 = wave % 2
     const float a = A[h];
     const float twoD = 2.f * Dv[h];
     constexpr int PS = P * S;
 
     f32x16 hacc[HT];
-#pragma unroll
-    for (int i = 0; i < HT; ++i) hacc[i] = f32x16{};
-    if (hact) {
+    {
         const float *src = hinF + (bh * nseg + seg) * (size_t)PS;
 #pragma unroll
         for (int i = 0; i < HT; ++i)
@@ -635,38 +655,36 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
                 for (int j = 0; j < 4; ++j) hacc[i][4 * g4 + j] = v4[j];
             }
     }
-    // Border state of the backward direction (bf16), for this thread's staging chunks.
-    constexpr int HBC = PS / 8 / NT;  // 16-byte chunks of Hb per thread
-    // (pieces in the stored states' accumulator order; see hb_piece)
+    // Border state of the backward direction (bf16), for this thread's staging pieces (in the stored
+    // states' accumulator order; see hb_piece). It is the same for the whole segment and L2-resident;
+    // it is reloaded before each staging rather than held in registers through the compute phase (the
+    // pinned offset keeps the compiler from hoisting the loads out of the loop).
+    constexpr int HBC = PS / 8 / NT;
     u32x4 hinb[HBC];
-    {
-        const __bf16 *src = hinB + (bh * nseg + seg) * (size_t)PS;
+    const size_t hinb_off = (bh * nseg + seg) * (size_t)PS;
+    auto load_hinb = [&]() {
+        size_t off = hinb_off;
+        asm volatile("" : "+s"(off));
+        const __bf16 *hs = hinB + off;
 #pragma unroll
         for (int it = 0; it < HBC; ++it) {
             const HbPiece pc = hb_piece(tid + NT * it);
-            const u32x2 lo = *(const u32x2 *)(src + pc.p * S + pc.s_a);
-            const u32x2 hi = *(const u32x2 *)(src + pc.p * S + pc.s_a + 8);
+            const u32x2 lo = *(const u32x2 *)(hs + pc.p * S + pc.s_a);
+            const u32x2 hi = *(const u32x2 *)(hs + pc.p * S + pc.s_a + 8);
             hinb[it] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
-    }
+    };
 
     Rows<Q, P, NT> xr;
-    constexpr int BPER = Q * S / 8 / NT;  // 16-byte pieces of the B tile per thread
     const size_t gch = ((size_t)b * G + g) * nch;  // chunk index base of this group
     const int t_tok = 32 * tb + col;  // this lane's token inside the chunk (Y^T column)
 
-    // Staging data of the next chunk: loaded in the build phase, consumed by the staging at the end of
-    // the same iteration.
-    u32x4 bru[BPER];
+    // Per-head data of the next chunk (HBM): loaded during the compute phase, consumed by the staging
+    // at the end of the same iteration.
     u32x4 hbr[HBC];
-    u32x4 cbr[UB];  // CB row pieces, for mt
     float tok_d = 0.f, tok_c = 0.f, tot = 0.f, dl = 0.f;
     uint32_t pnext = 0u;
     bool pvalid = false;
-    // The next chunk's data comes in two groups: per-head data that misses to HBM (x, the stored
-    // states, per-token values) early in the build phase, and the chunk's group data that other
-    // heads have just read (B, CB; L2-resident) in the use phase, where it overlaps the MFMAs
-    // instead of queueing in one burst before them.
     auto fetch = [&](int c) {
         xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * N);
         const __bf16 *src = hb_local + (bh * nch + c) * (size_t)PS;
@@ -685,36 +703,26 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
         tot = csT[crow0 + Q - 1];
         dl = delta[bh * nch + c];
     };
-    auto fetch_group = [&](int c) {
-        const _Float16 *bsrc = b16 + (gch + c) * (size_t)(Q * S);
-#pragma unroll
-        for (int it = 0; it < BPER; ++it) bru[it] = *(const u32x4 *)(bsrc + 8 * (tid + NT * it));
-        const _Float16 *cbs = cb + (gch + c) * (size_t)(Q * Q) + 8 * (size_t)tid;  // cb_piece(mrow, U, msub)
-#pragma unroll
-        for (int U = 0; U < UB; ++U) cbr[U] = *(const u32x4 *)(cbs + U * (Q / 16) * 512);
-    };
     uint32_t rowc = 0u;  // row-thread: global row of token tid of the staged chunk (~0u past the end)
+    // The staging and output addresses come from a thread index pinned where they are used, so the
+    // compiler recomputes them per chunk rather than holding them (and spilling them) across the loop.
     auto stage = [&]() {
-        xr.template store_f16<LX>((__bf16 *)xn);
+        int pt = tid;
+        pin(pt);
+        const int pcol = pt & 31, phalf = (pt >> 5) & 1;
+        xr.template store_f16_at<LX>((__bf16 *)xn, pt);
 #pragma unroll
-        for (int it = 0; it < BPER; ++it) {
-            const int k = tid + NT * it;
-            *(u32x4 *)&bn[(k / (S / 8)) * LB + 8 * (k % (S / 8))] = bru[it];
-        }
-        if (hact) {
+        for (int i = 0; i < HT; ++i)
 #pragma unroll
-            for (int i = 0; i < HT; ++i)
+            for (int g4 = 0; g4 < 4; ++g4) {
+                bf16x4 v4;
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    bf16x4 v4;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) v4[j] = (__bf16)hacc[i][4 * g4 + j];
-                    *(bf16x4 *)&hfl[(32 * (hpb0 + i) + col) * SS + 32 * hsb + 8 * g4 + 4 * half] = v4;
-                }
-        }
+                for (int j = 0; j < 4; ++j) v4[j] = (__bf16)hacc[i][4 * g4 + j];
+                *(bf16x4 *)&hfl[(32 * (hpb0 + i) + pcol) * SS + 32 * hsb + 8 * g4 + 4 * phalf] = v4;
+            }
 #pragma unroll
         for (int it = 0; it < HBC; ++it) {
-            const HbPiece pc = hb_piece(tid + NT * it);
+            const HbPiece pc = hb_piece(pt + NT * it);
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -722,8 +730,6 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
             *(u32x2 *)&hbl[pc.p * SS + pc.s_a] = u32x2{o[0], o[1]};
             *(u32x2 *)&hbl[pc.p * SS + pc.s_a + 8] = u32x2{o[2], o[3]};
         }
-#pragma unroll
-        for (int U = 0; U < UB; ++U) *(u32x4 *)(mt + mrow * LM + 32 * U + 8 * msub) = cbr[U];
         // Block-edge values of this token's 32-token block, from its lanes 0/31 (or 32/63).
         const int c0l = __builtin_amdgcn_readlane(__float_as_int(tok_c), 0);
         const int c31l = __builtin_amdgcn_readlane(__float_as_int(tok_c), 31);
@@ -736,23 +742,38 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
             const float blk_cs_end = __int_as_float(half ? c31h : c31l);
             const float blk_dt0 = __int_as_float(half ? d0h : d0l);
             const float cs2 = tok_c * LOG2E, ce2 = (tok_c - tok_d * a) * LOG2E;
-            s_dt[tid] = tok_d;
-            s_cs[tid] = cs2;
-            s_ce[tid] = ce2;
+            s_dt[pt] = tok_d;
+            s_cs[pt] = cs2;
+            s_ce[pt] = ce2;
             // below-diagonal blocks: exp(cs_end - cs_u); above: exp(ce_u - ce_start); both <= 1
-            s_gl[tid] = (_Float16)(tok_d * ex2(blk_cs_end * LOG2E - cs2));
-            s_gu[tid] = (_Float16)(tok_d * ex2(ce2 - (blk_cs0 - blk_dt0 * a) * LOG2E));
+            s_gl[pt] = (_Float16)(tok_d * ex2(blk_cs_end * LOG2E - cs2));
+            s_gu[pt] = (_Float16)(tok_d * ex2(ce2 - (blk_cs0 - blk_dt0 * a) * LOG2E));
             // weight of token u in the state carried out of the chunk
-            s_w[tid] = (_Float16)(tok_d * ex2(tot * LOG2E - cs2));
-            rowc = s_row[tid];
-            s_row[tid] = pvalid ? pnext : ~0u;
+            s_w[pt] = (_Float16)(tok_d * ex2(tot * LOG2E - cs2));
+            rowc = s_row[pt];
+            s_row[pt] = pvalid ? pnext : ~0u;
         }
     };
     // Output rows of the chunk in ybuf: contiguous 16-byte pieces (a past-the-end row goes to scratch).
+    // B^T (state update) and CB (intra-chunk product) of a chunk, per k-block in the order they are
+    // consumed: group data that the heads of a group share in L2. The first half of the k-blocks is
+    // loaded during the previous chunk, the second half at the start of the chunk.
+    u32x4 bfr[KU], cbf[KU];
+    auto fetch_group = [&](int c, int half_k) {
+        const _Float16 *bs = bfrag + (gch + c) * (size_t)(Q * S) + op_piece(hsb, 0, KU, lane);
+        const _Float16 *cs = cb + (gch + c) * (size_t)(Q * Q) + op_piece(tb, 0, KU, lane);
+#pragma unroll
+        for (int kb = half_k * (KU / 2); kb < (half_k + 1) * (KU / 2); ++kb) {
+            bfr[kb] = *(const u32x4 *)(bs + 512 * kb);
+            cbf[kb] = *(const u32x4 *)(cs + 512 * kb);
+        }
+    };
     auto store_y = [&]() {
+        int pt = tid;
+        pin(pt);
 #pragma unroll
         for (int it = 0; it < Q * (P / 8) / NT; ++it) {
-            const int k = tid + NT * it;
+            const int k = pt + NT * it;
             const int t = k / (P / 8), p8 = 8 * (k % (P / 8));
             const uint32_t r = s_rowy[t];
             __bf16 *dst = r != ~0u ? y + (((size_t)b * N + r) * nheads + h) * P + p8 : ytrash + p8;
@@ -764,107 +785,113 @@ __global__ __launch_bounds__(Q * 4) void k_out(const __bf16 *__restrict__ x, con
     if (row_thread) s_row[tid] = seq_row(perm, (uint32_t)c_lo * Q + tid, N);
     __syncthreads();
     fetch(c_lo);
-    fetch_group(c_lo);
+    load_hinb();
     __syncthreads();
     stage();
+    fetch_group(c_lo, 0);
 
     for (int c = c_lo; c < c_hi; ++c) {
         __syncthreads();  // staged chunk c visible
 
-        // ---- build ----
         const float tot_c = tot;
         const int cn = c + 1 < c_hi ? c + 1 : c;  // on the last iteration the loads are issued but unused
-        u32x4 cfr[S / 16];  // C operands of this lane's token: contiguous 1 KB per wave and k-block
+        // Load order within the chunk, so that every wait covers only older loads: the second half of
+        // this chunk's B^T and CB; mid-loop, C of this chunk (inter-chunk terms, after the k-block
+        // loop) and the next chunk's per-head data; after the inter-chunk terms, the border state
+        // (staging) and the first half of the next chunk's B^T and CB.
+        fetch_group(c, 1);
+        u32x4 cfr[KS];
+        const float cs_t = s_cs[t_tok], ce_t = s_ce[t_tok], dt_t = s_dt[t_tok];
+        // position of this lane's token inside its diagonal pieces (pinned: recomputed per chunk
+        // rather than held as hoisted per-element masks)
+        int jd = col - 8 * half;
+        pin(jd);
         {
-            const __bf16 *src = cfrag + (gch + c) * (size_t)(Q * S) + (size_t)tb * (S / 16) * 512 + 8 * lane;
-#pragma unroll
-            for (int kb = 0; kb < S / 16; ++kb) cfr[kb] = *(const u32x4 *)(src + 512 * kb);
-        }
-        fetch(cn);
-
-        // Hf = exp(tot) Hf + sum_u w_u x_u B_u^T (as Hf^T = B^T (w x)^T, fp16 operands)
-        if (hact) {
             const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
             for (int i = 0; i < HT; ++i) hacc[i] *= dec;
+        }
+        f32x16 yacc[YT];
 #pragma unroll
-            for (int kb = 0; kb < Q / 16; ++kb) {
-                const f16x8 af = __builtin_bit_cast(f16x8, frag_tr((const __bf16 *)bn, LB, 16 * kb, 32 * hsb));
-                const f16x8 w8 = *(const f16x8 *)(s_w + 16 * kb + 8 * half);
+        for (int j = 0; j < YT; ++j) yacc[j] = f32x16{};
 #pragma unroll
-                for (int i = 0; i < HT; ++i) {
-                    const f16x8 xv = __builtin_bit_cast(f16x8, frag_tr((const __bf16 *)xn, LX, 16 * kb, 32 * (hpb0 + i)));
-                    hacc[i] = mfma16(af, xv * w8, hacc[i]);
-                }
+        for (int kb = 0; kb < KU; ++kb) {
+            if (kb == KU / 2) {
+                const __bf16 *src = cfrag + (gch + c) * (size_t)(Q * S) + op_piece(tb, 0, KS, lane);
+#pragma unroll
+                for (int k2 = 0; k2 < KS; ++k2) cfr[k2] = *(const u32x4 *)(src + 512 * k2);
+                fetch(cn);
             }
+            f16x8 xa[NPX];
+#pragma unroll
+            for (int i = 0; i < NPX; ++i)
+                xa[i] = __builtin_bit_cast(f16x8, frag_tr((const __bf16 *)xn, LX, 16 * kb, 32 * (px0 + i)));
+            // M^T operand: M[t_tok][u0 + 0..7]
+            const int U = kb >> 1, u0 = 16 * kb + 8 * half;
+            const f16x8 cb8 = __builtin_bit_cast(f16x8, cbf[kb]);
+            f16x8 mf;
+            if (U == tb) {
+                const f32x4 d0 = *(const f32x4 *)(s_dt + u0), d1 = *(const f32x4 *)(s_dt + u0 + 4);
+                const f32x4 c0 = *(const f32x4 *)(s_cs + u0), c1 = *(const f32x4 *)(s_cs + u0 + 4);
+                const f32x4 e0 = *(const f32x4 *)(s_ce + u0), e1 = *(const f32x4 *)(s_ce + u0 + 4);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float cbv = (float)cb8[j];
+                    const float dtu = j < 4 ? d0[j] : d1[j - 4];
+                    const float csu = j < 4 ? c0[j] : c1[j - 4];
+                    const float ceu = j < 4 ? e0[j] : e1[j - 4];
+                    // the decay exponent of the right direction is the non-positive one
+                    const float m = cbv * dtu * ex2(fminf(cs_t - csu, ceu - ce_t));
+                    mf[j] = (_Float16)(16 * (kb & 1) + j == jd ? 2.f * cbv * dt_t + twoD : m);
+                }
+            } else if (U < tb) {
+                const f16x8 g8 = *(const f16x8 *)(s_gl + u0);
+                mf = cb8 * (g8 * (_Float16)ex2(cs_t - s_cs[32 * U + 31]));
+            } else {
+                const f16x8 g8 = *(const f16x8 *)(s_gu + u0);
+                mf = cb8 * (g8 * (_Float16)ex2(s_ce[32 * U] - ce_t));
+            }
+#pragma unroll
+            for (int j = 0; j < YT; ++j) yacc[j] = mfma16(xa[pb0 + j - px0], mf, yacc[j]);
+            // state update: Hf^T += B^T (w x)^T
+            const f16x8 w8 = *(const f16x8 *)(s_w + u0);
+            const f16x8 af = __builtin_bit_cast(f16x8, bfr[kb]);
+#pragma unroll
+            for (int i = 0; i < HT; ++i) hacc[i] = mfma16(af, xa[hpb0 + i - px0] * w8, hacc[i]);
         }
 
-        {
-            const float cs_t = s_cs[mrow], ce_t = s_ce[mrow], dt_t = s_dt[mrow];
-            _Float16 *mrw = mt + mrow * LM + 8 * msub;
+        // inter-chunk terms, one Y^T tile at a time: ef * (Hf C^T) + eb * (Hb C^T)
+        const float ef = ex2(cs_t);
+        const float eb = ex2(tot_c * LOG2E - ce_t);
 #pragma unroll
-            for (int U = 0; U < UB; ++U) {
-                const int u0 = 32 * U + 8 * msub;
-                const f16x8 cb8 = *(const f16x8 *)(mrw + 32 * U);
-                f16x8 mf;
-                if (U == mtb) {
-                    const f32x4 d0 = *(const f32x4 *)(s_dt + u0), d1 = *(const f32x4 *)(s_dt + u0 + 4);
-                    const f32x4 c0 = *(const f32x4 *)(s_cs + u0), c1 = *(const f32x4 *)(s_cs + u0 + 4);
-                    const f32x4 e0 = *(const f32x4 *)(s_ce + u0), e1 = *(const f32x4 *)(s_ce + u0 + 4);
+        for (int j = 0; j < YT; ++j) {
+            const int pb = pb0 + j;
+            f32x16 yb = f32x16{};
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float cbv = (float)cb8[j];
-                        const float dtu = j < 4 ? d0[j] : d1[j - 4];
-                        const float csu = j < 4 ? c0[j] : c1[j - 4];
-                        const float ceu = j < 4 ? e0[j] : e1[j - 4];
-                        // the decay exponent of the right direction is the non-positive one
-                        const float m = cbv * dtu * ex2(fminf(cs_t - csu, ceu - ce_t));
-                        mf[j] = (_Float16)(u0 + j == mrow ? 2.f * cbv * dt_t + twoD : m);
-                    }
-                } else if (U < mtb) {
-                    const f16x8 g8 = *(const f16x8 *)(s_gl + u0);
-                    mf = cb8 * (g8 * (_Float16)ex2(cs_t - s_cs[32 * U + 31]));
-                } else {
-                    const f16x8 g8 = *(const f16x8 *)(s_gu + u0);
-                    mf = cb8 * (g8 * (_Float16)ex2(s_ce[32 * U] - ce_t));
-                }
-                *(f16x8 *)(mrw + 32 * U) = mf;
+            for (int kb = 0; kb < KS; ++kb)
+                yb = mfma(frag_rm(hfl, SS, 32 * pb, 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) yacc[j][e] += ef * yb[e];
+            yb = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < KS; ++kb)
+                yb = mfma(frag_rm(hbl, SS, 32 * pb, 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb);
+            // Y = acc + eb * yb into ybuf (lane: token t_tok, 4 consecutive p per group)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                bf16x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(yacc[j][4 * g4 + e] + eb * yb[4 * g4 + e]);
+                *(bf16x4 *)&ybuf[t_tok * LY + 32 * pb + 8 * g4 + 4 * half] = v4;
             }
         }
-        __syncthreads();  // M complete
-
-        // ---- use ----
-        fetch_group(cn);
-        f32x16 yacc = f32x16{}, yb = f32x16{};
-        // intra-chunk term X^T M^T (fp16 MFMA)
-#pragma unroll
-        for (int kb = 0; kb < Q / 16; ++kb)
-            yacc = mfma16(__builtin_bit_cast(f16x8, frag_tr((const __bf16 *)xn, LX, 16 * kb, 32 * pb)),
-                          *(const f16x8 *)(mt + t_tok * LM + 16 * kb + 8 * half), yacc);
-        // forward inter-chunk term: ef * (Hf C^T)
-#pragma unroll
-        for (int kb = 0; kb < S / 16; ++kb)
-            yb = mfma(frag_rm(hfl, SS, 32 * pb, 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb);
-        {
-            const float ef = ex2(s_cs[t_tok]);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) yacc[j] += ef * yb[j];
+        load_hinb();
+        fetch_group(cn, 0);
+        if (row_thread) {
+            int pt = tid;
+            pin(pt);
+            s_rowy[pt] = rowc;
         }
-        yb = f32x16{};
-        // backward inter-chunk term: eb * (Hb C^T)
-#pragma unroll
-        for (int kb = 0; kb < S / 16; ++kb)
-            yb = mfma(frag_rm(hbl, SS, 32 * pb, 16 * kb), __builtin_bit_cast(bf16x8, cfr[kb]), yb);
-        const float eb = ex2(tot_c * LOG2E - s_ce[t_tok]);
-        // Y = acc + eb * yb into ybuf (lane: token t_tok, 4 consecutive p per group)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            bf16x4 v4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(yacc[4 * g4 + j] + eb * yb[4 * g4 + j]);
-            *(bf16x4 *)&ybuf[t_tok * LY + 32 * pb + 8 * g4 + 4 * half] = v4;
-        }
-        if (row_thread) s_rowy[tid] = rowc;
         __syncthreads();  // ybuf complete; this chunk's other LDS reads are done
 
         // ---- store, then stage the next chunk ----
@@ -877,7 +904,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
     int nseg, segch, nsegT;
-    size_t perm, dtT, csT, cb, b16, cfrag, hbl, delta, segF, segB, segA, hinF, hinB, ytrash, rx, rB, rdt, rdtT, rcsT,
+    size_t perm, dtT, csT, cb, b16, cfrag, bfrag, hbl, delta, segF, segB, segA, hinF, hinB, ytrash, rx, rB, rdt, rdtT, rcsT,
         total;
 };
 
@@ -886,8 +913,8 @@ Plan make_plan(const SsdProblem &p)
     Plan pl{};
     const size_t B = p.batch, Hs = p.nheads, S = p.d_state, Q = p.chunk, PS = (size_t)P * S;
     const size_t Lpad = (size_t)p.nch * Q;
-    // About five workgroups per CU over the whole launch.
-    int want = (int)((1280 + B * Hs - 1) / (B * Hs));
+    // About five rounds of the output sweep's resident workgroups (two per CU) over the whole launch.
+    int want = (int)((2560 + B * Hs - 1) / (B * Hs));
     if (want < 1) want = 1;
     if (want > p.nch) want = p.nch;
     pl.segch = (p.nch + want - 1) / want;
@@ -901,6 +928,7 @@ Plan make_plan(const SsdProblem &p)
     pl.cb = take(B * p.ngroups * p.nch * Q * Q * 2);
     pl.b16 = take(B * p.ngroups * p.nch * Q * S * 2);
     pl.cfrag = take(B * p.ngroups * p.nch * Q * S * 2);
+    pl.bfrag = take(B * p.ngroups * p.nch * Q * S * 2);
     pl.hbl = take(B * Hs * p.nch * PS * 2);
     pl.delta = take(B * Hs * p.nch * 4);
     pl.segF = take(B * Hs * pl.nsegT * PS * 4);
@@ -932,6 +960,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, 
     float *dtT = (float *)(w + pl.dtT), *csT = (float *)(w + pl.csT);
     _Float16 *cb = (_Float16 *)(w + pl.cb), *b16 = (_Float16 *)(w + pl.b16);
     __bf16 *cfrag = (__bf16 *)(w + pl.cfrag);
+    _Float16 *bfrag = (_Float16 *)(w + pl.bfrag);
     __bf16 *hbl = (__bf16 *)(w + pl.hbl);
     float *delta = (float *)(w + pl.delta), *segF = (float *)(w + pl.segF), *segB = (float *)(w + pl.segB);
     float *segA = (float *)(w + pl.segA), *hinF = (float *)(w + pl.hinF);
@@ -990,7 +1019,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, 
     }
     {
         timing::Scope ts_(K_SSD_CB, st);
-        k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, b16, cfrag, G, N);
+        k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, b16, cfrag, bfrag, G, N);
     }
     const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
     {
@@ -1009,7 +1038,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, 
     }
     {
         timing::Scope ts_(K_SSD_OUT, st);
-        k_out<S, Q><<<grid_of(items), Q * 4, 0, st>>>(x, b16, cfrag, cb, perm, dtT, csT, a.a, a.d, hbl, delta, hinF,
+        k_out<S, Q><<<grid_of(items), NT, 0, st>>>(x, bfrag, cfrag, cb, perm, dtT, csT, a.a, a.d, hbl, delta, hinF,
                                                    hinB, (__bf16 *)a.y, (__bf16 *)(w + pl.ytrash), Hs, G, N, Lpad,
                                                    p.nch, pl.segch, pl.nseg, (uint32_t)items);
     }
