@@ -2,8 +2,8 @@
 //
 // Same chunked (state space duality) evaluation as the portable path, with
 // the chunk states kept on chip. The sequence of each head is cut into
-// segments of whole chunks; a workgroup of Q/16 waves (two per SIMD at
-// Q = 128) owns one (head, segment):
+// segments of whole chunks; a workgroup of four waves (two workgroups per CU)
+// owns one (head, segment) in the two sweeps:
 //
 //  1. states   sweeps its segment right to left, carrying the backward state
 //              G in MFMA accumulators. Before adding chunk c it stores G (the
@@ -13,7 +13,8 @@
 //              The review tokens form one extra segment whose G and F are the
 //              initial states of the two directions.
 //  2. seg pass turns summaries into the true states at every segment border.
-//  3. cb       C_t . B_u (fp16) for every chunk (shared by all heads of a group).
+//  3. cb       per chunk and group (shared by its heads): C_t . B_u (fp16), and
+//              B^T, C and CB in MFMA operand order (used by 1 and 4).
 //  4. out      sweeps its segment left to right carrying the forward state Hf
 //              and computes, per chunk,
 //                 Y^T = X^T M^T + ef * (Hf C^T) + eb * (Hb C^T)
@@ -26,17 +27,19 @@
 //              mantissa bits than bf16.
 //              Then Hf = exp(tot) Hf + sum_u exp(tot - cs_u) dt_u x_u B_u^T.
 //
-// Data layout on chip: x and B chunks are staged in LDS in their natural
-// row-major layout (token rows) with plain 16-byte copies; the operands of the
-// contractions over tokens are read with the gfx950 LDS transpose read
-// (ds_read_b64_tr_b16), which hands each lane 4 consecutive rows of one
-// column. C rows, CB rows and the stored states are contiguous along their
-// contraction axis and are used as MFMA fragments directly.
+// Data layout: operands with one consumer wave (B^T of a state block, C and CB
+// of a token block) are stored per chunk in MFMA operand order, 1 KB per
+// k-block, and loaded straight into registers (one contiguous load per wave).
+// x, whose operands every wave reads, and the two states of the output sweep
+// are staged in LDS in row-major layout; x operands of the contractions over
+// tokens are read with the gfx950 LDS transpose read (ds_read_b64_tr_b16),
+// which hands each lane 4 consecutive rows of one column.
 //
-// Decay weights of M: inside the 32x32 diagonal block of a lane's token block
-// each weight is one exp2; in the blocks below (above) it, exp(cs_t - cs_u)
-// (exp(ce_u - ce_t)) is split at the block edge into a per-lane factor and a
-// per-token factor, both <= 1, so no exponent is evaluated per element.
+// Decay weights of M: each lane builds its M^T operand (its token's row, 8
+// consecutive u) in registers from its CB piece. Inside the 32x32 diagonal
+// block each weight is one exp2; in the blocks below (above) it, exp(cs_t -
+// cs_u) (exp(ce_u - ce_t)) is split at the block edge into a per-lane factor
+// and a per-token factor, both <= 1, so no exponent is evaluated per element.
 //
 // Scan order: a table of the RMS permutation (scan position -> canonical
 // token) is built once per call; every gather reads it instead of dividing.
@@ -243,27 +246,22 @@ __global__ __launch_bounds__(256) void k_perm(uint32_t *__restrict__ perm, uint3
 }
 
 // ---------------------------------------------------------------------------
-// 1. Right-to-left segment sweep: stored backward chunk states + summaries.
-// grid = 8 * ceil(batch * nseg * nheads / 8); item = (b * nseg + seg) * nheads + h.
-// MAIN: the main sequence (x rows through perm, B from the fp16 scan-order copy; stores the per-chunk
-// states); else the review sequence (rows in order, B pooled bf16; summaries only).
+// 1a. Right-to-left sweep of the review sequence (pooled rows in order, B pooled bf16): segment
+// summaries only. grid = 8 * ceil(batch * nheads / 8); one segment per head.
 // Each wave owns (s-block, p-block) tile pairs: the backward state G^T and the forward sum F^T of the
 // same tile share both operand tiles, B^T and x (fp16); the per-token weights of the two sums,
 // dt exp(ce) and dt exp(tot - cs + logD), are applied to the x operand in registers (packed fp16).
-// The x rows and per-token values of the chunk two to the left (and B of the next one) are loaded every
-// step (clamped at the segment start), and the per-step stores are made by every wave, so the
-// compiler's memory waits are not widened by paths that skip them.
+// The x and B rows and per-token values of the chunk two to the left are loaded every step (clamped at
+// the segment start), so the compiler's memory waits are not widened by paths that skip them.
 // ---------------------------------------------------------------------------
-template <int S, int Q, bool MAIN>
-__global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
-                                                  const _Float16 *__restrict__ b16,
-                                                  const uint32_t *__restrict__ perm, const float *__restrict__ dtT,
-                                                  const float *__restrict__ csT, const float *__restrict__ A,
-                                                  __bf16 *__restrict__ hb_local, float *__restrict__ delta,
-                                                  float *__restrict__ segF, float *__restrict__ segB,
-                                                  float *__restrict__ segA, int nheads, int G, uint32_t L,
-                                                  uint32_t Lpad, int nch, int segch, int nseg, int seg_base,
-                                                  int nseg_total, uint32_t total_items)
+template <int S, int Q>
+__global__ __launch_bounds__(Q * 4) void k_states_review(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
+                                                         const float *__restrict__ dtT, const float *__restrict__ csT,
+                                                         const float *__restrict__ A, float *__restrict__ segF,
+                                                         float *__restrict__ segB, float *__restrict__ segA,
+                                                         int nheads, int G, uint32_t L, uint32_t Lpad, int nch,
+                                                         int segch, int nseg, int seg_base, int nseg_total,
+                                                         uint32_t total_items)
 {
     constexpr int NT = Q * 4, NW = Q / 16;          // Q/16 waves, two per SIMD at Q = 128
     constexpr int LX = P + XPAD, LB = S + XPAD;
@@ -294,54 +292,35 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
     const float a = A[h];
     const size_t bh = (size_t)b * nheads + h;
     const size_t drow = bh * Lpad;
-    const size_t gch = ((size_t)b * G + g) * nch;
-    // x rows and per-token values are fetched two chunks ahead into two alternating
-    // register stages (their HBM latency exceeds a chunk's work). B of the main pass
-    // (contiguous fp16 rows of group data, L2-resident) comes one chunk ahead; the
-    // review pass gathers B with the chunk's row table, so it rides in the stage.
+    // x and B rows and per-token values are fetched two chunks ahead into two alternating register
+    // stages (their latency exceeds a chunk's work).
     struct Stage {
         Rows<Q, P, NT> xr;
-        u32x4 bq[BPER];  // review pass: B pieces k = tid + NT it (row k / (S / 8), 8 columns at 8 (k % (S / 8)))
+        u32x4 bq[BPER];  // B pieces k = tid + NT it (row k / (S / 8), 8 columns at 8 (k % (S / 8)))
         float tok_d, tok_c, tot;
     };
     Stage stA, stB;
-    u32x4 bm[BPER];       // main pass: B of the chunk after the current one, same pieces
     uint32_t pnext = 0u;  // row-table entry of the chunk after the one fetched last
     bool pvalid = false;
     auto fetch = [&](Stage &stg, int c) {
-        // The row-table load first: the compiler may move its use above the next barrier, and a wait for
-        // it then covers only older loads.
         const int tq = tid & (Q - 1);
         const uint32_t i = (uint32_t)(c - 1) * Q + tq;
         pvalid = c > c_lo && i < L;
-        if constexpr (MAIN)
-            pnext = perm[pvalid ? i : 0u];  // selected against pvalid where it is stored
-        else
-            pnext = i;
+        pnext = i;
         stg.xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
-        if constexpr (!MAIN) {
-            Rows<Q, S, NT> br;
-            br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * L);
+        Rows<Q, S, NT> br;
+        br.load(Bm + (size_t)g * S, (size_t)G * S, s_row, (size_t)b * L);
 #pragma unroll
-            for (int it = 0; it < BPER; ++it) stg.bq[it] = br.r[it];
-        }
+        for (int it = 0; it < BPER; ++it) stg.bq[it] = br.r[it];
         const size_t crow0 = drow + (size_t)c * Q;
         stg.tok_d = dtT[crow0 + tq];
         stg.tok_c = csT[crow0 + tq];
         stg.tot = csT[crow0 + Q - 1];
     };
-    auto fetch_b = [&](int c) {
-        if constexpr (MAIN) {
-            const _Float16 *src = b16 + (gch + c) * (size_t)(Q * S);
-#pragma unroll
-            for (int it = 0; it < BPER; ++it) bm[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
-        }
-    };
     // Prologue: rows and data of the rightmost chunk, then the rows and x of the one before.
-    if (row_thread) s_row[tid] = seq_row(MAIN ? perm : nullptr, (uint32_t)(c_hi - 1) * Q + tid, L);
+    if (row_thread) s_row[tid] = seq_row(nullptr, (uint32_t)(c_hi - 1) * Q + tid, L);
     __syncthreads();
     fetch(stA, c_hi - 1);
-    fetch_b(c_hi - 1);
     __syncthreads();  // every lane has read the rows of chunk c_hi - 1
     s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
     __syncthreads();
@@ -349,36 +328,12 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
     float logD = 0.f;  // sum of dt*A over the chunks right of the current one
 
     auto step = [&](Stage &cur, int c) {
-        if constexpr (MAIN) {
-            // Backward state entering chunk c from the right, in accumulator order (see hb_piece).
-            if (active) {
-                __bf16 *dst = hb_local + (bh * nch + c) * (size_t)(P * S);
-#pragma unroll
-                for (int i = 0; i < TP; ++i) {
-                    const int j = wave * TP + i;
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        bf16x8 v8;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) v8[e] = (__bf16)accG[i][8 * q + e];
-                        *(bf16x8 *)(dst + ((j * 2 + q) * 64 + lane) * 8) = v8;
-                    }
-                }
-            }
-            delta[bh * nch + c] = ex2(logD * LOG2E);  // every thread writes the same value
-        }
-
         __syncthreads();  // previous chunk's MFMA reads of LDS and the row-table reads are done
         // The staged values are used from here on (their loads had two steps to complete).
 #pragma unroll
         for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) pin(cur.xr.r[it]);
 #pragma unroll
-        for (int it = 0; it < BPER; ++it) {
-            if constexpr (MAIN)
-                pin(bm[it]);
-            else
-                pin(cur.bq[it]);
-        }
+        for (int it = 0; it < BPER; ++it) pin(cur.bq[it]);
         pin(cur.tok_d);
         pin(cur.tok_c);
         pin(cur.tot);
@@ -388,14 +343,9 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
 #pragma unroll
         for (int it = 0; it < BPER; ++it) {
             const int k = tid + NT * it;
-            u32x4 v;
-            if constexpr (MAIN) {
-                v = bm[it];
-            } else {
-                v = cur.bq[it];
+            u32x4 v = cur.bq[it];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = pack2h(lo_f(v[e]), hi_f(v[e]));
-            }
+            for (int e = 0; e < 4; ++e) v[e] = pack2h(lo_f(v[e]), hi_f(v[e]));
             *(u32x4 *)&bn[(k / (S / 8)) * LB + 8 * (k % (S / 8))] = v;
         }
         if (row_thread) {
@@ -408,8 +358,6 @@ __global__ __launch_bounds__(Q * 4) void k_states(const __bf16 *__restrict__ x, 
         s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
         __syncthreads();
 
-        // B (needed next step) before x (needed in two): waits complete in issue order.
-        fetch_b(max(c - 1, c_lo));
         fetch(cur, max(c - 2, c_lo));  // near the segment start: issued, unused
         if (active) {
             const float dec = ex2(tot_c * LOG2E);
@@ -488,15 +436,14 @@ __global__ __launch_bounds__(256) void k_seg_pass(const float *__restrict__ segF
 //    (see op_piece), so that each wave reads each operand with one contiguous 1 KB load per k-block:
 //    cb    CB[t][u] = C_t . B_u (fp16), token block tb = t / 32, k-blocks over u;
 //    cfrag C rows (bf16), token block tb, k-blocks over the state index s;
-//    bfrag B^T rows (fp16), state block sb = s / 32, k-blocks over u;
-//    b16   and, for the state sweep, the chunk's B rows in scan order as fp16 ([Q][S]).
+//    bfrag B^T rows (fp16), state block sb = s / 32, k-blocks over u.
 // CB is computed as CB^T = B C^T so each lane holds 4 consecutive u of one t. B^T goes through LDS:
 // the B rows are written there and read back with the transposing LDS read.
 // ---------------------------------------------------------------------------
 template <int S, int Q>
 __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
                                            const uint32_t *__restrict__ perm, _Float16 *__restrict__ cb,
-                                           _Float16 *__restrict__ b16, __bf16 *__restrict__ cfrag,
+                                           __bf16 *__restrict__ cfrag,
                                            _Float16 *__restrict__ bfrag, int G, uint32_t L)
 {
     constexpr int LB = S + XPAD;
@@ -537,11 +484,9 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
             *(f16x4 *)(out + op_piece(tb, 2 * ub + (g4 >> 1), KU, col + 32 * (g4 & 1)) + 4 * half) = v4;
         }
     }
-    // B rows as fp16 (exact for bf16 values in fp16's normal range), to global and LDS; C rows in
-    // operand order.
+    // B rows as fp16 (exact for bf16 values in fp16's normal range) to LDS; C rows in operand order.
     constexpr int PIECES = Q * S / 8, PER = PIECES / NT;
     static_assert(PIECES % NT == 0, "pieces must split evenly");
-    _Float16 *bo = b16 + chunk * (size_t)(Q * S);
     __bf16 *co = cfrag + chunk * (size_t)(Q * S);
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
@@ -553,7 +498,6 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = i < L ? pack2h(lo_f(v[e]), hi_f(v[e])) : 0u;
-            *(u32x4 *)(bo + (size_t)row * S + 8 * c8) = o;
             *(u32x4 *)(bt + row * LB + 8 * c8) = o;
         }
         {
@@ -575,6 +519,171 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
         const int sb = blk / KU, kb = blk % KU;
         *(bf16x8 *)(bfo + op_piece(sb, kb, KU, lane)) = frag_tr((const __bf16 *)bt, LB, 16 * kb, 32 * sb);
     }
+}
+
+// ---------------------------------------------------------------------------
+// 1b. Right-to-left sweep of the main sequence: the backward state entering every chunk from the right
+// (stored as bf16 for the output sweep) and the segment summaries G, F and sum(dt A).
+// grid = 8 * ceil(batch * nseg * nheads / 8); item = (b * nseg + seg) * nheads + h.
+// Workgroups of four waves, two per CU. B^T comes from L2 in MFMA operand order (bfrag, one
+// chunk ahead in two alternating register sets) and only x passes through LDS. Wave w owns the G^T
+// and F^T tiles of state block s-block(w) (both p-blocks at S = 128); the per-token weights of the two
+// sums are applied to the B^T operand, so one scaled operand serves both p-blocks. x rows and
+// per-token values come two chunks ahead through two register stages.
+// ---------------------------------------------------------------------------
+template <int S, int Q>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, const uint32_t *__restrict__ perm,
+               const float *__restrict__ dtT, const float *__restrict__ csT, const float *__restrict__ A,
+               __bf16 *__restrict__ hb_local, float *__restrict__ delta, float *__restrict__ segF,
+               float *__restrict__ segB, float *__restrict__ segA, int nheads, int G, uint32_t L, uint32_t Lpad,
+               int nch, int segch, int nseg, int nseg_total, uint32_t total_items)
+{
+    constexpr int LX = P + XPAD;
+    constexpr int KU = Q / 16;  // k-blocks over the chunk's tokens
+    constexpr int TT = S / 64;  // G^T (and F^T) tiles per wave: state block sb, p-blocks pb0 ..
+    __shared__ _Float16 xn[Q * LX];  // x (fp16)
+    __shared__ __attribute__((aligned(16))) _Float16 s_wb[Q], s_wf[Q];  // per-token weights
+    __shared__ uint32_t s_row[Q];    // global rows of the next chunk to fetch
+
+    const uint32_t item = xcd_item();
+    if (item >= total_items) return;
+    const int h = item % nheads;
+    const uint32_t rest = item / nheads;
+    const int seg = rest % nseg, b = rest / nseg;
+    const int g = h / (nheads / G);
+    const int c_lo = seg * segch, c_hi = min(nch, c_lo + segch);
+
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool row_thread = tid < Q;
+    const int sb = (wave * TT) >> 1, pb0 = (wave * TT) & 1;
+    f32x16 accG[TT], accF[TT];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) accG[i] = accF[i] = f32x16{};
+
+    const float a = A[h];
+    const size_t bh = (size_t)b * nheads + h;
+    const size_t drow = bh * Lpad;
+    const size_t gch = ((size_t)b * G + g) * nch;
+    struct Stage {
+        Rows<Q, P, NT> xr;
+        float tok_d, tok_c, tot;
+    };
+    Stage stA, stB;
+    u32x4 bA[KU], bB[KU];  // B^T operands of the chunk being summed and of the next one
+    uint32_t pnext = 0u;   // row-table entry of the chunk after the one fetched last
+    bool pvalid = false;
+    auto fetch = [&](Stage &stg, int c) {
+        // The row-table load first: a wait for it then covers only older loads.
+        const int tq = tid & (Q - 1);
+        const uint32_t i = (uint32_t)(c - 1) * Q + tq;
+        pvalid = c > c_lo && i < L;
+        pnext = perm[pvalid ? i : 0u];  // selected against pvalid where it is stored
+        stg.xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
+        const size_t crow0 = drow + (size_t)c * Q;
+        stg.tok_d = dtT[crow0 + tq];
+        stg.tok_c = csT[crow0 + tq];
+        stg.tot = csT[crow0 + Q - 1];
+    };
+    auto fetch_b = [&](u32x4 (&bq)[KU], int c) {
+        const _Float16 *src = bfrag + (gch + c) * (size_t)(Q * S) + op_piece(sb, 0, KU, lane);
+#pragma unroll
+        for (int kb = 0; kb < KU; ++kb) bq[kb] = *(const u32x4 *)(src + 512 * kb);
+    };
+    // Prologue: rows and data of the rightmost chunk, then the rows and x of the one before.
+    if (row_thread) s_row[tid] = seq_row(perm, (uint32_t)(c_hi - 1) * Q + tid, L);
+    __syncthreads();
+    fetch(stA, c_hi - 1);
+    fetch_b(bA, c_hi - 1);
+    __syncthreads();  // every lane has read the rows of chunk c_hi - 1
+    s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
+    __syncthreads();
+    fetch(stB, max(c_hi - 2, c_lo));  // a one-chunk segment: issued, unused
+    float logD = 0.f;  // sum of dt*A over the chunks right of the current one
+
+    auto step = [&](Stage &cur, u32x4 (&bc)[KU], u32x4 (&bn)[KU], int c) {
+        {
+            // Backward state entering chunk c from the right, in accumulator order (see hb_piece).
+            __bf16 *dst = hb_local + (bh * nch + c) * (size_t)(P * S);
+#pragma unroll
+            for (int i = 0; i < TT; ++i) {
+                const int j = wave * TT + i;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    bf16x8 v8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v8[e] = (__bf16)accG[i][8 * q + e];
+                    *(bf16x8 *)(dst + ((j * 2 + q) * 64 + lane) * 8) = v8;
+                }
+            }
+            delta[bh * nch + c] = ex2(logD * LOG2E);  // every thread writes the same value
+        }
+
+        __syncthreads();  // previous chunk's reads of xn and the row-table reads are done
+        // The staged values are used from here on (their loads had two steps to complete).
+#pragma unroll
+        for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) pin(cur.xr.r[it]);
+        pin(cur.tok_d);
+        pin(cur.tok_c);
+        pin(cur.tot);
+        pin(pnext);
+        const float tot_c = cur.tot;
+        cur.xr.template store_f16<LX>((__bf16 *)xn);
+        if (row_thread) {
+            const float d = cur.tok_d, cs = cur.tok_c;
+            s_wb[tid] = (_Float16)(d * ex2((cs - d * a) * LOG2E));
+            s_wf[tid] = (_Float16)(d * ex2((tot_c - cs + logD) * LOG2E));
+        }
+        // Rows of chunk c - 2. Every thread stores its (identical) entry: a use on all paths keeps
+        // the row load where it is issued.
+        s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
+        __syncthreads();
+
+        // B (needed next step) before x (needed in two): waits complete in issue order.
+        fetch_b(bn, max(c - 1, c_lo));
+        fetch(cur, max(c - 2, c_lo));  // near the segment start: issued, unused
+        const float dec = ex2(tot_c * LOG2E);
+#pragma unroll
+        for (int i = 0; i < TT; ++i) accG[i] *= dec;
+#pragma unroll
+        for (int kb = 0; kb < KU; ++kb) {
+            const f16x8 wb8 = *(const f16x8 *)(s_wb + 16 * kb + 8 * half);
+            const f16x8 wf8 = *(const f16x8 *)(s_wf + 16 * kb + 8 * half);
+            const f16x8 af = __builtin_bit_cast(f16x8, bc[kb]);
+            const f16x8 afb = af * wb8, aff = af * wf8;
+#pragma unroll
+            for (int i = 0; i < TT; ++i) {
+                const f16x8 xv = __builtin_bit_cast(f16x8, frag_tr((const __bf16 *)xn, LX, 16 * kb, 32 * (pb0 + i)));
+                accG[i] = mfma16(afb, xv, accG[i]);
+                accF[i] = mfma16(aff, xv, accF[i]);
+            }
+        }
+        logD += tot_c;
+    };
+    int c = c_hi - 1;
+    for (; c - 1 >= c_lo; c -= 2) {
+        step(stA, bA, bB, c);
+        step(stB, bB, bA, c - 1);
+    }
+    if (c >= c_lo) step(stA, bA, bB, c);
+
+    // Segment summaries: G (backward state entering the segment from its right end, from zero) and F.
+    {
+        float *dG = segB + (bh * nseg_total + seg) * (size_t)(P * S);
+        float *dF = segF + (bh * nseg_total + seg) * (size_t)(P * S);
+#pragma unroll
+        for (int i = 0; i < TT; ++i) {
+            const int pb = pb0 + i;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const size_t o = (size_t)(32 * pb + col) * S + 32 * sb + 8 * g4 + 4 * half;
+                *(f32x4 *)(dG + o) = f32x4{accG[i][4 * g4], accG[i][4 * g4 + 1], accG[i][4 * g4 + 2], accG[i][4 * g4 + 3]};
+                *(f32x4 *)(dF + o) = f32x4{accF[i][4 * g4], accF[i][4 * g4 + 1], accF[i][4 * g4 + 2], accF[i][4 * g4 + 3]};
+            }
+        }
+    }
+    if (tid == 0) segA[bh * nseg_total + seg] = logD;
 }
 
 // ---------------------------------------------------------------------------
@@ -811,6 +920,12 @@ void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, con
 #pragma unroll
             for (int i = 0; i < HT; ++i) hacc[i] *= dec;
         }
+        // Per-lane factor of each off-diagonal 32-token block U of M, both <= 1: below the diagonal
+        // block exp(cs_t - cs at the end of U), above it exp(ce at the start of U - ce_t).
+        _Float16 fac[Q / 32];
+#pragma unroll
+        for (int U = 0; U < Q / 32; ++U)
+            fac[U] = (_Float16)ex2(U < tb ? cs_t - s_cs[32 * U + 31] : s_ce[32 * U] - ce_t);
         f32x16 yacc[YT];
 #pragma unroll
         for (int j = 0; j < YT; ++j) yacc[j] = f32x16{};
@@ -844,16 +959,13 @@ void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, con
                     const float m = cbv * dtu * ex2(fminf(cs_t - csu, ceu - ce_t));
                     mf[j] = (_Float16)(16 * (kb & 1) + j == jd ? 2.f * cbv * dt_t + twoD : m);
                 }
-            } else if (U < tb) {
-                const f16x8 g8 = *(const f16x8 *)(s_gl + u0);
-                mf = cb8 * (g8 * (_Float16)ex2(cs_t - s_cs[32 * U + 31]));
             } else {
-                const f16x8 g8 = *(const f16x8 *)(s_gu + u0);
-                mf = cb8 * (g8 * (_Float16)ex2(s_ce[32 * U] - ce_t));
+                const f16x8 g8 = *(const f16x8 *)((U < tb ? s_gl : s_gu) + u0);
+                mf = cb8 * (g8 * fac[U]);
             }
 #pragma unroll
             for (int j = 0; j < YT; ++j) yacc[j] = mfma16(xa[pb0 + j - px0], mf, yacc[j]);
-            // state update: Hf^T += B^T (w x)^T
+            // state update: Hf^T += (B^T w) x^T, the token weights applied along the contraction
             const f16x8 w8 = *(const f16x8 *)(s_w + u0);
             const f16x8 af = __builtin_bit_cast(f16x8, bfr[kb]);
 #pragma unroll
@@ -904,7 +1016,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
     int nseg, segch, nsegT;
-    size_t perm, dtT, csT, cb, b16, cfrag, bfrag, hbl, delta, segF, segB, segA, hinF, hinB, ytrash, rx, rB, rdt, rdtT, rcsT,
+    size_t perm, dtT, csT, cb, cfrag, bfrag, hbl, delta, segF, segB, segA, hinF, hinB, ytrash, rx, rB, rdt, rdtT, rcsT,
         total;
 };
 
@@ -926,7 +1038,6 @@ Plan make_plan(const SsdProblem &p)
     pl.dtT = take(B * Hs * Lpad * 4);
     pl.csT = take(B * Hs * Lpad * 4);
     pl.cb = take(B * p.ngroups * p.nch * Q * Q * 2);
-    pl.b16 = take(B * p.ngroups * p.nch * Q * S * 2);
     pl.cfrag = take(B * p.ngroups * p.nch * Q * S * 2);
     pl.bfrag = take(B * p.ngroups * p.nch * Q * S * 2);
     pl.hbl = take(B * Hs * p.nch * PS * 2);
@@ -958,7 +1069,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, 
     char *w = (char *)ws;
     uint32_t *perm = (uint32_t *)(w + pl.perm);
     float *dtT = (float *)(w + pl.dtT), *csT = (float *)(w + pl.csT);
-    _Float16 *cb = (_Float16 *)(w + pl.cb), *b16 = (_Float16 *)(w + pl.b16);
+    _Float16 *cb = (_Float16 *)(w + pl.cb);
     __bf16 *cfrag = (__bf16 *)(w + pl.cfrag);
     _Float16 *bfrag = (_Float16 *)(w + pl.bfrag);
     __bf16 *hbl = (__bf16 *)(w + pl.hbl);
@@ -1002,10 +1113,9 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, 
         const uint64_t items = (uint64_t)Bn * Hs;
         {
             timing::Scope ts_(K_SSD_STATES, st);
-            k_states<S, Q, false><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, nullptr, nullptr,
-                                                                 rdtT, rcsT,
-                                                          a.a, nullptr, nullptr, segF, segB, segA, Hs, G, R, Rpad,
-                                                          p.nchR, p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)items);
+            k_states_review<S, Q><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, rdtT, rcsT,
+                                                                 a.a, segF, segB, segA, Hs, G, R, Rpad, p.nchR,
+                                                                 p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)items);
         }
     }
     {
@@ -1019,13 +1129,13 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, 
     }
     {
         timing::Scope ts_(K_SSD_CB, st);
-        k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, b16, cfrag, bfrag, G, N);
+        k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, cfrag, bfrag, G, N);
     }
     const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
     {
         timing::Scope ts_(K_SSD_STATES, st);
-        k_states<S, Q, true><<<grid_of(items), Q * 4, 0, st>>>(x, Bm, b16, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs, G,
-                                                      N, Lpad, p.nch, pl.segch, pl.nseg, 0, pl.nsegT, (uint32_t)items);
+        k_states<S, Q><<<grid_of(items), NT, 0, st>>>(x, bfrag, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs,
+                                                      G, N, Lpad, p.nch, pl.segch, pl.nseg, pl.nsegT, (uint32_t)items);
     }
     {
         timing::Scope ts_(K_SSD_SEG_PASS, st);
