@@ -818,6 +818,7 @@ void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, con
     auto stage = [&]() {
         int pt = tid;
         pin(pt);
+        pt &= NT - 1;  // lets the compiler fold the per-iteration offsets into immediates
         const int pcol = pt & 31, phalf = (pt >> 5) & 1;
         xr.template store_f16_at<LX>((__bf16 *)xn, pt);
 #pragma unroll
@@ -880,6 +881,7 @@ void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, con
     auto store_y = [&]() {
         int pt = tid;
         pin(pt);
+        pt &= NT - 1;  // lets the compiler fold the per-iteration offsets into immediates
 #pragma unroll
         for (int it = 0; it < Q * (P / 8) / NT; ++it) {
             const int k = pt + NT * it;
@@ -1002,7 +1004,7 @@ void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, con
         if (row_thread) {
             int pt = tid;
             pin(pt);
-            s_rowy[pt] = rowc;
+            s_rowy[pt & (NT - 1)] = rowc;
         }
         __syncthreads();  // ybuf complete; this chunk's other LDS reads are done
 
