@@ -29,16 +29,22 @@ __global__ __launch_bounds__(256) void k_prep_dt(const float *__restrict__ dt, c
                                                  uint32_t H, uint32_t W, const uint32_t *__restrict__ perm = nullptr)
 {
     __shared__ float sdt[kMaxQ][65];
+    __shared__ uint32_t srow[kMaxQ];
     const uint32_t c = blockIdx.x, b = blockIdx.z;
     const int h0 = blockIdx.y * 64;
+    // The chunk's rows first, so that the dt loads below depend on no other load and
+    // can all be in flight together.
+    for (int u = threadIdx.x; u < Q; u += 256) {
+        const uint32_t i = c * Q + u;
+        srow[u] = i < L ? (perm ? perm[i] : seq_row<PERM>(i, order, T, H, W)) : ~0u;
+    }
+    __syncthreads();
+#pragma unroll 8
     for (int k = threadIdx.x; k < Q * 64; k += 256) {
         const int u = k >> 6, hh = k & 63, h = h0 + hh;
-        const uint32_t i = c * Q + u;
+        const uint32_t row = srow[u];
         float v = 0.f;
-        if (i < L && h < nheads) {
-            const uint32_t row = perm ? perm[i] : seq_row<PERM>(i, order, T, H, W);
-            v = dt[((size_t)b * L + row) * nheads + h];
-        }
+        if (row != ~0u && h < nheads) v = dt[((size_t)b * L + row) * nheads + h];
         sdt[u][hh] = v;
     }
     __syncthreads();

@@ -419,12 +419,16 @@ __global__ __launch_bounds__(256) void k_seg_pass(const float *__restrict__ segF
     const float *F = segF + bh * nseg_total * PS + e;
     const float *Bk = segB + bh * nseg_total * PS + e;
     const float *sa = segA + bh * nseg_total;
+    // Unrolled so that the summary loads of several segments (independent of the carried
+    // state) are in flight together.
     float run = has_review ? F[(size_t)nseg * PS] : 0.f;
+#pragma unroll 8
     for (int j = 0; j < nseg; ++j) {
         hinF[(bh * nseg + j) * PS + e] = run;
         run = ex2(sa[j] * LOG2E) * run + F[(size_t)j * PS];
     }
     run = has_review ? Bk[(size_t)nseg * PS] : 0.f;
+#pragma unroll 8
     for (int j = nseg - 1; j >= 0; --j) {
         hinB[(bh * nseg + j) * PS + e] = (__bf16)run;
         run = ex2(sa[j] * LOG2E) * run + Bk[(size_t)j * PS];
@@ -432,48 +436,64 @@ __global__ __launch_bounds__(256) void k_seg_pass(const float *__restrict__ segF
 }
 
 // ---------------------------------------------------------------------------
-// 3. Per chunk and group (grid (nch, G, batch)), the output sweep's operands in MFMA operand order
-//    (see op_piece), so that each wave reads each operand with one contiguous 1 KB load per k-block:
+// 3. Per chunk and group (grid (nch, G, batch)), the sweeps' operands in MFMA operand order (see
+//    op_piece), so that each wave reads each operand with one contiguous 1 KB load per k-block:
 //    cb    CB[t][u] = C_t . B_u (fp16), token block tb = t / 32, k-blocks over u;
 //    cfrag C rows (bf16), token block tb, k-blocks over the state index s;
 //    bfrag B^T rows (fp16), state block sb = s / 32, k-blocks over u.
-// CB is computed as CB^T = B C^T so each lane holds 4 consecutive u of one t. B^T goes through LDS:
-// the B rows are written there and read back with the transposing LDS read.
+// The chunk's B and C rows are gathered once into LDS (B also as fp16 at the stride of the
+// transposing read); CB is computed as CB^T = B C^T so each lane holds 4 consecutive u of one t.
 // ---------------------------------------------------------------------------
 template <int S, int Q>
 __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
                                            const uint32_t *__restrict__ perm, _Float16 *__restrict__ cb,
-                                           __bf16 *__restrict__ cfrag,
-                                           _Float16 *__restrict__ bfrag, int G, uint32_t L)
+                                           __bf16 *__restrict__ cfrag, _Float16 *__restrict__ bfrag, int G, uint32_t L)
 {
-    constexpr int LB = S + XPAD;
-    __shared__ __attribute__((aligned(16))) _Float16 bt[Q * LB];
+    constexpr int LR = S + 8;     // row stride of the row-read tiles (conflict-free 16-byte reads)
+    constexpr int LT = S + XPAD;  // row stride of the fp16 B tile (conflict-free transposing reads)
+    __shared__ __attribute__((aligned(16))) __bf16 bs[Q * LR];
+    __shared__ __attribute__((aligned(16))) __bf16 cs[Q * LR];
+    __shared__ __attribute__((aligned(16))) _Float16 bt[Q * LT];
+    __shared__ uint32_t srow[Q];
     const uint32_t c = blockIdx.x;
     const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     constexpr int TB = Q / 32, KU = Q / 16, KS = S / 16;
-    constexpr int TILES = TB * TB / 4;  // per wave
     const size_t rs = (size_t)G * S;
     const size_t chunk = ((size_t)b * G + g) * gridDim.x + c;
+
+    for (int u = tid; u < Q; u += NT) srow[u] = seq_row(perm, c * Q + u, L);
+    __syncthreads();
+    // B and C rows, 16-byte pieces; a position past the end holds zeros.
+    constexpr int PER = Q * S / 8 / NT;
+    static_assert(Q * S / 8 % NT == 0, "pieces must split evenly");
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int k = tid + NT * it, row = k / (S / 8), c8 = k % (S / 8);
+        const uint32_t r = srow[row];
+        const size_t off = ((size_t)b * L + (r != ~0u ? r : 0u)) * rs + (size_t)g * S + 8 * c8;
+        u32x4 vb = *(const u32x4 *)(Bm + off), vc = *(const u32x4 *)(Cm + off);
+        if (r == ~0u) vb = vc = u32x4{0, 0, 0, 0};
+        *(u32x4 *)(bs + row * LR + 8 * c8) = vb;
+        *(u32x4 *)(cs + row * LR + 8 * c8) = vc;
+        u32x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = pack2h(lo_f(vb[e]), hi_f(vb[e]));
+        *(u32x4 *)(bt + row * LT + 8 * c8) = h;
+    }
+    __syncthreads();
+
     _Float16 *out = cb + chunk * (size_t)(Q * Q);
+    constexpr int TILES = TB * TB / 4;  // per wave
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
         const int ti = wave + 4 * k;
         const int ub = ti / TB, tb = ti % TB;
-        const uint32_t iu = c * Q + 32 * ub + col, itk = c * Q + 32 * tb + col;
-        const bool uok = iu < L, tok = itk < L;
-        const __bf16 *brow = Bm + ((size_t)b * L + (uok ? perm[iu] : 0u)) * rs + (size_t)g * S;
-        const __bf16 *crow = Cm + ((size_t)b * L + (tok ? perm[itk] : 0u)) * rs + (size_t)g * S;
         f32x16 acc = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < S / 16; ++kb) {
-            u32x4 av = *(const u32x4 *)(brow + 16 * kb + 8 * half);
-            u32x4 bv = *(const u32x4 *)(crow + 16 * kb + 8 * half);
-            av = uok ? av : u32x4{0, 0, 0, 0};
-            bv = tok ? bv : u32x4{0, 0, 0, 0};
-            acc = mfma(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc);
-        }
+        for (int kb = 0; kb < KS; ++kb)
+            acc = mfma(frag_rm(bs, LR, 32 * ub, 16 * kb), frag_rm(cs, LR, 32 * tb, 16 * kb), acc);
         // acc: rows u = 32 ub + 8 g4 + 4 half + j, column t = 32 tb + col. The 8-value piece holding
         // u = 32 ub + 8 g4 + 0..7 is k-block 2 ub + g4 / 2, lane col + 32 (g4 % 2).
 #pragma unroll
@@ -484,40 +504,19 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
             *(f16x4 *)(out + op_piece(tb, 2 * ub + (g4 >> 1), KU, col + 32 * (g4 & 1)) + 4 * half) = v4;
         }
     }
-    // B rows as fp16 (exact for bf16 values in fp16's normal range) to LDS; C rows in operand order.
-    constexpr int PIECES = Q * S / 8, PER = PIECES / NT;
-    static_assert(PIECES % NT == 0, "pieces must split evenly");
+    // C pieces: block (token block tb, k-block kb over s); B^T pieces: block (state block sb, k-block
+    // kb over u), lane l holding B[16 kb + 8 (l / 32) + 0..7][32 sb + l % 32].
     __bf16 *co = cfrag + chunk * (size_t)(Q * S);
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-        const int k = tid + NT * it;
-        {
-            const int row = k / (S / 8), c8 = k % (S / 8);
-            const uint32_t i = c * Q + row;
-            const u32x4 v = *(const u32x4 *)(Bm + ((size_t)b * L + (i < L ? perm[i] : 0u)) * rs + (size_t)g * S + 8 * c8);
-            u32x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = i < L ? pack2h(lo_f(v[e]), hi_f(v[e])) : 0u;
-            *(u32x4 *)(bt + row * LB + 8 * c8) = o;
-        }
-        {
-            const int l = k % 64, kb = (k / 64) % KS, tb = k / (64 * KS);
-            const uint32_t i = c * Q + 32 * tb + (l & 31);
-            const u32x4 v = *(const u32x4 *)(Cm + ((size_t)b * L + (i < L ? perm[i] : 0u)) * rs + (size_t)g * S +
-                                              16 * kb + 8 * (l >> 5));
-            *(u32x4 *)(co + 8 * (size_t)k) = i < L ? v : u32x4{0, 0, 0, 0};
-        }
-    }
-    __syncthreads();
-    // B^T pieces: block (state block sb, k-block kb) holds, for lane l, B[16 kb + 8 (l / 32) + 0..7][32 sb + l % 32].
     _Float16 *bfo = bfrag + chunk * (size_t)(Q * S);
-    constexpr int BLOCKS = (S / 32) * KU;
+    constexpr int BLOCKS = TB * KS;  // = (S / 32) * KU
     static_assert(BLOCKS % 4 == 0, "blocks must split evenly over the waves");
 #pragma unroll
     for (int k = 0; k < BLOCKS / 4; ++k) {
         const int blk = wave + 4 * k;
-        const int sb = blk / KU, kb = blk % KU;
-        *(bf16x8 *)(bfo + op_piece(sb, kb, KU, lane)) = frag_tr((const __bf16 *)bt, LB, 16 * kb, 32 * sb);
+        const int tb = blk / KS, kb = blk % KS;
+        *(bf16x8 *)(co + op_piece(tb, kb, KS, lane)) = frag_rm(cs, LR, 32 * tb, 16 * kb);
+        const int sb = blk / KU, kbu = blk % KU;
+        *(bf16x8 *)(bfo + op_piece(sb, kbu, KU, lane)) = frag_tr((const __bf16 *)bt, LT, 16 * kbu, 32 * sb);
     }
 }
 
