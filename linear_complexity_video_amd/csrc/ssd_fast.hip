@@ -165,6 +165,18 @@ struct Rows {
             r[it] = *(const u32x4 *)(base + (batch_rows + (row != ~0u ? row : 0u)) * row_stride + 8 * cc_of(it));
         }
     }
+    // load with streaming (non-temporal) loads: for rows read once per sweep, so that they do
+    // not push data that other workgroups reuse out of L2
+    __device__ __forceinline__ void load_nt(const __bf16 *base, size_t row_stride, const uint32_t *srow,
+                                            size_t batch_rows)
+    {
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const uint32_t row = srow[row_of(it)];
+            r[it] = __builtin_nontemporal_load(
+                (const u32x4 *)(base + (batch_rows + (row != ~0u ? row : 0u)) * row_stride + 8 * cc_of(it)));
+        }
+    }
     template <int LD>
     __device__ __forceinline__ void store(__bf16 *dst) const
     {
@@ -579,7 +591,7 @@ void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, 
         const uint32_t i = (uint32_t)(c - 1) * Q + tq;
         pvalid = c > c_lo && i < L;
         pnext = perm[pvalid ? i : 0u];  // selected against pvalid where it is stored
-        stg.xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
+        stg.xr.load_nt(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
         const size_t crow0 = drow + (size_t)c * Q;
         stg.tok_d = dtT[crow0 + tq];
         stg.tok_c = csT[crow0 + tq];
@@ -613,7 +625,7 @@ void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, 
                     bf16x8 v8;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v8[e] = (__bf16)accG[i][8 * q + e];
-                    *(bf16x8 *)(dst + ((j * 2 + q) * 64 + lane) * 8) = v8;
+                    __builtin_nontemporal_store(v8, (bf16x8 *)(dst + ((j * 2 + q) * 64 + lane) * 8));
                 }
             }
             delta[bh * nch + c] = ex2(logD * LOG2E);  // every thread writes the same value
@@ -794,10 +806,12 @@ void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, con
     uint32_t pnext = 0u;
     bool pvalid = false;
     auto fetch = [&](int c) {
-        xr.load(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * N);
+        // x rows and stored states are read once: streaming loads keep the group operands and
+        // border states that other workgroups reuse in L2
+        xr.load_nt(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * N);
         const __bf16 *src = hb_local + (bh * nch + c) * (size_t)PS;
 #pragma unroll
-        for (int it = 0; it < HBC; ++it) hbr[it] = *(const u32x4 *)(src + 8 * (tid + NT * it));
+        for (int it = 0; it < HBC; ++it) hbr[it] = __builtin_nontemporal_load((const u32x4 *)(src + 8 * (tid + NT * it)));
         // Every thread issues the same loads; the per-token values matter for tid < Q only.
         const int tq = tid & (Q - 1);
         const size_t crow0 = drow + (size_t)c * Q;
@@ -887,7 +901,7 @@ void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, con
             const int t = k / (P / 8), p8 = 8 * (k % (P / 8));
             const uint32_t r = s_rowy[t];
             __bf16 *dst = r != ~0u ? y + (((size_t)b * N + r) * nheads + h) * P + p8 : ytrash + p8;
-            *(u32x4 *)dst = *(const u32x4 *)&ybuf[t * LY + p8];
+            __builtin_nontemporal_store(*(const u32x4 *)&ybuf[t * LY + p8], (u32x4 *)dst);
         }
     };
 
