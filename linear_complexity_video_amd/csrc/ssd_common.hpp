@@ -182,7 +182,8 @@ __global__ __launch_bounds__(256) void k_pool8(const bf16_t *__restrict__ src, O
                     const size_t row0 = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw;
 #pragma unroll 8
                     for (int dw = 0; dw < pw; ++dw) {
-                        const u32x4 v = *(const u32x4 *)(src + ((size_t)b * N + row0 + dw) * C + ch);
+                        // read once: streaming loads leave L2 to the kernels running beside
+                        const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(src + ((size_t)b * N + row0 + dw) * C + ch));
 #pragma unroll
                         for (int e2 = 0; e2 < 4; ++e2) {
                             acc[2 * e2] += __uint_as_float(v[e2] << 16);
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256) void k_pool8(const bf16_t *__restrict__ src, O
         for (int e = r; e < cnt; e += rp) {
             const int dw = e % pw, dh = (e / pw) % ph, dt_ = e / (pw * ph);
             const size_t n = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw + dw;
-            const u32x4 v = *(const u32x4 *)(src + ((size_t)b * N + n) * C + ch);
+            const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(src + ((size_t)b * N + n) * C + ch));
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 acc[2 * e2] += __uint_as_float(v[e2] << 16);
