@@ -186,15 +186,14 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     auto row_of = [&](int tb, int l) -> size_t { return WHOLE ? (size_t)l : (size_t)sm.row[tb * MAXW + l]; };
 
     // Q^T fragments (B operand of S^T = K Q^T) of this lane's query: d = 16 kb + 8 half + 0..7.
+    // A query past the window reads the window's first row (finite; its output is never stored),
+    // so the loaded values are used as they are and the wait for them falls at their first use.
     auto load_q = [&](const Item &I, int tb, bf16x8 (&qf)[DH / 16]) {
         const int qi = I.q_base + wave * QW + col;
-        const bool ok = qi < I.m;
-        const __bf16 *qrow = q + I.head_off + row_of(tb, ok ? qi : 0) * rowstride;
+        const __bf16 *qrow = q + I.head_off + row_of(tb, qi < I.m ? qi : 0) * rowstride;
 #pragma unroll
-        for (int kb = 0; kb < DH / 16; ++kb) {
-            const u32x4 raw = *(const u32x4 *)(qrow + 16 * kb + 8 * half);
-            qf[kb] = __builtin_bit_cast(bf16x8, ok ? raw : u32x4{0, 0, 0, 0});
-        }
+        for (int kb = 0; kb < DH / 16; ++kb)
+            qf[kb] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 16 * kb + 8 * half));
     };
 
     // Tile loader: K and V rows as 16-byte chunks, natural layout.
