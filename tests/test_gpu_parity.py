@@ -314,6 +314,35 @@ def test_ssd_fast_ragged_with_review(oracle_mod, S, chunk):
         assert err <= 2e-2, (order, err)
 
 
+def test_ssd_fast_uneven_segments(oracle_mod):
+    """512 heads over 1450 tokens (chunk 64: 23 chunks, the last ragged) make the scan cut each head
+    into segments of 5, 5, 5, 5 and 3 chunks, so one workgroup runs both the paired steps and the odd
+    last step of the state sweep; 5 review tokens; sampled heads against the oracle in every order."""
+    rng = np.random.default_rng(11)
+    bsz, T, H, W, nh, P, S, G = 1, 2, 25, 29, 512, 64, 64, 1
+    say(f"ssd fast uneven segments {nh} heads grid {T}x{H}x{W}")
+    rnd = lambda *s: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32)))
+    x = rnd(bsz, T, H, W, nh, P) / 8
+    Bm, Cm = rnd(bsz, T, H, W, G, S) / 8, rnd(bsz, T, H, W, G, S) / 8
+    dt = np.log1p(np.exp(rng.normal(-1, 0.5, (bsz, T, H, W, nh)))).astype(np.float32)
+    A = -np.exp(rng.uniform(0, 1, nh)).astype(np.float32)
+    D = rng.standard_normal(nh).astype(np.float32)
+    dev = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in (x, Bm, Cm)] + \
+          [torch.from_numpy(a).cuda() for a in (dt, A, D)]
+    y = torch.full_like(dev[0], float("nan"))
+    for order in range(4):
+        B.mate_bissd_scan(*dev, y, order, 64, (2, 5, 29), B.ALGO_FAST)
+        torch.cuda.synchronize()
+        assert not torch.isnan(y).any().item(), "unwritten outputs"
+        for lo, hi in ((0, 1), (255, 256), (511, 512)):
+            want = oracle_mod.bissd(np.ascontiguousarray(x[..., lo:hi, :]), Bm, Cm,
+                                    np.ascontiguousarray(dt[..., lo:hi]), A[lo:hi], D[lo:hi],
+                                    (bsz, T, H, W), order, (2, 5, 29))
+            err = parity_error(to_f64(y[..., lo:hi, :]), want)
+            say(f"  order {order} heads {lo}:{hi} err={err:.3e}")
+            assert err <= 2e-2, (order, lo, err)
+
+
 @pytest.mark.parametrize("cfg,order", [(1, 0), (1, 3), (2, 0), (3, 2)])
 def test_ssd_fast_matches_portable(cfg, order):
     say(f"ssd fast vs portable cfg{cfg} order{order}")
