@@ -16,6 +16,11 @@
  *     xllm-io review "LinGen: Towards High-Resolution Minute-Length ...",
  *     section 三 "MA-Branch" item 2, which names the four orders and the flip
  *     n_flip = T*H*W - n).
+ *   - Zigzag scan, the alternative the pages compare RMS against (QbitAI
+ *     article, section "方法"; xllm-io review, section 三 "MA-Branch" and
+ *     Table 2, row "Zigzag"). The pages name it without defining it; it is
+ *     read here as the snake path through the grid, whose consecutive tokens
+ *     are always grid neighbours.
  *   - Review tokens: an average-pooled copy of the token tensor, unrolled in
  *     the same order and put in front of the sequence (forward) or, flipped,
  *     in front of the flipped sequence (xllm-io review, section 三 item 3;
@@ -61,10 +66,14 @@
  *   order 1 spatial-column major:  for t, for w, for h
  *   order 2 temporal-row major:    for h, for w, for t
  *   order 3 temporal-column major: for w, for h, for t
+ *   order 4 zigzag: frames in time order; frame t visits its rows h = 0..H-1
+ *     on even t and H-1..0 on odd t; the path walks each row along w, turning
+ *     round after every row it has covered (rows counted from the start of
+ *     the path), so it never jumps: each step changes one coordinate by one.
  * flip != 0 reverses the sequence. */
 int oracle_rms_sequence(int64_t T, int64_t H, int64_t W, int order, int flip, int64_t *seq)
 {
-    if (T <= 0 || H <= 0 || W <= 0 || order < 0 || order > 3 || !seq) return ORACLE_EINVAL;
+    if (T <= 0 || H <= 0 || W <= 0 || order < 0 || order > 4 || !seq) return ORACLE_EINVAL;
     int64_t i = 0;
     if (order == 0) {
         for (int64_t t = 0; t < T; ++t)
@@ -78,10 +87,20 @@ int oracle_rms_sequence(int64_t T, int64_t H, int64_t W, int order, int flip, in
         for (int64_t h = 0; h < H; ++h)
             for (int64_t w = 0; w < W; ++w)
                 for (int64_t t = 0; t < T; ++t) seq[i++] = (t * H + h) * W + w;
-    } else {
+    } else if (order == 3) {
         for (int64_t w = 0; w < W; ++w)
             for (int64_t h = 0; h < H; ++h)
                 for (int64_t t = 0; t < T; ++t) seq[i++] = (t * H + h) * W + w;
+    } else {
+        int64_t rows_done = 0;
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t r = 0; r < H; ++r, ++rows_done) {
+                const int64_t h = (t % 2 == 0) ? r : H - 1 - r;
+                for (int64_t c = 0; c < W; ++c) {
+                    const int64_t w = (rows_done % 2 == 0) ? c : W - 1 - c;
+                    seq[i++] = (t * H + h) * W + w;
+                }
+            }
     }
     if (flip) {
         int64_t N = T * H * W;
@@ -293,7 +312,7 @@ int oracle_bissd(const float *x, const float *B, const float *C, const float *dt
     if (!x || !B || !C || !dt || !A || !D || !y) return ORACLE_EINVAL;
     if (batch <= 0 || T <= 0 || H <= 0 || W <= 0 || nheads <= 0 || P <= 0 || S <= 0 || G <= 0)
         return ORACLE_EINVAL;
-    if (nheads % G || order < 0 || order > 3) return ORACLE_EINVAL;
+    if (nheads % G || order < 0 || order > 4) return ORACLE_EINVAL;
     if (head_lo < 0 || head_hi > nheads || head_lo >= head_hi) return ORACLE_EINVAL;
     int pooled = pool_t || pool_h || pool_w;
     if (pooled && (pool_t <= 0 || pool_h <= 0 || pool_w <= 0 || T % pool_t || H % pool_h || W % pool_w))

@@ -19,9 +19,23 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 _AXES = {0: (0, 1, 2), 1: (0, 2, 1), 2: (1, 2, 0), 3: (2, 1, 0)}
 
 
+def zigzag_closed_form(T, H, W):
+    """The snake path by array reversals: odd frames' rows reversed, then every
+    other row of the frame-by-frame row list reversed along w."""
+    a = np.arange(T * H * W).reshape(T, H, W).copy()
+    a[1::2] = a[1::2, ::-1, :]
+    rows = a.reshape(T * H, W)
+    rows[1::2] = rows[1::2, ::-1]
+    return rows.ravel()
+
+
 def rms_closed_form(T, H, W, order, flip=False):
-    """The four unroll orders as a transpose of the canonical index grid."""
-    s = np.arange(T * H * W).reshape(T, H, W).transpose(_AXES[order]).ravel()
+    """The four unroll orders as a transpose of the canonical index grid (order 4:
+    the zigzag path)."""
+    if order == 4:
+        s = zigzag_closed_form(T, H, W)
+    else:
+        s = np.arange(T * H * W).reshape(T, H, W).transpose(_AXES[order]).ravel()
     return s[::-1].copy() if flip else s
 
 
@@ -106,7 +120,7 @@ def test_rms_golden_hand_example(oracle_mod):
 def test_rms_closed_form_bijection_and_flip(oracle_mod):
     for T, H, W in itertools.product(range(1, 6), repeat=3):
         N = T * H * W
-        for order in range(4):
+        for order in range(5):
             s = oracle_mod.rms_sequence(T, H, W, order, False)
             f = oracle_mod.rms_sequence(T, H, W, order, True)
             np.testing.assert_array_equal(np.sort(s), np.arange(N))          # bijection
@@ -120,7 +134,7 @@ def test_rms_reorder_roundtrip(oracle_mod):
     for (T, H, W) in [(2, 3, 5), (4, 1, 7), (3, 3, 3)]:
         N = T * H * W
         src = rng.integers(0, 256, size=(2, N, 6), dtype=np.uint8)
-        for order in range(4):
+        for order in range(5):
             for flip in (False, True):
                 fwd = oracle_mod.rms_reorder(src, T, H, W, order, flip, inverse=False)
                 seq = rms_closed_form(T, H, W, order, flip)
@@ -130,8 +144,39 @@ def test_rms_reorder_roundtrip(oracle_mod):
 
 
 def test_rms_rejects_bad_order(oracle_mod):
-    with pytest.raises(ValueError):
-        oracle_mod.rms_sequence(2, 2, 2, 4)
+    for order in (-1, 5):
+        with pytest.raises(ValueError):
+            oracle_mod.rms_sequence(2, 2, 2, order)
+
+
+def test_zigzag_golden_hand_example(oracle_mod):
+    rows = [l for l in open(os.path.join(GOLDEN, "zigzag_2x2x3.txt")) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 2
+    for line in rows:
+        head, seq = line.split(":")
+        order, flip = (int(v) for v in head.split())
+        assert order == 4
+        want = np.array([int(v) for v in seq.split()])
+        np.testing.assert_array_equal(oracle_mod.rms_sequence(2, 2, 3, order, bool(flip)), want)
+
+
+def test_zigzag_is_a_path_of_grid_neighbours(oracle_mod):
+    # The property that sets the zigzag apart from the four RMS orders: it starts at the
+    # origin, visits every token once and moves by one step along one axis each time.
+    for T, H, W in itertools.product(range(1, 6), repeat=3):
+        N = T * H * W
+        s = oracle_mod.rms_sequence(T, H, W, 4, False)
+        np.testing.assert_array_equal(np.sort(s), np.arange(N))
+        np.testing.assert_array_equal(s, zigzag_closed_form(T, H, W))
+        np.testing.assert_array_equal(oracle_mod.rms_sequence(T, H, W, 4, True), s[::-1])
+        t, r = np.divmod(s, H * W)
+        h, w = np.divmod(r, W)
+        assert s[0] == 0
+        steps = np.abs(np.diff(t)) + np.abs(np.diff(h)) + np.abs(np.diff(w))
+        assert np.all(steps == 1), (T, H, W)
+    # A single frame with one row is the identity; a single column is the time-then-row snake.
+    np.testing.assert_array_equal(oracle_mod.rms_sequence(1, 1, 7, 4, False), np.arange(7))
+    np.testing.assert_array_equal(oracle_mod.rms_sequence(3, 2, 1, 4, False), [0, 1, 3, 2, 4, 5])
 
 
 # ----------------------------------------------------------------------------
@@ -142,7 +187,7 @@ def test_review_pool_brute_force(oracle_mod):
     rng = np.random.default_rng(2)
     for (T, H, W, pool) in [(4, 4, 6, (2, 2, 3)), (2, 4, 4, (2, 2, 2)), (6, 2, 4, (3, 1, 2))]:
         a = rng.standard_normal((T, H, W, 5)).astype(np.float32)
-        for order in range(4):
+        for order in range(5):
             got = oracle_mod.review_pool(a, T, H, W, pool, order)
             np.testing.assert_allclose(got, pool_brute(a, T, H, W, pool, order), rtol=1e-13, atol=1e-14)
 
@@ -159,7 +204,7 @@ def test_review_pool_unit_window_is_identity(oracle_mod):
 # Bidirectional Mamba2 scan
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("order", [0, 1, 2, 3])
+@pytest.mark.parametrize("order", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("pool", [(0, 0, 0), (2, 2, 2)])
 def test_ssd_equals_quadratic_dual_form(oracle_mod, order, pool):
     rng = np.random.default_rng(10 + order)
