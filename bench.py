@@ -201,6 +201,76 @@ def scaling_sweep(torch, np, B, reps):
                       "unit": "ms", "data": "synthetic", "points": points}), flush=True)
 
 
+def table2_variants(torch, np, B, wl, ssd, att, ws, reps, algo):
+    """Per-layer cost of the variants the pages compare in their ablation (xllm-io review, Table 2 and
+    section 五): the RMS layer schedule against the zigzag scan, the layer without review tokens, and
+    each branch alone, all on the same inputs at the workload's full size. The pages' zigzag overhead
+    comes from reordering large 3D tensors; here every order is index math inside the scan's gathers,
+    so the cost of materializing a scan order as tensors (x, B, C and dt gathered into it, y scattered
+    back, each a `mate_rms_reorder`) is reported beside it. Prints one JSON line.
+    """
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, reps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    def forward(order, shifted, pool):
+        return timed(lambda: B.mate_forward(ssd, att, order, wl.chunk, pool, wl.window, wl.layer_shift(shifted),
+                                            algo=algo, workspace=ws))
+
+    sched = list(wl.schedule)
+    mean = lambda xs: float(np.mean(xs))
+    log("variants: RMS schedule")
+    rms = [forward(o, sh, wl.pool) for o, sh in sched]
+    log("variants: zigzag")
+    zig = [forward(B.ORDER_ZIGZAG, sh, wl.pool) for _, sh in sched]
+    log("variants: no review tokens")
+    norev = [forward(o, sh, (0, 0, 0)) for o, sh in sched]
+    log("variants: branches alone")
+    te = [timed(lambda sh=sh: B.mate_tesa(att["q"], att["k"], att["v"], att["o"], wl.window, wl.layer_shift(sh),
+                                          0.0, algo)) for _, sh in sched]
+    ma = {o: timed(lambda o=o: B.mate_bissd_scan(ssd["x"], ssd["b"], ssd["c"], ssd["dt"], ssd["a"], ssd["d"],
+                                                 ssd["y"], o, wl.chunk, wl.pool, algo, workspace=ws))
+          for o in [o for o, _ in sched] + [B.ORDER_ZIGZAG]}
+    log("variants: materialized reorders")
+    mat = {}
+    for order in (2, B.ORDER_ZIGZAG):
+        total = 0.0
+        for key, inverse in (("x", False), ("b", False), ("c", False), ("dt", False), ("y", True)):
+            src = ssd[key]
+            dst = torch.empty_like(src)
+            total += timed(lambda src=src, dst=dst: B.mate_rms_reorder(src, dst, wl.grid, order, False, inverse))
+            del dst
+        mat["zigzag" if order == B.ORDER_ZIGZAG else f"rms_order_{order}"] = total
+    torch.cuda.empty_cache()
+    ms_rms = mean(rms)
+    rows = {
+        "rms_schedule": {"ms": ms_rms, "per_layer_ms": rms},
+        "zigzag": {"ms": mean(zig), "per_layer_ms": zig, "vs_rms": mean(zig) / ms_rms},
+        "no_review_tokens": {"ms": mean(norev), "per_layer_ms": norev, "vs_rms": mean(norev) / ms_rms},
+        "te_branch_only": {"ms": mean(te), "vs_rms": mean(te) / ms_rms},
+        "ma_branch_only": {"ms": mean([ma[o] for o, _ in sched]),
+                           "per_order_ms": {str(o): t for o, t in ma.items() if o != B.ORDER_ZIGZAG},
+                           "zigzag_ms": ma[B.ORDER_ZIGZAG]},
+        "materialized_scan_order": {"ms": mat, "tensors": "x, B, C, dt gathered; y scattered back"},
+    }
+    print(json.dumps({"metric": "per-layer forward time of the ablation variants (one MI355X)", "unit": "ms",
+                      "data": "synthetic",
+                      "config": {"workload": wl.name, "grid": list(wl.grid), "chunk": wl.chunk,
+                                 "pool": list(wl.pool), "window": list(wl.window)},
+                      "variants": rows}), flush=True)
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
@@ -218,6 +288,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed repetitions of each single call")
     ap.add_argument("--scaling", action="store_true",
                     help="instead of the throughput line: MATE core vs full attention per layer as T grows")
+    ap.add_argument("--variants", action="store_true",
+                    help="instead of the throughput line: per-layer time of the ablation variants (zigzag scan, "
+                         "no review tokens, each branch alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -266,6 +339,9 @@ def main():
     ws = torch.empty(max(1, B.mate_forward_workspace_size(wl.grid, sdesc, tdesc)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s; workspace {ws.numel() / 2**30:.2f} GiB")
+    if args.variants:
+        table2_variants(torch, np, B, wl, ssd, att, ws, args.kernel_reps, algo)
+        return
 
     def layer(order, shifted):
         B.mate_forward(ssd, att, order, wl.chunk, wl.pool, wl.window, wl.layer_shift(shifted), algo=algo,

@@ -43,11 +43,12 @@ extern "C" {
 #endif
 
 #define MATE_ABI_VERSION 1
+#define MATE_ORDER_ZIGZAG 4
 
 typedef enum {
     MATE_OK = 0,
     MATE_ERR_NULL = 1,        /* a required pointer is NULL */
-    MATE_ERR_SHAPE = 2,       /* an extent <= 0, order not in 0..3, window/pool not dividing
+    MATE_ERR_SHAPE = 2,       /* an extent <= 0, order not in 0..4, window/pool not dividing
                                  the grid, shift outside [0, window), heads not divisible by
                                  groups, chunk < 1 */
     MATE_ERR_UNSUPPORTED = 3, /* legal for the method but not built (e.g. a head size the
@@ -80,6 +81,13 @@ typedef struct {
  *   order 1 spatial-column major   for t, for w, for h
  *   order 2 temporal-row major     for h, for w, for t
  *   order 3 temporal-column major  for w, for h, for t
+ * Order 4 (MATE_ORDER_ZIGZAG) is the zigzag scan that the pages compare RMS
+ * against (QbitAI article, section "方法"; xllm-io review, section 三 and
+ * Table 2, row "Zigzag"). The pages do not define it; it is the snake path:
+ * frame t visits rows h = 0..H-1 on even t and H-1..0 on odd t, and the k-th
+ * row of the path (k = t*H + its position in the frame) runs w = 0..W-1 on
+ * even k and W-1..0 on odd k, so consecutive tokens are grid neighbours. Every
+ * entry point that takes an order accepts it.
  * flip != 0 reverses the sequence: perm'(i) = perm(N-1-i), N = T*H*W.
  *
  * Copies whole token rows of `row_bytes` bytes:

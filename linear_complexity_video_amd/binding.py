@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmate.so")
 MATE_OK, MATE_ERR_NULL, MATE_ERR_SHAPE, MATE_ERR_UNSUPPORTED, MATE_ERR_WORKSPACE, MATE_ERR_DEVICE = range(6)
 MATE_F32, MATE_BF16 = 0, 1
 ALGO_AUTO, ALGO_PORTABLE, ALGO_FAST = 0, 1, 2
+ORDER_ZIGZAG = 4  # MATE_ORDER_ZIGZAG: the snake path; orders 0..3 are the RMS orders
 
 EXPORTED = (
     "mate_rms_reorder", "mate_bissd_workspace_size", "mate_bissd_scan", "mate_tesa",

@@ -33,6 +33,11 @@ template <> struct elem<bf16_t> {
 // Rotary Major Scan: canonical token index of scan position i (0 <= i < T*H*W)
 // for unroll order `order`, loops written outermost first:
 //   0: t,h,w   1: t,w,h   2: h,w,t   3: w,h,t
+// Order 4 is the zigzag (snake) path that RMS replaces (QbitAI article, section
+// "方法"; xllm-io review, Table 2): frame t runs its rows forward on even t and
+// backward on odd t, and row k of the path (k = t*H + position in the frame)
+// runs along w forward on even k and backward on odd k, so consecutive tokens
+// are grid neighbours.
 __device__ __forceinline__ int64_t rms_index(int64_t i, int order, int64_t T, int64_t H, int64_t W)
 {
     int64_t t, h, w;
@@ -53,11 +58,20 @@ __device__ __forceinline__ int64_t rms_index(int64_t i, int order, int64_t T, in
         t = r - w * T;
         break;
     }
-    default: {
+    case 3: {
         w = i / (H * T);
         int64_t r = i - w * (H * T);
         h = r / T;
         t = r - h * T;
+        break;
+    }
+    default: {
+        const int64_t k = i / W;  // row of the path
+        const int64_t c = i - k * W;
+        t = k / H;
+        const int64_t r = k - t * H;
+        h = (t & 1) ? H - 1 - r : r;
+        w = (k & 1) ? W - 1 - c : c;
         break;
     }
     }
@@ -85,11 +99,20 @@ __device__ __forceinline__ uint32_t rms_index32(uint32_t i, int order, uint32_t 
         t = r - w * T;
         break;
     }
-    default: {
+    case 3: {
         w = i / (H * T);
         uint32_t r = i - w * (H * T);
         h = r / T;
         t = r - h * T;
+        break;
+    }
+    default: {
+        const uint32_t k = i / W;  // row of the path
+        const uint32_t c = i - k * W;
+        t = k / H;
+        const uint32_t r = k - t * H;
+        h = (t & 1u) ? H - 1u - r : r;
+        w = (k & 1u) ? W - 1u - c : c;
         break;
     }
     }

@@ -104,7 +104,7 @@ mate_status make_ssd_problem(mate_grid g, int order, const mate_ssd_desc *d, mat
     if (!d) return fail(MATE_ERR_NULL, "ssd descriptor is NULL");
     mate_status s = check_grid(g);
     if (s != MATE_OK) return s;
-    if (order < 0 || order > 3) return fail(MATE_ERR_SHAPE, "order %d not in 0..3", order);
+    if (order < 0 || order > MATE_ORDER_ZIGZAG) return fail(MATE_ERR_SHAPE, "order %d not in 0..4", order);
     if (d->nheads <= 0 || d->headdim <= 0 || d->d_state <= 0 || d->ngroups <= 0)
         return fail(MATE_ERR_SHAPE, "nheads, headdim, d_state and ngroups must be positive");
     if (d->chunk < 1) return fail(MATE_ERR_SHAPE, "chunk %d < 1", d->chunk);
@@ -231,7 +231,7 @@ mate_status mate_rms_reorder(const void *src, void *dst, mate_grid g, int64_t ro
     mate_status s = check_grid(g);
     if (s != MATE_OK) return s;
     if (row_bytes <= 0) return fail(MATE_ERR_SHAPE, "row_bytes %lld must be positive", (long long)row_bytes);
-    if (order < 0 || order > 3) return fail(MATE_ERR_SHAPE, "order %d not in 0..3", order);
+    if (order < 0 || order > MATE_ORDER_ZIGZAG) return fail(MATE_ERR_SHAPE, "order %d not in 0..4", order);
     const int64_t rows = g.batch * g.T * g.H * g.W;
     if (row_bytes > ((int64_t)1 << 40) / rows) return fail(MATE_ERR_UNSUPPORTED, "tensor above 1 TiB");
     const uintptr_t bytes = (uintptr_t)(rows * row_bytes);

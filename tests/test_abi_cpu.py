@@ -50,8 +50,9 @@ def test_rms_validation():
     lib = B.lib()
     g = B.Grid(1, 2, 2, 2)
     assert lib.mate_rms_reorder(None, FAKE, g, 16, 0, 0, 0, None) == B.MATE_ERR_NULL
-    assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), g, 16, 4, 0, 0, None) == B.MATE_ERR_SHAPE
+    assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), g, 16, 5, 0, 0, None) == B.MATE_ERR_SHAPE
     assert "order" in lib.mate_last_error().decode()
+    assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), g, 16, -1, 0, 0, None) == B.MATE_ERR_SHAPE
     assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), B.Grid(1, 0, 2, 2), 16, 0, 0, 0, None) == B.MATE_ERR_SHAPE
     assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), g, 0, 0, 0, 0, None) == B.MATE_ERR_SHAPE
     # overlapping buffers

@@ -44,7 +44,7 @@ def test_rms_reorder_bitexact_all_orders(oracle_mod, cfg):
     rows = x.reshape(wl.batch, wl.N, -1).view(np.uint8)
     src = torch.from_numpy(rows).cuda()
     dst = torch.empty_like(src)
-    for order in range(4):
+    for order in range(5):  # the four RMS orders and the zigzag
         for flip in (False, True):
             for inverse in (False, True):
                 say(f"rms cfg{cfg} order{order} flip{flip} inv{inverse}")
@@ -61,7 +61,7 @@ def test_rms_reorder_bitexact_long_grid(oracle_mod):
     src = torch.from_numpy(rows).cuda()
     dst = torch.empty_like(src)
     for order, flip, inverse in ((0, True, False), (1, False, False), (2, True, True), (3, False, False),
-                                 (3, True, True)):
+                                 (3, True, True), (4, True, False), (4, False, True)):
         say(f"rms long grid order{order} flip{flip} inv{inverse}")
         B.mate_rms_reorder(src, dst, wl.grid, order, flip, inverse)
         want = oracle_mod.rms_reorder(rows, wl.T, wl.H, wl.W, order, flip, inverse)
@@ -76,7 +76,7 @@ def test_rms_reorder_odd_rows(oracle_mod, row_bytes):
     rows = rng.integers(0, 256, size=(2, 105, row_bytes), dtype=np.uint8)
     src = torch.from_numpy(rows).cuda()
     dst = torch.empty_like(src)
-    for order in range(4):
+    for order in range(5):  # the four RMS orders and the zigzag
         for flip, inverse in ((False, False), (True, True)):
             B.mate_rms_reorder(src, dst, grid, order, flip, inverse)
             want = oracle_mod.rms_reorder(rows, 3, 5, 7, order, flip, inverse)
@@ -87,7 +87,7 @@ def test_rms_reorder_roundtrip_on_device():
     g = (1, 8, 16, 16)
     src = torch.randn(1, 2048, 40, device="cuda").to(torch.bfloat16)
     mid, back = torch.empty_like(src), torch.empty_like(src)
-    for order in range(4):
+    for order in range(5):  # the four RMS orders and the zigzag
         B.mate_rms_reorder(src, mid, g, order, True, False)
         B.mate_rms_reorder(mid, back, g, order, True, True)
         assert torch.equal(back, src)
@@ -126,7 +126,7 @@ def oracle_ssd(oracle_mod, cfg, inp, order, heads):
                             wl.grid, order, wl.pool)
 
 
-@pytest.mark.parametrize("cfg,order", [(0, o) for o in range(4)] + [(1, o) for o in range(4)])
+@pytest.mark.parametrize("cfg,order", [(0, o) for o in range(5)] + [(1, o) for o in range(5)])
 def test_ssd_parity_full(oracle_mod, cfg, order):
     say(f"ssd cfg{cfg} order{order}")
     inp, y = run_ssd(cfg, order)
@@ -136,7 +136,7 @@ def test_ssd_parity_full(oracle_mod, cfg, order):
     assert err <= TOL[cfg]
 
 
-@pytest.mark.parametrize("cfg,order", [(2, 0), (3, 0), (3, 1), (3, 2), (3, 3), (4, 0), (4, 3)])
+@pytest.mark.parametrize("cfg,order", [(2, 0), (3, 0), (3, 1), (3, 2), (3, 3), (3, 4), (4, 0), (4, 3), (4, 4)])
 def test_ssd_parity_sampled_heads(oracle_mod, cfg, order):
     say(f"ssd cfg{cfg} order{order} (sampled heads)")
     inp, y = run_ssd(cfg, order)
@@ -179,7 +179,7 @@ def test_ssd_ragged_grid_with_review(oracle_mod, dtype):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     dev = [torch.from_numpy(a).cuda().to(tdt) for a in (x, Bm, Cm)] + [torch.from_numpy(a).cuda() for a in (dt, A, D)]
     y = torch.full_like(dev[0], float("nan"))
-    for order in range(4):
+    for order in range(5):  # the four RMS orders and the zigzag
         B.mate_bissd_scan(*dev, y, order, 16, (3, 1, 7))
         want = oracle_mod.bissd(x, Bm, Cm, dt, A, D, (bsz, T, H, W), order, (3, 1, 7))
         err = parity_error(to_f64(y), want)
@@ -277,7 +277,7 @@ def test_forward_equals_composed_calls(cfg):
     wl = WORKLOADS[cfg]
     _, sd = ssd_device(cfg)
     _, td = tesa_device(cfg)
-    for order, shifted in wl.schedule[:2]:
+    for order, shifted in tuple(wl.schedule[:2]) + ((B.ORDER_ZIGZAG, True),):
         shift = wl.layer_shift(shifted)
         y1, o1 = torch.full_like(sd["x"], float("nan")), torch.full_like(td["q"], float("nan"))
         y2, o2 = torch.full_like(sd["x"], float("nan")), torch.full_like(td["q"], float("nan"))
@@ -307,7 +307,7 @@ def test_ssd_fast_ragged_with_review(oracle_mod, S, chunk):
     dev = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in (x, Bm, Cm)] + \
           [torch.from_numpy(a).cuda() for a in (dt, A, D)]
     y = torch.full_like(dev[0], float("nan"))
-    for order in range(4):
+    for order in range(5):  # the four RMS orders and the zigzag
         B.mate_bissd_scan(*dev, y, order, chunk, (3, 1, 7), B.ALGO_FAST)
         want = oracle_mod.bissd(x, Bm, Cm, dt, A, D, (bsz, T, H, W), order, (3, 1, 7))
         err = parity_error(to_f64(y), want)
@@ -330,7 +330,7 @@ def test_ssd_fast_uneven_segments(oracle_mod):
     dev = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in (x, Bm, Cm)] + \
           [torch.from_numpy(a).cuda() for a in (dt, A, D)]
     y = torch.full_like(dev[0], float("nan"))
-    for order in range(4):
+    for order in range(5):  # the four RMS orders and the zigzag
         B.mate_bissd_scan(*dev, y, order, 64, (2, 5, 29), B.ALGO_FAST)
         torch.cuda.synchronize()
         assert not torch.isnan(y).any().item(), "unwritten outputs"
