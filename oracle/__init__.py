@@ -45,12 +45,13 @@ def _load():
     lib.oracle_rms_reorder.argtypes = [p, p, i64, i64, i64, i64, i64, i32, i32, i32]
     lib.oracle_review_pool.argtypes = [p, i64, i64, i64, i64, i32, i32, i32, i32, p]
     lib.oracle_bissd.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64] + [i32] * 11 + [p]
+    lib.oracle_biscan1.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64] + [i32] * 9 + [p]
     lib.oracle_tesa_region_counts.argtypes = [i64, i64, i64] + [i32] * 6 + [p]
     lib.oracle_tesa.argtypes = (
         [p, p, p, i64, i64, i64, i64] + [i32] * 8 + [ctypes.c_double, i32, i32, p, i64, i32, p]
     )
     for f in ("oracle_rms_sequence", "oracle_rms_reorder", "oracle_review_pool", "oracle_bissd",
-              "oracle_tesa_region_counts", "oracle_tesa"):
+              "oracle_biscan1", "oracle_tesa_region_counts", "oracle_tesa"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -122,6 +123,25 @@ def bissd(x, B, C, dt, A, D, grid, order: int, pool=(0, 0, 0), heads=None, nthre
                               nheads, P, S, G, order, pool[0], pool[1], pool[2], lo, hi,
                               nthreads or default_threads(), _ptr(y))
     _check(rc, "bissd")
+    return y
+
+
+def biscan1(x, B, C, dt, A, D, grid, order: int, pool=(0, 0, 0), channels=None, nthreads=None) -> np.ndarray:
+    """Bidirectional Mamba (selective scan); returns y[b][T][H][W][nc] (float64) for ``channels``.
+
+    x, dt [b][T][H][W][nch], B/C [b][T][H][W][S], A [nch][S], D [nch]. ``channels`` is a (lo, hi)
+    range, default all channels.
+    """
+    batch, T, H, W = grid
+    x, B, C, dt, A, D = (_f32(a) for a in (x, B, C, dt, A, D))
+    nch, S = x.shape[-1], B.shape[-1]
+    assert A.shape == (nch, S) and dt.shape[-1] == nch and D.shape == (nch,)
+    lo, hi = channels if channels is not None else (0, nch)
+    y = np.empty((batch, T, H, W, hi - lo), dtype=np.float64)
+    rc = _load().oracle_biscan1(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), batch, T, H, W,
+                                nch, S, order, pool[0], pool[1], pool[2], lo, hi,
+                                nthreads or default_threads(), _ptr(y))
+    _check(rc, "biscan1")
     return y
 
 

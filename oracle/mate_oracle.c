@@ -366,6 +366,122 @@ done:
 }
 
 /* ------------------------------------------------------------------------ */
+/* Bidirectional Mamba (selective scan), the MA branch of the ablation        */
+/* ------------------------------------------------------------------------ */
+/* The xllm-io review compares the MA branch built on Mamba with the one built
+ * on Mamba2 (Table 2, row "Mamba", and the Mamba2 bullet under it). Mamba's
+ * selective scan gives every channel c its own d_state states with their own
+ * decay rates: A is a [channels][d_state] matrix and dt comes per channel,
+ * where Mamba2 has one A and one dt per head. Per channel c and state s:
+ *   h_u[c][s] = exp(dt_u[c] A[c][s]) h_{u-1}[c][s] + dt_u[c] x_u[c] B_u[s]
+ *   y_u[c]    = sum_s C_u[s] h_u[c][s] + D[c] x_u[c]
+ * The sequences, review tokens, flip and sum are those of the Mamba2 scan. */
+typedef struct {
+    const float *x, *B, *C, *dt, *A, *D;
+    int64_t batch, N, R;
+    int nch, S, ch_lo, ch_hi;
+    const int64_t *seq;
+    const double *rx, *rB, *rdt; /* review tokens per batch: [b][R][nch], [b][R][S], [b][R][nch] */
+    double *yf, *yb;             /* [b][N][ch_hi - ch_lo] for the forward / backward direction */
+} scan1_ctx;
+
+static void scan1_unit(void *vctx, int64_t unit)
+{
+    scan1_ctx *c = (scan1_ctx *)vctx;
+    int nc = c->ch_hi - c->ch_lo;
+    int64_t b = unit / (2 * nc);
+    int cl = (int)((unit / 2) % nc);
+    int dir = (int)(unit % 2);
+    int ch = c->ch_lo + cl;
+    int S = c->S;
+    int64_t N = c->N, R = c->R, nch = c->nch;
+    const float *A = c->A + (int64_t)ch * S;
+    double D = (double)c->D[ch];
+    double *h = (double *)calloc((size_t)S, sizeof(double));
+    double *out = (dir == 0 ? c->yf : c->yb) + b * N * nc;
+    if (!h) return;
+    for (int64_t jj = 0; jj < R; ++jj) {
+        int64_t j = dir == 0 ? jj : R - 1 - jj;
+        double xv = c->rx[(b * R + j) * nch + ch], dt = c->rdt[(b * R + j) * nch + ch];
+        const double *Bv = c->rB + (b * R + j) * S;
+        for (int s = 0; s < S; ++s) h[s] = exp(dt * (double)A[s]) * h[s] + dt * xv * Bv[s];
+    }
+    for (int64_t ii = 0; ii < N; ++ii) {
+        int64_t i = dir == 0 ? ii : N - 1 - ii;
+        int64_t n = c->seq[i];
+        double xv = (double)c->x[(b * N + n) * nch + ch], dt = (double)c->dt[(b * N + n) * nch + ch];
+        const float *Br = c->B + (b * N + n) * S, *Cr = c->C + (b * N + n) * S;
+        double acc = 0.0;
+        for (int s = 0; s < S; ++s) {
+            h[s] = exp(dt * (double)A[s]) * h[s] + dt * xv * (double)Br[s];
+            acc += (double)Cr[s] * h[s];
+        }
+        out[n * nc + cl] = acc + D * xv;
+    }
+    free(h);
+}
+
+/* y[b][n][c - ch_lo] for channels in [ch_lo, ch_hi).
+ * x, dt [batch][T][H][W][nch] (dt > 0)   B, C [batch][T][H][W][S]
+ * A [nch][S] (< 0)                        D [nch]
+ * pool_* all zero: no review tokens; otherwise they must divide T, H, W. */
+int oracle_biscan1(const float *x, const float *B, const float *C, const float *dt, const float *A,
+                   const float *D, int64_t batch, int64_t T, int64_t H, int64_t W, int nch, int S,
+                   int order, int pool_t, int pool_h, int pool_w, int ch_lo, int ch_hi, int nthreads,
+                   double *y)
+{
+    if (!x || !B || !C || !dt || !A || !D || !y) return ORACLE_EINVAL;
+    if (batch <= 0 || T <= 0 || H <= 0 || W <= 0 || nch <= 0 || S <= 0 || order < 0 || order > 4)
+        return ORACLE_EINVAL;
+    if (ch_lo < 0 || ch_hi > nch || ch_lo >= ch_hi) return ORACLE_EINVAL;
+    int pooled = pool_t || pool_h || pool_w;
+    if (pooled && (pool_t <= 0 || pool_h <= 0 || pool_w <= 0 || T % pool_t || H % pool_h || W % pool_w))
+        return ORACLE_EINVAL;
+    int64_t N = T * H * W;
+    int64_t R = pooled ? (T / pool_t) * (H / pool_h) * (W / pool_w) : 0;
+    int nc = ch_hi - ch_lo;
+    int rc = ORACLE_OK;
+
+    int64_t *seq = (int64_t *)malloc(sizeof(int64_t) * (size_t)N);
+    double *yb = (double *)malloc(sizeof(double) * (size_t)(batch * N * nc));
+    double *rx = NULL, *rB = NULL, *rdt = NULL;
+    if (!seq || !yb) { rc = ORACLE_ENOMEM; goto done; }
+    rc = oracle_rms_sequence(T, H, W, order, 0, seq);
+    if (rc) goto done;
+    if (R > 0) {
+        rx = (double *)malloc(sizeof(double) * (size_t)(batch * R * nch));
+        rB = (double *)malloc(sizeof(double) * (size_t)(batch * R * S));
+        rdt = (double *)malloc(sizeof(double) * (size_t)(batch * R * nch));
+        if (!rx || !rB || !rdt) { rc = ORACLE_ENOMEM; goto done; }
+        for (int64_t b = 0; b < batch && !rc; ++b) {
+            rc = oracle_review_pool(x + b * N * nch, T, H, W, nch, pool_t, pool_h, pool_w, order, rx + b * R * nch);
+            if (!rc) rc = oracle_review_pool(B + b * N * S, T, H, W, S, pool_t, pool_h, pool_w, order, rB + b * R * S);
+            if (!rc)
+                rc = oracle_review_pool(dt + b * N * nch, T, H, W, nch, pool_t, pool_h, pool_w, order, rdt + b * R * nch);
+        }
+        if (rc) goto done;
+    }
+    {
+        scan1_ctx c;
+        c.x = x; c.B = B; c.C = C; c.dt = dt; c.A = A; c.D = D;
+        c.batch = batch; c.N = N; c.R = R;
+        c.nch = nch; c.S = S; c.ch_lo = ch_lo; c.ch_hi = ch_hi;
+        c.seq = seq; c.rx = rx; c.rB = rB; c.rdt = rdt;
+        c.yf = y; c.yb = yb;
+        run_units(scan1_unit, &c, batch * nc * 2, nthreads);
+        int64_t total = batch * N * nc;
+        for (int64_t e = 0; e < total; ++e) y[e] += yb[e];
+    }
+done:
+    free(seq);
+    free(yb);
+    free(rx);
+    free(rB);
+    free(rdt);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* TESA: attention inside shifted 3D windows                                  */
 /* ------------------------------------------------------------------------ */
 

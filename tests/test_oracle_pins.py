@@ -215,6 +215,100 @@ def test_ssd_equals_quadratic_dual_form(oracle_mod, order, pool):
     assert relerr(got, want) < 1e-12
 
 
+# ----------------------------------------------------------------------------
+# Bidirectional Mamba (selective scan), the ablation's MA-branch variant
+# ----------------------------------------------------------------------------
+
+def scan1_dual_bidirectional(x, B, C, dt, A, D, T, H, W, order, pool):
+    """Per channel, the sum over states of masked rank-one matrices
+    M_uv = C_u[s] B_v[s] exp(cs_s(u) - cs_s(v)) dt_v (v <= u), cs_s = cumsum(dt A[c][s]),
+    over rev ++ seq and its reversal; one batch."""
+    N = T * H * W
+    nch, S = x.shape[-1], B.shape[-1]
+    x = x.reshape(N, nch).astype(np.float64)
+    B = B.reshape(N, S).astype(np.float64)
+    C = C.reshape(N, S).astype(np.float64)
+    dt = dt.reshape(N, nch).astype(np.float64)
+    seq = rms_closed_form(T, H, W, order)
+    if any(pool):
+        rx, rB, rdt = (pool_brute(a, T, H, W, pool, order) for a in (x, B, dt))
+    else:
+        rx, rB, rdt = np.zeros((0, nch)), np.zeros((0, S)), np.zeros((0, nch))
+    R = rx.shape[0]
+    y = np.zeros((N, nch))
+    for s_main, rsel in ((seq, slice(None)), (seq[::-1], slice(None, None, -1))):
+        xs = np.concatenate([rx[rsel], x[s_main]])
+        Bs = np.concatenate([rB[rsel], B[s_main]])
+        Cs = np.concatenate([np.zeros((R, S)), C[s_main]])  # review outputs are dropped
+        ds = np.concatenate([rdt[rsel], dt[s_main]])
+        for c in range(nch):
+            M = np.zeros((R + N, R + N))
+            for st in range(S):
+                cs = np.cumsum(ds[:, c] * float(A[c, st]))
+                M += np.outer(Cs[:, st], Bs[:, st]) * np.exp(np.minimum(cs[:, None] - cs[None, :], 0.0))
+            M = np.tril(M) * ds[None, :, c]
+            y[s_main, c] += (M @ xs[:, c] + float(D[c]) * xs[:, c])[R:]
+    return y.reshape(1, T, H, W, nch)
+
+
+def rand_scan1(rng, T, H, W, nch, S):
+    x = rng.standard_normal((1, T, H, W, nch)).astype(np.float32)
+    B = rng.standard_normal((1, T, H, W, S)).astype(np.float32)
+    C = rng.standard_normal((1, T, H, W, S)).astype(np.float32)
+    dt = np.log1p(np.exp(rng.normal(-1.0, 0.5, (1, T, H, W, nch)))).astype(np.float32)
+    A = (-np.exp(rng.uniform(0, 1, (nch, S)))).astype(np.float32)
+    D = rng.standard_normal(nch).astype(np.float32)
+    return x, B, C, dt, A, D
+
+
+@pytest.mark.parametrize("order", [0, 2, 4])
+@pytest.mark.parametrize("pool", [(0, 0, 0), (2, 2, 2)])
+def test_scan1_equals_quadratic_form(oracle_mod, order, pool):
+    rng = np.random.default_rng(30 + order)
+    T, H, W = 2, 4, 4
+    x, B, C, dt, A, D = rand_scan1(rng, T, H, W, nch=5, S=3)
+    got = oracle_mod.biscan1(x, B, C, dt, A, D, (1, T, H, W), order, pool)
+    want = scan1_dual_bidirectional(x, B, C, dt, A, D, T, H, W, order, pool)
+    assert relerr(got, want) < 1e-12
+
+
+@pytest.mark.parametrize("pool", [(0, 0, 0), (2, 2, 2)])
+def test_scan1_with_head_shared_rates_is_mamba2(oracle_mod, pool):
+    # One decay rate per head (A[c][s] = A_h for every state s and channel c of head h) and one dt
+    # per head: the selective scan is then the Mamba2 scan with P = channels per head and one B/C
+    # group, which the dual-form pins above fix independently.
+    rng = np.random.default_rng(33)
+    T, H, W, nheads, P, S = 2, 4, 4, 3, 4, 5
+    x, B, C, dt, A, D = rand_ssd(rng, T, H, W, nheads, P, S)
+    nch = nheads * P
+    x1 = x.reshape(1, T, H, W, nch)
+    dt1 = np.repeat(dt, P, axis=-1)
+    A1 = np.repeat(A, P)[:, None] * np.ones((1, S), np.float32)
+    D1 = np.repeat(D, P)
+    got = oracle_mod.biscan1(x1, B[..., 0, :], C[..., 0, :], dt1, A1, D1, (1, T, H, W), 1, pool)
+    want = oracle_mod.bissd(x, B, C, dt, A, D, (1, T, H, W), 1, pool).reshape(1, T, H, W, nch)
+    assert relerr(got, want) < 1e-12
+
+
+def test_scan1_special_cases_and_channel_range(oracle_mod):
+    rng = np.random.default_rng(34)
+    T, H, W = 2, 2, 4
+    x, B, C, dt, A, D = rand_scan1(rng, T, H, W, nch=6, S=4)
+    full = oracle_mod.biscan1(x, B, C, dt, A, D, (1, T, H, W), 3, (1, 2, 2))
+    part = oracle_mod.biscan1(x, B, C, dt, A, D, (1, T, H, W), 3, (1, 2, 2), channels=(2, 5))
+    np.testing.assert_array_equal(part, full[..., 2:5])
+    # B = 0: no state, each direction gives D x
+    got = oracle_mod.biscan1(x, np.zeros_like(B), C, dt, A, D, (1, T, H, W), 0)
+    np.testing.assert_allclose(got, 2 * D * x.astype(np.float64), rtol=1e-14, atol=1e-14)
+    # one token: each direction gives (dt x C.B + D x)
+    x1, B1, C1, dt1 = x[:, :1, :1, :1], B[:, :1, :1, :1], C[:, :1, :1, :1], dt[:, :1, :1, :1]
+    got = oracle_mod.biscan1(x1, B1, C1, dt1, A, D, (1, 1, 1, 1), 0)
+    cb = float(np.dot(C1.reshape(-1).astype(np.float64), B1.reshape(-1).astype(np.float64)))
+    xd = x1.astype(np.float64)
+    want = 2 * (dt1.astype(np.float64) * xd * cb + D.astype(np.float64) * xd)
+    np.testing.assert_allclose(got, want, rtol=1e-13)
+
+
 def test_ssd_groups_split_heads(oracle_mod):
     rng = np.random.default_rng(11)
     T, H, W = 2, 2, 4
