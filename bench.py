@@ -207,7 +207,9 @@ def table2_variants(torch, np, B, wl, ssd, att, ws, reps, algo):
     each branch alone, all on the same inputs at the workload's full size. The pages' zigzag overhead
     comes from reordering large 3D tensors; here every order is index math inside the scan's gathers,
     so the cost of materializing a scan order as tensors (x, B, C and dt gathered into it, y scattered
-    back, each a `mate_rms_reorder`) is reported beside it. Prints one JSON line.
+    back, each a `mate_rms_reorder`) is reported beside it. The Mamba row runs the selective scan
+    (`mate_bimamba_scan`) on the same x as 5120 channels, with per-channel dt and A and d_state 16
+    (sizes the pages do not give), then TESA. Prints one JSON line.
     """
     stream = torch.cuda.current_stream()
 
@@ -253,6 +255,30 @@ def table2_variants(torch, np, B, wl, ssd, att, ws, reps, algo):
             del dst
         mat["zigzag" if order == B.ORDER_ZIGZAG else f"rms_order_{order}"] = total
     torch.cuda.empty_cache()
+    log("variants: Mamba (selective scan) MA branch")
+    T, H, W = wl.T, wl.H, wl.W
+    dev = ssd["x"].device
+    g = torch.Generator(device=dev).manual_seed(7)
+    nch, S1 = ssd["x"].shape[-2] * ssd["x"].shape[-1], 16
+    mx = ssd["x"].view(wl.batch, T, H, W, nch)
+    mB = (torch.randn(wl.batch, T, H, W, S1, device=dev, generator=g) / 4).to(torch.bfloat16)
+    mC = (torch.randn(wl.batch, T, H, W, S1, device=dev, generator=g) / 4).to(torch.bfloat16)
+    mdt = torch.nn.functional.softplus(torch.randn(wl.batch, T, H, W, nch, device=dev, generator=g) * 0.5 - 2)
+    mA = -torch.exp(torch.rand(nch, S1, device=dev, generator=g) * 2)
+    mD = torch.randn(nch, device=dev, generator=g)
+    my = torch.empty_like(mx)
+    mws = torch.empty(B.mate_bimamba_workspace_size(wl.grid, B.mamba_desc(mx, mB, wl.pool)), dtype=torch.uint8,
+                      device=dev)
+    mamba_ma = {o: timed(lambda o=o: B.mate_bimamba_scan(mx, mB, mC, mdt, mA, mD, my, o, wl.pool, workspace=mws))
+                for o in sorted(set(o for o, _ in sched))}
+
+    def mamba_layer(o, sh):
+        B.mate_bimamba_scan(mx, mB, mC, mdt, mA, mD, my, o, wl.pool, workspace=mws)
+        B.mate_tesa(att["q"], att["k"], att["v"], att["o"], wl.window, wl.layer_shift(sh), 0.0, algo)
+
+    mamba = [timed(lambda o=o, sh=sh: mamba_layer(o, sh)) for o, sh in sched]
+    del mB, mC, mdt, my, mws
+    torch.cuda.empty_cache()
     ms_rms = mean(rms)
     rows = {
         "rms_schedule": {"ms": ms_rms, "per_layer_ms": rms},
@@ -263,6 +289,10 @@ def table2_variants(torch, np, B, wl, ssd, att, ws, reps, algo):
                            "per_order_ms": {str(o): t for o, t in ma.items() if o != B.ORDER_ZIGZAG},
                            "zigzag_ms": ma[B.ORDER_ZIGZAG]},
         "materialized_scan_order": {"ms": mat, "tensors": "x, B, C, dt gathered; y scattered back"},
+        "mamba_selective_scan": {"ms": mean(mamba), "per_layer_ms": mamba, "vs_rms": mean(mamba) / ms_rms,
+                                 "ma_branch_ms": mean(list(mamba_ma.values())),
+                                 "ma_branch_per_order_ms": {str(o): t for o, t in mamba_ma.items()},
+                                 "channels": nch, "d_state": S1},
     }
     print(json.dumps({"metric": "per-layer forward time of the ablation variants (one MI355X)", "unit": "ms",
                       "data": "synthetic",

@@ -148,6 +148,38 @@ mate_status mate_bissd_scan(const mate_ssd_tensors *t, mate_grid g, int order, c
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Bidirectional Mamba (selective scan), the ablation's MA-branch variant     */
+/* ------------------------------------------------------------------------ */
+/* The ablation of the xllm-io review (Table 2, row "Mamba", and the Mamba2
+ * bullet under it) builds the MA branch on Mamba instead of Mamba2. Mamba's
+ * selective scan gives every channel c (c < channels) its own d_state states
+ * and decay rates. For each direction, over the sequences of mate_bissd_scan
+ * (review tokens first, order `order`, reversed for the backward direction),
+ * from h = 0:
+ *     h_u[c][s] = exp(dt_u[c] * A[c][s]) h_{u-1}[c][s] + dt_u[c] x_u[c] B_u[s]
+ *     y_u[c]    = sum_s C_u[s] h_u[c][s] + D[c] x_u[c]
+ * and y = y_forward + y_backward at the main tokens, in canonical order.
+ * Review tokens average x, B and dt over the pool blocks as in
+ * mate_bissd_scan. The tensors are a mate_ssd_tensors with these layouts:
+ *   x, y [batch][T][H][W][channels] (dtype)   b, c [batch][T][H][W][d_state] (dtype)
+ *   dt [batch][T][H][W][channels] fp32 (> 0)  a [channels][d_state] fp32 (< 0)
+ *   d [channels] fp32
+ * x, b, c, y 16-byte aligned; dt, a, d 4-byte aligned. */
+typedef struct {
+    int32_t channels, d_state;
+    int32_t pool_t, pool_h, pool_w; /* all 0: no review tokens */
+    mate_dtype dtype;
+} mate_mamba_desc;
+
+size_t mate_bimamba_workspace_size(mate_grid g, const mate_mamba_desc *d);
+
+/* Supported: d_state 8, 16 or 32, any channel count (MATE_ERR_UNSUPPORTED for
+ * another d_state). The workspace (at least mate_bimamba_workspace_size bytes,
+ * 256-byte aligned) is scratch for the call. Other errors as mate_bissd_scan. */
+mate_status mate_bimamba_scan(const mate_ssd_tensors *t, mate_grid g, int order, const mate_mamba_desc *d,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* TESA: attention inside shifted 3D windows                                  */
 /* ------------------------------------------------------------------------ */
 /* The grid is cut into windows win_t x win_h x win_w (Tw x Sw x Sw) and every
@@ -211,7 +243,7 @@ int mate_abi_version(void);
  * of it (by any call, any stream) is bracketed by a pair of HIP events
  * recorded on the stream it is launched on. Other kernels are untouched.
  * Names: "rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb", "ssd_states",
- * "ssd_seg_pass", "ssd_out", "tesa" (unknown name: MATE_ERR_SHAPE; a timing
+ * "ssd_seg_pass", "ssd_out", "tesa", "mamba_scan" (unknown name: MATE_ERR_SHAPE; a timing
  * already armed: MATE_ERR_SHAPE).
  * mate_timing_end waits for the recorded events (a host synchronisation on
  * them), stores the number of timed launches and their summed duration in

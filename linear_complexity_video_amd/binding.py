@@ -22,7 +22,8 @@ ORDER_ZIGZAG = 4  # MATE_ORDER_ZIGZAG: the snake path; orders 0..3 are the RMS o
 EXPORTED = (
     "mate_rms_reorder", "mate_bissd_workspace_size", "mate_bissd_scan", "mate_tesa",
     "mate_forward_workspace_size", "mate_forward", "mate_status_string", "mate_last_error",
-    "mate_abi_version", "mate_timing_begin", "mate_timing_end",
+    "mate_abi_version", "mate_timing_begin", "mate_timing_end", "mate_bimamba_workspace_size",
+    "mate_bimamba_scan",
 )
 
 
@@ -47,6 +48,11 @@ class SsdDesc(ctypes.Structure):
 class SsdTensors(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p), ("dt", ctypes.c_void_p),
                 ("a", ctypes.c_void_p), ("d", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class MambaDesc(ctypes.Structure):
+    _fields_ = [("channels", ctypes.c_int32), ("d_state", ctypes.c_int32), ("pool_t", ctypes.c_int32),
+                ("pool_h", ctypes.c_int32), ("pool_w", ctypes.c_int32), ("dtype", ctypes.c_int)]
 
 
 class TesaDesc(ctypes.Structure):
@@ -77,11 +83,14 @@ def lib() -> ctypes.CDLL:
     L.mate_bissd_workspace_size.restype = SZ
     L.mate_bissd_scan.argtypes = [ctypes.POINTER(SsdTensors), Grid, I32, ctypes.POINTER(SsdDesc), P, SZ, P]
     L.mate_tesa.argtypes = [ctypes.POINTER(TesaTensors), Grid, ctypes.POINTER(TesaDesc), P]
+    L.mate_bimamba_workspace_size.argtypes = [Grid, ctypes.POINTER(MambaDesc)]
+    L.mate_bimamba_workspace_size.restype = SZ
+    L.mate_bimamba_scan.argtypes = [ctypes.POINTER(SsdTensors), Grid, I32, ctypes.POINTER(MambaDesc), P, SZ, P]
     L.mate_forward_workspace_size.argtypes = [Grid, ctypes.POINTER(SsdDesc), ctypes.POINTER(TesaDesc)]
     L.mate_forward_workspace_size.restype = SZ
     L.mate_forward.argtypes = [ctypes.POINTER(SsdTensors), ctypes.POINTER(SsdDesc), ctypes.POINTER(TesaTensors),
                                ctypes.POINTER(TesaDesc), Grid, I32, P, SZ, P]
-    for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_tesa", "mate_forward"):
+    for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_bimamba_scan", "mate_tesa", "mate_forward"):
         getattr(L, f).restype = ctypes.c_int
     L.mate_status_string.argtypes = [ctypes.c_int]
     L.mate_status_string.restype = ctypes.c_char_p
@@ -179,6 +188,30 @@ def mate_bissd_scan(x, b, c, dt, a, d, y, order: int, chunk: int, pool=(0, 0, 0)
     t = SsdTensors(_ptr(x), _ptr(b), _ptr(c), _ptr(dt), _ptr(a), _ptr(d), _ptr(y))
     _check(lib().mate_bissd_scan(ctypes.byref(t), Grid(*grid), order, ctypes.byref(desc), _ptr(workspace),
                                  workspace.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Bidirectional Mamba (selective scan)
+# ---------------------------------------------------------------------------
+
+def mamba_desc(x, b, pool=(0, 0, 0)) -> MambaDesc:
+    return MambaDesc(x.shape[-1], b.shape[-1], pool[0], pool[1], pool[2], _dtype(x))
+
+
+def mate_bimamba_workspace_size(grid, desc: MambaDesc) -> int:
+    return int(lib().mate_bimamba_workspace_size(Grid(*grid), ctypes.byref(desc)))
+
+
+def mate_bimamba_scan(x, b, c, dt, a, d, y, order: int, pool=(0, 0, 0), workspace=None, stream=None):
+    """y = bidirectional Mamba selective scan of x (channels last) in ``order`` (see include/mate.h)."""
+    _dev(x, b, c, dt, a, d, y)
+    grid = tuple(x.shape[:4])
+    desc = mamba_desc(x, b, pool)
+    if workspace is None:
+        workspace = _workspace(mate_bimamba_workspace_size(grid, desc), x)
+    t = SsdTensors(_ptr(x), _ptr(b), _ptr(c), _ptr(dt), _ptr(a), _ptr(d), _ptr(y))
+    _check(lib().mate_bimamba_scan(ctypes.byref(t), Grid(*grid), order, ctypes.byref(desc), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -37,6 +37,24 @@ struct TesaArgs {
     void *o;
 };
 
+// Validated bidirectional Mamba (selective scan) problem.
+struct MambaProblem {
+    int64_t batch, T, H, W;
+    int channels, d_state, order;
+    int pool_t, pool_h, pool_w;
+    int64_t R;  // review tokens (0 = none)
+    int dtype;  // 0 fp32, 1 bf16
+};
+
+struct MambaArgs {
+    const void *x, *b, *c;
+    const float *dt, *a, *d;
+    void *y;
+};
+
+size_t mamba_workspace(const MambaProblem &p);
+hipError_t mamba_scan(const MambaProblem &p, const MambaArgs &a, void *ws, hipStream_t st);
+
 hipError_t launch_rms_reorder(const void *src, void *dst, int64_t batch, int64_t T, int64_t H, int64_t W,
                               int64_t row_bytes, int order, int flip, int inverse, hipStream_t stream);
 

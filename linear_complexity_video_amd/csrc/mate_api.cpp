@@ -139,6 +139,34 @@ mate_status make_ssd_problem(mate_grid g, int order, const mate_ssd_desc *d, mat
     return MATE_OK;
 }
 
+// Validates the Mamba (selective scan) descriptor and fills the derived problem.
+mate_status make_mamba_problem(mate_grid g, int order, const mate_mamba_desc *d, mate::MambaProblem &p)
+{
+    if (!d) return fail(MATE_ERR_NULL, "mamba descriptor is NULL");
+    mate_status s = check_grid(g);
+    if (s != MATE_OK) return s;
+    if (order < 0 || order > MATE_ORDER_ZIGZAG) return fail(MATE_ERR_SHAPE, "order %d not in 0..4", order);
+    if (d->channels <= 0 || d->d_state <= 0) return fail(MATE_ERR_SHAPE, "channels and d_state must be positive");
+    if (!valid_dtype(d->dtype)) return fail(MATE_ERR_SHAPE, "unknown dtype %d", (int)d->dtype);
+    const bool pooled = d->pool_t || d->pool_h || d->pool_w;
+    if (pooled) {
+        if (d->pool_t <= 0 || d->pool_h <= 0 || d->pool_w <= 0)
+            return fail(MATE_ERR_SHAPE, "pool extents must be all zero or all positive");
+        if (g.T % d->pool_t || g.H % d->pool_h || g.W % d->pool_w)
+            return fail(MATE_ERR_SHAPE, "pool %dx%dx%d does not divide the grid", d->pool_t, d->pool_h, d->pool_w);
+    }
+    if (d->d_state != 8 && d->d_state != 16 && d->d_state != 32)
+        return fail(MATE_ERR_UNSUPPORTED, "d_state %d not built (8, 16 or 32)", d->d_state);
+    if ((int64_t)d->channels * g.batch * g.T * g.H * g.W >= ((int64_t)1 << 40))
+        return fail(MATE_ERR_UNSUPPORTED, "batch*tokens*channels must stay below 2^40");
+    p.batch = g.batch; p.T = g.T; p.H = g.H; p.W = g.W;
+    p.channels = d->channels; p.d_state = d->d_state; p.order = order;
+    p.pool_t = pooled ? d->pool_t : 0; p.pool_h = pooled ? d->pool_h : 0; p.pool_w = pooled ? d->pool_w : 0;
+    p.R = pooled ? (g.T / d->pool_t) * (g.H / d->pool_h) * (g.W / d->pool_w) : 0;
+    p.dtype = d->dtype == MATE_BF16 ? 1 : 0;
+    return MATE_OK;
+}
+
 mate_status make_tesa_problem(mate_grid g, const mate_tesa_desc *d, mate::TesaProblem &p, bool &fast)
 {
     if (!d) return fail(MATE_ERR_NULL, "tesa descriptor is NULL");
@@ -268,6 +296,30 @@ mate_status mate_bissd_scan(const mate_ssd_tensors *t, mate_grid g, int order, c
     hipError_t e = fast ? mate::ssd_fast(p, a, workspace, (hipStream_t)stream)
                         : mate::ssd_portable(p, a, workspace, (hipStream_t)stream);
     if (e != hipSuccess) return device_fail(e, "bissd launch");
+    return MATE_OK;
+}
+
+size_t mate_bimamba_workspace_size(mate_grid g, const mate_mamba_desc *d)
+{
+    mate::MambaProblem p;
+    if (make_mamba_problem(g, 0, d, p) != MATE_OK) return 0;
+    return mate::mamba_workspace(p);
+}
+
+mate_status mate_bimamba_scan(const mate_ssd_tensors *t, mate_grid g, int order, const mate_mamba_desc *d,
+                              void *workspace, size_t workspace_bytes, void *stream)
+{
+    mate_status s = check_ssd_tensors(t);
+    if (s != MATE_OK) return s;
+    mate::MambaProblem p;
+    if ((s = make_mamba_problem(g, order, d, p)) != MATE_OK) return s;
+    const size_t need = mate::mamba_workspace(p);
+    if (!workspace || workspace_bytes < need)
+        return fail(MATE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+    if ((uintptr_t)workspace & 255) return fail(MATE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    mate::MambaArgs a{t->x, t->b, t->c, t->dt, t->a, t->d, t->y};
+    hipError_t e = mate::mamba_scan(p, a, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "bimamba launch");
     return MATE_OK;
 }
 

@@ -16,6 +16,7 @@ enum KernelId : int {
     K_SSD_SEG_PASS,
     K_SSD_OUT,
     K_TESA,
+    K_MAMBA,
     K_COUNT
 };
 

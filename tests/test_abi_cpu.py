@@ -80,6 +80,42 @@ def _scan(t, g, order, desc, ws=0x800000, wsb=1 << 40):
     return B.lib().mate_bissd_scan(ctypes.byref(t), g, order, ctypes.byref(desc), ctypes.c_void_p(ws), wsb, None)
 
 
+def _mamba(**kw):
+    d = dict(channels=12, d_state=16, pool_t=0, pool_h=0, pool_w=0, dtype=B.MATE_BF16)
+    d.update(kw)
+    return B.MambaDesc(**d)
+
+
+def _mscan(t, g, order, desc, ws=0x800000, wsb=1 << 40):
+    return B.lib().mate_bimamba_scan(ctypes.byref(t), g, order, ctypes.byref(desc), ctypes.c_void_p(ws), wsb, None)
+
+
+def test_mamba_validation():
+    g = B.Grid(1, 2, 4, 4)
+    assert _mscan(_ssd_t(dt=0), g, 0, _mamba()) == B.MATE_ERR_NULL
+    assert B.lib().mate_bimamba_scan(ctypes.byref(_ssd_t()), g, 0, None, ctypes.c_void_p(0x800000), 1 << 40,
+                                     None) == B.MATE_ERR_NULL
+    assert _mscan(_ssd_t(), g, 5, _mamba()) == B.MATE_ERR_SHAPE
+    assert _mscan(_ssd_t(), g, B.ORDER_ZIGZAG, _mamba(), wsb=16) == B.MATE_ERR_WORKSPACE  # zigzag is accepted
+    assert _mscan(_ssd_t(), g, 0, _mamba(channels=0)) == B.MATE_ERR_SHAPE
+    assert _mscan(_ssd_t(), g, 0, _mamba(pool_t=2, pool_h=3, pool_w=2)) == B.MATE_ERR_SHAPE
+    assert _mscan(_ssd_t(), g, 0, _mamba(pool_t=2, pool_h=0, pool_w=2)) == B.MATE_ERR_SHAPE
+    assert _mscan(_ssd_t(), g, 0, _mamba(d_state=12)) == B.MATE_ERR_UNSUPPORTED
+    assert _mscan(_ssd_t(), g, 0, _mamba(dtype=7)) == B.MATE_ERR_SHAPE
+    assert _mscan(_ssd_t(x=0x100008), g, 0, _mamba()) == B.MATE_ERR_UNSUPPORTED  # misaligned x
+    assert _mscan(_ssd_t(), g, 0, _mamba(), ws=0) == B.MATE_ERR_WORKSPACE
+    assert _mscan(_ssd_t(), g, 0, _mamba(), ws=0x800010) == B.MATE_ERR_WORKSPACE
+    # workspace: a bf16 partial of y and 256 spare elements, plus the pooled review x (bf16), dt (fp32)
+    # and B (bf16) when pooled
+    n = 2 * 4 * 4
+    al = lambda v: (v + 255) // 256 * 256
+    assert B.mate_bimamba_workspace_size((1, 2, 4, 4), _mamba()) == al(n * 12 * 2) + al(256 * 2)
+    R = 1 * 2 * 2
+    assert B.mate_bimamba_workspace_size((1, 2, 4, 4), _mamba(pool_t=2, pool_h=2, pool_w=2)) == \
+        al(n * 12 * 2) + al(256 * 2) + al(R * 12 * 2) + al(R * 12 * 4) + al(R * 16 * 2)
+    assert B.mate_bimamba_workspace_size((1, 2, 4, 4), _mamba(d_state=12)) == 0
+
+
 def test_ssd_validation():
     g = B.Grid(1, 2, 4, 4)
     assert _scan(_ssd_t(y=0), g, 0, _ssd()) == B.MATE_ERR_NULL
@@ -166,6 +202,7 @@ def test_timing_arming_rules():
     assert lib.mate_timing_begin(b"tesa") == B.MATE_ERR_SHAPE      # one timing at a time
     assert lib.mate_timing_end(None, None) == B.MATE_ERR_NULL      # stays armed
     assert B.mate_timing_end() == (0, 0.0)
-    for name in ("rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb", "ssd_states", "ssd_seg_pass", "ssd_out", "tesa"):
+    for name in ("rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb", "ssd_states", "ssd_seg_pass", "ssd_out", "tesa",
+                 "mamba_scan"):
         B.mate_timing_begin(name)
         assert B.mate_timing_end() == (0, 0.0)

@@ -428,3 +428,89 @@ def test_fast_paths_deterministic():
     _, o1 = run_tesa(2, True, B.ALGO_FAST, dev)
     _, o2 = run_tesa(2, True, B.ALGO_FAST, dev)
     assert torch.equal(o1, o2)
+
+
+# ----------------------------------------------------------------------------
+# Bidirectional Mamba (selective scan), the ablation's MA-branch variant
+# ----------------------------------------------------------------------------
+
+def _mamba_inputs(rng, bsz, T, H, W, nch, S, bf16, xs=1.0, bs=1.0):
+    x = rng.standard_normal((bsz, T, H, W, nch)).astype(np.float32) * xs
+    Bm = rng.standard_normal((bsz, T, H, W, S)).astype(np.float32) * bs
+    Cm = rng.standard_normal((bsz, T, H, W, S)).astype(np.float32) * bs
+    dt = np.log1p(np.exp(rng.normal(-1, 0.5, (bsz, T, H, W, nch)))).astype(np.float32)
+    A = -np.exp(rng.uniform(0, 1, (nch, S))).astype(np.float32)
+    D = rng.standard_normal(nch).astype(np.float32)
+    if bf16:
+        x, Bm, Cm = (synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)) for a in (x, Bm, Cm))
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    dev = [torch.from_numpy(a).cuda().to(tdt) for a in (x, Bm, Cm)] + \
+          [torch.from_numpy(a).cuda() for a in (dt, A, D)]
+    return (x, Bm, Cm, dt, A, D), dev
+
+
+@pytest.mark.parametrize("S", [8, 16, 32])
+def test_mamba_fp32_every_order(oracle_mod, S):
+    """2x4x4 grid, 12 channels, 2x2x2 review pooling, fp32: every order against the oracle."""
+    rng = np.random.default_rng(40 + S)
+    host, dev = _mamba_inputs(rng, 1, 2, 4, 4, 12, S, bf16=False)
+    y = torch.full_like(dev[0], float("nan"))
+    for order in range(5):
+        say(f"mamba fp32 S{S} order{order}")
+        B.mate_bimamba_scan(*dev, y, order, (2, 2, 2))
+        want = oracle_mod.biscan1(*host, (1, 2, 4, 4), order, (2, 2, 2))
+        err = parity_error(to_f64(y), want)
+        assert err <= 1e-4, (order, err)
+
+
+@pytest.mark.parametrize("S,pool", [(16, (3, 1, 7)), (32, (3, 1, 7)), (16, (0, 0, 0))])
+def test_mamba_ragged_bf16(oracle_mod, S, pool):
+    """105 tokens (ragged last token tile), 70 channels (a partial channel block), batch 2, bf16."""
+    rng = np.random.default_rng(50 + S + pool[0])
+    host, dev = _mamba_inputs(rng, 2, 3, 5, 7, 70, S, bf16=True)
+    y = torch.full_like(dev[0], float("nan"))
+    for order in range(5):
+        say(f"mamba bf16 ragged S{S} pool{pool} order{order}")
+        B.mate_bimamba_scan(*dev, y, order, pool)
+        want = oracle_mod.biscan1(*host, (2, 3, 5, 7), order, pool)
+        err = parity_error(to_f64(y), want)
+        assert err <= 2e-2, (order, err)
+
+
+def test_mamba_deterministic():
+    rng = np.random.default_rng(60)
+    _, dev = _mamba_inputs(rng, 1, 4, 8, 8, 96, 16, bf16=True)
+    y1, y2 = torch.empty_like(dev[0]), torch.empty_like(dev[0])
+    B.mate_bimamba_scan(*dev, y1, 2, (2, 2, 2))
+    B.mate_bimamba_scan(*dev, y2, 2, (2, 2, 2))
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("order", [1, 4])
+def test_mamba_long_grid_sampled_channels(oracle_mod, order):
+    """The ablation's size: 128x48x48 tokens, 5120 channels (the MA branch's 80 x 64), d_state 16,
+    8x8x8 review pooling, bf16; channels are independent, so sampled channel slices go to the oracle."""
+    T, H, W, nch, S = 128, 48, 48, 5120, 16
+    say(f"mamba long grid order{order}")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(70 + order)
+    x = (torch.randn(1, T, H, W, nch, device=dev, generator=g) / 8).to(torch.bfloat16)
+    Bm = (torch.randn(1, T, H, W, S, device=dev, generator=g) / 4).to(torch.bfloat16)
+    Cm = (torch.randn(1, T, H, W, S, device=dev, generator=g) / 4).to(torch.bfloat16)
+    dt = torch.nn.functional.softplus(torch.randn(1, T, H, W, nch, device=dev, generator=g) * 0.5 - 2)
+    A = -torch.exp(torch.rand(nch, S, device=dev, generator=g) * 2)
+    D = torch.randn(nch, device=dev, generator=g)
+    y = torch.full_like(x, float("nan"))
+    B.mate_bimamba_scan(x, Bm, Cm, dt, A, D, y, order, (8, 8, 8))
+    torch.cuda.synchronize()
+    Bh, Ch = (t.float().cpu().numpy() for t in (Bm, Cm))
+    for lo, hi in ((0, 3), (2559, 2562), (5117, 5120)):
+        xs = x[..., lo:hi].float().cpu().numpy()
+        dts = dt[..., lo:hi].contiguous().cpu().numpy()
+        want = oracle_mod.biscan1(xs, Bh, Ch, dts, A[lo:hi].cpu().numpy(), D[lo:hi].cpu().numpy(),
+                                  (1, T, H, W), order, (8, 8, 8))
+        err = parity_error(to_f64(y[..., lo:hi]), want)
+        assert err <= 2e-2, (lo, hi, err)
+    assert not torch.isnan(y).any()
+    del x, dt, y
+    torch.cuda.empty_cache()
