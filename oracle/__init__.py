@@ -50,8 +50,11 @@ def _load():
     lib.oracle_tesa.argtypes = (
         [p, p, p, i64, i64, i64, i64] + [i32] * 8 + [ctypes.c_double, i32, i32, p, i64, i32, p]
     )
+    lib.oracle_tesa_backward.argtypes = (
+        [p, p, p, p, i64, i64, i64, i64] + [i32] * 8 + [ctypes.c_double, i32, i32, p, i64, i32, p, p, p]
+    )
     for f in ("oracle_rms_sequence", "oracle_rms_reorder", "oracle_review_pool", "oracle_bissd",
-              "oracle_biscan1", "oracle_tesa_region_counts", "oracle_tesa"):
+              "oracle_biscan1", "oracle_tesa_region_counts", "oracle_tesa", "oracle_tesa_backward"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -172,3 +175,25 @@ def tesa(q, k, v, grid, window, shift=(0, 0, 0), scale: float = 0.0, heads=None,
                              float(scale), lo, hi, rp, nr, nthreads or default_threads(), _ptr(o))
     _check(rc, "tesa")
     return o
+
+
+def tesa_backward(q, k, v, dout, grid, window, shift=(0, 0, 0), scale: float = 0.0, heads=None, regions=None,
+                  nthreads=None):
+    """Gradients (dq, dk, dv) of shifted-window attention for the upstream gradient ``dout``;
+    each [b][T][H][W][nh][d] (float64). With ``regions`` only those regions' tokens are
+    written; the rest is NaN."""
+    batch, T, H, W = grid
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    nheads, d = q.shape[-2], q.shape[-1]
+    lo, hi = heads if heads is not None else (0, nheads)
+    out = [np.full((batch, T, H, W, hi - lo, d), np.nan, dtype=np.float64) for _ in range(3)]
+    if regions is None:
+        rp, nr = None, 0
+    else:
+        reg = np.ascontiguousarray(regions, dtype=np.int64)
+        rp, nr = _ptr(reg), reg.size
+    rc = _load().oracle_tesa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), batch, T, H, W, nheads, d, *window,
+                                      *shift, float(scale), lo, hi, rp, nr, nthreads or default_threads(),
+                                      *(_ptr(a) for a in out))
+    _check(rc, "tesa_backward")
+    return tuple(out)

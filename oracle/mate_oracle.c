@@ -559,6 +559,140 @@ static void tesa_unit(void *vctx, int64_t unit)
     free(sc);
 }
 
+/* Gradients of TESA for an upstream gradient dO of the output. Inside each
+ * region, with S = scale q k^T, P = softmax over each row of S and O = P v,
+ * the chain rule through these steps gives
+ *   dv = P^T dO,  dP = dO v^T,  dS_ij = P_ij (dP_ij - sum_l P_il dP_il),
+ *   dq = scale dS k,  dk = scale dS^T q
+ * (the backward pass of softmax attention; the pages train LinGen, the
+ * xllm-io review, section 四 on training, and this is TESA's part of it). */
+int oracle_tesa_region_counts(int64_t T, int64_t H, int64_t W, int wt, int wh, int ww, int st, int sh,
+                              int sw, int64_t *counts3);
+
+typedef struct {
+    tesa_ctx f;
+    const float *dout;
+    double *dq, *dk, *dv; /* [b][N][nh][d] */
+} tesa_bwd_ctx;
+
+static void tesa_bwd_unit(void *vctx, int64_t unit)
+{
+    tesa_bwd_ctx *cb = (tesa_bwd_ctx *)vctx;
+    tesa_ctx *c = &cb->f;
+    int nh = c->head_hi - c->head_lo;
+    int64_t r_idx = unit % c->nregions;
+    int hl = (int)((unit / c->nregions) % nh);
+    int64_t b = unit / (c->nregions * nh);
+    int head = c->head_lo + hl;
+    int64_t r = c->regions ? c->regions[r_idx] : r_idx;
+    int64_t rw = r % c->nrw, rh = (r / c->nrw) % c->nrh, rt = r / (c->nrw * c->nrh);
+    int64_t want_t = c->id0t + rt, want_h = c->id0h + rh, want_w = c->id0w + rw;
+    int d = c->d;
+
+    int64_t cap = c->wt * c->wh * c->ww, m = 0;
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+    if (!tok) return;
+    for (int64_t t = 0; t < c->T; ++t) {
+        if (region_id(t, c->wt, c->st) != want_t) continue;
+        for (int64_t h = 0; h < c->H; ++h) {
+            if (region_id(h, c->wh, c->sh) != want_h) continue;
+            for (int64_t w = 0; w < c->W; ++w) {
+                if (region_id(w, c->ww, c->sw) != want_w) continue;
+                if (m < cap) tok[m] = (t * c->H + h) * c->W + w;
+                ++m;
+            }
+        }
+    }
+    if (m > cap) m = cap;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(m * m));
+    double *dP = (double *)malloc(sizeof(double) * (size_t)(m * m));
+    if (!P || !dP) { free(tok); free(P); free(dP); return; }
+#define ROW(ptr, i) ((ptr) + ((b * c->N + tok[i]) * c->nheads + head) * d)
+#define OUT(ptr, i) ((ptr) + ((b * c->N + tok[i]) * nh + hl) * d)
+    /* P: the softmax of each row of S. */
+    for (int64_t i = 0; i < m; ++i) {
+        double mx = -INFINITY, l = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            double s = 0.0;
+            for (int e = 0; e < d; ++e) s += (double)ROW(c->q, i)[e] * (double)ROW(c->k, j)[e];
+            P[i * m + j] = c->scale * s;
+            if (P[i * m + j] > mx) mx = P[i * m + j];
+        }
+        for (int64_t j = 0; j < m; ++j) {
+            P[i * m + j] = exp(P[i * m + j] - mx);
+            l += P[i * m + j];
+        }
+        for (int64_t j = 0; j < m; ++j) P[i * m + j] /= l;
+    }
+    /* dP = dO v^T, then dS (kept in dP). */
+    for (int64_t i = 0; i < m; ++i) {
+        double rowdot = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            double s = 0.0;
+            for (int e = 0; e < d; ++e) s += (double)ROW(cb->dout, i)[e] * (double)ROW(c->v, j)[e];
+            dP[i * m + j] = s;
+            rowdot += P[i * m + j] * s;
+        }
+        for (int64_t j = 0; j < m; ++j) dP[i * m + j] = P[i * m + j] * (dP[i * m + j] - rowdot);
+    }
+    for (int64_t i = 0; i < m; ++i) {
+        double *dq = OUT(cb->dq, i), *dk = OUT(cb->dk, i), *dv = OUT(cb->dv, i);
+        for (int e = 0; e < d; ++e) dq[e] = dk[e] = dv[e] = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            const double sij = dP[i * m + j], sji = dP[j * m + i], pji = P[j * m + i];
+            for (int e = 0; e < d; ++e) {
+                dq[e] += c->scale * sij * (double)ROW(c->k, j)[e];
+                dk[e] += c->scale * sji * (double)ROW(c->q, j)[e];
+                dv[e] += pji * (double)ROW(cb->dout, j)[e];
+            }
+        }
+    }
+#undef ROW
+#undef OUT
+    free(tok);
+    free(P);
+    free(dP);
+}
+
+/* dq, dk, dv [b][n][head - head_lo][e] for heads in [head_lo, head_hi), same
+ * arguments as oracle_tesa plus dout [batch][T][H][W][nheads][d]. */
+int oracle_tesa_backward(const float *q, const float *k, const float *v, const float *dout, int64_t batch,
+                         int64_t T, int64_t H, int64_t W, int nheads, int d, int wt, int wh, int ww, int st,
+                         int sh, int sw, double scale, int head_lo, int head_hi, const int64_t *regions,
+                         int64_t nregions, int nthreads, double *dq, double *dk, double *dv)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || batch <= 0 || T <= 0 || H <= 0 || W <= 0 ||
+        nheads <= 0 || d <= 0)
+        return ORACLE_EINVAL;
+    if (head_lo < 0 || head_hi > nheads || head_lo >= head_hi) return ORACLE_EINVAL;
+    if (T % wt || H % wh || W % ww) return ORACLE_EINVAL;
+    int64_t counts[3];
+    int rc = oracle_tesa_region_counts(T, H, W, wt, wh, ww, st, sh, sw, counts);
+    if (rc) return rc;
+    int64_t total_regions = counts[0] * counts[1] * counts[2];
+    if (regions) {
+        for (int64_t i = 0; i < nregions; ++i)
+            if (regions[i] < 0 || regions[i] >= total_regions) return ORACLE_EINVAL;
+    } else {
+        nregions = total_regions;
+    }
+    if (nregions <= 0) return ORACLE_OK;
+    tesa_bwd_ctx cb;
+    tesa_ctx *c = &cb.f;
+    c->q = q; c->k = k; c->v = v;
+    c->batch = batch; c->T = T; c->H = H; c->W = W; c->N = T * H * W;
+    c->nheads = nheads; c->d = d; c->head_lo = head_lo; c->head_hi = head_hi;
+    c->wt = wt; c->wh = wh; c->ww = ww; c->st = st; c->sh = sh; c->sw = sw;
+    c->id0t = region_id(0, wt, st); c->id0h = region_id(0, wh, sh); c->id0w = region_id(0, ww, sw);
+    c->nrt = counts[0]; c->nrh = counts[1]; c->nrw = counts[2];
+    c->regions = regions; c->nregions = nregions;
+    c->scale = scale > 0 ? scale : 1.0 / sqrt((double)d);
+    c->o = NULL;
+    cb.dout = dout; cb.dq = dq; cb.dk = dk; cb.dv = dv;
+    run_units(tesa_bwd_unit, &cb, batch * (int64_t)(head_hi - head_lo) * nregions, nthreads);
+    return ORACLE_OK;
+}
+
 /* Number of regions along each axis (useful to build region lists). */
 int oracle_tesa_region_counts(int64_t T, int64_t H, int64_t W, int wt, int wh, int ww, int st, int sh,
                               int sw, int64_t *counts3)

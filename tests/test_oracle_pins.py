@@ -538,3 +538,76 @@ def test_tesa_rejects_bad_shift(oracle_mod):
     q = np.zeros((1, 2, 2, 2, 1, 2), np.float32)
     with pytest.raises(ValueError):
         oracle_mod.tesa(q, q, q, (1, 2, 2, 2), (2, 2, 2), (2, 0, 0))
+
+
+# ----------------------------------------------------------------------------
+# TESA backward
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window,shift", [((2, 2, 2), (0, 0, 0)), ((2, 2, 2), (1, 1, 1))])
+def test_tesa_backward_equals_central_differences(oracle_mod, window, shift):
+    # L = sum(dO * O); every input element is moved by +-2^-10 on values that are multiples of 2^-12,
+    # so the moved inputs are exact in float32 and the central difference is exact up to O(eps^2).
+    rng = np.random.default_rng(80)
+    T, H, W, nh, d = 2, 2, 4, 2, 3
+    grid = (1, T, H, W)
+    q, k, v = (np.round(rng.standard_normal((1, T, H, W, nh, d)) * 4096) / 4096 for _ in range(3))
+    q, k, v = (a.astype(np.float32) for a in (q, k, v))
+    dout = rng.standard_normal((1, T, H, W, nh, d))
+    got = oracle_mod.tesa_backward(q, k, v, dout.astype(np.float32), grid, window, shift)
+    dout32 = dout.astype(np.float32).astype(np.float64)
+    eps = 2.0 ** -10
+    for which, base in enumerate((q, k, v)):
+        num = np.zeros(base.shape)
+        for idx in np.ndindex(base.shape):
+            vals = []
+            for sgn in (1, -1):
+                moved = base.copy()
+                moved[idx] += sgn * eps
+                args = [q, k, v]
+                args[which] = moved
+                vals.append(float(np.sum(dout32 * oracle_mod.tesa(*args, grid, window, shift))))
+            num[idx] = (vals[0] - vals[1]) / (2 * eps)
+        assert relerr(got[which], num) < 1e-5, which
+
+
+@pytest.mark.parametrize("window,shift", [((2, 2, 2), (1, 1, 1)), ((4, 2, 4), (2, 1, 3))])
+def test_tesa_backward_equals_autograd_of_swin_masked_attention(oracle_mod, window, shift):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(81)
+    T, H, W, nh, d = 4, 4, 8, 2, 5
+    q, k, v, dout = (rng.standard_normal((1, T, H, W, nh, d)).astype(np.float32) for _ in range(4))
+    got = oracle_mod.tesa_backward(q, k, v, dout, (1, T, H, W), window, shift)
+    mask = torch.from_numpy(swin_same_window(T, H, W, window, shift))
+    N = T * H * W
+    for h in range(nh):
+        tq, tk, tv = (torch.tensor(a.reshape(N, nh, d)[:, h].astype(np.float64), requires_grad=True)
+                      for a in (q, k, v))
+        s = (tq @ tk.T) / np.sqrt(d)
+        o = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=1) @ tv
+        o.backward(torch.from_numpy(dout.reshape(N, nh, d)[:, h].astype(np.float64)))
+        for g, t in zip(got, (tq, tk, tv)):
+            np.testing.assert_allclose(g.reshape(N, nh, d)[:, h], t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_tesa_backward_special_cases(oracle_mod):
+    rng = np.random.default_rng(82)
+    q, k, v, dout = (rng.standard_normal((1, 2, 3, 4, 2, 3)).astype(np.float32) for _ in range(4))
+    # a window of one token: O = v, so dv = dO and nothing flows to q or k
+    dq, dk, dv = oracle_mod.tesa_backward(q, k, v, dout, (1, 2, 3, 4), (1, 1, 1))
+    np.testing.assert_array_equal(dv, dout.astype(np.float64))
+    np.testing.assert_array_equal(dq, 0.0)
+    np.testing.assert_array_equal(dk, 0.0)
+    # v = 1: dP_ij = sum of dO_i for every key j, so every row of dS is P_i (c_i - c_i) = 0 and no
+    # gradient reaches q or k
+    dq, dk, dv = oracle_mod.tesa_backward(q, k, np.ones_like(v), dout, (1, 2, 3, 4), (2, 3, 4))
+    np.testing.assert_allclose(dq, 0.0, atol=1e-13)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-13)
+    # region subsets: only the listed regions are written, and equal the full result there
+    full = oracle_mod.tesa_backward(q, k, v, dout, (1, 2, 3, 4), (2, 3, 2), (1, 1, 1))
+    sub = oracle_mod.tesa_backward(q, k, v, dout, (1, 2, 3, 4), (2, 3, 2), (1, 1, 1), regions=[0, 3])
+    for f, s_ in zip(full, sub):
+        written = ~np.isnan(s_)
+        assert written.any() and not written.all()
+        np.testing.assert_array_equal(s_[written], f[written])
+
