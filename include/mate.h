@@ -212,6 +212,29 @@ typedef struct {
  * whole grid (full attention over all T*H*W tokens, any size). */
 mate_status mate_tesa(const mate_tesa_tensors *t, mate_grid g, const mate_tesa_desc *d, void *stream);
 
+/* Backward of mate_tesa for an upstream gradient dout of its output o. Inside
+ * each window, with S = scale q k^T, P = softmax of each row of S and o = P v:
+ *   dv = P^T dout,  dP = dout v^T,  dS_ij = P_ij (dP_ij - sum_l P_il dP_il),
+ *   dq = scale dS k,  dk = scale dS^T q
+ * (the chain rule through TESA, the attention half of training the MATE block;
+ * the xllm-io review, section 四, trains LinGen end to end). The forward output
+ * is not an input: the kernels recompute P. All seven tensors are
+ * [batch][T][H][W][nheads][headdim] in the descriptor's dtype, 16-byte aligned;
+ * dq, dk, dv are written whole and must not overlap the inputs. */
+typedef struct {
+    const void *q, *k, *v, *dout;
+    void *dq, *dk, *dv;
+} mate_tesa_grad_tensors;
+
+/* Bytes of workspace (256-byte aligned device memory, scratch for the call):
+ * two floats per token and head. 0 when the descriptor is invalid or not built. */
+size_t mate_tesa_backward_workspace_size(mate_grid g, const mate_tesa_desc *d);
+
+/* Supported: bf16, headdim 64 or 128, windows of at most 4096 tokens
+ * (MATE_ERR_UNSUPPORTED otherwise). Other errors as mate_tesa. */
+mate_status mate_tesa_backward(const mate_tesa_grad_tensors *t, mate_grid g, const mate_tesa_desc *d,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* One MATE core forward                                                     */
 /* ------------------------------------------------------------------------ */
@@ -243,7 +266,8 @@ int mate_abi_version(void);
  * of it (by any call, any stream) is bracketed by a pair of HIP events
  * recorded on the stream it is launched on. Other kernels are untouched.
  * Names: "rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb", "ssd_states",
- * "ssd_seg_pass", "ssd_out", "tesa", "mamba_scan" (unknown name: MATE_ERR_SHAPE; a timing
+ * "ssd_seg_pass", "ssd_out", "tesa", "mamba_scan", "tesa_backward" (unknown name:
+ * MATE_ERR_SHAPE; a timing
  * already armed: MATE_ERR_SHAPE).
  * mate_timing_end waits for the recorded events (a host synchronisation on
  * them), stores the number of timed launches and their summed duration in

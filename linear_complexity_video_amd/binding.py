@@ -23,7 +23,7 @@ EXPORTED = (
     "mate_rms_reorder", "mate_bissd_workspace_size", "mate_bissd_scan", "mate_tesa",
     "mate_forward_workspace_size", "mate_forward", "mate_status_string", "mate_last_error",
     "mate_abi_version", "mate_timing_begin", "mate_timing_end", "mate_bimamba_workspace_size",
-    "mate_bimamba_scan",
+    "mate_bimamba_scan", "mate_tesa_backward_workspace_size", "mate_tesa_backward",
 )
 
 
@@ -66,6 +66,10 @@ class TesaTensors(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("o", ctypes.c_void_p)]
 
 
+class TesaGradTensors(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "dout", "dq", "dk", "dv")]
+
+
 _lib = None
 
 
@@ -83,6 +87,9 @@ def lib() -> ctypes.CDLL:
     L.mate_bissd_workspace_size.restype = SZ
     L.mate_bissd_scan.argtypes = [ctypes.POINTER(SsdTensors), Grid, I32, ctypes.POINTER(SsdDesc), P, SZ, P]
     L.mate_tesa.argtypes = [ctypes.POINTER(TesaTensors), Grid, ctypes.POINTER(TesaDesc), P]
+    L.mate_tesa_backward_workspace_size.argtypes = [Grid, ctypes.POINTER(TesaDesc)]
+    L.mate_tesa_backward_workspace_size.restype = SZ
+    L.mate_tesa_backward.argtypes = [ctypes.POINTER(TesaGradTensors), Grid, ctypes.POINTER(TesaDesc), P, SZ, P]
     L.mate_bimamba_workspace_size.argtypes = [Grid, ctypes.POINTER(MambaDesc)]
     L.mate_bimamba_workspace_size.restype = SZ
     L.mate_bimamba_scan.argtypes = [ctypes.POINTER(SsdTensors), Grid, I32, ctypes.POINTER(MambaDesc), P, SZ, P]
@@ -90,7 +97,8 @@ def lib() -> ctypes.CDLL:
     L.mate_forward_workspace_size.restype = SZ
     L.mate_forward.argtypes = [ctypes.POINTER(SsdTensors), ctypes.POINTER(SsdDesc), ctypes.POINTER(TesaTensors),
                                ctypes.POINTER(TesaDesc), Grid, I32, P, SZ, P]
-    for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_bimamba_scan", "mate_tesa", "mate_forward"):
+    for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_bimamba_scan", "mate_tesa", "mate_tesa_backward",
+              "mate_forward"):
         getattr(L, f).restype = ctypes.c_int
     L.mate_status_string.argtypes = [ctypes.c_int]
     L.mate_status_string.restype = ctypes.c_char_p
@@ -229,6 +237,22 @@ def mate_tesa(q, k, v, o, window, shift=(0, 0, 0), scale: float = 0.0, algo: int
     desc = tesa_desc(q, window, shift, scale, algo)
     t = TesaTensors(_ptr(q), _ptr(k), _ptr(v), _ptr(o))
     _check(lib().mate_tesa(ctypes.byref(t), grid_of(q), ctypes.byref(desc), _stream(stream)))
+
+
+def mate_tesa_backward_workspace_size(grid, desc: TesaDesc) -> int:
+    return int(lib().mate_tesa_backward_workspace_size(Grid(*grid), ctypes.byref(desc)))
+
+
+def mate_tesa_backward(q, k, v, dout, dq, dk, dv, window, shift=(0, 0, 0), scale: float = 0.0, workspace=None,
+                       stream=None):
+    """(dq, dk, dv) of mate_tesa for the upstream gradient dout (see include/mate.h)."""
+    _dev(q, k, v, dout, dq, dk, dv)
+    desc = tesa_desc(q, window, shift, scale)
+    if workspace is None:
+        workspace = _workspace(mate_tesa_backward_workspace_size(tuple(q.shape[:4]), desc), q)
+    t = TesaGradTensors(*(_ptr(a) for a in (q, k, v, dout, dq, dk, dv)))
+    _check(lib().mate_tesa_backward(ctypes.byref(t), grid_of(q), ctypes.byref(desc), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

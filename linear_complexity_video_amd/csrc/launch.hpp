@@ -37,6 +37,11 @@ struct TesaArgs {
     void *o;
 };
 
+struct TesaGradArgs {
+    const void *q, *k, *v, *dout;
+    void *dq, *dk, *dv;
+};
+
 // Validated bidirectional Mamba (selective scan) problem.
 struct MambaProblem {
     int64_t batch, T, H, W;
@@ -73,5 +78,9 @@ hipError_t tesa_portable(const TesaProblem &p, const TesaArgs &a, hipStream_t st
 
 bool tesa_fast_supports(const TesaProblem &p);
 hipError_t tesa_fast(const TesaProblem &p, const TesaArgs &a, hipStream_t st);
+
+bool tesa_backward_supports(const TesaProblem &p);
+size_t tesa_backward_workspace(const TesaProblem &p);
+hipError_t tesa_backward(const TesaProblem &p, const TesaGradArgs &a, void *ws, hipStream_t st);
 
 } // namespace mate

@@ -337,6 +337,39 @@ mate_status mate_tesa(const mate_tesa_tensors *t, mate_grid g, const mate_tesa_d
     return MATE_OK;
 }
 
+size_t mate_tesa_backward_workspace_size(mate_grid g, const mate_tesa_desc *d)
+{
+    mate::TesaProblem p;
+    bool fast = false;
+    if (make_tesa_problem(g, d, p, fast) != MATE_OK || !mate::tesa_backward_supports(p)) return 0;
+    return mate::tesa_backward_workspace(p);
+}
+
+mate_status mate_tesa_backward(const mate_tesa_grad_tensors *t, mate_grid g, const mate_tesa_desc *d,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!t) return fail(MATE_ERR_NULL, "tesa gradient tensors struct is NULL");
+    if (!t->q || !t->k || !t->v || !t->dout || !t->dq || !t->dk || !t->dv)
+        return fail(MATE_ERR_NULL, "a tesa gradient tensor pointer (q, k, v, dout, dq, dk, dv) is NULL");
+    if (((uintptr_t)t->q | (uintptr_t)t->k | (uintptr_t)t->v | (uintptr_t)t->dout | (uintptr_t)t->dq |
+         (uintptr_t)t->dk | (uintptr_t)t->dv) & 15)
+        return fail(MATE_ERR_UNSUPPORTED, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
+    mate::TesaProblem p;
+    bool fast = false;
+    mate_status s = make_tesa_problem(g, d, p, fast);
+    if (s != MATE_OK) return s;
+    if (!mate::tesa_backward_supports(p))
+        return fail(MATE_ERR_UNSUPPORTED, "tesa backward is built for bf16, headdim 64 or 128, windows of at most 4096 tokens");
+    const size_t need = mate::tesa_backward_workspace(p);
+    if (!workspace || workspace_bytes < need)
+        return fail(MATE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+    if ((uintptr_t)workspace & 255) return fail(MATE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    mate::TesaGradArgs a{t->q, t->k, t->v, t->dout, t->dq, t->dk, t->dv};
+    hipError_t e = mate::tesa_backward(p, a, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "tesa backward launch");
+    return MATE_OK;
+}
+
 size_t mate_forward_workspace_size(mate_grid g, const mate_ssd_desc *sd, const mate_tesa_desc *td)
 {
     mate::TesaProblem tp;

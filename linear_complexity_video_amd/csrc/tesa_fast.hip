@@ -23,19 +23,12 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "tesa_common.hpp"
 #include "timing.hpp"
 
 namespace mate {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int KT = 64;            // keys per LDS tile
 constexpr int QW = 32;            // queries per wave
@@ -43,21 +36,6 @@ constexpr int NWAVE = 8;          // waves per workgroup
 constexpr int QB = QW * NWAVE;    // queries per workgroup
 constexpr int KPAD = 8;           // K tile row padding (bf16)
 constexpr int VPAD = 32;          // V tile row padding (bf16): spreads transpose reads over the banks
-
-__device__ __forceinline__ void region_extent(int r, int D, int w, int s, int &lo, int &hi)
-{
-    if (s == 0) {
-        lo = r * w;
-        hi = lo + w;
-    } else if (r == 0) {
-        lo = 0;
-        hi = s;
-    } else {
-        lo = s + (r - 1) * w;
-        hi = lo + w;
-    }
-    if (hi > D) hi = D;
-}
 
 constexpr int MAXW = 4096;        // largest window (tokens) of the MFMA kernel
 
@@ -68,34 +46,6 @@ struct __attribute__((aligned(16))) Smem {
     __bf16 ostage[8][32 * (DH == 128 ? 64 : 32)];  // per wave: output rows on their way out
     uint32_t row[ROWS];           // canonical token of each window position
 };
-
-// A operand of O^T += V^T P^T from the row-major V tile: lane l gets column
-// (value dim) n_base + l % 32 at keys k_base + 4 (l / 32) + {0..3} and
-// k_base + 8 + 4 (l / 32) + {0..3}, the key order of the P^T fragment.
-template <int LD>
-__device__ __forceinline__ bf16x8 v_frag(const __bf16 *tile, int k_base, int n_base)
-{
-    const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
-    const __bf16 *p = tile + (k_base + 4 * (g >> 1) + (s >> 2)) * LD + n_base + 16 * (g & 1) + 4 * (s & 3);
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
-    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * LD));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// a / d for 0 <= a, d < 2^22 from a float reciprocal of d: the estimate is
-// within one of the quotient, and one correction step makes it exact.
-__device__ __forceinline__ int div_small(int a, int d, float inv_d)
-{
-    int qt = (int)((float)a * inv_d);
-    const int r = a - qt * d;
-    qt += (r >= d) - (r < 0);
-    return qt;
-}
 
 // One work item: a (batch, head, region, query block) and what the kernel
 // derives from it.

@@ -25,7 +25,8 @@ bool g_open = false;         // a begin is recorded without its end
 hipError_t g_error = hipSuccess;
 
 const char *const kNames[K_COUNT] = {"rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb",
-                                     "ssd_states", "ssd_seg_pass", "ssd_out", "tesa", "mamba_scan"};
+                                     "ssd_states", "ssd_seg_pass", "ssd_out", "tesa", "mamba_scan",
+                                     "tesa_backward"};
 
 } // namespace
 

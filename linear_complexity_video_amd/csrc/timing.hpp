@@ -17,6 +17,7 @@ enum KernelId : int {
     K_SSD_OUT,
     K_TESA,
     K_MAMBA,
+    K_TESA_BWD,
     K_COUNT
 };
 

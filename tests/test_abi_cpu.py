@@ -116,6 +116,28 @@ def test_mamba_validation():
     assert B.mate_bimamba_workspace_size((1, 2, 4, 4), _mamba(d_state=12)) == 0
 
 
+def test_tesa_backward_validation():
+    lib = B.lib()
+    g = B.Grid(1, 4, 4, 4)
+    desc = lambda **kw: B.TesaDesc(**{**dict(nheads=2, headdim=64, win_t=2, win_h=2, win_w=2, shift_t=0, shift_h=0,
+                                             shift_w=0, scale=0.0, dtype=B.MATE_BF16, algo=B.ALGO_AUTO), **kw})
+    ptrs = {n: 0x100000 + 0x1000 * i for i, n in enumerate(("q", "k", "v", "dout", "dq", "dk", "dv"))}
+    t = lambda **kw: B.TesaGradTensors(**{**ptrs, **kw})
+    call = lambda tt, dd, ws=0x800000, wsb=1 << 40: lib.mate_tesa_backward(ctypes.byref(tt), g, ctypes.byref(dd),
+                                                                           ctypes.c_void_p(ws), wsb, None)
+    assert call(t(dout=0), desc()) == B.MATE_ERR_NULL
+    assert call(t(dq=0x100008), desc()) == B.MATE_ERR_UNSUPPORTED           # misaligned
+    assert call(t(), desc(win_t=3)) == B.MATE_ERR_SHAPE                     # does not divide the grid
+    assert call(t(), desc(shift_t=2)) == B.MATE_ERR_SHAPE                   # shift not below the window
+    assert call(t(), desc(headdim=32)) == B.MATE_ERR_UNSUPPORTED
+    assert call(t(), desc(dtype=B.MATE_F32)) == B.MATE_ERR_UNSUPPORTED
+    assert call(t(), desc(), wsb=16) == B.MATE_ERR_WORKSPACE
+    assert call(t(), desc(), ws=0x800010) == B.MATE_ERR_WORKSPACE
+    # two floats per token and head
+    assert B.mate_tesa_backward_workspace_size((1, 4, 4, 4), desc()) == 64 * 2 * 8
+    assert B.mate_tesa_backward_workspace_size((1, 4, 4, 4), desc(headdim=32)) == 0
+
+
 def test_ssd_validation():
     g = B.Grid(1, 2, 4, 4)
     assert _scan(_ssd_t(y=0), g, 0, _ssd()) == B.MATE_ERR_NULL
@@ -203,6 +225,6 @@ def test_timing_arming_rules():
     assert lib.mate_timing_end(None, None) == B.MATE_ERR_NULL      # stays armed
     assert B.mate_timing_end() == (0, 0.0)
     for name in ("rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb", "ssd_states", "ssd_seg_pass", "ssd_out", "tesa",
-                 "mamba_scan"):
+                 "mamba_scan", "tesa_backward"):
         B.mate_timing_begin(name)
         assert B.mate_timing_end() == (0, 0.0)

@@ -514,3 +514,75 @@ def test_mamba_long_grid_sampled_channels(oracle_mod, order):
     assert not torch.isnan(y).any()
     del x, dt, y
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# TESA backward
+# ----------------------------------------------------------------------------
+
+def _bf16_host(rng, shape, scale=1.0):
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32)))
+
+
+def _tesa_grads(q, k, v, dout, window, shift):
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    B.mate_tesa_backward(q, k, v, dout, dq, dk, dv, window, shift)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("window,shift", [((3, 5, 7), (0, 0, 0)), ((3, 5, 7), (1, 2, 3))])
+def test_tesa_backward_ragged_windows(oracle_mod, d, window, shift):
+    """105-token windows (a ragged second tile) and, shifted, edge regions of 1 to 70 tokens; batch 2."""
+    rng = np.random.default_rng(90 + d)
+    grid = (2, 3, 5, 7)
+    host = [_bf16_host(rng, (2, 3, 5, 7, 3, d)) for _ in range(4)]
+    q, k, v, dout = (torch.from_numpy(a).cuda().to(torch.bfloat16) for a in host)
+    say(f"tesa backward d{d} window{window} shift{shift}")
+    got = _tesa_grads(q, k, v, dout, window, shift)
+    want = oracle_mod.tesa_backward(*host, grid, window, shift)
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        err = parity_error(to_f64(g), w)
+        say(f"  {name} err={err:.3e}")
+        assert err <= 2e-2, (name, err)
+
+
+def test_tesa_backward_full_window_shifted(oracle_mod):
+    """512-token windows (8 key tiles, two query blocks, four key blocks), shift (4,4,4), d 128."""
+    rng = np.random.default_rng(93)
+    grid, window, shift = (1, 16, 16, 16), (8, 8, 8), (4, 4, 4)
+    host = [_bf16_host(rng, (1, 16, 16, 16, 2, 128), 128 ** -0.25) for _ in range(3)] + \
+           [_bf16_host(rng, (1, 16, 16, 16, 2, 128))]
+    q, k, v, dout = (torch.from_numpy(a).cuda().to(torch.bfloat16) for a in host)
+    say("tesa backward 512-token windows")
+    got = _tesa_grads(q, k, v, dout, window, shift)
+    want = oracle_mod.tesa_backward(*host, grid, window, shift)
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        err = parity_error(to_f64(g), w)
+        say(f"  {name} err={err:.3e}")
+        assert err <= 2e-2, (name, err)
+
+
+@pytest.mark.parametrize("cfg,shifted", [(2, True), (4, False), (4, True)])
+def test_tesa_backward_sampled(oracle_mod, cfg, shifted):
+    """The workloads' grids and widths (20 heads of 128, 8x8x8 windows): sampled windows and heads."""
+    wl = WORKLOADS[cfg]
+    say(f"tesa backward cfg{cfg} shifted={shifted} (sampled)")
+    inp, d = tesa_device(cfg)
+    g = torch.Generator(device="cuda").manual_seed(94 + cfg)
+    dout = torch.randn(d["q"].shape, device="cuda", generator=g).to(torch.bfloat16)
+    shift = wl.layer_shift(shifted)
+    got = _tesa_grads(d["q"], d["k"], d["v"], dout, wl.window, shift)
+    for t in got:
+        assert not torch.isnan(t).any().item(), "unwritten gradients"
+    regions = sample_regions(oracle_mod.tesa_region_counts(wl.T, wl.H, wl.W, wl.window, shift))
+    for lo, hi in ((0, 1), (wl.t_heads - 1, wl.t_heads)):
+        args = [f32_of(inp[n], (lo, hi)) for n in ("q", "k", "v")] + \
+               [np.ascontiguousarray(dout[..., lo:hi, :].float().cpu().numpy())]
+        want = oracle_mod.tesa_backward(*args, wl.grid, wl.window, shift, regions=regions)
+        for name, gt, w in zip(("dq", "dk", "dv"), got, want):
+            mask = ~np.isnan(w)
+            err = parity_error(to_f64(gt[..., lo:hi, :])[mask], w[mask])
+            say(f"  heads {lo}:{hi} {name} err={err:.3e}")
+            assert err <= 2e-2, (lo, name, err)
