@@ -301,6 +301,49 @@ def table2_variants(torch, np, B, wl, ssd, att, ws, reps, algo):
                       "variants": rows}), flush=True)
 
 
+def tesa_backward_bench(torch, np, B, wl, att, reps):
+    """Per-layer time of TESA's backward (`mate_tesa_backward`: dq, dk, dv for an upstream gradient) beside
+    its forward, unshifted and shifted, on the workload's q, k, v. Algorithmic work: the forward's two
+    products per in-window pair (4 d flops), the backward's five (recomputed scores, dP, dV, dQ, dK: 10 d
+    flops). Prints one JSON line."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, reps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    g = torch.Generator(device=att["q"].device).manual_seed(11)
+    dout = (torch.randn(att["q"].shape, device=att["q"].device, generator=g) / 11.3).to(att["q"].dtype)
+    dq, dk, dv = (torch.empty_like(att["q"]) for _ in range(3))
+    ws = torch.empty(max(1, B.mate_tesa_backward_workspace_size(wl.grid, B.tesa_desc(att["q"], wl.window))),
+                     dtype=torch.uint8, device=att["q"].device)
+    rows = {}
+    for shifted in (False, True):
+        shift = wl.layer_shift(shifted)
+        pairs = tesa_pairs(wl, shift) * wl.batch * wl.t_heads
+        log(f"tesa backward: shift {shift}")
+        tf = timed(lambda: B.mate_tesa(att["q"], att["k"], att["v"], att["o"], wl.window, shift))
+        tb = timed(lambda: B.mate_tesa_backward(att["q"], att["k"], att["v"], dout, dq, dk, dv, wl.window, shift,
+                                                workspace=ws))
+        ff, fb = 4.0 * wl.t_dim * pairs, 10.0 * wl.t_dim * pairs
+        rows["shifted" if shifted else "unshifted"] = {
+            "forward_ms": tf, "backward_ms": tb, "backward_over_forward": tb / tf,
+            "forward_tflops": ff / tf / 1e9, "backward_tflops": fb / tb / 1e9,
+            "backward_mfma_frac": fb / tb / 1e9 / PEAK_BF16_TFLOPS}
+    print(json.dumps({"metric": "TESA backward vs forward per layer (one MI355X)", "unit": "ms", "data": "synthetic",
+                      "config": {"workload": wl.name, "grid": list(wl.grid), "heads": wl.t_heads,
+                                 "head_dim": wl.t_dim, "window": list(wl.window)}, "layers": rows}), flush=True)
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
@@ -318,6 +361,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed repetitions of each single call")
     ap.add_argument("--scaling", action="store_true",
                     help="instead of the throughput line: MATE core vs full attention per layer as T grows")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the throughput line: TESA's backward beside its forward, per layer")
     ap.add_argument("--variants", action="store_true",
                     help="instead of the throughput line: per-layer time of the ablation variants (zigzag scan, "
                          "no review tokens, each branch alone)")
@@ -371,6 +416,9 @@ def main():
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s; workspace {ws.numel() / 2**30:.2f} GiB")
     if args.variants:
         table2_variants(torch, np, B, wl, ssd, att, ws, args.kernel_reps, algo)
+        return
+    if args.backward:
+        tesa_backward_bench(torch, np, B, wl, att, args.kernel_reps)
         return
 
     def layer(order, shifted):
