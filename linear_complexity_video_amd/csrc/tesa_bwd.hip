@@ -16,10 +16,12 @@
 //    delta (online, against a running maximum); the second forms P^T, dP^T = V dO^T and
 //    dS^T, and accumulates dQ^T += K^T dS^T. It also stores (log-sum-exp, delta) per
 //    query for the second kernel.
-//  - k_tesa_bwd_dkdv: 4 waves (one per SIMD: K, V and both accumulator sets take more
-//    than the 256 registers of two waves), each 32 keys, one per lane column (S = Q K^T): per query
-//    tile it forms P, dP = dO V^T and dS, and accumulates dV^T += dO^T P and
-//    dK^T += Q^T dS, the transposed tiles read with the LDS transpose read.
+//  - k_tesa_bwd_dkdv<DK>: 8 waves, each 32 keys, one per lane column (S = Q K^T): per
+//    query tile it forms P and accumulates dV^T += dO^T P (DK false), or forms P,
+//    dP = dO V^T and dS and accumulates dK^T += Q^T dS (DK true), the transposed
+//    tiles read with the LDS transpose read. dV and dK are two launches: together
+//    (K, V and both accumulator sets) they need more than the 256 registers of two
+//    waves per SIMD, and one wave per SIMD ran slower than recomputing the scores.
 // Key or query tiles of 64 rows pass through LDS, the next tile's rows loading
 // into registers while the current one is used.
 #include "common.hpp"
@@ -32,7 +34,7 @@ namespace {
 
 constexpr int BT = 64;        // rows (keys or queries) per LDS tile
 constexpr int NTQ = 512;      // threads of the dQ kernel (8 waves x 32 queries)
-constexpr int NTK = 256;      // threads of the dK/dV kernel (4 waves x 32 keys)
+constexpr int NTK = 512;      // threads of the dK and dV kernels (8 waves x 32 keys)
 constexpr int BPAD = 8;       // tile row padding (bf16)
 constexpr int BMAXW = 4096;   // largest window
 
@@ -265,11 +267,11 @@ __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ 
     }
 }
 
-template <int DH>
+template <int DH, bool DK>
 __global__ __launch_bounds__(NTK) void k_tesa_bwd_dkdv(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                                                        const __bf16 *__restrict__ v, const __bf16 *__restrict__ dout,
-                                                       const float2 *__restrict__ stats, __bf16 *__restrict__ dk,
-                                                       __bf16 *__restrict__ dv, int nheads, int Tn, int Hn, int Wn,
+                                                       const float2 *__restrict__ stats, __bf16 *__restrict__ dout_kv,
+                                                       int nheads, int Tn, int Hn, int Wn,
                                                        int wt, int wh, int ww, int st, int sh, int sw, int nrh,
                                                        int nrw, int nrb, float scale, float c_log2)
 {
@@ -290,14 +292,14 @@ __global__ __launch_bounds__(NTK) void k_tesa_bwd_dkdv(const __bf16 *__restrict_
     const int kj = k_base + wave * 32 + col;
     const bool kvalid = kj < X.m;
     const size_t koff = X.head_off + (size_t)row[kvalid ? kj : 0] * rowstride;
-    bf16x8 kf[DH / 16], vf[DH / 16];
+    bf16x8 kf[DH / 16], vf[DK ? DH / 16 : 1];
     row_frags<DH>(k + koff, kf);
-    row_frags<DH>(v + koff, vf);
+    if constexpr (DK) row_frags<DH>(v + koff, vf);
 
     const int ntile = (X.m + BT - 1) / BT;
-    f32x16 dka[DH / 32], dva[DH / 32];
+    f32x16 acc[DH / 32];
 #pragma unroll
-    for (int i = 0; i < DH / 32; ++i) dka[i] = dva[i] = f32x16{};
+    for (int i = 0; i < DH / 32; ++i) acc[i] = f32x16{};
     TilePair<DH, NTK> tp;
     float2 stv = make_float2(0.f, 0.f);
     auto fetch_stats = [&](int base) {
@@ -320,14 +322,14 @@ __global__ __launch_bounds__(NTK) void k_tesa_bwd_dkdv(const __bf16 *__restrict_
             tp.fetch(q, dout, row, X, (qt + 1) * BT, rowstride);
             fetch_stats((qt + 1) * BT);
         }
-        bf16x8 pf[4], dsh[4], dsl[4];
+        bf16x8 pf[DK ? 1 : 4], dsh[DK ? 4 : 1], dsl[DK ? 4 : 1];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int kb = 0; kb < DH / 16; ++kb) {
                 s = mfma(*(const bf16x8 *)&qs[32 * sub + col][16 * kb + 8 * half], kf[kb], s);
-                dp = mfma(*(const bf16x8 *)&dos[32 * sub + col][16 * kb + 8 * half], vf[kb], dp);
+                if constexpr (DK) dp = mfma(*(const bf16x8 *)&dos[32 * sub + col][16 * kb + 8 * half], vf[kb], dp);
             }
             // rows of the accumulators: queries 32 sub + 8 i + 4 half + j of this tile
 #pragma unroll
@@ -340,11 +342,14 @@ __global__ __launch_bounds__(NTK) void k_tesa_bwd_dkdv(const __bf16 *__restrict_
                     const int rr = 4 * i + j;
                     const bool ok = qt * BT + ql + j < X.m;
                     const float p = ok ? __builtin_amdgcn_exp2f(s[rr] * c_log2 - lv[j]) : 0.f;
-                    const float dsv = p * (dp[rr] - dvv[j]);
-                    const __bf16 hi = (__bf16)dsv;
-                    pf[2 * sub + (rr >> 3)][rr & 7] = (__bf16)p;
-                    dsh[2 * sub + (rr >> 3)][rr & 7] = hi;
-                    dsl[2 * sub + (rr >> 3)][rr & 7] = (__bf16)(dsv - (float)hi);
+                    if constexpr (DK) {
+                        const float dsv = p * (dp[rr] - dvv[j]);
+                        const __bf16 hi = (__bf16)dsv;
+                        dsh[2 * sub + (rr >> 3)][rr & 7] = hi;
+                        dsl[2 * sub + (rr >> 3)][rr & 7] = (__bf16)(dsv - (float)hi);
+                    } else {
+                        pf[2 * sub + (rr >> 3)][rr & 7] = (__bf16)p;
+                    }
                 }
             }
         }
@@ -352,16 +357,16 @@ __global__ __launch_bounds__(NTK) void k_tesa_bwd_dkdv(const __bf16 *__restrict_
         for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
             for (int kb2 = 0; kb2 < 4; ++kb2) {
-                dva[dt] = mfma(v_frag<DH + BPAD>(&dos[0][0], 16 * kb2, 32 * dt), pf[kb2], dva[dt]);
-                const bf16x8 qt_ = v_frag<DH + BPAD>(&qs[0][0], 16 * kb2, 32 * dt);
-                dka[dt] = mfma(qt_, dsh[kb2], dka[dt]);
-                dka[dt] = mfma(qt_, dsl[kb2], dka[dt]);
+                if constexpr (DK) {
+                    const bf16x8 qt_ = v_frag<DH + BPAD>(&qs[0][0], 16 * kb2, 32 * dt);
+                    acc[dt] = mfma(qt_, dsh[kb2], acc[dt]);
+                    acc[dt] = mfma(qt_, dsl[kb2], acc[dt]);
+                } else {
+                    acc[dt] = mfma(v_frag<DH + BPAD>(&dos[0][0], 16 * kb2, 32 * dt), pf[kb2], acc[dt]);
+                }
             }
     }
-    if (kvalid) {
-        store_col<DH>(dk + koff, dka, scale);
-        store_col<DH>(dv + koff, dva, 1.f);
-    }
+    if (kvalid) store_col<DH>(dout_kv + koff, acc, DK ? scale : 1.f);
 }
 
 template <int DH>
@@ -378,10 +383,15 @@ hipError_t launch_bwd(const TesaProblem &p, const TesaGradArgs &a, void *ws, hip
                                              (const __bf16 *)a.dout, (__bf16 *)a.dq, stats,
                                              p.nheads, (int)p.T, (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st, p.sh,
                                              p.sw, p.nrh, p.nrw, nqb, scale, c_log2);
-    k_tesa_bwd_dkdv<DH><<<dim3((unsigned)(nreg * nkb), (unsigned)p.nheads, (unsigned)p.batch), NTK, 0, st>>>((const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
-                                               (const __bf16 *)a.dout, stats, (__bf16 *)a.dk, (__bf16 *)a.dv,
-                                               p.nheads, (int)p.T, (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st,
-                                               p.sh, p.sw, p.nrh, p.nrw, nkb, scale, c_log2);
+    const dim3 gk((unsigned)(nreg * nkb), (unsigned)p.nheads, (unsigned)p.batch);
+    k_tesa_bwd_dkdv<DH, false><<<gk, NTK, 0, st>>>((const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                                                    (const __bf16 *)a.dout, stats, (__bf16 *)a.dv, p.nheads, (int)p.T,
+                                                    (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st, p.sh, p.sw, p.nrh,
+                                                    p.nrw, nkb, scale, c_log2);
+    k_tesa_bwd_dkdv<DH, true><<<gk, NTK, 0, st>>>((const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                                                   (const __bf16 *)a.dout, stats, (__bf16 *)a.dk, p.nheads, (int)p.T,
+                                                   (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st, p.sh, p.sw, p.nrh,
+                                                   p.nrw, nkb, scale, c_log2);
     return hipGetLastError();
 }
 
