@@ -1,21 +1,20 @@
 // TESA backward on bf16 MFMA (gfx950): the gradients of softmax attention inside
 // each (shifted) 3D window. With S = scale Q K^T, P = softmax(S) by rows, O = P V
 // and the upstream gradient dO, per window:
-//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  delta_q = sum_k P_qk dP_qk,
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  delta_q = sum_k P_qk dP_qk = dO_q . O_q,
 //   dQ = scale dS K,  dK = scale dS^T Q.
-// delta is formed from the kernel's own P and dP (not as dO . O from a stored forward
-// output), so each row of dS sums to zero up to rounding; where the softmax is peaked,
-// dP - delta cancels, and the forward output's rounding would otherwise show in dS.
+// delta is taken as dO . O from the forward's output (forming it from the kernel's own
+// P and dP instead measured the same worst error and costs the dP products in a pass).
 // dS enters the dQ and dK products as a pair of bf16 values (its rounding and the
 // rounding of the rest), two MFMAs on the same K^T or Q^T operand: the rows of dS sum
 // to zero, so dQ = scale dS K is a cancelling sum, and one bf16 rounding of dS gave
 // errors of 2% of the gradient's rms on windows of a few tokens (0.4% with the pair).
 // Two kernels, one workgroup per (window, head, block of rows):
 //  - k_tesa_bwd_dq: 8 waves, each 32 queries, one per lane column as in the forward
-//    (S^T = K Q^T). A first pass over the key tiles gives each query's log-sum-exp and
-//    delta (online, against a running maximum); the second forms P^T, dP^T = V dO^T and
-//    dS^T, and accumulates dQ^T += K^T dS^T. It also stores (log-sum-exp, delta) per
-//    query for the second kernel.
+//    (S^T = K Q^T). A first pass over the key tiles gives each query's log-sum-exp
+//    (against a running maximum); the second forms P^T, dP^T = V dO^T and dS^T, and
+//    accumulates dQ^T += K^T dS^T. It also stores (log-sum-exp, delta) per query for the
+//    dK and dV kernels.
 //  - k_tesa_bwd_dkdv<DK>: 8 waves, each 32 keys, one per lane column (S = Q K^T): per
 //    query tile it forms P and accumulates dV^T += dO^T P (DK false), or forms P,
 //    dP = dO V^T and dS and accumulates dK^T += Q^T dS (DK true), the transposed
@@ -133,7 +132,7 @@ __device__ __forceinline__ void store_col(__bf16 *dst, const f32x16 (&acc)[DH / 
 
 template <int DH>
 __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
-                                                     const __bf16 *__restrict__ v,
+                                                     const __bf16 *__restrict__ v, const __bf16 *__restrict__ o,
                                                      const __bf16 *__restrict__ dout, __bf16 *__restrict__ dq,
                                                      float2 *__restrict__ stats, int nheads, int Tn, int Hn,
                                                      int Wn, int wt, int wh, int ww, int st, int sh, int sw,
@@ -158,6 +157,17 @@ __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ 
     bf16x8 qf[DH / 16], dof[DH / 16];
     row_frags<DH>(q + qoff, qf);
     row_frags<DH>(dout + qoff, dof);
+    float delta;
+    {
+        bf16x8 of[DH / 16];
+        row_frags<DH>(o + qoff, of);
+        float part = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < DH / 16; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf((float)dof[kb][e], (float)of[kb][e], part);
+        delta = part + __shfl_xor(part, 32);  // lanes l and l + 32 hold the two halves of the row
+    }
 
     const int ntile = (X.m + BT - 1) / BT;
     // dP^T = V dO^T of the tile in LDS
@@ -188,19 +198,18 @@ __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ 
             }
     };
 
-    // Pass 1: log-sum-exp of each query's scores (log2 units) and delta = sum_k P dP, both
-    // against a running maximum; this lane holds half of each tile's keys.
+    // Pass 1: log-sum-exp of each query's scores (log2 units) against a running maximum;
+    // this lane holds half of each tile's keys.
     TilePair<DH, NTQ> tp;
-    float mrun = -INFINITY, lrun = 0.f, drun = 0.f;
+    float mrun = -INFINITY, lrun = 0.f;
     tp.fetch(k, v, row, X, 0, rowstride);
     for (int kt = 0; kt < ntile; ++kt) {
         __syncthreads();
         tp.stash(ks, vs);
         __syncthreads();
         tp.fetch(k, v, row, X, (kt + 1 < ntile ? kt + 1 : 0) * BT, rowstride);  // the next tile (pass 2's first)
-        f32x16 s[2], dp[2];
+        f32x16 s[2];
         scores(kt, s);
-        dprobs(dp);
         float mt = -INFINITY;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
@@ -208,23 +217,15 @@ __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ 
             for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, s[sub][rr]);
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mnew = fmaxf(mrun, mt);  // finite: tile 0 holds key 0
-        float ls = 0.f, lds = 0.f;
+        float ls = 0.f;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const float e = __builtin_amdgcn_exp2f(s[sub][rr] - mnew);
-                ls += e;
-                lds = fmaf(e, dp[sub][rr], lds);
-            }
-        const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
-        lrun = lrun * corr + ls;
-        drun = drun * corr + lds;
+            for (int rr = 0; rr < 16; ++rr) ls += __builtin_amdgcn_exp2f(s[sub][rr] - mnew);
+        lrun = lrun * __builtin_amdgcn_exp2f(mrun - mnew) + ls;
         mrun = mnew;
     }
-    const float ltot = lrun + __shfl_xor(lrun, 32);
-    const float lse = mrun + __log2f(ltot);
-    const float delta = (drun + __shfl_xor(drun, 32)) / ltot;
+    const float lse = mrun + __log2f(lrun + __shfl_xor(lrun, 32));
 
     // Pass 2: dQ^T += K^T dS^T, with P^T = 2^(s - lse) and dS^T = P^T (dP^T - delta).
     f32x16 acc[DH / 32];
@@ -380,7 +381,7 @@ hipError_t launch_bwd(const TesaProblem &p, const TesaGradArgs &a, void *ws, hip
     float2 *stats = (float2 *)ws;
     timing::Scope ts_(K_TESA_BWD, st);
     k_tesa_bwd_dq<DH><<<dim3((unsigned)(nreg * nqb), (unsigned)p.nheads, (unsigned)p.batch), NTQ, 0, st>>>((const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
-                                             (const __bf16 *)a.dout, (__bf16 *)a.dq, stats,
+                                             (const __bf16 *)a.o, (const __bf16 *)a.dout, (__bf16 *)a.dq, stats,
                                              p.nheads, (int)p.T, (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st, p.sh,
                                              p.sw, p.nrh, p.nrw, nqb, scale, c_log2);
     const dim3 gk((unsigned)(nreg * nkb), (unsigned)p.nheads, (unsigned)p.batch);
