@@ -85,7 +85,8 @@ __device__ __forceinline__ void row_frags(const __bf16 *rowp, bf16x8 (&f)[DH / 1
     for (int kb = 0; kb < DH / 16; ++kb) f[kb] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(rowp + 16 * kb + 8 * half));
 }
 
-// Tile of BT rows of two tensors through registers: 16-byte chunks, natural layout.
+// Tile of BT rows of two tensors through registers: 16-byte chunks, natural layout. A null
+// second tensor (or tile) moves the first alone.
 template <int DH, int NT>
 struct TilePair {
     static constexpr int DC = DH / 8, PER = BT * DC / NT;
@@ -100,7 +101,7 @@ struct TilePair {
             // a row past the window reads the window's first row: finite, and masked where used
             const size_t off = X.head_off + (size_t)row[idx < X.m ? idx : 0] * rowstride + 8 * dc;
             a[it] = *(const u32x4 *)(pa + off);
-            b[it] = *(const u32x4 *)(pb + off);
+            if (pb) b[it] = *(const u32x4 *)(pb + off);
         }
     }
     __device__ __forceinline__ void stash(__bf16 (*ta)[DH + BPAD], __bf16 (*tb)[DH + BPAD]) const
@@ -109,7 +110,7 @@ struct TilePair {
         for (int it = 0; it < PER; ++it) {
             const int c = threadIdx.x + NT * it;
             *(u32x4 *)&ta[c / DC][8 * (c % DC)] = a[it];
-            *(u32x4 *)&tb[c / DC][8 * (c % DC)] = b[it];
+            if (tb) *(u32x4 *)&tb[c / DC][8 * (c % DC)] = b[it];
         }
     }
 };
@@ -199,15 +200,17 @@ __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ 
     };
 
     // Pass 1: log-sum-exp of each query's scores (log2 units) against a running maximum;
-    // this lane holds half of each tile's keys.
+    // this lane holds half of each tile's keys. Only K tiles are staged; the last fetch
+    // brings pass 2's first tile, K and V.
     TilePair<DH, NTQ> tp;
     float mrun = -INFINITY, lrun = 0.f;
-    tp.fetch(k, v, row, X, 0, rowstride);
+    tp.fetch(k, ntile > 1 ? nullptr : v, row, X, 0, rowstride);
     for (int kt = 0; kt < ntile; ++kt) {
         __syncthreads();
-        tp.stash(ks, vs);
+        tp.stash(ks, nullptr);
         __syncthreads();
-        tp.fetch(k, v, row, X, (kt + 1 < ntile ? kt + 1 : 0) * BT, rowstride);  // the next tile (pass 2's first)
+        if (kt + 1 < ntile) tp.fetch(k, nullptr, row, X, (kt + 1) * BT, rowstride);
+        else tp.fetch(k, v, row, X, 0, rowstride);
         f32x16 s[2];
         scores(kt, s);
         float mt = -INFINITY;
