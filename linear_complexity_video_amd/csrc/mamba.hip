@@ -196,7 +196,7 @@ __global__ __launch_bounds__(MB_NT) void k_mamba(const E *__restrict__ x, const 
         // lane j % 8 keeps that of token j, so the group's results leave in one store per lane.
         constexpr int GS = 8, KPL = GS / MB_LPC;
         // Stage by stage over the group's tokens (decays and inputs, the state chain, the C h
-        // products, each DPP step), so that the one wave of a SIMD has independent work in flight.
+        // products, each DPP step), so that a wave has independent work in flight.
         for (int t0 = 0; t0 < MB_TT; t0 += GS) {
             float gd[GS], gx[GS], e[GS][SPL], u[GS][SPL], acc[GS];
 #pragma unroll

@@ -1,15 +1,15 @@
 // TESA backward on bf16 MFMA (gfx950): the gradients of softmax attention inside
 // each (shifted) 3D window. With S = scale Q K^T, P = softmax(S) by rows, O = P V
 // and the upstream gradient dO, per window:
-//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  delta_q = sum_k P_qk dP_qk = dO_q . O_q,
+//   dV = P^T dO,  dP = dO V^T,  dS_qk = P_qk (dP_qk - delta_q),  delta_q = sum_k P_qk dP_qk = dO_q . O_q,
 //   dQ = scale dS K,  dK = scale dS^T Q.
 // delta is taken as dO . O from the forward's output (forming it from the kernel's own
 // P and dP instead measured the same worst error and costs the dP products in a pass).
-// dS enters the dQ and dK products as a pair of bf16 values (its rounding and the
-// rounding of the rest), two MFMAs on the same K^T or Q^T operand: the rows of dS sum
+// dS enters the dQ and dK products as a pair of bf16 values (its bf16 rounding and the
+// bf16 rounding of what that leaves), two MFMAs on the same K^T or Q^T operand: the rows of dS sum
 // to zero, so dQ = scale dS K is a cancelling sum, and one bf16 rounding of dS gave
 // errors of 2% of the gradient's rms on windows of a few tokens (0.4% with the pair).
-// Two kernels, one workgroup per (window, head, block of rows):
+// Two kernel templates (three launches), one workgroup per (window, head, block of rows):
 //  - k_tesa_bwd_dq: 8 waves, each 32 queries, one per lane column as in the forward
 //    (S^T = K Q^T). A first pass over the key tiles gives each query's log-sum-exp
 //    (against a running maximum); the second forms P^T, dP^T = V dO^T and dS^T, and
