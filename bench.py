@@ -332,8 +332,8 @@ def tesa_backward_bench(torch, np, B, wl, att, reps):
         pairs = tesa_pairs(wl, shift) * wl.batch * wl.t_heads
         log(f"tesa backward: shift {shift}")
         tf = timed(lambda: B.mate_tesa(att["q"], att["k"], att["v"], att["o"], wl.window, shift))
-        tb = timed(lambda: B.mate_tesa_backward(att["q"], att["k"], att["v"], att["o"], dout, dq, dk, dv, wl.window,
-                                                shift, workspace=ws))
+        tb = timed(lambda: B.mate_tesa_backward(att["q"], att["k"], att["v"], dout, dq, dk, dv, wl.window, shift,
+                                                workspace=ws))
         ff, fb = 4.0 * wl.t_dim * pairs, 10.0 * wl.t_dim * pairs
         rows["shifted" if shifted else "unshifted"] = {
             "forward_ms": tf, "backward_ms": tb, "backward_over_forward": tb / tf,

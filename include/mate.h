@@ -217,13 +217,13 @@ mate_status mate_tesa(const mate_tesa_tensors *t, mate_grid g, const mate_tesa_d
  *   dv = P^T dout,  dP = dout v^T,  dS_ij = P_ij (dP_ij - sum_l P_il dP_il),
  *   dq = scale dS k,  dk = scale dS^T q
  * (the chain rule through TESA, the attention half of training the MATE block;
- * the xllm-io review, section 四, trains LinGen end to end). o is mate_tesa's
- * output for the same q, k, v and descriptor; it gives sum_l P_il dP_il as
- * dout_i . o_i, and P is recomputed. All eight tensors are
- * [batch][T][H][W][nheads][headdim] in the descriptor's dtype, 16-byte aligned;
- * dq, dk, dv are written whole and must not overlap the inputs. */
+ * the xllm-io review, section 四, trains LinGen end to end). P and
+ * sum_l P_il dP_il are recomputed from q, k, v and dout, so the forward's output
+ * is not an input. All seven tensors are [batch][T][H][W][nheads][headdim] in
+ * the descriptor's dtype, 16-byte aligned; dq, dk, dv are written whole and
+ * must not overlap the inputs. */
 typedef struct {
-    const void *q, *k, *v, *o, *dout;
+    const void *q, *k, *v, *dout;
     void *dq, *dk, *dv;
 } mate_tesa_grad_tensors;
 

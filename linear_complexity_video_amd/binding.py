@@ -67,7 +67,7 @@ class TesaTensors(ctypes.Structure):
 
 
 class TesaGradTensors(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "o", "dout", "dq", "dk", "dv")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "dout", "dq", "dk", "dv")]
 
 
 _lib = None
@@ -243,14 +243,14 @@ def mate_tesa_backward_workspace_size(grid, desc: TesaDesc) -> int:
     return int(lib().mate_tesa_backward_workspace_size(Grid(*grid), ctypes.byref(desc)))
 
 
-def mate_tesa_backward(q, k, v, o, dout, dq, dk, dv, window, shift=(0, 0, 0), scale: float = 0.0, workspace=None,
+def mate_tesa_backward(q, k, v, dout, dq, dk, dv, window, shift=(0, 0, 0), scale: float = 0.0, workspace=None,
                        stream=None):
-    """(dq, dk, dv) of mate_tesa (whose output is o) for the upstream gradient dout (see include/mate.h)."""
-    _dev(q, k, v, o, dout, dq, dk, dv)
+    """(dq, dk, dv) of mate_tesa for the upstream gradient dout (see include/mate.h)."""
+    _dev(q, k, v, dout, dq, dk, dv)
     desc = tesa_desc(q, window, shift, scale)
     if workspace is None:
         workspace = _workspace(mate_tesa_backward_workspace_size(tuple(q.shape[:4]), desc), q)
-    t = TesaGradTensors(*(_ptr(a) for a in (q, k, v, o, dout, dq, dk, dv)))
+    t = TesaGradTensors(*(_ptr(a) for a in (q, k, v, dout, dq, dk, dv)))
     _check(lib().mate_tesa_backward(ctypes.byref(t), grid_of(q), ctypes.byref(desc), _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
 

@@ -38,7 +38,7 @@ struct TesaArgs {
 };
 
 struct TesaGradArgs {
-    const void *q, *k, *v, *o, *dout;
+    const void *q, *k, *v, *dout;
     void *dq, *dk, *dv;
 };
 

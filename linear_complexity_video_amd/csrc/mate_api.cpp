@@ -349,11 +349,11 @@ mate_status mate_tesa_backward(const mate_tesa_grad_tensors *t, mate_grid g, con
                                void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!t) return fail(MATE_ERR_NULL, "tesa gradient tensors struct is NULL");
-    if (!t->q || !t->k || !t->v || !t->o || !t->dout || !t->dq || !t->dk || !t->dv)
-        return fail(MATE_ERR_NULL, "a tesa gradient tensor pointer (q, k, v, o, dout, dq, dk, dv) is NULL");
-    if (((uintptr_t)t->q | (uintptr_t)t->k | (uintptr_t)t->v | (uintptr_t)t->o | (uintptr_t)t->dout |
-         (uintptr_t)t->dq | (uintptr_t)t->dk | (uintptr_t)t->dv) & 15)
-        return fail(MATE_ERR_UNSUPPORTED, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+    if (!t->q || !t->k || !t->v || !t->dout || !t->dq || !t->dk || !t->dv)
+        return fail(MATE_ERR_NULL, "a tesa gradient tensor pointer (q, k, v, dout, dq, dk, dv) is NULL");
+    if (((uintptr_t)t->q | (uintptr_t)t->k | (uintptr_t)t->v | (uintptr_t)t->dout | (uintptr_t)t->dq |
+         (uintptr_t)t->dk | (uintptr_t)t->dv) & 15)
+        return fail(MATE_ERR_UNSUPPORTED, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
     mate::TesaProblem p;
     bool fast = false;
     mate_status s = make_tesa_problem(g, d, p, fast);
@@ -364,7 +364,7 @@ mate_status mate_tesa_backward(const mate_tesa_grad_tensors *t, mate_grid g, con
     if (!workspace || workspace_bytes < need)
         return fail(MATE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
     if ((uintptr_t)workspace & 255) return fail(MATE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    mate::TesaGradArgs a{t->q, t->k, t->v, t->o, t->dout, t->dq, t->dk, t->dv};
+    mate::TesaGradArgs a{t->q, t->k, t->v, t->dout, t->dq, t->dk, t->dv};
     hipError_t e = mate::tesa_backward(p, a, workspace, (hipStream_t)stream);
     if (e != hipSuccess) return device_fail(e, "tesa backward launch");
     return MATE_OK;

@@ -1,20 +1,21 @@
 // TESA backward on bf16 MFMA (gfx950): the gradients of softmax attention inside
 // each (shifted) 3D window. With S = scale Q K^T, P = softmax(S) by rows, O = P V
 // and the upstream gradient dO, per window:
-//   dV = P^T dO,  dP = dO V^T,  dS_qk = P_qk (dP_qk - delta_q),  delta_q = sum_k P_qk dP_qk = dO_q . O_q,
+//   dV = P^T dO,  dP = dO V^T,  dS_qk = P_qk (dP_qk - delta_q),  delta_q = sum_k P_qk dP_qk,
 //   dQ = scale dS K,  dK = scale dS^T Q.
-// delta is taken as dO . O from the forward's output (forming it from the kernel's own
-// P and dP instead measured the same worst error and costs the dP products in a pass).
-// dS enters the dQ and dK products as a pair of bf16 values (its bf16 rounding and the
-// bf16 rounding of what that leaves), two MFMAs on the same K^T or Q^T operand: the rows of dS sum
-// to zero, so dQ = scale dS K is a cancelling sum, and one bf16 rounding of dS gave
-// errors of 2% of the gradient's rms on windows of a few tokens (0.4% with the pair).
+// delta is formed from the kernel's own P and dP rather than as dO . O from the forward's
+// bf16 output: where the softmax is peaked, dP - delta cancels and the forward output's
+// error shows in dS (dK 1.9% of its rms against 0.4%, unscaled 64-dim inputs).
+// dS and P enter the dQ, dK and dV products as pairs of bf16 values (the bf16 rounding and
+// the bf16 rounding of what that leaves), two MFMAs on the same operand: these products
+// are cancelling sums (the rows of dS sum to zero; dV sums dO rows of mixed sign), and one
+// bf16 rounding gave errors of 1.7-2.1% of the gradients' rms (0.4% with the pairs).
 // Two kernel templates (three launches), one workgroup per (window, head, block of rows):
 //  - k_tesa_bwd_dq: 8 waves, each 32 queries, one per lane column as in the forward
-//    (S^T = K Q^T). A first pass over the key tiles gives each query's log-sum-exp
-//    (against a running maximum); the second forms P^T, dP^T = V dO^T and dS^T, and
-//    accumulates dQ^T += K^T dS^T. It also stores (log-sum-exp, delta) per query for the
-//    dK and dV kernels.
+//    (S^T = K Q^T). A first pass over the key tiles gives each query's log-sum-exp and
+//    delta (online, against a running maximum); the second forms P^T, dP^T = V dO^T and
+//    dS^T, and accumulates dQ^T += K^T dS^T. It also stores (log-sum-exp, delta) per
+//    query for the dK and dV kernels.
 //  - k_tesa_bwd_dkdv<DK>: 8 waves, each 32 keys, one per lane column (S = Q K^T): per
 //    query tile it forms P and accumulates dV^T += dO^T P (DK false), or forms P,
 //    dP = dO V^T and dS and accumulates dK^T += Q^T dS (DK true), the transposed
@@ -85,8 +86,7 @@ __device__ __forceinline__ void row_frags(const __bf16 *rowp, bf16x8 (&f)[DH / 1
     for (int kb = 0; kb < DH / 16; ++kb) f[kb] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(rowp + 16 * kb + 8 * half));
 }
 
-// Tile of BT rows of two tensors through registers: 16-byte chunks, natural layout. A null
-// second tensor (or tile) moves the first alone.
+// Tile of BT rows of two tensors through registers: 16-byte chunks, natural layout.
 template <int DH, int NT>
 struct TilePair {
     static constexpr int DC = DH / 8, PER = BT * DC / NT;
@@ -101,7 +101,7 @@ struct TilePair {
             // a row past the window reads the window's first row: finite, and masked where used
             const size_t off = X.head_off + (size_t)row[idx < X.m ? idx : 0] * rowstride + 8 * dc;
             a[it] = *(const u32x4 *)(pa + off);
-            if (pb) b[it] = *(const u32x4 *)(pb + off);
+            b[it] = *(const u32x4 *)(pb + off);
         }
     }
     __device__ __forceinline__ void stash(__bf16 (*ta)[DH + BPAD], __bf16 (*tb)[DH + BPAD]) const
@@ -110,7 +110,7 @@ struct TilePair {
         for (int it = 0; it < PER; ++it) {
             const int c = threadIdx.x + NT * it;
             *(u32x4 *)&ta[c / DC][8 * (c % DC)] = a[it];
-            if (tb) *(u32x4 *)&tb[c / DC][8 * (c % DC)] = b[it];
+            *(u32x4 *)&tb[c / DC][8 * (c % DC)] = b[it];
         }
     }
 };
@@ -133,7 +133,7 @@ __device__ __forceinline__ void store_col(__bf16 *dst, const f32x16 (&acc)[DH / 
 
 template <int DH>
 __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
-                                                     const __bf16 *__restrict__ v, const __bf16 *__restrict__ o,
+                                                     const __bf16 *__restrict__ v,
                                                      const __bf16 *__restrict__ dout, __bf16 *__restrict__ dq,
                                                      float2 *__restrict__ stats, int nheads, int Tn, int Hn,
                                                      int Wn, int wt, int wh, int ww, int st, int sh, int sw,
@@ -158,17 +158,6 @@ __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ 
     bf16x8 qf[DH / 16], dof[DH / 16];
     row_frags<DH>(q + qoff, qf);
     row_frags<DH>(dout + qoff, dof);
-    float delta;
-    {
-        bf16x8 of[DH / 16];
-        row_frags<DH>(o + qoff, of);
-        float part = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < DH / 16; ++kb)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part = fmaf((float)dof[kb][e], (float)of[kb][e], part);
-        delta = part + __shfl_xor(part, 32);  // lanes l and l + 32 hold the two halves of the row
-    }
 
     const int ntile = (X.m + BT - 1) / BT;
     // dP^T = V dO^T of the tile in LDS
@@ -199,20 +188,19 @@ __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ 
             }
     };
 
-    // Pass 1: log-sum-exp of each query's scores (log2 units) against a running maximum;
-    // this lane holds half of each tile's keys. Only K tiles are staged; the last fetch
-    // brings pass 2's first tile, K and V.
+    // Pass 1: log-sum-exp of each query's scores (log2 units) and delta = sum_k P dP, both
+    // against a running maximum; this lane holds half of each tile's keys.
     TilePair<DH, NTQ> tp;
-    float mrun = -INFINITY, lrun = 0.f;
-    tp.fetch(k, ntile > 1 ? nullptr : v, row, X, 0, rowstride);
+    float mrun = -INFINITY, lrun = 0.f, drun = 0.f;
+    tp.fetch(k, v, row, X, 0, rowstride);
     for (int kt = 0; kt < ntile; ++kt) {
         __syncthreads();
-        tp.stash(ks, nullptr);
+        tp.stash(ks, vs);
         __syncthreads();
-        if (kt + 1 < ntile) tp.fetch(k, nullptr, row, X, (kt + 1) * BT, rowstride);
-        else tp.fetch(k, v, row, X, 0, rowstride);
-        f32x16 s[2];
+        tp.fetch(k, v, row, X, (kt + 1 < ntile ? kt + 1 : 0) * BT, rowstride);  // the next tile (pass 2's first)
+        f32x16 s[2], dp[2];
         scores(kt, s);
+        dprobs(dp);
         float mt = -INFINITY;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
@@ -220,15 +208,24 @@ __global__ __launch_bounds__(NTQ) void k_tesa_bwd_dq(const __bf16 *__restrict__ 
             for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, s[sub][rr]);
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mnew = fmaxf(mrun, mt);  // finite: tile 0 holds key 0
-        float ls = 0.f;
+        float ls = 0.f, lds = 0.f;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) ls += __builtin_amdgcn_exp2f(s[sub][rr] - mnew);
-        lrun = lrun * __builtin_amdgcn_exp2f(mrun - mnew) + ls;
+            for (int rr = 0; rr < 16; ++rr) {
+                const float e = __builtin_amdgcn_exp2f(s[sub][rr] - mnew);
+                ls += e;
+                lds = fmaf(e, dp[sub][rr], lds);
+            }
+        const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
+        lrun = lrun * corr + ls;
+        drun = drun * corr + lds;
         mrun = mnew;
     }
-    const float lse = mrun + __log2f(lrun + __shfl_xor(lrun, 32));
+    // lanes l and l + 32 hold the two halves of each query's keys
+    const float ltot = lrun + __shfl_xor(lrun, 32);
+    const float lse = mrun + __log2f(ltot);
+    const float delta = (drun + __shfl_xor(drun, 32)) / ltot;
 
     // Pass 2: dQ^T += K^T dS^T, with P^T = 2^(s - lse) and dS^T = P^T (dP^T - delta).
     f32x16 acc[DH / 32];
@@ -326,7 +323,7 @@ __global__ __launch_bounds__(NTK) void k_tesa_bwd_dkdv(const __bf16 *__restrict_
             tp.fetch(q, dout, row, X, (qt + 1) * BT, rowstride);
             fetch_stats((qt + 1) * BT);
         }
-        bf16x8 pf[DK ? 1 : 4], dsh[DK ? 4 : 1], dsl[DK ? 4 : 1];
+        bf16x8 dsh[4], dsl[4];  // dS (DK) or P (dV) as bf16 pairs
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             f32x16 s = f32x16{}, dp = f32x16{};
@@ -346,14 +343,10 @@ __global__ __launch_bounds__(NTK) void k_tesa_bwd_dkdv(const __bf16 *__restrict_
                     const int rr = 4 * i + j;
                     const bool ok = qt * BT + ql + j < X.m;
                     const float p = ok ? __builtin_amdgcn_exp2f(s[rr] * c_log2 - lv[j]) : 0.f;
-                    if constexpr (DK) {
-                        const float dsv = p * (dp[rr] - dvv[j]);
-                        const __bf16 hi = (__bf16)dsv;
-                        dsh[2 * sub + (rr >> 3)][rr & 7] = hi;
-                        dsl[2 * sub + (rr >> 3)][rr & 7] = (__bf16)(dsv - (float)hi);
-                    } else {
-                        pf[2 * sub + (rr >> 3)][rr & 7] = (__bf16)p;
-                    }
+                    const float val = DK ? p * (dp[rr] - dvv[j]) : p;
+                    const __bf16 hi = (__bf16)val;
+                    dsh[2 * sub + (rr >> 3)][rr & 7] = hi;
+                    dsl[2 * sub + (rr >> 3)][rr & 7] = (__bf16)(val - (float)hi);
                 }
             }
         }
@@ -361,13 +354,10 @@ __global__ __launch_bounds__(NTK) void k_tesa_bwd_dkdv(const __bf16 *__restrict_
         for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
             for (int kb2 = 0; kb2 < 4; ++kb2) {
-                if constexpr (DK) {
-                    const bf16x8 qt_ = v_frag<DH + BPAD>(&qs[0][0], 16 * kb2, 32 * dt);
-                    acc[dt] = mfma(qt_, dsh[kb2], acc[dt]);
-                    acc[dt] = mfma(qt_, dsl[kb2], acc[dt]);
-                } else {
-                    acc[dt] = mfma(v_frag<DH + BPAD>(&dos[0][0], 16 * kb2, 32 * dt), pf[kb2], acc[dt]);
-                }
+                // dK^T += Q^T dS, or dV^T += dO^T P
+                const bf16x8 at = v_frag<DH + BPAD>(DK ? &qs[0][0] : &dos[0][0], 16 * kb2, 32 * dt);
+                acc[dt] = mfma(at, dsh[kb2], acc[dt]);
+                acc[dt] = mfma(at, dsl[kb2], acc[dt]);
             }
     }
     if (kvalid) store_col<DH>(dout_kv + koff, acc, DK ? scale : 1.f);
@@ -384,7 +374,7 @@ hipError_t launch_bwd(const TesaProblem &p, const TesaGradArgs &a, void *ws, hip
     float2 *stats = (float2 *)ws;
     timing::Scope ts_(K_TESA_BWD, st);
     k_tesa_bwd_dq<DH><<<dim3((unsigned)(nreg * nqb), (unsigned)p.nheads, (unsigned)p.batch), NTQ, 0, st>>>((const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
-                                             (const __bf16 *)a.o, (const __bf16 *)a.dout, (__bf16 *)a.dq, stats,
+                                             (const __bf16 *)a.dout, (__bf16 *)a.dq, stats,
                                              p.nheads, (int)p.T, (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st, p.sh,
                                              p.sw, p.nrh, p.nrw, nqb, scale, c_log2);
     const dim3 gk((unsigned)(nreg * nkb), (unsigned)p.nheads, (unsigned)p.batch);

@@ -121,12 +121,12 @@ def test_tesa_backward_validation():
     g = B.Grid(1, 4, 4, 4)
     desc = lambda **kw: B.TesaDesc(**{**dict(nheads=2, headdim=64, win_t=2, win_h=2, win_w=2, shift_t=0, shift_h=0,
                                              shift_w=0, scale=0.0, dtype=B.MATE_BF16, algo=B.ALGO_AUTO), **kw})
-    ptrs = {n: 0x100000 + 0x1000 * i for i, n in enumerate(("q", "k", "v", "o", "dout", "dq", "dk", "dv"))}
+    ptrs = {n: 0x100000 + 0x1000 * i for i, n in enumerate(("q", "k", "v", "dout", "dq", "dk", "dv"))}
     t = lambda **kw: B.TesaGradTensors(**{**ptrs, **kw})
     call = lambda tt, dd, ws=0x800000, wsb=1 << 40: lib.mate_tesa_backward(ctypes.byref(tt), g, ctypes.byref(dd),
                                                                            ctypes.c_void_p(ws), wsb, None)
     assert call(t(dout=0), desc()) == B.MATE_ERR_NULL
-    assert call(t(o=0), desc()) == B.MATE_ERR_NULL
+    assert call(t(dv=0), desc()) == B.MATE_ERR_NULL
     assert call(t(dq=0x100008), desc()) == B.MATE_ERR_UNSUPPORTED           # misaligned
     assert call(t(), desc(win_t=3)) == B.MATE_ERR_SHAPE                     # does not divide the grid
     assert call(t(), desc(shift_t=2)) == B.MATE_ERR_SHAPE                   # shift not below the window

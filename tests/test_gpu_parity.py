@@ -525,11 +525,8 @@ def _bf16_host(rng, shape, scale=1.0):
 
 
 def _tesa_grads(q, k, v, dout, window, shift):
-    """Forward on the GPU (its output feeds the backward, as in training), then the backward."""
-    o = torch.empty_like(q)
-    B.mate_tesa(q, k, v, o, window, shift)
     dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
-    B.mate_tesa_backward(q, k, v, o, dout, dq, dk, dv, window, shift)
+    B.mate_tesa_backward(q, k, v, dout, dq, dk, dv, window, shift)
     torch.cuda.synchronize()
     return dq, dk, dv
 
