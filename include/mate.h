@@ -217,7 +217,7 @@ mate_status mate_tesa(const mate_tesa_tensors *t, mate_grid g, const mate_tesa_d
  *   dv = P^T dout,  dP = dout v^T,  dS_ij = P_ij (dP_ij - sum_l P_il dP_il),
  *   dq = scale dS k,  dk = scale dS^T q
  * (the chain rule through TESA, the attention half of training the MATE block;
- * the xllm-io review, section 四, trains LinGen end to end). P and
+ * the xllm-io review, section 三, "训练配方", trains LinGen end to end). P and
  * sum_l P_il dP_il are recomputed from q, k, v and dout, so the forward's output
  * is not an input. All seven tensors are [batch][T][H][W][nheads][headdim] in
  * the descriptor's dtype, 16-byte aligned; dq, dk, dv are written whole and

@@ -565,7 +565,7 @@ static void tesa_unit(void *vctx, int64_t unit)
  *   dv = P^T dO,  dP = dO v^T,  dS_ij = P_ij (dP_ij - sum_l P_il dP_il),
  *   dq = scale dS k,  dk = scale dS^T q
  * (the backward pass of softmax attention; the pages train LinGen, the
- * xllm-io review, section 四 on training, and this is TESA's part of it). */
+ * xllm-io review, section 三, "训练配方", and this is TESA's part of it). */
 int oracle_tesa_region_counts(int64_t T, int64_t H, int64_t W, int wt, int wh, int ww, int st, int sh,
                               int sw, int64_t *counts3);
 
