@@ -344,6 +344,80 @@ def tesa_backward_bench(torch, np, B, wl, att, reps):
                                  "head_dim": wl.t_dim, "window": list(wl.window)}, "layers": rows}), flush=True)
 
 
+def block_bench(torch, np, B, wl, reps):
+    """One LinGen-4B layer's token mixing with its projections, to place the MATE core in it. Widths from
+    the xllm-io review's model table (embedding 2560, 20 heads) and the core's own (MA: 80 heads x 64 =
+    2 x 2560, d_state 128; TE: 20 x 128). The projections are plain library GEMMs (torch matmul, i.e.
+    hipBLASLt / rocBLAS): MA in 2560 -> x 5120, B and C 2 x 128, dt 80 (softplus); MA out 5120 -> 2560;
+    TE in 2560 -> q, k, v 3 x 2560; TE out 2560 -> 2560; the two branch outputs are summed. The Mamba2
+    block's conv1d, gating and norm are not on the pages and are left out. Prints one JSON line."""
+    stream = torch.cuda.current_stream()
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(13)
+    N, d = wl.N * wl.batch, 2560
+    Hs, P, S, th, td = wl.nheads, wl.headdim, wl.d_state, wl.t_heads, wl.t_dim
+    bf = torch.bfloat16
+    w = lambda i, o: (torch.randn(i, o, device=dev, generator=g) / np.sqrt(i)).to(bf)
+    h = torch.randn(N, d, device=dev, generator=g).to(bf)
+    W = {"x": w(d, Hs * P), "bc": w(d, 2 * S), "dt": w(d, Hs), "ma_out": w(Hs * P, d),
+         "q": w(d, th * td), "k": w(d, th * td), "v": w(d, th * td), "te_out": w(th * td, d)}
+    A = -torch.exp(torch.rand(Hs, device=dev, generator=g) * 2)
+    Dp = torch.randn(Hs, device=dev, generator=g)
+    shape_ssd = (wl.batch, wl.T, wl.H, wl.W)
+    y = torch.empty(*shape_ssd, Hs, P, device=dev, dtype=bf)
+    o = torch.empty(*shape_ssd, th, td, device=dev, dtype=bf)
+    sdesc = B.ssd_desc(y, torch.empty(*shape_ssd, 1, S, device=dev, dtype=bf), wl.chunk, wl.pool)
+    ws = torch.empty(B.mate_forward_workspace_size(wl.grid, sdesc, B.tesa_desc(o, wl.window)), dtype=torch.uint8,
+                     device=dev)
+    t = {}
+
+    def proj_in():
+        t["x"] = (h @ W["x"]).view(*shape_ssd, Hs, P)
+        bc = h @ W["bc"]
+        t["b"] = bc[:, :S].contiguous().view(*shape_ssd, 1, S)
+        t["c"] = bc[:, S:].contiguous().view(*shape_ssd, 1, S)
+        t["dt"] = torch.nn.functional.softplus((h @ W["dt"]).float()).view(*shape_ssd, Hs)
+        for n in ("q", "k", "v"):
+            t[n] = (h @ W[n]).view(*shape_ssd, th, td)
+
+    def core(order, shifted):
+        B.mate_forward({"x": t["x"], "b": t["b"], "c": t["c"], "dt": t["dt"], "a": A, "d": Dp, "y": y},
+                       {"q": t["q"], "k": t["k"], "v": t["v"], "o": o}, order, wl.chunk, wl.pool, wl.window,
+                       wl.layer_shift(shifted), workspace=ws)
+
+    def proj_out():
+        t["out"] = y.view(N, Hs * P) @ W["ma_out"] + o.view(N, th * td) @ W["te_out"]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, reps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    log("block: projections and core")
+    t_in, t_out = timed(proj_in), timed(proj_out)
+    t_core = [timed(lambda o_=o_, s_=s_: core(o_, s_)) for o_, s_ in wl.schedule]
+    t_layer = [timed(lambda o_=o_, s_=s_: (proj_in(), core(o_, s_), proj_out())) for o_, s_ in wl.schedule]
+    gemm_flops = 2.0 * N * d * (Hs * P + 2 * S + Hs + 3 * th * td) + 2.0 * N * d * (Hs * P + th * td)
+    mean = lambda xs: float(np.mean(xs))
+    print(json.dumps({"metric": "one LinGen-4B layer's token mixing with its projections (one MI355X)", "unit": "ms",
+                      "data": "synthetic",
+                      "config": {"workload": wl.name, "tokens": N, "embedding": d, "ma": [Hs, P, S], "te": [th, td],
+                                 "layers_of_model": 32},
+                      "projections_in_ms": t_in, "projections_out_ms": t_out,
+                      "projection_tflops": gemm_flops / (t_in + t_out) / 1e9,
+                      "core_ms": mean(t_core), "layer_ms": mean(t_layer), "per_layer_ms": t_layer,
+                      "core_share": mean(t_core) / mean(t_layer),
+                      "model_token_mixing_s": 32 * mean(t_layer) / 1e3}), flush=True)
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
@@ -361,6 +435,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=5, help="timed repetitions of each single call")
     ap.add_argument("--scaling", action="store_true",
                     help="instead of the throughput line: MATE core vs full attention per layer as T grows")
+    ap.add_argument("--block", action="store_true",
+                    help="instead of the throughput line: one layer's token mixing with its projections (library GEMMs)")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the throughput line: TESA's backward beside its forward, per layer")
     ap.add_argument("--variants", action="store_true",
@@ -389,6 +465,9 @@ def main():
     B.lib()
     if args.scaling:
         scaling_sweep(torch, np, B, args.kernel_reps)
+        return
+    if args.block:
+        block_bench(torch, np, B, WORKLOADS[args.config], args.kernel_reps)
         return
     algo = {"auto": B.ALGO_AUTO, "portable": B.ALGO_PORTABLE, "fast": B.ALGO_FAST}[args.algo]
     wl = WORKLOADS[args.config]
