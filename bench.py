@@ -418,6 +418,18 @@ def block_bench(torch, np, B, wl, reps):
                       "model_token_mixing_s": 32 * mean(t_layer) / 1e3}), flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where there is none)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
@@ -561,8 +573,8 @@ def main():
               for sh in (False, True)}
     t_ssd = time_call(lambda: B.mate_bissd_scan(ssd["x"], ssd["b"], ssd["c"], ssd["dt"], ssd["a"], ssd["d"],
                                                 ssd["y"], 0, wl.chunk, wl.pool, algo, workspace=ws), reps)
-    # One layer per RMS order (mate_forward alone, events on torch's stream; TESA's side stream is
-    # joined back into it inside the call): median of the repetitions.
+    # One layer per RMS order (mate_forward alone, events on torch's stream, which every kernel of the
+    # call is launched on): median of the repetitions.
     layers = []
     for order, shifted in wl.schedule:
         ts = []
@@ -651,9 +663,14 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = COPY_BYTES
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        # Every host CPU this process may run on, up to the 16 threads that one GPU's share of a GPU host
+        # is sized for.
+        host_cpus = len(os.sched_getaffinity(0))
+        threads = max(1, min(16, host_cpus))
         log(f"timing the CPU oracle on a sample with {threads} threads ...")
         out["cpu_baseline"] = cpu_baseline(wl, si, ti, threads)
+        out["cpu_baseline"]["host_cpus"] = host_cpus
+        out["cpu_baseline"]["cpu_model"] = cpu_model()
     print(json.dumps(out), flush=True)
 
 

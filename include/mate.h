@@ -16,8 +16,8 @@
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA storage).
  *     The caller owns every buffer; the library never allocates, frees or
- *     keeps device memory between calls (HIP streams and events aside: the
- *     side stream of mate_forward and the timing diagnostics below).
+ *     keeps device memory between calls, and creates no streams (the HIP
+ *     events of the timing diagnostics below aside).
  *   - Token tensors are channels-last: [batch][T][H][W][...], so the canonical
  *     token index is n = (t*H + h)*W + w and a token's channels are contiguous.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
@@ -62,7 +62,8 @@ typedef enum { MATE_F32 = 0, MATE_BF16 = 1 } mate_dtype;
 /* Kernel family. AUTO picks the MFMA kernels when the shape has them and the
  * portable kernels otherwise; the other values force one family (FAST returns
  * MATE_ERR_UNSUPPORTED when the shape has no MFMA kernel). Both compute the
- * same result up to rounding order. */
+ * same result up to rounding order, within the input range that
+ * mate_bissd_scan states for its MFMA kernels. */
 typedef enum { MATE_ALGO_AUTO = 0, MATE_ALGO_PORTABLE = 1, MATE_ALGO_FAST = 2 } mate_algo;
 
 typedef struct {
@@ -143,7 +144,21 @@ size_t mate_bissd_workspace_size(mate_grid g, const mate_ssd_desc *d);
  * product headdim*d_state <= 16384), chunk in 1..128; bf16 with headdim 64,
  * d_state 64 or 128 and chunk 64 or 128 also has MFMA kernels. The workspace
  * (device memory, at least mate_bissd_workspace_size bytes, 256-byte aligned)
- * is scratch for the call; its contents on entry do not matter. */
+ * is scratch for the call; its contents on entry do not matter.
+ *
+ * Input range of the MFMA kernels (MATE_ALGO_AUTO picks them for bf16 with the
+ * sizes above). Their intra-chunk products and state updates run on fp16 MFMA:
+ * x and B are converted to fp16, and C_t . B_u, the decay-weighted products
+ * dt_u C_t . B_u, dt_u x_u and dt_u B_u are held in fp16 (accumulation stays
+ * fp32; the states are carried in fp32 and staged as bf16). The result is
+ * therefore correct to bf16 accuracy when, for every pair of tokens t, u of
+ * one chunk,
+ *     |x_u| * max(1, dt_u) < 2^15,   |B_u| * max(1, dt_u) < 2^15 (element-wise),
+ *     2 |C_t . B_u| * max(1, dt_u) + 2 |D| < 2^15;
+ * larger values overflow to inf, and elements of x and B below 2^-14 in
+ * magnitude keep fewer significant bits (fp16 subnormals), which matters only
+ * when such elements dominate the output. Outside this range, MATE_ALGO_PORTABLE
+ * computes in fp32 throughout and has no such limit beyond fp32's own. */
 mate_status mate_bissd_scan(const mate_ssd_tensors *t, mate_grid g, int order, const mate_ssd_desc *d,
                             void *workspace, size_t workspace_bytes, void *stream);
 
@@ -239,16 +254,19 @@ mate_status mate_tesa_backward(const mate_tesa_grad_tensors *t, mate_grid g, con
 /* ------------------------------------------------------------------------ */
 /* One MATE core forward                                                     */
 /* ------------------------------------------------------------------------ */
-/* One layer's token mixing: the MA branch (mate_bissd_scan in RMS order
- * `order`) and the TE branch (mate_tesa with the descriptor's shift) on the
- * same grid. The two branch outputs are returned separately (s->y and a->o):
- * their widths differ and the pages leave their combination to the layer's
- * projections. The result equals the two calls made one after the other.
- * The TE branch runs beside the MA branch on a stream the library creates for
- * the current device on first use (kept until the process ends). It starts
- * after the work already queued on `stream`, and `stream` waits for it before
- * the call's last kernel, so both outputs are ordered on `stream` exactly as
- * if every kernel had been launched there. */
+/* One layer's token mixing. The MATE block replaces a DiT layer's
+ * self-attention with two branches whose outputs it combines: the MA branch
+ * (RMS reorder of the layer, review tokens, bidirectional Mamba2) and the TE
+ * branch (TESA), with the RMS order and the window shift alternating from
+ * layer to layer (QbitAI article on LinGen, section "方法": MATE = MA-branch +
+ * TE-branch; xllm-io review, section 三 "MA-Branch" item 2 for the alternating
+ * orders and "TE-Branch" for the alternating shift). Here the MA branch is
+ * mate_bissd_scan in RMS order `order` and the TE branch mate_tesa with the
+ * descriptor's shift, on the same grid. The two branch outputs are returned
+ * separately (s->y and a->o): their widths differ, and the pages leave their
+ * combination to the layer's projections. Both run on `stream`, one after the
+ * other; the result equals the two calls made one after the other. The
+ * workspace is mate_forward_workspace_size bytes (the scan's). */
 size_t mate_forward_workspace_size(mate_grid g, const mate_ssd_desc *sd, const mate_tesa_desc *td);
 mate_status mate_forward(const mate_ssd_tensors *s, const mate_ssd_desc *sd, const mate_tesa_tensors *a,
                          const mate_tesa_desc *td, mate_grid g, int order, void *workspace,

@@ -147,6 +147,72 @@ def _dev(*ts):
         _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
 
 
+# Shape and dtype checks of every wrapper. The C ABI receives raw pointers and
+# cannot see extents, so a tensor smaller than its descriptor says would be
+# read or written past its end on the device; these checks run before any
+# pointer leaves Python.
+
+def _shape(t, shape, name):
+    _need(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _is_f32(t, name):
+    import torch
+    _need(t.dtype == torch.float32, f"{name} must be float32, got {t.dtype}")
+
+
+def _same_dtype(ref, name_ref, **ts):
+    for n, t in ts.items():
+        _need(t.dtype == ref.dtype, f"{n} has dtype {t.dtype}, expected {ref.dtype} (the dtype of {name_ref})")
+
+
+def _check_ssd_tensors(x, b, c, dt, a, d, y):
+    """x, y [batch][T][H][W][nheads][headdim]; b, c [batch][T][H][W][ngroups][d_state] in x's dtype;
+    dt float32 [batch][T][H][W][nheads]; a, d float32 [nheads]."""
+    _need(x.dim() == 6, f"x must be [batch][T][H][W][nheads][headdim], got {x.dim()} dims")
+    _dtype(x)
+    grid, nh = tuple(x.shape[:4]), x.shape[4]
+    _shape(y, x.shape, "y")
+    _need(b.dim() == 6 and tuple(b.shape[:4]) == grid, f"b must be [{grid}][ngroups][d_state], got {tuple(b.shape)}")
+    _shape(c, b.shape, "c")
+    _same_dtype(x, "x", y=y, b=b, c=c)
+    _shape(dt, grid + (nh,), "dt")
+    _shape(a, (nh,), "a")
+    _shape(d, (nh,), "d")
+    for n, t in (("dt", dt), ("a", a), ("d", d)):
+        _is_f32(t, n)
+
+
+def _check_mamba_tensors(x, b, c, dt, a, d, y):
+    """x, y [batch][T][H][W][channels]; b, c [batch][T][H][W][d_state] in x's dtype;
+    dt float32 [batch][T][H][W][channels]; a float32 [channels][d_state]; d float32 [channels]."""
+    _need(x.dim() == 5, f"x must be [batch][T][H][W][channels], got {x.dim()} dims")
+    _dtype(x)
+    grid, nch = tuple(x.shape[:4]), x.shape[4]
+    _shape(y, x.shape, "y")
+    _need(b.dim() == 5 and tuple(b.shape[:4]) == grid, f"b must be [{grid}][d_state], got {tuple(b.shape)}")
+    _shape(c, b.shape, "c")
+    _same_dtype(x, "x", y=y, b=b, c=c)
+    _shape(dt, x.shape, "dt")
+    _shape(a, (nch, b.shape[4]), "a")
+    _shape(d, (nch,), "d")
+    for n, t in (("dt", dt), ("a", a), ("d", d)):
+        _is_f32(t, n)
+
+
+def _check_token_tensors(ref_name, ref, **ts):
+    """Attention tensors: all [batch][T][H][W][nheads][headdim] of one shape and dtype."""
+    _need(ref.dim() == 6, f"{ref_name} must be [batch][T][H][W][nheads][headdim], got {ref.dim()} dims")
+    _dtype(ref)
+    for n, t in ts.items():
+        _shape(t, ref.shape, n)
+    _same_dtype(ref, ref_name, **ts)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def grid_of(t) -> Grid:
     """Grid of a [batch][T][H][W][...] tensor."""
     return Grid(*t.shape[:4])
@@ -188,6 +254,7 @@ def _workspace(nbytes: int, like):
 def mate_bissd_scan(x, b, c, dt, a, d, y, order: int, chunk: int, pool=(0, 0, 0), algo: int = ALGO_AUTO,
                     workspace=None, stream=None):
     """y = bidirectional Mamba2 scan of x in RMS ``order`` (see include/mate.h)."""
+    _check_ssd_tensors(x, b, c, dt, a, d, y)
     _dev(x, b, c, dt, a, d, y)
     grid = tuple(x.shape[:4])
     desc = ssd_desc(x, b, chunk, pool, algo)
@@ -195,7 +262,7 @@ def mate_bissd_scan(x, b, c, dt, a, d, y, order: int, chunk: int, pool=(0, 0, 0)
         workspace = _workspace(mate_bissd_workspace_size(grid, desc), x)
     t = SsdTensors(_ptr(x), _ptr(b), _ptr(c), _ptr(dt), _ptr(a), _ptr(d), _ptr(y))
     _check(lib().mate_bissd_scan(ctypes.byref(t), Grid(*grid), order, ctypes.byref(desc), _ptr(workspace),
-                                 workspace.numel(), _stream(stream)))
+                                 _nbytes(workspace), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------
@@ -212,6 +279,7 @@ def mate_bimamba_workspace_size(grid, desc: MambaDesc) -> int:
 
 def mate_bimamba_scan(x, b, c, dt, a, d, y, order: int, pool=(0, 0, 0), workspace=None, stream=None):
     """y = bidirectional Mamba selective scan of x (channels last) in ``order`` (see include/mate.h)."""
+    _check_mamba_tensors(x, b, c, dt, a, d, y)
     _dev(x, b, c, dt, a, d, y)
     grid = tuple(x.shape[:4])
     desc = mamba_desc(x, b, pool)
@@ -219,7 +287,7 @@ def mate_bimamba_scan(x, b, c, dt, a, d, y, order: int, pool=(0, 0, 0), workspac
         workspace = _workspace(mate_bimamba_workspace_size(grid, desc), x)
     t = SsdTensors(_ptr(x), _ptr(b), _ptr(c), _ptr(dt), _ptr(a), _ptr(d), _ptr(y))
     _check(lib().mate_bimamba_scan(ctypes.byref(t), Grid(*grid), order, ctypes.byref(desc), _ptr(workspace),
-                                   workspace.numel(), _stream(stream)))
+                                   _nbytes(workspace), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------
@@ -233,6 +301,7 @@ def tesa_desc(q, window, shift=(0, 0, 0), scale: float = 0.0, algo: int = ALGO_A
 
 def mate_tesa(q, k, v, o, window, shift=(0, 0, 0), scale: float = 0.0, algo: int = ALGO_AUTO, stream=None):
     """o = attention of q, k, v inside (shifted) 3D windows (see include/mate.h)."""
+    _check_token_tensors("q", q, k=k, v=v, o=o)
     _dev(q, k, v, o)
     desc = tesa_desc(q, window, shift, scale, algo)
     t = TesaTensors(_ptr(q), _ptr(k), _ptr(v), _ptr(o))
@@ -246,13 +315,14 @@ def mate_tesa_backward_workspace_size(grid, desc: TesaDesc) -> int:
 def mate_tesa_backward(q, k, v, dout, dq, dk, dv, window, shift=(0, 0, 0), scale: float = 0.0, workspace=None,
                        stream=None):
     """(dq, dk, dv) of mate_tesa for the upstream gradient dout (see include/mate.h)."""
+    _check_token_tensors("q", q, k=k, v=v, dout=dout, dq=dq, dk=dk, dv=dv)
     _dev(q, k, v, dout, dq, dk, dv)
     desc = tesa_desc(q, window, shift, scale)
     if workspace is None:
         workspace = _workspace(mate_tesa_backward_workspace_size(tuple(q.shape[:4]), desc), q)
     t = TesaGradTensors(*(_ptr(a) for a in (q, k, v, dout, dq, dk, dv)))
     _check(lib().mate_tesa_backward(ctypes.byref(t), grid_of(q), ctypes.byref(desc), _ptr(workspace),
-                                    workspace.numel(), _stream(stream)))
+                                    _nbytes(workspace), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------
@@ -267,6 +337,10 @@ def mate_forward(ssd: dict, tesa: dict, order: int, chunk: int, pool, window, sh
                  algo: int = ALGO_AUTO, workspace=None, stream=None):
     """One layer's MATE core: ssd{x,b,c,dt,a,d,y} and tesa{q,k,v,o} (see include/mate.h)."""
     x = ssd["x"]
+    _check_ssd_tensors(*(ssd[k] for k in ("x", "b", "c", "dt", "a", "d", "y")))
+    _check_token_tensors("q", tesa["q"], k=tesa["k"], v=tesa["v"], o=tesa["o"])
+    _need(tuple(tesa["q"].shape[:4]) == tuple(x.shape[:4]),
+          f"the TESA tensors' grid {tuple(tesa['q'].shape[:4])} differs from the scan's {tuple(x.shape[:4])}")
     _dev(*ssd.values(), *tesa.values())
     grid = tuple(x.shape[:4])
     sdesc = ssd_desc(x, ssd["b"], chunk, pool, algo)
@@ -276,7 +350,7 @@ def mate_forward(ssd: dict, tesa: dict, order: int, chunk: int, pool, window, sh
     st = SsdTensors(*(_ptr(ssd[k]) for k in ("x", "b", "c", "dt", "a", "d", "y")))
     tt = TesaTensors(*(_ptr(tesa[k]) for k in ("q", "k", "v", "o")))
     _check(lib().mate_forward(ctypes.byref(st), ctypes.byref(sdesc), ctypes.byref(tt), ctypes.byref(tdesc),
-                              Grid(*grid), order, _ptr(workspace), workspace.numel(), _stream(stream)))
+                              Grid(*grid), order, _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def mate_timing_begin(kernel: str):

@@ -7,7 +7,6 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
-#include <mutex>
 
 #include "launch.hpp"
 
@@ -54,43 +53,6 @@ mate_status prepare_device()
     if ((e = mate::ssd_portable_prepare()) != hipSuccess) return device_fail(e, "hipFuncSetAttribute");
     if ((e = mate::ssd_fast_prepare()) != hipSuccess) return device_fail(e, "hipFuncSetAttribute");
     done[dev].store(1, std::memory_order_release);
-    return MATE_OK;
-}
-
-// Per-device stream on which mate_forward runs the TE branch beside the MA
-// branch, with the two events that fork it from and join it to the caller's
-// stream. Created on first use and kept until the process ends. The mutex
-// keeps one call's record/wait pairs from interleaving with another's.
-struct Side {
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mu;
-Side g_side[64];
-
-// Returns the current device's side stream (caller holds g_side_mu), or
-// nullptr for a device index the table does not cover.
-mate_status side_stream(Side *&out)
-{
-    out = nullptr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return device_fail(e, "hipGetDevice");
-    if (dev < 0 || dev >= 64) return MATE_OK;
-    Side &sd = g_side[dev];
-    if (!sd.stream) {
-        Side n;
-        e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
-        if (e != hipSuccess) {
-            if (n.fork) (void)hipEventDestroy(n.fork);
-            if (n.stream) (void)hipStreamDestroy(n.stream);
-            return device_fail(e, "forward: side stream");
-        }
-        sd = n;
-    }
-    out = &sd;
     return MATE_OK;
 }
 
@@ -262,6 +224,9 @@ mate_status mate_rms_reorder(const void *src, void *dst, mate_grid g, int64_t ro
     if (order < 0 || order > MATE_ORDER_ZIGZAG) return fail(MATE_ERR_SHAPE, "order %d not in 0..4", order);
     const int64_t rows = g.batch * g.T * g.H * g.W;
     if (row_bytes > ((int64_t)1 << 40) / rows) return fail(MATE_ERR_UNSUPPORTED, "tensor above 1 TiB");
+    // the kernels count a row's vectors in 32 bits
+    if (row_bytes >= ((int64_t)1 << 32) - 1024)
+        return fail(MATE_ERR_UNSUPPORTED, "rows of 4 GiB or more are not built");
     const uintptr_t bytes = (uintptr_t)(rows * row_bytes);
     const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
     if (a < b + bytes && b < a + bytes) return fail(MATE_ERR_SHAPE, "src and dst overlap");
@@ -396,39 +361,16 @@ mate_status mate_forward(const mate_ssd_tensors *s, const mate_ssd_desc *sd, con
         return fail(MATE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
     if ((uintptr_t)workspace & 255) return fail(MATE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if ((st = prepare_device()) != MATE_OK) return st;
+    // Both branches run on the caller's stream, one after the other: the TE branch's persistent
+    // workgroups hold every CU, so running it beside the scan on a second stream overlaps little, and
+    // one stream keeps the call free of library-owned streams and events.
     const hipStream_t stream_h = (hipStream_t)stream;
     mate::SsdArgs sa{s->x, s->b, s->c, s->dt, s->a, s->d, s->y};
     mate::TesaArgs ta{a->q, a->k, a->v, a->o};
-    auto run_tesa = [&](hipStream_t st) {
-        return tfast ? mate::tesa_fast(tp, ta, st) : mate::tesa_portable(tp, ta, st);
-    };
-    std::lock_guard<std::mutex> lk(g_side_mu);
-    Side *side = nullptr;
-    if ((st = side_stream(side)) != MATE_OK) return st;
-    if (!side) {
-        hipError_t e = sfast ? mate::ssd_fast(sp, sa, workspace, stream_h) : mate::ssd_portable(sp, sa, workspace, stream_h);
-        if (e != hipSuccess) return device_fail(e, "forward: bissd launch");
-        if ((e = run_tesa(stream_h)) != hipSuccess) return device_fail(e, "forward: tesa launch");
-        return MATE_OK;
-    }
-    // The TE branch runs on the side stream, after everything already queued
-    // on the caller's stream; the caller's stream waits for it before the
-    // scan's output sweep (the fast scan) or after the scan (portable scan).
-    hipError_t e = hipEventRecord(side->fork, stream_h);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
-    if (e != hipSuccess) return device_fail(e, "forward: fork");
-    const hipError_t et = run_tesa(side->stream);
-    e = hipEventRecord(side->join, side->stream);
-    if (e != hipSuccess) return device_fail(e, "forward: join");
-    if (et != hipSuccess) {
-        (void)hipStreamWaitEvent(stream_h, side->join, 0);
-        return device_fail(et, "forward: tesa launch");
-    }
-    e = sfast ? mate::ssd_fast(sp, sa, workspace, stream_h, side->join)
-              : mate::ssd_portable(sp, sa, workspace, stream_h);
-    const hipError_t ej = hipStreamWaitEvent(stream_h, side->join, 0);
+    hipError_t e = tfast ? mate::tesa_fast(tp, ta, stream_h) : mate::tesa_portable(tp, ta, stream_h);
+    if (e != hipSuccess) return device_fail(e, "forward: tesa launch");
+    e = sfast ? mate::ssd_fast(sp, sa, workspace, stream_h) : mate::ssd_portable(sp, sa, workspace, stream_h);
     if (e != hipSuccess) return device_fail(e, "forward: bissd launch");
-    if (ej != hipSuccess) return device_fail(ej, "forward: join");
     return MATE_OK;
 }
 

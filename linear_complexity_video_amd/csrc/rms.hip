@@ -67,7 +67,10 @@ hipError_t launch_typed(const void *src, void *dst, uint32_t batch, uint32_t T, 
     const V *s = (const V *)src;
     V *d = (V *)dst;
     if (vpr >= 64) {
+        // The kernel strides over rows, so the grid is capped: a few rounds of resident blocks on
+        // every CU, far below the launch limit for any row count the ABI accepts.
         uint32_t blocks = (total + 3u) / 4u;
+        if (blocks > 65536u) blocks = 65536u;
         if (inverse)
             rms_rows_wave<V, true><<<blocks, 256, 0, stream>>>(s, d, N, vpr, total, order, flip, T, H, W);
         else

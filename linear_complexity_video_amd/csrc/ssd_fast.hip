@@ -1078,7 +1078,7 @@ Plan make_plan(const SsdProblem &p)
 unsigned grid_of(uint64_t items) { return (unsigned)((items + 7) / 8 * 8); }
 
 template <int S, int Q>
-hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, hipEvent_t before_out)
+hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
 {
     const Plan pl = make_plan(p);
     char *w = (char *)ws;
@@ -1157,10 +1157,6 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, 
         k_seg_pass<<<dim3((P * S + 255) / 256, Hs, Bn), 256, 0, st>>>(segF, segB, segA, hinF, hinB, P * S, pl.nseg,
                                                                       pl.nsegT, p.R > 0 ? 1 : 0);
     }
-    if (before_out) {
-        const hipError_t e = hipStreamWaitEvent(st, before_out, 0);
-        if (e != hipSuccess) return e;
-    }
     {
         timing::Scope ts_(K_SSD_OUT, st);
         k_out<S, Q><<<grid_of(items), NT, 0, st>>>(x, bfrag, cfrag, cb, perm, dtT, csT, a.a, a.d, hbl, delta, hinF,
@@ -1180,12 +1176,12 @@ bool ssd_fast_supports(const SsdProblem &p)
 
 size_t ssd_fast_workspace(const SsdProblem &p) { return make_plan(p).total; }
 
-hipError_t ssd_fast(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st, hipEvent_t before_out)
+hipError_t ssd_fast(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
 {
-    if (p.d_state == 128 && p.chunk == 128) return run<128, 128>(p, a, ws, st, before_out);
-    if (p.d_state == 64 && p.chunk == 64) return run<64, 64>(p, a, ws, st, before_out);
-    if (p.d_state == 128 && p.chunk == 64) return run<128, 64>(p, a, ws, st, before_out);
-    return run<64, 128>(p, a, ws, st, before_out);
+    if (p.d_state == 128 && p.chunk == 128) return run<128, 128>(p, a, ws, st);
+    if (p.d_state == 64 && p.chunk == 64) return run<64, 64>(p, a, ws, st);
+    if (p.d_state == 128 && p.chunk == 64) return run<128, 64>(p, a, ws, st);
+    return run<64, 128>(p, a, ws, st);
 }
 
 hipError_t ssd_fast_prepare() { return hipSuccess; }

@@ -68,7 +68,12 @@ def _f32(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float32)
 
 
+ORACLE_EINVAL, ORACLE_ENOMEM = -1, -2
+
+
 def _check(rc: int, what: str):
+    if rc == ORACLE_ENOMEM:
+        raise MemoryError(f"oracle {what} could not allocate its scratch memory")
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
 
@@ -121,7 +126,7 @@ def bissd(x, B, C, dt, A, D, grid, order: int, pool=(0, 0, 0), heads=None, nthre
     nheads, P = x.shape[-2], x.shape[-1]
     G, S = B.shape[-2], B.shape[-1]
     lo, hi = heads if heads is not None else (0, nheads)
-    y = np.empty((batch, T, H, W, hi - lo, P), dtype=np.float64)
+    y = np.full((batch, T, H, W, hi - lo, P), np.nan, dtype=np.float64)
     rc = _load().oracle_bissd(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), batch, T, H, W,
                               nheads, P, S, G, order, pool[0], pool[1], pool[2], lo, hi,
                               nthreads or default_threads(), _ptr(y))
@@ -140,7 +145,7 @@ def biscan1(x, B, C, dt, A, D, grid, order: int, pool=(0, 0, 0), channels=None, 
     nch, S = x.shape[-1], B.shape[-1]
     assert A.shape == (nch, S) and dt.shape[-1] == nch and D.shape == (nch,)
     lo, hi = channels if channels is not None else (0, nch)
-    y = np.empty((batch, T, H, W, hi - lo), dtype=np.float64)
+    y = np.full((batch, T, H, W, hi - lo), np.nan, dtype=np.float64)
     rc = _load().oracle_biscan1(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), batch, T, H, W,
                                 nch, S, order, pool[0], pool[1], pool[2], lo, hi,
                                 nthreads or default_threads(), _ptr(y))

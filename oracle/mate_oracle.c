@@ -187,12 +187,16 @@ int oracle_review_pool(const float *src, int64_t T, int64_t H, int64_t W, int64_
 /* A tiny work queue over pthreads                                           */
 /* ------------------------------------------------------------------------ */
 
-typedef void (*unit_fn)(void *ctx, int64_t unit);
+/* A unit returns ORACLE_OK, or an error code (ORACLE_ENOMEM when it could not
+ * allocate its scratch); run_units then returns the first error, so a failed
+ * unit fails the whole call instead of leaving its outputs unwritten. */
+typedef int (*unit_fn)(void *ctx, int64_t unit);
 typedef struct {
     unit_fn fn;
     void *ctx;
     int64_t nunits;
     int64_t next;
+    int failed;
     pthread_mutex_t lock;
 } work_queue;
 
@@ -204,18 +208,25 @@ static void *worker(void *arg)
         int64_t u = q->next++;
         pthread_mutex_unlock(&q->lock);
         if (u >= q->nunits) break;
-        q->fn(q->ctx, u);
+        int rc = q->fn(q->ctx, u);
+        if (rc) {
+            pthread_mutex_lock(&q->lock);
+            if (!q->failed) q->failed = rc;
+            q->next = q->nunits; /* no further units start */
+            pthread_mutex_unlock(&q->lock);
+        }
     }
     return NULL;
 }
 
-static void run_units(unit_fn fn, void *ctx, int64_t nunits, int nthreads)
+static int run_units(unit_fn fn, void *ctx, int64_t nunits, int nthreads)
 {
     work_queue q;
     q.fn = fn;
     q.ctx = ctx;
     q.nunits = nunits;
     q.next = 0;
+    q.failed = ORACLE_OK;
     pthread_mutex_init(&q.lock, NULL);
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 1024) nthreads = 1024;
@@ -228,6 +239,7 @@ static void run_units(unit_fn fn, void *ctx, int64_t nunits, int nthreads)
     for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
     free(th);
     pthread_mutex_destroy(&q.lock);
+    return q.failed;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -250,7 +262,7 @@ static void ssd_step(double *h, int P, int S, double decay, double dt, const dou
         for (int s = 0; s < S; ++s) h[p * S + s] = decay * h[p * S + s] + dt * xv[p] * bv[s];
 }
 
-static void ssd_unit(void *vctx, int64_t unit)
+static int ssd_unit(void *vctx, int64_t unit)
 {
     ssd_ctx *c = (ssd_ctx *)vctx;
     int nh = c->head_hi - c->head_lo;
@@ -266,7 +278,7 @@ static void ssd_unit(void *vctx, int64_t unit)
     double *xv = (double *)malloc(sizeof(double) * P);
     double *bv = (double *)malloc(sizeof(double) * S);
     double *out = (dir == 0 ? c->yf : c->yb) + b * N * nh * P;
-    if (!h || !xv || !bv) { free(h); free(xv); free(bv); return; }
+    if (!h || !xv || !bv) { free(h); free(xv); free(bv); return ORACLE_ENOMEM; }
 
     /* Review prefix: rev_o for the forward direction, its reversal for the
      * backward direction. Only the state is kept. */
@@ -298,6 +310,7 @@ static void ssd_unit(void *vctx, int64_t unit)
     free(h);
     free(xv);
     free(bv);
+    return ORACLE_OK;
 }
 
 /* y[b][n][head - head_lo][p] for heads in [head_lo, head_hi).
@@ -352,7 +365,8 @@ int oracle_bissd(const float *x, const float *B, const float *C, const float *dt
         c.nheads = nheads; c.P = P; c.S = S; c.G = G; c.head_lo = head_lo; c.head_hi = head_hi;
         c.seq = seq; c.rx = rx; c.rB = rB; c.rdt = rdt;
         c.yf = y; c.yb = yb;
-        run_units(ssd_unit, &c, batch * nh * 2, nthreads);
+        rc = run_units(ssd_unit, &c, batch * nh * 2, nthreads);
+        if (rc) goto done;
         int64_t total = batch * N * nh * P;
         for (int64_t e = 0; e < total; ++e) y[e] += yb[e];
     }
@@ -385,7 +399,7 @@ typedef struct {
     double *yf, *yb;             /* [b][N][ch_hi - ch_lo] for the forward / backward direction */
 } scan1_ctx;
 
-static void scan1_unit(void *vctx, int64_t unit)
+static int scan1_unit(void *vctx, int64_t unit)
 {
     scan1_ctx *c = (scan1_ctx *)vctx;
     int nc = c->ch_hi - c->ch_lo;
@@ -399,7 +413,7 @@ static void scan1_unit(void *vctx, int64_t unit)
     double D = (double)c->D[ch];
     double *h = (double *)calloc((size_t)S, sizeof(double));
     double *out = (dir == 0 ? c->yf : c->yb) + b * N * nc;
-    if (!h) return;
+    if (!h) return ORACLE_ENOMEM;
     for (int64_t jj = 0; jj < R; ++jj) {
         int64_t j = dir == 0 ? jj : R - 1 - jj;
         double xv = c->rx[(b * R + j) * nch + ch], dt = c->rdt[(b * R + j) * nch + ch];
@@ -419,6 +433,7 @@ static void scan1_unit(void *vctx, int64_t unit)
         out[n * nc + cl] = acc + D * xv;
     }
     free(h);
+    return ORACLE_OK;
 }
 
 /* y[b][n][c - ch_lo] for channels in [ch_lo, ch_hi).
@@ -468,7 +483,8 @@ int oracle_biscan1(const float *x, const float *B, const float *C, const float *
         c.nch = nch; c.S = S; c.ch_lo = ch_lo; c.ch_hi = ch_hi;
         c.seq = seq; c.rx = rx; c.rB = rB; c.rdt = rdt;
         c.yf = y; c.yb = yb;
-        run_units(scan1_unit, &c, batch * nc * 2, nthreads);
+        rc = run_units(scan1_unit, &c, batch * nc * 2, nthreads);
+        if (rc) goto done;
         int64_t total = batch * N * nc;
         for (int64_t e = 0; e < total; ++e) y[e] += yb[e];
     }
@@ -501,7 +517,7 @@ typedef struct {
     double *o;                /* [b][N][nh][d] */
 } tesa_ctx;
 
-static void tesa_unit(void *vctx, int64_t unit)
+static int tesa_unit(void *vctx, int64_t unit)
 {
     tesa_ctx *c = (tesa_ctx *)vctx;
     int nh = c->head_hi - c->head_lo;
@@ -518,7 +534,7 @@ static void tesa_unit(void *vctx, int64_t unit)
     int64_t cap = c->wt * c->wh * c->ww, m = 0;
     int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
     double *sc = (double *)malloc(sizeof(double) * (size_t)cap);
-    if (!tok || !sc) { free(tok); free(sc); return; }
+    if (!tok || !sc) { free(tok); free(sc); return ORACLE_ENOMEM; }
     for (int64_t t = 0; t < c->T; ++t) {
         if (region_id(t, c->wt, c->st) != want_t) continue;
         for (int64_t h = 0; h < c->H; ++h) {
@@ -557,6 +573,7 @@ static void tesa_unit(void *vctx, int64_t unit)
     }
     free(tok);
     free(sc);
+    return ORACLE_OK;
 }
 
 /* Gradients of TESA for an upstream gradient dO of the output. Inside each
@@ -575,7 +592,7 @@ typedef struct {
     double *dq, *dk, *dv; /* [b][N][nh][d] */
 } tesa_bwd_ctx;
 
-static void tesa_bwd_unit(void *vctx, int64_t unit)
+static int tesa_bwd_unit(void *vctx, int64_t unit)
 {
     tesa_bwd_ctx *cb = (tesa_bwd_ctx *)vctx;
     tesa_ctx *c = &cb->f;
@@ -591,7 +608,7 @@ static void tesa_bwd_unit(void *vctx, int64_t unit)
 
     int64_t cap = c->wt * c->wh * c->ww, m = 0;
     int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
-    if (!tok) return;
+    if (!tok) return ORACLE_ENOMEM;
     for (int64_t t = 0; t < c->T; ++t) {
         if (region_id(t, c->wt, c->st) != want_t) continue;
         for (int64_t h = 0; h < c->H; ++h) {
@@ -606,7 +623,7 @@ static void tesa_bwd_unit(void *vctx, int64_t unit)
     if (m > cap) m = cap;
     double *P = (double *)malloc(sizeof(double) * (size_t)(m * m));
     double *dP = (double *)malloc(sizeof(double) * (size_t)(m * m));
-    if (!P || !dP) { free(tok); free(P); free(dP); return; }
+    if (!P || !dP) { free(tok); free(P); free(dP); return ORACLE_ENOMEM; }
 #define ROW(ptr, i) ((ptr) + ((b * c->N + tok[i]) * c->nheads + head) * d)
 #define OUT(ptr, i) ((ptr) + ((b * c->N + tok[i]) * nh + hl) * d)
     /* P: the softmax of each row of S. */
@@ -652,6 +669,7 @@ static void tesa_bwd_unit(void *vctx, int64_t unit)
     free(tok);
     free(P);
     free(dP);
+    return ORACLE_OK;
 }
 
 /* dq, dk, dv [b][n][head - head_lo][e] for heads in [head_lo, head_hi), same
@@ -689,8 +707,7 @@ int oracle_tesa_backward(const float *q, const float *k, const float *v, const f
     c->scale = scale > 0 ? scale : 1.0 / sqrt((double)d);
     c->o = NULL;
     cb.dout = dout; cb.dq = dq; cb.dk = dk; cb.dv = dv;
-    run_units(tesa_bwd_unit, &cb, batch * (int64_t)(head_hi - head_lo) * nregions, nthreads);
-    return ORACLE_OK;
+    return run_units(tesa_bwd_unit, &cb, batch * (int64_t)(head_hi - head_lo) * nregions, nthreads);
 }
 
 /* Number of regions along each axis (useful to build region lists). */
@@ -738,6 +755,5 @@ int oracle_tesa(const float *q, const float *k, const float *v, int64_t batch, i
     c.regions = regions; c.nregions = nregions;
     c.scale = scale > 0 ? scale : 1.0 / sqrt((double)d);
     c.o = o;
-    run_units(tesa_unit, &c, batch * (int64_t)(head_hi - head_lo) * nregions, nthreads);
-    return ORACLE_OK;
+    return run_units(tesa_unit, &c, batch * (int64_t)(head_hi - head_lo) * nregions, nthreads);
 }

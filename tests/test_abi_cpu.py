@@ -61,6 +61,10 @@ def test_rms_validation():
     # more than 2^31 tokens
     assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), B.Grid(1, 2048, 2048, 1024), 2, 0, 0, 0,
                                 None) == B.MATE_ERR_UNSUPPORTED
+    # rows of 4 GiB or more (the kernels count a row's vectors in 32 bits)
+    assert lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), B.Grid(1, 1, 1, 2), 1 << 32, 0, 0, 0,
+                                None) == B.MATE_ERR_UNSUPPORTED
+    assert "4 GiB" in lib.mate_last_error().decode()
 
 
 def _ssd(**kw):

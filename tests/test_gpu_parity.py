@@ -97,7 +97,8 @@ def test_rms_reorder_roundtrip_on_device():
 # Bidirectional SSD
 # ----------------------------------------------------------------------------
 
-SSD_SAMPLE_HEADS = {2: [(0, 1), (41, 42), (79, 80)], 3: [(0, 1), (63, 64)], 4: [(5, 6), (78, 79)]}
+# First, middle and last head of the LinGen-4B-width workloads (every output of a sampled head is compared).
+SSD_SAMPLE_HEADS = {2: [(0, 1), (41, 42), (79, 80)], 3: [(0, 1), (40, 41), (79, 80)], 4: [(0, 1), (40, 41), (79, 80)]}
 
 
 def ssd_device(cfg):
@@ -136,7 +137,8 @@ def test_ssd_parity_full(oracle_mod, cfg, order):
     assert err <= TOL[cfg]
 
 
-@pytest.mark.parametrize("cfg,order", [(2, 0), (3, 0), (3, 1), (3, 2), (3, 3), (3, 4), (4, 0), (4, 3), (4, 4)])
+@pytest.mark.parametrize("cfg,order", [(2, 0), (3, 0), (3, 1), (3, 2), (3, 3), (3, 4), (4, 0), (4, 1), (4, 2), (4, 3),
+                                       (4, 4)])
 def test_ssd_parity_sampled_heads(oracle_mod, cfg, order):
     say(f"ssd cfg{cfg} order{order} (sampled heads)")
     inp, y = run_ssd(cfg, order)
@@ -222,7 +224,12 @@ def sample_regions(counts):
     return sorted((t * nh + h) * nw + w for t, h, w in picks)
 
 
-@pytest.mark.parametrize("cfg,shifted", [(2, False), (2, True), (3, True), (4, False), (4, True)])
+def tesa_sample_heads(wl):
+    """First, middle and last TESA head."""
+    return ((0, 1), (wl.t_heads // 2, wl.t_heads // 2 + 1), (wl.t_heads - 1, wl.t_heads))
+
+
+@pytest.mark.parametrize("cfg,shifted", [(2, False), (2, True), (3, False), (3, True), (4, False), (4, True)])
 def test_tesa_parity_sampled(oracle_mod, cfg, shifted):
     wl = WORKLOADS[cfg]
     say(f"tesa cfg{cfg} shifted={shifted} (sampled)")
@@ -230,7 +237,7 @@ def test_tesa_parity_sampled(oracle_mod, cfg, shifted):
     assert not torch.isnan(o).any().item(), "unwritten outputs"
     shift = wl.layer_shift(shifted)
     regions = sample_regions(oracle_mod.tesa_region_counts(wl.T, wl.H, wl.W, wl.window, shift))
-    for lo, hi in ((0, 1), (wl.t_heads - 1, wl.t_heads)):
+    for lo, hi in tesa_sample_heads(wl):
         qkv = [f32_of(inp[k], (lo, hi)) for k in ("q", "k", "v")]
         want = oracle_mod.tesa(*qkv, wl.grid, wl.window, shift, regions=regions)
         mask = ~np.isnan(want)
@@ -289,6 +296,47 @@ def test_forward_equals_composed_calls(cfg):
         assert torch.equal(y1, y2) and torch.equal(o1, o2)
 
 
+def forward_layers(cfg):
+    """The (order, shifted) layers of a workload's schedule; the one-layer 32^3 workload also runs unshifted."""
+    wl = WORKLOADS[cfg]
+    layers = list(wl.schedule)
+    if cfg == 2:
+        layers.append((0, False))
+    return layers
+
+
+@pytest.mark.parametrize("cfg,order,shifted", [(c, o, s) for c in range(5) for o, s in forward_layers(c)])
+def test_forward_parity_oracle(oracle_mod, cfg, order, shifted):
+    """mate_forward (the call the benchmark times) against the oracle: both branch outputs of every layer of
+    each workload's schedule. The two small workloads are compared in full; the LinGen-4B-width ones on the
+    first, middle and last SSD and TESA heads, and on TESA regions at the corners and centre of the grid and
+    at each axis's edges (so every shifted edge region of a shifted layer is among them)."""
+    wl = WORKLOADS[cfg]
+    shift = wl.layer_shift(shifted)
+    say(f"forward cfg{cfg} order{order} shift{shift}")
+    si, sd = ssd_device(cfg)
+    ti, td = tesa_device(cfg)
+    y, o = torch.full_like(sd["x"], float("nan")), torch.full_like(td["q"], float("nan"))
+    ssd = dict(x=sd["x"], b=sd["B"], c=sd["C"], dt=sd["dt"], a=sd["A"], d=sd["D"], y=y)
+    B.mate_forward(ssd, dict(q=td["q"], k=td["k"], v=td["v"], o=o), order, wl.chunk, wl.pool, wl.window, shift)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any().item() and not torch.isnan(o).any().item(), "unwritten outputs"
+    full = cfg <= 1
+    for lo, hi in ([(0, wl.nheads)] if full else SSD_SAMPLE_HEADS[cfg]):
+        want = oracle_ssd(oracle_mod, cfg, si, order, (lo, hi))
+        err = parity_error(to_f64(y[..., lo:hi, :]), want)
+        say(f"  y heads {lo}:{hi} err={err:.3e}")
+        assert err <= TOL[cfg], ("y", lo, err)
+    regions = None if full else sample_regions(oracle_mod.tesa_region_counts(wl.T, wl.H, wl.W, wl.window, shift))
+    for lo, hi in ([(0, wl.t_heads)] if full else tesa_sample_heads(wl)):
+        want = oracle_mod.tesa(*(f32_of(ti[k], (lo, hi)) for k in ("q", "k", "v")), wl.grid, wl.window, shift,
+                               regions=regions)
+        mask = ~np.isnan(want)
+        err = parity_error(to_f64(o[..., lo:hi, :])[mask], want[mask])
+        say(f"  o heads {lo}:{hi} err={err:.3e}")
+        assert err <= TOL[cfg], ("o", lo, err)
+
+
 # ----------------------------------------------------------------------------
 # MFMA kernels against the oracle on ragged shapes, and against the portable kernels
 # ----------------------------------------------------------------------------
@@ -341,6 +389,53 @@ def test_ssd_fast_uneven_segments(oracle_mod):
             err = parity_error(to_f64(y[..., lo:hi, :]), want)
             say(f"  order {order} heads {lo}:{hi} err={err:.3e}")
             assert err <= 2e-2, (order, lo, err)
+
+
+def _ssd_host_inputs(rng, grid, nh, P, S, G, xs, bs):
+    bsz, T, H, W = grid
+    # scaled, then rounded to bf16: the device and the oracle see the same values
+    rnd = lambda sc, *s: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(
+        (rng.standard_normal(s) * sc).astype(np.float32)))
+    x = rnd(xs, bsz, T, H, W, nh, P)
+    Bm, Cm = rnd(bs, bsz, T, H, W, G, S), rnd(bs, bsz, T, H, W, G, S)
+    dt = np.log1p(np.exp(rng.normal(-1, 0.5, (bsz, T, H, W, nh)))).astype(np.float32)
+    A = -np.exp(rng.uniform(0, 1, nh)).astype(np.float32)
+    D = rng.standard_normal(nh).astype(np.float32)
+    dev = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in (x, Bm, Cm)] + \
+          [torch.from_numpy(a).cuda() for a in (dt, A, D)]
+    return (x, Bm, Cm, dt, A, D), dev
+
+
+@pytest.mark.parametrize("order", [0, 3])
+def test_ssd_fast_large_magnitudes(oracle_mod, order):
+    """The MFMA scan's fp16 intermediates near the top of their stated range: |x| up to ~1.5e3 (N(0,1) x 300)
+    and |B|, |C| up to ~25 (N(0,1) x 5) at d_state 128, so |C.B| reaches ~1.5e3 and the states ~1e4;
+    1024 tokens, 2x4x4 review pooling (32 review tokens), against the oracle."""
+    rng = np.random.default_rng(31 + order)
+    grid, pool = (1, 4, 16, 16), (2, 4, 4)
+    host, dev = _ssd_host_inputs(rng, grid, 4, 64, 128, 1, 300.0, 5.0)
+    say(f"ssd fast large magnitudes order {order}: max|x| {np.abs(host[0]).max():.1f}, "
+        f"max|B| {np.abs(host[1]).max():.1f}")
+    y = torch.full_like(dev[0], float("nan"))
+    B.mate_bissd_scan(*dev, y, order, 128, pool, B.ALGO_FAST)
+    want = oracle_mod.bissd(*host, grid, order, pool)
+    err = parity_error(to_f64(y), want)
+    say(f"  err={err:.3e}")
+    assert err <= 2e-2
+
+
+def test_ssd_portable_beyond_fp16_range(oracle_mod):
+    """Inputs outside the MFMA kernels' range (|x| ~ 1e6, |B|, |C| ~ 1e3, far above fp16's 65504) run on the
+    portable kernels, which compute in fp32, against the oracle."""
+    rng = np.random.default_rng(33)
+    grid, pool = (1, 4, 16, 16), (2, 4, 4)
+    host, dev = _ssd_host_inputs(rng, grid, 4, 64, 128, 1, 1e6, 1e3)
+    y = torch.full_like(dev[0], float("nan"))
+    B.mate_bissd_scan(*dev, y, 1, 128, pool, B.ALGO_PORTABLE)
+    want = oracle_mod.bissd(*host, grid, 1, pool)
+    err = parity_error(to_f64(y), want)
+    say(f"ssd portable beyond fp16 range: err={err:.3e}")
+    assert err <= 2e-2
 
 
 @pytest.mark.parametrize("cfg,order", [(1, 0), (1, 3), (2, 0), (3, 2)])
