@@ -15,9 +15,10 @@
  *
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA storage).
- *     The caller owns every buffer; the library never allocates, frees or
- *     keeps device memory between calls, and creates no streams (the HIP
- *     events of the timing diagnostics below aside).
+ *     The caller owns every buffer; the library never allocates or frees
+ *     device memory and creates no streams (the HIP events of the timing
+ *     diagnostics below aside). The one device memory it holds is the fixed
+ *     scratch array of mate_bissd_scan_noalloc, loaded with the library.
  *   - Token tensors are channels-last: [batch][T][H][W][...], so the canonical
  *     token index is n = (t*H + h)*W + w and a token's channels are contiguous.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
@@ -161,6 +162,23 @@ size_t mate_bissd_workspace_size(mate_grid g, const mate_ssd_desc *d);
  * computes in fp32 throughout and has no such limit beyond fp32's own. */
 mate_status mate_bissd_scan(const mate_ssd_tensors *t, mate_grid g, int order, const mate_ssd_desc *d,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* The same scan for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Instead of a caller-provided workspace it uses a scratch array of
+ * MATE_STATIC_SCRATCH_BYTES that the library holds in device memory on every
+ * GPU it runs on (from the first call on that GPU until the process ends); the
+ * call itself allocates and frees nothing. The caller still passes every input
+ * and output. Problems whose workspace (mate_bissd_workspace_size) exceeds the
+ * array are rejected with MATE_ERR_WORKSPACE before anything is launched; the
+ * array holds the scan of the 8x16x16 (16 heads of 64, d_state 64) and smaller
+ * workloads. Every call on one GPU shares that GPU's array and leaves its
+ * contents behind (the scan needs none of them on entry): calls that overlap on
+ * one GPU (different streams, or threads) race and must be serialised by the
+ * caller. Other arguments, results and errors as mate_bissd_scan. */
+#define MATE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+mate_status mate_bissd_scan_noalloc(const mate_ssd_tensors *t, mate_grid g, int order, const mate_ssd_desc *d,
+                                    void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Bidirectional Mamba (selective scan), the ablation's MA-branch variant     */

@@ -23,8 +23,9 @@ EXPORTED = (
     "mate_rms_reorder", "mate_bissd_workspace_size", "mate_bissd_scan", "mate_tesa",
     "mate_forward_workspace_size", "mate_forward", "mate_status_string", "mate_last_error",
     "mate_abi_version", "mate_timing_begin", "mate_timing_end", "mate_bimamba_workspace_size",
-    "mate_bimamba_scan", "mate_tesa_backward_workspace_size", "mate_tesa_backward",
+    "mate_bimamba_scan", "mate_tesa_backward_workspace_size", "mate_tesa_backward", "mate_bissd_scan_noalloc",
 )
+STATIC_SCRATCH_BYTES = 64 << 20  # MATE_STATIC_SCRATCH_BYTES
 
 
 class MateError(RuntimeError):
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
     L.mate_bissd_workspace_size.argtypes = [Grid, ctypes.POINTER(SsdDesc)]
     L.mate_bissd_workspace_size.restype = SZ
     L.mate_bissd_scan.argtypes = [ctypes.POINTER(SsdTensors), Grid, I32, ctypes.POINTER(SsdDesc), P, SZ, P]
+    L.mate_bissd_scan_noalloc.argtypes = [ctypes.POINTER(SsdTensors), Grid, I32, ctypes.POINTER(SsdDesc), P]
     L.mate_tesa.argtypes = [ctypes.POINTER(TesaTensors), Grid, ctypes.POINTER(TesaDesc), P]
     L.mate_tesa_backward_workspace_size.argtypes = [Grid, ctypes.POINTER(TesaDesc)]
     L.mate_tesa_backward_workspace_size.restype = SZ
@@ -97,8 +99,8 @@ def lib() -> ctypes.CDLL:
     L.mate_forward_workspace_size.restype = SZ
     L.mate_forward.argtypes = [ctypes.POINTER(SsdTensors), ctypes.POINTER(SsdDesc), ctypes.POINTER(TesaTensors),
                                ctypes.POINTER(TesaDesc), Grid, I32, P, SZ, P]
-    for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_bimamba_scan", "mate_tesa", "mate_tesa_backward",
-              "mate_forward"):
+    for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_bissd_scan_noalloc", "mate_bimamba_scan", "mate_tesa",
+              "mate_tesa_backward", "mate_forward"):
         getattr(L, f).restype = ctypes.c_int
     L.mate_status_string.argtypes = [ctypes.c_int]
     L.mate_status_string.restype = ctypes.c_char_p
@@ -263,6 +265,16 @@ def mate_bissd_scan(x, b, c, dt, a, d, y, order: int, chunk: int, pool=(0, 0, 0)
     t = SsdTensors(_ptr(x), _ptr(b), _ptr(c), _ptr(dt), _ptr(a), _ptr(d), _ptr(y))
     _check(lib().mate_bissd_scan(ctypes.byref(t), Grid(*grid), order, ctypes.byref(desc), _ptr(workspace),
                                  _nbytes(workspace), _stream(stream)))
+
+
+def mate_bissd_scan_noalloc(x, b, c, dt, a, d, y, order: int, chunk: int, pool=(0, 0, 0), algo: int = ALGO_AUTO,
+                            stream=None):
+    """mate_bissd_scan on the library's static scratch: no workspace, nothing allocated (see include/mate.h)."""
+    _check_ssd_tensors(x, b, c, dt, a, d, y)
+    _dev(x, b, c, dt, a, d, y)
+    desc = ssd_desc(x, b, chunk, pool, algo)
+    t = SsdTensors(_ptr(x), _ptr(b), _ptr(c), _ptr(dt), _ptr(a), _ptr(d), _ptr(y))
+    _check(lib().mate_bissd_scan_noalloc(ctypes.byref(t), grid_of(x), order, ctypes.byref(desc), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -60,6 +60,10 @@ struct MambaArgs {
 size_t mamba_workspace(const MambaProblem &p);
 hipError_t mamba_scan(const MambaProblem &p, const MambaArgs &a, void *ws, hipStream_t st);
 
+// Device address of the library-held scratch array (MATE_STATIC_SCRATCH_BYTES) on the current
+// device, looked up once per device.
+hipError_t static_scratch(void **out);
+
 hipError_t launch_rms_reorder(const void *src, void *dst, int64_t batch, int64_t T, int64_t H, int64_t W,
                               int64_t row_bytes, int order, int flip, int inverse, hipStream_t stream);
 

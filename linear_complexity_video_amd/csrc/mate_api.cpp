@@ -264,6 +264,28 @@ mate_status mate_bissd_scan(const mate_ssd_tensors *t, mate_grid g, int order, c
     return MATE_OK;
 }
 
+mate_status mate_bissd_scan_noalloc(const mate_ssd_tensors *t, mate_grid g, int order, const mate_ssd_desc *d,
+                                    void *stream)
+{
+    mate_status s = check_ssd_tensors(t);
+    if (s != MATE_OK) return s;
+    mate::SsdProblem p;
+    bool fast = false;
+    if ((s = make_ssd_problem(g, order, d, p, fast)) != MATE_OK) return s;
+    const size_t need = ssd_workspace(p, fast);
+    if (need > MATE_STATIC_SCRATCH_BYTES)
+        return fail(MATE_ERR_WORKSPACE, "the scan needs %zu bytes of scratch; the library's static scratch holds %zu",
+                    need, (size_t)MATE_STATIC_SCRATCH_BYTES);
+    if ((s = prepare_device()) != MATE_OK) return s;
+    void *ws = nullptr;
+    hipError_t e = mate::static_scratch(&ws);
+    if (e != hipSuccess) return device_fail(e, "static scratch address");
+    mate::SsdArgs a{t->x, t->b, t->c, t->dt, t->a, t->d, t->y};
+    e = fast ? mate::ssd_fast(p, a, ws, (hipStream_t)stream) : mate::ssd_portable(p, a, ws, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "bissd launch");
+    return MATE_OK;
+}
+
 size_t mate_bimamba_workspace_size(mate_grid g, const mate_mamba_desc *d)
 {
     mate::MambaProblem p;

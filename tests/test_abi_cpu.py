@@ -233,3 +233,21 @@ def test_timing_arming_rules():
                  "mamba_scan", "tesa_backward"):
         B.mate_timing_begin(name)
         assert B.mate_timing_end() == (0, 0.0)
+
+
+def test_noalloc_scan_validation_and_scratch_limit():
+    """The entry point without a workspace validates like mate_bissd_scan and rejects problems whose scan
+    workspace exceeds the library's static scratch before touching a device."""
+    lib = B.lib()
+    g = B.Grid(1, 8, 16, 16)
+    desc = _ssd(nheads=16, headdim=64, d_state=64, chunk=64, dtype=B.MATE_BF16)
+    need = lib.mate_bissd_workspace_size(g, ctypes.byref(desc))
+    assert 0 < need <= B.STATIC_SCRATCH_BYTES  # the 8x16x16 workload fits
+    t = _ssd_t()
+    assert lib.mate_bissd_scan_noalloc(None, g, 0, ctypes.byref(desc), None) == B.MATE_ERR_NULL
+    assert lib.mate_bissd_scan_noalloc(ctypes.byref(t), g, 7, ctypes.byref(desc), None) == B.MATE_ERR_SHAPE
+    big = _ssd(nheads=80, headdim=64, d_state=128, chunk=128, dtype=B.MATE_BF16)
+    g2 = B.Grid(1, 32, 32, 32)
+    assert lib.mate_bissd_workspace_size(g2, ctypes.byref(big)) > B.STATIC_SCRATCH_BYTES
+    assert lib.mate_bissd_scan_noalloc(ctypes.byref(t), g2, 0, ctypes.byref(big), None) == B.MATE_ERR_WORKSPACE
+    assert "static scratch" in lib.mate_last_error().decode()
