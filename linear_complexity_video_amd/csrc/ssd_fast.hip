@@ -106,6 +106,12 @@ __device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Value of the lane 8 apart in the same row of 16 lanes (a rotation by 8 within the row, i.e. lane ^ 8).
+__device__ __forceinline__ float dpp_ror8(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+
 // Pins a value at this point of the program: an empty volatile asm that reads and redefines it, so the
 // compiler cannot compute with the value (and wait for the load that produced it) any earlier.
 template <typename T>
@@ -146,14 +152,26 @@ __device__ __forceinline__ bf16x8 frag_rm(const __bf16 *tile, int ld, int m_base
 // a position past the end reads row 0 of the batch, a finite row that the
 // kernels multiply by that position's weight dt = 0 (or never store), so no
 // select waits on the load.
-template <int Q, int COLS, int NT>
+// GROUPED: the four pieces of a thread are four rows of one aligned group of 8 rows (rows 8 g + 2 it +
+// (r8 & 1), g = 4 wave + r8 / 2, r8 = lane / 8), so that a thread sums its pieces and one exchange with
+// the lane 8 apart completes a group's sum (the fused review pooling of the state sweep).
+template <int Q, int COLS, int NT, bool GROUPED = false>
 struct Rows {
     static constexpr int UPR = COLS / 8;
     static constexpr int PER = Q * UPR / NT;
     static_assert(Q * UPR % NT == 0, "tile must split evenly over the workgroup");
+    static_assert(!GROUPED || (UPR == 8 && PER == 4 && NT == 256), "grouped rows: 64 columns, 128 rows, 256 threads");
     u32x4 r[PER];
 
-    __device__ __forceinline__ static int row_of(int it) { return (threadIdx.x + NT * it) / UPR; }
+    __device__ __forceinline__ static int row_of(int it)
+    {
+        if constexpr (GROUPED) {
+            const int lane = threadIdx.x & 63, r8 = lane >> 3;
+            return 8 * (4 * (int)(threadIdx.x >> 6) + (r8 >> 1)) + 2 * it + (r8 & 1);
+        } else {
+            return (threadIdx.x + NT * it) / UPR;
+        }
+    }
     __device__ __forceinline__ static int cc_of(int it) { return (threadIdx.x + NT * it) % UPR; }
 
     __device__ __forceinline__ void load(const __bf16 *base, size_t row_stride, const uint32_t *srow,
@@ -542,13 +560,18 @@ __global__ __launch_bounds__(NT) void k_cb(const __bf16 *__restrict__ Bm, const 
 // sums are applied to the B^T operand, so one scaled operand serves both p-blocks. x rows and
 // per-token values come two chunks ahead through two register stages.
 // ---------------------------------------------------------------------------
-template <int S, int Q>
+// POOL: the review pooling of x is fused into the sweep. Every aligned group of 8 consecutive scan
+// positions lies in one pool block (the scan's fastest axis has a pool extent that is a multiple of 8), so
+// the sweep sums each group's x rows (fp32, rounded to bf16) into xpart[b][run][head][P], run = the group's
+// index along that axis; k_pool_runs then averages the runs of each pool block. x is read once for both.
+template <int S, int Q, bool POOL>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, const uint32_t *__restrict__ perm,
                const float *__restrict__ dtT, const float *__restrict__ csT, const float *__restrict__ A,
                __bf16 *__restrict__ hb_local, float *__restrict__ delta, float *__restrict__ segF,
-               float *__restrict__ segB, float *__restrict__ segA, int nheads, int G, uint32_t L, uint32_t Lpad,
-               int nch, int segch, int nseg, int nseg_total, uint32_t total_items)
+               float *__restrict__ segB, float *__restrict__ segA, __bf16 *__restrict__ xpart, uint32_t run_stride,
+               uint32_t nrun, int nheads, int G, uint32_t L, uint32_t Lpad, int nch, int segch, int nseg,
+               int nseg_total, uint32_t total_items)
 {
     constexpr int LX = P + XPAD;
     constexpr int KU = Q / 16;  // k-blocks over the chunk's tokens
@@ -577,9 +600,11 @@ void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, 
     const size_t bh = (size_t)b * nheads + h;
     const size_t drow = bh * Lpad;
     const size_t gch = ((size_t)b * G + g) * nch;
+    using XRows = Rows<Q, P, NT, POOL>;
     struct Stage {
-        Rows<Q, P, NT> xr;
+        XRows xr;
         float tok_d, tok_c, tot;
+        uint32_t prow;  // POOL: canonical token of this thread's first row (~0u past the end)
     };
     Stage stA, stB;
     u32x4 bA[KU], bB[KU];  // B^T operands of the chunk being summed and of the next one
@@ -592,6 +617,7 @@ void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, 
         pvalid = c > c_lo && i < L;
         pnext = perm[pvalid ? i : 0u];  // selected against pvalid where it is stored
         stg.xr.load_nt(x + (size_t)h * P, (size_t)nheads * P, s_row, (size_t)b * L);
+        if constexpr (POOL) stg.prow = s_row[XRows::row_of(0)];
         const size_t crow0 = drow + (size_t)c * Q;
         stg.tok_d = dtT[crow0 + tq];
         stg.tok_c = csT[crow0 + tq];
@@ -634,13 +660,41 @@ void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, 
         __syncthreads();  // previous chunk's reads of xn and the row-table reads are done
         // The staged values are used from here on (their loads had two steps to complete).
 #pragma unroll
-        for (int it = 0; it < Rows<Q, P, NT>::PER; ++it) pin(cur.xr.r[it]);
+        for (int it = 0; it < XRows::PER; ++it) pin(cur.xr.r[it]);
         pin(cur.tok_d);
         pin(cur.tok_c);
         pin(cur.tot);
         pin(pnext);
         const float tot_c = cur.tot;
         cur.xr.template store_f16<LX>((__bf16 *)xn);
+        if constexpr (POOL) {
+            // This thread's four rows of its group, then the lane 8 apart holds the group's other four.
+            float acc[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = lo_f(cur.xr.r[0][e]);
+                acc[2 * e + 1] = hi_f(cur.xr.r[0][e]);
+            }
+#pragma unroll
+            for (int it = 1; it < 4; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += lo_f(cur.xr.r[it][e]);
+                    acc[2 * e + 1] += hi_f(cur.xr.r[it][e]);
+                }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += dpp_ror8(acc[e]);
+            pin(cur.prow);
+            const uint32_t n = cur.prow;
+            if (!(lane & 8) && n != ~0u) {
+                const size_t run = (size_t)(n / (8u * run_stride)) * run_stride + n % run_stride;
+                bf16x8 v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (__bf16)acc[e];
+                __builtin_nontemporal_store(
+                    v, (bf16x8 *)(xpart + (((size_t)b * nrun + run) * nheads + h) * P + 8 * (lane & 7)));
+            }
+        }
         if (row_thread) {
             const float d = cur.tok_d, cs = cur.tok_c;
             s_wb[tid] = (_Float16)(d * ex2((cs - d * a) * LOG2E));
@@ -1027,12 +1081,63 @@ void k_out(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, con
     }
 }
 
+// ---------------------------------------------------------------------------
+// 5. Review tokens of x from the run sums of the fused state sweep: the mean over each pool block (its
+// runs of 8 tokens along the run axis, every token of the block once), rx[b][j][c] with j in RMS order of
+// the pooled grid. grid (ceil(C / 2048), R, batch); 8 channels per thread. axis: 0 t, 1 h, 2 w.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pool_runs(const __bf16 *__restrict__ xpart, bf16_t *__restrict__ rx,
+                                                   int64_t C, uint32_t Tn, uint32_t Hn, uint32_t Wn, int pt, int ph,
+                                                   int pw, int order, int axis)
+{
+    const int64_t ch = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (ch >= C) return;
+    const uint32_t j = blockIdx.y, b = blockIdx.z, R = gridDim.y;
+    const uint32_t Tp = Tn / pt, Hp = Hn / ph, Wp = Wn / pw;
+    const uint32_t np = rms_index32(j, order, Tp, Hp, Wp);
+    const uint32_t tq = np / (Hp * Wp), hq = (np / Wp) % Hp, wq = np % Wp;
+    const size_t nrun = (size_t)Tn * Hn * Wn / 8;
+    const int st = axis == 0 ? 8 : 1, sh = axis == 1 ? 8 : 1, sw = axis == 2 ? 8 : 1;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int dt_ = 0; dt_ < pt; dt_ += st)
+        for (int dh = 0; dh < ph; dh += sh)
+            for (int dw = 0; dw < pw; dw += sw) {
+                const uint32_t t = tq * pt + dt_, h = hq * ph + dh, w = wq * pw + dw;
+                const size_t run = axis == 2 ? ((size_t)t * Hn + h) * (Wn / 8) + w / 8
+                                 : axis == 1 ? ((size_t)t * (Hn / 8) + h / 8) * Wn + w
+                                             : ((size_t)(t / 8) * Hn + h) * Wn + w;
+                const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(xpart + ((size_t)b * nrun + run) * C + ch));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += lo_f(v[e]);
+                    acc[2 * e + 1] += hi_f(v[e]);
+                }
+            }
+    const float inv = 1.f / (float)(pt * ph * pw);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    *(u32x4 *)(rx + ((size_t)b * R + j) * C + ch) = o;
+}
+
+// The fused review pooling applies when every aligned group of 8 consecutive positions of the scan lies in
+// one pool block: the scan's fastest axis (w for orders 0 and 4, h for order 1, t for orders 2 and 3) has a
+// pool extent that is a multiple of 8 (so the grid's extent along it is too) and x rows are 64 channels.
+// Returns that axis (0 t, 1 h, 2 w), or -1.
+int fused_pool_axis(const SsdProblem &p)
+{
+    if (p.R <= 0 || p.chunk != 128) return -1;
+    const int axis = (p.order == 0 || p.order == 4) ? 2 : p.order == 1 ? 1 : 0;
+    const int pool = axis == 2 ? p.pool_w : axis == 1 ? p.pool_h : p.pool_t;
+    return pool % 8 == 0 ? axis : -1;
+}
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
     int nseg, segch, nsegT;
     size_t perm, dtT, csT, cb, cfrag, bfrag, hbl, delta, segF, segB, segA, hinF, hinB, ytrash, rx, rB, rdt, rdtT, rcsT,
-        total;
+        xpart, total;
 };
 
 Plan make_plan(const SsdProblem &p)
@@ -1070,6 +1175,14 @@ Plan make_plan(const SsdProblem &p)
         pl.rdt = take(B * p.R * Hs * 4);
         pl.rdtT = take(B * Hs * Rpad * 4);
         pl.rcsT = take(B * Hs * Rpad * 4);
+        // run sums of the fused pooling (any order may take it: sized for all)
+        SsdProblem q = p;
+        bool any = false;
+        for (int o = 0; o <= 4 && !any; ++o) {
+            q.order = o;
+            any = fused_pool_axis(q) >= 0;
+        }
+        if (any) pl.xpart = take(B * (size_t)(p.N / 8) * Hs * P * 2);
     }
     pl.total = off;
     return pl;
@@ -1096,6 +1209,39 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
     const uint32_t T = (uint32_t)p.T, H = (uint32_t)p.H, W = (uint32_t)p.W;
     const __bf16 *x = (const __bf16 *)a.x, *Bm = (const __bf16 *)a.b, *Cm = (const __bf16 *)a.c;
 
+    const int pool_axis = fused_pool_axis(p);
+    __bf16 *xpart = pool_axis >= 0 ? (__bf16 *)(w + pl.xpart) : nullptr;
+    const uint32_t run_stride = pool_axis == 2 ? 1u : pool_axis == 1 ? W : H * W;
+    {
+        timing::Scope ts_(K_SSD_PREP, st);
+        k_perm<<<(N + 255) / 256, 256, 0, st>>>(perm, N, p.order, T, H, W);
+    }
+    {
+        timing::Scope ts_(K_SSD_PREP, st);
+        ssd::k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, Bn), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q,
+                                                                             p.order, T, H, W, perm);
+    }
+    {
+        timing::Scope ts_(K_SSD_CB, st);
+        k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, cfrag, bfrag, G, N);
+    }
+    const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
+    {
+        timing::Scope ts_(K_SSD_STATES, st);
+        if constexpr (Q == 128) {
+            if (xpart) {
+                k_states<S, Q, true><<<grid_of(items), NT, 0, st>>>(
+                    x, bfrag, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, xpart, run_stride, N / 8, Hs, G, N,
+                    Lpad, p.nch, pl.segch, pl.nseg, pl.nsegT, (uint32_t)items);
+            }
+        }
+        if (!xpart)
+            k_states<S, Q, false><<<grid_of(items), NT, 0, st>>>(x, bfrag, perm, dtT, csT, a.a, hbl, delta, segF, segB,
+                                                                 segA, nullptr, 1u, 0u, Hs, G, N, Lpad, p.nch,
+                                                                 pl.segch, pl.nseg, pl.nsegT, (uint32_t)items);
+    }
+    // Review tokens (after the main sweep, which leaves the run sums of x when the pooling is fused):
+    // pooled x, B and dt, their dt table, and the review segment's summaries.
     if (p.R > 0) {
         bf16_t *rx = (bf16_t *)(w + pl.rx), *rB = (bf16_t *)(w + pl.rB);
         float *rdt = (float *)(w + pl.rdt), *rdtT = (float *)(w + pl.rdtT), *rcsT = (float *)(w + pl.rcsT);
@@ -1103,8 +1249,12 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
         const int64_t Cx = (int64_t)Hs * P, Cb = (int64_t)G * S;
         {
             timing::Scope ts_(K_SSD_POOL, st);
-            ssd::k_pool8<bf16_t><<<dim3((Cx + 2047) / 2048, R, Bn), 256, 0, st>>>(
-                (const bf16_t *)a.x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+            if (xpart)
+                k_pool_runs<<<dim3((Cx / 8 + 255) / 256, R, Bn), 256, 0, st>>>(
+                    xpart, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order, pool_axis);
+            else
+                ssd::k_pool8<bf16_t><<<dim3((Cx + 2047) / 2048, R, Bn), 256, 0, st>>>(
+                    (const bf16_t *)a.x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
         }
         {
             timing::Scope ts_(K_SSD_POOL, st);
@@ -1125,32 +1275,13 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
             ssd::k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, Bn), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad,
                                                                                     Q, 0, 1, 1, R);
         }
-        const uint64_t items = (uint64_t)Bn * Hs;
+        const uint64_t ritems = (uint64_t)Bn * Hs;
         {
             timing::Scope ts_(K_SSD_STATES, st);
-            k_states_review<S, Q><<<grid_of(items), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, rdtT, rcsT,
-                                                                 a.a, segF, segB, segA, Hs, G, R, Rpad, p.nchR,
-                                                                 p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)items);
+            k_states_review<S, Q><<<grid_of(ritems), Q * 4, 0, st>>>((const __bf16 *)rx, (const __bf16 *)rB, rdtT, rcsT,
+                                                                  a.a, segF, segB, segA, Hs, G, R, Rpad, p.nchR,
+                                                                  p.nchR, 1, pl.nseg, pl.nsegT, (uint32_t)ritems);
         }
-    }
-    {
-        timing::Scope ts_(K_SSD_PREP, st);
-        k_perm<<<(N + 255) / 256, 256, 0, st>>>(perm, N, p.order, T, H, W);
-    }
-    {
-        timing::Scope ts_(K_SSD_PREP, st);
-        ssd::k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, Bn), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q,
-                                                                             p.order, T, H, W, perm);
-    }
-    {
-        timing::Scope ts_(K_SSD_CB, st);
-        k_cb<S, Q><<<dim3(p.nch, G, Bn), NT, 0, st>>>(Bm, Cm, perm, cb, cfrag, bfrag, G, N);
-    }
-    const uint64_t items = (uint64_t)Bn * pl.nseg * Hs;
-    {
-        timing::Scope ts_(K_SSD_STATES, st);
-        k_states<S, Q><<<grid_of(items), NT, 0, st>>>(x, bfrag, perm, dtT, csT, a.a, hbl, delta, segF, segB, segA, Hs,
-                                                      G, N, Lpad, p.nch, pl.segch, pl.nseg, pl.nsegT, (uint32_t)items);
     }
     {
         timing::Scope ts_(K_SSD_SEG_PASS, st);

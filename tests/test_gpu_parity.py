@@ -362,6 +362,26 @@ def test_ssd_fast_ragged_with_review(oracle_mod, S, chunk):
         assert err <= 2e-2, (order, err)
 
 
+@pytest.mark.parametrize("grid,pool,orders", [((2, 16, 3, 5), (8, 1, 1), (2, 3)),
+                                               ((2, 2, 3, 40), (1, 1, 8), (0, 4)),
+                                               ((2, 2, 16, 5), (1, 8, 1), (1,)),
+                                               ((1, 16, 16, 16), (8, 8, 8), (0, 1, 2, 3, 4))])
+def test_ssd_fast_fused_review_pooling(oracle_mod, grid, pool, orders):
+    """Review pooling fused into the state sweep (the pool extent along the scan's fastest axis is a multiple of
+    8): ragged sequences of 160-240 tokens over 128-token chunks, batch 2, every order whose fastest axis
+    qualifies, and a 16^3 grid in every order; d_state 128, chunk 128, against the oracle."""
+    rng = np.random.default_rng(sum(grid) + sum(pool))
+    host, dev = _ssd_host_inputs(rng, grid, 4, 64, 128, 1, 0.125, 128 ** -0.5)
+    y = torch.full_like(dev[0], float("nan"))
+    for order in orders:
+        say(f"ssd fused pooling grid {grid} pool {pool} order {order}")
+        B.mate_bissd_scan(*dev, y, order, 128, pool, B.ALGO_FAST)
+        want = oracle_mod.bissd(*host, grid, order, pool)
+        err = parity_error(to_f64(y), want)
+        say(f"  err={err:.3e}")
+        assert err <= 2e-2, (order, err)
+
+
 def test_ssd_fast_uneven_segments(oracle_mod):
     """512 heads over 1450 tokens (chunk 64: 23 chunks, the last ragged) make the scan cut each head
     into segments of 5, 5, 5, 5 and 3 chunks, so one workgroup runs both the paired steps and the odd
