@@ -45,6 +45,7 @@ def _load():
     lib.oracle_rms_reorder.argtypes = [p, p, i64, i64, i64, i64, i64, i32, i32, i32]
     lib.oracle_review_pool.argtypes = [p, i64, i64, i64, i64, i32, i32, i32, i32, p]
     lib.oracle_bissd.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64] + [i32] * 11 + [p]
+    lib.oracle_bissd_backward.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64] + [i32] * 11 + [p] * 6
     lib.oracle_biscan1.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64] + [i32] * 9 + [p]
     lib.oracle_tesa_region_counts.argtypes = [i64, i64, i64] + [i32] * 6 + [p]
     lib.oracle_tesa.argtypes = (
@@ -53,7 +54,7 @@ def _load():
     lib.oracle_tesa_backward.argtypes = (
         [p, p, p, p, i64, i64, i64, i64] + [i32] * 8 + [ctypes.c_double, i32, i32, p, i64, i32, p, p, p]
     )
-    for f in ("oracle_rms_sequence", "oracle_rms_reorder", "oracle_review_pool", "oracle_bissd",
+    for f in ("oracle_rms_sequence", "oracle_rms_reorder", "oracle_review_pool", "oracle_bissd", "oracle_bissd_backward",
               "oracle_biscan1", "oracle_tesa_region_counts", "oracle_tesa", "oracle_tesa_backward"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -132,6 +133,28 @@ def bissd(x, B, C, dt, A, D, grid, order: int, pool=(0, 0, 0), heads=None, nthre
                               nthreads or default_threads(), _ptr(y))
     _check(rc, "bissd")
     return y
+
+
+def bissd_backward(x, B, C, dt, A, D, dy, grid, order: int, pool=(0, 0, 0), heads=None, nthreads=None) -> dict:
+    """Gradients of ``bissd`` for the upstream gradient ``dy`` (same layout as y), float64:
+    dx [b][T][H][W][nh][P], dB and dC [b][T][H][W][G][S] (summed over the heads in ``heads`` only),
+    ddt [b][T][H][W][nh], dA and dD [nh] (summed over the batch); ``heads`` is a (lo, hi) range."""
+    batch, T, H, W = grid
+    x, B, C, dt, A, D, dy = (_f32(a) for a in (x, B, C, dt, A, D, dy))
+    nheads, P = x.shape[-2], x.shape[-1]
+    G, S = B.shape[-2], B.shape[-1]
+    assert dy.shape == x.shape
+    lo, hi = heads if heads is not None else (0, nheads)
+    nh = hi - lo
+    out = {"dx": np.full((batch, T, H, W, nh, P), np.nan), "dB": np.full((batch, T, H, W, G, S), np.nan),
+           "dC": np.full((batch, T, H, W, G, S), np.nan), "ddt": np.full((batch, T, H, W, nh), np.nan),
+           "dA": np.full(nh, np.nan), "dD": np.full(nh, np.nan)}
+    rc = _load().oracle_bissd_backward(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), _ptr(dy), batch, T, H,
+                                       W, nheads, P, S, G, order, pool[0], pool[1], pool[2], lo, hi,
+                                       nthreads or default_threads(),
+                                       *(_ptr(out[k]) for k in ("dx", "dB", "dC", "ddt", "dA", "dD")))
+    _check(rc, "bissd_backward")
+    return out
 
 
 def biscan1(x, B, C, dt, A, D, grid, order: int, pool=(0, 0, 0), channels=None, nthreads=None) -> np.ndarray:

@@ -380,6 +380,287 @@ done:
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward of the bidirectional Mamba2 scan                                 */
+/* ------------------------------------------------------------------------ */
+/* Gradients of the scan above for an upstream gradient dy of its output y
+ * (the MA half of training the MATE block; the xllm-io review, section 三,
+ * "训练配方", trains LinGen end to end). For one direction, over its sequence
+ * z (review tokens, then the main tokens, as in the forward), with
+ * a_u = exp(dt_u A), the forward recurrence
+ *     h_u = a_u h_{u-1} + dt_u x_u B_u^T,   y_u = h_u C_u + D x_u
+ * has the adjoint G_u = dL/dh_u, run from the end of z to its start:
+ *     G_u = dy_u C_u^T + a_{u+1} G_{u+1}       (G after the last token is 0)
+ * and the chain rule through each step gives, at position u,
+ *     dx_u   += dt_u G_u B_u + D dy_u
+ *     dB_u   += dt_u G_u^T x_u
+ *     dC_u   += h_u^T dy_u
+ *     ddt_u  += x_u^T G_u B_u + A a_u <h_{u-1}, G_u>
+ *     dA     += dt_u a_u <h_{u-1}, G_u>
+ *     dD     += x_u . dy_u
+ * (<.,.> the sum of the elementwise product of two P x S matrices). dy is 0 at
+ * review positions (their outputs are dropped), so pooled C gets no gradient;
+ * the review tokens' dx, dB and ddt flow back through the average pooling: each
+ * token of a pool block receives the block's gradient divided by the block's
+ * token count. Both directions add into the same gradients.
+ *
+ * The states h_u that the adjoint needs are recomputed: the forward pass keeps
+ * the state before every block of ORACLE_CKPT positions, and the backward pass
+ * recomputes each block's states from its checkpoint before walking it
+ * backwards. */
+#define ORACLE_CKPT 256
+
+typedef struct {
+    const float *x, *B, *C, *dt, *A, *D, *dy;
+    int64_t batch, N, R;
+    int nheads, P, S, G, head_lo, head_hi;
+    const int64_t *seq;            /* scan order, N entries */
+    const double *rx, *rB, *rdt;   /* review tokens per batch: [b][R][nheads*P], [b][R][G*S], [b][R][nheads] */
+    /* per (batch, local head) results, written only by that unit */
+    double *dx;                    /* [b][N][nh][P] */
+    double *dBh, *dCh;             /* [b][nh][N][S]: this head's part of dB, dC */
+    double *ddt;                   /* [b][N][nh] */
+    double *drx, *drB, *drdt;      /* [b][nh][R][P], [b][nh][R][S], [b][nh][R]: review-token gradients */
+    double *dA, *dD;               /* [b][nh] */
+} ssd_bwd_ctx;
+
+static int ssd_bwd_unit(void *vctx, int64_t unit)
+{
+    ssd_bwd_ctx *c = (ssd_bwd_ctx *)vctx;
+    const int nh = c->head_hi - c->head_lo;
+    const int64_t b = unit / nh;
+    const int hl = (int)(unit % nh);
+    const int head = c->head_lo + hl;
+    const int g = head / (c->nheads / c->G);
+    const int P = c->P, S = c->S;
+    const int64_t N = c->N, R = c->R, L = R + N, PS = (int64_t)P * S;
+    const double A = (double)c->A[head], D = (double)c->D[head];
+    const int64_t nblk = (L + ORACLE_CKPT - 1) / ORACLE_CKPT;
+
+    double *ckpt = (double *)malloc(sizeof(double) * (size_t)(nblk * PS));   /* state before each block */
+    double *hb = (double *)malloc(sizeof(double) * (size_t)(ORACLE_CKPT * PS)); /* states of one block */
+    double *h = (double *)malloc(sizeof(double) * (size_t)PS);
+    double *Gm = (double *)malloc(sizeof(double) * (size_t)PS);               /* G_u */
+    double *carry = (double *)malloc(sizeof(double) * (size_t)PS);            /* a_{u+1} G_{u+1} */
+    double *xv = (double *)malloc(sizeof(double) * (size_t)P), *dyv = (double *)malloc(sizeof(double) * (size_t)P);
+    double *bv = (double *)malloc(sizeof(double) * (size_t)S), *cv = (double *)malloc(sizeof(double) * (size_t)S);
+    double *gB = (double *)malloc(sizeof(double) * (size_t)P);
+    if (!ckpt || !hb || !h || !Gm || !carry || !xv || !dyv || !bv || !cv || !gB) {
+        free(ckpt); free(hb); free(h); free(Gm); free(carry); free(xv); free(dyv); free(bv); free(cv); free(gB);
+        return ORACLE_ENOMEM;
+    }
+    double dA = 0.0, dD = 0.0;
+    for (int dir = 0; dir < 2; ++dir) {
+        /* Position u of this direction's sequence: its inputs, and where its gradients go. */
+#define LOAD(u)                                                                                        \
+    int64_t rj = -1, n = -1;                                                                           \
+    double dtu;                                                                                        \
+    if ((u) < R) {                                                                                     \
+        rj = dir == 0 ? (u) : R - 1 - (u);                                                             \
+        const double *rxp = c->rx + (b * R + rj) * c->nheads * P + (int64_t)head * P;                  \
+        const double *rbp = c->rB + (b * R + rj) * c->G * S + (int64_t)g * S;                          \
+        for (int p = 0; p < P; ++p) { xv[p] = rxp[p]; dyv[p] = 0.0; }                                  \
+        for (int s = 0; s < S; ++s) { bv[s] = rbp[s]; cv[s] = 0.0; }                                   \
+        dtu = c->rdt[(b * R + rj) * c->nheads + head];                                                 \
+    } else {                                                                                           \
+        const int64_t i = (u) - R;                                                                     \
+        n = c->seq[dir == 0 ? i : N - 1 - i];                                                          \
+        const float *xr = c->x + ((b * N + n) * c->nheads + head) * P;                                 \
+        const float *dyr = c->dy + ((b * N + n) * c->nheads + head) * P;                               \
+        const float *Br = c->B + ((b * N + n) * c->G + g) * S;                                         \
+        const float *Cr = c->C + ((b * N + n) * c->G + g) * S;                                         \
+        for (int p = 0; p < P; ++p) { xv[p] = (double)xr[p]; dyv[p] = (double)dyr[p]; }               \
+        for (int s = 0; s < S; ++s) { bv[s] = (double)Br[s]; cv[s] = (double)Cr[s]; }                  \
+        dtu = (double)c->dt[(b * N + n) * c->nheads + head];                                           \
+    }
+        /* Forward pass: the state before every block. */
+        for (int64_t e = 0; e < PS; ++e) h[e] = 0.0;
+        for (int64_t u = 0; u < L; ++u) {
+            if (u % ORACLE_CKPT == 0) memcpy(ckpt + (u / ORACLE_CKPT) * PS, h, sizeof(double) * (size_t)PS);
+            LOAD(u);
+            (void)rj; (void)n;
+            ssd_step(h, P, S, exp(dtu * A), dtu, xv, bv);
+        }
+        /* Backward pass, block by block from the end. */
+        for (int64_t e = 0; e < PS; ++e) carry[e] = 0.0;
+        for (int64_t k = nblk - 1; k >= 0; --k) {
+            const int64_t u0 = k * ORACLE_CKPT, u1 = u0 + ORACLE_CKPT < L ? u0 + ORACLE_CKPT : L;
+            memcpy(h, ckpt + k * PS, sizeof(double) * (size_t)PS);
+            for (int64_t u = u0; u < u1; ++u) {
+                LOAD(u);
+                (void)rj; (void)n;
+                ssd_step(h, P, S, exp(dtu * A), dtu, xv, bv);
+                memcpy(hb + (u - u0) * PS, h, sizeof(double) * (size_t)PS);
+            }
+            for (int64_t u = u1 - 1; u >= u0; --u) {
+                LOAD(u);
+                const double au = exp(dtu * A);
+                const double *hcur = hb + (u - u0) * PS;
+                const double *hprev = u > u0 ? hb + (u - 1 - u0) * PS : ckpt + k * PS;
+                double gh = 0.0, xgb = 0.0;
+                for (int p = 0; p < P; ++p) {
+                    double acc = 0.0;
+                    for (int s = 0; s < S; ++s) {
+                        const double gv = dyv[p] * cv[s] + carry[p * S + s];
+                        Gm[p * S + s] = gv;
+                        acc += gv * bv[s];
+                        gh += gv * hprev[p * S + s];
+                    }
+                    gB[p] = acc;
+                    xgb += xv[p] * acc;
+                }
+                double *gx, *gbb, *gdt;
+                if (rj >= 0) {
+                    gx = c->drx + ((b * nh + hl) * R + rj) * P;
+                    gbb = c->drB + ((b * nh + hl) * R + rj) * S;
+                    gdt = c->drdt + (b * nh + hl) * R + rj;
+                } else {
+                    gx = c->dx + ((b * N + n) * nh + hl) * P;
+                    gbb = c->dBh + ((b * nh + hl) * N + n) * S;
+                    gdt = c->ddt + (b * N + n) * nh + hl;
+                    double *gc = c->dCh + ((b * nh + hl) * N + n) * S;
+                    for (int s = 0; s < S; ++s) {
+                        double acc = 0.0;
+                        for (int p = 0; p < P; ++p) acc += hcur[p * S + s] * dyv[p];
+                        gc[s] += acc;
+                    }
+                }
+                for (int p = 0; p < P; ++p) gx[p] += dtu * gB[p] + D * dyv[p];
+                for (int s = 0; s < S; ++s) {
+                    double acc = 0.0;
+                    for (int p = 0; p < P; ++p) acc += Gm[p * S + s] * xv[p];
+                    gbb[s] += dtu * acc;
+                }
+                *gdt += xgb + A * au * gh;
+                dA += dtu * au * gh;
+                for (int p = 0; p < P; ++p) dD += xv[p] * dyv[p];
+                for (int64_t e = 0; e < PS; ++e) carry[e] = au * Gm[e];
+            }
+        }
+#undef LOAD
+    }
+    c->dA[b * nh + hl] = dA;
+    c->dD[b * nh + hl] = dD;
+    free(ckpt); free(hb); free(h); free(Gm); free(carry); free(xv); free(dyv); free(bv); free(cv); free(gB);
+    return ORACLE_OK;
+}
+
+/* Gradients of oracle_bissd for the upstream gradient dy [batch][T][H][W][nheads][P]
+ * (same arguments as oracle_bissd otherwise), for the heads in [head_lo, head_hi):
+ *   dx  [batch][T][H][W][nh][P]      ddt [batch][T][H][W][nh]
+ *   dB, dC [batch][T][H][W][G][S]   (summed over the heads in the range only)
+ *   dA, dD [nh]                      (summed over the batch)
+ * with nh = head_hi - head_lo. */
+int oracle_bissd_backward(const float *x, const float *B, const float *C, const float *dt, const float *A,
+                          const float *D, const float *dy, int64_t batch, int64_t T, int64_t H, int64_t W,
+                          int nheads, int P, int S, int G, int order, int pool_t, int pool_h, int pool_w,
+                          int head_lo, int head_hi, int nthreads, double *dx, double *dB, double *dC, double *ddt,
+                          double *dA, double *dD)
+{
+    if (!x || !B || !C || !dt || !A || !D || !dy || !dx || !dB || !dC || !ddt || !dA || !dD) return ORACLE_EINVAL;
+    if (batch <= 0 || T <= 0 || H <= 0 || W <= 0 || nheads <= 0 || P <= 0 || S <= 0 || G <= 0)
+        return ORACLE_EINVAL;
+    if (nheads % G || order < 0 || order > 4) return ORACLE_EINVAL;
+    if (head_lo < 0 || head_hi > nheads || head_lo >= head_hi) return ORACLE_EINVAL;
+    const int pooled = pool_t || pool_h || pool_w;
+    if (pooled && (pool_t <= 0 || pool_h <= 0 || pool_w <= 0 || T % pool_t || H % pool_h || W % pool_w))
+        return ORACLE_EINVAL;
+    const int64_t N = T * H * W;
+    const int64_t Tp = pooled ? T / pool_t : 0, Hp = pooled ? H / pool_h : 0, Wp = pooled ? W / pool_w : 0;
+    const int64_t R = Tp * Hp * Wp;
+    const int nh = head_hi - head_lo;
+    int rc = ORACLE_OK;
+    int64_t *seq = (int64_t *)malloc(sizeof(int64_t) * (size_t)N);
+    int64_t *rseq = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R > 0 ? R : 1));
+    double *dBh = (double *)calloc((size_t)(batch * nh * N * S), sizeof(double));
+    double *dCh = (double *)calloc((size_t)(batch * nh * N * S), sizeof(double));
+    double *drx = (double *)calloc((size_t)(batch * nh * (R > 0 ? R : 1) * P), sizeof(double));
+    double *drB = (double *)calloc((size_t)(batch * nh * (R > 0 ? R : 1) * S), sizeof(double));
+    double *drdt = (double *)calloc((size_t)(batch * nh * (R > 0 ? R : 1)), sizeof(double));
+    double *dAb = (double *)calloc((size_t)(batch * nh), sizeof(double));
+    double *dDb = (double *)calloc((size_t)(batch * nh), sizeof(double));
+    double *rx = NULL, *rB = NULL, *rdt = NULL;
+    if (!seq || !rseq || !dBh || !dCh || !drx || !drB || !drdt || !dAb || !dDb) { rc = ORACLE_ENOMEM; goto done; }
+    rc = oracle_rms_sequence(T, H, W, order, 0, seq);
+    if (rc) goto done;
+    if (R > 0) {
+        rc = oracle_rms_sequence(Tp, Hp, Wp, order, 0, rseq);
+        if (rc) goto done;
+        rx = (double *)malloc(sizeof(double) * (size_t)(batch * R * nheads * P));
+        rB = (double *)malloc(sizeof(double) * (size_t)(batch * R * G * S));
+        rdt = (double *)malloc(sizeof(double) * (size_t)(batch * R * nheads));
+        if (!rx || !rB || !rdt) { rc = ORACLE_ENOMEM; goto done; }
+        for (int64_t b = 0; b < batch && !rc; ++b) {
+            rc = oracle_review_pool(x + b * N * nheads * P, T, H, W, (int64_t)nheads * P, pool_t, pool_h, pool_w,
+                                    order, rx + b * R * nheads * P);
+            if (!rc)
+                rc = oracle_review_pool(B + b * N * G * S, T, H, W, (int64_t)G * S, pool_t, pool_h, pool_w, order,
+                                        rB + b * R * G * S);
+            if (!rc)
+                rc = oracle_review_pool(dt + b * N * nheads, T, H, W, nheads, pool_t, pool_h, pool_w, order,
+                                        rdt + b * R * nheads);
+        }
+        if (rc) goto done;
+    }
+    for (int64_t e = 0; e < batch * N * nh * P; ++e) dx[e] = 0.0;
+    for (int64_t e = 0; e < batch * N * nh; ++e) ddt[e] = 0.0;
+    {
+        ssd_bwd_ctx c;
+        c.x = x; c.B = B; c.C = C; c.dt = dt; c.A = A; c.D = D; c.dy = dy;
+        c.batch = batch; c.N = N; c.R = R;
+        c.nheads = nheads; c.P = P; c.S = S; c.G = G; c.head_lo = head_lo; c.head_hi = head_hi;
+        c.seq = seq; c.rx = rx; c.rB = rB; c.rdt = rdt;
+        c.dx = dx; c.dBh = dBh; c.dCh = dCh; c.ddt = ddt; c.drx = drx; c.drB = drB; c.drdt = drdt;
+        c.dA = dAb; c.dD = dDb;
+        rc = run_units(ssd_bwd_unit, &c, batch * nh, nthreads);
+        if (rc) goto done;
+    }
+    /* Review tokens back through the average pooling: every token of the block of review token j
+     * (the pooled grid unrolled in the scan order) receives its gradient over the block's size. */
+    if (R > 0) {
+        const double inv = 1.0 / ((double)pool_t * pool_h * pool_w);
+        for (int64_t b = 0; b < batch; ++b)
+            for (int hl = 0; hl < nh; ++hl)
+                for (int64_t j = 0; j < R; ++j) {
+                    const int64_t pc = rseq[j];
+                    const int64_t tq = pc / (Hp * Wp), hq = (pc / Wp) % Hp, wq = pc % Wp;
+                    const double *gx = drx + ((b * nh + hl) * R + j) * P;
+                    const double *gb = drB + ((b * nh + hl) * R + j) * S;
+                    const double gd = drdt[(b * nh + hl) * R + j];
+                    for (int64_t t = tq * pool_t; t < (tq + 1) * pool_t; ++t)
+                        for (int64_t hh = hq * pool_h; hh < (hq + 1) * pool_h; ++hh)
+                            for (int64_t w = wq * pool_w; w < (wq + 1) * pool_w; ++w) {
+                                const int64_t n = (t * H + hh) * W + w;
+                                for (int p = 0; p < P; ++p) dx[((b * N + n) * nh + hl) * P + p] += gx[p] * inv;
+                                for (int s = 0; s < S; ++s) dBh[((b * nh + hl) * N + n) * S + s] += gb[s] * inv;
+                                ddt[(b * N + n) * nh + hl] += gd * inv;
+                            }
+                }
+    }
+    /* dB and dC: each group's heads summed, in head order. */
+    for (int64_t e = 0; e < batch * N * G * S; ++e) dB[e] = dC[e] = 0.0;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int hl = 0; hl < nh; ++hl) {
+            const int g = (head_lo + hl) / (nheads / G);
+            for (int64_t n = 0; n < N; ++n)
+                for (int s = 0; s < S; ++s) {
+                    dB[((b * N + n) * G + g) * S + s] += dBh[((b * nh + hl) * N + n) * S + s];
+                    dC[((b * N + n) * G + g) * S + s] += dCh[((b * nh + hl) * N + n) * S + s];
+                }
+        }
+    for (int hl = 0; hl < nh; ++hl) {
+        dA[hl] = dD[hl] = 0.0;
+        for (int64_t b = 0; b < batch; ++b) {
+            dA[hl] += dAb[b * nh + hl];
+            dD[hl] += dDb[b * nh + hl];
+        }
+    }
+done:
+    free(seq); free(rseq); free(dBh); free(dCh); free(drx); free(drB); free(drdt); free(dAb); free(dDb);
+    free(rx); free(rB); free(rdt);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Bidirectional Mamba (selective scan), the MA branch of the ablation        */
 /* ------------------------------------------------------------------------ */
 /* The xllm-io review compares the MA branch built on Mamba with the one built

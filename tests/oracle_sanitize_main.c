@@ -14,7 +14,8 @@
  *     and the selective scan);
  *   - a one-token grid gives y = 2 (dt (C . B) x + D x);
  *   - a 1x1x1 attention window gives o = v, and its backward dv = dout,
- *     dq = dk = 0.
+ *     dq = dk = 0;
+ *   - the scan's backward satisfies <dx, x> = <dy, y> (y is linear in x).
  * Prints "ALL OK" and exits 0 when every check passes.
  */
 #include <math.h>
@@ -31,6 +32,11 @@ int oracle_review_pool(const float *src, int64_t T, int64_t H, int64_t W, int64_
 int oracle_bissd(const float *x, const float *B, const float *C, const float *dt, const float *A, const float *D,
                  int64_t batch, int64_t T, int64_t H, int64_t W, int nheads, int P, int S, int G, int order,
                  int pool_t, int pool_h, int pool_w, int head_lo, int head_hi, int nthreads, double *y);
+int oracle_bissd_backward(const float *x, const float *B, const float *C, const float *dt, const float *A,
+                          const float *D, const float *dy, int64_t batch, int64_t T, int64_t H, int64_t W,
+                          int nheads, int P, int S, int G, int order, int pool_t, int pool_h, int pool_w,
+                          int head_lo, int head_hi, int nthreads, double *dx, double *dB, double *dC, double *ddt,
+                          double *dA, double *dD);
 int oracle_biscan1(const float *x, const float *B, const float *C, const float *dt, const float *A, const float *D,
                    int64_t batch, int64_t T, int64_t H, int64_t W, int nch, int S, int order, int pool_t,
                    int pool_h, int pool_w, int ch_lo, int ch_hi, int nthreads, double *y);
@@ -176,6 +182,37 @@ static void check_scans(void)
     free(x1); free(dt1); free(A1); free(D1); free(B1); free(C1); free(y1);
 }
 
+/* The scan's backward on a ragged shape with review tokens, more positions than one checkpoint block, a head
+ * range and several threads; y is linear in x, so <dx, x> = <dy, y>. */
+static void check_scan_backward(void)
+{
+    const int64_t batch = 2, T = 4, H = 9, W = 10, N = T * H * W; /* 360 positions + 45 review tokens */
+    const int nh = 3, P = 2, S = 3, G = 1, lo = 1, hi = 3, nr = hi - lo;
+    float *x = rnd_array((size_t)(batch * N * nh * P), -1, 1), *dy = rnd_array((size_t)(batch * N * nh * P), -1, 1);
+    float *Bm = rnd_array((size_t)(batch * N * G * S), -1, 1), *Cm = rnd_array((size_t)(batch * N * G * S), -1, 1);
+    float *dt = rnd_array((size_t)(batch * N * nh), 0.05f, 0.5f);
+    float *A = rnd_array((size_t)nh, -1.0f, -0.2f), *D = rnd_array((size_t)nh, -1, 1);
+    double *y = (double *)malloc(sizeof(double) * batch * N * nr * P);
+    double *dx = (double *)malloc(sizeof(double) * batch * N * nr * P), *ddt = (double *)malloc(sizeof(double) * batch * N * nr);
+    double *dB = (double *)malloc(sizeof(double) * batch * N * G * S), *dC = (double *)malloc(sizeof(double) * batch * N * G * S);
+    double dA[3], dD[3];
+    for (int order = 0; order <= 4; order += 2) {
+        CHECK(oracle_bissd(x, Bm, Cm, dt, A, D, batch, T, H, W, nh, P, S, G, order, 2, 3, 5, lo, hi, 3, y) == 0, "bissd");
+        CHECK(oracle_bissd_backward(x, Bm, Cm, dt, A, D, dy, batch, T, H, W, nh, P, S, G, order, 2, 3, 5, lo, hi, 3, dx,
+                                    dB, dC, ddt, dA, dD) == 0,
+              "bissd backward");
+        double lhs = 0.0, rhs = 0.0;
+        for (int64_t t = 0; t < batch * N; ++t)
+            for (int h = lo; h < hi; ++h)
+                for (int p = 0; p < P; ++p) {
+                    lhs += dx[(t * nr + (h - lo)) * P + p] * x[(t * nh + h) * P + p];
+                    rhs += (double)dy[(t * nh + h) * P + p] * y[(t * nr + (h - lo)) * P + p];
+                }
+        CHECK(close_to(lhs, rhs, 1e-10), "backward adjoint identity, order %d: %g vs %g", order, lhs, rhs);
+    }
+    free(x); free(dy); free(Bm); free(Cm); free(dt); free(A); free(D); free(y); free(dx); free(ddt); free(dB); free(dC);
+}
+
 /* Unit windows: o = v and the backward passes dout to dv; shifted ragged windows run through. */
 static void check_tesa(void)
 {
@@ -213,6 +250,7 @@ int main(void)
     check_rms();
     check_pool();
     check_scans();
+    check_scan_backward();
     check_tesa();
     if (failures) {
         fprintf(stderr, "%d check(s) failed\n", failures);

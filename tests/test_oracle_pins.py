@@ -611,3 +611,136 @@ def test_tesa_backward_special_cases(oracle_mod):
         assert written.any() and not written.all()
         np.testing.assert_array_equal(s_[written], f[written])
 
+
+
+# ----------------------------------------------------------------------------
+# Backward of the bidirectional scan
+# ----------------------------------------------------------------------------
+
+def exact_grid(a, bits=12):
+    """Values on a 2^-bits grid: moved by multiples of 2^-bits they stay exact in float32."""
+    return (np.round(np.asarray(a, dtype=np.float64) * 2.0 ** bits) / 2.0 ** bits).astype(np.float32)
+
+
+def rand_ssd_exact(rng, T, H, W, nheads, P, S, G):
+    x, B, C, dy = (exact_grid(rng.standard_normal(s)) for s in ((1, T, H, W, nheads, P), (1, T, H, W, G, S),
+                                                               (1, T, H, W, G, S), (1, T, H, W, nheads, P)))
+    dt = exact_grid(0.2 + 0.5 * rng.random((1, T, H, W, nheads)))
+    A = exact_grid(-(0.5 + rng.random(nheads)))
+    D = exact_grid(rng.standard_normal(nheads))
+    return x, B, C, dt, A, D, dy
+
+
+@pytest.mark.parametrize("order,pool,G", [(1, (2, 1, 3), 1), (4, (1, 2, 3), 1), (2, (0, 0, 0), 2)])
+def test_ssd_backward_equals_central_differences(oracle_mod, order, pool, G):
+    # L = sum(dy * y): every input element is moved by +-2^-10 on values that are multiples of 2^-12, so the
+    # moved inputs are exact in float32 and the central difference of the fp64 forward is exact up to O(eps^2).
+    rng = np.random.default_rng(120 + order)
+    T, H, W, nh, P, S = 2, 2, 3, 2, 2, 3
+    grid = (1, T, H, W)
+    x, B, C, dt, A, D, dy = rand_ssd_exact(rng, T, H, W, nh, P, S, G)
+    got = oracle_mod.bissd_backward(x, B, C, dt, A, D, dy, grid, order, pool, nthreads=2)
+    dy64 = dy.astype(np.float64)
+    eps = 2.0 ** -10
+    inputs = [x, B, C, dt, A, D]
+    for which, name in enumerate(("dx", "dB", "dC", "ddt", "dA", "dD")):
+        base = inputs[which]
+        num = np.zeros(base.shape)
+        for idx in np.ndindex(base.shape):
+            vals = []
+            for sgn in (1, -1):
+                args = list(inputs)
+                moved = base.copy()
+                moved[idx] += sgn * eps
+                args[which] = moved
+                vals.append(float(np.sum(dy64 * oracle_mod.bissd(*args, grid, order, pool, nthreads=1))))
+            num[idx] = (vals[0] - vals[1]) / (2 * eps)
+        assert relerr(got[name], num) < 2e-5, (name, relerr(got[name], num))
+
+
+def dual_form_torch(torch, x, B, C, dt, A, D, T, H, W, order, pool):
+    """The bidirectional scan as the sum of two masked quadratic forms in float64 torch ops, review tokens
+    built by reshape-mean pooling and the closed-form unroll orders, so that autograd differentiates a
+    construction that shares nothing with the oracle's recurrence."""
+    N = T * H * W
+    nheads, P = x.shape[-2], x.shape[-1]
+    G, S = B.shape[-2], B.shape[-1]
+    xs, Bs, Cs, dts = x.reshape(N, nheads, P), B.reshape(N, G, S), C.reshape(N, G, S), dt.reshape(N, nheads)
+    seq = torch.from_numpy(rms_closed_form(T, H, W, order))
+    per_head = []
+
+    def pooled(a):
+        pt, ph, pw = pool
+        c = a.shape[-1]
+        m = a.reshape(T // pt, pt, H // ph, ph, W // pw, pw, c).mean(dim=(1, 3, 5)).reshape(-1, c)
+        return m[torch.from_numpy(rms_closed_form(T // pt, H // ph, W // pw, order))]
+
+    for h in range(nheads):
+        g = h // (nheads // G)
+        if any(pool):
+            rx, rB, rdt = pooled(xs[:, h]), pooled(Bs[:, g]), pooled(dts[:, h:h + 1])[:, 0]
+        else:
+            rx = torch.zeros(0, P, dtype=torch.float64)
+            rB = torch.zeros(0, S, dtype=torch.float64)
+            rdt = torch.zeros(0, dtype=torch.float64)
+        R = rx.shape[0]
+        yh = torch.zeros(N, P, dtype=torch.float64)
+        for main in (seq, seq.flip(0)):
+            rev = torch.arange(R) if main is seq else torch.arange(R).flip(0)
+            zx = torch.cat([rx[rev], xs[main, h]])
+            zB = torch.cat([rB[rev], Bs[main, g]])
+            zC = torch.cat([torch.zeros(R, S, dtype=torch.float64), Cs[main, g]])
+            zd = torch.cat([rdt[rev], dts[main, h]])
+            cs = torch.cumsum(zd * A[h], 0)
+            M = torch.tril((zC @ zB.T) * torch.exp(cs[:, None] - cs[None, :]) * zd[None, :])
+            yz = M @ zx + D[h] * zx
+            yh = yh.index_add(0, main, yz[R:])
+        per_head.append(yh)
+    return torch.stack(per_head, dim=1)
+
+
+@pytest.mark.parametrize("order,pool", [(0, (2, 2, 2)), (3, (1, 2, 4)), (4, (2, 1, 2)), (1, (0, 0, 0))])
+def test_ssd_backward_equals_autograd_of_dual_form(oracle_mod, order, pool):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(130 + order)
+    T, H, W, nh, P, S, G = 2, 4, 4, 4, 3, 5, 2
+    x, B, C, dt, A, D = rand_ssd(rng, T, H, W, nh, P, S, G)
+    dy = rng.standard_normal(x.shape).astype(np.float32)
+    got = oracle_mod.bissd_backward(x, B, C, dt, A, D, dy, (1, T, H, W), order, pool)
+    ts = [torch.tensor(a.astype(np.float64), requires_grad=True) for a in (x, B, C, dt, A, D)]
+    y = dual_form_torch(torch, *ts, T, H, W, order, pool)
+    y.backward(torch.from_numpy(dy.astype(np.float64).reshape(y.shape)))
+    for name, t in zip(("dx", "dB", "dC", "ddt", "dA", "dD"), ts):
+        np.testing.assert_allclose(got[name], t.grad.numpy().reshape(got[name].shape), rtol=1e-9, atol=1e-11,
+                                   err_msg=name)
+
+
+def test_ssd_backward_special_cases_and_identities(oracle_mod):
+    rng = np.random.default_rng(140)
+    T, H, W, nh, P, S, G = 2, 3, 4, 4, 3, 5, 2
+    grid, pool = (1, T, H, W), (1, 3, 2)
+    x, B, C, dt, A, D = rand_ssd(rng, T, H, W, nh, P, S, G)
+    dy = rng.standard_normal(x.shape).astype(np.float32)
+    x64, C64, dy64 = (a.astype(np.float64) for a in (x, C, dy))
+    got = oracle_mod.bissd_backward(x, B, C, dt, A, D, dy, grid, 2, pool)
+    y = oracle_mod.bissd(x, B, C, dt, A, D, grid, 2, pool)
+    # y is linear in x (review tokens included: pooling is linear), so <dx, x> = <dy, y>
+    np.testing.assert_allclose(np.sum(got["dx"] * x64), np.sum(dy64 * y), rtol=1e-11)
+    # y - 2 D x is linear in C, so <dC, C> = <dy, y - 2 D x>
+    np.testing.assert_allclose(np.sum(got["dC"] * C64), np.sum(dy64 * (y - 2 * D[:, None] * x64)), rtol=1e-11)
+    # dD: each direction adds D x
+    np.testing.assert_allclose(got["dD"], 2 * (x64 * dy64).sum(axis=(0, 1, 2, 3, 5)), rtol=1e-12)
+    # B = 0: the scan contributes nothing, so dx = 2 D dy and no gradient reaches C, dt or A
+    z = oracle_mod.bissd_backward(x, np.zeros_like(B), C, dt, A, D, dy, grid, 2, pool)
+    np.testing.assert_allclose(z["dx"], 2 * D[:, None] * dy64, rtol=1e-13)
+    for k in ("dC", "ddt", "dA"):
+        np.testing.assert_array_equal(z[k], 0.0)
+    assert np.abs(z["dB"]).max() > 0  # but B itself has a gradient
+    # a head range equals the full result's slice; dB and dC split additively over head ranges
+    lo = oracle_mod.bissd_backward(x, B, C, dt, A, D, dy, grid, 2, pool, heads=(0, 2))
+    hi = oracle_mod.bissd_backward(x, B, C, dt, A, D, dy, grid, 2, pool, heads=(2, 4))
+    np.testing.assert_allclose(lo["dx"], got["dx"][..., 0:2, :], rtol=1e-13)
+    np.testing.assert_allclose(hi["ddt"], got["ddt"][..., 2:4], rtol=1e-13)
+    np.testing.assert_allclose(np.concatenate([lo["dA"], hi["dA"]]), got["dA"], rtol=1e-13)
+    np.testing.assert_allclose(lo["dB"] + hi["dB"], got["dB"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lo["dC"] + hi["dC"], got["dC"], rtol=1e-12, atol=1e-14)
