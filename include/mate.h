@@ -163,6 +163,42 @@ size_t mate_bissd_workspace_size(mate_grid g, const mate_ssd_desc *d);
 mate_status mate_bissd_scan(const mate_ssd_tensors *t, mate_grid g, int order, const mate_ssd_desc *d,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* Backward of mate_bissd_scan for an upstream gradient dy of its output y (the
+ * MA half of training the MATE block; the xllm-io review, section 三, "训练配方",
+ * trains LinGen end to end). For each direction, with a_u = exp(dt_u A), the
+ * adjoint of the recurrence runs from the end of that direction's sequence to
+ * its start, G_u = dy_u C_u^T + a_{u+1} G_{u+1}, and the chain rule through each
+ * step gives
+ *     dx_u  += dt_u G_u B_u + D dy_u,        dB_u += dt_u G_u^T x_u,
+ *     dC_u  += h_u^T dy_u,                   ddt_u += x_u^T G_u B_u + A a_u <h_{u-1}, G_u>,
+ *     dA    += dt_u a_u <h_{u-1}, G_u>,      dD   += x_u . dy_u;
+ * both directions add into the same gradients, dy is 0 at review positions
+ * (their outputs are dropped) and the review tokens' dx, dB and ddt flow back
+ * through the average pooling to the tokens of their pool blocks. dB and dC are
+ * summed over the heads of each group, dA and dD over the batch.
+ * Layouts: x, dy, dx [batch][T][H][W][nheads][headdim]   (desc dtype)
+ *          b, c, db, dc [batch][T][H][W][ngroups][d_state] (desc dtype)
+ *          dt, ddt [batch][T][H][W][nheads] fp32;  a, d, da, dd [nheads] fp32
+ * Every output is written whole; outputs must not overlap the inputs. The
+ * evaluation is chunked with chunks of its own (64 tokens, 32 for the widest
+ * states), whatever the descriptor's chunk; arithmetic is fp32. Supported:
+ * headdim 16, 32 or 64, d_state a multiple of 8 up to 128 (MATE_ERR_UNSUPPORTED
+ * otherwise); the descriptor's algo is ignored. The workspace (at least
+ * mate_bissd_backward_workspace_size bytes, 256-byte aligned) is scratch for
+ * the call: it holds four fp32 states per chunk and head. Other errors as
+ * mate_bissd_scan. */
+typedef struct {
+    const void *x, *b, *c;
+    const float *dt, *a, *d;
+    const void *dy;
+    void *dx, *db, *dc;
+    float *ddt, *da, *dd;
+} mate_ssd_grad_tensors;
+
+size_t mate_bissd_backward_workspace_size(mate_grid g, const mate_ssd_desc *d);
+mate_status mate_bissd_backward(const mate_ssd_grad_tensors *t, mate_grid g, int order, const mate_ssd_desc *d,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 /* The same scan for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Instead of a caller-provided workspace it uses a scratch array of
@@ -303,7 +339,8 @@ int mate_abi_version(void);
  * of it (by any call, any stream) is bracketed by a pair of HIP events
  * recorded on the stream it is launched on. Other kernels are untouched.
  * Names: "rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb", "ssd_states",
- * "ssd_seg_pass", "ssd_out", "tesa", "mamba_scan", "tesa_backward" (unknown name:
+ * "ssd_seg_pass", "ssd_out", "tesa", "mamba_scan", "tesa_backward",
+ * "ssd_backward" (the whole backward of the scan) (unknown name:
  * MATE_ERR_SHAPE; a timing
  * already armed: MATE_ERR_SHAPE).
  * mate_timing_end waits for the recorded events (a host synchronisation on

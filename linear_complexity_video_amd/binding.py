@@ -24,6 +24,7 @@ EXPORTED = (
     "mate_forward_workspace_size", "mate_forward", "mate_status_string", "mate_last_error",
     "mate_abi_version", "mate_timing_begin", "mate_timing_end", "mate_bimamba_workspace_size",
     "mate_bimamba_scan", "mate_tesa_backward_workspace_size", "mate_tesa_backward", "mate_bissd_scan_noalloc",
+    "mate_bissd_backward_workspace_size", "mate_bissd_backward",
 )
 STATIC_SCRATCH_BYTES = 64 << 20  # MATE_STATIC_SCRATCH_BYTES
 
@@ -49,6 +50,11 @@ class SsdDesc(ctypes.Structure):
 class SsdTensors(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p), ("dt", ctypes.c_void_p),
                 ("a", ctypes.c_void_p), ("d", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class SsdGradTensors(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("x", "b", "c", "dt", "a", "d", "dy", "dx", "db", "dc", "ddt", "da",
+                                                "dd")]
 
 
 class MambaDesc(ctypes.Structure):
@@ -88,6 +94,9 @@ def lib() -> ctypes.CDLL:
     L.mate_bissd_workspace_size.restype = SZ
     L.mate_bissd_scan.argtypes = [ctypes.POINTER(SsdTensors), Grid, I32, ctypes.POINTER(SsdDesc), P, SZ, P]
     L.mate_bissd_scan_noalloc.argtypes = [ctypes.POINTER(SsdTensors), Grid, I32, ctypes.POINTER(SsdDesc), P]
+    L.mate_bissd_backward_workspace_size.argtypes = [Grid, ctypes.POINTER(SsdDesc)]
+    L.mate_bissd_backward_workspace_size.restype = SZ
+    L.mate_bissd_backward.argtypes = [ctypes.POINTER(SsdGradTensors), Grid, I32, ctypes.POINTER(SsdDesc), P, SZ, P]
     L.mate_tesa.argtypes = [ctypes.POINTER(TesaTensors), Grid, ctypes.POINTER(TesaDesc), P]
     L.mate_tesa_backward_workspace_size.argtypes = [Grid, ctypes.POINTER(TesaDesc)]
     L.mate_tesa_backward_workspace_size.restype = SZ
@@ -99,8 +108,8 @@ def lib() -> ctypes.CDLL:
     L.mate_forward_workspace_size.restype = SZ
     L.mate_forward.argtypes = [ctypes.POINTER(SsdTensors), ctypes.POINTER(SsdDesc), ctypes.POINTER(TesaTensors),
                                ctypes.POINTER(TesaDesc), Grid, I32, P, SZ, P]
-    for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_bissd_scan_noalloc", "mate_bimamba_scan", "mate_tesa",
-              "mate_tesa_backward", "mate_forward"):
+    for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_bissd_scan_noalloc", "mate_bissd_backward",
+              "mate_bimamba_scan", "mate_tesa", "mate_tesa_backward", "mate_forward"):
         getattr(L, f).restype = ctypes.c_int
     L.mate_status_string.argtypes = [ctypes.c_int]
     L.mate_status_string.restype = ctypes.c_char_p
@@ -275,6 +284,33 @@ def mate_bissd_scan_noalloc(x, b, c, dt, a, d, y, order: int, chunk: int, pool=(
     desc = ssd_desc(x, b, chunk, pool, algo)
     t = SsdTensors(_ptr(x), _ptr(b), _ptr(c), _ptr(dt), _ptr(a), _ptr(d), _ptr(y))
     _check(lib().mate_bissd_scan_noalloc(ctypes.byref(t), grid_of(x), order, ctypes.byref(desc), _stream(stream)))
+
+
+def mate_bissd_backward_workspace_size(grid, desc: SsdDesc) -> int:
+    return int(lib().mate_bissd_backward_workspace_size(Grid(*grid), ctypes.byref(desc)))
+
+
+def mate_bissd_backward(x, b, c, dt, a, d, dy, dx, db, dc, ddt, da, dd, order: int, pool=(0, 0, 0),
+                        workspace=None, stream=None):
+    """Gradients (dx, db, dc, ddt, da, dd) of mate_bissd_scan for the upstream gradient dy (see include/mate.h)."""
+    _check_ssd_tensors(x, b, c, dt, a, d, dx)
+    _shape(dy, x.shape, "dy")
+    _shape(db, b.shape, "db")
+    _shape(dc, b.shape, "dc")
+    _shape(ddt, dt.shape, "ddt")
+    _shape(da, a.shape, "da")
+    _shape(dd, d.shape, "dd")
+    _same_dtype(x, "x", dy=dy, db=db, dc=dc)
+    for n, t in (("ddt", ddt), ("da", da), ("dd", dd)):
+        _is_f32(t, n)
+    _dev(x, b, c, dt, a, d, dy, dx, db, dc, ddt, da, dd)
+    grid = tuple(x.shape[:4])
+    desc = ssd_desc(x, b, 64, pool)
+    if workspace is None:
+        workspace = _workspace(mate_bissd_backward_workspace_size(grid, desc), x)
+    t = SsdGradTensors(*(_ptr(v) for v in (x, b, c, dt, a, d, dy, dx, db, dc, ddt, da, dd)))
+    _check(lib().mate_bissd_backward(ctypes.byref(t), Grid(*grid), order, ctypes.byref(desc), _ptr(workspace),
+                                     _nbytes(workspace), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

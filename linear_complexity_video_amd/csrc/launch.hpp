@@ -23,6 +23,15 @@ struct SsdArgs {
     void *y;
 };
 
+// Inputs and gradients of the scan's backward (dt, a, d, ddt, da, dd fp32; the rest in the scan's dtype).
+struct SsdGradArgs {
+    const void *x, *b, *c;
+    const float *dt, *a, *d;
+    const void *dy;
+    void *dx, *db, *dc;
+    float *ddt, *da, *dd;
+};
+
 struct TesaProblem {
     int64_t batch, T, H, W;
     int nheads, headdim;
@@ -75,6 +84,11 @@ bool ssd_fast_supports(const SsdProblem &p);
 size_t ssd_fast_workspace(const SsdProblem &p);
 hipError_t ssd_fast(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st);
 hipError_t ssd_fast_prepare();
+
+bool ssd_backward_supports(const SsdProblem &p);
+size_t ssd_backward_workspace(const SsdProblem &p);
+hipError_t ssd_backward(const SsdProblem &p, const SsdGradArgs &a, void *ws, hipStream_t st);
+hipError_t ssd_backward_prepare();
 
 bool tesa_portable_supports(const TesaProblem &p);
 hipError_t tesa_portable(const TesaProblem &p, const TesaArgs &a, hipStream_t st);

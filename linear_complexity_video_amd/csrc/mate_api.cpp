@@ -52,6 +52,7 @@ mate_status prepare_device()
     if (done[dev].load(std::memory_order_acquire)) return MATE_OK;
     if ((e = mate::ssd_portable_prepare()) != hipSuccess) return device_fail(e, "hipFuncSetAttribute");
     if ((e = mate::ssd_fast_prepare()) != hipSuccess) return device_fail(e, "hipFuncSetAttribute");
+    if ((e = mate::ssd_backward_prepare()) != hipSuccess) return device_fail(e, "hipFuncSetAttribute");
     done[dev].store(1, std::memory_order_release);
     return MATE_OK;
 }
@@ -283,6 +284,45 @@ mate_status mate_bissd_scan_noalloc(const mate_ssd_tensors *t, mate_grid g, int 
     mate::SsdArgs a{t->x, t->b, t->c, t->dt, t->a, t->d, t->y};
     e = fast ? mate::ssd_fast(p, a, ws, (hipStream_t)stream) : mate::ssd_portable(p, a, ws, (hipStream_t)stream);
     if (e != hipSuccess) return device_fail(e, "bissd launch");
+    return MATE_OK;
+}
+
+size_t mate_bissd_backward_workspace_size(mate_grid g, const mate_ssd_desc *d)
+{
+    mate::SsdProblem p;
+    bool fast = false;
+    if (make_ssd_problem(g, 0, d, p, fast) != MATE_OK || !mate::ssd_backward_supports(p)) return 0;
+    return mate::ssd_backward_workspace(p);
+}
+
+mate_status mate_bissd_backward(const mate_ssd_grad_tensors *t, mate_grid g, int order, const mate_ssd_desc *d,
+                                void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!t) return fail(MATE_ERR_NULL, "ssd gradient tensors struct is NULL");
+    if (!t->x || !t->b || !t->c || !t->dt || !t->a || !t->d || !t->dy || !t->dx || !t->db || !t->dc || !t->ddt ||
+        !t->da || !t->dd)
+        return fail(MATE_ERR_NULL, "an ssd gradient tensor pointer is NULL");
+    if (((uintptr_t)t->x | (uintptr_t)t->b | (uintptr_t)t->c | (uintptr_t)t->dy | (uintptr_t)t->dx |
+         (uintptr_t)t->db | (uintptr_t)t->dc) & 15)
+        return fail(MATE_ERR_UNSUPPORTED, "x, b, c, dy, dx, db and dc must be 16-byte aligned");
+    if (((uintptr_t)t->dt | (uintptr_t)t->a | (uintptr_t)t->d | (uintptr_t)t->ddt | (uintptr_t)t->da |
+         (uintptr_t)t->dd) & 3)
+        return fail(MATE_ERR_UNSUPPORTED, "dt, a, d, ddt, da and dd must be 4-byte aligned");
+    mate::SsdProblem p;
+    bool fast = false;
+    mate_status s = make_ssd_problem(g, order, d, p, fast);
+    if (s != MATE_OK) return s;
+    if (!mate::ssd_backward_supports(p))
+        return fail(MATE_ERR_UNSUPPORTED, "the scan's backward is built for headdim 16, 32 or 64 and d_state <= 128 "
+                                          "(a multiple of 8)");
+    const size_t need = mate::ssd_backward_workspace(p);
+    if (!workspace || workspace_bytes < need)
+        return fail(MATE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+    if ((uintptr_t)workspace & 255) return fail(MATE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if ((s = prepare_device()) != MATE_OK) return s;
+    mate::SsdGradArgs a{t->x, t->b, t->c, t->dt, t->a, t->d, t->dy, t->dx, t->db, t->dc, t->ddt, t->da, t->dd};
+    hipError_t e = mate::ssd_backward(p, a, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "bissd backward launch");
     return MATE_OK;
 }
 

@@ -17,6 +17,7 @@
 // and across a chunk both states decay by exp(tot).
 #include "common.hpp"
 #include "launch.hpp"
+#include "ssd_chunks.hpp"
 #include "ssd_common.hpp"
 #include "timing.hpp"
 
@@ -25,150 +26,15 @@ namespace mate {
 namespace {
 
 using ssd::kMaxQ;
+using ssd::k_cb;
+using ssd::k_chunk_states;
+using ssd::k_state_pass;
 using ssd::k_pool;
 using ssd::k_prep_dt;
 using ssd::k_pool_f32x4;
 using ssd::pool_f32x4_ok;
 using ssd::seq_row;
 
-
-// Per-chunk state contributions Sf, Sb (P x S, fp32) of one head.
-// grid (nchunks, nheads, batch), 256 threads. LDS: X (Q x P) and B (Q x S) in fp32.
-template <typename E, bool PERM>
-__global__ __launch_bounds__(256) void k_chunk_states(const E *__restrict__ x, const E *__restrict__ Bm,
-                                                      const float *__restrict__ dtT, const float *__restrict__ csT,
-                                                      const float *__restrict__ A, float *__restrict__ Sf,
-                                                      float *__restrict__ Sb, int nheads, int P, int S, int G,
-                                                      uint32_t L, uint32_t Lpad, int Q, int order, uint32_t T,
-                                                      uint32_t H, uint32_t W)
-{
-    extern __shared__ float smem[];
-    float *Xs = smem;                 // [Q][P]
-    float *Bs = Xs + Q * P;           // [Q][S]
-    float *wf = Bs + Q * S;           // [Q]
-    float *wb = wf + Q;               // [Q]
-    const uint32_t c = blockIdx.x, b = blockIdx.z;
-    const int h = blockIdx.y, g = h / (nheads / G);
-    const uint32_t nch = gridDim.x;
-    for (int k = threadIdx.x; k < Q * P; k += 256) {
-        const int u = k / P, p = k - u * P;
-        const uint32_t i = c * Q + u;
-        float v = 0.f;
-        if (i < L) v = elem<E>::load(x + (((size_t)b * L + seq_row<PERM>(i, order, T, H, W)) * nheads + h) * P + p);
-        Xs[k] = v;
-    }
-    for (int k = threadIdx.x; k < Q * S; k += 256) {
-        const int u = k / S, s = k - u * S;
-        const uint32_t i = c * Q + u;
-        float v = 0.f;
-        if (i < L) v = elem<E>::load(Bm + (((size_t)b * L + seq_row<PERM>(i, order, T, H, W)) * G + g) * S + s);
-        Bs[k] = v;
-    }
-    const size_t row = ((size_t)b * nheads + h) * Lpad + (size_t)c * Q;
-    const float a = A[h];
-    const float tot = csT[row + Q - 1];
-    for (int u = threadIdx.x; u < Q; u += 256) {
-        const float d = dtT[row + u], cs = csT[row + u];
-        wf[u] = d * __expf(tot - cs);
-        wb[u] = d * __expf(cs - d * a);
-    }
-    __syncthreads();
-    const int PS = P * S;
-    float *outf = Sf + (((size_t)b * nheads + h) * nch + c) * PS;
-    float *outb = Sb + (((size_t)b * nheads + h) * nch + c) * PS;
-    for (int e = threadIdx.x; e < PS; e += 256) {
-        const int p = e / S, s = e - p * S;
-        float af = 0.f, ab = 0.f;
-        for (int u = 0; u < Q; ++u) {
-            const float xb = Xs[u * P + p] * Bs[u * S + s];
-            af += xb * wf[u];
-            ab += xb * wb[u];
-        }
-        outf[e] = af;
-        outb[e] = ab;
-    }
-}
-
-// Turns chunk contributions into the states entering each chunk: Sf[c] becomes
-// the forward state after chunk c-1, Sb[c] the backward state after chunk c+1.
-// h0f / h0b (optional) are the initial states; finF / finB (optional) receive
-// the final states. grid (ceil(P*S / 256), nheads, batch).
-__global__ __launch_bounds__(256) void k_state_pass(float *__restrict__ Sf, float *__restrict__ Sb,
-                                                    const float *__restrict__ csT, const float *__restrict__ h0f,
-                                                    const float *__restrict__ h0b, float *__restrict__ finF,
-                                                    float *__restrict__ finB, int PS, int nch, int Q, uint32_t Lpad)
-{
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= PS) return;
-    const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
-    const float *cs = csT + bh * Lpad;
-    float *f = Sf + bh * nch * PS + e;
-    float *bk = Sb + bh * nch * PS + e;
-    float run = h0f ? h0f[bh * PS + e] : 0.f;
-    for (int c = 0; c < nch; ++c) {
-        const float tot = cs[(size_t)c * Q + Q - 1];
-        const float s = f[(size_t)c * PS];
-        f[(size_t)c * PS] = run;
-        run = __expf(tot) * run + s;
-    }
-    if (finF) finF[bh * PS + e] = run;
-    run = h0b ? h0b[bh * PS + e] : 0.f;
-    for (int c = nch - 1; c >= 0; --c) {
-        const float tot = cs[(size_t)c * Q + Q - 1];
-        const float s = bk[(size_t)c * PS];
-        bk[(size_t)c * PS] = run;
-        run = __expf(tot) * run + s;
-    }
-    if (finB) finB[bh * PS + e] = run;
-}
-
-// CB[t][u] = C_t . B_u for every chunk and group. grid (nchunks, G, batch).
-template <typename E>
-__global__ __launch_bounds__(256) void k_cb(const E *__restrict__ Bm, const E *__restrict__ Cm,
-                                            float *__restrict__ CB, int G, int S, uint32_t L, int Q, int order,
-                                            uint32_t T_, uint32_t H, uint32_t W)
-{
-    __shared__ float Bs[kMaxQ][33];
-    __shared__ float Cs[kMaxQ][33];
-    const uint32_t c = blockIdx.x, b = blockIdx.z;
-    const int g = blockIdx.y;
-    const int QQ = Q * Q;
-    float acc[kMaxQ * kMaxQ / 256];
-#pragma unroll
-    for (int k = 0; k < kMaxQ * kMaxQ / 256; ++k) acc[k] = 0.f;
-    for (int s0 = 0; s0 < S; s0 += 32) {
-        __syncthreads();
-        for (int k = threadIdx.x; k < Q * 32; k += 256) {
-            const int u = k >> 5, s = k & 31;
-            const uint32_t i = c * Q + u;
-            float bv = 0.f, cv = 0.f;
-            if (i < L && s0 + s < S) {
-                const size_t off = (((size_t)b * L + rms_index32(i, order, T_, H, W)) * G + g) * S + s0 + s;
-                bv = elem<E>::load(Bm + off);
-                cv = elem<E>::load(Cm + off);
-            }
-            Bs[u][s] = bv;
-            Cs[u][s] = cv;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < kMaxQ * kMaxQ / 256; ++k) {
-            const int e = threadIdx.x + 256 * k;
-            if (e < QQ) {
-                const int t = e / Q, u = e - t * Q;
-                float a = 0.f;
-                for (int s = 0; s < 32; ++s) a += Cs[t][s] * Bs[u][s];
-                acc[k] += a;
-            }
-        }
-    }
-    float *out = CB + (((size_t)b * G + g) * gridDim.x + c) * QQ;
-#pragma unroll
-    for (int k = 0; k < kMaxQ * kMaxQ / 256; ++k) {
-        const int e = threadIdx.x + 256 * k;
-        if (e < QQ) out[e] = acc[k];
-    }
-}
 
 // Outputs of one chunk and head; Sf / Sb hold the entering states.
 // grid (nchunks, nheads, batch), 256 threads.
@@ -366,7 +232,7 @@ static hipError_t run_portable(const SsdProblem &p, const SsdArgs &a, void *ws, 
         }
         {
             timing::Scope ts_(K_SSD_STATES, st);
-            k_chunk_states<float, false><<<dim3(p.nchR, Hs, B), 256, states_lds, st>>>(
+            k_chunk_states<float, false, false><<<dim3(p.nchR, Hs, B), 256, states_lds, st>>>(
                 rx, rB, rdtT, rcsT, a.a, rSf, rSb, Hs, P, S, G, R, Rpad, Q, 0, 1, 1, R);
         }
         {
@@ -382,7 +248,7 @@ static hipError_t run_portable(const SsdProblem &p, const SsdArgs &a, void *ws, 
     }
     {
         timing::Scope ts_(K_SSD_STATES, st);
-        k_chunk_states<E, true><<<dim3(p.nch, Hs, B), 256, states_lds, st>>>(x, Bm, dtT, csT, a.a, Sf, Sb, Hs, P, S, G, N,
+        k_chunk_states<E, true, false><<<dim3(p.nch, Hs, B), 256, states_lds, st>>>(x, Bm, dtT, csT, a.a, Sf, Sb, Hs, P, S, G, N,
                                                                              Lpad, Q, p.order, T, H, W);
     }
     {
@@ -413,11 +279,11 @@ hipError_t ssd_portable_prepare()
     // The state kernel may take more than 64 KB of dynamic LDS.
     const int lds = 160 * 1024;
     hipError_t e;
-    if ((e = hipFuncSetAttribute((const void *)k_chunk_states<float, false>,
+    if ((e = hipFuncSetAttribute((const void *)k_chunk_states<float, false, false>,
                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
-    if ((e = hipFuncSetAttribute((const void *)k_chunk_states<float, true>,
+    if ((e = hipFuncSetAttribute((const void *)k_chunk_states<float, true, false>,
                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
-    return hipFuncSetAttribute((const void *)k_chunk_states<bf16_t, true>,
+    return hipFuncSetAttribute((const void *)k_chunk_states<bf16_t, true, false>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
 

@@ -26,7 +26,7 @@ hipError_t g_error = hipSuccess;
 
 const char *const kNames[K_COUNT] = {"rms_reorder", "ssd_pool", "ssd_prep", "ssd_cb",
                                      "ssd_states", "ssd_seg_pass", "ssd_out", "tesa", "mamba_scan",
-                                     "tesa_backward"};
+                                     "tesa_backward", "ssd_backward"};
 
 } // namespace
 

@@ -18,6 +18,7 @@ enum KernelId : int {
     K_TESA,
     K_MAMBA,
     K_TESA_BWD,
+    K_SSD_BWD,
     K_COUNT
 };
 

@@ -415,24 +415,32 @@ typedef struct {
     int nheads, P, S, G, head_lo, head_hi;
     const int64_t *seq;            /* scan order, N entries */
     const double *rx, *rB, *rdt;   /* review tokens per batch: [b][R][nheads*P], [b][R][G*S], [b][R][nheads] */
-    /* per (batch, local head) results, written only by that unit */
-    double *dx;                    /* [b][N][nh][P] */
-    double *dBh, *dCh;             /* [b][nh][N][S]: this head's part of dB, dC */
-    double *ddt;                   /* [b][N][nh] */
-    double *drx, *drB, *drdt;      /* [b][nh][R][P], [b][nh][R][S], [b][nh][R]: review-token gradients */
-    double *dA, *dD;               /* [b][nh] */
+    /* per (direction, batch, local head) results, written only by that unit; each array has one copy
+     * per direction (index dir first), summed after all units have run */
+    double *dx;                    /* [2][b][N][nh][P] */
+    double *dBh, *dCh;             /* [2][b][nh][N][S]: this head's part of dB, dC */
+    double *ddt;                   /* [2][b][N][nh] */
+    double *drx, *drB, *drdt;      /* [2][b][nh][R][P], [2][b][nh][R][S], [2][b][nh][R]: review-token gradients */
+    double *dA, *dD;               /* [2][b][nh] */
 } ssd_bwd_ctx;
 
 static int ssd_bwd_unit(void *vctx, int64_t unit)
 {
     ssd_bwd_ctx *c = (ssd_bwd_ctx *)vctx;
     const int nh = c->head_hi - c->head_lo;
-    const int64_t b = unit / nh;
-    const int hl = (int)(unit % nh);
+    const int64_t b = unit / (2 * nh);
+    const int hl = (int)((unit / 2) % nh);
+    const int dir = (int)(unit % 2);
     const int head = c->head_lo + hl;
     const int g = head / (c->nheads / c->G);
     const int P = c->P, S = c->S;
     const int64_t N = c->N, R = c->R, L = R + N, PS = (int64_t)P * S;
+    const int64_t Rn = R > 0 ? R : 1, B = c->batch;
+    /* this direction's copy of every result */
+    double *dxo = c->dx + dir * B * N * nh * P, *dBo = c->dBh + dir * B * nh * N * S;
+    double *dCo = c->dCh + dir * B * nh * N * S, *ddto = c->ddt + dir * B * N * nh;
+    double *drxo = c->drx + dir * B * nh * Rn * P, *drBo = c->drB + dir * B * nh * Rn * S;
+    double *drdto = c->drdt + dir * B * nh * Rn;
     const double A = (double)c->A[head], D = (double)c->D[head];
     const int64_t nblk = (L + ORACLE_CKPT - 1) / ORACLE_CKPT;
 
@@ -449,7 +457,7 @@ static int ssd_bwd_unit(void *vctx, int64_t unit)
         return ORACLE_ENOMEM;
     }
     double dA = 0.0, dD = 0.0;
-    for (int dir = 0; dir < 2; ++dir) {
+    {
         /* Position u of this direction's sequence: its inputs, and where its gradients go. */
 #define LOAD(u)                                                                                        \
     int64_t rj = -1, n = -1;                                                                           \
@@ -510,14 +518,14 @@ static int ssd_bwd_unit(void *vctx, int64_t unit)
                 }
                 double *gx, *gbb, *gdt;
                 if (rj >= 0) {
-                    gx = c->drx + ((b * nh + hl) * R + rj) * P;
-                    gbb = c->drB + ((b * nh + hl) * R + rj) * S;
-                    gdt = c->drdt + (b * nh + hl) * R + rj;
+                    gx = drxo + ((b * nh + hl) * R + rj) * P;
+                    gbb = drBo + ((b * nh + hl) * R + rj) * S;
+                    gdt = drdto + (b * nh + hl) * R + rj;
                 } else {
-                    gx = c->dx + ((b * N + n) * nh + hl) * P;
-                    gbb = c->dBh + ((b * nh + hl) * N + n) * S;
-                    gdt = c->ddt + (b * N + n) * nh + hl;
-                    double *gc = c->dCh + ((b * nh + hl) * N + n) * S;
+                    gx = dxo + ((b * N + n) * nh + hl) * P;
+                    gbb = dBo + ((b * nh + hl) * N + n) * S;
+                    gdt = ddto + (b * N + n) * nh + hl;
+                    double *gc = dCo + ((b * nh + hl) * N + n) * S;
                     for (int s = 0; s < S; ++s) {
                         double acc = 0.0;
                         for (int p = 0; p < P; ++p) acc += hcur[p * S + s] * dyv[p];
@@ -538,8 +546,8 @@ static int ssd_bwd_unit(void *vctx, int64_t unit)
         }
 #undef LOAD
     }
-    c->dA[b * nh + hl] = dA;
-    c->dD[b * nh + hl] = dD;
+    c->dA[(dir * B + b) * nh + hl] = dA;
+    c->dD[(dir * B + b) * nh + hl] = dD;
     free(ckpt); free(hb); free(h); free(Gm); free(carry); free(xv); free(dyv); free(bv); free(cv); free(gB);
     return ORACLE_OK;
 }
@@ -569,17 +577,24 @@ int oracle_bissd_backward(const float *x, const float *B, const float *C, const 
     const int64_t R = Tp * Hp * Wp;
     const int nh = head_hi - head_lo;
     int rc = ORACLE_OK;
+    const int64_t Rn = R > 0 ? R : 1;
     int64_t *seq = (int64_t *)malloc(sizeof(int64_t) * (size_t)N);
-    int64_t *rseq = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R > 0 ? R : 1));
-    double *dBh = (double *)calloc((size_t)(batch * nh * N * S), sizeof(double));
-    double *dCh = (double *)calloc((size_t)(batch * nh * N * S), sizeof(double));
-    double *drx = (double *)calloc((size_t)(batch * nh * (R > 0 ? R : 1) * P), sizeof(double));
-    double *drB = (double *)calloc((size_t)(batch * nh * (R > 0 ? R : 1) * S), sizeof(double));
-    double *drdt = (double *)calloc((size_t)(batch * nh * (R > 0 ? R : 1)), sizeof(double));
-    double *dAb = (double *)calloc((size_t)(batch * nh), sizeof(double));
-    double *dDb = (double *)calloc((size_t)(batch * nh), sizeof(double));
+    int64_t *rseq = (int64_t *)malloc(sizeof(int64_t) * (size_t)Rn);
+    /* one copy per direction of every per-unit result */
+    double *dx2 = (double *)calloc((size_t)(2 * batch * N * nh * P), sizeof(double));
+    double *ddt2 = (double *)calloc((size_t)(2 * batch * N * nh), sizeof(double));
+    double *dBh = (double *)calloc((size_t)(2 * batch * nh * N * S), sizeof(double));
+    double *dCh = (double *)calloc((size_t)(2 * batch * nh * N * S), sizeof(double));
+    double *drx = (double *)calloc((size_t)(2 * batch * nh * Rn * P), sizeof(double));
+    double *drB = (double *)calloc((size_t)(2 * batch * nh * Rn * S), sizeof(double));
+    double *drdt = (double *)calloc((size_t)(2 * batch * nh * Rn), sizeof(double));
+    double *dAb = (double *)calloc((size_t)(2 * batch * nh), sizeof(double));
+    double *dDb = (double *)calloc((size_t)(2 * batch * nh), sizeof(double));
     double *rx = NULL, *rB = NULL, *rdt = NULL;
-    if (!seq || !rseq || !dBh || !dCh || !drx || !drB || !drdt || !dAb || !dDb) { rc = ORACLE_ENOMEM; goto done; }
+    if (!seq || !rseq || !dx2 || !ddt2 || !dBh || !dCh || !drx || !drB || !drdt || !dAb || !dDb) {
+        rc = ORACLE_ENOMEM;
+        goto done;
+    }
     rc = oracle_rms_sequence(T, H, W, order, 0, seq);
     if (rc) goto done;
     if (R > 0) {
@@ -601,18 +616,34 @@ int oracle_bissd_backward(const float *x, const float *B, const float *C, const 
         }
         if (rc) goto done;
     }
-    for (int64_t e = 0; e < batch * N * nh * P; ++e) dx[e] = 0.0;
-    for (int64_t e = 0; e < batch * N * nh; ++e) ddt[e] = 0.0;
     {
         ssd_bwd_ctx c;
         c.x = x; c.B = B; c.C = C; c.dt = dt; c.A = A; c.D = D; c.dy = dy;
         c.batch = batch; c.N = N; c.R = R;
         c.nheads = nheads; c.P = P; c.S = S; c.G = G; c.head_lo = head_lo; c.head_hi = head_hi;
         c.seq = seq; c.rx = rx; c.rB = rB; c.rdt = rdt;
-        c.dx = dx; c.dBh = dBh; c.dCh = dCh; c.ddt = ddt; c.drx = drx; c.drB = drB; c.drdt = drdt;
+        c.dx = dx2; c.dBh = dBh; c.dCh = dCh; c.ddt = ddt2; c.drx = drx; c.drB = drB; c.drdt = drdt;
         c.dA = dAb; c.dD = dDb;
-        rc = run_units(ssd_bwd_unit, &c, batch * nh, nthreads);
+        rc = run_units(ssd_bwd_unit, &c, batch * nh * 2, nthreads);
         if (rc) goto done;
+    }
+    /* The two directions summed (forward copy first). */
+    {
+        const int64_t nx = batch * N * nh * P, nd = batch * N * nh, ns = batch * nh * N * S;
+        const int64_t nrx = batch * nh * Rn * P, nrb = batch * nh * Rn * S, nrd = batch * nh * Rn;
+        for (int64_t e = 0; e < nx; ++e) dx[e] = dx2[e] + dx2[nx + e];
+        for (int64_t e = 0; e < nd; ++e) ddt[e] = ddt2[e] + ddt2[nd + e];
+        for (int64_t e = 0; e < ns; ++e) {
+            dBh[e] += dBh[ns + e];
+            dCh[e] += dCh[ns + e];
+        }
+        for (int64_t e = 0; e < nrx; ++e) drx[e] += drx[nrx + e];
+        for (int64_t e = 0; e < nrb; ++e) drB[e] += drB[nrb + e];
+        for (int64_t e = 0; e < nrd; ++e) drdt[e] += drdt[nrd + e];
+        for (int64_t e = 0; e < batch * nh; ++e) {
+            dAb[e] += dAb[batch * nh + e];
+            dDb[e] += dDb[batch * nh + e];
+        }
     }
     /* Review tokens back through the average pooling: every token of the block of review token j
      * (the pooled grid unrolled in the scan order) receives its gradient over the block's size. */
@@ -655,7 +686,7 @@ int oracle_bissd_backward(const float *x, const float *B, const float *C, const 
         }
     }
 done:
-    free(seq); free(rseq); free(dBh); free(dCh); free(drx); free(drB); free(drdt); free(dAb); free(dDb);
+    free(seq); free(rseq); free(dx2); free(ddt2); free(dBh); free(dCh); free(drx); free(drB); free(drdt); free(dAb); free(dDb);
     free(rx); free(rB); free(rdt);
     return rc;
 }

@@ -701,3 +701,135 @@ def test_tesa_backward_sampled(oracle_mod, cfg, shifted):
             err = parity_error(to_f64(gt[..., lo:hi, :])[mask], w[mask])
             say(f"  heads {lo}:{hi} {name} err={err:.3e}")
             assert err <= 2e-2, (lo, name, err)
+
+
+# ----------------------------------------------------------------------------
+# Backward of the bidirectional scan
+# ----------------------------------------------------------------------------
+
+SSD_GRADS = ("dx", "dB", "dC", "ddt", "dA", "dD")
+
+
+def run_ssd_backward(dev, dy, order, pool):
+    """dev: device x, B, C, dt, A, D; returns the six gradients (NaN-poisoned before the call)."""
+    x, Bm, Cm, dt, A, D = dev
+    out = {"dx": torch.full_like(x, float("nan")), "dB": torch.full_like(Bm, float("nan")),
+           "dC": torch.full_like(Cm, float("nan")), "ddt": torch.full_like(dt, float("nan")),
+           "dA": torch.full_like(A, float("nan")), "dD": torch.full_like(D, float("nan"))}
+    B.mate_bissd_backward(x, Bm, Cm, dt, A, D, dy, out["dx"], out["dB"], out["dC"], out["ddt"], out["dA"], out["dD"],
+                          order, pool)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_ssd_grads(got, want, tol, names=SSD_GRADS, heads=None):
+    for name in names:
+        g = to_f64(got[name])
+        if heads is not None and name in ("dx", "ddt"):
+            g = g[..., heads[0]:heads[1], :] if name == "dx" else g[..., heads[0]:heads[1]]
+        elif heads is not None and name in ("dA", "dD"):
+            g = g[heads[0]:heads[1]]
+        err = parity_error(g, want[name])
+        say(f"  {name} err={err:.3e}")
+        assert err <= tol, (name, err)
+
+
+def _dy_like(x, seed, scale=1.0):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return (torch.randn(x.shape, device="cuda", generator=g) * scale).to(x.dtype)
+
+
+@pytest.mark.parametrize("cfg,order", [(0, o) for o in range(5)] + [(1, 0), (1, 2), (1, 4)])
+def test_ssd_backward_parity_full(oracle_mod, cfg, order):
+    """Every gradient of the scan against the oracle on the tiny fp32 and the 8x16x16 bf16 workloads."""
+    wl = WORKLOADS[cfg]
+    say(f"ssd backward cfg{cfg} order{order}")
+    inp, d = ssd_device(cfg)
+    dev = [d[k] for k in ("x", "B", "C", "dt", "A", "D")]
+    dy = _dy_like(dev[0], 300 + cfg)
+    got = run_ssd_backward(dev, dy, order, wl.pool)
+    want = oracle_mod.bissd_backward(*(f32_of(inp[k]) for k in ("x", "B", "C")), inp["dt"].dev, inp["A"].dev,
+                                     inp["D"].dev, to_f64(dy).astype(np.float32), wl.grid, order, wl.pool)
+    check_ssd_grads(got, want, TOL[cfg])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P,S", [(16, 24), (64, 128)])
+def test_ssd_backward_ragged_with_review(oracle_mod, dtype, P, S):
+    """105 tokens (a ragged last chunk), 3x1x7 review pooling (5 review tokens), batch 2, 2 groups of 2 heads,
+    every order; bf16 gradients at 2e-2, fp32 at 1e-4."""
+    rng = np.random.default_rng(310 + P + S)
+    bsz, T, H, W, nh, G = 2, 3, 5, 7, 4, 2
+    rnd = lambda sc, *s: (rng.standard_normal(s) * sc).astype(np.float32)
+    x, Bm, Cm, dy = rnd(0.5, bsz, T, H, W, nh, P), rnd(0.5, bsz, T, H, W, G, S), rnd(0.5, bsz, T, H, W, G, S), \
+        rnd(1.0, bsz, T, H, W, nh, P)
+    if dtype == "bf16":
+        x, Bm, Cm, dy = (synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)) for a in (x, Bm, Cm, dy))
+    dt = np.log1p(np.exp(rng.normal(-1, 0.5, (bsz, T, H, W, nh)))).astype(np.float32)
+    A = -np.exp(rng.uniform(0, 1, nh)).astype(np.float32)
+    D = rng.standard_normal(nh).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = [torch.from_numpy(a).cuda().to(tdt) for a in (x, Bm, Cm)] + [torch.from_numpy(a).cuda() for a in (dt, A, D)]
+    dyd = torch.from_numpy(dy).cuda().to(tdt)
+    for order in range(5):
+        say(f"ssd backward ragged {dtype} P{P} S{S} order {order}")
+        got = run_ssd_backward(dev, dyd, order, (3, 1, 7))
+        want = oracle_mod.bissd_backward(x, Bm, Cm, dt, A, D, dy, (bsz, T, H, W), order, (3, 1, 7))
+        check_ssd_grads(got, want, 1e-4 if dtype == "f32" else 2e-2)
+
+
+def test_ssd_backward_deterministic():
+    _, d = ssd_device(1)
+    dev = [d[k] for k in ("x", "B", "C", "dt", "A", "D")]
+    dy = _dy_like(dev[0], 320)
+    g1 = run_ssd_backward(dev, dy, 3, (0, 0, 0))
+    g2 = run_ssd_backward(dev, dy, 3, (0, 0, 0))
+    for name in SSD_GRADS:
+        assert torch.equal(g1[name], g2[name]), name
+
+
+@pytest.mark.parametrize("cfg,order", [(3, 1), (4, 2)])
+def test_ssd_backward_sampled_heads(oracle_mod, cfg, order):
+    """The LinGen-4B-width workloads with review tokens, the full launch of all 80 heads: dx, ddt, dA and dD of
+    the first, middle and last head against the oracle. dB and dC sum over all heads, so they are checked by
+    additivity (the full launch equals the sum of launches over two halves of the heads) and, for one
+    half-sized launch of the sampled heads, against the oracle."""
+    wl = WORKLOADS[cfg]
+    say(f"ssd backward cfg{cfg} order{order} (sampled heads)")
+    inp, d = ssd_device(cfg)
+    dev = [d[k] for k in ("x", "B", "C", "dt", "A", "D")]
+    dy = _dy_like(dev[0], 330 + cfg)
+    got = run_ssd_backward(dev, dy, order, wl.pool)
+    for name in SSD_GRADS:
+        assert not torch.isnan(got[name]).any().item(), name
+    xh, Bh, Ch = f32_of(inp["x"]), f32_of(inp["B"]), f32_of(inp["C"])
+    dyh = to_f64(dy).astype(np.float32)
+    for lo, hi in SSD_SAMPLE_HEADS[cfg]:
+        want = oracle_mod.bissd_backward(xh, Bh, Ch, inp["dt"].dev, inp["A"].dev, inp["D"].dev, dyh, wl.grid, order,
+                                         wl.pool, heads=(lo, hi))
+        say(f" heads {lo}:{hi}")
+        check_ssd_grads(got, want, TOL[cfg], names=("dx", "ddt", "dA", "dD"), heads=(lo, hi))
+    # dB and dC: additivity over two halves of the heads, and the oracle on a launch of the sampled heads
+    half = wl.nheads // 2
+    parts = []
+    for lo, hi in ((0, half), (half, wl.nheads)):
+        sub = [dev[0][..., lo:hi, :].contiguous(), dev[1], dev[2], dev[3][..., lo:hi].contiguous(),
+               dev[4][lo:hi].contiguous(), dev[5][lo:hi].contiguous()]
+        parts.append(run_ssd_backward(sub, dy[..., lo:hi, :].contiguous(), order, wl.pool))
+    for name in ("dB", "dC"):
+        # each of the three launches rounds its fp32 sum to bf16 once (half an ulp, 2^-8 relative): where the
+        # two halves cancel, that rounding is large against the total, so the bound is taken per element
+        h1, h2, full = to_f64(parts[0][name]), to_f64(parts[1][name]), to_f64(got[name])
+        bound = 2.0 ** -8 * (np.abs(h1) + np.abs(h2) + np.abs(full)) + 1e-4 * np.sqrt(np.mean(full * full))
+        excess = float(np.max(np.abs(full - (h1 + h2)) / bound))
+        say(f"  {name} additivity: worst error {excess:.3f} of the rounding bound")
+        assert excess <= 1.0, (name, excess)
+    sel = [lo for lo, _ in SSD_SAMPLE_HEADS[cfg]]
+    sub = [dev[0][..., sel, :].contiguous(), dev[1], dev[2], dev[3][..., sel].contiguous(), dev[4][sel].contiguous(),
+           dev[5][sel].contiguous()]
+    got_s = run_ssd_backward(sub, dy[..., sel, :].contiguous(), order, wl.pool)
+    want_s = oracle_mod.bissd_backward(np.ascontiguousarray(xh[..., sel, :]), Bh, Ch,
+                                       np.ascontiguousarray(inp["dt"].dev[..., sel]), inp["A"].dev[sel],
+                                       inp["D"].dev[sel], np.ascontiguousarray(dyh[..., sel, :]), wl.grid, order,
+                                       wl.pool)
+    check_ssd_grads(got_s, want_s, TOL[cfg], names=("dB", "dC"))
