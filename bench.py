@@ -301,11 +301,12 @@ def table2_variants(torch, np, B, wl, ssd, att, ws, reps, algo):
                       "variants": rows}), flush=True)
 
 
-def tesa_backward_bench(torch, np, B, wl, att, reps):
-    """Per-layer time of TESA's backward (`mate_tesa_backward`: dq, dk, dv for an upstream gradient) beside
-    its forward, unshifted and shifted, on the workload's q, k, v. Algorithmic work: the forward's two
-    products per in-window pair (4 d flops), the backward's five (recomputed scores, dP, dV, dQ, dK: 10 d
-    flops). Prints one JSON line."""
+def backward_bench(torch, np, B, wl, att, ssd, ws_fwd, reps):
+    """Per-layer time of the two backward passes beside their forwards on the workload's inputs: TESA's
+    (`mate_tesa_backward`: dq, dk, dv for an upstream gradient), unshifted and shifted, and the
+    bidirectional scan's (`mate_bissd_backward`), per RMS order of the schedule. TESA's algorithmic work:
+    the forward's two products per in-window pair (4 d flops), the backward's five (recomputed scores, dP,
+    dV, dQ, dK: 10 d flops). Prints one JSON line."""
     stream = torch.cuda.current_stream()
 
     def timed(fn):
@@ -339,9 +340,40 @@ def tesa_backward_bench(torch, np, B, wl, att, reps):
             "forward_ms": tf, "backward_ms": tb, "backward_over_forward": tb / tf,
             "forward_tflops": ff / tf / 1e9, "backward_tflops": fb / tb / 1e9,
             "backward_mfma_frac": fb / tb / 1e9 / PEAK_BF16_TFLOPS}
-    print(json.dumps({"metric": "TESA backward vs forward per layer (one MI355X)", "unit": "ms", "data": "synthetic",
-                      "config": {"workload": wl.name, "grid": list(wl.grid), "heads": wl.t_heads,
-                                 "head_dim": wl.t_dim, "window": list(wl.window)}, "layers": rows}), flush=True)
+    del dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    # The scan's backward (mate_bissd_backward: dx, dB, dC, ddt, dA, dD) beside its forward, per RMS order.
+    # Algorithmic work of the backward: the chunked evaluation's products per token and head (both
+    # directions): the two state contributions and the two adjoint contributions, M^T dy and the four
+    # state products of dx, dB and dC (each 2 P S flops), and the intra-chunk products
+    # DX = dy x^T, M^T dy, Z B, Z^T C (2 Q P or 2 Q S flops each), Q the backward's chunk.
+    Hs, P, S, Q = wl.nheads, wl.headdim, wl.d_state, 64
+    flops_per_token = Hs * (2 * P * S * (4 + 2 + 4) + 2 * Q * (2 * P + 2 * S))
+    g2 = torch.Generator(device=ssd["x"].device).manual_seed(12)
+    dy = torch.randn(ssd["x"].shape, device=ssd["x"].device, generator=g2).to(ssd["x"].dtype)
+    grads = {"dx": torch.empty_like(ssd["x"]), "db": torch.empty_like(ssd["b"]), "dc": torch.empty_like(ssd["c"]),
+             "ddt": torch.empty_like(ssd["dt"]), "da": torch.empty_like(ssd["a"]), "dd": torch.empty_like(ssd["d"])}
+    bws = torch.empty(max(1, B.mate_bissd_backward_workspace_size(wl.grid, B.ssd_desc(ssd["x"], ssd["b"], 64,
+                                                                                       wl.pool))),
+                      dtype=torch.uint8, device=ssd["x"].device)
+    log(f"scan backward: workspace {bws.numel() / 2**30:.1f} GiB")
+    scan_rows = {}
+    for order in sorted(set(o for o, _ in wl.schedule)):
+        tf = timed(lambda: B.mate_bissd_scan(ssd["x"], ssd["b"], ssd["c"], ssd["dt"], ssd["a"], ssd["d"], ssd["y"],
+                                             order, wl.chunk, wl.pool, workspace=ws_fwd))
+        tb = timed(lambda: B.mate_bissd_backward(ssd["x"], ssd["b"], ssd["c"], ssd["dt"], ssd["a"], ssd["d"], dy,
+                                                 grads["dx"], grads["db"], grads["dc"], grads["ddt"], grads["da"],
+                                                 grads["dd"], order, wl.pool, workspace=bws))
+        fb = flops_per_token * wl.N * wl.batch
+        scan_rows[str(order)] = {"forward_ms": tf, "backward_ms": tb, "backward_over_forward": tb / tf,
+                                 "backward_tflops": fb / tb / 1e9,
+                                 "backward_fp32_frac": fb / tb / 1e9 / PEAK_FP32_TFLOPS}
+    print(json.dumps({"metric": "backward vs forward per layer: TESA and the bidirectional scan (one MI355X)",
+                      "unit": "ms", "data": "synthetic",
+                      "config": {"workload": wl.name, "grid": list(wl.grid), "tesa": [wl.t_heads, wl.t_dim],
+                                 "window": list(wl.window), "ssd": [Hs, P, S], "pool": list(wl.pool),
+                                 "ssd_backward_chunk": Q, "ssd_backward_workspace_gib": bws.numel() / 2**30},
+                      "tesa_layers": rows, "ssd_backward_per_order": scan_rows}), flush=True)
 
 
 def block_bench(torch, np, B, wl, reps):
@@ -450,7 +482,8 @@ def main():
     ap.add_argument("--block", action="store_true",
                     help="instead of the throughput line: one layer's token mixing with its projections (library GEMMs)")
     ap.add_argument("--backward", action="store_true",
-                    help="instead of the throughput line: TESA's backward beside its forward, per layer")
+                    help="instead of the throughput line: the backward passes (TESA, the scan) beside their "
+                         "forwards, per layer")
     ap.add_argument("--variants", action="store_true",
                     help="instead of the throughput line: per-layer time of the ablation variants (zigzag scan, "
                          "no review tokens, each branch alone)")
@@ -509,7 +542,7 @@ def main():
         table2_variants(torch, np, B, wl, ssd, att, ws, args.kernel_reps, algo)
         return
     if args.backward:
-        tesa_backward_bench(torch, np, B, wl, att, args.kernel_reps)
+        backward_bench(torch, np, B, wl, att, ssd, ws, args.kernel_reps)
         return
 
     def layer(order, shifted):
