@@ -30,8 +30,11 @@
 // whole sequence. Review tokens (whose outputs are dropped, dy = 0) receive the
 // adjoints of the initial states, and their gradients flow back through the
 // average pooling to the tokens of their pool blocks.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma_frag.hpp"
 #include "ssd_chunks.hpp"
 #include "ssd_common.hpp"
 #include "timing.hpp"
@@ -640,6 +643,601 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const float *__restrict__ pA
     dD[h] = sd;
 }
 
+// ---------------------------------------------------------------------------
+// MFMA kernels (bf16 tensors, headdim 64, d_state 64 or 128, chunks of 64): the
+// same chunked evaluation with every product on v_mfma_f32_32x32x16_bf16 and
+// fp32 accumulation. The tensors are bf16 already; the fp32 states enter the
+// products rounded to bf16, and the intra-chunk matrices M and Z, whose large
+// near-diagonal entries would otherwise dominate the error, as a pair of bf16
+// terms (hi = bf16(m), lo = bf16(m - hi)), i.e. to about 16 bits.
+// ---------------------------------------------------------------------------
+using frag::acc_row;
+using frag::bf16x8;
+using frag::f32x16;
+using frag::frag_rm;
+using frag::frag_tr;
+using frag::mfma_bf16;
+
+constexpr int QM = 64;         // chunk
+constexpr int PM = 64;         // head dim
+constexpr int LXM = PM + 8;    // row stride of [64][64] bf16 tiles
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kNoToken = 0xffffffffu;
+
+// Canonical token index of each scan position of chunk c (kNoToken past the end) and, with review tokens
+// (R > 0), the review token of its pool block. The caller synchronises before the indices are read.
+__device__ __forceinline__ void chunk_tokens(uint32_t *s_n, uint32_t *s_rv, uint32_t c, uint32_t N, int order,
+                                             uint32_t T, uint32_t H, uint32_t W, const int *rinv, int pt, int ph,
+                                             int pw, uint32_t R)
+{
+    for (int u = threadIdx.x; u < QM; u += NTB) {
+        const uint32_t i = c * QM + u;
+        uint32_t n = kNoToken, r = 0;
+        if (i < N) {
+            n = rms_index32(i, order, T, H, W);
+            if (R > 0) r = review_of(n, rinv, H, W, pt, ph, pw);
+        }
+        s_n[u] = n;
+        if (s_rv) s_rv[u] = r;
+    }
+}
+
+// 16-byte pieces of the chunk's token rows (COLS bf16 channels of head/group hd of nh) into an LDS tile of
+// stride ld, the tokens given by s_n; zero rows past the end.
+template <int COLS>
+__device__ __forceinline__ void load_rows_tok(__bf16 *dst, int ld, const __bf16 *src, int nh, int hd,
+                                              const uint32_t *s_n, size_t b, uint32_t N)
+{
+    constexpr int PPR = COLS / 8;  // pieces per row
+    for (int k = threadIdx.x; k < QM * PPR; k += NTB) {
+        const int u = k / PPR, pc = k % PPR;
+        const uint32_t n = s_n[u];
+        u32x4v v = u32x4v{0, 0, 0, 0};
+        if (n != kNoToken) v = *(const u32x4v *)(src + ((b * N + n) * nh + hd) * COLS + 8 * pc);
+        *(u32x4v *)(dst + u * ld + 8 * pc) = v;
+    }
+}
+
+// The four P x S bf16 states of one chunk and head (Hf, Hb, Gf, Gb) into consecutive LDS tiles [P][S]
+// (stride ld); returns this thread's part of <Hf, Gf> + <Hb, Gb> (fp32 sums of the bf16 values).
+template <int S>
+__device__ __forceinline__ float load_states_bf16(__bf16 *dst, int ld, const __bf16 *hf, const __bf16 *hb,
+                                                  const __bf16 *gf, const __bf16 *gb)
+{
+    float cross = 0.f;
+    for (int k = threadIdx.x; k < PM * S / 8; k += NTB) {
+        const int p = k / (S / 8), s8 = 8 * (k - p * (S / 8));
+        const size_t o = (size_t)p * S + s8;
+        const bf16x8 vhf = *(const bf16x8 *)(hf + o), vhb = *(const bf16x8 *)(hb + o);
+        const bf16x8 vgf = *(const bf16x8 *)(gf + o), vgb = *(const bf16x8 *)(gb + o);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cross += (float)vhf[j] * (float)vgf[j] + (float)vhb[j] * (float)vgb[j];
+        __bf16 *d = dst + p * ld + s8;
+        *(bf16x8 *)d = vhf;
+        *(bf16x8 *)(d + PM * ld) = vhb;
+        *(bf16x8 *)(d + 2 * PM * ld) = vgf;
+        *(bf16x8 *)(d + 3 * PM * ld) = vgb;
+    }
+    return cross;
+}
+
+// Sums over the 32 lanes of each half-wave of the 16 values v[e] (one per accumulator row of a 32 x 32
+// tile). Halving exchanges: after them lane j of the half holds the total of value (j >> 1) & 15.
+__device__ __forceinline__ float half_sum16(const float (&v)[16])
+{
+    const int l = threadIdx.x & 63;
+    float a8[8], a4[4], a2[2];
+    const bool b4 = l & 16, b3 = l & 8, b2 = l & 4, b1 = l & 2;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a8[k] = (b4 ? v[k + 8] : v[k]) + __shfl_xor(b4 ? v[k] : v[k + 8], 16, 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a4[k] = (b3 ? a8[k + 4] : a8[k]) + __shfl_xor(b3 ? a8[k] : a8[k + 4], 8, 64);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) a2[k] = (b2 ? a4[k + 2] : a4[k]) + __shfl_xor(b2 ? a4[k] : a4[k + 2], 4, 64);
+    const float a1 = (b1 ? a2[1] : a2[0]) + __shfl_xor(b1 ? a2[0] : a2[1], 2, 64);
+    return a1 + __shfl_xor(a1, 1, 64);
+}
+
+// Sum of v over the 256 threads of the block (every thread gets it); red holds NTB / 64 floats.
+__device__ __forceinline__ float block_sum(float v, float *red)
+{
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < NTB / 64; ++k) t += red[k];
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk contributions of the states (ADJ false: x, B) or the adjoint states (ADJ true: dy, C) on MFMA:
+// Sf = X^T diag(wf) B, Sb = X^T diag(wb) B (P x S, stored bf16), the weights as in k_chunk_states, applied
+// to the X^T operand in registers. Waves 0-1 make Sf, waves 2-3 Sb, S/32 tiles each.
+// grid (nch, nheads, batch), 256 threads.
+// ---------------------------------------------------------------------------
+template <int S, bool ADJ>
+__global__ __launch_bounds__(NTB) void k_bwd_states_mfma(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
+                                                         const float *__restrict__ dtT, const float *__restrict__ csT,
+                                                         const float *__restrict__ A, __bf16 *__restrict__ Sf,
+                                                         __bf16 *__restrict__ Sb, int nheads, int G, uint32_t N,
+                                                         uint32_t Lpad, int order, uint32_t T, uint32_t H, uint32_t W)
+{
+    constexpr int LS = S + 8, NT = S / 32, TPW = S / 32;
+    __shared__ __attribute__((aligned(16))) __bf16 sX[QM * LXM];
+    __shared__ __attribute__((aligned(16))) __bf16 sB[QM * LS];
+    __shared__ float s_w[2][QM];
+    __shared__ uint32_t s_n[QM];
+    const uint32_t c = blockIdx.x, nch = gridDim.x;
+    const int h = blockIdx.y, g = h / (nheads / G);
+    const size_t b = blockIdx.z;
+    const size_t row = (b * nheads + h) * Lpad + (size_t)c * QM;
+    const float a = A[h];
+    chunk_tokens(s_n, nullptr, c, N, order, T, H, W, nullptr, 1, 1, 1, 0);
+    __syncthreads();
+    load_rows_tok<PM>(sX, LXM, x, nheads, h, s_n, b, N);
+    load_rows_tok<S>(sB, LS, Bm, G, g, s_n, b, N);
+    {
+        const float tot = csT[row + QM - 1];
+        for (int u = threadIdx.x; u < QM; u += NTB) {
+            const float d = dtT[row + u], cs = csT[row + u];
+            s_w[0][u] = ADJ ? __expf(cs) : d * __expf(tot - cs);
+            s_w[1][u] = ADJ ? __expf(tot - (cs - d * a)) : d * __expf(cs - d * a);
+        }
+    }
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int which = wave >> 1;  // 0: Sf, 1: Sb
+    __bf16 *out = (which ? Sb : Sf) + ((b * nheads + h) * nch + c) * (size_t)(PM * S);
+    f32x16 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
+#pragma unroll
+    for (int k0 = 0; k0 < QM; k0 += 16) {
+        float w8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w8[j] = s_w[which][k0 + 8 * (lane >> 5) + j];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int tile = (wave & 1) * TPW + i, mt = tile / NT, nt = tile % NT;
+            bf16x8 af = frag_tr(sX, LXM, k0, 32 * mt);  // X^T[p][u]
+#pragma unroll
+            for (int j = 0; j < 8; ++j) af[j] = (__bf16)((float)af[j] * w8[j]);
+            acc[i] = mfma_bf16(af, frag_tr(sB, LS, k0, 32 * nt), acc[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int tile = (wave & 1) * TPW + i, mt = tile / NT, nt = tile % NT;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            out[(size_t)(32 * mt + acc_row(e, lane)) * S + 32 * nt + (lane & 31)] = (__bf16)acc[i][e];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Turns bf16 chunk contributions into the bf16 states entering each chunk, in place, with the running
+// state in fp32: the even blockIdx.y of a head runs left to right over Sf (Sf[c] becomes the state after
+// chunk c - 1), the odd one right to left over Sb (the state after chunk c + 1). h0f / h0b (optional) are
+// the initial states, finF / finB (optional) receive the final ones, fp32 [batch][nheads][P*S]. Each
+// thread carries 8 consecutive elements; the loads of U chunks are issued before their updates.
+// grid (ceil(P*S / 2048), 2 nheads, batch), 256 threads; P*S a multiple of 8.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_state_pass_bf16(__bf16 *__restrict__ Sf, __bf16 *__restrict__ Sb,
+                                                         const float *__restrict__ csT, const float *__restrict__ h0f,
+                                                         const float *__restrict__ h0b, float *__restrict__ finF,
+                                                         float *__restrict__ finB, int PS, int nch, uint32_t Lpad)
+{
+    constexpr int U = 8;
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (e >= PS) return;
+    const int h = blockIdx.y >> 1, dir = blockIdx.y & 1;
+    const size_t bh = (size_t)blockIdx.z * (gridDim.y >> 1) + h;
+    const float *tot = csT + bh * Lpad + (QM - 1);
+    __bf16 *base = (dir ? Sb : Sf) + bh * nch * (size_t)PS + e;
+    const float *h0 = dir ? h0b : h0f;
+    float *fin = dir ? finB : finF;
+    float run[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) run[j] = h0 ? h0[bh * PS + e + j] : 0.f;
+    for (int c0 = 0; c0 < nch; c0 += U) {
+        const int n = min(U, nch - c0);
+        bf16x8 v[U];
+        float dec[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (k < n) {
+                const int c = dir ? nch - 1 - (c0 + k) : c0 + k;
+                v[k] = *(const bf16x8 *)(base + (size_t)c * PS);
+                dec[k] = __expf(tot[(size_t)c * QM]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (k < n) {
+                const int c = dir ? nch - 1 - (c0 + k) : c0 + k;
+                bf16x8 o;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    o[j] = (__bf16)run[j];
+                    run[j] = dec[k] * run[j] + (float)v[k][j];
+                }
+                *(bf16x8 *)(base + (size_t)c * PS) = o;
+            }
+        }
+    }
+    if (fin)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fin[bh * PS + e + j] = run[j];
+}
+
+// ---------------------------------------------------------------------------
+// dB and dC of one chunk and group on MFMA, the group's heads in turn (sums in accumulators), with each
+// head's rf_t = exp(cs_t) C_t . (Hf^T dy_t), rb_t = exp(tot - ce_t) C_t . (Hb^T dy_t) and its
+// cross term exp(tot) (<Hf, Gf> + <Hb, Gb>) (fp32 sums of the stored bf16 states). Per head: DX = dy x^T and
+// Z = DX o L (to LDS), then for the wave's output tiles (rows: tokens, columns: state)
+//   dC[t][s] += (Z B)[t][s] + exp(cs_t) (dy Hf)[t][s] + exp(tot - ce_t) (dy Hb)[t][s],
+//   dB[u][s] += (Z^T C)[u][s] + ef_u (x Gf)[u][s] + eb_u (x Gb)[u][s].
+// grid (nch, G, batch), 256 threads.
+// ---------------------------------------------------------------------------
+template <int S>
+__global__ __launch_bounds__(NTB) void k_bwd_dbdc_mfma(const __bf16 *__restrict__ x, const __bf16 *__restrict__ dy,
+                                                       const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
+                                                       const float *__restrict__ dtT, const float *__restrict__ csT,
+                                                       const float *__restrict__ A, const __bf16 *__restrict__ Hf,
+                                                       const __bf16 *__restrict__ Hb, const __bf16 *__restrict__ Gf,
+                                                       const __bf16 *__restrict__ Gb, const float *__restrict__ drBg,
+                                                       const int *__restrict__ rinv, __bf16 *__restrict__ dB,
+                                                       __bf16 *__restrict__ dC, float *__restrict__ rfo,
+                                                       float *__restrict__ rbo, float *__restrict__ crs, int nheads,
+                                                       int G, uint32_t N, uint32_t Lpad, int order, uint32_t T,
+                                                       uint32_t H, uint32_t W, int pt, int ph, int pw, uint32_t R)
+{
+    constexpr int LS = S + 8, NT = S / 32, TPW = 2 * NT / 4;  // output tiles (of 2 NT) per wave
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    __bf16 *sB = (__bf16 *)smem_raw;       // [Q][LS]
+    __bf16 *sC = sB + QM * LS;             // [Q][LS]
+    __bf16 *sX = sC + QM * LS;             // [Q][LXM]
+    __bf16 *sY = sX + QM * LXM;            // [Q][LXM]
+    __bf16 *sZ = sY + QM * LXM;            // 2 x [Q][LXM]  Z_tu as bf16 hi + lo
+    __bf16 *sH = sZ + 2 * QM * LXM;        // 4 x [P][LS]: Hf, Hb, Gf, Gb
+    float *tkm = (float *)(sH + 4 * PM * LS);
+    const TokLds tk{tkm, tkm + QM, tkm + 2 * QM, tkm + 3 * QM, tkm + 4 * QM};
+    float *s_rp = tkm + 5 * QM;            // [2][NT][Q] partial row sums of rf, rb
+    float *s_red = s_rp + 2 * NT * QM;     // [NTB / 64]
+    __shared__ uint32_t s_n[QM], s_rv[QM];
+    const uint32_t c = blockIdx.x, nch = gridDim.x;
+    const int g = blockIdx.y, hpg = nheads / G;
+    const size_t b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    chunk_tokens(s_n, s_rv, c, N, order, T, H, W, rinv, pt, ph, pw, R);
+    __syncthreads();
+    load_rows_tok<S>(sB, LS, Bm, G, g, s_n, b, N);
+    load_rows_tok<S>(sC, LS, Cm, G, g, s_n, b, N);
+    f32x16 accB[TPW], accC[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) accB[i] = accC[i] = f32x16{};
+    const size_t PS = (size_t)PM * S;
+    for (int hk = 0; hk < hpg; ++hk) {
+        const int h = g * hpg + hk;
+        const float a = A[h];
+        const size_t row = (b * nheads + h) * Lpad + (size_t)c * QM;
+        const size_t so = ((b * nheads + h) * nch + c) * PS;
+        __syncthreads();  // the previous head's reads of the tiles, tokens and partial sums are done
+        load_tokens(tk, dtT, csT, row, QM, a);
+        load_rows_tok<PM>(sX, LXM, x, nheads, h, s_n, b, N);
+        load_rows_tok<PM>(sY, LXM, dy, nheads, h, s_n, b, N);
+        const float cr = load_states_bf16<S>(sH, LS, Hf + so, Hb + so, Gf + so, Gb + so);
+        __syncthreads();
+        {  // DX tile (t, u) of this wave, then Z = DX o L into LDS
+            const int mt = wave >> 1, nt = wave & 1;
+            f32x16 d = f32x16{};
+#pragma unroll
+            for (int k0 = 0; k0 < PM; k0 += 16)
+                d = mfma_bf16(frag_rm(sY, LXM, 32 * mt, k0), frag_rm(sX, LXM, 32 * nt, k0), d);
+            const int u = 32 * nt + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = 32 * mt + acc_row(e, lane);
+                const float z = d[e] * ldt(tk, t, u);
+                const __bf16 hi = (__bf16)z;
+                sZ[t * LXM + u] = hi;
+                sZ[QM * LXM + t * LXM + u] = (__bf16)(z - (float)hi);
+            }
+        }
+        const float crt = block_sum(cr, s_red);  // also orders the Z stores before the reads below
+        if (threadIdx.x == 0) crs[(b * nheads + h) * nch + c] = __expf(tk.cs[QM - 1]) * crt;
+        const float tot = tk.cs[QM - 1];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int tile = wave * TPW + i, mt = tile / NT, nt = tile % NT;
+#pragma unroll
+            for (int k0 = 0; k0 < QM; k0 += 16) {
+                const bf16x8 bb = frag_tr(sB, LS, k0, 32 * nt), cc = frag_tr(sC, LS, k0, 32 * nt);
+#pragma unroll
+                for (int part = 0; part < 2; ++part) {
+                    const __bf16 *z = sZ + part * QM * LXM;
+                    accC[i] = mfma_bf16(frag_rm(z, LXM, 32 * mt, k0), bb, accC[i]);
+                    accB[i] = mfma_bf16(frag_tr(z, LXM, k0, 32 * mt), cc, accB[i]);
+                }
+            }
+            // the A operand's row (token u of dB) is this lane's: its weights ef_u, eb_u scale the x fragment
+            const float wxf = tk.ef[32 * mt + (lane & 31)], wxb = tk.eb[32 * mt + (lane & 31)];
+            f32x16 hf = f32x16{}, hb = f32x16{};
+#pragma unroll
+            for (int k0 = 0; k0 < PM; k0 += 16) {
+                const bf16x8 ya = frag_rm(sY, LXM, 32 * mt, k0), xa = frag_rm(sX, LXM, 32 * mt, k0);
+                bf16x8 xf, xb;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    xf[j] = (__bf16)(wxf * (float)xa[j]);
+                    xb[j] = (__bf16)(wxb * (float)xa[j]);
+                }
+                hf = mfma_bf16(ya, frag_tr(sH, LS, k0, 32 * nt), hf);
+                hb = mfma_bf16(ya, frag_tr(sH + PM * LS, LS, k0, 32 * nt), hb);
+                accB[i] = mfma_bf16(xf, frag_tr(sH + 2 * PM * LS, LS, k0, 32 * nt), accB[i]);
+                accB[i] = mfma_bf16(xb, frag_tr(sH + 3 * PM * LS, LS, k0, 32 * nt), accB[i]);
+            }
+            const int s = 32 * nt + (lane & 31);
+            float pf[16], pb[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = 32 * mt + acc_row(e, lane);  // token of this row of dC
+                const float vf = __expf(tk.cs[t]) * hf[e], vb = __expf(tot - tk.ce[t]) * hb[e];
+                accC[i][e] += vf + vb;
+                const float cv = (float)sC[t * LS + s];
+                pf[e] = cv * vf;
+                pb[e] = cv * vb;
+            }
+            const float rf = half_sum16(pf), rb = half_sum16(pb);
+            if ((lane & 1) == 0) {
+                const int t = 32 * mt + acc_row((lane & 31) >> 1, lane);
+                s_rp[nt * QM + t] = rf;
+                s_rp[(NT + nt) * QM + t] = rb;
+            }
+        }
+        __syncthreads();
+        for (int t = threadIdx.x; t < QM; t += NTB) {
+            float vf = 0.f, vb = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                vf += s_rp[nt * QM + t];
+                vb += s_rp[(NT + nt) * QM + t];
+            }
+            rfo[row + t] = vf;
+            rbo[row + t] = vb;
+        }
+    }
+    const float inv_cnt = R > 0 ? 1.f / (float)(pt * ph * pw) : 0.f;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int tile = wave * TPW + i, mt = tile / NT, nt = tile % NT;
+        const int s = 32 * nt + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int t = 32 * mt + acc_row(e, lane);
+            const uint32_t n = s_n[t];
+            if (n != kNoToken) {
+                const size_t o = ((b * N + n) * G + g) * S + s;
+                float vb = accB[i][e];
+                if (R > 0) vb += drBg[((b * R + s_rv[t]) * G + g) * S + s] * inv_cnt;
+                dB[o] = (__bf16)vb;
+                dC[o] = (__bf16)accC[i][e];
+            }
+        }
+    }
+}
+
+// Inclusive prefix (SUFFIX false) or suffix sum over the 64 lanes of a wave.
+template <bool SUFFIX>
+__device__ __forceinline__ float wave_scan(float v)
+{
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = SUFFIX ? __shfl_down(v, off, 64) : __shfl_up(v, off, 64);
+        if (SUFFIX ? l + off < 64 : l >= off) v += y;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// dx and ddt of one chunk and head on MFMA. CB = C B^T and DX = dy x^T (tile (t, u) per wave) give
+// M = CB o L (to LDS as bf16 hi + lo) and, in registers, W = M o DX (t != u), whose strict row and column
+// sums are reduced across lanes; then per wave a tile (u, p) of (Gf, Gb read as MFMA operands from memory)
+//   dx = M^T dy + ef_u (B Gf^T) + eb_u (B Gb^T) + 2 D dy (+ the review token's share),
+// and the per-token sums expl, cf, cb. Last, one wave (a lane per token k) forms
+//   span(k) = Sf(k) + sum_{t >= k} rf_t + sum_{u < k} cf_u + Sb(k) + sum_{t <= k} rb_t + sum_{u > k} cb_u
+//             + exp(tot) (<Hf, Gf> + <Hb, Gb>)
+// (Sf, Sb as in k_bwd_ddt; rf, rb and the cross term from the dB/dC kernel) with two wave scans:
+// ddt_k = expl_k + A span(k), and the chunk's parts of dA and dD. grid (nch, nheads, batch), 256 threads.
+// ---------------------------------------------------------------------------
+template <int S>
+__global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ x, const __bf16 *__restrict__ dy,
+                                                     const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
+                                                     const float *__restrict__ dtT, const float *__restrict__ csT,
+                                                     const float *__restrict__ A, const float *__restrict__ Dv,
+                                                     const __bf16 *__restrict__ Gf, const __bf16 *__restrict__ Gb,
+                                                     const float *__restrict__ rfi, const float *__restrict__ rbi,
+                                                     const float *__restrict__ crs, const float *__restrict__ drx,
+                                                     const float *__restrict__ drdt, const int *__restrict__ rinv,
+                                                     __bf16 *__restrict__ dx, float *__restrict__ ddt,
+                                                     float *__restrict__ pA, float *__restrict__ pD, int nheads, int G,
+                                                     uint32_t N, uint32_t Lpad, int order, uint32_t T, uint32_t H,
+                                                     uint32_t W, int pt, int ph, int pw, uint32_t R)
+{
+    constexpr int LS = S + 8;
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    __shared__ uint32_t s_n[QM], s_rv[QM];
+    __bf16 *sB = (__bf16 *)smem_raw;       // [Q][LS]
+    __bf16 *sC = sB + QM * LS;             // [Q][LS]
+    __bf16 *sX = sC + QM * LS;             // [Q][LXM]
+    __bf16 *sY = sX + QM * LXM;            // [Q][LXM]
+    __bf16 *sM = sY + QM * LXM;            // 2 x [Q][LXM]  M_tu as bf16 hi + lo
+    float *tkm = (float *)(sM + 2 * QM * LXM);
+    const TokLds tk{tkm, tkm + QM, tkm + 2 * QM, tkm + 3 * QM, tkm + 4 * QM};
+    float *s_red = tkm + 5 * QM;           // [3][2][Q]: expl, cf, cb partials per p-tile
+    float *s_w = s_red + 6 * QM;           // [4][2][Q]: W's column sums below / above, row sums left / right
+    float *s_blk = s_w + 8 * QM;           // [NTB / 64]
+    const uint32_t c = blockIdx.x, nch = gridDim.x;
+    const int h = blockIdx.y, g = h / (nheads / G);
+    const size_t b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const size_t row = (b * nheads + h) * Lpad + (size_t)c * QM;
+    const size_t PS = (size_t)PM * S, so = ((b * nheads + h) * nch + c) * PS;
+    const float a = A[h];
+    // B operands of this wave's dx tile straight from the stored states (rows 32 nt + l % 32 of Gf and Gb),
+    // issued first so that they arrive while the chunk is staged
+    bf16x8 gfr[S / 16], gbr[S / 16];
+    {
+        const size_t o = so + (size_t)(32 * (wave & 1) + (lane & 31)) * S + 8 * (lane >> 5);
+#pragma unroll
+        for (int k = 0; k < S / 16; ++k) {
+            gfr[k] = *(const bf16x8 *)(Gf + o + 16 * k);
+            gbr[k] = *(const bf16x8 *)(Gb + o + 16 * k);
+        }
+    }
+    chunk_tokens(s_n, s_rv, c, N, order, T, H, W, rinv, pt, ph, pw, R);
+    load_tokens(tk, dtT, csT, row, QM, a);
+    __syncthreads();
+    load_rows_tok<S>(sB, LS, Bm, G, g, s_n, b, N);
+    load_rows_tok<S>(sC, LS, Cm, G, g, s_n, b, N);
+    load_rows_tok<PM>(sX, LXM, x, nheads, h, s_n, b, N);
+    load_rows_tok<PM>(sY, LXM, dy, nheads, h, s_n, b, N);
+    __syncthreads();
+    float xdy = 0.f;  // x . dy over the chunk (rows past the end hold zeros)
+    for (int e = threadIdx.x; e < QM * PM; e += NTB) {
+        const int u = e / PM, p = e - u * PM;
+        xdy += (float)sX[u * LXM + p] * (float)sY[u * LXM + p];
+    }
+    {  // CB and DX tile (t, u) of this wave: M, and W's strict row and column sums
+        const int mt = wave >> 1, nt = wave & 1;
+        f32x16 cb = f32x16{}, d = f32x16{};
+#pragma unroll
+        for (int k0 = 0; k0 < S; k0 += 16)
+            cb = mfma_bf16(frag_rm(sC, LS, 32 * mt, k0), frag_rm(sB, LS, 32 * nt, k0), cb);
+#pragma unroll
+        for (int k0 = 0; k0 < PM; k0 += 16)
+            d = mfma_bf16(frag_rm(sY, LXM, 32 * mt, k0), frag_rm(sX, LXM, 32 * nt, k0), d);
+        const int u = 32 * nt + (lane & 31);
+        float below = 0.f, above = 0.f, left[16], right[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int t = 32 * mt + acc_row(e, lane);
+            const float m = cb[e] * ldt(tk, t, u);
+            const __bf16 hi = (__bf16)m;
+            sM[t * LXM + u] = hi;
+            sM[QM * LXM + t * LXM + u] = (__bf16)(m - (float)hi);
+            const float w = m * d[e];
+            below += t > u ? w : 0.f;
+            above += t < u ? w : 0.f;
+            left[e] = u < t ? w : 0.f;
+            right[e] = u > t ? w : 0.f;
+        }
+        below += __shfl_xor(below, 32, 64);
+        above += __shfl_xor(above, 32, 64);
+        const float rl = half_sum16(left), rr = half_sum16(right);
+        if (lane < 32) {
+            s_w[(0 * 2 + mt) * QM + u] = below;
+            s_w[(1 * 2 + mt) * QM + u] = above;
+        }
+        if ((lane & 1) == 0) {
+            const int t = 32 * mt + acc_row((lane & 31) >> 1, lane);
+            s_w[(2 * 2 + nt) * QM + t] = rl;
+            s_w[(3 * 2 + nt) * QM + t] = rr;
+        }
+    }
+    const float dD = block_sum(xdy, s_blk);  // also orders the M stores before the reads below
+    {  // dx tile (u, p) of this wave
+        const int mt = wave >> 1, nt = wave & 1;
+        f32x16 in = f32x16{}, af = f32x16{}, ab = f32x16{};
+#pragma unroll
+        for (int k0 = 0; k0 < QM; k0 += 16) {
+            const bf16x8 yy = frag_tr(sY, LXM, k0, 32 * nt);
+            in = mfma_bf16(frag_tr(sM, LXM, k0, 32 * mt), yy, in);
+            in = mfma_bf16(frag_tr(sM + QM * LXM, LXM, k0, 32 * mt), yy, in);
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < S; k0 += 16) {
+            const bf16x8 ba = frag_rm(sB, LS, 32 * mt, k0);
+            af = mfma_bf16(ba, gfr[k0 / 16], af);
+            ab = mfma_bf16(ba, gbr[k0 / 16], ab);
+        }
+        const int p = 32 * nt + (lane & 31);
+        const float twoD = 2.f * Dv[h];
+        const float inv_cnt = R > 0 ? 1.f / (float)(pt * ph * pw) : 0.f;
+        float ve[16], vf[16], vb[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int u = 32 * mt + acc_row(e, lane);
+            const float sf = tk.ef[u] * af[e], sb = tk.eb[u] * ab[e];
+            const float scan = in[e] + sf + sb;
+            const float xv = (float)sX[u * LXM + p], dtu = tk.dt[u];
+            ve[e] = dtu > 0.f ? xv * scan / dtu : 0.f;
+            vf[e] = xv * sf;
+            vb[e] = xv * sb;
+            const uint32_t n = s_n[u];
+            if (n != kNoToken) {
+                float v = scan + twoD * (float)sY[u * LXM + p];
+                if (R > 0) v += drx[((b * R + s_rv[u]) * nheads + h) * PM + p] * inv_cnt;
+                dx[((b * N + n) * nheads + h) * PM + p] = (__bf16)v;
+            }
+        }
+        const float re = half_sum16(ve), rf = half_sum16(vf), rb = half_sum16(vb);
+        if ((lane & 1) == 0) {
+            const int u = 32 * mt + acc_row((lane & 31) >> 1, lane);
+            s_red[(0 * 2 + nt) * QM + u] = re;
+            s_red[(1 * 2 + nt) * QM + u] = rf;
+            s_red[(2 * 2 + nt) * QM + u] = rb;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {  // lane k: token k of the chunk
+        const int k = lane;
+        const float expl = s_red[k] + s_red[QM + k];
+        const float cf = s_red[2 * QM + k] + s_red[3 * QM + k], cbk = s_red[4 * QM + k] + s_red[5 * QM + k];
+        const float dj_f = (s_w[k] + s_w[QM + k]) - (s_w[4 * QM + k] + s_w[5 * QM + k]);
+        const float dj_b = (s_w[6 * QM + k] + s_w[7 * QM + k]) - (s_w[2 * QM + k] + s_w[3 * QM + k]);
+        const float rf = rfi[row + k], rb = rbi[row + k];
+        // Sf + cf_lt: exclusive prefix of dj_f + cf; Sb + rb_le: inclusive prefix of dj_b + rb;
+        // rf_ge: inclusive suffix of rf; cb_gt: exclusive suffix of cb
+        const float fa = dj_f + cf;
+        const float pre = wave_scan<false>(fa + dj_b + rb) - fa;
+        const float suf = wave_scan<true>(rf + cbk) - cbk;
+        const float span = pre + suf + crs[(b * nheads + h) * nch + c];
+        const uint32_t n = s_n[k];
+        float dA = 0.f;
+        if (n != kNoToken) {
+            float v = expl + a * span;
+            if (R > 0) v += drdt[(b * R + s_rv[k]) * nheads + h] / (float)(pt * ph * pw);
+            ddt[(b * N + n) * nheads + h] = v;
+            dA = tk.dt[k] * span;
+        }
+        for (int off = 32; off > 0; off >>= 1) dA += __shfl_xor(dA, off, 64);
+        if (lane == 0) {
+            pA[(b * nheads + h) * nch + c] = dA;
+            pD[(b * nheads + h) * nch + c] = 2.f * dD;
+        }
+    }
+}
+
+// LDS bytes of the two MFMA kernels.
+template <int S>
+constexpr size_t dbdc_mfma_lds()
+{
+    return (size_t)2 * QM * (S + 8) * 2 + 4 * QM * LXM * 2 + 4 * PM * (S + 8) * 2 +
+           (5 * QM + 2 * (S / 32) * QM + NTB / 64) * 4;
+}
+template <int S>
+constexpr size_t dx_mfma_lds()
+{
+    return (size_t)2 * QM * (S + 8) * 2 + 4 * QM * LXM * 2 + (5 * QM + 6 * QM + 8 * QM + NTB / 64) * 4;
+}
+
+static_assert(dbdc_mfma_lds<128>() <= 160 * 1024 && dx_mfma_lds<128>() <= 160 * 1024, "LDS of the MFMA kernels");
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // LDS floats of the dB/dC kernel (the largest of the per-chunk kernels) for chunk Q.
@@ -648,14 +1246,18 @@ size_t dbdc_lds(int Q, int P, int S)
     return (size_t)2 * Q * (S + 1) + 2 * Q * (P + 1) + (size_t)Q * (Q + 1) + 4 * P * (SL + 1) + 5 * Q;
 }
 
+// The MFMA kernels take bf16 tensors with headdim 64 and d_state 64 or 128.
+bool bwd_mfma(const SsdProblem &p) { return p.dtype != 0 && p.headdim == PM && (p.d_state == 64 || p.d_state == 128); }
+
 int bwd_chunk(const SsdProblem &p)
 {
+    if (bwd_mfma(p)) return QM;
     return dbdc_lds(64, p.headdim, p.d_state) * 4 <= 150 * 1024 ? 64 : 32;
 }
 
 struct BwdLayout {
     int Q, nch, nchR;
-    size_t dtT, csT, Sf, Sb, Uf, Ub, CB, expl, cf, cb, rf, rb, pA, pD;
+    size_t dtT, csT, Sf, Sb, Uf, Ub, CB, expl, cf, cb, rf, rb, crs, pA, pD;
     size_t rx, rB, rdt, rdtT, rcsT, rSf, rSb, h0f, h0b, Gf0, Gb0, drx, drB, drBg, drdt, pAr, rinv, total;
 };
 
@@ -671,14 +1273,19 @@ BwdLayout bwd_layout(const SsdProblem &p)
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     l.dtT = take(B * Hs * Lpad * 4);
     l.csT = take(B * Hs * Lpad * 4);
-    l.Sf = take(B * Hs * l.nch * PS * 4);
-    l.Sb = take(B * Hs * l.nch * PS * 4);
-    l.Uf = take(B * Hs * l.nch * PS * 4);
-    l.Ub = take(B * Hs * l.nch * PS * 4);
-    l.CB = take(B * G * l.nch * (size_t)l.Q * l.Q * 4);
-    l.expl = take(B * Hs * Lpad * 4);
-    l.cf = take(B * Hs * Lpad * 4);
-    l.cb = take(B * Hs * Lpad * 4);
+    const size_t se = bwd_mfma(p) ? 2 : 4;  // bytes per stored state element (bf16 on the MFMA path)
+    l.Sf = take(B * Hs * l.nch * PS * se);
+    l.Sb = take(B * Hs * l.nch * PS * se);
+    l.Uf = take(B * Hs * l.nch * PS * se);
+    l.Ub = take(B * Hs * l.nch * PS * se);
+    if (bwd_mfma(p)) {
+        l.crs = take(B * Hs * l.nch * 4);
+    } else {
+        l.CB = take(B * G * l.nch * (size_t)l.Q * l.Q * 4);
+        l.expl = take(B * Hs * Lpad * 4);
+        l.cf = take(B * Hs * Lpad * 4);
+        l.cb = take(B * Hs * Lpad * 4);
+    }
     l.rf = take(B * Hs * Lpad * 4);
     l.rb = take(B * Hs * Lpad * 4);
     l.pA = take(B * Hs * l.nch * 4);
@@ -710,6 +1317,44 @@ BwdLayout bwd_layout(const SsdProblem &p)
 size_t review_lds(const SsdProblem &p)
 {
     return ((size_t)2 * p.headdim * p.d_state + p.headdim + p.d_state + 4 * (size_t)p.R + 2 * NTB) * 4;
+}
+
+// Chunk states, their passes, and the per-chunk gradient kernels on MFMA (after the review tokens'
+// states and dt's cumulative sums are in place).
+template <int S>
+hipError_t run_chunks_mfma(const SsdProblem &p, const SsdGradArgs &a, const BwdLayout &l, char *w, const int *rinv,
+                           const float *h0f, const float *h0b, float *Gf0, float *Gb0, const float *drx,
+                           const float *drdt, const float *drBg, const float *pAr, hipStream_t st)
+{
+    auto F = [&](size_t off) { return (float *)(w + off); };
+    auto Hh = [&](size_t off) { return (__bf16 *)(w + off); };
+    float *dtT = F(l.dtT), *csT = F(l.csT);
+    __bf16 *Sf = Hh(l.Sf), *Sb = Hh(l.Sb), *Uf = Hh(l.Uf), *Ub = Hh(l.Ub);
+    float *rf = F(l.rf), *rb = F(l.rb), *crs = F(l.crs), *pA = F(l.pA), *pD = F(l.pD);
+    const int Hs = p.nheads, G = p.ngroups, B = (int)p.batch;
+    const uint32_t N = (uint32_t)p.N, Lpad = (uint32_t)(l.nch * QM), R = (uint32_t)p.R;
+    const uint32_t T = (uint32_t)p.T, H = (uint32_t)p.H, W = (uint32_t)p.W;
+    const __bf16 *x = (const __bf16 *)a.x, *Bm = (const __bf16 *)a.b, *Cm = (const __bf16 *)a.c;
+    const __bf16 *dy = (const __bf16 *)a.dy;
+    const dim3 gh(l.nch, Hs, B), gg(l.nch, G, B), gp((PM * S / 8 + 255) / 256, 2 * Hs, B);
+    k_bwd_states_mfma<S, false><<<gh, NTB, 0, st>>>(x, Bm, dtT, csT, a.a, Sf, Sb, Hs, G, N, Lpad, p.order, T, H, W);
+    k_state_pass_bf16<<<gp, 256, 0, st>>>(Sf, Sb, csT, h0f, h0b, nullptr, nullptr, PM * S, l.nch, Lpad);
+    k_bwd_states_mfma<S, true><<<gh, NTB, 0, st>>>(dy, Cm, dtT, csT, a.a, Uf, Ub, Hs, G, N, Lpad, p.order, T, H, W);
+    k_state_pass_bf16<<<gp, 256, 0, st>>>(Ub, Uf, csT, nullptr, nullptr, Gb0, Gf0, PM * S, l.nch, Lpad);
+    if (R > 0) {
+        k_review_grads<<<B * Hs, NTB, review_lds(p), st>>>(F(l.rx), F(l.rB), F(l.rdt), a.a, Gf0, Gb0,
+                                                           (float *)drx, F(l.drB), (float *)drdt, (float *)pAr, Hs,
+                                                           PM, S, G, (int)R);
+        k_review_group<<<dim3(R, B), 256, 0, st>>>(F(l.drB), (float *)drBg, Hs, S, G);
+    }
+    k_bwd_dbdc_mfma<S><<<gg, NTB, dbdc_mfma_lds<S>(), st>>>(
+        x, dy, Bm, Cm, dtT, csT, a.a, Sf, Sb, Uf, Ub, drBg, rinv, (__bf16 *)a.db, (__bf16 *)a.dc, rf, rb, crs, Hs, G,
+        N, Lpad, p.order, T, H, W, p.pool_t, p.pool_h, p.pool_w, R);
+    k_bwd_dx_mfma<S><<<gh, NTB, dx_mfma_lds<S>(), st>>>(x, dy, Bm, Cm, dtT, csT, a.a, a.d, Uf, Ub, rf, rb, crs, drx,
+                                                        drdt, rinv, (__bf16 *)a.dx, a.ddt, pA, pD, Hs, G, N, Lpad,
+                                                        p.order, T, H, W, p.pool_t, p.pool_h, p.pool_w, R);
+    k_bwd_reduce<<<(Hs + 255) / 256, 256, 0, st>>>(pA, pD, pAr, a.da, a.dd, Hs, l.nch, B);
+    return hipGetLastError();
 }
 
 template <typename E>
@@ -763,6 +1408,12 @@ hipError_t run_backward(const SsdProblem &p, const SsdGradArgs &a, void *ws, hip
     }
     k_prep_dt<true><<<dim3(l.nch, (Hs + 63) / 64, B), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q, p.order, T,
                                                                     H, W);
+    if constexpr (std::is_same<E, bf16_t>::value) {
+        if (bwd_mfma(p)) {
+            if (S == 64) return run_chunks_mfma<64>(p, a, l, w, rinv, h0f, h0b, Gf0, Gb0, drx, drdt, drBg, pAr, st);
+            return run_chunks_mfma<128>(p, a, l, w, rinv, h0f, h0b, Gf0, Gb0, drx, drdt, drBg, pAr, st);
+        }
+    }
     // states of the forward pass (entering each chunk), then the adjoint states
     k_chunk_states<E, true, false><<<dim3(l.nch, Hs, B), 256, states_lds, st>>>(x, Bm, dtT, csT, a.a, Sf, Sb, Hs, P, S,
                                                                                G, N, Lpad, Q, p.order, T, H, W);
@@ -829,6 +1480,14 @@ hipError_t ssd_backward_prepare()
     if ((e = set_lds_attrs<bf16_t>()) != hipSuccess) return e;
     if ((e = hipFuncSetAttribute((const void *)k_chunk_states<float, false, false>,
                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)k_bwd_dbdc_mfma<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)dbdc_mfma_lds<64>())) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)k_bwd_dbdc_mfma<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)dbdc_mfma_lds<128>())) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)k_bwd_dx_mfma<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)dx_mfma_lds<64>())) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)k_bwd_dx_mfma<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)dx_mfma_lds<128>())) != hipSuccess) return e;
     return hipFuncSetAttribute((const void *)k_review_grads, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 

@@ -47,6 +47,7 @@
 // consecutive heads of one segment and share B, C and CB in that XCD's L2.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma_frag.hpp"
 #include "ssd_common.hpp"
 #include "timing.hpp"
 
@@ -127,24 +128,8 @@ __device__ __forceinline__ uint32_t xcd_item()
     return (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 }
 
-// MFMA operand fragment from a row-major [k][n] LDS tile (row stride ld):
-// lane l gets column n_base + l % 32 at rows k_base + 8 (l / 32) + 0..7.
-__device__ __forceinline__ bf16x8 frag_tr(const __bf16 *tile, int ld, int k_base, int n_base)
-{
-    const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
-    const __bf16 *p = tile + (k_base + 8 * (g >> 1) + (s >> 2)) * ld + n_base + 16 * (g & 1) + 4 * (s & 3);
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
-    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 4 * ld));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// MFMA operand fragment from a row-major [m][k] LDS tile: lane l gets row
-// m_base + l % 32 at columns k_base + 8 (l / 32) + 0..7.
-__device__ __forceinline__ bf16x8 frag_rm(const __bf16 *tile, int ld, int m_base, int k_base)
-{
-    const int l = threadIdx.x & 63;
-    return *(const bf16x8 *)(tile + (m_base + (l & 31)) * ld + k_base + 8 * (l >> 5));
-}
+using frag::frag_rm;
+using frag::frag_tr;
 
 // Q token rows of COLS bf16 each, split in 16-byte units over the workgroup.
 // Row u of the chunk is read from global row srow[u] (an LDS table of the
