@@ -663,6 +663,19 @@ constexpr int PM = 64;         // head dim
 constexpr int LXM = PM + 8;    // row stride of [64][64] bf16 tiles
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
+// L_tu without branches (the exponent is selected first, so the other direction's never overflows).
+__device__ __forceinline__ float ldt_sel(const TokLds &tk, int t, int u)
+{
+    const float arg = u < t ? tk.cs[t] - tk.cs[u] : tk.ce[u] - tk.ce[t];
+    const float v = tk.dt[u] * __expf(arg);
+    return u == t ? 2.f * tk.dt[t] : v;
+}
+
+// Workgroup barrier for data exchanged through LDS: waits for this wave's LDS operations only, so global
+// loads issued ahead (prefetches into registers) stay in flight across it. Everything the MFMA kernels
+// share between waves is written to LDS explicitly.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 constexpr uint32_t kNoToken = 0xffffffffu;
 
 // Canonical token index of each scan position of chunk c (kNoToken past the end) and, with review tokens
@@ -683,43 +696,54 @@ __device__ __forceinline__ void chunk_tokens(uint32_t *s_n, uint32_t *s_rv, uint
     }
 }
 
-// 16-byte pieces of the chunk's token rows (COLS bf16 channels of head/group hd of nh) into an LDS tile of
-// stride ld, the tokens given by s_n; zero rows past the end.
-template <int COLS>
-__device__ __forceinline__ void load_rows_tok(__bf16 *dst, int ld, const __bf16 *src, int nh, int hd,
-                                              const uint32_t *s_n, size_t b, uint32_t N)
+// 16-byte pieces of the chunk's token rows (COLS bf16 channels of head/group hd of nh, the tokens given
+// by s_n; zeros past the end) into registers, NTH threads sharing the QM x COLS tile ...
+template <int COLS, int NTH>
+__device__ __forceinline__ void fetch_rows(u32x4v (&r)[QM * COLS / 8 / NTH], const __bf16 *src, int nh, int hd,
+                                           const uint32_t *s_n, size_t b, uint32_t N)
 {
     constexpr int PPR = COLS / 8;  // pieces per row
-    for (int k = threadIdx.x; k < QM * PPR; k += NTB) {
-        const int u = k / PPR, pc = k % PPR;
+    static_assert(QM * PPR % NTH == 0, "row pieces");
+#pragma unroll
+    for (int j = 0; j < QM * PPR / NTH; ++j) {
+        const int k = threadIdx.x + NTH * j, u = k / PPR, pc = k % PPR;
         const uint32_t n = s_n[u];
-        u32x4v v = u32x4v{0, 0, 0, 0};
-        if (n != kNoToken) v = *(const u32x4v *)(src + ((b * N + n) * nh + hd) * COLS + 8 * pc);
-        *(u32x4v *)(dst + u * ld + 8 * pc) = v;
+        // an unconditional load (token 0's row past the end, zeroed when stored): no branch around it
+        r[j] = *(const u32x4v *)(src + ((b * N + (n == kNoToken ? 0u : n)) * nh + hd) * COLS + 8 * pc);
     }
 }
 
-// The four P x S bf16 states of one chunk and head (Hf, Hb, Gf, Gb) into consecutive LDS tiles [P][S]
-// (stride ld); returns this thread's part of <Hf, Gf> + <Hb, Gb> (fp32 sums of the bf16 values).
-template <int S>
-__device__ __forceinline__ float load_states_bf16(__bf16 *dst, int ld, const __bf16 *hf, const __bf16 *hb,
-                                                  const __bf16 *gf, const __bf16 *gb)
+// ... and from registers into an LDS tile of row stride ld (rows past the end as zeros).
+template <int COLS, int NTH>
+__device__ __forceinline__ void store_rows(__bf16 *dst, int ld, const u32x4v (&r)[QM * COLS / 8 / NTH],
+                                           const uint32_t *s_n)
 {
-    float cross = 0.f;
-    for (int k = threadIdx.x; k < PM * S / 8; k += NTB) {
-        const int p = k / (S / 8), s8 = 8 * (k - p * (S / 8));
-        const size_t o = (size_t)p * S + s8;
-        const bf16x8 vhf = *(const bf16x8 *)(hf + o), vhb = *(const bf16x8 *)(hb + o);
-        const bf16x8 vgf = *(const bf16x8 *)(gf + o), vgb = *(const bf16x8 *)(gb + o);
+    constexpr int PPR = COLS / 8;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) cross += (float)vhf[j] * (float)vgf[j] + (float)vhb[j] * (float)vgb[j];
-        __bf16 *d = dst + p * ld + s8;
-        *(bf16x8 *)d = vhf;
-        *(bf16x8 *)(d + PM * ld) = vhb;
-        *(bf16x8 *)(d + 2 * PM * ld) = vgf;
-        *(bf16x8 *)(d + 3 * PM * ld) = vgb;
+    for (int j = 0; j < QM * PPR / NTH; ++j) {
+        const int k = threadIdx.x + NTH * j, u = k / PPR, pc = k % PPR;
+        *(u32x4v *)(dst + u * ld + 8 * pc) = s_n[u] == kNoToken ? u32x4v{0, 0, 0, 0} : r[j];
     }
-    return cross;
+}
+
+template <int COLS, int NTH>
+__device__ __forceinline__ void load_rows_tok(__bf16 *dst, int ld, const __bf16 *src, int nh, int hd,
+                                              const uint32_t *s_n, size_t b, uint32_t N)
+{
+    u32x4v r[QM * COLS / 8 / NTH];
+    fetch_rows<COLS, NTH>(r, src, nh, hd, s_n, b, N);
+    store_rows<COLS, NTH>(dst, ld, r, s_n);
+}
+
+// Block -> (chunk c, head h) with all heads of a chunk on one XCD, so that the chunk's B and C rows are
+// fetched into that XCD's L2 once: blocks are handed to the 8 XCDs in turn (block id mod 8), and block
+// id = 8 (nheads grp + h) + k takes chunk 8 grp + k. Returns false for the padding past the last chunk.
+__device__ __forceinline__ bool chunk_head_of(uint32_t nch, int nheads, uint32_t &c, int &h)
+{
+    const uint32_t id = blockIdx.x, q = id >> 3;
+    h = (int)(q % (uint32_t)nheads);
+    c = 8 * (q / (uint32_t)nheads) + (id & 7);
+    return c < nch;
 }
 
 // Sums over the 32 lanes of each half-wave of the 16 values v[e] (one per accumulator row of a 32 x 32
@@ -739,16 +763,17 @@ __device__ __forceinline__ float half_sum16(const float (&v)[16])
     return a1 + __shfl_xor(a1, 1, 64);
 }
 
-// Sum of v over the 256 threads of the block (every thread gets it); red holds NTB / 64 floats.
+// Sum of v over the NTH threads of the block (every thread gets it); red holds NTH / 64 floats.
+template <int NTH>
 __device__ __forceinline__ float block_sum(float v, float *red)
 {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
+    lds_barrier();
     float t = 0.f;
 #pragma unroll
-    for (int k = 0; k < NTB / 64; ++k) t += red[k];
+    for (int k = 0; k < NTH / 64; ++k) t += red[k];
     return t;
 }
 
@@ -756,29 +781,32 @@ __device__ __forceinline__ float block_sum(float v, float *red)
 // Chunk contributions of the states (ADJ false: x, B) or the adjoint states (ADJ true: dy, C) on MFMA:
 // Sf = X^T diag(wf) B, Sb = X^T diag(wb) B (P x S, stored bf16), the weights as in k_chunk_states, applied
 // to the X^T operand in registers. Waves 0-1 make Sf, waves 2-3 Sb, S/32 tiles each.
-// grid (nch, nheads, batch), 256 threads.
+// grid (8 nheads ceil(nch / 8), batch), 256 threads (chunk and head as in chunk_head_of).
 // ---------------------------------------------------------------------------
 template <int S, bool ADJ>
 __global__ __launch_bounds__(NTB) void k_bwd_states_mfma(const __bf16 *__restrict__ x, const __bf16 *__restrict__ Bm,
                                                          const float *__restrict__ dtT, const float *__restrict__ csT,
                                                          const float *__restrict__ A, __bf16 *__restrict__ Sf,
                                                          __bf16 *__restrict__ Sb, int nheads, int G, uint32_t N,
-                                                         uint32_t Lpad, int order, uint32_t T, uint32_t H, uint32_t W)
+                                                         uint32_t Lpad, uint32_t nch, int order, uint32_t T,
+                                                         uint32_t H, uint32_t W)
 {
     constexpr int LS = S + 8, NT = S / 32, TPW = S / 32;
     __shared__ __attribute__((aligned(16))) __bf16 sX[QM * LXM];
     __shared__ __attribute__((aligned(16))) __bf16 sB[QM * LS];
     __shared__ float s_w[2][QM];
     __shared__ uint32_t s_n[QM];
-    const uint32_t c = blockIdx.x, nch = gridDim.x;
-    const int h = blockIdx.y, g = h / (nheads / G);
-    const size_t b = blockIdx.z;
+    uint32_t c;
+    int h;
+    if (!chunk_head_of(nch, nheads, c, h)) return;
+    const int g = h / (nheads / G);
+    const size_t b = blockIdx.y;
     const size_t row = (b * nheads + h) * Lpad + (size_t)c * QM;
     const float a = A[h];
     chunk_tokens(s_n, nullptr, c, N, order, T, H, W, nullptr, 1, 1, 1, 0);
-    __syncthreads();
-    load_rows_tok<PM>(sX, LXM, x, nheads, h, s_n, b, N);
-    load_rows_tok<S>(sB, LS, Bm, G, g, s_n, b, N);
+    lds_barrier();
+    load_rows_tok<PM, NTB>(sX, LXM, x, nheads, h, s_n, b, N);
+    load_rows_tok<S, NTB>(sB, LS, Bm, G, g, s_n, b, N);
     {
         const float tot = csT[row + QM - 1];
         for (int u = threadIdx.x; u < QM; u += NTB) {
@@ -787,7 +815,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_states_mfma(const __bf16 *__restric
             s_w[1][u] = ADJ ? __expf(tot - (cs - d * a)) : d * __expf(cs - d * a);
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int which = wave >> 1;  // 0: Sf, 1: Sb
     __bf16 *out = (which ? Sb : Sf) + ((b * nheads + h) * nch + c) * (size_t)(PM * S);
@@ -877,25 +905,26 @@ __global__ __launch_bounds__(256) void k_state_pass_bf16(__bf16 *__restrict__ Sf
 // dB and dC of one chunk and group on MFMA, the group's heads in turn (sums in accumulators), with each
 // head's rf_t = exp(cs_t) C_t . (Hf^T dy_t), rb_t = exp(tot - ce_t) C_t . (Hb^T dy_t) and its
 // cross term exp(tot) (<Hf, Gf> + <Hb, Gb>) (fp32 sums of the stored bf16 states). Per head: DX = dy x^T and
-// Z = DX o L (to LDS), then for the wave's output tiles (rows: tokens, columns: state)
+// Z = DX o L (to LDS), then for the wave's output tile (rows: tokens, columns: state)
 //   dC[t][s] += (Z B)[t][s] + exp(cs_t) (dy Hf)[t][s] + exp(tot - ce_t) (dy Hb)[t][s],
 //   dB[u][s] += (Z^T C)[u][s] + ef_u (x Gf)[u][s] + eb_u (x Gb)[u][s].
-// grid (nch, G, batch), 256 threads.
+// The next head's operands are fetched into registers while this one computes.
+// grid (nch, G, batch), S / 16 waves (one 32 x 32 tile of dB and of dC each).
 // ---------------------------------------------------------------------------
 template <int S>
-__global__ __launch_bounds__(NTB) void k_bwd_dbdc_mfma(const __bf16 *__restrict__ x, const __bf16 *__restrict__ dy,
-                                                       const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
-                                                       const float *__restrict__ dtT, const float *__restrict__ csT,
-                                                       const float *__restrict__ A, const __bf16 *__restrict__ Hf,
-                                                       const __bf16 *__restrict__ Hb, const __bf16 *__restrict__ Gf,
-                                                       const __bf16 *__restrict__ Gb, const float *__restrict__ drBg,
-                                                       const int *__restrict__ rinv, __bf16 *__restrict__ dB,
-                                                       __bf16 *__restrict__ dC, float *__restrict__ rfo,
-                                                       float *__restrict__ rbo, float *__restrict__ crs, int nheads,
-                                                       int G, uint32_t N, uint32_t Lpad, int order, uint32_t T,
-                                                       uint32_t H, uint32_t W, int pt, int ph, int pw, uint32_t R)
+__global__ __launch_bounds__(4 * S) void k_bwd_dbdc_mfma(const __bf16 *__restrict__ x, const __bf16 *__restrict__ dy,
+                                                         const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
+                                                         const float *__restrict__ dtT, const float *__restrict__ csT,
+                                                         const float *__restrict__ A, const __bf16 *__restrict__ Hf,
+                                                         const __bf16 *__restrict__ Hb, const __bf16 *__restrict__ Gf,
+                                                         const __bf16 *__restrict__ Gb, const float *__restrict__ drBg,
+                                                         const int *__restrict__ rinv, __bf16 *__restrict__ dB,
+                                                         __bf16 *__restrict__ dC, float *__restrict__ rfo,
+                                                         float *__restrict__ rbo, float *__restrict__ crs, int nheads,
+                                                         int G, uint32_t N, uint32_t Lpad, int order, uint32_t T,
+                                                         uint32_t H, uint32_t W, int pt, int ph, int pw, uint32_t R)
 {
-    constexpr int LS = S + 8, NT = S / 32, TPW = 2 * NT / 4;  // output tiles (of 2 NT) per wave
+    constexpr int LS = S + 8, NT = S / 32, NTH = 4 * S;  // 2 NT tiles of 32 x 32, a wave each
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     __bf16 *sB = (__bf16 *)smem_raw;       // [Q][LS]
     __bf16 *sC = sB + QM * LS;             // [Q][LS]
@@ -906,126 +935,161 @@ __global__ __launch_bounds__(NTB) void k_bwd_dbdc_mfma(const __bf16 *__restrict_
     float *tkm = (float *)(sH + 4 * PM * LS);
     const TokLds tk{tkm, tkm + QM, tkm + 2 * QM, tkm + 3 * QM, tkm + 4 * QM};
     float *s_rp = tkm + 5 * QM;            // [2][NT][Q] partial row sums of rf, rb
-    float *s_red = s_rp + 2 * NT * QM;     // [NTB / 64]
+    float *s_red = s_rp + 2 * NT * QM;     // [NTH / 64]
     __shared__ uint32_t s_n[QM], s_rv[QM];
     const uint32_t c = blockIdx.x, nch = gridDim.x;
     const int g = blockIdx.y, hpg = nheads / G;
     const size_t b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int mt = wave / NT, nt = wave % NT;  // this wave's tile: tokens 32 mt + .., state columns 32 nt + ..
     chunk_tokens(s_n, s_rv, c, N, order, T, H, W, rinv, pt, ph, pw, R);
-    __syncthreads();
-    load_rows_tok<S>(sB, LS, Bm, G, g, s_n, b, N);
-    load_rows_tok<S>(sC, LS, Cm, G, g, s_n, b, N);
-    f32x16 accB[TPW], accC[TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) accB[i] = accC[i] = f32x16{};
+    lds_barrier();
+    load_rows_tok<S, NTH>(sB, LS, Bm, G, g, s_n, b, N);
+    load_rows_tok<S, NTH>(sC, LS, Cm, G, g, s_n, b, N);
+    f32x16 accB = f32x16{}, accC = f32x16{};
     const size_t PS = (size_t)PM * S;
+    // A head's operands are fetched into registers (the next head's while this one computes), then staged
+    // in LDS: the four states, the x and dy rows, and the tokens' dt and cumulative sums.
+    constexpr int NPS = PM * S / 8 / NTH, NPX = QM * PM / 8 / NTH;  // 16-byte pieces per thread
+    static_assert(NPS * NTH * 8 == PM * S, "state pieces");
+    bf16x8 rh[4][NPS];
+    u32x4v rx[NPX], ry[NPX];
+    float rdt = 0.f, rcs = 0.f, rtot = 0.f;
+    auto fetch = [&](int h) {
+        const size_t so = ((b * nheads + h) * nch + c) * PS;
+        const __bf16 *src[4] = {Hf + so, Hb + so, Gf + so, Gb + so};
+#pragma unroll
+        for (int j = 0; j < NPS; ++j) {
+            const int k = threadIdx.x + NTH * j, pp = k / (S / 8), s8 = 8 * (k % (S / 8));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rh[q][j] = *(const bf16x8 *)(src[q] + (size_t)pp * S + s8);
+        }
+        fetch_rows<PM, NTH>(rx, x, nheads, h, s_n, b, N);
+        fetch_rows<PM, NTH>(ry, dy, nheads, h, s_n, b, N);
+        const size_t row = (b * nheads + h) * Lpad + (size_t)c * QM;
+        const int u = threadIdx.x & (QM - 1);  // the tokens' values (threads past QM load duplicates)
+        rdt = dtT[row + u];
+        rcs = csT[row + u];
+        rtot = csT[row + QM - 1];
+    };
+    // stores the fetched head into LDS; returns this thread's part of <Hf, Gf> + <Hb, Gb>
+    auto stage = [&](int h) {
+        float cross = 0.f;
+#pragma unroll
+        for (int j = 0; j < NPS; ++j) {
+            const int k = threadIdx.x + NTH * j, pp = k / (S / 8), s8 = 8 * (k % (S / 8));
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                cross += (float)rh[0][j][e] * (float)rh[2][j][e] + (float)rh[1][j][e] * (float)rh[3][j][e];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) *(bf16x8 *)(sH + q * PM * LS + pp * LS + s8) = rh[q][j];
+        }
+        store_rows<PM, NTH>(sX, LXM, rx, s_n);
+        store_rows<PM, NTH>(sY, LXM, ry, s_n);
+        if (threadIdx.x < QM) {
+            const int u = threadIdx.x;
+            const float ce = rcs - rdt * A[h];
+            tk.dt[u] = rdt;
+            tk.cs[u] = rcs;
+            tk.ce[u] = ce;
+            tk.ef[u] = rdt * __expf(rtot - rcs);
+            tk.eb[u] = rdt * __expf(ce);
+        }
+        return cross;
+    };
+    fetch(g * hpg);
+    float cr = stage(g * hpg);
     for (int hk = 0; hk < hpg; ++hk) {
         const int h = g * hpg + hk;
-        const float a = A[h];
         const size_t row = (b * nheads + h) * Lpad + (size_t)c * QM;
-        const size_t so = ((b * nheads + h) * nch + c) * PS;
-        __syncthreads();  // the previous head's reads of the tiles, tokens and partial sums are done
-        load_tokens(tk, dtT, csT, row, QM, a);
-        load_rows_tok<PM>(sX, LXM, x, nheads, h, s_n, b, N);
-        load_rows_tok<PM>(sY, LXM, dy, nheads, h, s_n, b, N);
-        const float cr = load_states_bf16<S>(sH, LS, Hf + so, Hb + so, Gf + so, Gb + so);
-        __syncthreads();
-        {  // DX tile (t, u) of this wave, then Z = DX o L into LDS
-            const int mt = wave >> 1, nt = wave & 1;
+        lds_barrier();  // this head's operands are staged
+        if (hk + 1 < hpg) fetch(h + 1);
+        if (wave < 4) {  // DX tile (t, u) of this wave, then Z = DX o L into LDS
+            const int dm = wave >> 1, dn = wave & 1;
             f32x16 d = f32x16{};
 #pragma unroll
             for (int k0 = 0; k0 < PM; k0 += 16)
-                d = mfma_bf16(frag_rm(sY, LXM, 32 * mt, k0), frag_rm(sX, LXM, 32 * nt, k0), d);
-            const int u = 32 * nt + (lane & 31);
+                d = mfma_bf16(frag_rm(sY, LXM, 32 * dm, k0), frag_rm(sX, LXM, 32 * dn, k0), d);
+            const int u = 32 * dn + (lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int t = 32 * mt + acc_row(e, lane);
-                const float z = d[e] * ldt(tk, t, u);
+                const int t = 32 * dm + acc_row(e, lane);
+                const float z = d[e] * ldt_sel(tk, t, u);
                 const __bf16 hi = (__bf16)z;
                 sZ[t * LXM + u] = hi;
                 sZ[QM * LXM + t * LXM + u] = (__bf16)(z - (float)hi);
             }
         }
-        const float crt = block_sum(cr, s_red);  // also orders the Z stores before the reads below
+        const float crt = block_sum<NTH>(cr, s_red);  // also orders the Z stores before the reads below
         if (threadIdx.x == 0) crs[(b * nheads + h) * nch + c] = __expf(tk.cs[QM - 1]) * crt;
         const float tot = tk.cs[QM - 1];
+#pragma unroll 1
+        for (int k0 = 0; k0 < QM; k0 += 16) {
+            const bf16x8 bb = frag_tr(sB, LS, k0, 32 * nt), cc = frag_tr(sC, LS, k0, 32 * nt);
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int tile = wave * TPW + i, mt = tile / NT, nt = tile % NT;
-#pragma unroll
-            for (int k0 = 0; k0 < QM; k0 += 16) {
-                const bf16x8 bb = frag_tr(sB, LS, k0, 32 * nt), cc = frag_tr(sC, LS, k0, 32 * nt);
-#pragma unroll
-                for (int part = 0; part < 2; ++part) {
-                    const __bf16 *z = sZ + part * QM * LXM;
-                    accC[i] = mfma_bf16(frag_rm(z, LXM, 32 * mt, k0), bb, accC[i]);
-                    accB[i] = mfma_bf16(frag_tr(z, LXM, k0, 32 * mt), cc, accB[i]);
-                }
+            for (int part = 0; part < 2; ++part) {
+                const __bf16 *z = sZ + part * QM * LXM;
+                accC = mfma_bf16(frag_rm(z, LXM, 32 * mt, k0), bb, accC);
+                accB = mfma_bf16(frag_tr(z, LXM, k0, 32 * mt), cc, accB);
             }
-            // the A operand's row (token u of dB) is this lane's: its weights ef_u, eb_u scale the x fragment
-            const float wxf = tk.ef[32 * mt + (lane & 31)], wxb = tk.eb[32 * mt + (lane & 31)];
-            f32x16 hf = f32x16{}, hb = f32x16{};
+        }
+        // The states' terms, one direction at a time (dir 0: Hf, Gf with ef; dir 1: Hb, Gb with eb). The A
+        // operand's row (token u of dB) is this lane's, so its weight scales the x fragment in registers.
+        const int s = 32 * nt + (lane & 31);
 #pragma unroll
+        for (int dir = 0; dir < 2; ++dir) {
+            const float wx = dir ? tk.eb[32 * mt + (lane & 31)] : tk.ef[32 * mt + (lane & 31)];
+            const __bf16 *sHd = sH + dir * PM * LS, *sGd = sH + (2 + dir) * PM * LS;
+            f32x16 hd = f32x16{};
+#pragma unroll 1
             for (int k0 = 0; k0 < PM; k0 += 16) {
                 const bf16x8 ya = frag_rm(sY, LXM, 32 * mt, k0), xa = frag_rm(sX, LXM, 32 * mt, k0);
-                bf16x8 xf, xb;
+                bf16x8 xw;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    xf[j] = (__bf16)(wxf * (float)xa[j]);
-                    xb[j] = (__bf16)(wxb * (float)xa[j]);
-                }
-                hf = mfma_bf16(ya, frag_tr(sH, LS, k0, 32 * nt), hf);
-                hb = mfma_bf16(ya, frag_tr(sH + PM * LS, LS, k0, 32 * nt), hb);
-                accB[i] = mfma_bf16(xf, frag_tr(sH + 2 * PM * LS, LS, k0, 32 * nt), accB[i]);
-                accB[i] = mfma_bf16(xb, frag_tr(sH + 3 * PM * LS, LS, k0, 32 * nt), accB[i]);
+                for (int j = 0; j < 8; ++j) xw[j] = (__bf16)(wx * (float)xa[j]);
+                hd = mfma_bf16(ya, frag_tr(sHd, LS, k0, 32 * nt), hd);
+                accB = mfma_bf16(xw, frag_tr(sGd, LS, k0, 32 * nt), accB);
             }
-            const int s = 32 * nt + (lane & 31);
-            float pf[16], pb[16];
+            float pr[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = 32 * mt + acc_row(e, lane);  // token of this row of dC
-                const float vf = __expf(tk.cs[t]) * hf[e], vb = __expf(tot - tk.ce[t]) * hb[e];
-                accC[i][e] += vf + vb;
-                const float cv = (float)sC[t * LS + s];
-                pf[e] = cv * vf;
-                pb[e] = cv * vb;
+                const float v = (dir ? __expf(tot - tk.ce[t]) : __expf(tk.cs[t])) * hd[e];
+                accC[e] += v;
+                pr[e] = (float)sC[t * LS + s] * v;
             }
-            const float rf = half_sum16(pf), rb = half_sum16(pb);
-            if ((lane & 1) == 0) {
-                const int t = 32 * mt + acc_row((lane & 31) >> 1, lane);
-                s_rp[nt * QM + t] = rf;
-                s_rp[(NT + nt) * QM + t] = rb;
-            }
+            const float r = half_sum16(pr);
+            if ((lane & 1) == 0) s_rp[(dir * NT + nt) * QM + 32 * mt + acc_row((lane & 31) >> 1, lane)] = r;
         }
-        __syncthreads();
-        for (int t = threadIdx.x; t < QM; t += NTB) {
+        lds_barrier();  // this head's reads of the staged operands are done
+        for (int t = threadIdx.x; t < QM; t += NTH) {
             float vf = 0.f, vb = 0.f;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                vf += s_rp[nt * QM + t];
-                vb += s_rp[(NT + nt) * QM + t];
+            for (int k = 0; k < NT; ++k) {
+                vf += s_rp[k * QM + t];
+                vb += s_rp[(NT + k) * QM + t];
             }
             rfo[row + t] = vf;
             rbo[row + t] = vb;
         }
+        if (hk + 1 < hpg) cr = stage(h + 1);
     }
     const float inv_cnt = R > 0 ? 1.f / (float)(pt * ph * pw) : 0.f;
+    const int s = 32 * nt + (lane & 31);
+    float rvB[16];  // the review tokens' shares of this wave's dB tile, loaded together
+    if (R > 0)
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int tile = wave * TPW + i, mt = tile / NT, nt = tile % NT;
-        const int s = 32 * nt + (lane & 31);
+        for (int e = 0; e < 16; ++e) rvB[e] = drBg[((b * R + s_rv[32 * mt + acc_row(e, lane)]) * G + g) * S + s];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int t = 32 * mt + acc_row(e, lane);
-            const uint32_t n = s_n[t];
-            if (n != kNoToken) {
-                const size_t o = ((b * N + n) * G + g) * S + s;
-                float vb = accB[i][e];
-                if (R > 0) vb += drBg[((b * R + s_rv[t]) * G + g) * S + s] * inv_cnt;
-                dB[o] = (__bf16)vb;
-                dC[o] = (__bf16)accC[i][e];
-            }
+    for (int e = 0; e < 16; ++e) {
+        const int t = 32 * mt + acc_row(e, lane);
+        const uint32_t n = s_n[t];
+        if (n != kNoToken) {
+            const size_t o = ((b * N + n) * G + g) * S + s;
+            float vb = accB[e];
+            if (R > 0) vb += rvB[e] * inv_cnt;
+            dB[o] = (__bf16)vb;
+            dC[o] = (__bf16)accC[e];
         }
     }
 }
@@ -1052,7 +1116,8 @@ __device__ __forceinline__ float wave_scan(float v)
 //   span(k) = Sf(k) + sum_{t >= k} rf_t + sum_{u < k} cf_u + Sb(k) + sum_{t <= k} rb_t + sum_{u > k} cb_u
 //             + exp(tot) (<Hf, Gf> + <Hb, Gb>)
 // (Sf, Sb as in k_bwd_ddt; rf, rb and the cross term from the dB/dC kernel) with two wave scans:
-// ddt_k = expl_k + A span(k), and the chunk's parts of dA and dD. grid (nch, nheads, batch), 256 threads.
+// ddt_k = expl_k + A span(k), and the chunk's parts of dA and dD.
+// grid (8 nheads ceil(nch / 8), batch), 256 threads (chunk and head as in chunk_head_of).
 // ---------------------------------------------------------------------------
 template <int S>
 __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ x, const __bf16 *__restrict__ dy,
@@ -1065,8 +1130,8 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
                                                      const float *__restrict__ drdt, const int *__restrict__ rinv,
                                                      __bf16 *__restrict__ dx, float *__restrict__ ddt,
                                                      float *__restrict__ pA, float *__restrict__ pD, int nheads, int G,
-                                                     uint32_t N, uint32_t Lpad, int order, uint32_t T, uint32_t H,
-                                                     uint32_t W, int pt, int ph, int pw, uint32_t R)
+                                                     uint32_t N, uint32_t Lpad, uint32_t nch, int order, uint32_t T,
+                                                     uint32_t H, uint32_t W, int pt, int ph, int pw, uint32_t R)
 {
     constexpr int LS = S + 8;
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -1081,15 +1146,34 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
     float *s_red = tkm + 5 * QM;           // [3][2][Q]: expl, cf, cb partials per p-tile
     float *s_w = s_red + 6 * QM;           // [4][2][Q]: W's column sums below / above, row sums left / right
     float *s_blk = s_w + 8 * QM;           // [NTB / 64]
-    const uint32_t c = blockIdx.x, nch = gridDim.x;
-    const int h = blockIdx.y, g = h / (nheads / G);
-    const size_t b = blockIdx.z;
+    uint32_t c;
+    int h;
+    if (!chunk_head_of(nch, nheads, c, h)) return;
+    const int g = h / (nheads / G);
+    const size_t b = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const size_t row = (b * nheads + h) * Lpad + (size_t)c * QM;
     const size_t PS = (size_t)PM * S, so = ((b * nheads + h) * nch + c) * PS;
     const float a = A[h];
-    // B operands of this wave's dx tile straight from the stored states (rows 32 nt + l % 32 of Gf and Gb),
-    // issued first so that they arrive while the chunk is staged
+    // the dt tail's inputs from the dB/dC kernel, for wave 0 (a lane per token)
+    float rf_k = 0.f, rb_k = 0.f, cr_c = 0.f;
+    if (wave == 0) {
+        rf_k = rfi[row + lane];
+        rb_k = rbi[row + lane];
+        cr_c = crs[(b * nheads + h) * nch + c];
+    }
+    chunk_tokens(s_n, s_rv, c, N, order, T, H, W, rinv, pt, ph, pw, R);
+    load_tokens(tk, dtT, csT, row, QM, a);
+    lds_barrier();
+    // Loads in the order of use (the memory counters retire in order): the chunk's rows, then the B
+    // operands of this wave's dx tile straight from the stored states (rows 32 nt + l % 32 of Gf and Gb),
+    // then the review tokens' shares of the outputs
+    u32x4v rb_rows[QM * S / 8 / NTB], rc_rows[QM * S / 8 / NTB], rx_rows[QM * PM / 8 / NTB],
+        ry_rows[QM * PM / 8 / NTB];
+    fetch_rows<S, NTB>(rb_rows, Bm, G, g, s_n, b, N);
+    fetch_rows<S, NTB>(rc_rows, Cm, G, g, s_n, b, N);
+    fetch_rows<PM, NTB>(rx_rows, x, nheads, h, s_n, b, N);
+    fetch_rows<PM, NTB>(ry_rows, dy, nheads, h, s_n, b, N);
     bf16x8 gfr[S / 16], gbr[S / 16];
     {
         const size_t o = so + (size_t)(32 * (wave & 1) + (lane & 31)) * S + 8 * (lane >> 5);
@@ -1099,14 +1183,19 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
             gbr[k] = *(const bf16x8 *)(Gb + o + 16 * k);
         }
     }
-    chunk_tokens(s_n, s_rv, c, N, order, T, H, W, rinv, pt, ph, pw, R);
-    load_tokens(tk, dtT, csT, row, QM, a);
-    __syncthreads();
-    load_rows_tok<S>(sB, LS, Bm, G, g, s_n, b, N);
-    load_rows_tok<S>(sC, LS, Cm, G, g, s_n, b, N);
-    load_rows_tok<PM>(sX, LXM, x, nheads, h, s_n, b, N);
-    load_rows_tok<PM>(sY, LXM, dy, nheads, h, s_n, b, N);
-    __syncthreads();
+    float rvx[16], rvt = 0.f;
+    if (R > 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            rvx[e] = drx[((b * R + s_rv[32 * (wave >> 1) + acc_row(e, lane)]) * nheads + h) * PM + 32 * (wave & 1) +
+                         (lane & 31)];
+        if (wave == 0) rvt = drdt[(b * R + s_rv[lane]) * nheads + h];
+    }
+    store_rows<S, NTB>(sB, LS, rb_rows, s_n);
+    store_rows<S, NTB>(sC, LS, rc_rows, s_n);
+    store_rows<PM, NTB>(sX, LXM, rx_rows, s_n);
+    store_rows<PM, NTB>(sY, LXM, ry_rows, s_n);
+    lds_barrier();
     float xdy = 0.f;  // x . dy over the chunk (rows past the end hold zeros)
     for (int e = threadIdx.x; e < QM * PM; e += NTB) {
         const int u = e / PM, p = e - u * PM;
@@ -1126,7 +1215,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int t = 32 * mt + acc_row(e, lane);
-            const float m = cb[e] * ldt(tk, t, u);
+            const float m = cb[e] * ldt_sel(tk, t, u);
             const __bf16 hi = (__bf16)m;
             sM[t * LXM + u] = hi;
             sM[QM * LXM + t * LXM + u] = (__bf16)(m - (float)hi);
@@ -1149,7 +1238,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
             s_w[(3 * 2 + nt) * QM + t] = rr;
         }
     }
-    const float dD = block_sum(xdy, s_blk);  // also orders the M stores before the reads below
+    const float dD = block_sum<NTB>(xdy, s_blk);  // also orders the M stores before the reads below
     {  // dx tile (u, p) of this wave
         const int mt = wave >> 1, nt = wave & 1;
         f32x16 in = f32x16{}, af = f32x16{}, ab = f32x16{};
@@ -1181,7 +1270,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
             const uint32_t n = s_n[u];
             if (n != kNoToken) {
                 float v = scan + twoD * (float)sY[u * LXM + p];
-                if (R > 0) v += drx[((b * R + s_rv[u]) * nheads + h) * PM + p] * inv_cnt;
+                if (R > 0) v += rvx[e] * inv_cnt;
                 dx[((b * N + n) * nheads + h) * PM + p] = (__bf16)v;
             }
         }
@@ -1193,25 +1282,24 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
             s_red[(2 * 2 + nt) * QM + u] = rb;
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {  // lane k: token k of the chunk
         const int k = lane;
         const float expl = s_red[k] + s_red[QM + k];
         const float cf = s_red[2 * QM + k] + s_red[3 * QM + k], cbk = s_red[4 * QM + k] + s_red[5 * QM + k];
         const float dj_f = (s_w[k] + s_w[QM + k]) - (s_w[4 * QM + k] + s_w[5 * QM + k]);
         const float dj_b = (s_w[6 * QM + k] + s_w[7 * QM + k]) - (s_w[2 * QM + k] + s_w[3 * QM + k]);
-        const float rf = rfi[row + k], rb = rbi[row + k];
         // Sf + cf_lt: exclusive prefix of dj_f + cf; Sb + rb_le: inclusive prefix of dj_b + rb;
         // rf_ge: inclusive suffix of rf; cb_gt: exclusive suffix of cb
         const float fa = dj_f + cf;
-        const float pre = wave_scan<false>(fa + dj_b + rb) - fa;
-        const float suf = wave_scan<true>(rf + cbk) - cbk;
-        const float span = pre + suf + crs[(b * nheads + h) * nch + c];
+        const float pre = wave_scan<false>(fa + dj_b + rb_k) - fa;
+        const float suf = wave_scan<true>(rf_k + cbk) - cbk;
+        const float span = pre + suf + cr_c;
         const uint32_t n = s_n[k];
         float dA = 0.f;
         if (n != kNoToken) {
             float v = expl + a * span;
-            if (R > 0) v += drdt[(b * R + s_rv[k]) * nheads + h] / (float)(pt * ph * pw);
+            if (R > 0) v += rvt / (float)(pt * ph * pw);
             ddt[(b * N + n) * nheads + h] = v;
             dA = tk.dt[k] * span;
         }
@@ -1228,7 +1316,7 @@ template <int S>
 constexpr size_t dbdc_mfma_lds()
 {
     return (size_t)2 * QM * (S + 8) * 2 + 4 * QM * LXM * 2 + 4 * PM * (S + 8) * 2 +
-           (5 * QM + 2 * (S / 32) * QM + NTB / 64) * 4;
+           (5 * QM + 2 * (S / 32) * QM + 4 * S / 64) * 4;
 }
 template <int S>
 constexpr size_t dx_mfma_lds()
@@ -1336,10 +1424,13 @@ hipError_t run_chunks_mfma(const SsdProblem &p, const SsdGradArgs &a, const BwdL
     const uint32_t T = (uint32_t)p.T, H = (uint32_t)p.H, W = (uint32_t)p.W;
     const __bf16 *x = (const __bf16 *)a.x, *Bm = (const __bf16 *)a.b, *Cm = (const __bf16 *)a.c;
     const __bf16 *dy = (const __bf16 *)a.dy;
-    const dim3 gh(l.nch, Hs, B), gg(l.nch, G, B), gp((PM * S / 8 + 255) / 256, 2 * Hs, B);
-    k_bwd_states_mfma<S, false><<<gh, NTB, 0, st>>>(x, Bm, dtT, csT, a.a, Sf, Sb, Hs, G, N, Lpad, p.order, T, H, W);
+    const uint32_t nch = (uint32_t)l.nch;
+    const dim3 gh(8 * Hs * ((nch + 7) / 8), B), gg(nch, G, B), gp((PM * S / 8 + 255) / 256, 2 * Hs, B);
+    k_bwd_states_mfma<S, false><<<gh, NTB, 0, st>>>(x, Bm, dtT, csT, a.a, Sf, Sb, Hs, G, N, Lpad, nch, p.order, T, H,
+                                                    W);
     k_state_pass_bf16<<<gp, 256, 0, st>>>(Sf, Sb, csT, h0f, h0b, nullptr, nullptr, PM * S, l.nch, Lpad);
-    k_bwd_states_mfma<S, true><<<gh, NTB, 0, st>>>(dy, Cm, dtT, csT, a.a, Uf, Ub, Hs, G, N, Lpad, p.order, T, H, W);
+    k_bwd_states_mfma<S, true><<<gh, NTB, 0, st>>>(dy, Cm, dtT, csT, a.a, Uf, Ub, Hs, G, N, Lpad, nch, p.order, T, H,
+                                                   W);
     k_state_pass_bf16<<<gp, 256, 0, st>>>(Ub, Uf, csT, nullptr, nullptr, Gb0, Gf0, PM * S, l.nch, Lpad);
     if (R > 0) {
         k_review_grads<<<B * Hs, NTB, review_lds(p), st>>>(F(l.rx), F(l.rB), F(l.rdt), a.a, Gf0, Gb0,
@@ -1347,12 +1438,12 @@ hipError_t run_chunks_mfma(const SsdProblem &p, const SsdGradArgs &a, const BwdL
                                                            PM, S, G, (int)R);
         k_review_group<<<dim3(R, B), 256, 0, st>>>(F(l.drB), (float *)drBg, Hs, S, G);
     }
-    k_bwd_dbdc_mfma<S><<<gg, NTB, dbdc_mfma_lds<S>(), st>>>(
+    k_bwd_dbdc_mfma<S><<<gg, 4 * S, dbdc_mfma_lds<S>(), st>>>(
         x, dy, Bm, Cm, dtT, csT, a.a, Sf, Sb, Uf, Ub, drBg, rinv, (__bf16 *)a.db, (__bf16 *)a.dc, rf, rb, crs, Hs, G,
         N, Lpad, p.order, T, H, W, p.pool_t, p.pool_h, p.pool_w, R);
     k_bwd_dx_mfma<S><<<gh, NTB, dx_mfma_lds<S>(), st>>>(x, dy, Bm, Cm, dtT, csT, a.a, a.d, Uf, Ub, rf, rb, crs, drx,
                                                         drdt, rinv, (__bf16 *)a.dx, a.ddt, pA, pD, Hs, G, N, Lpad,
-                                                        p.order, T, H, W, p.pool_t, p.pool_h, p.pool_w, R);
+                                                        nch, p.order, T, H, W, p.pool_t, p.pool_h, p.pool_w, R);
     k_bwd_reduce<<<(Hs + 255) / 256, 256, 0, st>>>(pA, pD, pAr, a.da, a.dd, Hs, l.nch, B);
     return hipGetLastError();
 }
