@@ -377,54 +377,47 @@ def backward_bench(torch, np, B, wl, att, ssd, ws_fwd, reps):
 
 
 def block_bench(torch, np, B, wl, reps):
-    """One LinGen-4B layer's token mixing with its projections, to place the MATE core in it. Widths from
-    the xllm-io review's model table (embedding 2560, 20 heads) and the core's own (MA: 80 heads x 64 =
-    2 x 2560, d_state 128; TE: 20 x 128). The projections are plain library GEMMs (torch matmul, i.e.
-    hipBLASLt / rocBLAS): MA in 2560 -> x 5120, B and C 2 x 128, dt 80 (softplus); MA out 5120 -> 2560;
-    TE in 2560 -> q, k, v 3 x 2560; TE out 2560 -> 2560; the two branch outputs are summed. The Mamba2
-    block's conv1d, gating and norm are not on the pages and are left out. Prints one JSON line."""
+    """LinGen-4B layers through the library's mate_layer (projections on hipBLASLt, the MATE core, the MA
+    branch's gate and norm, the MA+TE sum). Widths from the xllm-io review's model table (2560-wide rows,
+    20 heads) and the core's own (MA: 80 heads x 64 = 2 x 2560, d_state 128; TE: 20 x 128). Times one layer
+    per (order, shift) of the schedule, a real 32-layer stack (order l mod 4, shift on odd l; random weights
+    per layer, the output of one layer the input of the next), and, for a Table 2-style split, the MA and TE
+    branches' core calls on the same grid. Prints one JSON line."""
     stream = torch.cuda.current_stream()
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(13)
     N, d = wl.N * wl.batch, 2560
     Hs, P, S, th, td = wl.nheads, wl.headdim, wl.d_state, wl.t_heads, wl.t_dim
     bf = torch.bfloat16
-    w = lambda i, o: (torch.randn(i, o, device=dev, generator=g) / np.sqrt(i)).to(bf)
-    h = torch.randn(N, d, device=dev, generator=g).to(bf)
-    W = {"x": w(d, Hs * P), "bc": w(d, 2 * S), "dt": w(d, Hs), "ma_out": w(Hs * P, d),
-         "q": w(d, th * td), "k": w(d, th * td), "v": w(d, th * td), "te_out": w(th * td, d)}
-    A = -torch.exp(torch.rand(Hs, device=dev, generator=g) * 2)
-    Dp = torch.randn(Hs, device=dev, generator=g)
-    shape_ssd = (wl.batch, wl.T, wl.H, wl.W)
-    y = torch.empty(*shape_ssd, Hs, P, device=dev, dtype=bf)
-    o = torch.empty(*shape_ssd, th, td, device=dev, dtype=bf)
-    sdesc = B.ssd_desc(y, torch.empty(*shape_ssd, 1, S, device=dev, dtype=bf), wl.chunk, wl.pool)
-    ws = torch.empty(B.mate_forward_workspace_size(wl.grid, sdesc, B.tesa_desc(o, wl.window)), dtype=torch.uint8,
-                     device=dev)
-    t = {}
+    grid = wl.grid
+    nlayers = 32
 
-    def proj_in():
-        t["x"] = (h @ W["x"]).view(*shape_ssd, Hs, P)
-        bc = h @ W["bc"]
-        t["b"] = bc[:, :S].contiguous().view(*shape_ssd, 1, S)
-        t["c"] = bc[:, S:].contiguous().view(*shape_ssd, 1, S)
-        t["dt"] = torch.nn.functional.softplus((h @ W["dt"]).float()).view(*shape_ssd, Hs)
-        for n in ("q", "k", "v"):
-            t[n] = (h @ W[n]).view(*shape_ssd, th, td)
+    def weights():
+        m = lambda i, o: (torch.randn(i, o, device=dev, generator=g) / np.sqrt(i)).to(bf)
+        return {"w_x": m(d, Hs * P), "w_z": m(d, Hs * P), "w_b": m(d, S), "w_c": m(d, S),
+                "w_dt": (m(d, Hs).float() * 0.3).to(bf), "w_ma_out": m(Hs * P, d),
+                "dt_bias": torch.randn(Hs, device=dev, generator=g) * 0.5 - 1.0,
+                "a": -torch.exp(torch.rand(Hs, device=dev, generator=g) * 2),
+                "d": torch.randn(Hs, device=dev, generator=g),
+                "norm_w": 1 + 0.1 * torch.randn(Hs * P, device=dev, generator=g),
+                "w_q": m(d, th * td), "w_k": m(d, th * td), "w_v": m(d, th * td), "w_te_out": m(th * td, d)}
 
-    def core(order, shifted):
-        B.mate_forward({"x": t["x"], "b": t["b"], "c": t["c"], "dt": t["dt"], "a": A, "d": Dp, "y": y},
-                       {"q": t["q"], "k": t["k"], "v": t["v"], "o": o}, order, wl.chunk, wl.pool, wl.window,
-                       wl.layer_shift(shifted), workspace=ws)
+    log("block: weights of 32 layers")
+    layers = [weights() for _ in range(nlayers)]
+    ssd = dict(nheads=Hs, headdim=P, d_state=S, ngroups=1, chunk=wl.chunk, pool=wl.pool)
+    te = lambda shifted: dict(nheads=th, headdim=td, window=wl.window, shift=wl.layer_shift(shifted))
+    ld, sd, tdesc = B.layer_descs(grid, d, ssd, te(False))
+    ws = torch.empty(B.mate_layer_workspace_size(grid, ld, sd, tdesc), dtype=torch.uint8, device=dev)
+    h = [torch.randn(*grid, d, device=dev, generator=g).to(bf), torch.empty(*grid, d, device=dev, dtype=bf)]
 
-    def proj_out():
-        t["out"] = y.view(N, Hs * P) @ W["ma_out"] + o.view(N, th * td) @ W["te_out"]
+    def layer(i, src, dst):
+        B.mate_layer(src, dst, layers[i], d, ssd, te(i % 2 == 1), i % 4, workspace=ws)
 
-    def timed(fn):
+    def timed(fn, n=None):
         fn()
         torch.cuda.synchronize()
         ts = []
-        for _ in range(max(3, reps)):
+        for _ in range(n or max(3, reps)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fn()
@@ -433,21 +426,39 @@ def block_bench(torch, np, B, wl, reps):
             ts.append(e0.elapsed_time(e1))
         return float(np.median(ts))
 
-    log("block: projections and core")
-    t_in, t_out = timed(proj_in), timed(proj_out)
-    t_core = [timed(lambda o_=o_, s_=s_: core(o_, s_)) for o_, s_ in wl.schedule]
-    t_layer = [timed(lambda o_=o_, s_=s_: (proj_in(), core(o_, s_), proj_out())) for o_, s_ in wl.schedule]
-    gemm_flops = 2.0 * N * d * (Hs * P + 2 * S + Hs + 3 * th * td) + 2.0 * N * d * (Hs * P + th * td)
+    log("block: one layer per schedule entry")
+    t_layer = [timed(lambda i=i: layer(i, h[0], h[1])) for i in range(4)]
+
+    def stack():
+        for i in range(nlayers):
+            layer(i, h[i % 2], h[(i + 1) % 2])
+
+    log("block: 32-layer stack")
+    t_stack = timed(stack, 3)
+    ok = bool(torch.isfinite(h[0].float()).all().item())
+    # the two branches' core calls alone, on tensors of the layer's shapes
+    x = torch.randn(*grid, Hs, P, device=dev, generator=g).to(bf)
+    bc = torch.randn(*grid, 1, S, device=dev, generator=g).to(bf)
+    dt = torch.nn.functional.softplus(torch.randn(*grid, Hs, device=dev, generator=g) - 1.0)
+    y = torch.empty_like(x)
+    q = torch.randn(*grid, th, td, device=dev, generator=g).to(bf)
+    o = torch.empty_like(q)
+    swsp = torch.empty(B.mate_bissd_workspace_size(grid, B.ssd_desc(x, bc, wl.chunk, wl.pool)), dtype=torch.uint8,
+                       device=dev)
+    t_ma = [timed(lambda o_=o_: B.mate_bissd_scan(x, bc, bc, dt, layers[0]["a"], layers[0]["d"], y, o_, wl.chunk,
+                                                  wl.pool, workspace=swsp)) for o_ in range(4)]
+    t_te = [timed(lambda s_=s_: B.mate_tesa(q, q, q, o, wl.window, wl.layer_shift(s_))) for s_ in (False, True)]
+    gemm_flops = 2.0 * N * d * (2 * Hs * P + 2 * S + Hs + 3 * th * td) + 2.0 * N * d * (Hs * P + th * td)
     mean = lambda xs: float(np.mean(xs))
-    print(json.dumps({"metric": "one LinGen-4B layer's token mixing with its projections (one MI355X)", "unit": "ms",
-                      "data": "synthetic",
+    print(json.dumps({"metric": "LinGen-4B MATE layers through mate_layer (one MI355X)", "unit": "ms",
+                      "data": "synthetic, random weights",
                       "config": {"workload": wl.name, "tokens": N, "embedding": d, "ma": [Hs, P, S], "te": [th, td],
-                                 "layers_of_model": 32},
-                      "projections_in_ms": t_in, "projections_out_ms": t_out,
-                      "projection_tflops": gemm_flops / (t_in + t_out) / 1e9,
-                      "core_ms": mean(t_core), "layer_ms": mean(t_layer), "per_layer_ms": t_layer,
-                      "core_share": mean(t_core) / mean(t_layer),
-                      "model_token_mixing_s": 32 * mean(t_layer) / 1e3}), flush=True)
+                                 "layers": nlayers},
+                      "layer_ms_per_schedule_entry": t_layer, "layer_ms": mean(t_layer),
+                      "stack_32_layers_ms": t_stack, "stack_output_finite": ok,
+                      "ma_core_ms": mean(t_ma), "te_core_ms": mean(t_te),
+                      "ma_share_of_core": mean(t_ma) / (mean(t_ma) + mean(t_te)),
+                      "projection_gemm_tflop_per_layer": gemm_flops / 1e12}), flush=True)
 
 
 def cpu_model():
@@ -480,7 +491,8 @@ def main():
     ap.add_argument("--scaling", action="store_true",
                     help="instead of the throughput line: MATE core vs full attention per layer as T grows")
     ap.add_argument("--block", action="store_true",
-                    help="instead of the throughput line: one layer's token mixing with its projections (library GEMMs)")
+                    help="instead of the throughput line: LinGen-4B layers through mate_layer (one layer per schedule "
+                         "entry and a 32-layer stack)")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the throughput line: the backward passes (TESA, the scan) beside their "
                          "forwards, per layer")

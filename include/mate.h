@@ -10,15 +10,16 @@
  *     (SSD) scan over the sequence and its flip;
  *   - the TE branch: TESA, attention inside 3D windows Tw x Sw x Sw whose
  *     partition shifts on alternate layers.
- * This library computes that token-mixing core. The projections around it are
- * not part of it.
+ * This library computes that token-mixing core, and (mate_layer) one whole
+ * MATE layer with the projections around it.
  *
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA storage).
  *     The caller owns every buffer; the library never allocates or frees
- *     device memory and creates no streams (the HIP events of the timing
- *     diagnostics below aside). The one device memory it holds is the fixed
- *     scratch array of mate_bissd_scan_noalloc, loaded with the library.
+ *     device memory for them and creates no streams (the HIP events of the
+ *     timing diagnostics below aside). The device memory it holds is the fixed
+ *     scratch array of mate_bissd_scan_noalloc, loaded with the library, and
+ *     what hipBLASLt keeps for the handle mate_layer creates on first use.
  *   - Token tensors are channels-last: [batch][T][H][W][...], so the canonical
  *     token index is n = (t*H + h)*W + w and a token's channels are contiguous.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
@@ -325,6 +326,66 @@ size_t mate_forward_workspace_size(mate_grid g, const mate_ssd_desc *sd, const m
 mate_status mate_forward(const mate_ssd_tensors *s, const mate_ssd_desc *sd, const mate_tesa_tensors *a,
                          const mate_tesa_desc *td, mate_grid g, int order, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* One MATE layer                                                            */
+/* ------------------------------------------------------------------------ */
+/* A whole MATE block in place of a DiT layer's self-attention: the MA and TE
+ * branches with their projections, summed (QbitAI article on LinGen, section
+ * "方法": MATE, made of the MA and TE branches, replaces self-attention and the
+ * rest of the DiT stays as it is; the xllm-io review, section 5.1 and its model
+ * table, for the LinGen-4B widths: 2560-wide rows, 20 attention heads, and
+ * Table 2 for the two branches' shares of a layer's time). For token rows h:
+ *   MA:  x = h Wx, z = h Wz, B = h Wb, C = h Wc, dt = softplus(h Wdt + dt_bias),
+ *        y = mate_bissd_scan(x, B, C, dt, A, D) in RMS order `order`,
+ *        g = y * silu(z), normalised per group of nheads*headdim/ngroups
+ *            channels: g / sqrt(mean(g^2) + eps) * norm_w,
+ *   TE:  q = h Wq, k = h Wk, v = h Wv, o = mate_tesa(q, k, v),
+ *   out = g Wma_out + o Wte_out.
+ * The pages give neither the projections nor the MA branch's per-token steps.
+ * They follow the Mamba2 block that the MA branch is built from: dt through a
+ * bias and softplus, a gate silu(z), and an RMS norm after the gate before the
+ * out-projection. Mamba2's short causal convolution is left out: it mixes
+ * neighbouring tokens along the scan, so it is not a per-token step, and the
+ * pages say nothing about it.
+ * Precision: the GEMMs take bf16 operands with fp32 accumulation (hipBLASLt);
+ * x, z, B, C, q, k, v, y, o and g are rounded to bf16 between the steps, dt
+ * and the norm's sums stay fp32, out is bf16.
+ *
+ * Layouts: h, out [batch][T][H][W][d_model] bf16 (16-byte aligned, not
+ *          overlapping). Weights are row-major [in][out] bf16:
+ *   w_x, w_z [d_model][nheads*headdim]   w_b, w_c [d_model][ngroups*d_state]
+ *   w_dt [d_model][nheads]               w_ma_out [nheads*headdim][d_model]
+ *   w_q, w_k, w_v [d_model][tesa nheads*headdim]
+ *   w_te_out [tesa nheads*headdim][d_model]
+ *   dt_bias, a, d [nheads] fp32;  norm_w [nheads*headdim] fp32.
+ * sd and td describe the two branches as for mate_bissd_scan and mate_tesa
+ * (both dtype bf16; td's shift is the layer's); their tensors live in the
+ * workspace. */
+typedef struct {
+    const void *w_x, *w_z, *w_b, *w_c, *w_dt, *w_ma_out;
+    const float *dt_bias, *a, *d, *norm_w;
+    const void *w_q, *w_k, *w_v, *w_te_out;
+} mate_layer_weights;
+
+typedef struct {
+    int32_t d_model; /* width of the rows of h and out, a multiple of 8 */
+    float norm_eps;  /* eps of the gated RMS norm, >= 0 */
+} mate_layer_desc;
+
+/* Bytes of workspace mate_layer needs: the intermediates of both branches,
+ * the scan's workspace and 64 MiB for the GEMMs (0 on invalid arguments). */
+size_t mate_layer_workspace_size(mate_grid g, const mate_layer_desc *ld, const mate_ssd_desc *sd,
+                                 const mate_tesa_desc *td);
+
+/* Supported: what mate_bissd_scan and mate_tesa support in bf16, with
+ * nheads*headdim/ngroups a multiple of 8 and ngroups <= 64. The first call on
+ * a device creates the library's hipBLASLt handle for it, and each new GEMM
+ * shape its hipBLASLt descriptors (kept for the process). Errors: as the two
+ * calls; MATE_ERR_DEVICE also when hipBLASLt has no algorithm for a shape. */
+mate_status mate_layer(const void *h, void *out, const mate_layer_weights *w, const mate_layer_desc *ld,
+                       const mate_ssd_desc *sd, const mate_tesa_desc *td, mate_grid g, int order, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */

@@ -24,7 +24,7 @@ EXPORTED = (
     "mate_forward_workspace_size", "mate_forward", "mate_status_string", "mate_last_error",
     "mate_abi_version", "mate_timing_begin", "mate_timing_end", "mate_bimamba_workspace_size",
     "mate_bimamba_scan", "mate_tesa_backward_workspace_size", "mate_tesa_backward", "mate_bissd_scan_noalloc",
-    "mate_bissd_backward_workspace_size", "mate_bissd_backward",
+    "mate_bissd_backward_workspace_size", "mate_bissd_backward", "mate_layer_workspace_size", "mate_layer",
 )
 STATIC_SCRATCH_BYTES = 64 << 20  # MATE_STATIC_SCRATCH_BYTES
 
@@ -73,6 +73,18 @@ class TesaTensors(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("o", ctypes.c_void_p)]
 
 
+LAYER_WEIGHTS = ("w_x", "w_z", "w_b", "w_c", "w_dt", "w_ma_out", "dt_bias", "a", "d", "norm_w", "w_q", "w_k", "w_v",
+                 "w_te_out")
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHTS]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
+
+
 class TesaGradTensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "dout", "dq", "dk", "dv")]
 
@@ -108,8 +120,13 @@ def lib() -> ctypes.CDLL:
     L.mate_forward_workspace_size.restype = SZ
     L.mate_forward.argtypes = [ctypes.POINTER(SsdTensors), ctypes.POINTER(SsdDesc), ctypes.POINTER(TesaTensors),
                                ctypes.POINTER(TesaDesc), Grid, I32, P, SZ, P]
+    L.mate_layer_workspace_size.argtypes = [Grid, ctypes.POINTER(LayerDesc), ctypes.POINTER(SsdDesc),
+                                            ctypes.POINTER(TesaDesc)]
+    L.mate_layer_workspace_size.restype = SZ
+    L.mate_layer.argtypes = [P, P, ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerDesc), ctypes.POINTER(SsdDesc),
+                             ctypes.POINTER(TesaDesc), Grid, I32, P, SZ, P]
     for f in ("mate_rms_reorder", "mate_bissd_scan", "mate_bissd_scan_noalloc", "mate_bissd_backward",
-              "mate_bimamba_scan", "mate_tesa", "mate_tesa_backward", "mate_forward"):
+              "mate_bimamba_scan", "mate_tesa", "mate_tesa_backward", "mate_forward", "mate_layer"):
         getattr(L, f).restype = ctypes.c_int
     L.mate_status_string.argtypes = [ctypes.c_int]
     L.mate_status_string.restype = ctypes.c_char_p
@@ -399,6 +416,59 @@ def mate_forward(ssd: dict, tesa: dict, order: int, chunk: int, pool, window, sh
     tt = TesaTensors(*(_ptr(tesa[k]) for k in ("q", "k", "v", "o")))
     _check(lib().mate_forward(ctypes.byref(st), ctypes.byref(sdesc), ctypes.byref(tt), ctypes.byref(tdesc),
                               Grid(*grid), order, _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# One MATE layer
+# ---------------------------------------------------------------------------
+
+def layer_descs(grid, d_model: int, ssd: dict, tesa: dict, norm_eps: float = 1e-5):
+    """(LayerDesc, SsdDesc, TesaDesc) of a bf16 layer. ssd: nheads, headdim, d_state, ngroups, chunk, pool;
+    tesa: nheads, headdim, window, shift (and optional scale)."""
+    ld = LayerDesc(d_model, norm_eps)
+    pool = ssd.get("pool", (0, 0, 0))
+    sd = SsdDesc(ssd["nheads"], ssd["headdim"], ssd["d_state"], ssd.get("ngroups", 1), ssd["chunk"], pool[0],
+                 pool[1], pool[2], MATE_BF16, ALGO_AUTO)
+    win, sh = tesa["window"], tesa.get("shift", (0, 0, 0))
+    td = TesaDesc(tesa["nheads"], tesa["headdim"], win[0], win[1], win[2], sh[0], sh[1], sh[2],
+                  tesa.get("scale", 0.0), MATE_BF16, ALGO_AUTO)
+    return ld, sd, td
+
+
+def mate_layer_workspace_size(grid, ld: LayerDesc, sd: SsdDesc, td: TesaDesc) -> int:
+    return int(lib().mate_layer_workspace_size(Grid(*grid), ctypes.byref(ld), ctypes.byref(sd), ctypes.byref(td)))
+
+
+def _check_layer(h, out, w: dict, ld: LayerDesc, sd: SsdDesc, td: TesaDesc):
+    import torch
+    dm, inner, bc = ld.d_model, sd.nheads * sd.headdim, sd.ngroups * sd.d_state
+    tin = td.nheads * td.headdim
+    _need(h.dim() == 5 and h.shape[-1] == dm, f"h must be [batch][T][H][W][{dm}], got {tuple(h.shape)}")
+    _shape(out, h.shape, "out")
+    shapes = {"w_x": (dm, inner), "w_z": (dm, inner), "w_b": (dm, bc), "w_c": (dm, bc), "w_dt": (dm, sd.nheads),
+              "w_ma_out": (inner, dm), "dt_bias": (sd.nheads,), "a": (sd.nheads,), "d": (sd.nheads,),
+              "norm_w": (inner,), "w_q": (dm, tin), "w_k": (dm, tin), "w_v": (dm, tin), "w_te_out": (tin, dm)}
+    for n, shp in shapes.items():
+        _shape(w[n], shp, n)
+        want = torch.float32 if n in ("dt_bias", "a", "d", "norm_w") else torch.bfloat16
+        _need(w[n].dtype == want, f"{n} must be {want}, got {w[n].dtype}")
+    _need(h.dtype == torch.bfloat16 and out.dtype == torch.bfloat16, "h and out must be bfloat16")
+    _dev(h, out, *w.values())
+
+
+def mate_layer(h, out, weights: dict, d_model: int, ssd: dict, tesa: dict, order: int, norm_eps: float = 1e-5,
+               workspace=None, stream=None):
+    """One MATE layer: out = MA(h) + TE(h) with their projections (see include/mate.h). weights holds the
+    LAYER_WEIGHTS tensors; ssd and tesa the branch sizes as for layer_descs."""
+    grid = tuple(h.shape[:4])
+    ld, sd, td = layer_descs(grid, d_model, ssd, tesa, norm_eps)
+    _check_layer(h, out, weights, ld, sd, td)
+    if workspace is None:
+        workspace = _workspace(mate_layer_workspace_size(grid, ld, sd, td), h)
+    w = LayerWeights(*(_ptr(weights[n]) for n in LAYER_WEIGHTS))
+    _check(lib().mate_layer(_ptr(h), _ptr(out), ctypes.byref(w), ctypes.byref(ld), ctypes.byref(sd),
+                            ctypes.byref(td), Grid(*grid), order, _ptr(workspace), _nbytes(workspace),
+                            _stream(stream)))
 
 
 def mate_timing_begin(kernel: str):

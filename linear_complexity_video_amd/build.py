@@ -1,7 +1,8 @@
 """Builds the HIP library ``libmate.so`` for gfx950 in-tree with hipcc.
 
-Every ``csrc/*.hip`` file and ``csrc/mate_api.cpp`` is compiled to an object
-under ``_build/`` (in parallel) and linked into
+Every ``csrc/*.hip`` file and the host sources (``mate_api.cpp``,
+``timing.cpp``, ``layer.cpp``) are compiled to objects under ``_build/`` (in
+parallel) and linked, with hipBLASLt, into
 ``linear_complexity_video_amd/libmate.so``.
 """
 from __future__ import annotations
@@ -28,7 +29,7 @@ DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "mate_api.cpp"), os.path.join(CSRC, "timing.cpp")]
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, n) for n in ("mate_api.cpp", "timing.cpp", "layer.cpp")]
 
 
 def _compile(src: str) -> str:
@@ -49,7 +50,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lhipblaslt",
+           "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

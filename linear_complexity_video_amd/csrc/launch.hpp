@@ -100,4 +100,32 @@ bool tesa_backward_supports(const TesaProblem &p);
 size_t tesa_backward_workspace(const TesaProblem &p);
 hipError_t tesa_backward(const TesaProblem &p, const TesaGradArgs &a, void *ws, hipStream_t st);
 
+// One MATE layer around the core (layer.cpp, layer_ops.hip).
+struct LayerDims {
+    int64_t tokens;  // batch * T * H * W
+    int d_model;
+    int inner;       // nheads * headdim (x, z, y)
+    int bc;          // ngroups * d_state (b, c)
+    int nheads;
+    int t_inner;     // TESA heads * head size (q, k, v, o)
+};
+
+// Byte offsets of the layer's intermediates inside its workspace (256-byte aligned).
+struct LayerLayout {
+    size_t x, z, b, c, dt, q, k, v, y, o, core, blas, total;
+};
+
+constexpr size_t kGemmWorkspace = (size_t)64 << 20;  // reserved for hipBLASLt inside the layer's workspace
+
+LayerLayout layer_layout(const LayerDims &d, size_t core_ws);
+
+// Row-major D[M][Nout] = A[M][K] W[K][Nout] (+ D when accumulate) on hipBLASLt: bf16 A and W, fp32
+// accumulation, D fp32 (d_f32) or bf16. Returns 0, or 1 with a message in msg.
+int gemm_rowmajor(const void *A, const void *W, void *D, int64_t M, int64_t K, int64_t Nout, bool d_f32,
+                  bool accumulate, void *ws, size_t ws_bytes, hipStream_t st, char *msg, size_t msg_len);
+
+hipError_t layer_softplus_bias(float *dt, const float *bias, int64_t tokens, int nheads, hipStream_t st);
+hipError_t layer_gated_norm(const void *y, void *z, const float *w, int64_t tokens, int channels, int groups,
+                            float eps, hipStream_t st);
+
 } // namespace mate

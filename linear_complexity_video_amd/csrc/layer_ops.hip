@@ -1,0 +1,107 @@
+// Per-token operations of one MATE layer around the core: dt from its
+// projection (bias, then softplus) and the MA branch's gated RMS norm. The
+// pages give neither; both follow the Mamba2 block the MA branch is built from
+// (softplus keeps dt positive; the output is normalised after gating with
+// silu(z)).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mate {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// dt[n][h] = softplus(raw[n][h] + bias[h]), in place, fp32. softplus(v) = max(v, 0) + log1p(exp(-|v|)).
+__global__ __launch_bounds__(256) void k_softplus_bias(float *__restrict__ dt, const float *__restrict__ bias,
+                                                       int64_t total, int nheads)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const float v = dt[i] + bias[i % nheads];
+    dt[i] = fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v)));
+}
+
+// Eight bf16 values of a 16-byte piece as floats.
+__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8])
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(v[j] << 16);
+        f[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+
+constexpr int NT_NORM = 128;
+
+// One token row per block: g = y * silu(z) over the row's C channels, then per group of gs channels
+// out = g / sqrt(mean(g^2) + eps) * w, written over z (bf16). Two passes over the row: the group sums,
+// then the normalised values. gs is a multiple of 8, so no 16-byte piece straddles two groups.
+__global__ __launch_bounds__(NT_NORM) void k_gated_norm(const bf16_t *__restrict__ y, bf16_t *__restrict__ z,
+                                                        const float *__restrict__ w, int C, int G, float eps)
+{
+    __shared__ float s_part[NT_NORM / 64];
+    __shared__ float s_rs[64];  // reciprocal rms per group (G <= 64)
+    const size_t row = blockIdx.x;
+    const u32x4 *yr = (const u32x4 *)(y + row * C);
+    u32x4 *zr = (u32x4 *)(z + row * C);
+    const int npc = C / 8, gpc = npc / G;  // pieces per row and per group
+    for (int gi = 0; gi < G; ++gi) {
+        float acc = 0.f;
+        for (int k = gi * gpc + threadIdx.x; k < (gi + 1) * gpc; k += NT_NORM) {
+            float fy[8], fz[8];
+            unpack8(yr[k], fy);
+            unpack8(zr[k], fz);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float gv = fy[j] * silu(fz[j]);
+                acc += gv * gv;
+            }
+        }
+        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float t = 0.f;
+            for (int k = 0; k < NT_NORM / 64; ++k) t += s_part[k];
+            s_rs[gi] = rsqrtf(t / (float)(gpc * 8) + eps);
+        }
+        __syncthreads();
+    }
+    for (int k = threadIdx.x; k < npc; k += NT_NORM) {
+        float fy[8], fz[8];
+        unpack8(yr[k], fy);
+        unpack8(zr[k], fz);
+        const float rs = s_rs[k / gpc];
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a = fy[2 * j] * silu(fz[2 * j]) * rs * w[8 * k + 2 * j];
+            const float b = fy[2 * j + 1] * silu(fz[2 * j + 1]) * rs * w[8 * k + 2 * j + 1];
+            o[j] = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+        }
+        zr[k] = o;
+    }
+}
+
+} // namespace
+
+hipError_t layer_softplus_bias(float *dt, const float *bias, int64_t tokens, int nheads, hipStream_t st)
+{
+    const int64_t total = tokens * nheads;
+    if (total == 0) return hipSuccess;
+    k_softplus_bias<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(dt, bias, total, nheads);
+    return hipGetLastError();
+}
+
+hipError_t layer_gated_norm(const void *y, void *z, const float *w, int64_t tokens, int channels, int groups,
+                            float eps, hipStream_t st)
+{
+    if (tokens == 0) return hipSuccess;
+    k_gated_norm<<<(unsigned)tokens, NT_NORM, 0, st>>>((const bf16_t *)y, (bf16_t *)z, w, channels, groups, eps);
+    return hipGetLastError();
+}
+
+} // namespace mate

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -433,6 +434,122 @@ mate_status mate_forward(const mate_ssd_tensors *s, const mate_ssd_desc *sd, con
     if (e != hipSuccess) return device_fail(e, "forward: tesa launch");
     e = sfast ? mate::ssd_fast(sp, sa, workspace, stream_h) : mate::ssd_portable(sp, sa, workspace, stream_h);
     if (e != hipSuccess) return device_fail(e, "forward: bissd launch");
+    return MATE_OK;
+}
+
+} // extern "C"
+
+namespace {
+
+// Validates a layer call's descriptors (everything but the pointers); fills the branch problems and the
+// layer's dimensions.
+mate_status make_layer(mate_grid g, int order, const mate_layer_desc *ld, const mate_ssd_desc *sd,
+                       const mate_tesa_desc *td, mate::SsdProblem &sp, bool &sfast, mate::TesaProblem &tp,
+                       bool &tfast, mate::LayerDims &dims)
+{
+    if (!ld) return fail(MATE_ERR_NULL, "layer descriptor is NULL");
+    mate_status st = make_ssd_problem(g, order, sd, sp, sfast);
+    if (st != MATE_OK) return st;
+    if ((st = make_tesa_problem(g, td, tp, tfast)) != MATE_OK) return st;
+    if (sd->dtype != MATE_BF16 || td->dtype != MATE_BF16)
+        return fail(MATE_ERR_UNSUPPORTED, "mate_layer runs in bf16 (both descriptors' dtype)");
+    if (ld->d_model <= 0 || ld->d_model % 8)
+        return fail(MATE_ERR_SHAPE, "d_model %d must be a positive multiple of 8", ld->d_model);
+    if (!(ld->norm_eps >= 0.f)) return fail(MATE_ERR_SHAPE, "norm_eps must be >= 0");
+    const int inner = sd->nheads * sd->headdim;
+    if (sd->ngroups > 64 || (inner / sd->ngroups) % 8)
+        return fail(MATE_ERR_UNSUPPORTED, "the gated norm needs ngroups <= 64 and nheads*headdim/ngroups a multiple of 8");
+    dims.tokens = g.batch * g.T * g.H * g.W;
+    dims.d_model = ld->d_model;
+    dims.inner = inner;
+    dims.bc = sd->ngroups * sd->d_state;
+    dims.nheads = sd->nheads;
+    dims.t_inner = td->nheads * td->headdim;
+    if ((int64_t)dims.tokens * std::max({dims.d_model, dims.inner, dims.t_inner}) >= ((int64_t)1 << 40))
+        return fail(MATE_ERR_UNSUPPORTED, "layer too large");
+    return MATE_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+size_t mate_layer_workspace_size(mate_grid g, const mate_layer_desc *ld, const mate_ssd_desc *sd,
+                                 const mate_tesa_desc *td)
+{
+    mate::SsdProblem sp;
+    mate::TesaProblem tp;
+    mate::LayerDims dims;
+    bool sfast = false, tfast = false;
+    if (make_layer(g, 0, ld, sd, td, sp, sfast, tp, tfast, dims) != MATE_OK) return 0;
+    return mate::layer_layout(dims, ssd_workspace(sp, sfast)).total;
+}
+
+mate_status mate_layer(const void *h, void *out, const mate_layer_weights *w, const mate_layer_desc *ld,
+                       const mate_ssd_desc *sd, const mate_tesa_desc *td, mate_grid g, int order, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    if (!h || !out) return fail(MATE_ERR_NULL, "h or out is NULL");
+    if (!w) return fail(MATE_ERR_NULL, "layer weights struct is NULL");
+    if (!w->w_x || !w->w_z || !w->w_b || !w->w_c || !w->w_dt || !w->w_ma_out || !w->dt_bias || !w->a || !w->d ||
+        !w->norm_w || !w->w_q || !w->w_k || !w->w_v || !w->w_te_out)
+        return fail(MATE_ERR_NULL, "a layer weight pointer is NULL");
+    if (((uintptr_t)h | (uintptr_t)out) & 15) return fail(MATE_ERR_UNSUPPORTED, "h and out must be 16-byte aligned");
+    if (((uintptr_t)w->w_x | (uintptr_t)w->w_z | (uintptr_t)w->w_b | (uintptr_t)w->w_c | (uintptr_t)w->w_dt |
+         (uintptr_t)w->w_ma_out | (uintptr_t)w->w_q | (uintptr_t)w->w_k | (uintptr_t)w->w_v |
+         (uintptr_t)w->w_te_out) & 15)
+        return fail(MATE_ERR_UNSUPPORTED, "weight matrices must be 16-byte aligned");
+    if (((uintptr_t)w->dt_bias | (uintptr_t)w->a | (uintptr_t)w->d | (uintptr_t)w->norm_w) & 3)
+        return fail(MATE_ERR_UNSUPPORTED, "dt_bias, a, d and norm_w must be 4-byte aligned");
+    mate::SsdProblem sp;
+    mate::TesaProblem tp;
+    mate::LayerDims dims;
+    bool sfast = false, tfast = false;
+    mate_status st = make_layer(g, order, ld, sd, td, sp, sfast, tp, tfast, dims);
+    if (st != MATE_OK) return st;
+    const mate::LayerLayout l = mate::layer_layout(dims, ssd_workspace(sp, sfast));
+    if (!workspace || workspace_bytes < l.total)
+        return fail(MATE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                    l.total);
+    if ((uintptr_t)workspace & 255) return fail(MATE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if ((st = prepare_device()) != MATE_OK) return st;
+
+    const hipStream_t sh = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    void *x = ws + l.x, *z = ws + l.z, *b = ws + l.b, *c = ws + l.c, *q = ws + l.q, *k = ws + l.k, *v = ws + l.v;
+    void *y = ws + l.y, *o = ws + l.o, *blas = ws + l.blas;
+    float *dt = (float *)(ws + l.dt);
+    const int64_t M = dims.tokens, K = dims.d_model;
+    char msg[256];
+    struct Proj {
+        const void *wm;
+        void *dst;
+        int64_t n;
+        bool f32;
+    };
+    const Proj ins[] = {{w->w_x, x, dims.inner, false},   {w->w_z, z, dims.inner, false},
+                        {w->w_b, b, dims.bc, false},      {w->w_c, c, dims.bc, false},
+                        {w->w_dt, dt, dims.nheads, true}, {w->w_q, q, dims.t_inner, false},
+                        {w->w_k, k, dims.t_inner, false}, {w->w_v, v, dims.t_inner, false}};
+    for (const Proj &pj : ins)
+        if (mate::gemm_rowmajor(h, pj.wm, pj.dst, M, K, pj.n, pj.f32, false, blas, mate::kGemmWorkspace, sh, msg,
+                                sizeof(msg)))
+            return fail(MATE_ERR_DEVICE, "layer in-projection: %s", msg);
+    hipError_t e = mate::layer_softplus_bias(dt, w->dt_bias, M, dims.nheads, sh);
+    if (e != hipSuccess) return device_fail(e, "layer: dt");
+    const mate::TesaArgs ta{q, k, v, o};
+    e = tfast ? mate::tesa_fast(tp, ta, sh) : mate::tesa_portable(tp, ta, sh);
+    if (e != hipSuccess) return device_fail(e, "layer: tesa launch");
+    const mate::SsdArgs sa{x, b, c, dt, w->a, w->d, y};
+    e = sfast ? mate::ssd_fast(sp, sa, ws + l.core, sh) : mate::ssd_portable(sp, sa, ws + l.core, sh);
+    if (e != hipSuccess) return device_fail(e, "layer: bissd launch");
+    e = mate::layer_gated_norm(y, z, w->norm_w, M, dims.inner, sd->ngroups, ld->norm_eps, sh);
+    if (e != hipSuccess) return device_fail(e, "layer: gated norm");
+    if (mate::gemm_rowmajor(z, w->w_ma_out, out, M, dims.inner, K, false, false, blas, mate::kGemmWorkspace, sh,
+                            msg, sizeof(msg)) ||
+        mate::gemm_rowmajor(o, w->w_te_out, out, M, dims.t_inner, K, false, true, blas, mate::kGemmWorkspace, sh,
+                            msg, sizeof(msg)))
+        return fail(MATE_ERR_DEVICE, "layer out-projection: %s", msg);
     return MATE_OK;
 }
 

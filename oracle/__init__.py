@@ -225,3 +225,58 @@ def tesa_backward(q, k, v, dout, grid, window, shift=(0, 0, 0), scale: float = 0
                                       *(_ptr(a) for a in out))
     _check(rc, "tesa_backward")
     return tuple(out)
+
+
+def bf16_round(a) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even), returned as float64: the float32 value's low 16 bits
+    are rounded away (finite inputs)."""
+    u = np.asarray(a, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return u.view(np.float32).astype(np.float64)
+
+
+def layer(h, w: dict, grid, order: int, ssd: dict, tesa_sizes: dict, norm_eps: float = 1e-5,
+          storage=None, nthreads=None) -> np.ndarray:
+    """One MATE layer in float64: returns out[b][T][H][W][d_model].
+
+    The MATE block replaces a DiT layer's self-attention with the MA and TE
+    branches (QbitAI article on LinGen, section "方法"); the projections and the
+    MA branch's per-token steps around the scan are the Mamba2 block's, which
+    the pages do not spell out (the reading stated with ``mate_layer`` in
+    include/mate.h):
+        x, z, B, C = h Wx, h Wz, h Wb, h Wc;  dt = softplus(h Wdt + dt_bias)
+        y = bissd(x, B, C, dt, A, D);  g = y * silu(z), RMS-normalised per group
+        of nheads*headdim/ngroups channels (eps), times norm_w
+        q, k, v = h Wq, h Wk, h Wv;  o = tesa(q, k, v)
+        out = g Wma_out + o Wte_out
+    The products are numpy float64 matmuls; the scan and TESA are the oracle's
+    own (they take their inputs as float32, a rounding of 2^-24 relative).
+    ``w`` maps the names of mate_layer_weights to arrays; ``ssd`` holds nheads,
+    headdim, d_state, ngroups, pool; ``tesa_sizes`` nheads, headdim, window,
+    shift and optionally scale. With ``storage="bf16"`` the intermediates are
+    rounded to bfloat16 where mate_layer stores them (x, z, B, C, q, k, v, y,
+    o, g and out; dt stays exact): the documented layer with exact arithmetic
+    between the stores.
+    """
+    rnd = bf16_round if storage == "bf16" else (lambda a: a)
+    batch, T, H, W = grid
+    f = lambda n: np.asarray(w[n], dtype=np.float64)
+    hb = np.asarray(h, dtype=np.float64).reshape(-1, h.shape[-1])
+    nh, P, S, G = ssd["nheads"], ssd["headdim"], ssd["d_state"], ssd.get("ngroups", 1)
+    th, td = tesa_sizes["nheads"], tesa_sizes["headdim"]
+    tok = (batch, T, H, W)
+    x = rnd(hb @ f("w_x")).reshape(tok + (nh, P))
+    z = rnd(hb @ f("w_z"))
+    Bm = rnd(hb @ f("w_b")).reshape(tok + (G, S))
+    Cm = rnd(hb @ f("w_c")).reshape(tok + (G, S))
+    dt = np.logaddexp(0.0, hb @ f("w_dt") + f("dt_bias")).reshape(tok + (nh,))
+    y = rnd(bissd(x, Bm, Cm, dt, f("a"), f("d"), grid, order, ssd.get("pool", (0, 0, 0)), nthreads=nthreads))
+    gv = y.reshape(-1, nh * P) * (z / (1.0 + np.exp(-z)))
+    gv = gv.reshape(gv.shape[0], G, -1)
+    gv = gv / np.sqrt(np.mean(gv * gv, axis=-1, keepdims=True) + norm_eps)
+    gv = rnd(gv.reshape(-1, nh * P) * f("norm_w"))
+    q, k, v = (rnd(hb @ f(n)).reshape(tok + (th, td)) for n in ("w_q", "w_k", "w_v"))
+    o = rnd(tesa(q, k, v, grid, tesa_sizes["window"], tesa_sizes.get("shift", (0, 0, 0)),
+                 tesa_sizes.get("scale", 0.0), nthreads=nthreads))
+    out = gv @ f("w_ma_out") + o.reshape(-1, th * td) @ f("w_te_out")
+    return rnd(out).reshape(tok + (hb.shape[1],))

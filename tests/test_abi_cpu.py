@@ -251,3 +251,34 @@ def test_noalloc_scan_validation_and_scratch_limit():
     assert lib.mate_bissd_workspace_size(g2, ctypes.byref(big)) > B.STATIC_SCRATCH_BYTES
     assert lib.mate_bissd_scan_noalloc(ctypes.byref(t), g2, 0, ctypes.byref(big), None) == B.MATE_ERR_WORKSPACE
     assert "static scratch" in lib.mate_last_error().decode()
+
+
+def test_layer_validation_rejects_before_launch():
+    """mate_layer checks pointers, alignment, both descriptors (bf16 only), d_model and the workspace before
+    any device call; its workspace size is the intermediates plus the scan's workspace and 64 MiB."""
+    lib = B.lib()
+    g = B.Grid(1, 8, 16, 16)
+    ld, sd, td = B.layer_descs((1, 8, 16, 16), 256, dict(nheads=16, headdim=64, d_state=64, chunk=64),
+                               dict(nheads=8, headdim=64, window=(4, 8, 8)))
+    need = lib.mate_layer_workspace_size(g, ctypes.byref(ld), ctypes.byref(sd), ctypes.byref(td))
+    n = 8 * 16 * 16
+    inter = n * (3 * 1024 * 2 + 2 * 64 * 2 + 16 * 4 + 4 * 512 * 2)
+    scan = lib.mate_bissd_workspace_size(g, ctypes.byref(sd))
+    assert inter + scan + (64 << 20) <= need <= inter + scan + (64 << 20) + 16 * 256
+    w = B.LayerWeights(*([0x200000] * len(B.LAYER_WEIGHTS)))
+    h, out, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000), ctypes.c_void_p(0x4000000)
+    call = lambda w_, ld_, sd_, td_, ws_=ws, wsb=need, order=0, h_=h: lib.mate_layer(
+        h_, out, ctypes.byref(w_), ctypes.byref(ld_), ctypes.byref(sd_), ctypes.byref(td_), g, order, ws_, wsb, None)
+    assert call(B.LayerWeights(*([0x200000] * 13 + [0])), ld, sd, td) == B.MATE_ERR_NULL
+    assert call(w, ld, sd, td, h_=None) == B.MATE_ERR_NULL
+    assert call(w, ld, sd, td, h_=ctypes.c_void_p(0x100008)) == B.MATE_ERR_UNSUPPORTED
+    assert call(w, B.LayerDesc(250, 1e-5), sd, td) == B.MATE_ERR_SHAPE
+    assert call(w, B.LayerDesc(256, -1.0), sd, td) == B.MATE_ERR_SHAPE
+    sd32 = B.SsdDesc(16, 64, 64, 1, 64, 0, 0, 0, B.MATE_F32, B.ALGO_AUTO)
+    assert call(w, ld, sd32, td) == B.MATE_ERR_UNSUPPORTED
+    assert "bf16" in lib.mate_last_error().decode()
+    assert call(w, ld, sd, td, order=9) == B.MATE_ERR_SHAPE
+    assert call(w, ld, sd, td, wsb=need - 1) == B.MATE_ERR_WORKSPACE
+    assert call(w, ld, sd, td, ws_=ctypes.c_void_p(0x4000080)) == B.MATE_ERR_WORKSPACE
+    assert lib.mate_layer_workspace_size(g, ctypes.byref(B.LayerDesc(0, 1e-5)), ctypes.byref(sd),
+                                         ctypes.byref(td)) == 0

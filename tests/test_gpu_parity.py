@@ -833,3 +833,75 @@ def test_ssd_backward_sampled_heads(oracle_mod, cfg, order):
                                        inp["D"].dev[sel], np.ascontiguousarray(dyh[..., sel, :]), wl.grid, order,
                                        wl.pool)
     check_ssd_grads(got_s, want_s, TOL[cfg], names=("dB", "dC"))
+
+
+# ----------------------------------------------------------------------------
+# One MATE layer (projections, both branches, gate and norm, sum)
+# ----------------------------------------------------------------------------
+
+_LAYER_F32 = ("dt_bias", "a", "d", "norm_w")
+
+
+def _layer_case(seed, grid, dm, nh, P, S, G, th, td):
+    """bf16-valued float32 weights and input (so both sides see the same numbers) and float32 vectors."""
+    rng = np.random.default_rng(seed)
+    bf = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(np.asarray(a, dtype=np.float32)))
+    r = lambda *s: bf(rng.standard_normal(s) / np.sqrt(s[0]))
+    w = {"w_x": r(dm, nh * P), "w_z": r(dm, nh * P), "w_b": r(dm, G * S), "w_c": r(dm, G * S),
+         "w_dt": bf(r(dm, nh) * 0.3), "w_ma_out": r(nh * P, dm), "w_q": r(dm, th * td), "w_k": r(dm, th * td),
+         "w_v": r(dm, th * td), "w_te_out": r(th * td, dm),
+         "dt_bias": rng.normal(-1, 0.5, nh).astype(np.float32), "a": -np.exp(rng.uniform(0, 1, nh)).astype(np.float32),
+         "d": rng.standard_normal(nh).astype(np.float32), "norm_w": (1 + 0.2 * rng.standard_normal(nh * P)).astype(np.float32)}
+    h = bf(rng.standard_normal(tuple(grid) + (dm,)))
+    return h, w
+
+
+def _run_layer(h, w, dm, ssd, te, order):
+    dev = {n: torch.from_numpy(np.ascontiguousarray(v)).cuda().to(torch.float32 if n in _LAYER_F32 else torch.bfloat16)
+           for n, v in w.items()}
+    hd = torch.from_numpy(h).cuda().to(torch.bfloat16)
+    out = torch.full_like(hd, float("nan"))
+    B.mate_layer(hd, out, dev, dm, ssd, te, order)
+    torch.cuda.synchronize()
+    return to_f64(out)
+
+
+def _check_layer(oracle_mod, got, h, w, grid, order, ssd, te):
+    """Two checks. (1) The implementation: against the oracle of the documented layer (intermediates
+    stored as bf16 where mate_layer stores them, exact arithmetic between), at 2e-2. (2) The accuracy the
+    format allows: against the exact oracle, no worse than twice the bf16-storage layer's own error plus
+    5e-3. The per-row RMS norm turns an error that is small against the whole tensor into a large one in
+    rows whose y is small, so (2) is measured against what bf16 storage itself costs on the same input."""
+    stored = oracle_mod.layer(h, w, grid, order, ssd, te, storage="bf16")
+    exact = oracle_mod.layer(h, w, grid, order, ssd, te)
+    err_impl = parity_error(got, stored)
+    err_exact, err_format = parity_error(got, exact), parity_error(stored, exact)
+    say(f"  vs bf16-storage oracle err={err_impl:.3e}; vs exact err={err_exact:.3e} (format alone {err_format:.3e})")
+    assert err_impl <= 2e-2, err_impl
+    assert err_exact <= 2 * err_format + 5e-3, (err_exact, err_format)
+
+
+@pytest.mark.parametrize("order,shifted,batch", [(0, False, 1), (1, True, 2), (2, False, 1), (3, True, 1)])
+def test_layer_parity_small(oracle_mod, order, shifted, batch):
+    """mate_layer against the oracle in full: 8x16x16 grid, 256-wide rows, 16 scan heads of 64 (d_state 64),
+    8 TESA heads of 64 in 4x8x8 windows, the four RMS orders with the shift on odd layers."""
+    grid, dm = (batch, 8, 16, 16), 256
+    say(f"layer small order {order} shifted {shifted} batch {batch}")
+    h, w = _layer_case(400 + order, grid, dm, 16, 64, 64, 1, 8, 64)
+    ssd = dict(nheads=16, headdim=64, d_state=64, ngroups=1, chunk=64)
+    te = dict(nheads=8, headdim=64, window=(4, 8, 8), shift=(2, 4, 4) if shifted else (0, 0, 0))
+    got = _run_layer(h, w, dm, ssd, te, order)
+    _check_layer(oracle_mod, got, h, w, grid, order, ssd, te)
+
+
+@pytest.mark.parametrize("order,shifted", [(0, True), (3, False)])
+def test_layer_parity_lingen_widths(oracle_mod, order, shifted):
+    """The LinGen-4B layer widths (2560-wide rows; MA: 80 heads of 64, d_state 128, chunk 128, review tokens
+    pooled 2x4x4; TE: 20 heads of 128) on a 4x8x8 grid, against the oracle in full."""
+    grid, dm = (1, 4, 8, 8), 2560
+    say(f"layer lingen widths order {order} shifted {shifted}")
+    h, w = _layer_case(420 + order, grid, dm, 80, 64, 128, 1, 20, 128)
+    ssd = dict(nheads=80, headdim=64, d_state=128, ngroups=1, chunk=128, pool=(2, 4, 4))
+    te = dict(nheads=20, headdim=128, window=(4, 8, 8), shift=(2, 4, 4) if shifted else (0, 0, 0))
+    got = _run_layer(h, w, dm, ssd, te, order)
+    _check_layer(oracle_mod, got, h, w, grid, order, ssd, te)

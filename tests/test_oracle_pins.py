@@ -744,3 +744,117 @@ def test_ssd_backward_special_cases_and_identities(oracle_mod):
     np.testing.assert_allclose(np.concatenate([lo["dA"], hi["dA"]]), got["dA"], rtol=1e-13)
     np.testing.assert_allclose(lo["dB"] + hi["dB"], got["dB"], rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(lo["dC"] + hi["dC"], got["dC"], rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# One MATE layer (projections, the two branches, gate and norm, sum)
+# ----------------------------------------------------------------------------
+
+def _layer_weights(rng, dm, nh, P, S, G, th, td):
+    r = lambda *s: rng.standard_normal(s) / np.sqrt(s[0])
+    return {"w_x": r(dm, nh * P), "w_z": r(dm, nh * P), "w_b": r(dm, G * S), "w_c": r(dm, G * S),
+            "w_dt": r(dm, nh) * 0.3, "w_ma_out": r(nh * P, dm), "dt_bias": rng.normal(-1, 0.5, nh),
+            "a": -np.exp(rng.uniform(0, 1, nh)), "d": rng.standard_normal(nh),
+            "norm_w": 1 + 0.2 * rng.standard_normal(nh * P), "w_q": r(dm, th * td), "w_k": r(dm, th * td),
+            "w_v": r(dm, th * td), "w_te_out": r(th * td, dm)}
+
+
+_LAYER = dict(grid=(2, 2, 4, 4), dm=24, nh=3, P=8, S=8, G=1, th=2, td=8)
+
+
+# The oracle's scan and TESA take their inputs as float32, so results built from fp64 projections agree with
+# these float64 closed forms to about 2^-24 relative per input: the pins use rtol = atol = 1e-6.
+def _layer_case(seed=910, **over):
+    c = dict(_LAYER, **over)
+    rng = np.random.default_rng(seed)
+    w = _layer_weights(rng, c["dm"], c["nh"], c["P"], c["S"], c["G"], c["th"], c["td"])
+    h = rng.standard_normal(c["grid"] + (c["dm"],))
+    ssd = dict(nheads=c["nh"], headdim=c["P"], d_state=c["S"], ngroups=c["G"], pool=c.get("pool", (0, 0, 0)))
+    te = dict(nheads=c["th"], headdim=c["td"], window=c.get("window", (2, 2, 2)), shift=c.get("shift", (0, 0, 0)))
+    return c, w, h, ssd, te
+
+
+def test_layer_te_branch_with_one_token_windows_is_a_gemm_chain(oracle_mod):
+    """Windows of one token: each token attends only to itself (softmax over one key is 1), so o = v and,
+    with the MA out-projection zeroed, out = (h Wv) Wte_out."""
+    c, w, h, ssd, te = _layer_case(window=(1, 1, 1))
+    w["w_ma_out"] = np.zeros_like(w["w_ma_out"])
+    out = oracle_mod.layer(h, w, c["grid"], 0, ssd, te)
+    hb = h.reshape(-1, c["dm"])
+    want = (hb @ w["w_v"]) @ w["w_te_out"]
+    np.testing.assert_allclose(out.reshape(-1, c["dm"]), want, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("order", [0, 2])
+def test_layer_ma_branch_without_memory_is_closed_form(oracle_mod, order):
+    """A decay that underflows to zero within one step (A = -1e4, dt = softplus(0) = ln 2 from a zero dt
+    projection and bias) leaves only each token's own term in both directions:
+    y_t = 2 (dt C_t . B_t + D) x_t. With the TE out-projection zeroed, out = norm(y * silu(z)) Wma_out."""
+    c, w, h, ssd, te = _layer_case(G=1)
+    w["w_te_out"] = np.zeros_like(w["w_te_out"])
+    w["w_dt"] = np.zeros_like(w["w_dt"])
+    w["dt_bias"] = np.zeros(c["nh"])
+    w["a"] = np.full(c["nh"], -1e4)
+    out = oracle_mod.layer(h, w, c["grid"], order, ssd, te, norm_eps=1e-5)
+    hb = h.reshape(-1, c["dm"])
+    x = (hb @ w["w_x"]).reshape(-1, c["nh"], c["P"])
+    cb = np.sum((hb @ w["w_c"]) * (hb @ w["w_b"]), axis=1)  # one group
+    y = 2 * (np.log(2.0) * cb[:, None, None] + w["d"][None, :, None]) * x
+    z = hb @ w["w_z"]
+    g = y.reshape(len(hb), -1) * z * (1 / (1 + np.exp(-z)))
+    g = g / np.sqrt(np.mean(g * g, axis=1, keepdims=True) + 1e-5) * w["norm_w"]
+    np.testing.assert_allclose(out.reshape(-1, c["dm"]), g @ w["w_ma_out"], rtol=1e-6, atol=1e-6)
+
+
+def test_layer_is_the_sum_of_its_branches(oracle_mod):
+    """out is linear in the two out-projections: the layer equals the MA-only plus the TE-only layer, so
+    neither branch's output leaks into the other's, here with review tokens and a shifted window (the
+    branches' own values are pinned by the two closed forms above)."""
+    c, w, h, ssd, te = _layer_case(pool=(2, 2, 2), shift=(1, 1, 1), G=1)
+    full = oracle_mod.layer(h, w, c["grid"], 1, ssd, te)
+    w_ma = dict(w, w_te_out=np.zeros_like(w["w_te_out"]))
+    w_te = dict(w, w_ma_out=np.zeros_like(w["w_ma_out"]))
+    parts = oracle_mod.layer(h, w_ma, c["grid"], 1, ssd, te) + oracle_mod.layer(h, w_te, c["grid"], 1, ssd, te)
+    np.testing.assert_allclose(full, parts, rtol=1e-10, atol=1e-10)
+
+
+def test_layer_norm_groups_and_scale_invariance(oracle_mod):
+    """With an identity out-projection, unit norm weights and eps = 0, each group of nheads*headdim/ngroups
+    channels of the MA output has mean square 1; and scaling Wx (hence y and the gated values) leaves the
+    normalised output unchanged."""
+    c, w, h, ssd, te = _layer_case(G=3, nh=3, P=8, dm=24)
+    w["w_te_out"] = np.zeros_like(w["w_te_out"])
+    w["w_ma_out"] = np.eye(24)
+    w["norm_w"] = np.ones(24)
+    out = oracle_mod.layer(h, w, c["grid"], 3, ssd, te, norm_eps=0.0).reshape(-1, 3, 8)
+    np.testing.assert_allclose(np.mean(out * out, axis=-1), 1.0, rtol=1e-6)
+    w2 = dict(w, w_x=3.0 * w["w_x"])
+    out2 = oracle_mod.layer(h, w2, c["grid"], 3, ssd, te, norm_eps=0.0).reshape(-1, 3, 8)
+    np.testing.assert_allclose(out2, out, rtol=1e-6, atol=1e-6)
+
+
+def test_bf16_round_values(oracle_mod):
+    """Round-to-nearest-even onto the 8-bit significand: exact values stay, ties go to the even neighbour,
+    and a value above a tie rounds up (hand values)."""
+    e = 2.0 ** -8  # half an ulp of bf16 at 1
+    vals = np.array([1.0, 1.0 + e, 1.0 + 3 * e, 1.0 + 1.5 * e, -2.0 - 2 * e, 3.0, 2.0 ** -130, 65504.0])
+    want = np.array([1.0, 1.0, 1.0 + 4 * e, 1.0 + 2 * e, -2.0, 3.0, 2.0 ** -130, 65536.0])
+    np.testing.assert_array_equal(oracle_mod.bf16_round(vals), want)
+
+
+def test_layer_bf16_storage_rounds_only_where_stored(oracle_mod):
+    """With bf16 storage the layer differs from the exact one by about the format's precision, and on
+    weights and input whose every intermediate is a small integer (exact in bf16) the two agree exactly."""
+    c, w, h, ssd, te = _layer_case(window=(1, 1, 1))
+    exact = oracle_mod.layer(h, w, c["grid"], 0, ssd, te)
+    stored = oracle_mod.layer(h, w, c["grid"], 0, ssd, te, storage="bf16")
+    rel = np.max(np.abs(stored - exact)) / np.max(np.abs(exact))
+    assert 1e-4 < rel < 0.1, rel
+    # TE only, one-token windows (o = v): integer h and 0/1 weights keep q, k, v, o and out integers < 256
+    rng = np.random.default_rng(3)
+    hi = rng.integers(-3, 4, size=c["grid"] + (c["dm"],)).astype(np.float64)
+    wi = dict(w, w_v=rng.integers(0, 2, size=w["w_v"].shape).astype(np.float64),
+              w_te_out=rng.integers(0, 2, size=w["w_te_out"].shape).astype(np.float64),
+              w_ma_out=np.zeros_like(w["w_ma_out"]))
+    np.testing.assert_array_equal(oracle_mod.layer(hi, wi, c["grid"], 0, ssd, te, storage="bf16"),
+                                  oracle_mod.layer(hi, wi, c["grid"], 0, ssd, te))
