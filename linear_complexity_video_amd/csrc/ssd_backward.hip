@@ -121,29 +121,32 @@ __global__ __launch_bounds__(256) void k_review_index(int *__restrict__ rinv, ui
 }
 
 // ---------------------------------------------------------------------------
-// Gradients of the review tokens of one (batch, head). Forward direction: the
-// adjoint of the state the review tokens leave to the main sequence is Gf0; a
-// review token r reaches it with decay df_r = exp(sum_{j > r} dt_j A). Backward
-// direction (review tokens taken in reverse order): Gb0 and db_r = exp(sum_{j < r}
-// dt_j A). dy is 0 on review tokens, so each token's pairs are with main tokens
-// only and the pairs spanning r are those whose review end lies before r in
-// that direction. grid (batch * nheads), 256 threads; P <= 64, S <= 128.
+// Gradients of the review tokens of one (batch, head), RT tokens per workgroup. Forward direction: the
+// adjoint of the state the review tokens leave to the main sequence is Gf0; a review token r reaches it
+// with decay df_r = exp(sum_{j > r} dt_j A). Backward direction (review tokens taken in reverse order):
+// Gb0 and db_r = exp(sum_{j < r} dt_j A). dy is 0 on review tokens, so each token's pairs are with main
+// tokens only, and the pairs spanning r are those whose review end lies before r in that direction:
+// this kernel writes each token's pair sums (cfr, cbr) and the explicit part of its dt gradient;
+// k_review_spans adds the spans. grid (ceil(R / RT) * batch * nheads), 256 threads; P <= 64, S <= 128.
 // ---------------------------------------------------------------------------
+constexpr int RT = 16;  // review tokens per workgroup
+
 __global__ __launch_bounds__(NTB) void k_review_grads(const float *__restrict__ rx, const float *__restrict__ rB,
                                                       const float *__restrict__ rdt, const float *__restrict__ A,
                                                       const float *__restrict__ Gf0, const float *__restrict__ Gb0,
                                                       float *__restrict__ drx, float *__restrict__ drB,
-                                                      float *__restrict__ drdt, float *__restrict__ pAr, int nheads,
-                                                      int P, int S, int G, int R)
+                                                      float *__restrict__ drdt, float *__restrict__ cfr,
+                                                      float *__restrict__ cbr, int nheads, int P, int S, int G, int R)
 {
     extern __shared__ float sm[];
     const int PS = P * S;
     float *gf = sm, *gb = gf + PS;             // adjoint states [P][S]
     float *xs = gb + PS, *bs = xs + P;         // the token's x and B
-    float *decf = bs + S, *decb = decf + R;    // decays to the review end, per direction
-    float *cfr = decb + R, *cbr = cfr + R;     // per-token pair sums (dt x . dx-part)
-    float *red = cbr + R;                      // [2][NTB] partial sums
-    const int bh = blockIdx.x, b = bh / nheads, h = bh % nheads, g = h / (nheads / G);
+    float *decf = bs + S, *decb = decf + RT;   // decays to the review end, per direction
+    float *red = decb + RT;                    // [2][NTB] partial sums
+    const int nrb = (R + RT - 1) / RT;
+    const int bh = blockIdx.x / nrb, b = bh / nheads, h = bh % nheads, g = h / (nheads / G);
+    const int r0 = (blockIdx.x % nrb) * RT, r1 = min(R, r0 + RT);
     const float a = A[h];
     for (int e = threadIdx.x; e < PS; e += NTB) {
         gf[e] = Gf0[(size_t)bh * PS + e];
@@ -151,13 +154,13 @@ __global__ __launch_bounds__(NTB) void k_review_grads(const float *__restrict__ 
     }
     if (threadIdx.x == 0) {
         float run = 1.f;
-        for (int r = R - 1; r >= 0; --r) {
-            decf[r] = run;
+        for (int r = R - 1; r >= r0; --r) {
+            if (r < r1) decf[r - r0] = run;
             run *= __expf(rdt[((size_t)b * R + r) * nheads + h] * a);
         }
         run = 1.f;
-        for (int r = 0; r < R; ++r) {
-            decb[r] = run;
+        for (int r = 0; r < r1; ++r) {
+            if (r >= r0) decb[r - r0] = run;
             run *= __expf(rdt[((size_t)b * R + r) * nheads + h] * a);
         }
     }
@@ -165,8 +168,9 @@ __global__ __launch_bounds__(NTB) void k_review_grads(const float *__restrict__ 
     // thread layout: for G x B (P outputs), 4 threads per p split S; for G^T x (S outputs), 2 threads per s split P
     const int tp = threadIdx.x >> 2, tq = threadIdx.x & 3;
     const int ts = threadIdx.x >> 1, tr = threadIdx.x & 1;
-    for (int r = 0; r < R; ++r) {
+    for (int r = r0; r < r1; ++r) {
         const float d = rdt[((size_t)b * R + r) * nheads + h];
+        const float df = decf[r - r0], db = decb[r - r0];
         for (int p = threadIdx.x; p < P; p += NTB) xs[p] = rx[((size_t)b * R + r) * nheads * P + (size_t)h * P + p];
         for (int s = threadIdx.x; s < S; s += NTB) bs[s] = rB[((size_t)b * R + r) * G * S + (size_t)g * S + s];
         __syncthreads();
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(NTB) void k_review_grads(const float *__restrict__ 
         // dx = dt dec (G B); the explicit dt part x . (dec G B)
         float xf = 0.f, xb = 0.f;
         if (tp < P && tq == 0) {
-            const float vf = decf[r] * pf, vb = decb[r] * pb;
+            const float vf = df * pf, vb = db * pb;
             drx[(((size_t)b * R + r) * nheads + h) * P + tp] = d * (vf + vb);
             xf = xs[tp] * vf;
             xb = xs[tp] * vb;
@@ -196,8 +200,7 @@ __global__ __launch_bounds__(NTB) void k_review_grads(const float *__restrict__ 
             }
         qf = seg_sum(qf, 2);
         qb = seg_sum(qb, 2);
-        if (ts < S && tr == 0)
-            drB[(((size_t)b * R + r) * nheads + h) * S + ts] = d * (decf[r] * qf + decb[r] * qb);
+        if (ts < S && tr == 0) drB[(((size_t)b * R + r) * nheads + h) * S + ts] = d * (df * qf + db * qb);
         // block sums of the explicit parts
         red[threadIdx.x] = xf;
         red[NTB + threadIdx.x] = xb;
@@ -208,30 +211,40 @@ __global__ __launch_bounds__(NTB) void k_review_grads(const float *__restrict__ 
                 ef += red[k];
                 eb += red[NTB + k];
             }
-            drdt[((size_t)b * R + r) * nheads + h] = ef + eb;  // explicit part; decay part added below
-            cfr[r] = d * ef;
-            cbr[r] = d * eb;
+            drdt[((size_t)b * R + r) * nheads + h] = ef + eb;  // explicit part; k_review_spans adds the decay part
+            cfr[(size_t)bh * R + r] = d * ef;
+            cbr[(size_t)bh * R + r] = d * eb;
         }
         __syncthreads();
     }
-    if (threadIdx.x == 0) {
-        // spans: forward pairs spanning r have their review end u < r; backward pairs u > r
-        float below = 0.f, dA = 0.f;
-        for (int r = 0; r < R; ++r) {
-            float *o = drdt + ((size_t)b * R + r) * nheads + h;
-            *o += a * below;
-            dA += rdt[((size_t)b * R + r) * nheads + h] * below;
-            below += cfr[r];
-        }
-        float above = 0.f;
-        for (int r = R - 1; r >= 0; --r) {
-            float *o = drdt + ((size_t)b * R + r) * nheads + h;
-            *o += a * above;
-            dA += rdt[((size_t)b * R + r) * nheads + h] * above;
-            above += cbr[r];
-        }
-        pAr[bh] = dA;
+}
+
+// The decay part of the review tokens' dt gradients and their share of dA: forward pairs spanning r have
+// their review end u < r, backward pairs u > r. grid (ceil(batch * nheads / 256)).
+__global__ __launch_bounds__(256) void k_review_spans(const float *__restrict__ rdt, const float *__restrict__ A,
+                                                      const float *__restrict__ cfr, const float *__restrict__ cbr,
+                                                      float *__restrict__ drdt, float *__restrict__ pAr, int nheads,
+                                                      int R, int nbh)
+{
+    const int bh = blockIdx.x * 256 + threadIdx.x;
+    if (bh >= nbh) return;
+    const int b = bh / nheads, h = bh % nheads;
+    const float a = A[h];
+    float below = 0.f, dA = 0.f;
+    for (int r = 0; r < R; ++r) {
+        float *o = drdt + ((size_t)b * R + r) * nheads + h;
+        *o += a * below;
+        dA += rdt[((size_t)b * R + r) * nheads + h] * below;
+        below += cfr[(size_t)bh * R + r];
     }
+    float above = 0.f;
+    for (int r = R - 1; r >= 0; --r) {
+        float *o = drdt + ((size_t)b * R + r) * nheads + h;
+        *o += a * above;
+        dA += rdt[((size_t)b * R + r) * nheads + h] * above;
+        above += cbr[(size_t)bh * R + r];
+    }
+    pAr[bh] = dA;
 }
 
 // drBg[b][r][g][s] = sum over the heads of group g of drB[b][r][h][s]. grid (R, batch), 256 threads.
@@ -850,8 +863,10 @@ __global__ __launch_bounds__(NTB) void k_bwd_states_mfma(const __bf16 *__restric
 // state in fp32: the even blockIdx.y of a head runs left to right over Sf (Sf[c] becomes the state after
 // chunk c - 1), the odd one right to left over Sb (the state after chunk c + 1). h0f / h0b (optional) are
 // the initial states, finF / finB (optional) receive the final ones, fp32 [batch][nheads][P*S]. Each
-// thread carries 8 consecutive elements; the loads of U chunks are issued before their updates.
-// grid (ceil(P*S / 2048), 2 nheads, batch), 256 threads; P*S a multiple of 8.
+// thread carries 8 consecutive elements through batches of U chunks; a batch's loads are issued before
+// the previous batch's updates and stores, so waiting for them never waits for those stores (the memory
+// counter retires in issue order). grid (ceil(P*S / 2048), 2 nheads, batch), 256 threads; P*S a multiple
+// of 8.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_state_pass_bf16(__bf16 *__restrict__ Sf, __bf16 *__restrict__ Sb,
                                                          const float *__restrict__ csT, const float *__restrict__ h0f,
@@ -870,31 +885,45 @@ __global__ __launch_bounds__(256) void k_state_pass_bf16(__bf16 *__restrict__ Sf
     float run[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) run[j] = h0 ? h0[bh * PS + e + j] : 0.f;
-    for (int c0 = 0; c0 < nch; c0 += U) {
-        const int n = min(U, nch - c0);
-        bf16x8 v[U];
-        float dec[U];
+    // chunk of batch position k of the batch starting at c0 (clamped: loads past the end repeat the last
+    // chunk and are not used)
+    auto chunk = [&](int c0, int k) {
+        const int i = min(c0 + k, nch - 1);
+        return dir ? nch - 1 - i : i;
+    };
+    // two register sets, used alternately (static indices: the loop body covers one batch in each)
+    bf16x8 va[U], vb[U];
+    float da[U], db[U];
+    auto load = [&](int c0, bf16x8 (&v)[U], float (&d)[U]) {
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            if (k < n) {
-                const int c = dir ? nch - 1 - (c0 + k) : c0 + k;
-                v[k] = *(const bf16x8 *)(base + (size_t)c * PS);
-                dec[k] = __expf(tot[(size_t)c * QM]);
-            }
+            const int c = chunk(c0, k);
+            v[k] = *(const bf16x8 *)(base + (size_t)c * PS);
+            d[k] = __expf(tot[(size_t)c * QM]);
         }
+    };
+    auto update = [&](int c0, const bf16x8 (&v)[U], const float (&d)[U]) {
+        const int n = min(U, nch - c0);
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             if (k < n) {
-                const int c = dir ? nch - 1 - (c0 + k) : c0 + k;
                 bf16x8 o;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     o[j] = (__bf16)run[j];
-                    run[j] = dec[k] * run[j] + (float)v[k][j];
+                    run[j] = d[k] * run[j] + (float)v[k][j];
                 }
-                *(bf16x8 *)(base + (size_t)c * PS) = o;
+                *(bf16x8 *)(base + (size_t)chunk(c0, k) * PS) = o;
             }
         }
+    };
+    load(0, va, da);
+    for (int c0 = 0; c0 < nch; c0 += 2 * U) {
+        if (c0 + U < nch) load(c0 + U, vb, db);
+        update(c0, va, da);
+        if (c0 + U >= nch) break;
+        if (c0 + 2 * U < nch) load(c0 + 2 * U, va, da);
+        update(c0 + U, vb, db);
     }
     if (fin)
 #pragma unroll
@@ -1346,7 +1375,7 @@ int bwd_chunk(const SsdProblem &p)
 struct BwdLayout {
     int Q, nch, nchR;
     size_t dtT, csT, Sf, Sb, Uf, Ub, CB, expl, cf, cb, rf, rb, crs, pA, pD;
-    size_t rx, rB, rdt, rdtT, rcsT, rSf, rSb, h0f, h0b, Gf0, Gb0, drx, drB, drBg, drdt, pAr, rinv, total;
+    size_t rx, rB, rdt, rdtT, rcsT, rSf, rSb, h0f, h0b, Gf0, Gb0, drx, drB, drBg, drdt, pAr, rcf, rcb, rinv, total;
 };
 
 BwdLayout bwd_layout(const SsdProblem &p)
@@ -1396,6 +1425,8 @@ BwdLayout bwd_layout(const SsdProblem &p)
         l.drBg = take(B * R * G * p.d_state * 4);
         l.drdt = take(B * R * Hs * 4);
         l.pAr = take(B * Hs * 4);
+        l.rcf = take(B * Hs * R * 4);
+        l.rcb = take(B * Hs * R * 4);
         l.rinv = take(R * 4);
     }
     l.total = off;
@@ -1404,7 +1435,7 @@ BwdLayout bwd_layout(const SsdProblem &p)
 
 size_t review_lds(const SsdProblem &p)
 {
-    return ((size_t)2 * p.headdim * p.d_state + p.headdim + p.d_state + 4 * (size_t)p.R + 2 * NTB) * 4;
+    return ((size_t)2 * p.headdim * p.d_state + p.headdim + p.d_state + 2 * RT + 2 * NTB) * 4;
 }
 
 // Chunk states, their passes, and the per-chunk gradient kernels on MFMA (after the review tokens'
@@ -1433,9 +1464,11 @@ hipError_t run_chunks_mfma(const SsdProblem &p, const SsdGradArgs &a, const BwdL
                                                    W);
     k_state_pass_bf16<<<gp, 256, 0, st>>>(Ub, Uf, csT, nullptr, nullptr, Gb0, Gf0, PM * S, l.nch, Lpad);
     if (R > 0) {
-        k_review_grads<<<B * Hs, NTB, review_lds(p), st>>>(F(l.rx), F(l.rB), F(l.rdt), a.a, Gf0, Gb0,
-                                                           (float *)drx, F(l.drB), (float *)drdt, (float *)pAr, Hs,
-                                                           PM, S, G, (int)R);
+        k_review_grads<<<((R + RT - 1) / RT) * B * Hs, NTB, review_lds(p), st>>>(
+            F(l.rx), F(l.rB), F(l.rdt), a.a, Gf0, Gb0, (float *)drx, F(l.drB), (float *)drdt, F(l.rcf), F(l.rcb), Hs,
+            PM, S, G, (int)R);
+        k_review_spans<<<(B * Hs + 255) / 256, 256, 0, st>>>(F(l.rdt), a.a, F(l.rcf), F(l.rcb), (float *)drdt,
+                                                            (float *)pAr, Hs, (int)R, B * Hs);
         k_review_group<<<dim3(R, B), 256, 0, st>>>(F(l.drB), (float *)drBg, Hs, S, G);
     }
     k_bwd_dbdc_mfma<S><<<gg, 4 * S, dbdc_mfma_lds<S>(), st>>>(
@@ -1518,8 +1551,10 @@ hipError_t run_backward(const SsdProblem &p, const SsdGradArgs &a, void *ws, hip
                                                                   l.nch, Q, Lpad);
     k_cb<E><<<dim3(l.nch, G, B), 256, 0, st>>>(Bm, Cm, CB, G, S, N, Q, p.order, T, H, W);
     if (R > 0) {
-        k_review_grads<<<B * Hs, NTB, review_lds(p), st>>>(F(l.rx), F(l.rB), F(l.rdt), a.a, Gf0, Gb0, drx, F(l.drB),
-                                                           drdt, pAr, Hs, P, S, G, (int)R);
+        k_review_grads<<<((R + RT - 1) / RT) * B * Hs, NTB, review_lds(p), st>>>(
+            F(l.rx), F(l.rB), F(l.rdt), a.a, Gf0, Gb0, drx, F(l.drB), drdt, F(l.rcf), F(l.rcb), Hs, P, S, G, (int)R);
+        k_review_spans<<<(B * Hs + 255) / 256, 256, 0, st>>>(F(l.rdt), a.a, F(l.rcf), F(l.rcb), drdt, pAr, Hs,
+                                                            (int)R, B * Hs);
         k_review_group<<<dim3(R, B), 256, 0, st>>>(F(l.drB), drBg, Hs, S, G);
     }
     const size_t lds_dx =
