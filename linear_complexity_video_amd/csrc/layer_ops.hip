@@ -37,8 +37,9 @@ __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); 
 constexpr int NT_NORM = 128;
 
 // One token row per block: g = y * silu(z) over the row's C channels, then per group of gs channels
-// out = g / sqrt(mean(g^2) + eps) * w, written over z (bf16). Two passes over the row: the group sums,
-// then the normalised values. gs is a multiple of 8, so no 16-byte piece straddles two groups.
+// out = g / sqrt(mean(g^2) + eps) * w, written over z (bf16). Two passes over the row (rows wider than
+// the one-pass kernel's registers hold): the group sums, then the normalised values. gs is a multiple of
+// 8, so no 16-byte piece straddles two groups.
 __global__ __launch_bounds__(NT_NORM) void k_gated_norm(const bf16_t *__restrict__ y, bf16_t *__restrict__ z,
                                                         const float *__restrict__ w, int C, int G, float eps)
 {
@@ -86,6 +87,74 @@ __global__ __launch_bounds__(NT_NORM) void k_gated_norm(const bf16_t *__restrict
     }
 }
 
+// The same in one pass for rows of at most NP * NT_NORM 16-byte pieces: the row's y and z stay in registers
+// between the group sums and the output, so each row is read once.
+template <int NP>
+__global__ __launch_bounds__(NT_NORM) void k_gated_norm_1pass(const bf16_t *__restrict__ y, bf16_t *__restrict__ z,
+                                                              const float *__restrict__ w, int C, int G, float eps)
+{
+    __shared__ float s_part[NT_NORM / 64];
+    __shared__ float s_rs[64];
+    const size_t row = blockIdx.x;
+    const u32x4 *yr = (const u32x4 *)(y + row * C);
+    u32x4 *zr = (u32x4 *)(z + row * C);
+    const int npc = C / 8, gpc = npc / G;
+    u32x4 vy[NP], vz[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int k = threadIdx.x + NT_NORM * j;
+        const int kk = k < npc ? k : 0;  // unconditional loads; pieces past the row are not used
+        vy[j] = yr[kk];
+        vz[j] = zr[kk];
+    }
+    float sq[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        float fy[8], fz[8];
+        unpack8(vy[j], fy);
+        unpack8(vz[j], fz);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float gv = fy[e] * silu(fz[e]);
+            acc += gv * gv;
+        }
+        sq[j] = threadIdx.x + NT_NORM * j < npc ? acc : 0.f;
+    }
+    for (int gi = 0; gi < G; ++gi) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) acc += (threadIdx.x + NT_NORM * j) / gpc == gi ? sq[j] : 0.f;
+        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float t = 0.f;
+            for (int k = 0; k < NT_NORM / 64; ++k) t += s_part[k];
+            s_rs[gi] = rsqrtf(t / (float)(gpc * 8) + eps);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int k = threadIdx.x + NT_NORM * j;
+        if (k < npc) {
+            float fy[8], fz[8];
+            unpack8(vy[j], fy);
+            unpack8(vz[j], fz);
+            const float rs = s_rs[k / gpc];
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = fy[2 * e] * silu(fz[2 * e]) * rs * w[8 * k + 2 * e];
+                const float b = fy[2 * e + 1] * silu(fz[2 * e + 1]) * rs * w[8 * k + 2 * e + 1];
+                o[e] = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+            }
+            zr[k] = o;
+        }
+    }
+}
+
 } // namespace
 
 hipError_t layer_softplus_bias(float *dt, const float *bias, int64_t tokens, int nheads, hipStream_t st)
@@ -100,7 +169,17 @@ hipError_t layer_gated_norm(const void *y, void *z, const float *w, int64_t toke
                             float eps, hipStream_t st)
 {
     if (tokens == 0) return hipSuccess;
-    k_gated_norm<<<(unsigned)tokens, NT_NORM, 0, st>>>((const bf16_t *)y, (bf16_t *)z, w, channels, groups, eps);
+    const int np = (channels / 8 + NT_NORM - 1) / NT_NORM;
+    const bf16_t *yb = (const bf16_t *)y;
+    bf16_t *zb = (bf16_t *)z;
+    if (np <= 2)
+        k_gated_norm_1pass<2><<<(unsigned)tokens, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
+    else if (np <= 5)
+        k_gated_norm_1pass<5><<<(unsigned)tokens, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
+    else if (np <= 8)
+        k_gated_norm_1pass<8><<<(unsigned)tokens, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
+    else
+        k_gated_norm<<<(unsigned)tokens, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
     return hipGetLastError();
 }
 
