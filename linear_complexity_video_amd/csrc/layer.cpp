@@ -34,7 +34,8 @@ struct GemmPlan {
     size_t ws = 0;
 };
 
-std::mutex g_mu;
+std::mutex g_mu;                      // guards the handles and the plan cache
+std::mutex g_call_mu[kMaxDevices];    // one enqueue at a time per device's handle
 hipblasLtHandle_t g_handle[kMaxDevices] = {};
 std::map<GemmKey, GemmPlan> g_plans;
 
@@ -122,8 +123,12 @@ int gemm_rowmajor(const void *A, const void *Wt, void *D, int64_t M, int64_t K, 
         return 1;
     }
     const float alpha = 1.f, beta = accumulate ? 1.f : 0.f;
-    const hipblasStatus_t s = hipblasLtMatmul(g_handle[dev], p->op, &alpha, Wt, p->a, A, p->b, &beta, D, p->d, D,
-                                              p->d, &p->algo, ws, p->ws, st);
+    hipblasStatus_t s;
+    {
+        std::lock_guard<std::mutex> lk(g_call_mu[dev]);
+        s = hipblasLtMatmul(g_handle[dev], p->op, &alpha, Wt, p->a, A, p->b, &beta, D, p->d, D, p->d, &p->algo, ws,
+                            p->ws, st);
+    }
     if (s != HIPBLAS_STATUS_SUCCESS) {
         snprintf(msg, msg_len, "hipblasLtMatmul %lld x %lld x %lld: %s", (long long)M, (long long)K,
                  (long long)Nout, blas_name(s));
