@@ -71,11 +71,18 @@ int plan_for(const GemmKey &key, GemmPlan **out, char *msg, size_t msg_len)
     // Row-major D[M][Nout] = A[M][K] W[K][Nout] is the column-major product D^T = W^T A^T, with W^T the
     // column-major Nout x K matrix stored as W and A^T the column-major K x M matrix stored as A.
     GemmPlan p;
+    auto release = [&]() {
+        if (p.op) hipblasLtMatmulDescDestroy(p.op);
+        if (p.a) hipblasLtMatrixLayoutDestroy(p.a);
+        if (p.b) hipblasLtMatrixLayoutDestroy(p.b);
+        if (p.d) hipblasLtMatrixLayoutDestroy(p.d);
+    };
     const hipDataType dt = key.d_f32 ? HIP_R_32F : HIP_R_16BF;
     if ((s = hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F)) != HIPBLAS_STATUS_SUCCESS ||
         (s = hipblasLtMatrixLayoutCreate(&p.a, HIP_R_16BF, key.Nout, key.K, key.Nout)) != HIPBLAS_STATUS_SUCCESS ||
         (s = hipblasLtMatrixLayoutCreate(&p.b, HIP_R_16BF, key.K, key.M, key.K)) != HIPBLAS_STATUS_SUCCESS ||
         (s = hipblasLtMatrixLayoutCreate(&p.d, dt, key.Nout, key.M, key.Nout)) != HIPBLAS_STATUS_SUCCESS) {
+        release();
         snprintf(msg, msg_len, "hipBLASLt descriptors: %s", blas_name(s));
         return 1;
     }
@@ -90,6 +97,7 @@ int plan_for(const GemmKey &key, GemmPlan **out, char *msg, size_t msg_len)
             HIPBLAS_STATUS_SUCCESS ||
         found < 1) {
         if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+        release();
         snprintf(msg, msg_len, "hipBLASLt has no algorithm for %lld x %lld x %lld (%s)", (long long)key.M,
                  (long long)key.K, (long long)key.Nout, found < 1 ? "none found" : blas_name(s));
         return 1;
