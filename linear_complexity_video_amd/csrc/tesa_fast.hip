@@ -17,8 +17,8 @@
 // only when a later tile's probabilities reach 2^20, so most tiles compute no
 // maximum at all. O leaves through a per-wave LDS staging area as whole row
 // segments, so moving to the next item needs no barrier. Each XCD owns a
-// contiguous range of items, so the query blocks of one window run side by
-// side on one XCD and share its K/V in L2.
+// contiguous range of windows, and the query blocks of one window run side by
+// side on adjacent workgroups of that XCD and share its K/V in L2.
 #include <algorithm>
 
 #include "common.hpp"
@@ -73,27 +73,35 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     __shared__ Smem<DH, WHOLE ? 4 : 3 * MAXW> sm;
     constexpr int DC = DH / 8;  // 16-byte chunks per row
 
-    // Item sequence of this workgroup. Block L runs on XCD L % 8; XCD x owns the
-    // contiguous item range [x per, (x + 1) per), and its workgroups take those
-    // items in turn, so the query blocks of one window run side by side on one
-    // XCD and share its K/V in L2.
+    // Item sequence of this workgroup. Block L runs on XCD L % 8, and XCD x owns a contiguous range of
+    // windows (batch, head, region). When the query blocks of a window (nqb of them) divide the XCD's
+    // workgroups into groups, each group takes a contiguous run of the range's windows, and its members
+    // take one query block of each window, side by side, so that the blocks of a window share its K/V
+    // in L2; which member takes which block rotates from window to window, so that windows with fewer
+    // blocks (the narrower edge regions of shifted windows) spread their work over the whole group.
+    // Otherwise (few windows, many blocks each) the XCD's items (window, query block) are taken in turn.
     const uint32_t wpx = gridDim.x / 8;
-    const uint32_t per = (total + 7) / 8;
-    const uint32_t xcd = blockIdx.x % 8;
-    const uint32_t i_end = min(total, (xcd + 1) * per);
-    uint32_t i_next = xcd * per + blockIdx.x / 8;
+    const uint32_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const uint32_t nwin = total / nqb;
+    const bool grouped = (uint32_t)nqb <= wpx && wpx % nqb == 0 && nwin >= gridDim.x / nqb;
+    const uint32_t G = grouped ? nqb : 1, ng = wpx / G, side = slot % G;
+    const uint32_t per_x = grouped ? (nwin + 7) / 8 : (total + 7) / 8;   // windows or items per XCD
+    const uint32_t x_hi = min(grouped ? nwin : total, (xcd + 1) * per_x);
+    const uint32_t cw = grouped ? (per_x + ng - 1) / ng : 0;            // windows per group
+    const uint32_t x_end = grouped ? min(x_hi, xcd * per_x + (slot / G + 1) * cw) : x_hi;
+    uint32_t u_next = grouped ? min(x_end, xcd * per_x + (slot / G) * cw) : xcd * per_x + slot;
+    const uint32_t u_step = grouped ? 1 : wpx;
 
     const size_t N = (size_t)Tn * Hn * Wn;
     const size_t rowstride = (size_t)nheads * DH;
     const int nreg = nrt * nrh * nrw;
     // Next item of the sequence with queries in it (false when none is left).
     auto next_item = [&](Item &I) -> bool {
-        for (; i_next < i_end; i_next += wpx) {
-            const uint32_t item = i_next;
-            const int qb = item % nqb;
-            const uint32_t rest = item / nqb;
-            const int r = rest % nreg;
-            const int bh = rest / nreg;
+        for (; u_next < x_end; u_next += u_step) {
+            const uint32_t win = grouped ? u_next : u_next / nqb;
+            const int qb = grouped ? (int)((side + u_next) % G) : (int)(u_next % nqb);
+            const int r = win % nreg;
+            const int bh = win / nreg;
             const int h = bh % nheads, b = bh / nheads;
             const int rw = r % nrw, rh = (r / nrw) % nrh, rt = r / (nrw * nrh);
             int t0, t1, h0, h1, w0, w1;
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
             I.w0 = w0;
             I.head_off = ((size_t)b * N) * rowstride + (size_t)h * DH;
             if (I.q_base < I.m) {
-                i_next += wpx;
+                u_next += u_step;
                 return true;
             }
         }
