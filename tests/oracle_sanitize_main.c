@@ -1,5 +1,5 @@
 /*
- * Driver for the sanitizer build of the CPU oracle (test infrastructure).
+ * Main program of the sanitizer build of the CPU oracle (test infrastructure).
  *
  * tests/test_oracle_sanitize.py compiles this file together with
  * oracle/mate_oracle.c under -fsanitize=address,undefined and runs it. Every
