@@ -46,7 +46,7 @@ namespace {
 using ssd::k_cb;
 using ssd::k_chunk_states;
 using ssd::k_pool;
-using ssd::k_prep_dt;
+using ssd::prep_dt;
 using ssd::k_state_pass;
 
 constexpr int NTB = 256;  // threads per workgroup
@@ -1515,8 +1515,7 @@ hipError_t run_backward(const SsdProblem &p, const SsdGradArgs &a, void *ws, hip
                                                                         p.pool_w, p.order);
         k_pool<float, float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h,
                                                                           p.pool_w, p.order);
-        k_prep_dt<false><<<dim3(l.nchR, (Hs + 63) / 64, B), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1,
-                                                                         R);
+        prep_dt<false>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1, R, l.nchR, B, st);
         k_chunk_states<float, false, false><<<dim3(l.nchR, Hs, B), 256, states_lds, st>>>(
             rx, rB, rdtT, rcsT, a.a, rSf, rSb, Hs, P, S, G, R, Rpad, Q, 0, 1, 1, R);
         k_state_pass<<<dim3((P * S + 255) / 256, Hs, B), 256, 0, st>>>(rSf, rSb, rcsT, nullptr, nullptr, h0f, h0b,
@@ -1530,8 +1529,7 @@ hipError_t run_backward(const SsdProblem &p, const SsdGradArgs &a, void *ws, hip
         drdt = F(l.drdt);
         pAr = F(l.pAr);
     }
-    k_prep_dt<true><<<dim3(l.nch, (Hs + 63) / 64, B), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q, p.order, T,
-                                                                    H, W);
+    prep_dt<true>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q, p.order, T, H, W, l.nch, B, st);
     if constexpr (std::is_same<E, bf16_t>::value) {
         if (bwd_mfma(p)) {
             if (S == 64) return run_chunks_mfma<64>(p, a, l, w, rinv, h0f, h0b, Gf0, Gb0, drx, drdt, drBg, pAr, st);

@@ -21,37 +21,49 @@ __device__ __forceinline__ uint32_t seq_row(uint32_t i, int order, uint32_t T, u
 // dt * A. Positions >= L are zero (exact no-ops of the recurrence). The rows of
 // a chunk come from `perm` when given (scan position -> canonical token), else
 // from the RMS index (PERM) or the identity.
-// grid (nchunks, ceil(nheads / 64), batch), 256 threads; Q <= 128.
-template <bool PERM>
-__global__ __launch_bounds__(256) void k_prep_dt(const float *__restrict__ dt, const float *__restrict__ A,
-                                                 float *__restrict__ dtT, float *__restrict__ csT, int nheads,
-                                                 uint32_t L, uint32_t Lpad, int Q, int order, uint32_t T,
-                                                 uint32_t H, uint32_t W, const uint32_t *__restrict__ perm = nullptr)
+// grid (nchunks, ceil(nheads / kPrepHeads), batch), kPrepThreads threads; Q <= 128. VEC: the heads of
+// a token row are read as 16-byte pieces (nheads a multiple of 4, dt 16-byte aligned).
+constexpr int kPrepHeads = 128, kPrepThreads = 512;
+template <bool PERM, bool VEC>
+__global__ __launch_bounds__(kPrepThreads) void k_prep_dt(const float *__restrict__ dt, const float *__restrict__ A,
+                                                          float *__restrict__ dtT, float *__restrict__ csT, int nheads,
+                                                          uint32_t L, uint32_t Lpad, int Q, int order, uint32_t T,
+                                                          uint32_t H, uint32_t W, const uint32_t *__restrict__ perm)
 {
-    __shared__ float sdt[kMaxQ][65];
+    __shared__ float sdt[kMaxQ][kPrepHeads + 1];
     __shared__ uint32_t srow[kMaxQ];
     const uint32_t c = blockIdx.x, b = blockIdx.z;
-    const int h0 = blockIdx.y * 64;
+    const int h0 = blockIdx.y * kPrepHeads, nh = min(kPrepHeads, nheads - h0);
+    const int tid = threadIdx.x;
     // The chunk's rows first, so that the dt loads below depend on no other load and
     // can all be in flight together.
-    for (int u = threadIdx.x; u < Q; u += 256) {
+    for (int u = tid; u < Q; u += kPrepThreads) {
         const uint32_t i = c * Q + u;
         srow[u] = i < L ? (perm ? perm[i] : seq_row<PERM>(i, order, T, H, W)) : ~0u;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int k = threadIdx.x; k < Q * 64; k += 256) {
-        const int u = k >> 6, hh = k & 63, h = h0 + hh;
+    // Each thread keeps one column (a 16-byte piece, or one head) and walks the rows.
+    const int ncol = VEC ? nh / 4 : nh;
+    const int rpp = kPrepThreads / ncol, j = tid % ncol;  // rows per pass (ncol <= kPrepThreads)
+    for (int u = tid / ncol; u < Q && tid < rpp * ncol; u += rpp) {
         const uint32_t row = srow[u];
-        float v = 0.f;
-        if (row != ~0u && h < nheads) v = dt[((size_t)b * L + row) * nheads + h];
-        sdt[u][hh] = v;
+        const float *src = dt + ((size_t)b * L + (row != ~0u ? row : 0u)) * nheads + h0;
+        if constexpr (VEC) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row != ~0u) v = *(const float4 *)(src + 4 * j);
+            sdt[u][4 * j] = v.x;
+            sdt[u][4 * j + 1] = v.y;
+            sdt[u][4 * j + 2] = v.z;
+            sdt[u][4 * j + 3] = v.w;
+        } else {
+            sdt[u][j] = row != ~0u ? src[j] : 0.f;
+        }
     }
     __syncthreads();
     // One wave per head at a time: lane l owns positions 2l and 2l + 1; a wave-wide
     // inclusive scan of the lane sums gives the cumulative sums.
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int hh = wave; hh < 64 && h0 + hh < nheads; hh += 4) {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int hh = wave; hh < nh; hh += kPrepThreads / 64) {
         const int h = h0 + hh;
         const float a = A[h];
         const int u0 = 2 * lane;
@@ -79,6 +91,19 @@ __global__ __launch_bounds__(256) void k_prep_dt(const float *__restrict__ dt, c
             }
         }
     }
+}
+
+// Launches k_prep_dt for nch chunks of Q positions.
+template <bool PERM>
+inline void prep_dt(const float *dt, const float *A, float *dtT, float *csT, int nheads, uint32_t L, uint32_t Lpad,
+                    int Q, int order, uint32_t T, uint32_t H, uint32_t W, uint32_t nch, uint32_t batch,
+                    hipStream_t st, const uint32_t *perm = nullptr)
+{
+    const dim3 grid(nch, (unsigned)((nheads + kPrepHeads - 1) / kPrepHeads), batch);
+    if (nheads % 4 == 0 && ((uintptr_t)dt & 15) == 0)
+        k_prep_dt<PERM, true><<<grid, kPrepThreads, 0, st>>>(dt, A, dtT, csT, nheads, L, Lpad, Q, order, T, H, W, perm);
+    else
+        k_prep_dt<PERM, false><<<grid, kPrepThreads, 0, st>>>(dt, A, dtT, csT, nheads, L, Lpad, Q, order, T, H, W, perm);
 }
 
 // Whether k_pool_f32x4 applies: 16-byte aligned rows of at most 1024 channels.

@@ -1203,8 +1203,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
     }
     {
         timing::Scope ts_(K_SSD_PREP, st);
-        ssd::k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, Bn), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q,
-                                                                             p.order, T, H, W, perm);
+        ssd::prep_dt<true>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q, p.order, T, H, W, p.nch, Bn, st, perm);
     }
     {
         timing::Scope ts_(K_SSD_CB, st);
@@ -1257,8 +1256,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
         }
         {
             timing::Scope ts_(K_SSD_PREP, st);
-            ssd::k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, Bn), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad,
-                                                                                    Q, 0, 1, 1, R);
+            ssd::prep_dt<false>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1, R, p.nchR, Bn, st);
         }
         const uint64_t ritems = (uint64_t)Bn * Hs;
         {

@@ -30,7 +30,7 @@ using ssd::k_cb;
 using ssd::k_chunk_states;
 using ssd::k_state_pass;
 using ssd::k_pool;
-using ssd::k_prep_dt;
+using ssd::prep_dt;
 using ssd::k_pool_f32x4;
 using ssd::pool_f32x4_ok;
 using ssd::seq_row;
@@ -228,7 +228,7 @@ static hipError_t run_portable(const SsdProblem &p, const SsdArgs &a, void *ws, 
         }
         {
             timing::Scope ts_(K_SSD_PREP, st);
-            k_prep_dt<false><<<dim3(p.nchR, (Hs + 63) / 64, B), 256, 0, st>>>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1, R);
+            prep_dt<false>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1, R, p.nchR, B, st);
         }
         {
             timing::Scope ts_(K_SSD_STATES, st);
@@ -244,7 +244,7 @@ static hipError_t run_portable(const SsdProblem &p, const SsdArgs &a, void *ws, 
     }
     {
         timing::Scope ts_(K_SSD_PREP, st);
-        k_prep_dt<true><<<dim3(p.nch, (Hs + 63) / 64, B), 256, 0, st>>>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q, p.order, T, H, W);
+        prep_dt<true>(a.dt, a.a, dtT, csT, Hs, N, Lpad, Q, p.order, T, H, W, p.nch, B, st);
     }
     {
         timing::Scope ts_(K_SSD_STATES, st);
