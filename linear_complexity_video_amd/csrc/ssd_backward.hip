@@ -1509,12 +1509,27 @@ hipError_t run_backward(const SsdProblem &p, const SsdGradArgs &a, void *ws, hip
         h0b = F(l.h0b);
         const uint32_t Rpad = (uint32_t)(l.nchR * Q);
         const int64_t Cx = (int64_t)Hs * P, Cbw = (int64_t)G * S;
-        k_pool<E, float><<<dim3((Cx + 255) / 256, R, B), 256, 0, st>>>(x, rx, Cx, T, H, W, p.pool_t, p.pool_h, p.pool_w,
-                                                                       p.order);
-        k_pool<E, float><<<dim3((Cbw + 255) / 256, R, B), 256, 0, st>>>(Bm, rB, Cbw, T, H, W, p.pool_t, p.pool_h,
-                                                                        p.pool_w, p.order);
-        k_pool<float, float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h,
-                                                                          p.pool_w, p.order);
+        // bf16 rows of a multiple of 8 channels pool 8 channels per thread, fp32 rows of a multiple of 4
+        // (16-byte aligned) 4 per thread; anything else one channel per thread
+        auto pool_rows = [&](const E *src, float *dst, int64_t C) {
+            if constexpr (std::is_same<E, bf16_t>::value) {
+                if (C % 8 == 0 && ((uintptr_t)src & 15) == 0) {
+                    ssd::k_pool8<float><<<dim3((unsigned)((C + 2047) / 2048), R, B), 256, 0, st>>>(
+                        src, dst, C, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+                    return;
+                }
+            }
+            k_pool<E, float><<<dim3((unsigned)((C + 255) / 256), R, B), 256, 0, st>>>(src, dst, C, T, H, W, p.pool_t,
+                                                                                    p.pool_h, p.pool_w, p.order);
+        };
+        pool_rows(x, rx, Cx);
+        pool_rows(Bm, rB, Cbw);
+        if (ssd::pool_f32x4_ok(a.dt, Hs))
+            ssd::k_pool_f32x4<<<dim3(R, B), ssd::kPoolF4Threads, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w,
+                                                         p.order);
+        else
+            k_pool<float, float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t,
+                                                                              p.pool_h, p.pool_w, p.order);
         prep_dt<false>(rdt, a.a, rdtT, rcsT, Hs, R, Rpad, Q, 0, 1, 1, R, l.nchR, B, st);
         k_chunk_states<float, false, false><<<dim3(l.nchR, Hs, B), 256, states_lds, st>>>(
             rx, rB, rdtT, rcsT, a.a, rSf, rSb, Hs, P, S, G, R, Rpad, Q, 0, 1, 1, R);

@@ -112,17 +112,20 @@ inline bool pool_f32x4_ok(const float *src, int C)
     return C % 4 == 0 && C / 4 <= 256 && ((uintptr_t)src & 15) == 0;
 }
 
-// Average pool of fp32 rows, 4 channels per thread, several pooled tokens' rows
-// read in parallel per block and reduced through LDS. C must be a multiple of 4
-// and C / 4 <= 256. out[b][j][ch] with j in RMS order `order` of the pooled grid.
-// grid (R, batch), 256 threads.
+// Average pool of fp32 rows, 4 channels per thread, many pooled tokens' rows
+// read in parallel per block and reduced through LDS in two rounds. C must be a
+// multiple of 4 and C / 4 <= 256. out[b][j][ch] with j in RMS order `order` of
+// the pooled grid. grid (R, batch), kPoolF4Threads threads.
+constexpr int kPoolF4Threads = 1024;
 template <typename F = float>
-__global__ __launch_bounds__(256) void k_pool_f32x4(const F *__restrict__ src, F *__restrict__ out, int C,
-                                                    uint32_t Tn, uint32_t Hn, uint32_t Wn, int pt, int ph, int pw,
-                                                    int order)
+__global__ __launch_bounds__(kPoolF4Threads) void k_pool_f32x4(const F *__restrict__ src, F *__restrict__ out, int C,
+                                                               uint32_t Tn, uint32_t Hn, uint32_t Wn, int pt, int ph,
+                                                               int pw, int order)
 {
-    __shared__ float4 part[256];
-    const int cg = C / 4, rp = 256 / cg;  // channel groups; rows in flight
+    constexpr int NT = kPoolF4Threads, NP = 8;  // threads; partial sums per channel group after round one
+    __shared__ float4 part[NT];
+    __shared__ float4 part2[NP * 256];
+    const int cg = C / 4, rp = NT / cg;  // channel groups; rows in flight
     const int r = threadIdx.x / cg, g = threadIdx.x % cg;
     const uint32_t j = blockIdx.x, b = blockIdx.y, R = gridDim.x;
     const uint32_t Tp = Tn / pt, Hp = Hn / ph, Wp = Wn / pw;
@@ -141,10 +144,22 @@ __global__ __launch_bounds__(256) void k_pool_f32x4(const F *__restrict__ src, F
     }
     part[threadIdx.x] = acc;
     __syncthreads();
+    // round one: np2 partial sums per channel group, each over every np2-th row slot (np2 cg <= NT)
+    const int np2 = min(NP, NT / cg);
+    if (threadIdx.x < np2 * cg) {
+        const int gg = threadIdx.x % cg, k0 = threadIdx.x / cg;
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k = k0; k < rp; k += np2) {
+            const float4 v = part[k * cg + gg];
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
+        part2[threadIdx.x] = s;
+    }
+    __syncthreads();
     if (threadIdx.x < cg) {
-        float4 s = part[threadIdx.x];
-        for (int k = 1; k < rp; ++k) {
-            const float4 v = part[k * cg + threadIdx.x];
+        float4 s = part2[threadIdx.x];
+        for (int k = 1; k < np2; ++k) {
+            const float4 v = part2[k * cg + threadIdx.x];
             s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
         }
         const float inv = 1.f / (float)cnt;

@@ -1248,7 +1248,7 @@ hipError_t run(const SsdProblem &p, const SsdArgs &a, void *ws, hipStream_t st)
         {
             timing::Scope ts_(K_SSD_POOL, st);
             if (ssd::pool_f32x4_ok(a.dt, Hs))
-                ssd::k_pool_f32x4<<<dim3(R, Bn), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w,
+                ssd::k_pool_f32x4<<<dim3(R, Bn), ssd::kPoolF4Threads, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w,
                                                               p.order);
             else
                 ssd::k_pool<float, float><<<dim3((Hs + 255) / 256, R, Bn), 256, 0, st>>>(

@@ -221,7 +221,7 @@ static hipError_t run_portable(const SsdProblem &p, const SsdArgs &a, void *ws, 
         {
             timing::Scope ts_(K_SSD_POOL, st);
             if (pool_f32x4_ok(a.dt, Hs))
-                k_pool_f32x4<<<dim3(R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+                k_pool_f32x4<<<dim3(R, B), ssd::kPoolF4Threads, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
             else
                 k_pool<float, float><<<dim3((Hs + 255) / 256, R, B), 256, 0, st>>>(a.dt, rdt, Hs, T, H, W, p.pool_t,
                                                                                   p.pool_h, p.pool_w, p.order);
