@@ -8,7 +8,8 @@
 // (double buffered, both in their natural row layout; the V^T operand is read
 // with the gfx950 LDS transpose read), loaded two tiles ahead through two
 // register sets, and the tile stream runs on across items: the next item's
-// first tiles load during the current one's last, its Q rows right after.
+// first tiles load during the current one's last, and its Q rows once the
+// last tile's score products are issued (the Q fragments are then free).
 // Per tile each wave computes S^T = K Q^T, so that a lane holds one query's
 // scores and the softmax needs only one cross-lane exchange; exp'd
 // P^T is then directly the B operand of O^T += V^T P^T, and O^T again has one
@@ -154,6 +155,14 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
             qf[kb] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 16 * kb + 8 * half));
     };
 
+    // Items run in sequence; item number s keeps its window table in table s % 3.
+    Item I, J, K;
+    bool has_j = false, has_k = false;
+    int rt = 0;                 // table of the current item
+    auto nxt = [](int t) { return t == 2 ? 0 : t + 1; };
+    // The next item's Q rows (or the current ones again when none is left: the load is always issued).
+    auto load_q_next = [&](bf16x8 (&qf)[DH / 16]) { load_q(has_j ? J : I, has_j ? nxt(rt) : rt, qf); };
+
     // Tile loader: K and V rows as 16-byte chunks, natural layout.
     constexpr int KCH = KT * DC;                  // chunks per tile
     constexpr int KPER = KCH / 512;               // per thread
@@ -209,8 +218,8 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
     };
 
     // One key tile of the current item from LDS buffer b: S^T, softmax, O^T.
-    auto compute = [&](const Item &X, int kt, int b, const bf16x8 (&qf)[DH / 16], f32x16 (&acc)[DH / 32],
-                       float &mrun, float &lrun) {
+    auto compute = [&](const Item &X, int kt, int b, bf16x8 (&qf)[DH / 16], f32x16 (&acc)[DH / 32],
+                       float &mrun, float &lrun, bool last) {
         f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
@@ -219,6 +228,9 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
                 const bf16x8 a = *(const bf16x8 *)&sm.k[b][32 * sub + col][16 * kb + 8 * half];
                 s[sub] = mfma(a, qf[kb], s[sub]);
             }
+        // After the item's last score products, the next item's Q rows load into the fragments
+        // while this tile's softmax and P V run.
+        if (last) load_q_next(qf);
         // Keys past the window (only in the last, ragged tile) get -inf.
         if (kt * KT + KT > X.m) {
 #pragma unroll
@@ -259,16 +271,11 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
         return n + (n & 1);
     };
 
-    // Items run in sequence; item number s keeps its window table in table s % 3.
     // The table (and the decode) of the item after the next one is made during
     // the current item's first tile pair, after that pair's first barrier: by
     // then every wave has finished the item that used the same table.
-    Item I, J, K;
     if (!next_item(I)) return;  // uniform over the workgroup
-    bool has_j = next_item(J);
-    bool has_k = false;
-    int rt = 0;                 // table of the current item
-    auto nxt = [](int t) { return t == 2 ? 0 : t + 1; };
+    has_j = next_item(J);
     build_table(I, rt);
     if (has_j) build_table(J, nxt(rt));
     __syncthreads();
@@ -296,10 +303,11 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
 #pragma unroll
         for (int i = 0; i < DH / 32; ++i) acc[i] = f32x16{};
         float mrun = 0.f, lrun = 0.f;
+        const int last_kt = (I.m + KT - 1) / KT - 1;  // the item's last tile with keys
         for (int kt = 0; kt < n; kt += 2) {
             // even tile kt (buffer 0); tile kt + 1 waits in set 1, tile kt + 2 goes to set 0
             fetch_pos(kt + 2, n, k0, v0);
-            if (wave_active && kt * KT < I.m) compute(I, kt, 0, qf, acc, mrun, lrun);
+            if (wave_active && kt * KT < I.m) compute(I, kt, 0, qf, acc, mrun, lrun, kt == last_kt);
             stash(1, k1, v1);
             __syncthreads();
             // odd tile kt + 1 (buffer 1); tile kt + 2 waits in set 0, tile kt + 3 goes to set 1
@@ -308,13 +316,12 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
                 has_k = next_item(K);
                 if (has_k) build_table(K, nxt(nxt(rt)));
             }
-            if (wave_active && (kt + 1) * KT < I.m) compute(I, kt + 1, 1, qf, acc, mrun, lrun);
+            if (wave_active && (kt + 1) * KT < I.m) compute(I, kt + 1, 1, qf, acc, mrun, lrun, kt + 1 == last_kt);
             stash(0, k0, v0);
             __syncthreads();
         }
-        // The next item's Q rows (or the current ones again: the load is always issued),
-        // straight into the fragments this item no longer reads.
-        load_q(has_j ? J : I, has_j ? nxt(rt) : rt, qf);
+        // A wave with no queries in this item loads the next item's Q rows here.
+        if (!wave_active) load_q_next(qf);
 
         // O leaves through this wave's staging area, in rounds of RD value dims
         // (16-byte chunks XOR-swizzled by row against bank conflicts): all rows are
