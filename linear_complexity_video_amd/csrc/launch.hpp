@@ -110,9 +110,10 @@ struct LayerDims {
     int t_inner;     // TESA heads * head size (q, k, v, o)
 };
 
-// Byte offsets of the layer's intermediates inside its workspace (256-byte aligned).
+// Byte offsets of the layer's intermediates inside its workspace (256-byte aligned). The y region first
+// holds the fp32 output of the joint B, C and dt projection (bcd: its weights side by side).
 struct LayerLayout {
-    size_t x, z, b, c, dt, q, k, v, y, o, core, blas, total;
+    size_t x, z, b, c, dt, q, k, v, y, o, bcd, core, blas, total;
 };
 
 constexpr size_t kGemmWorkspace = (size_t)64 << 20;  // reserved for hipBLASLt inside the layer's workspace
@@ -124,7 +125,10 @@ LayerLayout layer_layout(const LayerDims &d, size_t core_ws);
 int gemm_rowmajor(const void *A, const void *W, void *D, int64_t M, int64_t K, int64_t Nout, bool d_f32,
                   bool accumulate, void *ws, size_t ws_bytes, hipStream_t st, char *msg, size_t msg_len);
 
-hipError_t layer_softplus_bias(float *dt, const float *bias, int64_t tokens, int nheads, hipStream_t st);
+// The joint projection's rows [B | C | dt] (fp32, bc + bc + nheads wide) split into B and C (bf16) and
+// dt = softplus(raw + bias) (fp32).
+hipError_t layer_split_bcdt(const float *bcd, void *b, void *c, float *dt, const float *bias, int64_t tokens, int bc,
+                            int nheads, hipStream_t st);
 hipError_t layer_gated_norm(const void *y, void *z, const float *w, int64_t tokens, int channels, int groups,
                             float eps, hipStream_t st);
 

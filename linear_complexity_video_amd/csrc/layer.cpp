@@ -4,6 +4,7 @@
 // runs.
 #include <hipblaslt/hipblaslt.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <map>
 #include <mutex>
@@ -163,8 +164,10 @@ LayerLayout layer_layout(const LayerDims &d, size_t core_ws)
     l.q = take(n * d.t_inner * 2);
     l.k = take(n * d.t_inner * 2);
     l.v = take(n * d.t_inner * 2);
-    l.y = take(n * d.inner * 2);
+    const size_t nbcd = (size_t)2 * d.bc + d.nheads;  // joint projection width
+    l.y = take(std::max(n * d.inner * 2, n * nbcd * 4));
     l.o = take(n * d.t_inner * 2);
+    l.bcd = take((size_t)d.d_model * nbcd * 2);
     l.core = take(core_ws);
     l.blas = take(kGemmWorkspace);
     l.total = off;

@@ -1,8 +1,10 @@
-// Per-token operations of one MATE layer around the core: dt from its
-// projection (bias, then softplus) and the MA branch's gated RMS norm. The
-// pages give neither; both follow the Mamba2 block the MA branch is built from
-// (softplus keeps dt positive; the output is normalised after gating with
-// silu(z)).
+// Per-token operations of one MATE layer around the core: B, C and dt from
+// their joint projection (dt: bias, then softplus) and the MA branch's gated
+// RMS norm. The pages give neither the dt activation nor the norm; both follow
+// the Mamba2 block the MA branch is built from (softplus keeps dt positive;
+// the output is normalised after gating with silu(z)).
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -12,14 +14,43 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// dt[n][h] = softplus(raw[n][h] + bias[h]), in place, fp32. softplus(v) = max(v, 0) + log1p(exp(-|v|)).
-__global__ __launch_bounds__(256) void k_softplus_bias(float *__restrict__ dt, const float *__restrict__ bias,
-                                                       int64_t total, int nheads)
+// Splits the joint projection's fp32 rows [B | C | dt] (width 2 bc + nheads): B and C rounded to bf16, dt
+// as softplus(raw + bias[h]) in fp32. Threads take columns (VEC: groups of 4, which never straddle two of
+// the parts when bc and nheads are multiples of 4) of several rows at a time; blocks stride over the rows.
+__device__ __forceinline__ float softplus(float u) { return fmaxf(u, 0.f) + log1pf(__expf(-fabsf(u))); }
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_split_bcdt(const float *__restrict__ src, bf16_t *__restrict__ b,
+                                                    bf16_t *__restrict__ c, float *__restrict__ dt,
+                                                    const float *__restrict__ bias, int64_t rows, int bc, int nheads)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    const float v = dt[i] + bias[i % nheads];
-    dt[i] = fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v)));
+    const int w = 2 * bc + nheads, ncol = VEC ? w / 4 : w;
+    const bool wide = ncol >= 256;
+    const int rpp = wide ? 1 : 256 / ncol;  // rows per pass
+    const int r_in = wide ? 0 : threadIdx.x / ncol, c0 = wide ? threadIdx.x : threadIdx.x % ncol;
+    if (r_in >= rpp) return;
+    for (int64_t row = (int64_t)blockIdx.x * rpp + r_in; row < rows; row += (int64_t)gridDim.x * rpp)
+        for (int cc = c0; cc < ncol; cc += wide ? 256 : ncol) {
+            if constexpr (VEC) {
+                const int col = 4 * cc;
+                const float4 v = *(const float4 *)(src + row * w + col);
+                if (col < 2 * bc) {
+                    bf16_t *dst = col < bc ? b + row * bc + col : c + row * bc + col - bc;
+                    *(uint2 *)dst = make_uint2((uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                                               (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16));
+                } else {
+                    const int h = col - 2 * bc;
+                    const float4 bi = *(const float4 *)(bias + h);
+                    *(float4 *)(dt + row * nheads + h) =
+                        make_float4(softplus(v.x + bi.x), softplus(v.y + bi.y), softplus(v.z + bi.z), softplus(v.w + bi.w));
+                }
+            } else {
+                const float v = src[row * w + cc];
+                if (cc < bc) b[row * bc + cc] = f32_to_bf16(v);
+                else if (cc < 2 * bc) c[row * bc + cc - bc] = f32_to_bf16(v);
+                else dt[row * nheads + cc - 2 * bc] = softplus(v + bias[cc - 2 * bc]);
+            }
+        }
 }
 
 // Eight bf16 values of a 16-byte piece as floats.
@@ -157,11 +188,18 @@ __global__ __launch_bounds__(NT_NORM) void k_gated_norm_1pass(const bf16_t *__re
 
 } // namespace
 
-hipError_t layer_softplus_bias(float *dt, const float *bias, int64_t tokens, int nheads, hipStream_t st)
+hipError_t layer_split_bcdt(const float *bcd, void *b, void *c, float *dt, const float *bias, int64_t tokens, int bc,
+                            int nheads, hipStream_t st)
 {
-    const int64_t total = tokens * nheads;
-    if (total == 0) return hipSuccess;
-    k_softplus_bias<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(dt, bias, total, nheads);
+    if (tokens == 0) return hipSuccess;
+    const bool vec = bc % 4 == 0 && nheads % 4 == 0 && ((uintptr_t)bias & 15) == 0;
+    const int w = 2 * bc + nheads, ncol = vec ? w / 4 : w;
+    const int64_t rpp = ncol >= 256 ? 1 : 256 / ncol;
+    const int64_t blocks = std::min<int64_t>((tokens + rpp - 1) / rpp, 8192);
+    if (vec)
+        k_split_bcdt<true><<<(unsigned)blocks, 256, 0, st>>>(bcd, (bf16_t *)b, (bf16_t *)c, dt, bias, tokens, bc, nheads);
+    else
+        k_split_bcdt<false><<<(unsigned)blocks, 256, 0, st>>>(bcd, (bf16_t *)b, (bf16_t *)c, dt, bias, tokens, bc, nheads);
     return hipGetLastError();
 }
 

@@ -527,16 +527,33 @@ mate_status mate_layer(const void *h, void *out, const mate_layer_weights *w, co
         int64_t n;
         bool f32;
     };
-    const Proj ins[] = {{w->w_x, x, dims.inner, false},   {w->w_z, z, dims.inner, false},
-                        {w->w_b, b, dims.bc, false},      {w->w_c, c, dims.bc, false},
-                        {w->w_dt, dt, dims.nheads, true}, {w->w_q, q, dims.t_inner, false},
-                        {w->w_k, k, dims.t_inner, false}, {w->w_v, v, dims.t_inner, false}};
+    const Proj ins[] = {{w->w_x, x, dims.inner, false},       {w->w_z, z, dims.inner, false},
+                        {w->w_q, q, dims.t_inner, false},     {w->w_k, k, dims.t_inner, false},
+                        {w->w_v, v, dims.t_inner, false}};
     for (const Proj &pj : ins)
         if (mate::gemm_rowmajor(h, pj.wm, pj.dst, M, K, pj.n, pj.f32, false, blas, mate::kGemmWorkspace, sh, msg,
                                 sizeof(msg)))
             return fail(MATE_ERR_DEVICE, "layer in-projection: %s", msg);
-    hipError_t e = mate::layer_softplus_bias(dt, w->dt_bias, M, dims.nheads, sh);
-    if (e != hipSuccess) return device_fail(e, "layer: dt");
+    // B, C and dt from one GEMM over their weights side by side (the narrow projections read h once), its
+    // fp32 rows in the y region (free until the scan), then split.
+    {
+        const size_t nb = (size_t)2 * dims.bc + dims.nheads, e2 = 2;
+        char *wb = ws + l.bcd;
+        hipError_t e = hipMemcpy2DAsync(wb, nb * e2, w->w_b, dims.bc * e2, dims.bc * e2, K, hipMemcpyDeviceToDevice, sh);
+        if (e == hipSuccess)
+            e = hipMemcpy2DAsync(wb + dims.bc * e2, nb * e2, w->w_c, dims.bc * e2, dims.bc * e2, K,
+                                 hipMemcpyDeviceToDevice, sh);
+        if (e == hipSuccess)
+            e = hipMemcpy2DAsync(wb + 2 * dims.bc * e2, nb * e2, w->w_dt, dims.nheads * e2, dims.nheads * e2, K,
+                                 hipMemcpyDeviceToDevice, sh);
+        if (e != hipSuccess) return device_fail(e, "layer: joint projection weights");
+        if (mate::gemm_rowmajor(h, wb, y, M, K, (int64_t)nb, true, false, blas, mate::kGemmWorkspace, sh, msg,
+                                sizeof(msg)))
+            return fail(MATE_ERR_DEVICE, "layer in-projection (B, C, dt): %s", msg);
+        e = mate::layer_split_bcdt((const float *)y, b, c, dt, w->dt_bias, M, dims.bc, dims.nheads, sh);
+        if (e != hipSuccess) return device_fail(e, "layer: B, C and dt");
+    }
+    hipError_t e;
     const mate::TesaArgs ta{q, k, v, o};
     e = tfast ? mate::tesa_fast(tp, ta, sh) : mate::tesa_portable(tp, ta, sh);
     if (e != hipSuccess) return device_fail(e, "layer: tesa launch");

@@ -255,14 +255,17 @@ def test_noalloc_scan_validation_and_scratch_limit():
 
 def test_layer_validation_rejects_before_launch():
     """mate_layer checks pointers, alignment, both descriptors (bf16 only), d_model and the workspace before
-    any device call; its workspace size is the intermediates plus the scan's workspace and 64 MiB."""
+    any device call; its workspace size is the intermediates, the joint B/C/dt weights, the scan's workspace
+    and 64 MiB."""
     lib = B.lib()
     g = B.Grid(1, 8, 16, 16)
     ld, sd, td = B.layer_descs((1, 8, 16, 16), 256, dict(nheads=16, headdim=64, d_state=64, chunk=64),
                                dict(nheads=8, headdim=64, window=(4, 8, 8)))
     need = lib.mate_layer_workspace_size(g, ctypes.byref(ld), ctypes.byref(sd), ctypes.byref(td))
     n = 8 * 16 * 16
-    inter = n * (3 * 1024 * 2 + 2 * 64 * 2 + 16 * 4 + 4 * 512 * 2)
+    nbcd = 2 * 64 + 16  # the joint B, C and dt projection's width
+    y_region = max(1024 * 2, nbcd * 4)  # y, which first holds the joint projection's fp32 rows
+    inter = n * (2 * 1024 * 2 + y_region + 2 * 64 * 2 + 16 * 4 + 4 * 512 * 2) + 256 * nbcd * 2
     scan = lib.mate_bissd_workspace_size(g, ctypes.byref(sd))
     assert inter + scan + (64 << 20) <= need <= inter + scan + (64 << 20) + 16 * 256
     w = B.LayerWeights(*([0x200000] * len(B.LAYER_WEIGHTS)))
