@@ -373,8 +373,9 @@ typedef struct {
     float norm_eps;  /* eps of the gated RMS norm, >= 0 */
 } mate_layer_desc;
 
-/* Bytes of workspace mate_layer needs: the intermediates of both branches,
- * the scan's workspace and 64 MiB for the GEMMs (0 on invalid arguments). */
+/* Bytes of workspace mate_layer needs: the intermediates of both branches, a
+ * copy of w_b, w_c and w_dt side by side (B, C and dt come from one GEMM), the
+ * scan's workspace and 64 MiB for the GEMMs (0 on invalid arguments). */
 size_t mate_layer_workspace_size(mate_grid g, const mate_layer_desc *ld, const mate_ssd_desc *sd,
                                  const mate_tesa_desc *td);
 
