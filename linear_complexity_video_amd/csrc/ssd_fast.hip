@@ -625,22 +625,24 @@ void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, 
     float logD = 0.f;  // sum of dt*A over the chunks right of the current one
 
     auto step = [&](Stage &cur, u32x4 (&bc)[KU], u32x4 (&bn)[KU], int c) {
-        {
-            // Backward state entering chunk c from the right, in accumulator order (see hb_piece).
+        // Backward state entering chunk c from the right, in accumulator order (see hb_piece): packed
+        // now, stored once the chunk's first MFMAs are issued.
+        bf16x8 hbv[TT][2];
+#pragma unroll
+        for (int i = 0; i < TT; ++i)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) hbv[i][q][e] = (__bf16)accG[i][8 * q + e];
+        auto store_hb = [&]() {
             __bf16 *dst = hb_local + (bh * nch + c) * (size_t)(P * S);
 #pragma unroll
-            for (int i = 0; i < TT; ++i) {
-                const int j = wave * TT + i;
+            for (int i = 0; i < TT; ++i)
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    bf16x8 v8;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v8[e] = (__bf16)accG[i][8 * q + e];
-                    __builtin_nontemporal_store(v8, (bf16x8 *)(dst + ((j * 2 + q) * 64 + lane) * 8));
-                }
-            }
+                for (int q = 0; q < 2; ++q)
+                    __builtin_nontemporal_store(hbv[i][q], (bf16x8 *)(dst + (((wave * TT + i) * 2 + q) * 64 + lane) * 8));
             delta[bh * nch + c] = ex2(logD * LOG2E);  // every thread writes the same value
-        }
+        };
 
         __syncthreads();  // previous chunk's reads of xn and the row-table reads are done
         // The staged values are used from here on (their loads had two steps to complete).
@@ -690,9 +692,6 @@ void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, 
         s_row[tid & (Q - 1)] = pvalid ? pnext : ~0u;
         __syncthreads();
 
-        // B (needed next step) before x (needed in two): waits complete in issue order.
-        fetch_b(bn, max(c - 1, c_lo));
-        fetch(cur, max(c - 2, c_lo));  // near the segment start: issued, unused
         const float dec = ex2(tot_c * LOG2E);
 #pragma unroll
         for (int i = 0; i < TT; ++i) accG[i] *= dec;
@@ -708,6 +707,12 @@ void k_states(const __bf16 *__restrict__ x, const _Float16 *__restrict__ bfrag, 
                 accG[i] = mfma16(afb, xv, accG[i]);
                 accF[i] = mfma16(aff, xv, accF[i]);
             }
+            // The next loads issue while this chunk's MFMAs run (a load waiting for the memory pipeline
+            // holds up only what this wave issues after it): B (needed next step) before x (needed in
+            // two), so that waits complete in issue order.
+            if (kb == 0) store_hb();
+            if (kb == 1) fetch_b(bn, max(c - 1, c_lo));
+            if (kb == 3) fetch(cur, max(c - 2, c_lo));  // near the segment start: issued, unused
         }
         logD += tot_c;
     };
