@@ -805,8 +805,11 @@ __global__ __launch_bounds__(NTB) void k_bwd_states_mfma(const __bf16 *__restric
                                                          uint32_t H, uint32_t W)
 {
     constexpr int LS = S + 8, NT = S / 32, TPW = S / 32;
+    constexpr int LG = 72;  // row pitch of a wave's output staging (64 columns + 8)
+    static_assert(TPW % 2 == 0, "tiles are staged two at a time");
     __shared__ __attribute__((aligned(16))) __bf16 sX[QM * LXM];
-    __shared__ __attribute__((aligned(16))) __bf16 sB[QM * LS];
+    // B rows; after the products, each wave's output staging
+    __shared__ __attribute__((aligned(16))) __bf16 sB[QM * LS > 4 * 32 * LG ? QM * LS : 4 * 32 * LG];
     __shared__ float s_w[2][QM];
     __shared__ uint32_t s_n[QM];
     uint32_t c;
@@ -849,12 +852,23 @@ __global__ __launch_bounds__(NTB) void k_bwd_states_mfma(const __bf16 *__restric
             acc[i] = mfma_bf16(af, frag_tr(sB, LS, k0, 32 * nt), acc[i]);
         }
     }
+    // The wave's tiles are rows 32 mt .. 32 mt + 31 of the output (mt = wave % 2), all S columns: they
+    // leave through LDS, two tiles (64 columns) at a time, as 16-byte row pieces.
+    typedef uint32_t piece __attribute__((ext_vector_type(4)));
+    lds_barrier();  // every wave is done with sX and sB
+    __bf16 *stg = sB + wave * (32 * LG);
+    const int mt = wave & 1;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int tile = (wave & 1) * TPW + i, mt = tile / NT, nt = tile % NT;
+    for (int r = 0; r < TPW / 2; ++r) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            out[(size_t)(32 * mt + acc_row(e, lane)) * S + 32 * nt + (lane & 31)] = (__bf16)acc[i][e];
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) stg[acc_row(e, lane) * LG + 32 * i2 + (lane & 31)] = (__bf16)acc[2 * r + i2][e];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int idx = lane + 64 * k, rr = idx >> 3, pc = idx & 7;
+            *(piece *)(out + (size_t)(32 * mt + rr) * S + 64 * r + 8 * pc) = *(const piece *)(stg + rr * LG + 8 * pc);
+        }
     }
 }
 
