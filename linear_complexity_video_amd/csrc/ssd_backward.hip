@@ -1300,6 +1300,13 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
         const int p = 32 * nt + (lane & 31);
         const float twoD = 2.f * Dv[h];
         const float inv_cnt = R > 0 ? 1.f / (float)(pt * ph * pw) : 0.f;
+        // The dx tile leaves through LDS as 16-byte row pieces: a 32 x 32 staging area per wave in sC,
+        // whose last reads (the C B^T tile) precede the barrier of block_sum. Row r sits in slot
+        // r ^ ((r >> 2) & 1), so that the two rows one accumulator element writes (r, r + 4) fall on
+        // different banks.
+        typedef uint32_t piece __attribute__((ext_vector_type(4)));
+        __bf16 *stg = sC + wave * (32 * 32);
+        auto slot = [](int r) { return r ^ ((r >> 2) & 1); };
         float ve[16], vf[16], vb[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -1310,12 +1317,17 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
             ve[e] = dtu > 0.f ? xv * scan / dtu : 0.f;
             vf[e] = xv * sf;
             vb[e] = xv * sb;
-            const uint32_t n = s_n[u];
-            if (n != kNoToken) {
-                float v = scan + twoD * (float)sY[u * LXM + p];
-                if (R > 0) v += rvx[e] * inv_cnt;
-                dx[((b * N + n) * nheads + h) * PM + p] = (__bf16)v;
-            }
+            float v = scan + twoD * (float)sY[u * LXM + p];
+            if (R > 0) v += rvx[e] * inv_cnt;
+            stg[slot(acc_row(e, lane)) * 32 + (lane & 31)] = (__bf16)v;
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int idx = lane + 64 * k, rr = idx >> 2, pc = idx & 3;
+            const uint32_t n = s_n[32 * mt + rr];
+            if (n != kNoToken)
+                *(piece *)(dx + ((b * N + n) * nheads + h) * PM + 32 * nt + 8 * pc) =
+                    *(const piece *)(stg + slot(rr) * 32 + 8 * pc);
         }
         const float re = half_sum16(ve), rf = half_sum16(vf), rb = half_sum16(vb);
         if ((lane & 1) == 0) {

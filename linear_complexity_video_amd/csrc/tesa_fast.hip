@@ -39,6 +39,7 @@ constexpr int KPAD = 8;           // K tile row padding (bf16)
 constexpr int VPAD = 32;          // V tile row padding (bf16): spreads transpose reads over the banks
 
 constexpr int MAXW = 4096;        // largest window (tokens) of the MFMA kernel
+constexpr int SMALLW = 512;       // windows up to this size take a table ring of this width
 
 template <int DH, int ROWS>
 struct __attribute__((aligned(16))) Smem {
@@ -58,20 +59,21 @@ struct Item {
 };
 
 // WHOLE: one window spanning the whole unshifted grid (full attention); a
-// window position is then its canonical token, and no table is kept.
+// window position is then its canonical token, and no table is kept. TW: the
+// width of each of the three window tables (the largest window it serves).
 //
 // Persistent: each workgroup runs a sequence of items. The tiles of
 // consecutive items form one stream, so during an item's last key tile the
 // next item's first tile and its Q fragments are already loading, and its
 // window table is built one item ahead.
-template <int DH, bool WHOLE>
+template <int DH, bool WHOLE, int TW>
 __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                                                    const __bf16 *__restrict__ v, __bf16 *__restrict__ o,
                                                    int nheads, int Tn, int Hn, int Wn, int wt, int wh, int ww,
                                                    int st, int sh, int sw, int nrt, int nrh, int nrw, int nqb,
                                                    uint32_t total, float c_log2)
 {
-    __shared__ Smem<DH, WHOLE ? 4 : 3 * MAXW> sm;
+    __shared__ Smem<DH, WHOLE ? 4 : 3 * TW> sm;
     constexpr int DC = DH / 8;  // 16-byte chunks per row
 
     // Item sequence of this workgroup. Block L runs on XCD L % 8, and XCD x owns a contiguous range of
@@ -138,11 +140,11 @@ __global__ __launch_bounds__(512) void k_tesa_fast(const __bf16 *__restrict__ q,
                 const int rem = l - lt * nhw;
                 const int lh = div_small(rem, I.nw, inv_w);
                 const int lw = rem - lh * I.nw;
-                sm.row[tb * MAXW + l] = (uint32_t)(((I.t0 + lt) * Hn + (I.h0 + lh)) * Wn + (I.w0 + lw));
+                sm.row[tb * TW + l] = (uint32_t)(((I.t0 + lt) * Hn + (I.h0 + lh)) * Wn + (I.w0 + lw));
             }
         }
     };
-    auto row_of = [&](int tb, int l) -> size_t { return WHOLE ? (size_t)l : (size_t)sm.row[tb * MAXW + l]; };
+    auto row_of = [&](int tb, int l) -> size_t { return WHOLE ? (size_t)l : (size_t)sm.row[tb * TW + l]; };
 
     // Q^T fragments (B operand of S^T = K Q^T) of this lane's query: d = 16 kb + 8 half + 0..7.
     // A query past the window reads the window's first row (finite; its output is never stored),
@@ -387,18 +389,19 @@ int cu_count()
     return cached[dev];
 }
 
-template <int DH, bool WHOLE>
+template <int DH, bool WHOLE, int TW>
 hipError_t launch(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
 {
     const int maxw = p.wt * p.wh * p.ww;
     const int nqb = (maxw + QB - 1) / QB;
     const uint64_t total = (uint64_t)p.batch * p.nheads * p.nrt * p.nrh * p.nrw * nqb;
-    // One workgroup per CU (the LDS footprint allows no second), a multiple of 8 (one set per XCD).
+    // One workgroup per CU (its LDS or its registers leave no room for a second), a multiple of 8 (one set
+    // per XCD).
     const uint64_t want = ((uint64_t)cu_count() + 7) / 8 * 8;
     const uint64_t blocks = std::min<uint64_t>(want, (total + 7) / 8 * 8);
     const float scale = p.scale > 0.f ? p.scale : 1.f / sqrtf((float)DH);
     timing::Scope ts_(K_TESA, stream);
-    k_tesa_fast<DH, WHOLE><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+    k_tesa_fast<DH, WHOLE, TW><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
         (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, p.nheads, (int)p.T,
         (int)p.H, (int)p.W, p.wt, p.wh, p.ww, p.st, p.sh, p.sw, p.nrt, p.nrh, p.nrw, nqb, (uint32_t)total,
         scale * 1.4426950408889634f);
@@ -419,8 +422,13 @@ bool tesa_fast_supports(const TesaProblem &p)
 hipError_t tesa_fast(const TesaProblem &p, const TesaArgs &a, hipStream_t stream)
 {
     const bool whole = p.nrt == 1 && p.nrh == 1 && p.nrw == 1;
-    if (p.headdim == 64) return whole ? launch<64, true>(p, a, stream) : launch<64, false>(p, a, stream);
-    return whole ? launch<128, true>(p, a, stream) : launch<128, false>(p, a, stream);
+    const bool small = (int64_t)p.wt * p.wh * p.ww <= SMALLW;
+    if (p.headdim == 64) {
+        if (whole) return launch<64, true, 1>(p, a, stream);
+        return small ? launch<64, false, SMALLW>(p, a, stream) : launch<64, false, MAXW>(p, a, stream);
+    }
+    if (whole) return launch<128, true, 1>(p, a, stream);
+    return small ? launch<128, false, SMALLW>(p, a, stream) : launch<128, false, MAXW>(p, a, stream);
 }
 
 } // namespace mate
