@@ -1305,6 +1305,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_dx_mfma(const __bf16 *__restrict__ 
         // r ^ ((r >> 2) & 1), so that the two rows one accumulator element writes (r, r + 4) fall on
         // different banks.
         typedef uint32_t piece __attribute__((ext_vector_type(4)));
+        static_assert(QM * LS >= NTB / 64 * 32 * 32, "sC holds every wave's staging area");
         __bf16 *stg = sC + wave * (32 * 32);
         auto slot = [](int r) { return r ^ ((r >> 2) & 1); };
         float ve[16], vf[16], vb[16];
