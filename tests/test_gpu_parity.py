@@ -511,6 +511,26 @@ def test_tesa_fast_late_dominant_keys(oracle_mod, grid, window, shift, d):
     assert parity_error(to_f64(o), want) <= 2e-2
 
 
+@pytest.mark.parametrize("grid,window,shift", [((1, 8, 16, 16), (8, 8, 16), (0, 0, 0)),
+                                               ((1, 24, 16, 16), (8, 16, 16), (4, 0, 0)),
+                                               ((1, 16, 16, 16), (16, 16, 16), (8, 8, 8))])
+@pytest.mark.parametrize("d", [64, 128])
+def test_tesa_fast_wide_windows(oracle_mod, grid, window, shift, d):
+    """Windows of more than 512 tokens take the MFMA kernel's wide window tables (4096 positions, the
+    narrow ones hold 512): two 1024-token windows; 2048-token windows shifted along t (regions of 1024
+    and 2048 tokens); and a whole-grid window shifted by half on every axis, whose eight 512-token
+    regions still use the wide tables (the width follows the window)."""
+    rng = np.random.default_rng(300 + d)
+    qkv = [synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(
+        (rng.standard_normal(grid + (2, d)) / np.sqrt(d)).astype(np.float32))) for _ in range(3)]
+    dev = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in qkv]
+    say(f"tesa fast wide windows grid={grid} window={window} shift={shift} d={d}")
+    o = torch.full_like(dev[0], float("nan"))
+    B.mate_tesa(*dev, o, window, shift, 0.0, B.ALGO_FAST)
+    want = oracle_mod.tesa(*qkv, grid, window, shift, nthreads=16)
+    assert parity_error(to_f64(o), want) <= 2e-2
+
+
 @pytest.mark.parametrize("grid", [(1, 4, 16, 16), (1, 5, 24, 23), (1, 8, 24, 24)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_tesa_whole_grid_window(oracle_mod, grid, d):
