@@ -17,6 +17,8 @@
 // Inside a tile, tokens go in groups of 8, stage by stage; the 8 lanes of a channel sum their C h
 // terms with three DPP steps. The forward direction writes y, the backward one a partial in the
 // workspace, and a last kernel adds the two.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "ssd_common.hpp"
@@ -306,12 +308,29 @@ hipError_t run(const MambaProblem &p, const MambaArgs &a, void *ws, hipStream_t 
         float *pdt = (float *)take((size_t)Bn * R * C * 4);
         E *pB = (E *)take((size_t)Bn * R * S * sizeof(E));
         timing::Scope ts_(K_SSD_POOL, st);
-        ssd::k_pool<E, E><<<dim3((C + 255) / 256, R, Bn), 256, 0, st>>>((const E *)a.x, px, C, T, H, W, p.pool_t,
-                                                                       p.pool_h, p.pool_w, p.order);
-        ssd::k_pool<float, float><<<dim3((C + 255) / 256, R, Bn), 256, 0, st>>>(a.dt, pdt, C, T, H, W, p.pool_t,
-                                                                               p.pool_h, p.pool_w, p.order);
-        ssd::k_pool<E, E><<<dim3((S + 255) / 256, R, Bn), 256, 0, st>>>((const E *)a.b, pB, S, T, H, W, p.pool_t,
-                                                                       p.pool_h, p.pool_w, p.order);
+        // bf16 rows of whole 16-byte pieces pool 8 channels per thread
+        auto pool_rows = [&](const E *src, E *dst, int64_t Cr) {
+            if constexpr (std::is_same<E, bf16_t>::value) {
+                if (Cr % 8 == 0 && ((uintptr_t)src & 15) == 0) {
+                    ssd::k_pool8<bf16_t><<<dim3((unsigned)((Cr + 2047) / 2048), R, Bn), 256, 0, st>>>(
+                        src, dst, Cr, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+                    return;
+                }
+            }
+            ssd::k_pool<E, E><<<dim3((unsigned)((Cr + 255) / 256), R, Bn), 256, 0, st>>>(src, dst, Cr, T, H, W, p.pool_t,
+                                                                                       p.pool_h, p.pool_w, p.order);
+        };
+        pool_rows((const E *)a.x, px, C);
+        if (ssd::pool_f32x4_ok(a.dt, C))
+            ssd::k_pool_f32x4<<<dim3(R, Bn), ssd::kPoolF4Threads, 0, st>>>(a.dt, pdt, C, T, H, W, p.pool_t, p.pool_h,
+                                                                         p.pool_w, p.order);
+        else if (C % 4 == 0 && ((uintptr_t)a.dt & 15) == 0)
+            ssd::k_pool_f32x4_wide<<<dim3((unsigned)((C + 1023) / 1024), R, Bn), 256, 0, st>>>(
+                a.dt, pdt, C, T, H, W, p.pool_t, p.pool_h, p.pool_w, p.order);
+        else
+            ssd::k_pool<float, float><<<dim3((C + 255) / 256, R, Bn), 256, 0, st>>>(a.dt, pdt, C, T, H, W, p.pool_t,
+                                                                                   p.pool_h, p.pool_w, p.order);
+        pool_rows((const E *)a.b, pB, S);
         rx = px;
         rdt = pdt;
         rB = pB;

@@ -168,6 +168,36 @@ __global__ __launch_bounds__(kPoolF4Threads) void k_pool_f32x4(const F *__restri
     }
 }
 
+// Average pool of wide fp32 rows (C a multiple of 4, rows 16-byte aligned): 4 channels per thread, each
+// thread walking its pool block's rows in the order of k_pool (so the sums are the same). grid
+// (ceil(C / 1024), R, batch).
+template <typename F = float>
+__global__ __launch_bounds__(256) void k_pool_f32x4_wide(const F *__restrict__ src, F *__restrict__ out,
+                                                        int64_t C, uint32_t Tn, uint32_t Hn, uint32_t Wn, int pt,
+                                                        int ph, int pw, int order)
+{
+    const int64_t ch = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (ch >= C) return;
+    const uint32_t j = blockIdx.y, b = blockIdx.z, R = gridDim.y;
+    const uint32_t Tp = Tn / pt, Hp = Hn / ph, Wp = Wn / pw;
+    const uint32_t np = rms_index32(j, order, Tp, Hp, Wp);
+    const uint32_t tq = np / (Hp * Wp), hq = (np / Wp) % Hp, wq = np % Wp;
+    const size_t N = (size_t)Tn * Hn * Wn;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int dt_ = 0; dt_ < pt; ++dt_)
+        for (int dh = 0; dh < ph; ++dh) {
+            const size_t row0 = ((size_t)(tq * pt + dt_) * Hn + hq * ph + dh) * Wn + wq * pw;
+#pragma unroll 8
+            for (int dw = 0; dw < pw; ++dw) {
+                typedef float f32x4v __attribute__((ext_vector_type(4)));
+                const f32x4v v = __builtin_nontemporal_load((const f32x4v *)(src + ((size_t)b * N + row0 + dw) * C + ch));
+                acc.x += v[0]; acc.y += v[1]; acc.z += v[2]; acc.w += v[3];
+            }
+        }
+    const float inv = 1.f / (float)(pt * ph * pw);
+    *(float4 *)(out + ((size_t)b * R + j) * C + ch) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
 // Average pool over disjoint pt x ph x pw blocks; out[b][j][ch] with j in RMS
 // order `order` of the pooled grid. grid (ceil(C / 256), R, batch).
 template <typename E, typename O>
