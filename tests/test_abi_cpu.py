@@ -143,6 +143,29 @@ def test_tesa_backward_validation():
     assert B.mate_tesa_backward_workspace_size((1, 4, 4, 4), desc(headdim=32)) == 0
 
 
+def test_last_error_is_per_thread():
+    """mate_last_error is thread-local: two threads that fail for different reasons each read their own
+    reason, also after the other thread's failure."""
+    import threading
+    lib = B.lib()
+    g = B.Grid(1, 2, 2, 2)
+    both_failed = threading.Barrier(2)
+    got = {}
+
+    def run(name, order, row_bytes):
+        status = lib.mate_rms_reorder(FAKE, ctypes.c_void_p(0x900000), g, row_bytes, order, 0, 0, None)
+        both_failed.wait(timeout=30)
+        got[name] = (status, lib.mate_last_error().decode())
+
+    threads = [threading.Thread(target=run, args=("order", 5, 16)), threading.Thread(target=run, args=("rows", 0, 0))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert got["order"][0] == B.MATE_ERR_SHAPE and "order" in got["order"][1] and "row_bytes" not in got["order"][1]
+    assert got["rows"][0] == B.MATE_ERR_SHAPE and "row_bytes" in got["rows"][1] and "order" not in got["rows"][1]
+
+
 def test_ssd_validation():
     g = B.Grid(1, 2, 4, 4)
     assert _scan(_ssd_t(y=0), g, 0, _ssd()) == B.MATE_ERR_NULL
