@@ -30,6 +30,17 @@ mate_status device_fail(hipError_t e, const char *what)
 }
 
 constexpr int64_t kMaxTokens = (int64_t)1 << 31;
+// Launch grids carry heads, groups, review tokens and the batch on their y and z extents, which the device
+// caps at 65536; larger counts are rejected here rather than failing at a launch.
+constexpr int64_t kMaxGridYZ = 65535;
+
+mate_status check_grid_yz(const char *what, int64_t v)
+{
+    if (v > kMaxGridYZ)
+        return fail(MATE_ERR_UNSUPPORTED, "%s %lld above %lld is not built (launch grid extent)", what, (long long)v,
+                    (long long)kMaxGridYZ);
+    return MATE_OK;
+}
 
 mate_status check_grid(mate_grid g)
 {
@@ -92,6 +103,9 @@ mate_status make_ssd_problem(mate_grid g, int order, const mate_ssd_desc *d, mat
     p.chunk = d->chunk; p.order = order;
     p.pool_t = pooled ? d->pool_t : 0; p.pool_h = pooled ? d->pool_h : 0; p.pool_w = pooled ? d->pool_w : 0;
     p.R = pooled ? (g.T / d->pool_t) * (g.H / d->pool_h) * (g.W / d->pool_w) : 0;
+    if ((s = check_grid_yz("batch", g.batch)) != MATE_OK || (s = check_grid_yz("nheads", d->nheads)) != MATE_OK ||
+        (s = check_grid_yz("review tokens", p.R)) != MATE_OK)
+        return s;
     p.nch = (int)((p.N + d->chunk - 1) / d->chunk);
     p.nchR = (int)((p.R + d->chunk - 1) / d->chunk);
     p.dtype = d->dtype == MATE_BF16 ? 1 : 0;
@@ -127,6 +141,8 @@ mate_status make_mamba_problem(mate_grid g, int order, const mate_mamba_desc *d,
     p.channels = d->channels; p.d_state = d->d_state; p.order = order;
     p.pool_t = pooled ? d->pool_t : 0; p.pool_h = pooled ? d->pool_h : 0; p.pool_w = pooled ? d->pool_w : 0;
     p.R = pooled ? (g.T / d->pool_t) * (g.H / d->pool_h) * (g.W / d->pool_w) : 0;
+    if ((s = check_grid_yz("batch", g.batch)) != MATE_OK || (s = check_grid_yz("review tokens", p.R)) != MATE_OK)
+        return s;
     p.dtype = d->dtype == MATE_BF16 ? 1 : 0;
     return MATE_OK;
 }
@@ -147,6 +163,8 @@ mate_status make_tesa_problem(mate_grid g, const mate_tesa_desc *d, mate::TesaPr
     if (!valid_algo(d->algo)) return fail(MATE_ERR_SHAPE, "unknown algo %d", (int)d->algo);
     if ((int64_t)d->nheads * g.batch * g.T * g.H * g.W >= kMaxTokens)
         return fail(MATE_ERR_UNSUPPORTED, "batch*tokens*nheads must stay below 2^31");
+    if ((s = check_grid_yz("batch", g.batch)) != MATE_OK || (s = check_grid_yz("nheads", d->nheads)) != MATE_OK)
+        return s;
     p.batch = g.batch; p.T = g.T; p.H = g.H; p.W = g.W;
     p.nheads = d->nheads; p.headdim = d->headdim;
     p.wt = d->win_t; p.wh = d->win_h; p.ww = d->win_w;

@@ -120,6 +120,27 @@ def test_mamba_validation():
     assert B.mate_bimamba_workspace_size((1, 2, 4, 4), _mamba(d_state=12)) == 0
 
 
+def test_launch_grid_extents_rejected_before_launch():
+    """Batch, head and review-token counts above 65535 (the launch grids' y and z extents) fail validation
+    with MATE_ERR_UNSUPPORTED instead of failing at a launch."""
+    lib = B.lib()
+    big = 70000
+    err = lambda: lib.mate_last_error().decode()
+    assert _scan(_ssd_t(), B.Grid(big, 1, 1, 2), 0, _ssd()) == B.MATE_ERR_UNSUPPORTED and "batch" in err()
+    assert _scan(_ssd_t(), B.Grid(1, 2, 2, 2), 0, _ssd(nheads=big)) == B.MATE_ERR_UNSUPPORTED and "nheads" in err()
+    one = B.Grid(1, 1, 256, 257)  # 65792 tokens, each its own review token under a 1x1x1 pool
+    assert _scan(_ssd_t(), one, 0, _ssd(pool_t=1, pool_h=1, pool_w=1)) == B.MATE_ERR_UNSUPPORTED
+    assert "review tokens" in err()
+    assert _mscan(_ssd_t(), one, 0, _mamba(pool_t=1, pool_h=1, pool_w=1)) == B.MATE_ERR_UNSUPPORTED
+    assert _mscan(_ssd_t(), B.Grid(big, 1, 1, 2), 0, _mamba()) == B.MATE_ERR_UNSUPPORTED
+    ptrs = {n: 0x100000 + 0x1000 * i for i, n in enumerate(("q", "k", "v", "o"))}
+    desc = lambda **kw: B.TesaDesc(**{**dict(nheads=2, headdim=64, win_t=1, win_h=1, win_w=2, shift_t=0, shift_h=0,
+                                             shift_w=0, scale=0.0, dtype=B.MATE_BF16, algo=B.ALGO_AUTO), **kw})
+    tesa = lambda g, d: lib.mate_tesa(ctypes.byref(B.TesaTensors(**ptrs)), g, ctypes.byref(d), None)
+    assert tesa(B.Grid(big, 1, 1, 2), desc()) == B.MATE_ERR_UNSUPPORTED and "batch" in err()
+    assert tesa(B.Grid(1, 1, 1, 2), desc(nheads=big)) == B.MATE_ERR_UNSUPPORTED and "nheads" in err()
+
+
 def test_tesa_backward_validation():
     lib = B.lib()
     g = B.Grid(1, 4, 4, 4)
