@@ -184,12 +184,16 @@ mate_status mate_bissd_scan(const mate_ssd_tensors *t, mate_grid g, int order, c
  *          dt, ddt [batch][T][H][W][nheads] fp32;  a, d, da, dd [nheads] fp32
  * Every output is written whole; outputs must not overlap the inputs. The
  * evaluation is chunked with chunks of its own (64 tokens, 32 for the widest
- * states), whatever the descriptor's chunk; arithmetic is fp32. Supported:
- * headdim 16, 32 or 64, d_state a multiple of 8 up to 128 (MATE_ERR_UNSUPPORTED
- * otherwise); the descriptor's algo is ignored. The workspace (at least
- * mate_bissd_backward_workspace_size bytes, 256-byte aligned) is scratch for
- * the call: it holds four fp32 states per chunk and head. Other errors as
- * mate_bissd_scan. */
+ * states), whatever the descriptor's chunk. bf16 tensors with headdim 64 and
+ * d_state 64 or 128 run on bf16 MFMA with fp32 accumulation (chunk states
+ * stored as bf16 and carried across chunks in fp32; the intra-chunk matrices
+ * enter as bf16 pairs); other shapes, and fp32 tensors, compute in fp32.
+ * Supported: headdim 16, 32 or 64, d_state a multiple of 8 up to 128, and
+ * ceil(R / 16) * batch * nheads < 2^24 for R review tokens
+ * (MATE_ERR_UNSUPPORTED otherwise); the descriptor's algo is ignored. The
+ * workspace (at least mate_bissd_backward_workspace_size bytes, 256-byte
+ * aligned) is scratch for the call: it holds four states per chunk and head
+ * (bf16 on the MFMA path, fp32 otherwise). Other errors as mate_bissd_scan. */
 typedef struct {
     const void *x, *b, *c;
     const float *dt, *a, *d;

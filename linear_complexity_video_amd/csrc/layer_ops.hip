@@ -208,16 +208,22 @@ hipError_t layer_gated_norm(const void *y, void *z, const float *w, int64_t toke
 {
     if (tokens == 0) return hipSuccess;
     const int np = (channels / 8 + NT_NORM - 1) / NT_NORM;
-    const bf16_t *yb = (const bf16_t *)y;
-    bf16_t *zb = (bf16_t *)z;
-    if (np <= 2)
-        k_gated_norm_1pass<2><<<(unsigned)tokens, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
-    else if (np <= 5)
-        k_gated_norm_1pass<5><<<(unsigned)tokens, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
-    else if (np <= 8)
-        k_gated_norm_1pass<8><<<(unsigned)tokens, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
-    else
-        k_gated_norm<<<(unsigned)tokens, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
+    // A block per row, in launches of at most 2^20 rows (a grid of all rows could pass the launch limit
+    // of 2^32 work-items).
+    constexpr int64_t kRowsPerLaunch = (int64_t)1 << 20;
+    for (int64_t r0 = 0; r0 < tokens; r0 += kRowsPerLaunch) {
+        const unsigned rows = (unsigned)std::min<int64_t>(kRowsPerLaunch, tokens - r0);
+        const bf16_t *yb = (const bf16_t *)y + r0 * channels;
+        bf16_t *zb = (bf16_t *)z + r0 * channels;
+        if (np <= 2)
+            k_gated_norm_1pass<2><<<rows, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
+        else if (np <= 5)
+            k_gated_norm_1pass<5><<<rows, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
+        else if (np <= 8)
+            k_gated_norm_1pass<8><<<rows, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
+        else
+            k_gated_norm<<<rows, NT_NORM, 0, st>>>(yb, zb, w, channels, groups, eps);
+    }
     return hipGetLastError();
 }
 

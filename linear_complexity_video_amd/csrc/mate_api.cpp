@@ -332,8 +332,8 @@ mate_status mate_bissd_backward(const mate_ssd_grad_tensors *t, mate_grid g, int
     mate_status s = make_ssd_problem(g, order, d, p, fast);
     if (s != MATE_OK) return s;
     if (!mate::ssd_backward_supports(p))
-        return fail(MATE_ERR_UNSUPPORTED, "the scan's backward is built for headdim 16, 32 or 64 and d_state <= 128 "
-                                          "(a multiple of 8)");
+        return fail(MATE_ERR_UNSUPPORTED, "the scan's backward is built for headdim 16, 32 or 64, d_state <= 128 "
+                                          "(a multiple of 8) and ceil(review tokens / 16) * batch * nheads < 2^24");
     const size_t need = mate::ssd_backward_workspace(p);
     if (!workspace || workspace_bytes < need)
         return fail(MATE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);

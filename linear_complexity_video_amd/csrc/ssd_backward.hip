@@ -1633,8 +1633,11 @@ hipError_t set_lds_attrs()
 
 bool ssd_backward_supports(const SsdProblem &p)
 {
+    // the review-token gradient launch: a workgroup per RT review tokens, head and batch element, its
+    // work-items below 2^32
+    const int64_t review_groups = (p.R + RT - 1) / RT * p.batch * p.nheads;
     return (p.headdim == 16 || p.headdim == 32 || p.headdim == 64) && p.d_state <= 128 && p.d_state % 8 == 0 &&
-           (size_t)review_lds(p) <= 160 * 1024;
+           (size_t)review_lds(p) <= 160 * 1024 && review_groups * NTB < ((int64_t)1 << 32);
 }
 
 size_t ssd_backward_workspace(const SsdProblem &p) { return bwd_layout(p).total; }

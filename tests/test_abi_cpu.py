@@ -141,6 +141,29 @@ def test_launch_grid_extents_rejected_before_launch():
     assert tesa(B.Grid(1, 1, 1, 2), desc(nheads=big)) == B.MATE_ERR_UNSUPPORTED and "nheads" in err()
 
 
+def test_ssd_backward_validation():
+    lib = B.lib()
+    g = B.Grid(1, 2, 4, 4)
+    ptrs = {f[0]: 0x100000 + 0x1000 * i for i, f in enumerate(B.SsdGradTensors._fields_)}
+    t = lambda **kw: B.SsdGradTensors(**{**ptrs, **kw})
+    call = lambda tt, gg, dd, ws=0x800000, wsb=1 << 40: lib.mate_bissd_backward(
+        ctypes.byref(tt), gg, 0, ctypes.byref(dd), ctypes.c_void_p(ws), wsb, None)
+    assert call(t(dy=0), g, _ssd()) == B.MATE_ERR_NULL
+    assert call(t(dd=0), g, _ssd()) == B.MATE_ERR_NULL
+    assert call(t(dx=0x100008), g, _ssd()) == B.MATE_ERR_UNSUPPORTED            # misaligned
+    assert call(t(), g, _ssd(chunk=0)) == B.MATE_ERR_SHAPE
+    assert call(t(), g, _ssd(headdim=24)) == B.MATE_ERR_UNSUPPORTED
+    assert call(t(), g, _ssd(d_state=12)) == B.MATE_ERR_UNSUPPORTED
+    # 65535 review tokens (a 1x1x1 pool) and 5000 heads: the review-gradient launch would pass 2^32
+    # work-items
+    big = B.Grid(1, 1, 255, 257)
+    assert call(t(), big, _ssd(nheads=5000, pool_t=1, pool_h=1, pool_w=1)) == B.MATE_ERR_UNSUPPORTED
+    assert "2^24" in lib.mate_last_error().decode()
+    assert call(t(), g, _ssd(), wsb=16) == B.MATE_ERR_WORKSPACE
+    assert call(t(), g, _ssd(), ws=0x800010) == B.MATE_ERR_WORKSPACE
+    assert call(t(), g, _ssd(), ws=0) == B.MATE_ERR_WORKSPACE
+
+
 def test_tesa_backward_validation():
     lib = B.lib()
     g = B.Grid(1, 4, 4, 4)
