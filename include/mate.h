@@ -54,9 +54,10 @@ typedef enum {
                                  the grid, shift outside [0, window), heads not divisible by
                                  groups, chunk < 1 */
     MATE_ERR_UNSUPPORTED = 3, /* legal for the method but not built (e.g. a head size the
-                                 kernels are not instantiated for, or a batch, head count or
+                                 kernels are not instantiated for; a batch, head count or
                                  review-token count above 65535, the launch grids' y and z
-                                 extents) */
+                                 extents; more than 2^22 scan chunks per sequence or window
+                                 regions, or 2^26 Mamba channels) */
     MATE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the *_workspace_size result */
     MATE_ERR_DEVICE = 5       /* a HIP call or kernel launch failed */
 } mate_status;

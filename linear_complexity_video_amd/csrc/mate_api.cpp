@@ -106,6 +106,8 @@ mate_status make_ssd_problem(mate_grid g, int order, const mate_ssd_desc *d, mat
     if ((s = check_grid_yz("batch", g.batch)) != MATE_OK || (s = check_grid_yz("nheads", d->nheads)) != MATE_OK ||
         (s = check_grid_yz("review tokens", p.R)) != MATE_OK)
         return s;
+    if ((p.N + d->chunk - 1) / d->chunk > ((int64_t)1 << 22))
+        return fail(MATE_ERR_UNSUPPORTED, "more than 2^22 chunks per sequence are not built (launch grid extent)");
     p.nch = (int)((p.N + d->chunk - 1) / d->chunk);
     p.nchR = (int)((p.R + d->chunk - 1) / d->chunk);
     p.dtype = d->dtype == MATE_BF16 ? 1 : 0;
@@ -137,6 +139,8 @@ mate_status make_mamba_problem(mate_grid g, int order, const mate_mamba_desc *d,
         return fail(MATE_ERR_UNSUPPORTED, "d_state %d not built (8, 16 or 32)", d->d_state);
     if ((int64_t)d->channels * g.batch * g.T * g.H * g.W >= ((int64_t)1 << 40))
         return fail(MATE_ERR_UNSUPPORTED, "batch*tokens*channels must stay below 2^40");
+    if (d->channels > (1 << 26))
+        return fail(MATE_ERR_UNSUPPORTED, "more than 2^26 channels are not built (launch grid extent)");
     p.batch = g.batch; p.T = g.T; p.H = g.H; p.W = g.W;
     p.channels = d->channels; p.d_state = d->d_state; p.order = order;
     p.pool_t = pooled ? d->pool_t : 0; p.pool_h = pooled ? d->pool_h : 0; p.pool_w = pooled ? d->pool_w : 0;
@@ -172,6 +176,8 @@ mate_status make_tesa_problem(mate_grid g, const mate_tesa_desc *d, mate::TesaPr
     p.nrt = (int)(g.T / d->win_t) + (d->shift_t ? 1 : 0);
     p.nrh = (int)(g.H / d->win_h) + (d->shift_h ? 1 : 0);
     p.nrw = (int)(g.W / d->win_w) + (d->shift_w ? 1 : 0);
+    if ((int64_t)p.nrt * p.nrh * p.nrw > ((int64_t)1 << 22))
+        return fail(MATE_ERR_UNSUPPORTED, "more than 2^22 window regions are not built (launch grid extent)");
     p.scale = d->scale;
     p.dtype = d->dtype == MATE_BF16 ? 1 : 0;
     const bool has_fast = mate::tesa_fast_supports(p);

@@ -139,6 +139,11 @@ def test_launch_grid_extents_rejected_before_launch():
     tesa = lambda g, d: lib.mate_tesa(ctypes.byref(B.TesaTensors(**ptrs)), g, ctypes.byref(d), None)
     assert tesa(B.Grid(big, 1, 1, 2), desc()) == B.MATE_ERR_UNSUPPORTED and "batch" in err()
     assert tesa(B.Grid(1, 1, 1, 2), desc(nheads=big)) == B.MATE_ERR_UNSUPPORTED and "nheads" in err()
+    # more than 2^22 one-token windows, scan chunks of 8 tokens, or 2^26 Mamba channels
+    assert tesa(B.Grid(1, 2, 2048, 1025), desc(win_w=1)) == B.MATE_ERR_UNSUPPORTED and "regions" in err()
+    assert _scan(_ssd_t(), B.Grid(1, 2, 4096, 4097), 0, _ssd()) == B.MATE_ERR_UNSUPPORTED and "chunks" in err()
+    assert _mscan(_ssd_t(), B.Grid(1, 1, 1, 2), 0, _mamba(channels=(1 << 26) + 8)) == B.MATE_ERR_UNSUPPORTED
+    assert "channels" in err()
 
 
 def test_ssd_backward_validation():
